@@ -1,0 +1,278 @@
+// Host side of the CSA2 C ABI: argument validation (all of it before any HIP call),
+// workspace carving, grid sizing and launches.  Declarations and contracts: include/csa2.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "csa2.h"
+
+namespace csa2 {
+
+// ---- mirrored from the kernels (kept in one place here) ----
+constexpr int kFullTile = 2048;
+constexpr int kHistBins = 2048;
+constexpr int kAttSplit = 64;
+constexpr int kAttNH = 16;
+constexpr int kAttPartStride = 132;
+constexpr size_t kAlign = 256;
+
+struct Thresh {
+    int32_t digit, above, in_bucket, total;
+};
+
+struct IndexWs {
+    uint32_t* ctrl;
+    uint32_t* hist;
+    Thresh* meta;
+    uint32_t* keys;
+    uint32_t* bkeys;
+    int32_t* sure_idx;
+    int32_t* sure_pool;
+    int32_t* cand_idx;
+    int32_t* cand_pool;
+};
+
+hipError_t launch_fp4_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
+                           uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream);
+hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
+                             const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
+                             int grid_tiles, int top_k, int pool_blocks, const IndexWs& ws, int32_t* idx_out,
+                             int32_t* pool_out, hipStream_t stream);
+hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
+                                const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
+                                const int32_t* pool, int pool_blocks, int top_k, const IndexWs& ws, int32_t* idx_out,
+                                hipStream_t stream);
+hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const int64_t* kv_row0,
+                         const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
+                         int top_k, const uint16_t* swa, const int64_t* swa_row0, int swa_cap, int64_t swa_rows,
+                         int window, int n_heads, float softmax_scale, float* out, uint32_t* ctrl, float* part,
+                         int n_split, hipStream_t stream);
+hipError_t launch_zero(void* ws, size_t bytes, hipStream_t stream);
+
+namespace {
+
+constexpr int64_t kMaxTiles = (int64_t)1 << 30;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// Common prefix of every workspace: counters, then the two 2048-bin histograms per query.
+size_t ctrl_bytes(int n_q) { return CSA2_CTRL_BYTES(n_q); }
+size_t hist_bytes(int n_q) { return align_up((size_t)n_q * 2 * kHistBins * 4); }
+
+int64_t full_grid_tiles(int n_q, int64_t total_len_ub, int32_t max_len_ub) {
+    const int64_t per_q = ((int64_t)max_len_ub + kFullTile - 1) / kFullTile;
+    int64_t a = (total_len_ub + kFullTile - 1) / kFullTile + n_q;
+    int64_t b = (int64_t)n_q * (per_q > 1 ? per_q : 1);
+    return a < b ? a : b;
+}
+
+struct Carve {
+    char* base;
+    size_t off = 0;
+    template <class T>
+    T* take(size_t count) {
+        T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+        off += align_up(count * sizeof(T));
+        return p;
+    }
+};
+
+IndexWs carve_full(void* ws, int n_q, int64_t tiles, int top_k, int pool_blocks, size_t* used) {
+    Carve c{static_cast<char*>(ws)};
+    IndexWs w{};
+    w.ctrl = c.take<uint32_t>(ctrl_bytes(n_q) / 4);
+    w.hist = c.take<uint32_t>(hist_bytes(n_q) / 4);
+    w.meta = c.take<Thresh>((size_t)n_q * 2);
+    w.keys = c.take<uint32_t>((size_t)tiles * kFullTile);
+    w.bkeys = c.take<uint32_t>((size_t)tiles * (kFullTile / 8));
+    w.sure_idx = c.take<int32_t>((size_t)n_q * top_k);
+    w.sure_pool = c.take<int32_t>((size_t)n_q * (pool_blocks > 0 ? pool_blocks : 1));
+    w.cand_idx = c.take<int32_t>((size_t)tiles * kFullTile);
+    w.cand_pool = c.take<int32_t>((size_t)tiles * (kFullTile / 8));
+    *used = c.off;
+    return w;
+}
+
+IndexWs carve_reindex(void* ws, int n_q, int top_k, int pool_blocks, size_t* used) {
+    Carve c{static_cast<char*>(ws)};
+    IndexWs w{};
+    w.ctrl = c.take<uint32_t>(ctrl_bytes(n_q) / 4);
+    w.hist = c.take<uint32_t>(hist_bytes(n_q) / 4);
+    w.meta = c.take<Thresh>((size_t)n_q * 2);
+    w.keys = c.take<uint32_t>((size_t)n_q * pool_blocks * 8);
+    w.sure_idx = c.take<int32_t>((size_t)n_q * top_k);
+    w.cand_idx = c.take<int32_t>((size_t)n_q * pool_blocks * 8);
+    *used = c.off;
+    return w;
+}
+
+int attend_splits(int top_k, int window) { return (top_k + window + kAttSplit - 1) / kAttSplit; }
+
+size_t attend_bytes(int n_q, int n_split, uint32_t** ctrl, float** part, void* ws) {
+    Carve c{static_cast<char*>(ws)};
+    uint32_t* ct = c.take<uint32_t>(ctrl_bytes(n_q) / 4);
+    c.take<uint32_t>(hist_bytes(n_q) / 4);
+    float* pt = c.take<float>((size_t)n_q * n_split * kAttNH * kAttPartStride);
+    if (ctrl) *ctrl = ct;
+    if (part) *part = pt;
+    return c.off;
+}
+
+int check_seqs(const csa2_seqs& s) {
+    if (s.n_q < 0 || s.n_q > CSA2_MAX_QUERIES || s.max_len_ub < 0 || s.total_len_ub < 0 || s.cache_rows < 0)
+        return CSA2_ERR_SHAPE;
+    if (s.n_q > 0 && (s.kv_row0 == nullptr || s.kv_len == nullptr)) return CSA2_ERR_NULL;
+    return CSA2_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH; }
+
+}  // namespace
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" {
+
+int fp4_kv_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64_t* dst_rows, int64_t row0, uint8_t* codes,
+                  uint8_t* scales, int64_t cap_rows, void* stream) {
+    if (n_tok < 0 || dim <= 0 || dim % 16 != 0 || dim > 1024 || cap_rows < 0) return CSA2_ERR_SHAPE;
+    if (n_tok == 0) return CSA2_OK;
+    if (x == nullptr || codes == nullptr || scales == nullptr) return CSA2_ERR_NULL;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0) return CSA2_ERR_SHAPE;
+    if (n_tok > ((int64_t)1 << 40)) return CSA2_ERR_SHAPE;
+    if (dst_rows == nullptr && (row0 < 0 || row0 > cap_rows || n_tok > cap_rows - row0)) return CSA2_ERR_CAPACITY;
+    return launch_status(launch_fp4_pack(x, n_tok, dim, dst_rows, row0, codes, scales, cap_rows,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32_t max_len_ub, int32_t top_k,
+                            int32_t pool_blocks) {
+    if (n_q < 0 || n_q > CSA2_MAX_QUERIES || total_len_ub < 0 || max_len_ub < 0) return 0;
+    size_t used = 0;
+    switch (op) {
+        case CSA2_OP_INDEX_FULL: {
+            if (top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 || pool_blocks > CSA2_MAX_SELECT) return 0;
+            const int64_t tiles = full_grid_tiles(n_q, total_len_ub, max_len_ub);
+            if (tiles > kMaxTiles) return 0;
+            carve_full(nullptr, n_q, tiles, top_k, pool_blocks, &used);
+            return used;
+        }
+        case CSA2_OP_INDEX_REINDEX:
+            if (top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 1 || pool_blocks > CSA2_MAX_SELECT) return 0;
+            carve_reindex(nullptr, n_q, top_k, pool_blocks, &used);
+            return used;
+        case CSA2_OP_ATTEND:
+            // top_k = selected slots, pool_blocks = window length
+            if (top_k < 0 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 || pool_blocks > CSA2_MAX_WINDOW) return 0;
+            return attend_bytes(n_q, attend_splits(top_k, pool_blocks) > 0 ? attend_splits(top_k, pool_blocks) : 1,
+                                nullptr, nullptr, nullptr);
+        default:
+            return 0;
+    }
+}
+
+int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
+                    int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
+                    int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
+    (void)shared_kv;
+    int st = check_seqs(seqs);
+    if (st) return st;
+    if (n_heads < 1 || n_heads > CSA2_MAX_IDX_HEADS || top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 ||
+        pool_blocks > CSA2_MAX_SELECT)
+        return CSA2_ERR_SHAPE;
+    if (block != CSA2_BLOCK) return CSA2_ERR_UNSUPPORTED;
+    if (seqs.n_q == 0) return CSA2_OK;
+    if (q_idx == nullptr || w == nullptr || k_idx == nullptr || idx_out == nullptr) return CSA2_ERR_NULL;
+    if (pool_blocks > 0 && pool_out == nullptr) return CSA2_ERR_NULL;
+    if (!aligned16(q_idx) || !aligned16(k_idx)) return CSA2_ERR_SHAPE;
+    const int64_t tiles = full_grid_tiles(seqs.n_q, seqs.total_len_ub, seqs.max_len_ub);
+    if (tiles > kMaxTiles) return CSA2_ERR_SHAPE;
+    size_t need = 0;
+    carve_full(nullptr, seqs.n_q, tiles, top_k, pool_blocks, &need);
+    if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return CSA2_ERR_WORKSPACE;
+    const IndexWs wsp = carve_full(ws, seqs.n_q, tiles, top_k, pool_blocks, &need);
+    return launch_status(launch_index_full(q_idx, w, k_idx, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
+                                           seqs.cache_rows, n_heads, (int)tiles, top_k, pool_blocks, wsp, idx_out,
+                                           pool_out, static_cast<hipStream_t>(stream)));
+}
+
+int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
+                       const int32_t* pool, int32_t pool_blocks, int32_t block, int32_t top_k, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, void* stream) {
+    int st = check_seqs(seqs);
+    if (st) return st;
+    if (n_heads < 1 || n_heads > CSA2_MAX_IDX_HEADS || top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 1 ||
+        pool_blocks > CSA2_MAX_SELECT)
+        return CSA2_ERR_SHAPE;
+    if (block != CSA2_BLOCK) return CSA2_ERR_UNSUPPORTED;
+    if (seqs.n_q == 0) return CSA2_OK;
+    if (q_idx == nullptr || w == nullptr || k_idx == nullptr || pool == nullptr || idx_out == nullptr)
+        return CSA2_ERR_NULL;
+    if (!aligned16(q_idx) || !aligned16(k_idx)) return CSA2_ERR_SHAPE;
+    size_t need = 0;
+    carve_reindex(nullptr, seqs.n_q, top_k, pool_blocks, &need);
+    if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return CSA2_ERR_WORKSPACE;
+    const IndexWs wsp = carve_reindex(ws, seqs.n_q, top_k, pool_blocks, &need);
+    return launch_status(launch_index_reindex(q_idx, w, k_idx, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
+                                              seqs.cache_rows, n_heads, pool, pool_blocks, top_k, wsp, idx_out,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs, const int32_t* idx,
+                int32_t top_k, const uint16_t* swa, const int64_t* swa_row0, int32_t swa_cap, int64_t swa_rows,
+                int32_t window, int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                void* stream) {
+    int st = check_seqs(seqs);
+    if (st) return st;
+    if (top_k < 0 || top_k > CSA2_MAX_SELECT || window < 0 || window > CSA2_MAX_WINDOW || n_heads < 1 ||
+        n_heads > CSA2_MAX_Q_HEADS || swa_rows < 0)
+        return CSA2_ERR_SHAPE;
+    if (window > 0 && (swa_cap < window)) return CSA2_ERR_SHAPE;
+    if (top_k + window == 0) return CSA2_ERR_SHAPE;
+    if (!(softmax_scale == softmax_scale)) return CSA2_ERR_SHAPE;
+    if (seqs.n_q == 0) return CSA2_OK;
+    if (q == nullptr || out == nullptr) return CSA2_ERR_NULL;
+    if (top_k > 0 && (codes == nullptr || scales == nullptr || idx == nullptr)) return CSA2_ERR_NULL;
+    if (window > 0 && (swa == nullptr || swa_row0 == nullptr)) return CSA2_ERR_NULL;
+    if (!aligned16(q) || (codes && !aligned16(codes)) || (swa && !aligned16(swa)) ||
+        (scales && (reinterpret_cast<uintptr_t>(scales) & 1u)))
+        return CSA2_ERR_SHAPE;
+    const int n_split = attend_splits(top_k, window);
+    const size_t need = attend_bytes(seqs.n_q, n_split, nullptr, nullptr, nullptr);
+    if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return CSA2_ERR_WORKSPACE;
+    uint32_t* ctrl = nullptr;
+    float* part = nullptr;
+    attend_bytes(seqs.n_q, n_split, &ctrl, &part, ws);
+    return launch_status(launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
+                                       seqs.cache_rows, idx, top_k, swa, swa_row0, window > 0 ? swa_cap : 1, swa_rows,
+                                       window, n_heads, softmax_scale, out, ctrl, part, n_split,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int csa2_workspace_init(void* ws, size_t bytes, void* stream) {
+    if (bytes == 0) return CSA2_OK;
+    if (ws == nullptr) return CSA2_ERR_NULL;
+    if (!aligned16(ws)) return CSA2_ERR_SHAPE;
+    return launch_status(launch_zero(ws, bytes, static_cast<hipStream_t>(stream)));
+}
+
+const char* csa2_status_string(int status) {
+    switch (status) {
+        case CSA2_OK: return "ok";
+        case CSA2_ERR_NULL: return "a required pointer is NULL";
+        case CSA2_ERR_SHAPE: return "a size argument is out of range";
+        case CSA2_ERR_UNSUPPORTED: return "size not supported by these kernels";
+        case CSA2_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case CSA2_ERR_CAPACITY: return "destination range exceeds capacity";
+        case CSA2_ERR_LAUNCH: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int csa2_version(void) { return 100; }
+
+}  // extern "C"

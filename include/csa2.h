@@ -1,0 +1,203 @@
+/*
+ * csa2.h -- C ABI of the CSA2 hot path on one MI355X (gfx950): FP4 pack-on-write,
+ * the Full / Reindex indexer with block pool and Top-K, and gather-dequant sparse
+ * attention with a bf16 sliding window.
+ *
+ * Sources (the method is described on three web pages):
+ *   [Viz]     "DeepSeek-V4.1-Flash: shrinking KV cache at 552B scale" visualisation
+ *             page (podcast.do-not-panic.com), figure captions.
+ *   [Summary] "DeepSeek Cuts KV Cache Footprint Fourfold" (sotapapers.com),
+ *             section "Technical Approach".
+ *   [Article] "DeepSeek-V4.1-Flash: Pushing KV Cache Compression to 890 Bytes per
+ *             Token" (trishampatil.com), sections VI, VIII, IX, XI.
+ *
+ * Conventions shared by every entry point
+ *   - All array pointers are DEVICE pointers owned by the caller (for example
+ *     torch tensors' data_ptr()).  The library allocates nothing, keeps no mutable
+ *     global state and is re-entrant; calls on one stream run in order.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   - bf16 arrays are uint16 bit patterns; fp32 arrays are IEEE binary32.
+ *   - Every argument that the host can see is validated before anything is
+ *     launched.  On a non-zero return nothing was launched and no output was
+ *     written.  After launching, hipGetLastError() is checked (CSA2_ERR_LAUNCH).
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - Values that live on the device (kv_len, kv_row0, idx, pool, dst_rows)
+ *     cannot be checked on the host.  Kernels clamp them so that no access leaves
+ *     the arrays described here: a length is clamped to [0, max_len_ub] and to the
+ *     cache rows that exist after kv_row0, selected indices outside [0, N) are
+ *     skipped, destination rows outside [0, cap_rows) are not written.  Results are
+ *     then those of the clamped problem.
+ *   - Inputs are finite.  Results are deterministic run to run (no float atomics).
+ *   - Workspace: index and attention calls take a caller-owned device workspace of
+ *     at least csa2_workspace_bytes(...) bytes.  Every workspace starts with the same
+ *     prefix for a given n_q: per-query counters (CSA2_CTRL_BYTES(n_q) bytes) and
+ *     per-query histograms.  That prefix must be zero when a call starts and every
+ *     call leaves it zero when it completes, so zero a new workspace once with
+ *     csa2_workspace_init() (a kernel, so it may be captured in a HIP graph).  Calls
+ *     may share a workspace (in stream order) only if they pass the same n_q; two
+ *     calls that may run concurrently must not share one.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---- */
+#define CSA2_OK 0
+#define CSA2_ERR_NULL 1        /* a required pointer is NULL */
+#define CSA2_ERR_SHAPE 2       /* a size argument is out of its valid range */
+#define CSA2_ERR_UNSUPPORTED 3 /* a valid size these kernels do not implement */
+#define CSA2_ERR_WORKSPACE 4   /* workspace NULL or smaller than csa2_workspace_bytes() */
+#define CSA2_ERR_CAPACITY 5    /* a destination range exceeds the stated capacity */
+#define CSA2_ERR_LAUNCH 6      /* the HIP runtime reported an error at launch */
+
+/* ---- limits of this implementation ---- */
+#define CSA2_KV_DIM 128         /* main-KV latent width = attention head dim */
+#define CSA2_IDX_DIM 64         /* indexer key / query width */
+#define CSA2_MAX_IDX_HEADS 8    /* indexer heads */
+#define CSA2_MAX_Q_HEADS 16     /* attention query heads sharing one KV head */
+#define CSA2_MAX_SELECT 4096    /* top_k and pool_blocks */
+#define CSA2_MAX_WINDOW 4096    /* sliding-window length */
+#define CSA2_MAX_QUERIES 65535  /* n_q */
+#define CSA2_BLOCK 8            /* positions per pool block */
+
+/* ---- operation ids for csa2_workspace_bytes ---- */
+#define CSA2_OP_INDEX_FULL 1
+#define CSA2_OP_INDEX_REINDEX 2
+#define CSA2_OP_ATTEND 3
+
+/* Bytes of self-cleaning counters at the start of every workspace. */
+#define CSA2_CTRL_BYTES(n_q) ((((size_t)(n_q) * 64u) + 255u) & ~(size_t)255u)
+
+/*
+ * Where each query's context lives.  Query i sees positions [0, N_i) of one
+ * sequence; position p of that sequence is row kv_row0[i] + p of the main-KV
+ * code/scale arrays and of the indexer-key array.  Decode passes one query per
+ * sequence; a prefill chunk passes one query per new token, all with the same
+ * kv_row0 and lengths C + t + 1 (a query sees its own token).
+ */
+typedef struct csa2_seqs {
+    const int64_t* kv_row0; /* device [n_q] */
+    const int32_t* kv_len;  /* device [n_q]: N_i */
+    int32_t n_q;            /* number of queries, >= 0 */
+    int32_t max_len_ub;     /* host: upper bound on every N_i, >= 0 */
+    int64_t total_len_ub;   /* host: upper bound on sum_i N_i, >= 0 */
+    int64_t cache_rows;     /* host: rows in the main-KV and indexer-key arrays */
+} csa2_seqs;
+
+/*
+ * fp4_kv_append -- pack-on-write of post-RoPE KV vectors into the FP4 cache.
+ * [Article] section XI and the [Viz] FP4 caption: E2M1 elements with one E4M3
+ * scale per 16 channels, no second-level scale, quantised after RoPE.
+ *
+ *   x        device bf16 [n_tok, dim], row-major.
+ *   dim      channels per vector; a multiple of 16, at most 1024.
+ *   dst_rows device int64 [n_tok] (token t goes to row dst_rows[t]) or NULL
+ *            (token t goes to row row0 + t; then row0 + n_tok <= cap_rows).
+ *   codes    device uint8 [cap_rows, dim/2]: byte j holds channel 2j in its low
+ *            nibble and channel 2j+1 in its high nibble (E2M1: sign bit 3).
+ *   scales   device uint8 [cap_rows, dim/16]: E4M3 (OCP "fn") byte of channels
+ *            [16g, 16g+16).
+ * Per group: scale = the E4M3 value nearest to amax/6, ties to even; each code is
+ * the E2M1 value nearest to x/scale, ties to even, saturating at 6, carrying x's
+ * sign bit; a zero scale gives zero magnitudes.  Rows outside [0, cap_rows) named
+ * by dst_rows are skipped.  n_tok == 0 is a no-op.
+ */
+int fp4_kv_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64_t* dst_rows,
+                  int64_t row0, uint8_t* codes, uint8_t* scales, int64_t cap_rows, void* stream);
+
+/*
+ * csa2_index_full -- Full-mode indexer for n_q queries.
+ * [Article] section IX (the Full layer scores every causally visible position,
+ * scores 8-position blocks by their best position and keeps the winning blocks as
+ * a shared pool) and [Summary] Technical Approach (Full mode computes Top-K fresh).
+ *
+ *   q_idx   device bf16 [n_q, n_heads, CSA2_IDX_DIM]: indexer queries.
+ *   w       device fp32 [n_q, n_heads]: per-head weights.
+ *   k_idx   device bf16 [seqs.cache_rows, CSA2_IDX_DIM]: indexer keys.
+ *   n_heads 1..CSA2_MAX_IDX_HEADS.
+ *   top_k   1..CSA2_MAX_SELECT; block must be CSA2_BLOCK.
+ *   pool_blocks 0 (no pool) or 1..CSA2_MAX_SELECT.
+ *   idx_out device int32 [n_q, top_k]: the top_k positions under (score desc,
+ *           position asc), written in ascending order, -1 padded when N_i < top_k.
+ *   pool_out device int32 [n_q, pool_blocks] or NULL when pool_blocks == 0: block
+ *           ids under (block max desc, block asc), ascending, -1 padded.
+ * Score of position p: sum_h w[h] * max(0, q_h . k_p), accumulated in fp32; with
+ * integer-valued inputs and |score| < 2^24 it is exact.  The scan is on vector
+ * ALUs when n_q is small; a prefill chunk (shared_kv != 0: every query has the same
+ * kv_row0) may use the MFMA path.  n_q == 0 is a no-op.
+ */
+int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
+                    int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
+                    int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * csa2_index_reindex -- Reindex-mode indexer: this layer's own query scored against
+ * the Full layer's keys, over the positions of the pool's blocks only.
+ * [Article] sections VIII-IX (Reindex reuses main KV and indexer K, runs its own
+ * selection inside the shared pool); [Summary] Technical Approach.
+ *
+ *   pool    device int32 [n_q, pool_blocks]: block ids from csa2_index_full; -1
+ *           entries and ids whose positions fall outside [0, N_i) contribute nothing.
+ *   Other arguments as in csa2_index_full.  idx_out gets the top_k candidate
+ *   positions under (score desc, position asc), ascending, -1 padded.
+ */
+int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
+                       int32_t n_heads, const int32_t* pool, int32_t pool_blocks, int32_t block,
+                       int32_t top_k, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_attend -- sparse attention of n_q queries over their selected FP4 entries
+ * plus their bf16 sliding window.  [Article] section VI ("What one layer looks
+ * like": own query, 512 selected entries plus the recent window) and section XI
+ * (entries are dequantised before attention).
+ *
+ *   q       device bf16 [n_q, n_heads, CSA2_KV_DIM].
+ *   codes, scales  the FP4 cache ([seqs.cache_rows, 64] and [seqs.cache_rows, 8]).
+ *   idx     device int32 [n_q, top_k]: selected positions; entries outside [0, N_i)
+ *           (e.g. -1 padding) are skipped.  A Reuse layer passes the idx of the
+ *           most recent index-producing layer.
+ *   swa     device bf16 [swa_rows, CSA2_KV_DIM]: the layer's window store; position
+ *           p of query i is row swa_row0[i] + (p mod swa_cap).
+ *   swa_row0 device int64 [n_q]; swa_cap >= window (>= 1); rows outside
+ *           [0, swa_rows) are skipped.
+ *   window  window length W >= 0: query i attends positions [max(0, N_i - W), N_i).
+ *   n_heads 1..CSA2_MAX_Q_HEADS.  softmax_scale multiplies q.k.
+ *   out     device fp32 [n_q, n_heads, CSA2_KV_DIM].
+ * Each entry's vector is both key and value.  One softmax runs over the selected
+ * entries and the window entries together (no de-duplication).  A query with
+ * nothing to attend gets zeros.  n_q == 0 is a no-op.
+ */
+int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
+                const int32_t* idx, int32_t top_k, const uint16_t* swa, const int64_t* swa_row0,
+                int32_t swa_cap, int64_t swa_rows, int32_t window, int32_t n_heads,
+                float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Workspace bytes for one call of `op` (CSA2_OP_*) with these sizes; 0 if the sizes
+ * are out of range.  For CSA2_OP_ATTEND pass the window length in `pool_blocks`
+ * (total_len_ub and max_len_ub are then unused); for CSA2_OP_INDEX_REINDEX
+ * total_len_ub and max_len_ub are unused.
+ */
+size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32_t max_len_ub,
+                            int32_t top_k, int32_t pool_blocks);
+
+/* Zero a workspace's first `bytes` bytes with a kernel on `stream` (call once after allocation). */
+int csa2_workspace_init(void* ws, size_t bytes, void* stream);
+
+/* Static text for a status code. */
+const char* csa2_status_string(int status);
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int csa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,230 @@
+"""GPU parity of each entry point against the CPU oracle at small and ragged sizes:
+bit-exact FP4 codes, scales, Top-K indices and pools; attention within 2e-3 * max|V|."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from compressed_sparse_attention_07_amd import csa2 as C
+from compressed_sparse_attention_07_amd import synth
+
+from gpu_helpers import AttendCase, IndexCase, bf16_tensor, DEV
+
+pytestmark = pytest.mark.gpu
+
+W_T = 900  # workload id for these tests' seeds
+
+
+# ---------------------------------------------------------------- FP4 pack-on-write
+@pytest.mark.parametrize("n_tok,dim", [(1, 128), (7, 16), (1000, 128), (4099, 128), (333, 1024), (64, 48)])
+def test_fp4_pack_bit_exact(n_tok, dim):
+    sig = synth.channel_sigma(W_T, synth.T_KV_SIGMA, dim, seq=n_tok)
+    x = synth.kv_bf16(W_T, synth.T_KV, n_tok, dim, sig, seq=n_tok)
+    codes = torch.zeros((n_tok, dim // 2), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((n_tok, dim // 16), dtype=torch.uint8, device=DEV)
+    C.fp4_kv_append(bf16_tensor(x), codes, scales)
+    c_ref, s_ref = O.fp4_quantize(x)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+
+
+def _special_groups():
+    f = synth.f32_to_bf16_bits
+    rows = []
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    for s in [1.0, 2.0 ** -9, 2.0 ** -6, 0.4375, 4.5, 448.0]:
+        g = [6 * s] + [m * s for m in mids] + [-m * s for m in mids] + [0.0]
+        rows.append(f(np.array(g, np.float32)))
+    rows.append(np.zeros(16, np.uint16))                    # amax 0
+    rows.append(np.full(16, 0x8000, np.uint16))             # all -0
+    rows.append(f(np.array([6 * 2.0 ** -10] + [0.0] * 15, np.float32)))   # scale tie to 0
+    rows.append(f(np.array([6.375] + [-6.375] * 15, np.float32)))         # saturation
+    rows.append(f(np.array([2688.0, -2688.0, 1.0] + [0.0] * 13, np.float32)))
+    r = np.random.default_rng(5)
+    for _ in range(200):                                     # every bf16 pattern class
+        rows.append(r.integers(0, 0x7F80, 16).astype(np.uint16) | (r.integers(0, 2, 16).astype(np.uint16) << 15))
+    x = np.stack(rows)
+    # keep finite, |x| <= 2688
+    v = O.bf16_to_f64(x)
+    x[np.abs(v) > 2688] = 0
+    return x
+
+
+def test_fp4_pack_special_groups():
+    x = _special_groups()
+    x = np.concatenate([x] * 8, axis=1)[:, :128]             # 128 channels per row
+    n = x.shape[0]
+    codes = torch.zeros((n, 64), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((n, 8), dtype=torch.uint8, device=DEV)
+    C.fp4_kv_append(bf16_tensor(x), codes, scales)
+    c_ref, s_ref = O.fp4_quantize(x)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+
+
+def test_fp4_pack_scatter_rows_and_skips_out_of_range():
+    n_tok, cap = 50, 80
+    sig = synth.channel_sigma(W_T, synth.T_KV_SIGMA, 128, seq=77)
+    x = synth.kv_bf16(W_T, synth.T_KV, n_tok, 128, sig, seq=77)
+    rows = np.random.default_rng(3).permutation(cap)[:n_tok].astype(np.int64)
+    rows[5] = -1
+    rows[9] = cap + 3
+    codes = torch.full((cap, 64), 0xAB, dtype=torch.uint8, device=DEV)
+    scales = torch.full((cap, 8), 0xCD, dtype=torch.uint8, device=DEV)
+    C.fp4_kv_append(bf16_tensor(x), codes, scales, dst_rows=torch.from_numpy(rows).to(DEV))
+    c_ref, s_ref = O.fp4_quantize(x)
+    cg, sg = codes.cpu().numpy(), scales.cpu().numpy()
+    written = set()
+    for t, r in enumerate(rows):
+        if 0 <= r < cap:
+            assert np.array_equal(cg[r], c_ref[t]) and np.array_equal(sg[r], s_ref[t])
+            written.add(int(r))
+    for r in range(cap):
+        if r not in written:
+            assert np.all(cg[r] == 0xAB) and np.all(sg[r] == 0xCD)
+
+
+def test_fp4_pack_row_offset_appends():
+    sig = synth.channel_sigma(W_T, synth.T_KV_SIGMA, 128, seq=78)
+    x = synth.kv_bf16(W_T, synth.T_KV, 10, 128, sig, seq=78)
+    codes = torch.zeros((30, 64), dtype=torch.uint8, device=DEV)
+    scales = torch.zeros((30, 8), dtype=torch.uint8, device=DEV)
+    C.fp4_kv_append(bf16_tensor(x), codes, scales, row0=17)
+    c_ref, s_ref = O.fp4_quantize(x)
+    assert np.array_equal(codes.cpu().numpy()[17:27], c_ref)
+    assert np.all(codes.cpu().numpy()[:17] == 0) and np.all(codes.cpu().numpy()[27:] == 0)
+    with pytest.raises(C.Csa2Error):
+        C.fp4_kv_append(bf16_tensor(x), codes, scales, row0=25)
+
+
+# ---------------------------------------------------------------- Full mode
+RAGGED = [0, 1, 7, 8, 9, 511, 512, 513, 2047, 2048, 2049, 4101, 20000]
+
+
+@pytest.mark.parametrize("top_k,pool_blocks,n_heads", [(512, 256, 4), (3, 1, 1), (64, 5, 8), (1, 0, 3),
+                                                       (2048, 2048, 4)])
+def test_index_full_bit_exact_ragged(top_k, pool_blocks, n_heads):
+    case = IndexCase(W_T + top_k, RAGGED, n_heads=n_heads)
+    idx, pool, _ = case.run_full(top_k, pool_blocks)
+    idx = idx.cpu().numpy()
+    pool = pool.cpu().numpy() if pool is not None else None
+    for i in range(len(RAGGED)):
+        ri, rp = case.oracle_full(i, top_k, pool_blocks)
+        assert np.array_equal(idx[i], ri), (i, RAGGED[i])
+        if pool_blocks:
+            assert np.array_equal(pool[i], rp), (i, RAGGED[i])
+
+
+def test_index_full_tie_heavy_and_repeatable():
+    lengths = [3000, 70000, 12345]
+    case = IndexCase(W_T + 1, lengths, n_heads=4, qlo=0, qhi=1)   # scores in a narrow integer range
+    ws = None
+    first = None
+    for rep in range(3):                                            # the workspace cleans itself
+        idx, pool, ws = case.run_full(512, 700, ws=ws)
+        got = (idx.cpu().numpy(), pool.cpu().numpy())
+        if first is None:
+            first = got
+        else:
+            assert np.array_equal(got[0], first[0]) and np.array_equal(got[1], first[1])
+    for i in range(len(lengths)):
+        ri, rp = case.oracle_full(i, 512, 700)
+        assert np.array_equal(first[0][i], ri)
+        assert np.array_equal(first[1][i], rp)
+
+
+def test_index_full_all_equal_scores_takes_lowest_positions():
+    # every score is 0: the whole context is one tie band (larger than the LDS sort)
+    lengths = [50000, 9000]
+    case = IndexCase(W_T + 2, lengths, n_heads=4, kfill=0)
+    idx, pool, _ = case.run_full(512, 2048)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for i in range(2):
+        assert np.array_equal(idx[i], np.arange(512))
+        nb = -(-lengths[i] // 8)
+        assert np.array_equal(pool[i], np.arange(2048) if nb >= 2048 else
+                              np.concatenate([np.arange(nb), -np.ones(2048 - nb, int)]))
+
+
+# ---------------------------------------------------------------- Reindex mode
+def test_index_reindex_bit_exact_and_invariant():
+    lengths = [4096, 65536, 777, 100, 30001]
+    case = IndexCase(W_T + 3, lengths, n_heads=4)
+    idx_f, pool, _ = case.run_full(512, 2048)
+    # Reindex with the Full layer's own query returns the Full Top-K (K <= P)
+    idx_r, _ = case.run_reindex(pool, 512)
+    assert np.array_equal(idx_r.cpu().numpy(), idx_f.cpu().numpy())
+    # another layer's query: bit-exact against the oracle
+    q2 = synth.int_bf16(W_T + 3, synth.T_IDX_Q, (len(lengths), 4, 64), seq=9)
+    w2 = synth.int_weights(W_T + 3, synth.T_IDX_W, (len(lengths), 4), seq=9)
+    idx2, _ = case.run_reindex(pool, 512, q_dev=bf16_tensor(q2), w_dev=torch.from_numpy(w2).to(DEV))
+    idx2 = idx2.cpu().numpy()
+    pool_np = pool.cpu().numpy()
+    for i in range(len(lengths)):
+        ref = case.oracle_reindex(i, pool_np[i], 512, q=q2[i], w=w2[i])
+        assert np.array_equal(idx2[i], ref), i
+
+
+def test_index_reindex_pool_with_padding_and_out_of_range_blocks():
+    lengths = [1000, 50]
+    case = IndexCase(W_T + 4, lengths, n_heads=4)
+    pool = np.full((2, 40), -1, dtype=np.int32)
+    pool[0, :10] = np.arange(0, 100, 10)
+    pool[0, 10] = 124                     # covers 992..999 (the last block, full)
+    pool[0, 11] = 5000                    # outside the context: contributes nothing
+    pool[1, :3] = [0, 6, 7]               # block 6 = 48..49 only (N = 50); block 7 is beyond
+    idx, _ = case.run_reindex(torch.from_numpy(pool).to(DEV), 100)
+    idx = idx.cpu().numpy()
+    for i in range(2):
+        assert np.array_equal(idx[i], case.oracle_reindex(i, pool[i], 100)), i
+
+
+# ---------------------------------------------------------------- attention
+def test_attend_selected_plus_window():
+    lengths = [4096, 300, 130, 5000]
+    case = AttendCase(W_T + 5, lengths, n_heads=16, window=128)
+    r = np.random.default_rng(11)
+    idx = np.full((len(lengths), 512), -1, dtype=np.int64)
+    for i, n in enumerate(lengths):
+        sel = np.sort(r.choice(n, size=min(n, 400), replace=False))
+        idx[i, :sel.size] = sel
+    out, _ = case.run(idx, 1 / np.sqrt(128))
+    case.check(out, idx, 1 / np.sqrt(128))
+
+
+@pytest.mark.parametrize("n_heads,top_k,window", [(5, 3, 0), (16, 0, 128), (1, 700, 17), (16, 64, 64)])
+def test_attend_shapes(n_heads, top_k, window):
+    lengths = [1000, 2, 64]
+    case = AttendCase(W_T + 6 + top_k, lengths, n_heads=n_heads, window=window, swa_cap=max(window, 1))
+    r = np.random.default_rng(12 + top_k)
+    idx = np.full((len(lengths), top_k), -1, dtype=np.int64)
+    for i, n in enumerate(lengths):
+        m = min(n, top_k)
+        idx[i, :m] = r.choice(n, size=m, replace=False)
+    out, _ = case.run(idx, 0.125)
+    case.check(out, idx, 0.125)
+
+
+def test_attend_empty_context_is_zero_and_duplicates_count():
+    lengths = [0, 10]
+    case = AttendCase(W_T + 7, lengths, n_heads=16, window=4)
+    idx = np.array([[-1, -1, 3, 3], [3, 3, 9, 12]])         # 12 >= N is ignored; duplicates kept
+    out, _ = case.run(idx, 0.1)
+    assert np.all(out[0] == 0.0)
+    case.check(out, idx, 0.1)
+
+
+def test_attend_dense_equivalence_all_positions():
+    lengths = [512, 200]
+    case = AttendCase(W_T + 8, lengths, n_heads=16, window=0, swa_cap=1)
+    idx = np.full((2, 512), -1, dtype=np.int64)
+    idx[0] = np.arange(512)
+    idx[1, :200] = np.arange(200)
+    out, _ = case.run(idx, 1 / np.sqrt(128))
+    for i, n in enumerate(lengths):
+        r0 = int(case.row0[i])
+        kv = torch.from_numpy(O.fp4_dequantize(case.codes_ref[r0:r0 + n], case.scales_ref[r0:r0 + n]))
+        qt = torch.from_numpy(O.bf16_to_f64(case.q[i]))[None, :, None, :]
+        kt = kv[None, None].expand(1, 16, -1, -1)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=1 / np.sqrt(128))[0, :, 0].numpy()
+        assert np.abs(out[i] - ref).max() <= 2e-3 * np.abs(kv.numpy()).max()
