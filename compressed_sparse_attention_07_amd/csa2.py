@@ -19,10 +19,13 @@ LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_CAPACITY, ERR_LAUNCH = range(7)
 OP_INDEX_FULL, OP_INDEX_REINDEX, OP_ATTEND = 1, 2, 3
 KV_DIM, IDX_DIM, BLOCK = 128, 64, 8
+SIZE_MAX = (1 << 64) - 1  # csa2_workspace_bytes: sizes out of range
 
 EXPORTS = (
     "fp4_kv_append",
     "csa2_index_full",
+    "csa2_index_full_scan",
+    "csa2_index_full_select",
     "csa2_index_reindex",
     "csa2_attend",
     "csa2_workspace_bytes",
@@ -62,7 +65,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
         L.fp4_kv_append.argtypes = [vp, i64, i32, vp, i64, vp, vp, i64, vp]
-        L.csa2_index_full.argtypes = [vp, vp, vp, SeqsC, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+        for name in ("csa2_index_full", "csa2_index_full_scan", "csa2_index_full_select"):
+            getattr(L, name).argtypes = [vp, vp, vp, SeqsC, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+            getattr(L, name).restype = ctypes.c_int
         L.csa2_index_reindex.argtypes = [vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
         L.csa2_attend.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, i32, f32, vp, vp, sz, vp]
         L.csa2_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
@@ -145,6 +150,8 @@ def csa2_workspace_init(ws, stream=None) -> None:
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A zeroed uint8 device workspace of at least nbytes (zeroed by the library's own kernel)."""
+    if nbytes == SIZE_MAX:
+        raise ValueError("workspace size query rejected the sizes")
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
     csa2_workspace_init(ws)
     return ws
@@ -155,6 +162,20 @@ def csa2_index_full(q_idx, w, k_idx, seqs: Seqs, top_k: int, pool_blocks: int, i
     n_heads = q_idx.shape[1]
     _check("csa2_index_full", lib().csa2_index_full(
         _ptr(q_idx), _ptr(w), _ptr(k_idx), seqs.c(), n_heads, top_k, block, pool_blocks, shared_kv,
+        _ptr(idx_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def csa2_index_full_scan(q_idx, w, k_idx, seqs: Seqs, top_k: int, pool_blocks: int, idx_out, pool_out, ws,
+                         block: int = BLOCK, shared_kv: int = 0, stream=None) -> None:
+    _check("csa2_index_full_scan", lib().csa2_index_full_scan(
+        _ptr(q_idx), _ptr(w), _ptr(k_idx), seqs.c(), q_idx.shape[1], top_k, block, pool_blocks, shared_kv,
+        _ptr(idx_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def csa2_index_full_select(q_idx, w, k_idx, seqs: Seqs, top_k: int, pool_blocks: int, idx_out, pool_out, ws,
+                           block: int = BLOCK, shared_kv: int = 0, stream=None) -> None:
+    _check("csa2_index_full_select", lib().csa2_index_full_select(
+        _ptr(q_idx), _ptr(w), _ptr(k_idx), seqs.c(), q_idx.shape[1], top_k, block, pool_blocks, shared_kv,
         _ptr(idx_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 

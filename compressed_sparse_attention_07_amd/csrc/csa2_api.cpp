@@ -11,10 +11,8 @@ namespace csa2 {
 
 // ---- mirrored from the kernels (kept in one place here) ----
 constexpr int kFullTile = 2048;
+constexpr int kFilterTile = 16384;
 constexpr int kHistBins = 2048;
-constexpr int kAttSplit = 64;
-constexpr int kAttNH = 16;
-constexpr int kAttPartStride = 132;
 constexpr size_t kAlign = 256;
 
 struct Thresh {
@@ -29,16 +27,16 @@ struct IndexWs {
     uint32_t* bkeys;
     int32_t* sure_idx;
     int32_t* sure_pool;
-    int32_t* cand_idx;
-    int32_t* cand_pool;
+    uint64_t* cand_idx;
+    uint64_t* cand_pool;
 };
 
 hipError_t launch_fp4_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
                            uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream);
 hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
                              const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
-                             int grid_tiles, int top_k, int pool_blocks, const IndexWs& ws, int32_t* idx_out,
-                             int32_t* pool_out, hipStream_t stream);
+                             int grid_tiles, int grid_ftiles, int top_k, int pool_blocks, const IndexWs& ws,
+                             int32_t* idx_out, int32_t* pool_out, int phase, hipStream_t stream);
 hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
                                 const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
                                 const int32_t* pool, int pool_blocks, int top_k, const IndexWs& ws, int32_t* idx_out,
@@ -46,8 +44,7 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const uin
 hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const int64_t* kv_row0,
                          const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
                          int top_k, const uint16_t* swa, const int64_t* swa_row0, int swa_cap, int64_t swa_rows,
-                         int window, int n_heads, float softmax_scale, float* out, uint32_t* ctrl, float* part,
-                         int n_split, hipStream_t stream);
+                         int window, int n_heads, float softmax_scale, float* out, hipStream_t stream);
 hipError_t launch_zero(void* ws, size_t bytes, hipStream_t stream);
 
 namespace {
@@ -60,9 +57,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 size_t ctrl_bytes(int n_q) { return CSA2_CTRL_BYTES(n_q); }
 size_t hist_bytes(int n_q) { return align_up((size_t)n_q * 2 * kHistBins * 4); }
 
-int64_t full_grid_tiles(int n_q, int64_t total_len_ub, int32_t max_len_ub) {
-    const int64_t per_q = ((int64_t)max_len_ub + kFullTile - 1) / kFullTile;
-    int64_t a = (total_len_ub + kFullTile - 1) / kFullTile + n_q;
+int64_t full_grid_tiles(int n_q, int64_t total_len_ub, int32_t max_len_ub, int tile = kFullTile) {
+    const int64_t per_q = ((int64_t)max_len_ub + tile - 1) / tile;
+    int64_t a = (total_len_ub + tile - 1) / tile + n_q;
     int64_t b = (int64_t)n_q * (per_q > 1 ? per_q : 1);
     return a < b ? a : b;
 }
@@ -88,8 +85,8 @@ IndexWs carve_full(void* ws, int n_q, int64_t tiles, int top_k, int pool_blocks,
     w.bkeys = c.take<uint32_t>((size_t)tiles * (kFullTile / 8));
     w.sure_idx = c.take<int32_t>((size_t)n_q * top_k);
     w.sure_pool = c.take<int32_t>((size_t)n_q * (pool_blocks > 0 ? pool_blocks : 1));
-    w.cand_idx = c.take<int32_t>((size_t)tiles * kFullTile);
-    w.cand_pool = c.take<int32_t>((size_t)tiles * (kFullTile / 8));
+    w.cand_idx = c.take<uint64_t>((size_t)tiles * kFullTile);
+    w.cand_pool = c.take<uint64_t>((size_t)tiles * (kFullTile / 8));
     *used = c.off;
     return w;
 }
@@ -102,21 +99,9 @@ IndexWs carve_reindex(void* ws, int n_q, int top_k, int pool_blocks, size_t* use
     w.meta = c.take<Thresh>((size_t)n_q * 2);
     w.keys = c.take<uint32_t>((size_t)n_q * pool_blocks * 8);
     w.sure_idx = c.take<int32_t>((size_t)n_q * top_k);
-    w.cand_idx = c.take<int32_t>((size_t)n_q * pool_blocks * 8);
+    w.cand_idx = c.take<uint64_t>((size_t)n_q * pool_blocks * 8);
     *used = c.off;
     return w;
-}
-
-int attend_splits(int top_k, int window) { return (top_k + window + kAttSplit - 1) / kAttSplit; }
-
-size_t attend_bytes(int n_q, int n_split, uint32_t** ctrl, float** part, void* ws) {
-    Carve c{static_cast<char*>(ws)};
-    uint32_t* ct = c.take<uint32_t>(ctrl_bytes(n_q) / 4);
-    c.take<uint32_t>(hist_bytes(n_q) / 4);
-    float* pt = c.take<float>((size_t)n_q * n_split * kAttNH * kAttPartStride);
-    if (ctrl) *ctrl = ct;
-    if (part) *part = pt;
-    return c.off;
 }
 
 int check_seqs(const csa2_seqs& s) {
@@ -151,34 +136,33 @@ int fp4_kv_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64_t* 
 
 size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32_t max_len_ub, int32_t top_k,
                             int32_t pool_blocks) {
-    if (n_q < 0 || n_q > CSA2_MAX_QUERIES || total_len_ub < 0 || max_len_ub < 0) return 0;
+    const size_t bad = (size_t)-1;
+    if (n_q < 0 || n_q > CSA2_MAX_QUERIES || total_len_ub < 0 || max_len_ub < 0) return bad;
     size_t used = 0;
     switch (op) {
         case CSA2_OP_INDEX_FULL: {
-            if (top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 || pool_blocks > CSA2_MAX_SELECT) return 0;
+            if (top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 || pool_blocks > CSA2_MAX_SELECT) return bad;
             const int64_t tiles = full_grid_tiles(n_q, total_len_ub, max_len_ub);
-            if (tiles > kMaxTiles) return 0;
+            if (tiles > kMaxTiles) return bad;
             carve_full(nullptr, n_q, tiles, top_k, pool_blocks, &used);
             return used;
         }
         case CSA2_OP_INDEX_REINDEX:
-            if (top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 1 || pool_blocks > CSA2_MAX_SELECT) return 0;
+            if (top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 1 || pool_blocks > CSA2_MAX_SELECT) return bad;
             carve_reindex(nullptr, n_q, top_k, pool_blocks, &used);
             return used;
         case CSA2_OP_ATTEND:
-            // top_k = selected slots, pool_blocks = window length
-            if (top_k < 0 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 || pool_blocks > CSA2_MAX_WINDOW) return 0;
-            return attend_bytes(n_q, attend_splits(top_k, pool_blocks) > 0 ? attend_splits(top_k, pool_blocks) : 1,
-                                nullptr, nullptr, nullptr);
-        default:
+            // top_k = selected slots, pool_blocks = window length; attention needs no workspace
+            if (top_k < 0 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 || pool_blocks > CSA2_MAX_WINDOW) return bad;
             return 0;
+        default:
+            return bad;
     }
 }
 
-int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
-                    int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
-                    int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
-    (void)shared_kv;
+static int index_full_phase(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const csa2_seqs& seqs,
+                            int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t* idx_out,
+                            int32_t* pool_out, void* ws, size_t ws_bytes, void* stream, int phase) {
     int st = check_seqs(seqs);
     if (st) return st;
     if (n_heads < 1 || n_heads > CSA2_MAX_IDX_HEADS || top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 ||
@@ -195,9 +179,34 @@ int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
     carve_full(nullptr, seqs.n_q, tiles, top_k, pool_blocks, &need);
     if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return CSA2_ERR_WORKSPACE;
     const IndexWs wsp = carve_full(ws, seqs.n_q, tiles, top_k, pool_blocks, &need);
+    const int64_t ftiles = full_grid_tiles(seqs.n_q, seqs.total_len_ub, seqs.max_len_ub, kFilterTile);
     return launch_status(launch_index_full(q_idx, w, k_idx, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
-                                           seqs.cache_rows, n_heads, (int)tiles, top_k, pool_blocks, wsp, idx_out,
-                                           pool_out, static_cast<hipStream_t>(stream)));
+                                           seqs.cache_rows, n_heads, (int)tiles, (int)ftiles, top_k, pool_blocks, wsp,
+                                           idx_out, pool_out, phase, static_cast<hipStream_t>(stream)));
+}
+
+int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
+                    int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
+                    int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
+    (void)shared_kv;
+    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, idx_out, pool_out, ws,
+                            ws_bytes, stream, 3);
+}
+
+int csa2_index_full_scan(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
+                         int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
+                         int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
+    (void)shared_kv;
+    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, idx_out, pool_out, ws,
+                            ws_bytes, stream, 1);
+}
+
+int csa2_index_full_select(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
+                           int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
+                           int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
+    (void)shared_kv;
+    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, idx_out, pool_out, ws,
+                            ws_bytes, stream, 2);
 }
 
 int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
@@ -229,7 +238,7 @@ int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, 
     int st = check_seqs(seqs);
     if (st) return st;
     if (top_k < 0 || top_k > CSA2_MAX_SELECT || window < 0 || window > CSA2_MAX_WINDOW || n_heads < 1 ||
-        n_heads > CSA2_MAX_Q_HEADS || swa_rows < 0)
+        n_heads > CSA2_MAX_Q_HEADS || swa_rows < 0 || swa_rows > INT32_MAX)
         return CSA2_ERR_SHAPE;
     if (window > 0 && (swa_cap < window)) return CSA2_ERR_SHAPE;
     if (top_k + window == 0) return CSA2_ERR_SHAPE;
@@ -241,16 +250,11 @@ int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, 
     if (!aligned16(q) || (codes && !aligned16(codes)) || (swa && !aligned16(swa)) ||
         (scales && (reinterpret_cast<uintptr_t>(scales) & 1u)))
         return CSA2_ERR_SHAPE;
-    const int n_split = attend_splits(top_k, window);
-    const size_t need = attend_bytes(seqs.n_q, n_split, nullptr, nullptr, nullptr);
-    if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return CSA2_ERR_WORKSPACE;
-    uint32_t* ctrl = nullptr;
-    float* part = nullptr;
-    attend_bytes(seqs.n_q, n_split, &ctrl, &part, ws);
+    (void)ws;
+    (void)ws_bytes;
     return launch_status(launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
                                        seqs.cache_rows, idx, top_k, swa, swa_row0, window > 0 ? swa_cap : 1, swa_rows,
-                                       window, n_heads, softmax_scale, out, ctrl, part, n_split,
-                                       static_cast<hipStream_t>(stream)));
+                                       window, n_heads, softmax_scale, out, static_cast<hipStream_t>(stream)));
 }
 
 int csa2_workspace_init(void* ws, size_t bytes, void* stream) {

@@ -53,6 +53,12 @@ __device__ __forceinline__ uint32_t composite_pos(uint64_t c) {
     return 0xffffffffu - (uint32_t)(c & 0xffffffffu);
 }
 
+__device__ __forceinline__ int pow2_ceil(int n) {
+    int p = 1;
+    while (p < n) p <<= 1;
+    return p;
+}
+
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
@@ -106,10 +112,12 @@ struct TileInfo {
     int32_t n;       // clamped visible length
 };
 
+// With want_query < 0: find the query owning tile `tile`.  With want_query >= 0: return the
+// map entry of that query (chunk = 0).
 template <int NT>
-__device__ TileInfo tile_lookup(const int32_t* kv_len, const int64_t* kv_row0, int n_q, int32_t max_len,
-                                int64_t cache_rows, int ch, int grid_tiles, int tile, int* sh_scan,
-                                TileInfo* sh_out) {
+__device__ TileInfo tile_map(const int32_t* kv_len, const int64_t* kv_row0, int n_q, int32_t max_len,
+                             int64_t cache_rows, int ch, int grid_tiles, int tile, int want_query, int* sh_scan,
+                             TileInfo* sh_out) {
     const int extra_cap = grid_tiles - n_q;  // tiles beyond one per query
     if (threadIdx.x == 0) sh_out->q = -1;
     int run = 0;  // raw prefix of extra tiles before this chunk of queries
@@ -128,10 +136,11 @@ __device__ TileInfo tile_lookup(const int32_t* kv_len, const int64_t* kv_row0, i
             int p1 = min(extra_cap, run + ex + x);
             int start = i + p0;
             int nt = 1 + (p1 - p0);
-            if (tile >= start && tile < start + nt) {
+            bool hit = want_query >= 0 ? (i == want_query) : (tile >= start && tile < start + nt);
+            if (hit) {
                 TileInfo ti;
                 ti.q = i;
-                ti.chunk = tile - start;
+                ti.chunk = want_query >= 0 ? 0 : tile - start;
                 ti.start = start;
                 ti.ntiles = nt;
                 ti.n = min(n, nt * ch);
@@ -147,20 +156,28 @@ __device__ TileInfo tile_lookup(const int32_t* kv_len, const int64_t* kv_row0, i
     return r;
 }
 
-// Search a 2048-bin histogram (global, counts of the top key digit) from the top for the
-// bucket holding the k-th largest element.  256 threads.  Result in *out (shared).
-__device__ inline void find_threshold_256(const uint32_t* hist, int k, int* sh_scan, Thresh* out) {
+template <int NT>
+__device__ __forceinline__ TileInfo tile_lookup(const int32_t* kv_len, const int64_t* kv_row0, int n_q,
+                                                int32_t max_len, int64_t cache_rows, int ch, int grid_tiles, int tile,
+                                                int* sh_scan, TileInfo* sh_out) {
+    return tile_map<NT>(kv_len, kv_row0, n_q, max_len, cache_rows, ch, grid_tiles, tile, -1, sh_scan, sh_out);
+}
+
+// Search a 2048-bin histogram (counts of the top key digit) from the top for the bucket
+// holding the k-th largest element.  NT threads (a divisor of 2048).  Result in *out (shared).
+template <int NT>
+__device__ inline void find_threshold(const uint32_t* hist, int k, int* sh_scan, Thresh* out) {
+    constexpr int BPT = kHistBins / NT;  // bins per thread, highest bins to thread 0
     const int t = threadIdx.x;
-    // thread t owns bins [2048 - 8(t+1), 2048 - 8t): thread 0 holds the highest bins
-    uint32_t h[8];
+    uint32_t h[BPT];
     int local = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        h[j] = hist[kHistBins - 1 - (8 * t + j)];
+    for (int j = 0; j < BPT; ++j) {
+        h[j] = hist[kHistBins - 1 - (BPT * t + j)];
         local += (int)h[j];
     }
     int total;
-    int above = block_exclusive_scan<256>(local, sh_scan, total);
+    int above = block_exclusive_scan<NT>(local, sh_scan, total);
     if (t == 0) {
         out->digit = -1;
         out->above = total;
@@ -171,10 +188,10 @@ __device__ inline void find_threshold_256(const uint32_t* hist, int k, int* sh_s
     if (total > k) {
         int a = above;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < BPT; ++j) {
             int c = (int)h[j];
             if (a < k && a + c >= k) {
-                out->digit = kHistBins - 1 - (8 * t + j);
+                out->digit = kHistBins - 1 - (BPT * t + j);
                 out->above = a;
                 out->in_bucket = c;
             }
@@ -182,6 +199,157 @@ __device__ inline void find_threshold_256(const uint32_t* hist, int k, int* sh_s
         }
     }
     __syncthreads();
+}
+
+__device__ inline void find_threshold_256(const uint32_t* hist, int k, int* sh_scan, Thresh* out) {
+    find_threshold<256>(hist, k, sh_scan, out);
+}
+
+// Among m <= kSortCap candidate composites in LDS (all sharing the 11-bit key prefix d1),
+// find the need-th largest (1 <= need <= m) with radix passes over LDS.  NT threads.
+// Returns the threshold: exactly `need` candidates are >= it.
+struct RadixShared {
+    uint32_t hist[kHistBins];
+    int scan[16];
+    int digit, above, inb;
+};
+
+template <int NT>
+__device__ uint64_t lds_radix_threshold(const uint64_t* c, int m, int need, int d1, RadixShared& R) {
+    constexpr int BPT = kHistBins / NT;
+    const int t = threadIdx.x;
+    uint64_t prefix = (uint64_t)(uint32_t)d1;
+    int pbits = kHistBits;
+    int matching = m;
+    while (pbits < 64 && matching > need) {
+        const int w = (64 - pbits) >= kHistBits ? kHistBits : (64 - pbits);
+        const int shift = 64 - pbits - w;
+        for (int b = t; b < kHistBins; b += NT) R.hist[b] = 0u;
+        __syncthreads();
+        for (int e = t; e < m; e += NT) {
+            const uint64_t v = c[e];
+            if ((v >> (64 - pbits)) == prefix) atomicAdd(&R.hist[(v >> shift) & ((1u << w) - 1)], 1u);
+        }
+        __syncthreads();
+        const int nb = 1 << w;
+        uint32_t h[BPT];
+        int local = 0;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            const int b = nb - 1 - (BPT * t + j);
+            h[j] = b >= 0 ? R.hist[b] : 0u;
+            local += (int)h[j];
+        }
+        int tot;
+        int a = block_exclusive_scan<NT>(local, R.scan, tot);
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            const int cnt = (int)h[j];
+            if (a < need && a + cnt >= need) {
+                R.digit = nb - 1 - (BPT * t + j);
+                R.above = a;
+                R.inb = cnt;
+            }
+            a += cnt;
+        }
+        __syncthreads();
+        prefix = (prefix << w) | (uint64_t)R.digit;
+        pbits += w;
+        need -= R.above;
+        matching = R.inb;
+        __syncthreads();
+    }
+    // every composite with this prefix (and `matching == need` of them remain) is selected
+    return pbits >= 64 ? prefix : (prefix << (64 - pbits));
+}
+
+// Ascending bitonic sort of n <= E*NT 32-bit values held E per thread (element e = E*t + i), padded
+// with 0xffffffff.  Partners within a thread or a wave are exchanged in registers and with
+// cross-lane shuffles; only partners in another wave go through LDS (xchg, E*NT words) with
+// workgroup barriers.
+template <int NT, int E>
+__device__ void regs_bitonic_asc(uint32_t (&x)[E], int n, uint32_t* xchg) {
+    const int t = threadIdx.x;
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride < E) {
+#pragma unroll
+                for (int i = 0; i < E; ++i) {
+                    const int j = i ^ stride;
+                    if (j > i) {
+                        const int e = E * t + i;
+                        const bool asc = (e & size) == 0;
+                        const uint32_t a = x[i], b = x[j];
+                        x[i] = asc ? min(a, b) : max(a, b);
+                        x[j] = asc ? max(a, b) : min(a, b);
+                    }
+                }
+            } else if (stride / E < kWave) {
+                const int lx = stride / E;
+                const bool lower = (t & lx) == 0;
+#pragma unroll
+                for (int i = 0; i < E; ++i) {
+                    const uint32_t y = (uint32_t)__shfl_xor((int)x[i], lx, kWave);
+                    const int e = E * t + i;
+                    const bool asc = (e & size) == 0;
+                    x[i] = (lower == asc) ? min(x[i], y) : max(x[i], y);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < E; ++i) xchg[E * t + i] = x[i];
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < E; ++i) {
+                    const int e = E * t + i;
+                    const uint32_t y = xchg[e ^ stride];
+                    const bool asc = (e & size) == 0;
+                    const bool lower = (e & stride) == 0;
+                    x[i] = (lower == asc) ? min(x[i], y) : max(x[i], y);
+                }
+                __syncthreads();
+            }
+        }
+    }
+}
+
+// Write the `total` (<= E*NT) distinct values of sel[] (LDS) to out[0..k) in ascending order,
+// -1 padded.  sel[] is also used as the exchange buffer of the sort.
+template <int NT, int E>
+__device__ void sort_write_ascending(uint32_t* sel, int total, int k, int32_t* out) {
+    const int t = threadIdx.x;
+    uint32_t x[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const int e = E * t + i;
+        x[i] = e < total ? sel[e] : 0xffffffffu;
+    }
+    __syncthreads();
+    regs_bitonic_asc<NT, E>(x, pow2_ceil(total > 1 ? total : 2), sel);
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const int e = E * t + i;
+        if (e < k) out[e] = e < total ? (int32_t)x[i] : -1;
+    }
+    for (int j = E * NT + t; j < k; j += NT) out[j] = -1;
+}
+
+// Write the `total` distinct positions in sel[] (LDS) to out[0..k) in ascending order, -1 padded:
+// each position's slot is the number of smaller positions (no sort network, no barriers).
+template <int NT>
+__device__ void write_ascending(const uint32_t* sel, int total, int k, int32_t* out) {
+    const int t = threadIdx.x;
+    for (int j = t; j < total; j += NT) {
+        const uint32_t p = sel[j];
+        int slot = 0;
+        int i = 0;
+        for (; i + 4 <= total; i += 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(sel + i);
+            slot += (v.x < p) + (v.y < p) + (v.z < p) + (v.w < p);
+        }
+        for (; i < total; ++i) slot += sel[i] < p;
+        out[slot] = (int32_t)p;
+    }
+    for (int j = total + t; j < k; j += NT) out[j] = -1;
 }
 
 // Bitonic sort of n (power of two, <= kSortCap) 64-bit values in LDS, descending.
@@ -224,125 +392,104 @@ __device__ inline void bitonic_asc_u32(uint32_t* a, int n) {
     }
 }
 
-__device__ __forceinline__ int pow2_ceil(int n) {
-    int p = 1;
-    while (p < n) p <<= 1;
-    return p;
-}
 
 // LDS working set of one workgroup-level selection.
 struct SelectShared {
     uint64_t buf[kSortCap];     // candidate composites, then reused for the output positions
     uint32_t hist[kHistBins];
-    int scan[8];
+    int scan[16];
     int cnt;
     int digit;
     int above;
     int inb;
 };
 
-// Select, with one 256-thread workgroup, the `need` largest composites among `count`
-// candidates whose keys all start with the 11-bit digit `d1`, then write the union of
-// those positions and `n_sure` positions already chosen (sure[]) to out[0..k) in
-// ascending order, -1 padded.
-//   elem(e) -> (key, pos) of candidate e (e in [0, count)).
-template <class Elem>
-__device__ void wg_select_write(const Elem& elem, int count, int need, int d1, const int32_t* sure, int n_sure,
-                                int k, int32_t* out, SelectShared& S) {
+// The need-th largest of `count` candidate composites (src(e), e in [0, count)) whose keys all
+// start with the 11-bit digit `d1`, for candidate sets of any size: 11-bit radix passes over
+// the (global) list narrow the set until it fits in LDS, where it is sorted.  NT threads.
+// Returns the threshold composite (exactly `need` candidates are >= it), ~0 if need <= 0.
+template <int NT, class Src>
+__device__ uint64_t wg_threshold(const Src& src, int count, int need, int d1, SelectShared& S) {
     const int t = threadIdx.x;
-    constexpr int NT = 256;
-    uint64_t thr = ~0ull;  // composites >= thr are selected
-    if (need > 0 && count > 0) {
-        uint64_t prefix = (uint64_t)(uint32_t)d1;
-        int pbits = kHistBits;
-        int matching = count;
-        // radix passes until the matching set fits in LDS
-        while (matching > kSortCap && pbits < 64) {
-            int w = (64 - pbits) >= kHistBits ? kHistBits : (64 - pbits);
-            int shift = 64 - pbits - w;
-            for (int b = t; b < kHistBins; b += NT) S.hist[b] = 0;
-            __syncthreads();
-            for (int e = t; e < count; e += NT) {
-                uint32_t key, pos;
-                elem(e, key, pos);
-                uint64_t c = composite(key, pos);
-                if ((c >> (64 - pbits)) == prefix) atomicAdd(&S.hist[(c >> shift) & ((1u << w) - 1)], 1u);
-            }
-            __syncthreads();
-            // top-down search over the (up to) 2048 bins; thread t owns 8 bins
-            int nb = 1 << w;
-            uint32_t h[8];
-            int local = 0;
+    constexpr int BPT = kHistBins / NT;
+    uint64_t thr = ~0ull;
+    if (need <= 0 || count <= 0) return thr;
+    uint64_t prefix = (uint64_t)(uint32_t)d1;
+    int pbits = kHistBits;
+    int matching = count;
+    while (matching > kSortCap && pbits < 64) {
+        const int w = (64 - pbits) >= kHistBits ? kHistBits : (64 - pbits);
+        const int shift = 64 - pbits - w;
+        for (int b = t; b < kHistBins; b += NT) S.hist[b] = 0;
+        __syncthreads();
+        for (int e0 = 0; e0 < count; e0 += 4 * NT) {
+            uint64_t c[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                int b = nb - 1 - (8 * t + j);
-                h[j] = b >= 0 ? S.hist[b] : 0u;
-                local += (int)h[j];
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * NT + t;
+                c[u] = e < count ? src(e) : 0ull;
             }
-            int tot;
-            int a = block_exclusive_scan<NT>(local, S.scan, tot);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                int c = (int)h[j];
-                if (a < need && a + c >= need) {
-                    S.digit = nb - 1 - (8 * t + j);
-                    S.above = a;
-                    S.inb = c;
-                }
-                a += c;
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * NT + t;
+                if (e < count && (c[u] >> (64 - pbits)) == prefix)
+                    atomicAdd(&S.hist[(c[u] >> shift) & ((1u << w) - 1)], 1u);
             }
-            __syncthreads();
-            prefix = (prefix << w) | (uint64_t)S.digit;
-            pbits += w;
-            need -= S.above;
-            matching = S.inb;
-            __syncthreads();
         }
-        if (pbits >= 64) {
-            thr = prefix;  // fully resolved (composites are unique)
-        } else {
-            // gather the matching composites and sort them
-            if (t == 0) S.cnt = 0;
-            __syncthreads();
-            for (int e = t; e < count; e += NT) {
-                uint32_t key, pos;
-                elem(e, key, pos);
-                uint64_t c = composite(key, pos);
-                if ((c >> (64 - pbits)) == prefix) {
-                    int slot = atomicAdd(&S.cnt, 1);
-                    S.buf[slot] = c;
-                }
+        __syncthreads();
+        const int nb = 1 << w;
+        uint32_t h[BPT];
+        int local = 0;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            const int b = nb - 1 - (BPT * t + j);
+            h[j] = b >= 0 ? S.hist[b] : 0u;
+            local += (int)h[j];
+        }
+        int tot;
+        int a = block_exclusive_scan<NT>(local, S.scan, tot);
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            const int cnt = (int)h[j];
+            if (a < need && a + cnt >= need) {
+                S.digit = nb - 1 - (BPT * t + j);
+                S.above = a;
+                S.inb = cnt;
             }
-            __syncthreads();
-            int m = S.cnt;
-            int p2 = pow2_ceil(m);
-            for (int j = m + t; j < p2; j += NT) S.buf[j] = 0ull;
-            __syncthreads();
-            bitonic_desc_u64<NT>(S.buf, p2);
-            thr = S.buf[need - 1];
-            __syncthreads();
+            a += cnt;
         }
+        __syncthreads();
+        prefix = (prefix << w) | (uint64_t)S.digit;
+        pbits += w;
+        need -= S.above;
+        matching = S.inb;
+        __syncthreads();
     }
-    // output = sure positions + candidates with composite >= thr, sorted ascending
-    uint32_t* o = reinterpret_cast<uint32_t*>(S.buf);
+    if (pbits >= 64) return prefix;  // fully resolved (composites are unique)
     if (t == 0) S.cnt = 0;
     __syncthreads();
-    for (int j = t; j < n_sure; j += NT) o[atomicAdd(&S.cnt, 1)] = (uint32_t)sure[j];
-    if (thr != ~0ull) {
-        for (int e = t; e < count; e += NT) {
-            uint32_t key, pos;
-            elem(e, key, pos);
-            if (composite(key, pos) >= thr) o[atomicAdd(&S.cnt, 1)] = pos;
+    for (int e0 = 0; e0 < count; e0 += 4 * NT) {
+        uint64_t c[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * NT + t;
+            c[u] = e < count ? src(e) : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * NT + t;
+            if (e < count && (c[u] >> (64 - pbits)) == prefix) S.buf[atomicAdd(&S.cnt, 1)] = c[u];
         }
     }
     __syncthreads();
-    int m = S.cnt;
-    int p2 = pow2_ceil(m > 1 ? m : 1);
-    for (int j = m + t; j < p2; j += NT) o[j] = 0xffffffffu;
+    const int m = S.cnt;
+    const int p2 = pow2_ceil(m);
+    for (int j = m + t; j < p2; j += NT) S.buf[j] = 0ull;
     __syncthreads();
-    bitonic_asc_u32<NT>(o, p2);
-    for (int j = t; j < k; j += NT) out[j] = j < m ? (int32_t)o[j] : -1;
+    bitonic_desc_u64<NT>(S.buf, p2);
+    thr = S.buf[need - 1];
     __syncthreads();
+    return thr;
 }
 
 }  // namespace csa2

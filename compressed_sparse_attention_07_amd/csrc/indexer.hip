@@ -22,8 +22,14 @@
 //   * the row's key (order-preserving u32 of the score) is stored; the 8-row block
 //     maximum and the top-11-bit histogram of both are fused in (LDS histograms,
 //     flushed with integer atomics).
-// The last workgroup of a query (ticket counter) turns the histograms into the
-// threshold bucket, so the filter pass only reads 4 B per position.
+// Kernels hand data to each other only across kernel boundaries (no device-scope fences
+// inside a kernel: on a multi-XCD part such a fence writes back the L2).
+//   Full:    scan (keys, block-max keys, histograms)
+//            -> filter (each workgroup derives the threshold buckets from the histograms and
+//               compacts its share of the keys: above-threshold positions to a "sure" list,
+//               threshold-bucket candidates to a candidate list, one global atomic per list)
+//            -> select (one workgroup per query and list: exact order inside the bucket).
+//   Reindex: score (pool positions) -> select (one workgroup per query).
 #include "csa2_device.hpp"
 
 namespace csa2 {
@@ -32,6 +38,7 @@ constexpr int kScoreNT = 256;
 constexpr int kFullTile = 2048;                 // positions per Full-scan workgroup
 constexpr int kFullTileBlocks = kFullTile / 8;  // 256 blocks
 constexpr int kReindexTile = 512;               // pool positions (64 blocks) per Reindex workgroup
+constexpr int kFilterTile = 16384;              // positions per filter workgroup (8 scan tiles)
 
 struct IndexWs {
     uint32_t* ctrl;      // [n_q][kCtlSlots]          self-cleaning counters
@@ -41,8 +48,8 @@ struct IndexWs {
     uint32_t* bkeys;     // [grid_tiles * 256]        per-block max keys
     int32_t* sure_idx;   // [n_q][top_k]
     int32_t* sure_pool;  // [n_q][pool_blocks]
-    int32_t* cand_idx;   // [grid_tiles * 2048]
-    int32_t* cand_pool;  // [grid_tiles * 256]
+    uint64_t* cand_idx;  // [grid_tiles * 2048]       threshold-bucket composites
+    uint64_t* cand_pool; // [grid_tiles * 256]
 };
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -112,35 +119,19 @@ __device__ __forceinline__ uint32_t max_over_8_quads(uint32_t k) {
     return k;
 }
 
-// Append `val` at the next free slot of list[] (counter *ctr) for every lane with pred set.
-__device__ __forceinline__ void wave_append(bool pred, int32_t val, int32_t* list, uint32_t* ctr) {
-    const uint64_t m = __ballot(pred);
-    if (m == 0) return;
-    const int lane = __lane_id();
-    const int leader = __ffsll((unsigned long long)m) - 1;
-    uint32_t base = 0;
-    if (lane == leader) base = atomicAdd(ctr, (uint32_t)__popcll(m));
-    base = (uint32_t)__shfl((int)base, leader, kWave);
-    if (pred) {
-        const uint64_t below = m & ((1ull << lane) - 1ull);
-        list[base + __popcll(below)] = val;
-    }
-}
 
 // ----------------------------------------------------------------------------------------
-// Full mode, pass 1: scores -> keys, block-max keys, histograms; last workgroup -> thresholds
+// Full mode, kernel 1: scores -> keys, block-max keys, first-digit histograms
 // ----------------------------------------------------------------------------------------
 template <int HI>
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len, int n_q, int32_t max_len,
-    int64_t cache_rows, int n_heads, int grid_tiles, int top_k, int pool_blocks, IndexWs ws) {
+    int64_t cache_rows, int n_heads, int grid_tiles, int pool_blocks, IndexWs ws) {
     __shared__ uint32_t sh_hist[kHistBins];
     __shared__ uint32_t sh_bhist[kHistBins];
     __shared__ int sh_scan[8];
     __shared__ TileInfo sh_ti;
-    __shared__ Thresh sh_th;
-    __shared__ int sh_last;
 
     const TileInfo ti =
         tile_lookup<kScoreNT>(kv_len, kv_row0, n_q, max_len, cache_rows, kFullTile, grid_tiles, blockIdx.x, sh_scan,
@@ -164,8 +155,7 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     const int n = ti.n;
     const int64_t row0 = kv_row0[i];
     const int64_t key_base = (int64_t)ti.start * kFullTile;
-    const int p_tile = ti.chunk * kFullTile;
-    const int p_wave = p_tile + wid * (kFullTile / 4);
+    const int p_wave = ti.chunk * kFullTile + wid * (kFullTile / 4);
 
     for (int b = 0; b < kFullTile / 4; b += 64) {
         const int base = p_wave + b;
@@ -173,8 +163,8 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
         uint4 A[4], B[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            int p = base + 16 * u + (lane >> 2);
-            int pc = p < n ? p : n - 1;
+            const int p = base + 16 * u + (lane >> 2);
+            const int pc = p < n ? p : n - 1;
             const uint16_t* row = k_idx + (row0 + pc) * 64;
             A[u] = *reinterpret_cast<const uint4*>(row + 8 * j);
             B[u] = *reinterpret_cast<const uint4*>(row + 32 + 8 * j);
@@ -207,122 +197,191 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
             if (hb) atomicAdd(&gh[kHistBins + b], hb);
         }
     }
-    __threadfence();
-    __syncthreads();
-    if (t == 0) sh_last = (atomicAdd(&ws.ctrl[(int64_t)i * kCtlSlots + kCtlScoreDone], 1u) == (uint32_t)(ti.ntiles - 1));
-    __syncthreads();
-    if (!sh_last) return;
-    __threadfence();
+}
 
-    find_threshold_256(gh, top_k, sh_scan, &sh_th);
-    if (t == 0) ws.meta[(int64_t)i * 2] = sh_th;
-    __syncthreads();
-    if (want_pool) {
-        find_threshold_256(gh + kHistBins, pool_blocks, sh_scan, &sh_th);
-        if (t == 0) ws.meta[(int64_t)i * 2 + 1] = sh_th;
+// Compact one workgroup's share of a key array: elements whose first digit is above the threshold
+// bucket go to sure[] (positions), elements in the bucket to cand[] (composites).  Two passes over
+// the keys (count, then write) so each list costs one global atomic per workgroup.
+template <int PER>
+__device__ void wg_compact(const uint32_t* keys, int e_begin, int e_end, const Thresh& th, int32_t* sure,
+                           uint32_t* sure_ctr, uint64_t* cand, uint32_t* cand_ctr, int* sh_scan, int* sh_base) {
+    const int t = threadIdx.x;
+    uint32_t kv[PER];
+    int ns = 0, nc = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int e = e_begin + u * kScoreNT + t;
+        kv[u] = e < e_end ? keys[e] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int dg = (int)(kv[u] >> 21);
+        ns += (kv[u] != 0u && dg > th.digit);
+        nc += (kv[u] != 0u && dg == th.digit);
+    }
+    int tot_s, tot_c;
+    int off_s = block_exclusive_scan<kScoreNT>(ns, sh_scan, tot_s);
+    int off_c = block_exclusive_scan<kScoreNT>(nc, sh_scan, tot_c);
+    if (t == 0) {
+        sh_base[0] = tot_s ? (int)atomicAdd(sure_ctr, (uint32_t)tot_s) : 0;
+        sh_base[1] = tot_c ? (int)atomicAdd(cand_ctr, (uint32_t)tot_c) : 0;
     }
     __syncthreads();
-    for (int b = t; b < 2 * kHistBins; b += kScoreNT) gh[b] = 0u;
-    if (t == 0) ws.ctrl[(int64_t)i * kCtlSlots + kCtlScoreDone] = 0u;
+    off_s += sh_base[0];
+    off_c += sh_base[1];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int e = e_begin + u * kScoreNT + t;
+        const int dg = (int)(kv[u] >> 21);
+        if (kv[u] != 0u && dg > th.digit) sure[off_s++] = e;
+        if (kv[u] != 0u && dg == th.digit) cand[off_c++] = composite(kv[u], (uint32_t)e);
+    }
+    __syncthreads();
 }
 
 // ----------------------------------------------------------------------------------------
-// Full mode, pass 2: compact the threshold bucket, last workgroup selects and writes
+// Full mode, kernel 2: thresholds from the histograms, compaction of the keys
 // ----------------------------------------------------------------------------------------
-struct FullElem {
-    const int32_t* cand;
-    const uint32_t* keys;
-    __device__ __forceinline__ void operator()(int e, uint32_t& key, uint32_t& pos) const {
-        pos = (uint32_t)cand[e];
-        key = keys[pos];
-    }
-};
-
 __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __restrict__ kv_row0,
                                                               const int32_t* __restrict__ kv_len, int n_q,
                                                               int32_t max_len, int64_t cache_rows, int grid_tiles,
-                                                              int top_k, int pool_blocks, IndexWs ws,
-                                                              int32_t* __restrict__ idx_out,
-                                                              int32_t* __restrict__ pool_out) {
-    __shared__ SelectShared S;
+                                                              int grid_ftiles, int top_k, int pool_blocks, IndexWs ws) {
+    __shared__ int sh_scan[8];
+    __shared__ int sh_base[2];
     __shared__ TileInfo sh_ti;
-    __shared__ int sh_last;
+    __shared__ Thresh sh_th;
 
-    const TileInfo ti = tile_lookup<kScoreNT>(kv_len, kv_row0, n_q, max_len, cache_rows, kFullTile, grid_tiles,
-                                              blockIdx.x, S.scan, &sh_ti);
-    if (ti.q < 0) return;
-    const int i = ti.q;
-    const int t = threadIdx.x;
-    const int n = ti.n;
-    const int64_t key_base = (int64_t)ti.start * kFullTile;
-    const int p_tile = ti.chunk * kFullTile;
+    const TileInfo tf = tile_lookup<kScoreNT>(kv_len, kv_row0, n_q, max_len, cache_rows, kFilterTile, grid_ftiles,
+                                              blockIdx.x, sh_scan, &sh_ti);
+    if (tf.q < 0) return;
+    const int i = tf.q;
+    const TileInfo ts = tile_map<kScoreNT>(kv_len, kv_row0, n_q, max_len, cache_rows, kFullTile, grid_tiles, 0, i,
+                                           sh_scan, &sh_ti);
+    const int n = min(tf.n, ts.n);
+    const int64_t key_base = (int64_t)ts.start * kFullTile;
     uint32_t* ctrl = ws.ctrl + (int64_t)i * kCtlSlots;
-    const Thresh th = ws.meta[(int64_t)i * 2];
-    const bool want_pool = pool_blocks > 0;
+    const uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
 
-    for (int r = t; r < kFullTile; r += kScoreNT) {
-        const int p = p_tile + r;
-        const uint32_t key = p < n ? ws.keys[key_base + p] : 0u;
-        const int dg = (int)(key >> 21);
-        wave_append(p < n && dg > th.digit, p, ws.sure_idx + (int64_t)i * top_k, ctrl + kCtlSureIdx);
-        wave_append(p < n && dg == th.digit, p, ws.cand_idx + key_base, ctrl + kCtlCandIdx);
-    }
-    if (want_pool) {
-        const Thresh tp = ws.meta[(int64_t)i * 2 + 1];
+    find_threshold_256(gh, top_k, sh_scan, &sh_th);
+    const Thresh th = sh_th;
+    __syncthreads();
+    const int p0 = tf.chunk * kFilterTile;
+    wg_compact<kFilterTile / kScoreNT>(ws.keys + key_base, p0, min(n, p0 + kFilterTile), th,
+                                       ws.sure_idx + (int64_t)i * top_k, ctrl + kCtlSureIdx, ws.cand_idx + key_base,
+                                       ctrl + kCtlCandIdx, sh_scan, sh_base);
+    if (pool_blocks > 0) {
+        find_threshold_256(gh + kHistBins, pool_blocks, sh_scan, &sh_th);
+        const Thresh tp = sh_th;
+        __syncthreads();
         const int nb = (n + 7) >> 3;
-        const int b_tile = ti.chunk * kFullTileBlocks;
-        for (int r = t; r < kFullTileBlocks; r += kScoreNT) {
-            const int bl = b_tile + r;
-            const uint32_t key = bl < nb ? ws.bkeys[key_base / 8 + bl] : 0u;
-            const int dg = (int)(key >> 21);
-            wave_append(bl < nb && dg > tp.digit, bl, ws.sure_pool + (int64_t)i * pool_blocks, ctrl + kCtlSurePool);
-            wave_append(bl < nb && dg == tp.digit, bl, ws.cand_pool + key_base / 8, ctrl + kCtlCandPool);
-        }
+        const int b0 = tf.chunk * (kFilterTile / 8);
+        wg_compact<kFilterTile / 8 / kScoreNT>(ws.bkeys + key_base / 8, b0, min(nb, b0 + kFilterTile / 8), tp,
+                                               ws.sure_pool + (int64_t)i * pool_blocks, ctrl + kCtlSurePool,
+                                               ws.cand_pool + key_base / 8, ctrl + kCtlCandPool, sh_scan, sh_base);
     }
-    __threadfence();
-    __syncthreads();
-    if (t == 0) sh_last = (atomicAdd(ctrl + kCtlFilterDone, 1u) == (uint32_t)(ti.ntiles - 1));
-    __syncthreads();
-    if (!sh_last) return;
-    __threadfence();
+}
 
-    {
-        FullElem el{ws.cand_idx + key_base, ws.keys + key_base};
-        wg_select_write(el, th.in_bucket, top_k - th.above, th.digit, ws.sure_idx + (int64_t)i * top_k,
-                        min(th.above, top_k), top_k, idx_out + (int64_t)i * top_k, S);
+struct CompositeList {
+    const uint64_t* c;
+    __device__ __forceinline__ uint64_t operator()(int e) const { return c[e]; }
+};
+
+constexpr int kSelNT = 1024;  // threads of the per-query selection workgroups
+
+struct SmallSel {
+    uint64_t cand[kSortCap];
+    uint32_t sel[kMaxSelect + 4];
+    RadixShared R;
+    int cnt;
+};
+union SelLds {
+    SelectShared big;
+    SmallSel small;
+};
+
+// Ascending output of up to kMaxSelect selected positions (sel[] in LDS, >= kMaxSelect words).
+__device__ __forceinline__ void sort_out(uint32_t* sel, int total, int k, int32_t* out) {
+    if (total <= kSelNT) {
+        sort_write_ascending<kSelNT, 1>(sel, total, k, out);
+    } else if (total <= 2 * kSelNT) {
+        sort_write_ascending<kSelNT, 2>(sel, total, k, out);
+    } else {
+        sort_write_ascending<kSelNT, 4>(sel, total, k, out);
     }
-    if (want_pool) {
-        const Thresh tp = ws.meta[(int64_t)i * 2 + 1];
-        FullElem el{ws.cand_pool + key_base / 8, ws.bkeys + key_base / 8};
-        wg_select_write(el, tp.in_bucket, pool_blocks - tp.above, tp.digit, ws.sure_pool + (int64_t)i * pool_blocks,
-                        min(tp.above, pool_blocks), pool_blocks, pool_out + (int64_t)i * pool_blocks, S);
-    }
-    if (t < kCtlSlots && t != kCtlScoreDone && t != kCtlAttendDone) ctrl[t] = 0u;
 }
 
 // ----------------------------------------------------------------------------------------
-// Reindex: score the pool's positions with this layer's query, select Top-K among them
+// Full mode, kernel 3: exact selection inside the threshold bucket; one workgroup per
+// (query, list).  The bucket's candidates normally fit in LDS: radix passes there find the
+// threshold, and each selected position's output slot is its rank among the selected.
+// Leaves the histograms and counters of the query zero for the next call.
 // ----------------------------------------------------------------------------------------
-struct ReindexElem {
-    const int32_t* cand;  // candidate element ids e (slot * 8 + r)
-    const uint32_t* keys;
-    const int32_t* pool;
-    __device__ __forceinline__ void operator()(int e, uint32_t& key, uint32_t& pos) const {
-        const int c = cand[e];
-        key = keys[c];
-        pos = (uint32_t)(pool[c >> 3] * 8 + (c & 7));
+__global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __restrict__ kv_row0,
+                                                            const int32_t* __restrict__ kv_len, int n_q,
+                                                            int32_t max_len, int64_t cache_rows, int grid_tiles,
+                                                            int top_k, int pool_blocks, IndexWs ws,
+                                                            int32_t* __restrict__ idx_out,
+                                                            int32_t* __restrict__ pool_out) {
+    __shared__ SelLds U;
+    __shared__ TileInfo sh_ti;
+    __shared__ Thresh sh_th;
+    const int i = blockIdx.x;
+    const int which = blockIdx.y;  // 0: positions, 1: pool blocks
+    const int t = threadIdx.x;
+    const TileInfo ts = tile_map<kSelNT>(kv_len, kv_row0, n_q, max_len, cache_rows, kFullTile, grid_tiles, 0, i,
+                                         U.small.R.scan, &sh_ti);
+    const int64_t key_base = (int64_t)ts.start * kFullTile;
+    uint32_t* ctrl = ws.ctrl + (int64_t)i * kCtlSlots;
+    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins + which * kHistBins;
+    const int k = which ? pool_blocks : top_k;
+    const uint64_t* cand = which ? ws.cand_pool + key_base / 8 : ws.cand_idx + key_base;
+    const int32_t* sure = which ? ws.sure_pool + (int64_t)i * pool_blocks : ws.sure_idx + (int64_t)i * top_k;
+    int32_t* out = which ? pool_out + (int64_t)i * pool_blocks : idx_out + (int64_t)i * top_k;
+    find_threshold<kSelNT>(gh, k, U.small.R.scan, &sh_th);
+    const Thresh th = sh_th;
+    const int need = k - th.above;
+    const int n_sure = min(th.above, k);
+    if (th.in_bucket <= kSortCap) {
+        SmallSel& W = U.small;
+        for (int e = t; e < th.in_bucket; e += kSelNT) W.cand[e] = cand[e];
+        for (int j = t; j < n_sure; j += kSelNT) W.sel[j] = (uint32_t)sure[j];
+        if (t == 0) W.cnt = n_sure;
+        __syncthreads();
+        const uint64_t thr = (need > 0 && th.in_bucket > 0)
+                                 ? lds_radix_threshold<kSelNT>(W.cand, th.in_bucket, need, th.digit, W.R)
+                                 : ~0ull;
+        for (int e = t; e < th.in_bucket; e += kSelNT)
+            if (W.cand[e] >= thr) W.sel[atomicAdd(&W.cnt, 1)] = composite_pos(W.cand[e]);
+        __syncthreads();
+        sort_out(W.sel, W.cnt, k, out);
+    } else {
+        SelectShared& S = U.big;
+        const uint64_t thr = wg_threshold<kSelNT>(CompositeList{cand}, th.in_bucket, need, th.digit, S);
+        uint32_t* sel = reinterpret_cast<uint32_t*>(S.buf);
+        if (t == 0) S.cnt = 0;
+        __syncthreads();
+        for (int j = t; j < n_sure; j += kSelNT) sel[atomicAdd(&S.cnt, 1)] = (uint32_t)sure[j];
+        for (int e = t; e < th.in_bucket; e += kSelNT)
+            if (cand[e] >= thr) sel[atomicAdd(&S.cnt, 1)] = composite_pos(cand[e]);
+        __syncthreads();
+        sort_out(sel, S.cnt, k, out);
     }
-};
+    for (int b = t; b < kHistBins; b += kSelNT) gh[b] = 0u;
+    if (t == 0) {
+        ctrl[which ? kCtlSurePool : kCtlSureIdx] = 0u;
+        ctrl[which ? kCtlCandPool : kCtlCandIdx] = 0u;
+    }
+}
 
+// ----------------------------------------------------------------------------------------
+// Reindex, kernel 1: score the pool's positions with this layer's query
+// ----------------------------------------------------------------------------------------
 template <int HI>
-__global__ __launch_bounds__(kScoreNT) void k_idx_reindex(
+__global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len, int32_t max_len, int64_t cache_rows,
-    int n_heads, const int32_t* __restrict__ pool, int pool_blocks, int top_k, IndexWs ws,
-    int32_t* __restrict__ idx_out) {
-    __shared__ SelectShared S;
-    __shared__ Thresh sh_th;
-    __shared__ int sh_last;
+    int n_heads, const int32_t* __restrict__ pool, int pool_blocks, IndexWs ws) {
+    __shared__ uint32_t sh_hist[kHistBins];
 
     const int i = blockIdx.y;
     const int t = threadIdx.x;
@@ -334,10 +393,8 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex(
     const int n_elem = pool_blocks * 8;
     const int32_t* qpool = pool + (int64_t)i * pool_blocks;
     uint32_t* keys = ws.keys + (int64_t)i * n_elem;
-    uint32_t* ctrl = ws.ctrl + (int64_t)i * kCtlSlots;
-    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
 
-    for (int b = t; b < kHistBins; b += kScoreNT) S.hist[b] = 0u;
+    for (int b = t; b < kHistBins; b += kScoreNT) sh_hist[b] = 0u;
     QSlice<HI> qs;
     load_qslice<HI>(qs, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, j);
     __syncthreads();
@@ -346,7 +403,6 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex(
     for (int b = 0; b < kReindexTile / 4; b += 64) {
         uint4 A[4], B[4];
         bool valid[4];
-        int e_of[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int e = e_wave + b + 16 * u + (lane >> 2);
@@ -354,7 +410,6 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex(
             const int blk = slot < pool_blocks ? qpool[slot] : -1;
             const int64_t p = (int64_t)blk * 8 + (e & 7);
             valid[u] = blk >= 0 && p < n;
-            e_of[u] = e;
             if (valid[u]) {
                 const uint16_t* row = k_idx + (row0 + p) * 64;
                 A[u] = *reinterpret_cast<const uint4*>(row + 8 * j);
@@ -366,68 +421,163 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex(
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+            const int e = e_wave + b + 16 * u + (lane >> 2);
             const float s = row_score<HI>(A[u], B[u], qs);
             const uint32_t key = valid[u] ? score_key(s) : 0u;
-            if (j == 0 && e_of[u] < n_elem) {
-                keys[e_of[u]] = key;
-                if (key) atomicAdd(&S.hist[key >> 21], 1u);
+            if (j == 0 && e < n_elem) {
+                keys[e] = key;
+                if (key) atomicAdd(&sh_hist[key >> 21], 1u);
             }
         }
     }
     __syncthreads();
+    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
     for (int b = t; b < kHistBins; b += kScoreNT) {
-        const uint32_t h = S.hist[b];
+        const uint32_t h = sh_hist[b];
         if (h) atomicAdd(&gh[b], h);
     }
-    __threadfence();
-    __syncthreads();
-    if (t == 0) sh_last = (atomicAdd(ctrl + kCtlScoreDone, 1u) == (uint32_t)(gridDim.x - 1));
-    __syncthreads();
-    if (!sh_last) return;
-    __threadfence();
+}
 
-    find_threshold_256(gh, top_k, S.scan, &sh_th);
-    const Thresh th = sh_th;
-    for (int b = t; b < kHistBins; b += kScoreNT) gh[b] = 0u;
-    // compact: above-threshold positions to the sure list, threshold bucket to the candidate list
-    int32_t* sure = ws.sure_idx + (int64_t)i * top_k;
-    int32_t* cand = ws.cand_idx + (int64_t)i * n_elem;
-    for (int e0 = 0; e0 < n_elem; e0 += kScoreNT) {  // uniform trip count: wave_append needs whole waves
-        const int e = e0 + t;
-        const uint32_t key = e < n_elem ? keys[e] : 0u;
-        const int dg = (int)(key >> 21);
-        const bool ok = key != 0u;
-        const int pos = ok ? qpool[e >> 3] * 8 + (e & 7) : 0;
-        wave_append(ok && dg > th.digit, pos, sure, ctrl + kCtlSureIdx);
-        wave_append(ok && dg == th.digit, e, cand, ctrl + kCtlCandIdx);
+struct ReindexList {
+    const uint64_t* c;  // composites with the candidate element id in place of the position
+    const int32_t* pool;
+    __device__ __forceinline__ uint64_t operator()(int e) const {
+        const uint64_t v = c[e];
+        const uint32_t el = composite_pos(v);
+        return composite((uint32_t)(v >> 32), (uint32_t)(pool[el >> 3] * 8 + (el & 7)));
     }
-    __threadfence();
-    __syncthreads();
-    ReindexElem el{cand, keys, qpool};
-    wg_select_write(el, th.in_bucket, top_k - th.above, th.digit, sure, min(th.above, top_k), top_k,
-                    idx_out + (int64_t)i * top_k, S);
-    if (t == kCtlScoreDone || t == kCtlSureIdx || t == kCtlCandIdx) ctrl[t] = 0u;
+};
+
+// ----------------------------------------------------------------------------------------
+// Reindex, kernel 2: one workgroup per query selects Top-K among the pool's positions.
+// Each thread holds a contiguous run of candidate elements in registers; since the pool is
+// ascending, element order is position order, so the output is written in order with one
+// block scan (no sort).
+// ----------------------------------------------------------------------------------------
+constexpr int kReEPT = 32;  // elements per thread at pool_blocks = 4096
+
+__global__ __launch_bounds__(kSelNT) void k_idx_reindex_select(const int32_t* __restrict__ pool, int pool_blocks,
+                                                               int top_k, IndexWs ws,
+                                                               int32_t* __restrict__ idx_out) {
+    __shared__ SelLds U;
+    __shared__ Thresh sh_th;
+    const int i = blockIdx.x;
+    const int t = threadIdx.x;
+    const int n_elem = pool_blocks * 8;
+    const int ept = (((n_elem + kSelNT - 1) / kSelNT) + 3) & ~3;  // multiple of 4, <= 32
+    const int e0 = t * ept;
+    const int32_t* qpool = pool + (int64_t)i * pool_blocks;
+    const uint32_t* keys = ws.keys + (int64_t)i * n_elem;
+    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
+
+    uint32_t kv[kReEPT];
+#pragma unroll
+    for (int j = 0; j < kReEPT; j += 4) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (j < ept && e0 + j + 3 < n_elem) {
+            v = *reinterpret_cast<const uint4*>(keys + e0 + j);
+        } else if (j < ept) {
+            v.x = e0 + j < n_elem ? keys[e0 + j] : 0u;
+            v.y = e0 + j + 1 < n_elem ? keys[e0 + j + 1] : 0u;
+            v.z = e0 + j + 2 < n_elem ? keys[e0 + j + 2] : 0u;
+            v.w = e0 + j + 3 < n_elem ? keys[e0 + j + 3] : 0u;
+        }
+        kv[j] = v.x;
+        kv[j + 1] = v.y;
+        kv[j + 2] = v.z;
+        kv[j + 3] = v.w;
+    }
+    find_threshold<kSelNT>(gh, top_k, U.small.R.scan, &sh_th);
+    const Thresh th = sh_th;
+    const int need = top_k - th.above;
+    uint64_t thr = ~0ull;
+    if (need > 0 && th.in_bucket > 0) {
+        if (th.in_bucket <= kSortCap) {
+            SmallSel& W = U.small;
+            if (t == 0) W.cnt = 0;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < kReEPT; ++j) {
+                const int e = e0 + j;
+                if (j < ept && kv[j] != 0u && (int)(kv[j] >> 21) == th.digit)
+                    W.cand[atomicAdd(&W.cnt, 1)] = composite(kv[j], (uint32_t)(qpool[e >> 3] * 8 + (e & 7)));
+            }
+            __syncthreads();
+            thr = lds_radix_threshold<kSelNT>(W.cand, th.in_bucket, need, th.digit, W.R);
+        } else {
+            // wide tie band: spill the bucket to the workspace and narrow it there
+            uint64_t* cand = ws.cand_idx + (int64_t)i * n_elem;
+            SelectShared& S = U.big;
+            if (t == 0) S.cnt = 0;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < kReEPT; ++j) {
+                const int e = e0 + j;
+                if (j < ept && kv[j] != 0u && (int)(kv[j] >> 21) == th.digit)
+                    cand[atomicAdd(&S.cnt, 1)] = composite(kv[j], (uint32_t)e);
+            }
+            __syncthreads();
+            thr = wg_threshold<kSelNT>(ReindexList{cand, qpool}, th.in_bucket, need, th.digit, S);
+        }
+    }
+    // ordered output: selected = above the bucket, or in it with composite >= thr
+    int cnt = 0;
+    uint32_t selmask = 0u;
+#pragma unroll
+    for (int j = 0; j < kReEPT; ++j) {
+        const int e = e0 + j;
+        bool sel = false;
+        if (j < ept && kv[j] != 0u) {
+            const int dg = (int)(kv[j] >> 21);
+            sel = dg > th.digit ||
+                  (dg == th.digit && composite(kv[j], (uint32_t)(qpool[e >> 3] * 8 + (e & 7))) >= thr);
+        }
+        selmask |= (uint32_t)sel << j;
+        cnt += sel;
+    }
+    int total;
+    int off = block_exclusive_scan<kSelNT>(cnt, U.small.R.scan, total);
+    int32_t* out = idx_out + (int64_t)i * top_k;
+#pragma unroll
+    for (int j = 0; j < kReEPT; ++j) {
+        if ((selmask >> j) & 1u) {
+            const int e = e0 + j;
+            out[off++] = qpool[e >> 3] * 8 + (e & 7);
+        }
+    }
+    for (int j = total + t; j < top_k; j += kSelNT) out[j] = -1;
+    for (int b = t; b < kHistBins; b += kSelNT) gh[b] = 0u;
 }
 
 // ----------------------------------------------------------------------------------------
 // host launchers
 // ----------------------------------------------------------------------------------------
+// phase: 1 = scan kernel, 2 = filter + select kernels, 3 = all
 hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
                              const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
-                             int grid_tiles, int top_k, int pool_blocks, const IndexWs& ws, int32_t* idx_out,
-                             int32_t* pool_out, hipStream_t stream) {
-    if (n_heads <= 4) {
-        hipLaunchKernelGGL(k_idx_score_full<4>, dim3(grid_tiles), dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0,
-                           kv_len, n_q, max_len, cache_rows, n_heads, grid_tiles, top_k, pool_blocks, ws);
-    } else {
-        hipLaunchKernelGGL(k_idx_score_full<8>, dim3(grid_tiles), dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0,
-                           kv_len, n_q, max_len, cache_rows, n_heads, grid_tiles, top_k, pool_blocks, ws);
+                             int grid_tiles, int grid_ftiles, int top_k, int pool_blocks, const IndexWs& ws,
+                             int32_t* idx_out, int32_t* pool_out, int phase, hipStream_t stream) {
+    if (phase & 1) {
+        if (n_heads <= 4) {
+            hipLaunchKernelGGL(k_idx_score_full<4>, dim3(grid_tiles), dim3(kScoreNT), 0, stream, q_idx, w, k_idx,
+                               kv_row0, kv_len, n_q, max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
+        } else {
+            hipLaunchKernelGGL(k_idx_score_full<8>, dim3(grid_tiles), dim3(kScoreNT), 0, stream, q_idx, w, k_idx,
+                               kv_row0, kv_len, n_q, max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_idx_filter_full, dim3(grid_tiles), dim3(kScoreNT), 0, stream, kv_row0, kv_len, n_q, max_len,
-                       cache_rows, grid_tiles, top_k, pool_blocks, ws, idx_out, pool_out);
-    return hipGetLastError();
+    if (phase & 2) {
+        hipLaunchKernelGGL(k_idx_filter_full, dim3(grid_ftiles), dim3(kScoreNT), 0, stream, kv_row0, kv_len, n_q,
+                           max_len, cache_rows, grid_tiles, grid_ftiles, top_k, pool_blocks, ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k_idx_select_full, dim3(n_q, pool_blocks > 0 ? 2 : 1), dim3(kSelNT), 0, stream, kv_row0,
+                           kv_len, n_q, max_len, cache_rows, grid_tiles, top_k, pool_blocks, ws, idx_out, pool_out);
+        return hipGetLastError();
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
@@ -437,12 +587,16 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const uin
     const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
     dim3 grid(chunks, n_q);
     if (n_heads <= 4) {
-        hipLaunchKernelGGL(k_idx_reindex<4>, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, kv_len,
-                           max_len, cache_rows, n_heads, pool, pool_blocks, top_k, ws, idx_out);
+        hipLaunchKernelGGL(k_idx_reindex_score<4>, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, kv_len,
+                           max_len, cache_rows, n_heads, pool, pool_blocks, ws);
     } else {
-        hipLaunchKernelGGL(k_idx_reindex<8>, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, kv_len,
-                           max_len, cache_rows, n_heads, pool, pool_blocks, top_k, ws, idx_out);
+        hipLaunchKernelGGL(k_idx_reindex_score<8>, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, kv_len,
+                           max_len, cache_rows, n_heads, pool, pool_blocks, ws);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_idx_reindex_select, dim3(n_q), dim3(kSelNT), 0, stream, pool, pool_blocks, top_k, ws,
+                       idx_out);
     return hipGetLastError();
 }
 

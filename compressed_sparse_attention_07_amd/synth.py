@@ -5,8 +5,9 @@ path consumes (bf16 bit patterns as uint16, fp32 weights, int64 row offsets).
 It holds none of the method's arithmetic: no quantisation, scoring, selection
 or attention.  Both the HIP path and the CPU oracle are fed from here.
 
-Every stream is numpy PCG64 seeded with SeedSequence([0xC5A2, workload, tensor, seq]),
-so a (workload, tensor, seq) triple always yields the same values on any host.
+Every stream is numpy PCG64 seeded with SeedSequence([0xC5A2, workload, tensor, seq]) (large
+arrays: one stream per 65,536-row chunk, SeedSequence([0xC5A2, workload, tensor, seq, chunk])),
+so the same arguments always yield the same values on any host.
 
 Value laws (the workloads this library is measured on):
   * main KV (post-RoPE latent, shared K=V): z ~ N(0,1) times a per-channel scale
@@ -20,6 +21,9 @@ magnitudes (it says at most about 26); the engineering article's section XI
 bounds the same quantity by sqrt(512) ~ 22.6.
 """
 from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -46,12 +50,12 @@ def rng(workload: int, tensor: int, seq: int = 0) -> np.random.Generator:
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bf16 (round to nearest, ties to even) and return the bit patterns."""
+    """Round finite float32 values to bf16 (round to nearest, ties to even); bit patterns.
+    (In uint32 arithmetic: b + 0x7fff + 1 stays below 2^32 for every finite float.)"""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    lsb = (b >> 16) & 1
-    r = ((b + 0x7FFF + lsb) >> 16).astype(np.uint16)
-    return r
+    b = x.view(np.uint32)
+    r = b + (np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))
+    return (r >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -68,23 +72,53 @@ def channel_sigma(workload: int, tensor: int, dim: int, seq: int = 0) -> np.ndar
     return np.exp(r.uniform(np.log(0.1), np.log(8.0), size=dim)).astype(np.float32)
 
 
-def kv_bf16(workload: int, tensor: int, n: int, dim: int, sigma: np.ndarray, seq: int = 0,
-            chunk: int = 1 << 20) -> np.ndarray:
-    """[n, dim] bf16 bits: clip(N(0,1) * sigma_c, +-26), generated in row chunks to bound host memory."""
+CHUNK_ROWS = 1 << 16  # rows per independent stream of the large generators
+
+
+def _chunked(n: int, fill) -> None:
+    """Run fill(chunk_index, row_start, row_end) over fixed row chunks on a thread pool (numpy's
+    generators release the GIL).  Each chunk has its own seeded stream, so the result does not
+    depend on the number of threads."""
+    chunks = [(c, s, min(n, s + CHUNK_ROWS)) for c, s in enumerate(range(0, n, CHUNK_ROWS))]
+    if len(chunks) <= 1:
+        for c in chunks:
+            fill(*c)
+        return
+    workers = max(1, min(16, (os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(lambda c: fill(*c), chunks))
+
+
+def kv_bf16(workload: int, tensor: int, n: int, dim: int, sigma: np.ndarray, seq: int = 0) -> np.ndarray:
+    """[n, dim] bf16 bits: clip(N(0,1) * sigma_c, +-26), one stream per 65,536-row chunk."""
     out = np.empty((n, dim), dtype=np.uint16)
-    r = rng(workload, tensor, seq)
-    for s in range(0, n, chunk):
-        e = min(n, s + chunk)
+
+    def fill(c, s, e):
+        r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, workload, tensor, seq, c])))
         z = r.standard_normal((e - s, dim), dtype=np.float32)
         z *= sigma[None, :]
         np.clip(z, -KV_CLIP, KV_CLIP, out=z)
         out[s:e] = f32_to_bf16_bits(z)
+
+    _chunked(n, fill)
     return out
 
 
 def int_bf16(workload: int, tensor: int, shape, lo: int = -4, hi: int = 4, seq: int = 0) -> np.ndarray:
-    """Integers uniform in [lo, hi] (within [-4, 4]) as bf16 bits."""
+    """Integers uniform in [lo, hi] (within [-4, 4]) as bf16 bits; 2-D arrays with more than one
+    chunk of rows use one stream per 65,536-row chunk."""
     assert -4 <= lo <= hi <= 4
+    shape = tuple(shape) if isinstance(shape, (tuple, list)) else (shape,)
+    if len(shape) == 2 and shape[0] > CHUNK_ROWS:
+        out = np.empty(shape, dtype=np.uint16)
+
+        def fill(c, s, e):
+            r = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_ROOT, workload, tensor, seq, c])))
+            v = r.integers(lo, hi + 1, size=(e - s, shape[1]), dtype=np.int8)
+            out[s:e] = _INT_BF16[(v + 4).astype(np.intp)]
+
+        _chunked(shape[0], fill)
+        return out
     r = rng(workload, tensor, seq)
     v = r.integers(lo, hi + 1, size=shape, dtype=np.int8)
     return _INT_BF16[(v + 4).astype(np.intp)]

@@ -198,8 +198,10 @@ class Runner:
     def n_q_swa(self) -> int:
         return 1 if self.wl.prefill_chunk else self.n_q
 
-    def step(self, stream=None) -> None:
-        """One pass of the hot path: append the step's KV, then every layer in order."""
+    def step(self, stream=None, scan_events=None) -> None:
+        """One pass of the hot path: append the step's KV, then every layer in order.
+        scan_events: optional list; a (start, end) torch.cuda.Event pair recorded around each
+        Full-mode scan kernel is appended to it (for timing that kernel inside a timed loop)."""
         wl = self.wl
         if wl.appends:
             for st in self.sets:
@@ -209,8 +211,17 @@ class Runner:
             st = self.sets[L.kv_set]
             if L.mode == "F":
                 want_pool = wl.pool_blocks if (self.pool is not None and not pool_built) else 0
-                C.csa2_index_full(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx,
-                                  self.pool if want_pool else None, self.ws_full, stream=stream)
+                pool = self.pool if want_pool else None
+                if scan_events is not None:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                C.csa2_index_full_scan(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
+                                       self.ws_full, stream=stream)
+                if scan_events is not None:
+                    e1.record()
+                    scan_events.append((e0, e1))
+                C.csa2_index_full_select(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
+                                         self.ws_full, stream=stream)
                 pool_built = pool_built or want_pool > 0
                 idx = L.idx
             elif L.mode == "R":

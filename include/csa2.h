@@ -138,6 +138,23 @@ int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
                     size_t ws_bytes, void* stream);
 
 /*
+ * The two halves of csa2_index_full, for callers that time or schedule them apart:
+ * _scan scores every visible position (fused block maxima and first-digit
+ * histograms, one kernel); _select compacts the threshold buckets and writes idx_out
+ * and pool_out (two kernels: a filter over all positions, then one workgroup per
+ * query and output).  Call _select after _scan, on the same stream, with
+ * identical arguments and workspace; together they equal one csa2_index_full call.
+ */
+int csa2_index_full_scan(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
+                         int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
+                         int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws,
+                         size_t ws_bytes, void* stream);
+int csa2_index_full_select(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
+                           int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
+                           int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
  * csa2_index_reindex -- Reindex-mode indexer: this layer's own query scored against
  * the Full layer's keys, over the positions of the pool's blocks only.
  * [Article] sections VIII-IX (Reindex reuses main KV and indexer K, runs its own
@@ -170,6 +187,9 @@ int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_
  *   window  window length W >= 0: query i attends positions [max(0, N_i - W), N_i).
  *   n_heads 1..CSA2_MAX_Q_HEADS.  softmax_scale multiplies q.k.
  *   out     device fp32 [n_q, n_heads, CSA2_KV_DIM].
+ *   ws, ws_bytes  unused by this implementation (pass NULL, 0); kept so that a future
+ *           split-entry variant can take a workspace without an ABI change.
+ *   swa_rows must be below 2^31.
  * Each entry's vector is both key and value.  One softmax runs over the selected
  * entries and the window entries together (no de-duplication).  A query with
  * nothing to attend gets zeros.  n_q == 0 is a no-op.
@@ -180,10 +200,10 @@ int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, 
                 float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Workspace bytes for one call of `op` (CSA2_OP_*) with these sizes; 0 if the sizes
- * are out of range.  For CSA2_OP_ATTEND pass the window length in `pool_blocks`
- * (total_len_ub and max_len_ub are then unused); for CSA2_OP_INDEX_REINDEX
- * total_len_ub and max_len_ub are unused.
+ * Workspace bytes for one call of `op` (CSA2_OP_*) with these sizes; SIZE_MAX if the
+ * sizes are out of range, 0 if the call needs no workspace.  For CSA2_OP_ATTEND pass the
+ * window length in `pool_blocks` (attention needs no workspace: it returns 0); for
+ * CSA2_OP_INDEX_REINDEX total_len_ub and max_len_ub are unused.
  */
 size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32_t max_len_ub,
                             int32_t top_k, int32_t pool_blocks);

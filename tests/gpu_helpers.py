@@ -71,7 +71,7 @@ class IndexCase:
         n_q = len(self.lengths)
         need = C.csa2_workspace_bytes(C.OP_INDEX_FULL, n_q, self.seqs.total_len_ub, self.seqs.max_len_ub, top_k,
                                       pool_blocks)
-        assert need > 0
+        assert 0 < need < C.SIZE_MAX
         ws = ws if ws is not None else C.alloc_workspace(need)
         idx = torch.full((n_q, top_k), -7, dtype=torch.int32, device=DEV)
         pool = torch.full((n_q, max(pool_blocks, 1)), -7, dtype=torch.int32, device=DEV) if pool_blocks else None

@@ -86,12 +86,11 @@ def test_reindex_and_attend_validation():
     assert L.csa2_index_reindex(FAKE, FAKE, FAKE, seqs(), 4, None, 2048, 8, 512, FAKE, FAKE, need_r, None) == C.ERR_NULL
     assert L.csa2_index_reindex(FAKE, FAKE, FAKE, seqs(), 4, FAKE, 2048, 8, 512, FAKE, FAKE, need_r - 1,
                                 None) == C.ERR_WORKSPACE
-    need_a = C.csa2_workspace_bytes(C.OP_ATTEND, 2, 0, 0, 512, 128)
-    assert need_a > 0
+    assert C.csa2_workspace_bytes(C.OP_ATTEND, 2, 0, 0, 512, 128) == 0     # attention needs none
 
-    def att(top_k=512, window=128, cap=128, heads=16, scale=0.1, idx=FAKE, swa=FAKE, ws_bytes=need_a):
-        return L.csa2_attend(FAKE, FAKE, FAKE, seqs(), idx, top_k, swa, FAKE, cap, 1000, window, heads,
-                             ctypes.c_float(scale), FAKE, FAKE, ws_bytes, None)
+    def att(top_k=512, window=128, cap=128, heads=16, scale=0.1, idx=FAKE, swa=FAKE, swa_rows=1000):
+        return L.csa2_attend(FAKE, FAKE, FAKE, seqs(), idx, top_k, swa, FAKE, cap, swa_rows, window, heads,
+                             ctypes.c_float(scale), FAKE, None, 0, None)
 
     assert att(heads=17) == C.ERR_SHAPE
     assert att(cap=100) == C.ERR_SHAPE          # the window ring must hold the window
@@ -99,7 +98,9 @@ def test_reindex_and_attend_validation():
     assert att(scale=float("nan")) == C.ERR_SHAPE
     assert att(idx=None) == C.ERR_NULL
     assert att(swa=None) == C.ERR_NULL
-    assert att(ws_bytes=need_a - 1) == C.ERR_WORKSPACE
+    assert att(swa_rows=1 << 31) == C.ERR_SHAPE
+    assert att(top_k=4097) == C.ERR_SHAPE
+    assert att(window=4097, cap=5000) == C.ERR_SHAPE
 
 
 def test_workspace_sizes():
@@ -108,8 +109,9 @@ def test_workspace_sizes():
     b = C.csa2_workspace_bytes(C.OP_INDEX_FULL, 8, 16 << 20, 2 << 20, 512, 2048)
     assert 0 < a < b
     assert a >= 8 * (1 << 20) * 8          # 4 B key + 4 B candidate per position
-    assert C.csa2_workspace_bytes(C.OP_INDEX_FULL, 8, 100, 10, 0, 0) == 0
+    assert C.csa2_workspace_bytes(C.OP_INDEX_FULL, 8, 100, 10, 0, 0) == C.SIZE_MAX
     r = C.csa2_workspace_bytes(C.OP_INDEX_REINDEX, 8, 0, 0, 512, 2048)
     assert r >= 8 * 2048 * 8 * 8
-    assert C.csa2_workspace_bytes(C.OP_ATTEND, 8, 0, 0, 512, 128) > C.csa2_workspace_bytes(C.OP_ATTEND, 8, 0, 0, 64, 0)
-    assert C.csa2_workspace_bytes(99, 8, 0, 0, 1, 1) == 0
+    assert C.csa2_workspace_bytes(C.OP_ATTEND, 8, 0, 0, 512, 128) == 0
+    assert C.csa2_workspace_bytes(C.OP_ATTEND, 8, 0, 0, 512, 5000) == C.SIZE_MAX
+    assert C.csa2_workspace_bytes(99, 8, 0, 0, 1, 1) == C.SIZE_MAX

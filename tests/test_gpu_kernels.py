@@ -115,6 +115,18 @@ def test_index_full_bit_exact_ragged(top_k, pool_blocks, n_heads):
             assert np.array_equal(pool[i], rp), (i, RAGGED[i])
 
 
+def test_index_full_many_queries():
+    # more queries than one workgroup's scan width: the ragged tile map is built in chunks
+    lengths = list(np.random.default_rng(21).integers(0, 5000, size=300))
+    case = IndexCase(W_T + 9, lengths, n_heads=4)
+    idx, pool, _ = case.run_full(16, 8)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for i in range(0, 300, 7):
+        ri, rp = case.oracle_full(i, 16, 8)
+        assert np.array_equal(idx[i], ri), i
+        assert np.array_equal(pool[i], rp), i
+
+
 def test_index_full_tie_heavy_and_repeatable():
     lengths = [3000, 70000, 12345]
     case = IndexCase(W_T + 1, lengths, n_heads=4, qlo=0, qhi=1)   # scores in a narrow integer range
