@@ -6,10 +6,13 @@ gather-dequant attention.  Inputs are synthetic and already resident in HBM when
 region starts.
 
 Prints ONE JSON line.  `value` is decode tokens/s of the batched 64K-context workload
-(32 sequences x 65,536 positions, 8 layers F R R R U U U U); the 1M-context workload (8 x 2^20,
+(32 sequences x 65,536 positions, 8 layers F R R R U U U U), timed over K replays of the step
+captured in HIP graphs (the host issues one launch per step); the 1M-context workload (8 x 2^20,
 20 layers) is reported in the same line under "also".  `roofline` covers the dominant kernel
-(the Full-mode scan), timed with HIP events around each of its launches inside the timed
-loop.  `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+(the Full-mode scan), timed with HIP events around each of its launches in K eager steps.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.  The 64K workload
+rotates two device copies of its inputs so that no step re-reads data a 256 MiB last-level
+cache could still hold.
 
   python bench.py [--steps K] [--warmup W] [--workload 1] [--also 2] [--no-cpu-baseline]
   python bench.py --mode copy      # plain 1 GiB device copy, for counter calibration
@@ -61,25 +64,40 @@ def read_traffic(workload_name: str):
         return None
 
 
-def measure(wid: int, steps: int, warmup: int, keep_host=False):
+def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
+    """Eager pass (HIP events around every Full scan launch -> the scan kernel's average duration),
+    then the timed region proper: `steps` replays of the step captured in HIP graphs."""
     import torch
     from compressed_sparse_attention_07_amd import workloads as W
 
     wl = W.WORKLOADS[wid]
     t_setup = time.perf_counter()
-    r = W.Runner(wl, keep_host=keep_host)
+    r = W.Runner(wl, keep_host=keep_host, copies=copies)
     setup_s = time.perf_counter() - t_setup
-    print(f"[bench] {wl.name}: setup {setup_s:.1f} s", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: setup {setup_s:.1f} s, {copies} input cop{'y' if copies == 1 else 'ies'}",
+          file=sys.stderr, flush=True)
     for _ in range(warmup):
         r.step()
     torch.cuda.synchronize()
+    # eager steps, scan kernel timed with events on the stream it runs on
     ev = []
     t0 = time.perf_counter()
     for _ in range(steps):
         r.step(scan_events=ev)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    eager_s = time.perf_counter() - t0
     scan_ms = [a.elapsed_time(b) for a, b in ev]
+    # graph replays: the timed region
+    graphs = r.capture()
+    for k in range(warmup):
+        graphs[k % len(graphs)].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        graphs[k % len(graphs)].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    del graphs
     tokens_per_step = wl.prefill_chunk or wl.batch
     alg = r.algorithmic_bytes()
     n_full = wl.layers.count("F")
@@ -90,12 +108,14 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False):
         "workload": wl.name,
         "tokens_per_s": tokens_per_step * steps / elapsed,
         "ms_per_step": ms_step,
+        "eager_tokens_per_s": tokens_per_step * steps / eager_s,
         "alg_bytes_per_step": int(sum(alg.values())),
         "alg_gbps_step": sum(alg.values()) / (ms_step / 1e3) / 1e9,
         "scan_avg_us": scan_avg_s * 1e6,
         "scan_alg_bytes_per_launch": int(scan_bytes_per_launch),
         "scan_gbps": scan_bytes_per_launch / scan_avg_s / 1e9,
         "scan_launches_timed": len(scan_ms),
+        "input_copies": copies,
     }
     res["config"] = {"workload": wl.name, "batch": wl.batch, "context": wl.context, "layers": wl.layers,
                      "top_k": wl.top_k, "pool_blocks": wl.pool_blocks, "window": wl.window,
@@ -200,7 +220,10 @@ def main() -> int:
     from compressed_sparse_attention_07_amd import csa2
     csa2.lib()  # fail loudly if the HIP library is missing
 
-    r, main_res = measure(args.workload, args.steps, args.warmup, keep_host=not args.no_cpu_baseline)
+    # a working set that could sit in the 256 MiB last-level cache is rotated over two copies
+    copies = 2 if args.workload in (0, 1) else 1
+    r, main_res = measure(args.workload, args.steps, args.warmup, keep_host=not args.no_cpu_baseline,
+                          copies=copies)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(r, min(args.cpu_seqs, r.wl.batch))
@@ -208,7 +231,7 @@ def main() -> int:
     torch.cuda.empty_cache()
     also = []
     for w in [int(x) for x in args.also.split(",") if x.strip()]:
-        rr, res = measure(w, max(3, args.steps // 2), args.warmup)
+        rr, res = measure(w, max(3, args.steps // 2), args.warmup, copies=2 if w in (0, 1) else 1)
         del rr
         torch.cuda.empty_cache()
         traffic = read_traffic(res["workload"])
@@ -238,6 +261,10 @@ def main() -> int:
                      "kernel": SCAN_KERNEL, "alg_bytes_per_launch": main_res["scan_alg_bytes_per_launch"],
                      "avg_launch_us": round(main_res["scan_avg_us"], 2)},
         "step_alg_gbps": round(main_res["alg_gbps_step"], 1),
+        "eager_tokens_per_s": round(main_res["eager_tokens_per_s"], 1),
+        "input_copies": main_res["input_copies"],
+        "timing": "value: K replays of the step captured in HIP graphs; roofline: HIP events around "
+                  "each Full-scan launch in K eager steps",
         "step_frac_of_hbm_peak": round(main_res["alg_gbps_step"] / HBM_PEAK_GBPS, 4),
         "cpu_baseline": cpu,
         "also": also,

@@ -10,7 +10,10 @@
 namespace csa2 {
 
 // ---- mirrored from the kernels (kept in one place here) ----
-constexpr int kFullTile = 2048;
+#ifndef CSA2_SCAN_TILE
+#define CSA2_SCAN_TILE 2048
+#endif
+constexpr int kFullTile = CSA2_SCAN_TILE;  // must match the scan kernel's tile
 constexpr int kFilterTile = 16384;
 constexpr int kHistBins = 2048;
 constexpr size_t kAlign = 256;

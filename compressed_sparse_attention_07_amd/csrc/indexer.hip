@@ -35,7 +35,22 @@
 namespace csa2 {
 
 constexpr int kScoreNT = 256;
-constexpr int kFullTile = 2048;                 // positions per Full-scan workgroup
+// Scan-kernel shape (compile-time; the defaults are the tuned ones):
+//   CSA2_SCAN_TILE  positions per workgroup, CSA2_SCAN_U  16-row groups per load batch of a wave,
+//   CSA2_SCAN_NT    non-temporal key loads,  CSA2_SCAN_PIPE  prefetch the next batch while computing.
+#ifndef CSA2_SCAN_TILE
+#define CSA2_SCAN_TILE 2048
+#endif
+#ifndef CSA2_SCAN_U
+#define CSA2_SCAN_U 4
+#endif
+#ifndef CSA2_SCAN_NT
+#define CSA2_SCAN_NT 0
+#endif
+#ifndef CSA2_SCAN_PIPE
+#define CSA2_SCAN_PIPE 0
+#endif
+constexpr int kFullTile = CSA2_SCAN_TILE;       // positions per Full-scan workgroup
 constexpr int kFullTileBlocks = kFullTile / 8;  // 256 blocks
 constexpr int kReindexTile = 512;               // pool positions (64 blocks) per Reindex workgroup
 constexpr int kFilterTile = 16384;              // positions per filter workgroup (8 scan tiles)
@@ -56,6 +71,16 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
                                           false);
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+#if CSA2_SCAN_NT
+    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+#else
+    return *reinterpret_cast<const uint4*>(p);
+#endif
 }
 
 __device__ __forceinline__ float quad_sum(float v) {
@@ -157,22 +182,27 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     const int64_t key_base = (int64_t)ti.start * kFullTile;
     const int p_wave = ti.chunk * kFullTile + wid * (kFullTile / 4);
 
-    for (int b = 0; b < kFullTile / 4; b += 64) {
-        const int base = p_wave + b;
-        if (base >= n) break;
-        uint4 A[4], B[4];
+    constexpr int U = CSA2_SCAN_U;
+    constexpr int kBatch = 16 * U;  // rows per wave per batch
+    uint4 A[U], B[U];
+#if CSA2_SCAN_PIPE
+    uint4 A2[U], B2[U];
+#endif
+    auto load_batch = [&](int base, uint4 (&a)[U], uint4 (&bb)[U]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int p = base + 16 * u + (lane >> 2);
             const int pc = p < n ? p : n - 1;
             const uint16_t* row = k_idx + (row0 + pc) * 64;
-            A[u] = *reinterpret_cast<const uint4*>(row + 8 * j);
-            B[u] = *reinterpret_cast<const uint4*>(row + 32 + 8 * j);
+            a[u] = ld16(row + 8 * j);
+            bb[u] = ld16(row + 32 + 8 * j);
         }
+    };
+    auto compute_batch = [&](int base, const uint4 (&a)[U], const uint4 (&bb)[U]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int p = base + 16 * u + (lane >> 2);
-            const float s = row_score<HI>(A[u], B[u], qs);
+            const float s = row_score<HI>(a[u], bb[u], qs);
             const uint32_t key = p < n ? score_key(s) : 0u;
             if (j == 0 && p < n) {
                 ws.keys[key_base + p] = key;
@@ -186,7 +216,26 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
                 }
             }
         }
+    };
+#if CSA2_SCAN_PIPE
+    if (p_wave < n) load_batch(p_wave, A, B);
+    for (int b = 0; b < kFullTile / 4; b += 2 * kBatch) {
+        const int base = p_wave + b;
+        if (base >= n) break;
+        if (base + kBatch < n) load_batch(base + kBatch, A2, B2);
+        compute_batch(base, A, B);
+        if (base + kBatch >= n) break;
+        if (base + 2 * kBatch < n && b + 2 * kBatch < kFullTile / 4) load_batch(base + 2 * kBatch, A, B);
+        compute_batch(base + kBatch, A2, B2);
     }
+#else
+    for (int b = 0; b < kFullTile / 4; b += kBatch) {
+        const int base = p_wave + b;
+        if (base >= n) break;
+        load_batch(base, A, B);
+        compute_batch(base, A, B);
+    }
+#endif
     __syncthreads();
     uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
     for (int b = t; b < kHistBins; b += kScoreNT) {

@@ -94,7 +94,10 @@ class Runner:
     """Device state of one workload and its step.  host copies of the inputs are kept in
     `self.host` when keep_host=True (for the oracle checks in tests and the bench baseline)."""
 
-    def __init__(self, wl: Workload, device="cuda", keep_host=False, seed=0):
+    def __init__(self, wl: Workload, device="cuda", keep_host=False, seed=0, copies=1):
+        """copies > 1 keeps that many device copies of the KV sets (identical values); step() then
+        rotates through them so consecutive steps never re-read a set that a last-level cache
+        could still hold."""
         self.wl = wl
         self.device = device
         self.host = {} if keep_host else None
@@ -150,6 +153,11 @@ class Runner:
         for st in self.sets:
             st.codes[st.new_rows] = 0xEE
             st.scales[st.new_rows] = 0x77
+        self.copies = [self.sets]
+        for _ in range(1, copies):
+            self.copies.append([KvSet(st.codes.clone(), st.scales.clone(), st.k_idx.clone(), st.x_new, st.new_rows)
+                                for st in self.sets])
+        self._next_copy = 0
         # layers
         self.swa_cap = wl.window + (wl.prefill_chunk or 0)
         self.layers = []
@@ -198,11 +206,16 @@ class Runner:
     def n_q_swa(self) -> int:
         return 1 if self.wl.prefill_chunk else self.n_q
 
-    def step(self, stream=None, scan_events=None) -> None:
+    def step(self, stream=None, scan_events=None, copy=None) -> None:
         """One pass of the hot path: append the step's KV, then every layer in order.
         scan_events: optional list; a (start, end) torch.cuda.Event pair recorded around each
-        Full-mode scan kernel is appended to it (for timing that kernel inside a timed loop)."""
+        Full-mode scan kernel is appended to it (for timing that kernel inside a timed loop).
+        copy: which device copy of the KV sets to use (default: the next one in rotation)."""
         wl = self.wl
+        if copy is None:
+            copy = self._next_copy
+            self._next_copy = (self._next_copy + 1) % len(self.copies)
+        self.sets = self.copies[copy]
         if wl.appends:
             for st in self.sets:
                 C.fp4_kv_append(st.x_new, st.codes, st.scales, dst_rows=st.new_rows, stream=stream)
@@ -232,6 +245,25 @@ class Runner:
                 idx = self.layers[L.idx_src].idx
             C.csa2_attend(L.q, st.codes, st.scales, self.seqs, idx, L.swa, self.swa_row0, self.swa_cap, wl.window,
                           self.scale, L.out, self.ws_att, stream=stream)
+
+    def capture(self):
+        """Capture one step per KV copy into HIP graphs (torch.cuda.CUDAGraph on torch's current
+        device).  Returns the list of graphs; replaying graph k runs the step on copy k.  The
+        kernels issue no memset, and workspaces were zeroed when allocated, outside capture."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for k in range(len(self.copies)):
+                self.step(copy=k)
+        torch.cuda.current_stream().wait_stream(side)
+        graphs = []
+        for k in range(len(self.copies)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(copy=k)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
 
     # ---- accounting of the bytes the method itself must move per step ----
     def algorithmic_bytes(self) -> dict:
