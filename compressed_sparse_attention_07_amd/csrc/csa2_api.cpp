@@ -22,6 +22,10 @@ struct Thresh {
     int32_t digit, above, in_bucket, total;
 };
 
+struct QMeta {
+    int32_t n, start, ntiles, fstart, fntiles, pad[3];
+};
+
 struct IndexWs {
     uint32_t* ctrl;
     uint32_t* hist;
@@ -32,14 +36,17 @@ struct IndexWs {
     int32_t* sure_pool;
     uint64_t* cand_idx;
     uint64_t* cand_pool;
+    QMeta* qmeta;
+    int32_t* tmap;
+    int32_t* fmap;
 };
 
 hipError_t launch_fp4_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
                            uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream);
 hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
                              const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
-                             int grid_tiles, int grid_ftiles, int top_k, int pool_blocks, const IndexWs& ws,
-                             int32_t* idx_out, int32_t* pool_out, int phase, hipStream_t stream);
+                             int grid_tiles, int grid_ftiles, int top_k, int pool_blocks, int prefill,
+                             const IndexWs& ws, int32_t* idx_out, int32_t* pool_out, int phase, hipStream_t stream);
 hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
                                 const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
                                 const int32_t* pool, int pool_blocks, int top_k, const IndexWs& ws, int32_t* idx_out,
@@ -78,7 +85,7 @@ struct Carve {
     }
 };
 
-IndexWs carve_full(void* ws, int n_q, int64_t tiles, int top_k, int pool_blocks, size_t* used) {
+IndexWs carve_full(void* ws, int n_q, int64_t tiles, int64_t ftiles, int top_k, int pool_blocks, size_t* used) {
     Carve c{static_cast<char*>(ws)};
     IndexWs w{};
     w.ctrl = c.take<uint32_t>(ctrl_bytes(n_q) / 4);
@@ -90,6 +97,9 @@ IndexWs carve_full(void* ws, int n_q, int64_t tiles, int top_k, int pool_blocks,
     w.sure_pool = c.take<int32_t>((size_t)n_q * (pool_blocks > 0 ? pool_blocks : 1));
     w.cand_idx = c.take<uint64_t>((size_t)tiles * kFullTile);
     w.cand_pool = c.take<uint64_t>((size_t)tiles * (kFullTile / 8));
+    w.qmeta = c.take<QMeta>((size_t)n_q);
+    w.tmap = c.take<int32_t>((size_t)tiles);
+    w.fmap = c.take<int32_t>((size_t)ftiles);
     *used = c.off;
     return w;
 }
@@ -146,8 +156,9 @@ size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32
         case CSA2_OP_INDEX_FULL: {
             if (top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 || pool_blocks > CSA2_MAX_SELECT) return bad;
             const int64_t tiles = full_grid_tiles(n_q, total_len_ub, max_len_ub);
+            const int64_t ftiles = full_grid_tiles(n_q, total_len_ub, max_len_ub, kFilterTile);
             if (tiles > kMaxTiles) return bad;
-            carve_full(nullptr, n_q, tiles, top_k, pool_blocks, &used);
+            carve_full(nullptr, n_q, tiles, ftiles, top_k, pool_blocks, &used);
             return used;
         }
         case CSA2_OP_INDEX_REINDEX:
@@ -164,8 +175,8 @@ size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32
 }
 
 static int index_full_phase(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const csa2_seqs& seqs,
-                            int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t* idx_out,
-                            int32_t* pool_out, void* ws, size_t ws_bytes, void* stream, int phase) {
+                            int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
+                            int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream, int phase) {
     int st = check_seqs(seqs);
     if (st) return st;
     if (n_heads < 1 || n_heads > CSA2_MAX_IDX_HEADS || top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 ||
@@ -177,39 +188,38 @@ static int index_full_phase(const uint16_t* q_idx, const float* w, const uint16_
     if (pool_blocks > 0 && pool_out == nullptr) return CSA2_ERR_NULL;
     if (!aligned16(q_idx) || !aligned16(k_idx)) return CSA2_ERR_SHAPE;
     const int64_t tiles = full_grid_tiles(seqs.n_q, seqs.total_len_ub, seqs.max_len_ub);
+    const int64_t ftiles = full_grid_tiles(seqs.n_q, seqs.total_len_ub, seqs.max_len_ub, kFilterTile);
     if (tiles > kMaxTiles) return CSA2_ERR_SHAPE;
     size_t need = 0;
-    carve_full(nullptr, seqs.n_q, tiles, top_k, pool_blocks, &need);
+    carve_full(nullptr, seqs.n_q, tiles, ftiles, top_k, pool_blocks, &need);
     if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return CSA2_ERR_WORKSPACE;
-    const IndexWs wsp = carve_full(ws, seqs.n_q, tiles, top_k, pool_blocks, &need);
-    const int64_t ftiles = full_grid_tiles(seqs.n_q, seqs.total_len_ub, seqs.max_len_ub, kFilterTile);
+    const IndexWs wsp = carve_full(ws, seqs.n_q, tiles, ftiles, top_k, pool_blocks, &need);
+    // prefill chunk: the MFMA scoring kernel (shared sequence, at most 4 heads, no pool, >= 16 queries)
+    const int prefill = (shared_kv != 0 && pool_blocks == 0 && n_heads <= 4 && seqs.n_q >= 16) ? 1 : 0;
     return launch_status(launch_index_full(q_idx, w, k_idx, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
-                                           seqs.cache_rows, n_heads, (int)tiles, (int)ftiles, top_k, pool_blocks, wsp,
-                                           idx_out, pool_out, phase, static_cast<hipStream_t>(stream)));
+                                           seqs.cache_rows, n_heads, (int)tiles, (int)ftiles, top_k, pool_blocks,
+                                           prefill, wsp, idx_out, pool_out, phase, static_cast<hipStream_t>(stream)));
 }
 
 int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
                     int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
                     int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
-    (void)shared_kv;
-    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, idx_out, pool_out, ws,
-                            ws_bytes, stream, 3);
+    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
+                            ws, ws_bytes, stream, 3);
 }
 
 int csa2_index_full_scan(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
                          int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
                          int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
-    (void)shared_kv;
-    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, idx_out, pool_out, ws,
-                            ws_bytes, stream, 1);
+    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
+                            ws, ws_bytes, stream, 1);
 }
 
 int csa2_index_full_select(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
                            int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
                            int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
-    (void)shared_kv;
-    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, idx_out, pool_out, ws,
-                            ws_bytes, stream, 2);
+    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
+                            ws, ws_bytes, stream, 2);
 }
 
 int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,

@@ -31,6 +31,16 @@ enum CtrlSlot {
     kCtlSlots = 16,
 };
 
+// Per-query metadata of the Full-mode kernels (written by the prep kernel).
+struct QMeta {
+    int32_t n;        // clamped visible length
+    int32_t start;    // first scan tile (keys of the query start at start * scan tile)
+    int32_t ntiles;   // scan tiles
+    int32_t fstart;   // first filter tile
+    int32_t fntiles;  // filter tiles
+    int32_t pad[3];
+};
+
 // Result of the first-digit threshold search for one query and one selection.
 struct Thresh {
     int32_t digit;      // bucket holding the K-th largest key; -1: everything is selected

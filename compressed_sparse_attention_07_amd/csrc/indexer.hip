@@ -65,6 +65,9 @@ struct IndexWs {
     int32_t* sure_pool;  // [n_q][pool_blocks]
     uint64_t* cand_idx;  // [grid_tiles * 2048]       threshold-bucket composites
     uint64_t* cand_pool; // [grid_tiles * 256]
+    QMeta* qmeta;        // [n_q]                      per-query length and tile ranges (prep kernel)
+    int32_t* tmap;       // [grid_tiles]               scan tile -> query (-1: unused)
+    int32_t* fmap;       // [grid_ftiles]              filter tile -> query (-1: unused)
 };
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -146,6 +149,55 @@ __device__ __forceinline__ uint32_t max_over_8_quads(uint32_t k) {
 
 
 // ----------------------------------------------------------------------------------------
+// Full mode, kernel 0: per-query metadata.  Query i owns max(1, ceil(n_i / tile)) consecutive
+// scan tiles (2,048 positions) and filter tiles (16,384), clamped so the map fits the grids the
+// host sized from its bounds (every query keeps at least one tile of each).  One workgroup.
+// ----------------------------------------------------------------------------------------
+constexpr int kPrepNT = 1024;
+
+__global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict__ kv_row0,
+                                                      const int32_t* __restrict__ kv_len, int n_q, int32_t max_len,
+                                                      int64_t cache_rows, int grid_tiles, int grid_ftiles,
+                                                      IndexWs ws) {
+    __shared__ int sh_scan[16];
+    const int t = threadIdx.x;
+    const int cap_s = grid_tiles - n_q, cap_f = grid_ftiles - n_q;
+    int run_s = 0, run_f = 0;
+    for (int base = 0; base < n_q; base += kPrepNT) {
+        const int i = base + t;
+        int n = 0, xs = 0, xf = 0;
+        if (i < n_q) {
+            n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
+            const int ts = (int)(((int64_t)n + kFullTile - 1) / kFullTile);
+            const int tf = (int)(((int64_t)n + kFilterTile - 1) / kFilterTile);
+            xs = ts > 1 ? ts - 1 : 0;
+            xf = tf > 1 ? tf - 1 : 0;
+        }
+        int tot_s, tot_f;
+        const int ex_s = block_exclusive_scan<kPrepNT>(xs, sh_scan, tot_s);
+        const int ex_f = block_exclusive_scan<kPrepNT>(xf, sh_scan, tot_f);
+        if (i < n_q) {
+            const int p0 = min(cap_s, run_s + ex_s), p1 = min(cap_s, run_s + ex_s + xs);
+            const int f0 = min(cap_f, run_f + ex_f), f1 = min(cap_f, run_f + ex_f + xf);
+            QMeta m;
+            m.start = i + p0;
+            m.ntiles = 1 + (p1 - p0);
+            m.fstart = i + f0;
+            m.fntiles = 1 + (f1 - f0);
+            m.n = (int)min((int64_t)n, min((int64_t)m.ntiles * kFullTile, (int64_t)m.fntiles * kFilterTile));
+            ws.qmeta[i] = m;
+            for (int k = 0; k < m.ntiles; ++k) ws.tmap[m.start + k] = i;
+            for (int k = 0; k < m.fntiles; ++k) ws.fmap[m.fstart + k] = i;
+        }
+        run_s = min(run_s + tot_s, cap_s + 1);
+        run_f = min(run_f + tot_f, cap_f + 1);
+    }
+    const int used_s = n_q + min(cap_s, run_s), used_f = n_q + min(cap_f, run_f);
+    for (int k = used_s + t; k < grid_tiles; k += kPrepNT) ws.tmap[k] = -1;
+    for (int k = used_f + t; k < grid_ftiles; k += kPrepNT) ws.fmap[k] = -1;
+}
+
+// ----------------------------------------------------------------------------------------
 // Full mode, kernel 1: scores -> keys, block-max keys, first-digit histograms
 // ----------------------------------------------------------------------------------------
 template <int HI>
@@ -155,14 +207,10 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     int64_t cache_rows, int n_heads, int grid_tiles, int pool_blocks, IndexWs ws) {
     __shared__ uint32_t sh_hist[kHistBins];
     __shared__ uint32_t sh_bhist[kHistBins];
-    __shared__ int sh_scan[8];
-    __shared__ TileInfo sh_ti;
 
-    const TileInfo ti =
-        tile_lookup<kScoreNT>(kv_len, kv_row0, n_q, max_len, cache_rows, kFullTile, grid_tiles, blockIdx.x, sh_scan,
-                              &sh_ti);
-    if (ti.q < 0) return;
-    const int i = ti.q;
+    const int i = ws.tmap[blockIdx.x];
+    if (i < 0) return;
+    const QMeta qm = ws.qmeta[i];
     const int t = threadIdx.x;
     const int lane = __lane_id();
     const int wid = t / kWave;
@@ -177,10 +225,10 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     load_qslice<HI>(qs, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, j);
     __syncthreads();
 
-    const int n = ti.n;
+    const int n = qm.n;
     const int64_t row0 = kv_row0[i];
-    const int64_t key_base = (int64_t)ti.start * kFullTile;
-    const int p_wave = ti.chunk * kFullTile + wid * (kFullTile / 4);
+    const int64_t key_base = (int64_t)qm.start * kFullTile;
+    const int p_wave = ((int)blockIdx.x - qm.start) * kFullTile + wid * (kFullTile / 4);
 
     constexpr int U = CSA2_SCAN_U;
     constexpr int kBatch = 16 * U;  // rows per wave per batch
@@ -248,6 +296,138 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     }
 }
 
+// ----------------------------------------------------------------------------------------
+// Full mode, kernel 1 (prefill chunk: every query reads the same sequence): the scores of
+// 16 queries x 16 positions per MFMA tile.  For indexer head h, D_h = Q_h . K^T on
+// v_mfma_f32_16x16x32_bf16 (two k-steps cover the 64 channels); lane (g, r) supplies query r
+// of Q_h and position r of K^T with channels 32s + 8g .. 32s + 8g + 7, so its key loads are
+// the scan's 16-byte slices.  The accumulator of lane (g, r) holds queries 4g+i at position r;
+// the lane folds its four heads (ReLU, weights), writes the keys and counts first digits in
+// an LDS histogram (two 16-bit counters per word: a workgroup counts at most kPfPos per bin).
+// ----------------------------------------------------------------------------------------
+constexpr int kPfQ = 16;       // queries per workgroup
+constexpr int kPfPos = 4096;   // positions per workgroup (1,024 per wave)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{v.x, v.y, v.z, v.w});
+}
+
+__global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
+    const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, IndexWs ws) {
+    __shared__ uint32_t sh_hist[kPfQ][kHistBins / 2];
+    __shared__ int sh_n[kPfQ];
+    __shared__ int64_t sh_base[kPfQ];
+    const int t = threadIdx.x;
+    const int lane = __lane_id();
+    const int wid = t / kWave;
+    const int g = lane >> 4, r = lane & 15;
+    const int q0 = blockIdx.y * kPfQ;
+    const int p_wg = blockIdx.x * kPfPos;
+    const int64_t row0 = kv_row0[0];
+    const int64_t row_room = (row0 >= 0 && row0 <= cache_rows) ? cache_rows - row0 : 0;
+    if (t < kPfQ) {
+        const int q = q0 + t;
+        int n = 0;
+        int64_t base = 0;
+        if (q < n_q) {
+            const QMeta m = ws.qmeta[q];
+            n = (int)min((int64_t)m.n, row_room);
+            base = (int64_t)m.start * kFullTile;
+        }
+        sh_n[t] = n;
+        sh_base[t] = base;
+    }
+    __syncthreads();
+    int n_max = 0;
+#pragma unroll
+    for (int k = 0; k < kPfQ; ++k) n_max = max(n_max, sh_n[k]);
+    if (p_wg >= n_max) return;  // uniform: nothing visible in this position chunk
+    for (int k = t; k < kPfQ * kHistBins / 2; k += kScoreNT) (&sh_hist[0][0])[k] = 0u;
+    // A fragments: query q0 + r, head h, channels 32s + 8g .. +8 ; weights of queries q0 + 4g + i
+    bf16x8_t qa[4][2];
+    float wq[4][4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const int q = q0 + r;
+        const bool ok = q < n_q && h < n_heads;
+        const uint16_t* qp = q_idx + ((int64_t)(ok ? q : 0) * n_heads + (ok ? h : 0)) * 64 + 8 * g;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+            qa[h][s2] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qp + 32 * s2) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int qi = q0 + 4 * g + i;
+            wq[i][h] = (qi < n_q && h < n_heads) ? w[(int64_t)qi * n_heads + h] : 0.f;
+        }
+    }
+    int nq[4];
+    int64_t bq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        nq[i] = sh_n[4 * g + i];
+        bq[i] = sh_base[4 * g + i];
+    }
+    __syncthreads();
+
+    const int p_wave = p_wg + wid * (kPfPos / 4);
+    constexpr int TB = 4;  // 16-position tiles per load batch
+    for (int b = 0; b < kPfPos / 4; b += 16 * TB) {
+        const int base = p_wave + b;
+        if (base >= n_max) break;
+        uint4 kb[TB][2];
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            const int p = base + 16 * u + r;
+            if (p < n_max) {
+                const uint16_t* row = k_idx + (row0 + p) * 64 + 8 * g;
+                kb[u][0] = *reinterpret_cast<const uint4*>(row);
+                kb[u][1] = *reinterpret_cast<const uint4*>(row + 32);
+            } else {
+                kb[u][0] = make_uint4(0, 0, 0, 0);
+                kb[u][1] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            f32x4_t acc[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][0], as_bf16x8(kb[u][0]), a, 0, 0, 0);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][1], as_bf16x8(kb[u][1]), a, 0, 0, 0);
+                acc[h] = a;
+            }
+            const int p = base + 16 * u + r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float sc = 0.f;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], fmaxf(acc[h][i], 0.f), sc);
+                if (p < nq[i]) {
+                    const uint32_t key = score_key(sc);
+                    ws.keys[bq[i] + p] = key;
+                    const uint32_t bin = key >> 21;
+                    atomicAdd(&sh_hist[4 * g + i][bin >> 1], 1u << (16 * (bin & 1)));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (int k = t; k < kPfQ * kHistBins / 2; k += kScoreNT) {
+        const int ql = k / (kHistBins / 2), wd = k % (kHistBins / 2);
+        const uint32_t v = sh_hist[ql][wd];
+        if (v == 0u || q0 + ql >= n_q) continue;
+        uint32_t* gh = ws.hist + (int64_t)(q0 + ql) * 2 * kHistBins;
+        if (v & 0xffffu) atomicAdd(&gh[2 * wd], v & 0xffffu);
+        if (v >> 16) atomicAdd(&gh[2 * wd + 1], v >> 16);
+    }
+}
+
 // Compact one workgroup's share of a key array: elements whose first digit is above the threshold
 // bucket go to sure[] (positions), elements in the bucket to cand[] (composites).  Two passes over
 // the keys (count, then write) so each list costs one global atomic per workgroup.
@@ -297,24 +477,21 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __r
                                                               int grid_ftiles, int top_k, int pool_blocks, IndexWs ws) {
     __shared__ int sh_scan[8];
     __shared__ int sh_base[2];
-    __shared__ TileInfo sh_ti;
     __shared__ Thresh sh_th;
 
-    const TileInfo tf = tile_lookup<kScoreNT>(kv_len, kv_row0, n_q, max_len, cache_rows, kFilterTile, grid_ftiles,
-                                              blockIdx.x, sh_scan, &sh_ti);
-    if (tf.q < 0) return;
-    const int i = tf.q;
-    const TileInfo ts = tile_map<kScoreNT>(kv_len, kv_row0, n_q, max_len, cache_rows, kFullTile, grid_tiles, 0, i,
-                                           sh_scan, &sh_ti);
-    const int n = min(tf.n, ts.n);
-    const int64_t key_base = (int64_t)ts.start * kFullTile;
+    const int i = ws.fmap[blockIdx.x];
+    if (i < 0) return;
+    const QMeta qm = ws.qmeta[i];
+    const int n = qm.n;
+    const int fchunk = (int)blockIdx.x - qm.fstart;
+    const int64_t key_base = (int64_t)qm.start * kFullTile;
     uint32_t* ctrl = ws.ctrl + (int64_t)i * kCtlSlots;
     const uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
 
     find_threshold_256(gh, top_k, sh_scan, &sh_th);
     const Thresh th = sh_th;
     __syncthreads();
-    const int p0 = tf.chunk * kFilterTile;
+    const int p0 = fchunk * kFilterTile;
     wg_compact<kFilterTile / kScoreNT>(ws.keys + key_base, p0, min(n, p0 + kFilterTile), th,
                                        ws.sure_idx + (int64_t)i * top_k, ctrl + kCtlSureIdx, ws.cand_idx + key_base,
                                        ctrl + kCtlCandIdx, sh_scan, sh_base);
@@ -323,7 +500,7 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __r
         const Thresh tp = sh_th;
         __syncthreads();
         const int nb = (n + 7) >> 3;
-        const int b0 = tf.chunk * (kFilterTile / 8);
+        const int b0 = fchunk * (kFilterTile / 8);
         wg_compact<kFilterTile / 8 / kScoreNT>(ws.bkeys + key_base / 8, b0, min(nb, b0 + kFilterTile / 8), tp,
                                                ws.sure_pool + (int64_t)i * pool_blocks, ctrl + kCtlSurePool,
                                                ws.cand_pool + key_base / 8, ctrl + kCtlCandPool, sh_scan, sh_base);
@@ -372,14 +549,11 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
                                                             int32_t* __restrict__ idx_out,
                                                             int32_t* __restrict__ pool_out) {
     __shared__ SelLds U;
-    __shared__ TileInfo sh_ti;
     __shared__ Thresh sh_th;
     const int i = blockIdx.x;
     const int which = blockIdx.y;  // 0: positions, 1: pool blocks
     const int t = threadIdx.x;
-    const TileInfo ts = tile_map<kSelNT>(kv_len, kv_row0, n_q, max_len, cache_rows, kFullTile, grid_tiles, 0, i,
-                                         U.small.R.scan, &sh_ti);
-    const int64_t key_base = (int64_t)ts.start * kFullTile;
+    const int64_t key_base = (int64_t)ws.qmeta[i].start * kFullTile;
     uint32_t* ctrl = ws.ctrl + (int64_t)i * kCtlSlots;
     uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins + which * kHistBins;
     const int k = which ? pool_blocks : top_k;
@@ -601,20 +775,30 @@ __global__ __launch_bounds__(kSelNT) void k_idx_reindex_select(const int32_t* __
 // ----------------------------------------------------------------------------------------
 // host launchers
 // ----------------------------------------------------------------------------------------
-// phase: 1 = scan kernel, 2 = filter + select kernels, 3 = all
+// phase: 1 = prep + scan kernels, 2 = filter + select kernels, 3 = all.
+// prefill != 0: every query reads the same sequence (kv_row0[0]) and no pool is asked for, so
+// the scores come from the MFMA kernel.
 hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
                              const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
-                             int grid_tiles, int grid_ftiles, int top_k, int pool_blocks, const IndexWs& ws,
-                             int32_t* idx_out, int32_t* pool_out, int phase, hipStream_t stream) {
+                             int grid_tiles, int grid_ftiles, int top_k, int pool_blocks, int prefill,
+                             const IndexWs& ws, int32_t* idx_out, int32_t* pool_out, int phase, hipStream_t stream) {
     if (phase & 1) {
-        if (n_heads <= 4) {
+        hipLaunchKernelGGL(k_idx_prep, dim3(1), dim3(kPrepNT), 0, stream, kv_row0, kv_len, n_q, max_len, cache_rows,
+                           grid_tiles, grid_ftiles, ws);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (prefill) {
+            const dim3 grid((unsigned)((max_len + kPfPos - 1) / kPfPos), (unsigned)((n_q + kPfQ - 1) / kPfQ));
+            hipLaunchKernelGGL(k_idx_score_prefill, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, n_q,
+                               cache_rows, n_heads, ws);
+        } else if (n_heads <= 4) {
             hipLaunchKernelGGL(k_idx_score_full<4>, dim3(grid_tiles), dim3(kScoreNT), 0, stream, q_idx, w, k_idx,
                                kv_row0, kv_len, n_q, max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
         } else {
             hipLaunchKernelGGL(k_idx_score_full<8>, dim3(grid_tiles), dim3(kScoreNT), 0, stream, q_idx, w, k_idx,
                                kv_row0, kv_len, n_q, max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
         }
-        hipError_t e = hipGetLastError();
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (phase & 2) {

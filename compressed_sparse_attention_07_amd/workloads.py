@@ -228,13 +228,14 @@ class Runner:
                 if scan_events is not None:
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record()
+                shared = 1 if wl.prefill_chunk else 0   # a prefill chunk: all queries read one sequence
                 C.csa2_index_full_scan(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
-                                       self.ws_full, stream=stream)
+                                       self.ws_full, shared_kv=shared, stream=stream)
                 if scan_events is not None:
                     e1.record()
                     scan_events.append((e0, e1))
                 C.csa2_index_full_select(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
-                                         self.ws_full, stream=stream)
+                                         self.ws_full, shared_kv=shared, stream=stream)
                 pool_built = pool_built or want_pool > 0
                 idx = L.idx
             elif L.mode == "R":

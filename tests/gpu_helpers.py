@@ -67,7 +67,7 @@ class IndexCase:
         w = self.w[i] if w is None else w
         return O.index_reindex(q, w, self.k[r0:r0 + max(n, 0)], n, pool, top_k, 8)
 
-    def run_full(self, top_k, pool_blocks, ws=None):
+    def run_full(self, top_k, pool_blocks, ws=None, shared_kv=0):
         n_q = len(self.lengths)
         need = C.csa2_workspace_bytes(C.OP_INDEX_FULL, n_q, self.seqs.total_len_ub, self.seqs.max_len_ub, top_k,
                                       pool_blocks)
@@ -75,7 +75,8 @@ class IndexCase:
         ws = ws if ws is not None else C.alloc_workspace(need)
         idx = torch.full((n_q, top_k), -7, dtype=torch.int32, device=DEV)
         pool = torch.full((n_q, max(pool_blocks, 1)), -7, dtype=torch.int32, device=DEV) if pool_blocks else None
-        C.csa2_index_full(self.q_dev, self.w_dev, self.k_dev, self.seqs, top_k, pool_blocks, idx, pool, ws)
+        C.csa2_index_full(self.q_dev, self.w_dev, self.k_dev, self.seqs, top_k, pool_blocks, idx, pool, ws,
+                          shared_kv=shared_kv)
         torch.cuda.synchronize()
         return idx, pool, ws
 
@@ -88,6 +89,24 @@ class IndexCase:
                              self.k_dev, self.seqs, pool, top_k, idx, ws)
         torch.cuda.synchronize()
         return idx, ws
+
+
+class SharedIndexCase(IndexCase):
+    """Queries that all read one sequence (a prefill chunk): query t sees lengths[t] positions."""
+
+    def __init__(self, workload, rows, lengths, n_heads=4, qlo=-4, qhi=4, seed=0):
+        self.lengths = np.asarray(lengths, dtype=np.int64)
+        self.row0 = np.zeros(len(lengths), dtype=np.int64)
+        self.rows = rows
+        n_q = len(lengths)
+        self.k = synth.int_bf16(workload, synth.T_IDX_K, (rows, 64), qlo, qhi, seq=seed)
+        self.q = synth.int_bf16(workload, synth.T_IDX_Q, (n_q, n_heads, 64), qlo, qhi, seq=seed)
+        self.w = synth.int_weights(workload, synth.T_IDX_W, (n_q, n_heads), seq=seed)
+        self.n_heads = n_heads
+        self.k_dev = bf16_tensor(self.k)
+        self.q_dev = bf16_tensor(self.q)
+        self.w_dev = torch.from_numpy(self.w).to(DEV)
+        self.seqs = seqs_for(self.lengths, self.row0, rows)
 
 
 class AttendCase:

@@ -8,7 +8,7 @@ import oracle as O
 from compressed_sparse_attention_07_amd import csa2 as C
 from compressed_sparse_attention_07_amd import synth
 
-from gpu_helpers import AttendCase, IndexCase, bf16_tensor, DEV
+from gpu_helpers import AttendCase, IndexCase, SharedIndexCase, bf16_tensor, DEV
 
 pytestmark = pytest.mark.gpu
 
@@ -156,6 +156,32 @@ def test_index_full_all_equal_scores_takes_lowest_positions():
         nb = -(-lengths[i] // 8)
         assert np.array_equal(pool[i], np.arange(2048) if nb >= 2048 else
                               np.concatenate([np.arange(nb), -np.ones(2048 - nb, int)]))
+
+
+# ---------------------------------------------------------------- prefill chunk (MFMA scoring)
+@pytest.mark.parametrize("n_heads,top_k", [(4, 512), (3, 100), (1, 7)])
+def test_index_prefill_mfma_causal_bit_exact(n_heads, top_k):
+    # 100 queries of one 6,000-position sequence; query t sees C + t + 1 positions
+    C_, T = 5900, 100
+    case = SharedIndexCase(W_T + 40 + n_heads, C_ + T, C_ + 1 + np.arange(T), n_heads=n_heads)
+    idx_m, _, _ = case.run_full(top_k, 0, shared_kv=1)
+    idx_v, _, _ = case.run_full(top_k, 0, shared_kv=0)          # decode VALU path on the same data
+    idx_m, idx_v = idx_m.cpu().numpy(), idx_v.cpu().numpy()
+    assert np.array_equal(idx_m, idx_v)
+    for t in list(range(0, T, 9)) + [T - 1]:
+        ri, _ = case.oracle_full(t, top_k, 0)
+        assert np.array_equal(idx_m[t], ri), t
+
+
+def test_index_prefill_mfma_arbitrary_lengths_and_ties():
+    # lengths in any order (not monotone), including empty and tiny queries, tie-heavy scores
+    lengths = [0, 1, 17, 4096, 4097, 9000, 3, 12345, 8191, 8192, 8193, 50, 7777, 2, 1000, 6000, 12000, 5]
+    case = SharedIndexCase(W_T + 50, 12345, lengths, n_heads=4, qlo=0, qhi=1)
+    idx_m, _, _ = case.run_full(512, 0, shared_kv=1)
+    idx_m = idx_m.cpu().numpy()
+    for t in range(len(lengths)):
+        ri, _ = case.oracle_full(t, 512, 0)
+        assert np.array_equal(idx_m[t], ri), t
 
 
 # ---------------------------------------------------------------- Reindex mode
