@@ -7,48 +7,57 @@
 //   section XI  - cached FP4 values are dequantised before attention (no FP4 matmul).
 // The cached latent is both key and value; 16 query heads share it.
 //
-// One workgroup (8 waves) per query, no cross-workgroup merge.  The entry list (top_k
-// selected slots, then min(W, N) window positions) is cut into pairs of 16-entry blocks;
-// waves take pairs round-robin and keep their own online-softmax state.  Both small
-// contractions run on bf16 MFMA (v_mfma_f32_16x16x32_bf16, 16 heads = the MFMA N size):
-//   S^T[entry][head] = K . Q^T   A = 16 entries x 32 channels, dequantised FP4 -> bf16
-//                                (exact: E2M1 x E4M3 needs at most 6 significant bits),
-//                                B = Q^T from registers;
-//   O^T[dim][head]  += V^T . P^T A = 16 channels x 32 entries read from a wave-private LDS
-//                                copy of the entries, B = P^T, which is exactly the S^T
-//                                accumulator layout, so P never leaves registers.  P is
-//                                split into bf16 hi + lo parts (two MFMAs) so the product
-//                                keeps ~16 mantissa bits; accumulation is fp32.
+// One workgroup (8 waves) per query.  At decode sizes this kernel is latency-bound (a few
+// hundred KB per launch), so it is built to put every memory access of the query in flight
+// at once and to keep the per-entry instruction count low:
+//   * work goes in rounds; in one round wave w owns FP4 blocks (16 entries each)
+//     32R + 4w .. 32R + 4w + 3 and window block 8R + w.  Top-512 with a 128 window is one
+//     round.  All gathers of a round are issued before anything waits on them.
+//   * FP4 entries are dequantised to f16 (hardware E2M1 -> f16, then one packed f16 multiply
+//     by the E4M3 group scale: both factors and the product are exact in f16) and contracted
+//     on v_mfma_f32_16x16x32_f16; window entries stay bf16 (v_mfma_f32_16x16x32_bf16).
+//     The query is given to the f16 contraction scaled per head by a power of two that
+//     keeps it inside f16 range; the logit is scaled back exactly.
+//   * every logit of the round is formed before any probability, so each wave exponentiates
+//     against its own round maximum and rescales its accumulator at most once per round.
+//   * P.V: V^T operands come from a wave-private LDS tile written row-major (one 16-byte
+//     store per 8 channels) and read with ds_read_b64_tr_b16, which returns the transposed
+//     4 x 16 sub-block the MFMA A operand needs.  P is f16 for FP4 entries (one MFMA) and a
+//     bf16 hi + lo pair for window entries (two MFMAs, ~16 mantissa bits).
+//   * waves merge once at the end: (max, sum, O) of each wave go through LDS and each
+//     thread finishes four outputs.
 // MFMA 16x16x32 lane layout (checked on gfx950): lane l supplies row/column l%16 of A/B and
 // eight K elements chosen by the lane group l/16 (the same K set for A and B); the
-// accumulator of lane l holds rows 4*(l/16)+i, column l%16.  Channel slice of lane group g:
-// channels [32g, 32g+32), k-step s covers channels 32g+8s .. 32g+8s+7.
+// accumulator of lane l holds rows 4*(l/16)+i, column l%16.  16x16x16: four K elements.
+// ds_read_b64_tr_b16 (checked on gfx950): within each 16-lane group, lane i's element j is
+// element i%4 of the four 16-bit values addressed by lane 4j + i/4.
+// Logits use S^T[entry][head] = K . Q^T (A = 16 entries x 32 channels from registers,
+// B = Q^T); the S^T accumulator is already the B operand layout P^T needs for
+// O^T[dim][head] += V^T . P^T, so P never leaves registers.
 #include "csa2_device.hpp"
 
 namespace csa2 {
 
 constexpr int kAttWaves = 8;
 constexpr int kAttNT = kAttWaves * 64;
-constexpr int kD = 128;                 // latent / head dim
-constexpr int kNH = 16;                 // heads (padded)
-constexpr int kMaxEntries = 4096 + 4096;  // top_k + window at their limits
-constexpr int kVtStride = 40;           // bf16 per LDS row of V^T (32 entries + 8 pad)
-constexpr int kVtSize = kD * kVtStride + 64;  // + skew: rows of channel quarter c>>5 shift by 16 bf16
+constexpr int kD = 128;                      // latent / head dim
+constexpr int kNH = 16;                      // heads (padded)
+constexpr int kRB = 4;                       // FP4 blocks per wave per round
+constexpr int kRoundFp4 = kAttWaves * kRB;   // FP4 blocks per round (512 entries)
+constexpr int kRoundWin = kAttWaves;         // window blocks per round (128 entries)
+constexpr int kRowB = 288;                   // bytes per tile row: 128 x 16-bit + 32 B skew
+constexpr int kTileB = 32 * kRowB;           // one wave's tile: 32 entries
+constexpr int kOStride = 132;                // floats per head row of the merge buffer
+static_assert(kNH * kOStride * 4 <= kTileB, "a wave's merge rows fit in its tile");
 
-// V^T tile address of (channel c, entry e): the 16-bf16 skew per 32-channel quarter puts the four
-// lane groups (which write different quarters) on different LDS banks.
-__device__ __forceinline__ int vt_at(int c, int e) { return c * kVtStride + (c >> 5) * 16 + e; }
-
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float e4m3_val(uint32_t b) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    float v = e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-    return (b & 0x80u) ? -v : v;
-}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
 
@@ -57,69 +66,46 @@ __device__ __forceinline__ uint32_t bf16_rne(float v) {
     return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
 }
 
-// One entry's 32-channel slice (channels [32g, 32g+32)) as four bf16x8 MFMA fragments.
-struct KSlice {
-    u32x4 f[4];
-};
-
-// Dequantise one lane's 32 FP4 codes (16 B, channels [32g, 32g+32)) with their two E4M3 scales.
-// The hardware conversion gives the raw E2M1 values exactly (its scale operand only carries a
-// power of two, so it is given 1.0); the E4M3 scale is applied with one exact fp32 multiply and
-// v_perm keeps the upper halves, which are the exact bf16 values.
-template <int Q>  // byte Q of w: (low nibble, high nibble) -> packed bf16 pair of value * sc
-__device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t w, float sc) {
-    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, Q);
-    return __builtin_amdgcn_perm(__float_as_uint(v[1] * sc), __float_as_uint(v[0] * sc), 0x07060302u);
+__device__ __forceinline__ uint32_t f16pair(float a, float b) {
+    const f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ void dequant_fp4_slice(const uint4 cb, uint32_t sb, KSlice& ks) {
-    const float s0 = e4m3_val(sb & 0xffu), s1 = e4m3_val((sb >> 8) & 0xffu);
+// Byte Q of w (low nibble = even channel, high nibble = odd channel) as two f16 values times
+// the group scale.  The conversion is given scale 1.0 (its scale operand only carries a power
+// of two); E2M1 x E4M3 needs at most 6 significant bits, so the f16 product is exact.
+template <int Q>
+__device__ __forceinline__ uint32_t fp4_pair_f16(uint32_t w, f16x2 sc) {
+    const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, Q);
+    return __builtin_bit_cast(uint32_t, v * sc);
+}
+
+// One lane's 32 FP4 codes (channels [32g, 32g+32)) and its two E4M3 scale bytes (low 16 bits
+// of sb) -> four f16x8 A fragments (fragment s = channels 32g + 8s .. 32g + 8s + 7).  The
+// hardware E4M3 -> f16 conversion is exact for every finite E4M3 value (the packer never
+// writes the NaN codes 0x7f / 0xff).
+__device__ __forceinline__ void dequant_f16(const uint4 cb, uint32_t sb, u32x4 (&f)[4]) {
+    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+    const f16x2 sc0 = {sc[0], sc[0]}, sc1 = {sc[1], sc[1]};
     const uint32_t w[4] = {cb.x, cb.y, cb.z, cb.w};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const float sc = s < 2 ? s0 : s1;
-        ks.f[s][0] = fp4_pair_bf16<0>(w[s], sc);
-        ks.f[s][1] = fp4_pair_bf16<1>(w[s], sc);
-        ks.f[s][2] = fp4_pair_bf16<2>(w[s], sc);
-        ks.f[s][3] = fp4_pair_bf16<3>(w[s], sc);
+        const f16x2 sc = s < 2 ? sc0 : sc1;
+        f[s][0] = fp4_pair_f16<0>(w[s], sc);
+        f[s][1] = fp4_pair_f16<1>(w[s], sc);
+        f[s][2] = fp4_pair_f16<2>(w[s], sc);
+        f[s][3] = fp4_pair_f16<3>(w[s], sc);
     }
 }
 
-// One lane's raw data for one entry: FP4 codes (16 B) + 2 scale bytes, or 64 B of bf16 window.
-struct RawEntry {
-    uint4 a[4];
-    uint32_t sb;
-    int kind;  // 0: nothing to attend, 1: FP4 cache entry, 2: window entry
-};
-
-__device__ __forceinline__ RawEntry load_entry(int32_t row, int e, int top_k, const uint8_t* codes,
-                                               const uint8_t* scales, const uint16_t* swa, int64_t row0, int g) {
-    RawEntry x;
-    x.kind = 0;
-    x.sb = 0;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) x.a[s] = make_uint4(0, 0, 0, 0);
-    if (row >= 0 && e < top_k) {
-        const int64_t cr = row0 + row;
-        x.a[0] = *reinterpret_cast<const uint4*>(codes + cr * 64 + 16 * g);
-        x.sb = *reinterpret_cast<const uint16_t*>(scales + cr * 8 + 2 * g);
-        x.kind = 1;
-    } else if (row >= 0) {
-        const uint4* src = reinterpret_cast<const uint4*>(swa + (int64_t)row * kD + 32 * g);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) x.a[s] = src[s];
-        x.kind = 2;
-    }
-    return x;
+__device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-__device__ __forceinline__ void entry_slice(const RawEntry& x, KSlice& ks) {
-    if (x.kind == 1) {
-        dequant_fp4_slice(x.a[0], x.sb, ks);
-    } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) ks.f[s] = u32x4{x.a[s].x, x.a[s].y, x.a[s].z, x.a[s].w};
-    }
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 __global__ __launch_bounds__(kAttNT) void k_attend(
@@ -127,9 +113,7 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
     const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len, int32_t max_len, int64_t cache_rows,
     const int32_t* __restrict__ idx, int top_k, const uint16_t* __restrict__ swa, const int64_t* __restrict__ swa_row0,
     int swa_cap, int64_t swa_rows, int window, int n_heads, float scale_log2, float* __restrict__ out) {
-    // LDS: per-wave V^T tile [128 channels][32 entries] (bf16); reused for the cross-wave merge
-    __shared__ __align__(16) uint16_t s_vt[kAttWaves][kVtSize];
-    __shared__ int32_t s_row[kMaxEntries];  // cache row (FP4) or window row (>= 0), -1 = skip
+    __shared__ __align__(16) uint8_t s_tile[kAttWaves][kTileB];
     __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
 
     const int i = blockIdx.x;
@@ -140,177 +124,236 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
     const int r = l & 15;   // row / column within the 16
     const int n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
     const int wc = min(window, n);
-    const int n_ent = top_k + wc;
-    const int n_pairs = (n_ent + 31) >> 5;
-    const int64_t row0 = kv_row0[i];
-    const int64_t wrow0 = wc > 0 ? swa_row0[i] : 0;
+    const int64_t row0 = n > 0 ? kv_row0[i] : 0;
+    const bool win_ok = wc > 0 && swa_rows > 0;
+    const int64_t wrow0 = win_ok ? swa_row0[i] : 0;
+    const int nb4 = n > 0 ? (top_k + 15) >> 4 : 0;  // FP4 blocks (none when nothing is visible)
+    const int nbw = win_ok ? (wc + 15) >> 4 : 0;    // window blocks
+    const int rounds = max((nb4 + kRoundFp4 - 1) / kRoundFp4, (nbw + kRoundWin - 1) / kRoundWin);
 
-    // entry list -> rows
-    for (int e = t; e < n_pairs * 32; e += kAttNT) {
-        int32_t row = -1;
-        if (e < top_k) {
-            const int pos = idx[(int64_t)i * top_k + e];
-            if (pos >= 0 && pos < n) row = pos;  // relative to row0
-        } else if (e < n_ent) {
-            const int p = n - wc + (e - top_k);
-            const int64_t sr = wrow0 + (p % swa_cap);
-            if (sr >= 0 && sr < swa_rows) row = (int32_t)sr;
-        }
-        s_row[e] = row;
-    }
-
-    // Q^T as B fragments: lane (g, r) holds Q[head r][32g + 8s + j], pre-scaled later (logits)
-    u32x4 qf[4];
+    // Q^T fragments of head r, channels 32g + 8s .. + 7: bf16 as given, and f16 scaled by 2^qe
+    u32x4 qb[4], qh[4];
+    float cf4;  // logit multiplier of the f16 contraction: scale_log2 * 2^-qe
     {
         const bool hv = r < n_heads;
         const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)i * n_heads + (hv ? r : 0)) * kD + 32 * g);
+        float amax = 0.f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const uint4 v = hv ? qp[s] : make_uint4(0, 0, 0, 0);
-            qf[s] = u32x4{v.x, v.y, v.z, v.w};
+            qb[s] = u32x4{v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                amax = fmaxf(amax, fmaxf(fabsf(bf16lo(qb[s][c])), fabsf(bf16hi(qb[s][c]))));
         }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        int ex = 0;
+        if (amax > 0.f) (void)frexpf(amax, &ex);    // amax < 2^ex
+        const int qe = min(120, max(-120, 15 - ex));  // scaled |q| < 2^15 < f16 max
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                qh[s][c] = f16pair(ldexpf(bf16lo(qb[s][c]), qe), ldexpf(bf16hi(qb[s][c]), qe));
+        cf4 = scale_log2 * ldexpf(1.f, -qe);
     }
-    __syncthreads();
 
-    float m_run = -INFINITY;  // running max (log2 units) of head r
+    float m_run = -INFINITY;  // running max (log2 units) of head r over this wave's entries
     float l_run = 0.f;        // this lane's share of the running sum
     f32x4 o[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint16_t* vt = s_vt[wave];
+    uint8_t* tile = s_tile[wave];
+    // tile addresses: row-major store of this lane's entry r; transposed read of rows 4g + r/4
+    const int st_off = r * kRowB + 64 * g;
+    const int tr_off = (4 * g + (r >> 2)) * kRowB + 8 * (r & 3);
 
-    // raw entry data of the current and the next pair (software pipeline: the next pair's
-    // gathers are in flight while the current pair is computed)
-    RawEntry cur[2], nxt[2];
-    if (wave < n_pairs) {
+    for (int R = 0; R < rounds; ++R) {
+        // ---- every gather of the round, issued before any wait ----
+        const int b0 = R * kRoundFp4 + wave * kRB;
+        int pos[kRB];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) cur[b] = load_entry(s_row[wave * 32 + 16 * b + r], wave * 32 + 16 * b + r, top_k,
-                                                        codes, scales, swa, row0, g);
-    }
-    for (int pr = wave; pr < n_pairs; pr += kAttWaves) {
-        if (pr + kAttWaves < n_pairs) {
+        for (int j = 0; j < kRB; ++j) {
+            const int e = 16 * (b0 + j) + r;
+            pos[j] = (b0 + j < nb4 && e < top_k) ? idx[(int64_t)i * top_k + e] : -1;
+        }
+        const int wb = R * kRoundWin + wave;
+        const bool wblk = wb < nbw;
+        u32x4 wf[4];
+        bool wvalid = false;
+        {
+            int64_t sr = -1;
+            const int ew = 16 * wb + r;
+            if (wblk && ew < wc) {
+                const int p = n - wc + ew;
+                sr = wrow0 + (p % swa_cap);
+                if (sr >= swa_rows) sr = -1;
+            }
+            wvalid = sr >= 0;
+            // rows of absent entries are clamped to row 0 and masked (win_ok: the store has rows)
+            const uint4* src = reinterpret_cast<const uint4*>(swa + (wvalid ? sr : 0) * kD + 32 * g);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int e = (pr + kAttWaves) * 32 + 16 * b + r;
-                nxt[b] = load_entry(s_row[e], e, top_k, codes, scales, swa, row0, g);
+            for (int s = 0; s < 4; ++s) {
+                const uint4 v = win_ok ? src[s] : make_uint4(0, 0, 0, 0);
+                wf[s] = u32x4{v.x, v.y, v.z, v.w};
             }
         }
-        f32x4 sacc[2];
-        uint64_t vmask[2];
+        uint4 cw[kRB];
+        uint32_t sw[kRB];
+        uint32_t vb[kRB];  // validity of the 16 entries of each block (bit e)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            KSlice ks;
-            entry_slice(cur[b], ks);
-            vmask[b] = __ballot(cur[b].kind != 0);
+        for (int j = 0; j < kRB; ++j) {
+            // inside the loop n > 0, so row0 is a cache row: absent entries read it and are masked
+            const bool ok = pos[j] >= 0 && pos[j] < n;
+            const int64_t cr = row0 + (ok ? pos[j] : 0);
+            cw[j] = top_k > 0 ? *reinterpret_cast<const uint4*>(codes + cr * 64 + 16 * g) : make_uint4(0, 0, 0, 0);
+            sw[j] = top_k > 0 ? (uint32_t)*reinterpret_cast<const uint16_t*>(scales + cr * 8 + 2 * g) : 0u;
+            vb[j] = (uint32_t)__ballot(ok) & 0xffffu;
+        }
+        const uint32_t vbw = (uint32_t)__ballot(wvalid) & 0xffffu;
+
+        // ---- logits of the whole round ----
+        u32x4 kf[kRB][4];
+        f32x4 sa[kRB];
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) {
+            dequant_f16(cw[j], sw[j], kf[j]);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ks.f[s]),
-                                                              __builtin_bit_cast(bf16x8, qf[s]), acc, 0, 0, 0);
-            sacc[b] = acc;
-            // V^T tile: channel 32g + 8s + j, entry 16b + r
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-#pragma unroll
-                for (int q2 = 0; q2 < 4; ++q2) {
-                    const int c0 = 32 * g + 8 * s + 2 * q2;
-                    vt[vt_at(c0, 16 * b + r)] = (uint16_t)(ks.f[s][q2] & 0xffffu);
-                    vt[vt_at(c0 + 1, 16 * b + r)] = (uint16_t)(ks.f[s][q2] >> 16);
-                }
-            }
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kf[j][s]),
+                                                             __builtin_bit_cast(f16x8, qh[s]), acc, 0, 0, 0);
+            sa[j] = acc;
         }
-        // the V^T tile is read by other lanes of this wave below: order LDS writes before reads
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        // logits of head r for entries 16b + 4g + i (valid bits come from the loading lanes 0..15)
-        float x[8];
+        f32x4 swc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            swc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[s]),
+                                                          __builtin_bit_cast(bf16x8, qb[s]), swc, 0, 0, 0);
+        // logits of head r for entries 4g + ii of each block (log2 units), masked
+        float x[kRB + 1][4];
         float mx = -INFINITY;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int j = 0; j <= kRB; ++j) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                const bool ok = (vmask[b] >> (4 * g + ii)) & 1ull;
-                x[4 * b + ii] = ok ? sacc[b][ii] * scale_log2 : -INFINITY;
-                mx = fmaxf(mx, x[4 * b + ii]);
+                const uint32_t bits = j < kRB ? vb[j] : vbw;
+                const bool ok = (bits >> (4 * g + ii)) & 1u;
+                const float v = j < kRB ? sa[j][ii] * cf4 : swc[ii] * scale_log2;
+                x[j][ii] = ok ? v : -INFINITY;
+                mx = fmaxf(mx, x[j][ii]);
             }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-        uint32_t ph[4], pl[4];
+        if (m_new == -INFINITY) continue;  // nothing valid yet (the same for every head)
+        if (m_run != -INFINITY) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) o[db] *= alpha;
+        }
+        m_run = m_new;
+        // probabilities: f16 for FP4 entries, bf16 hi + lo for window entries
+        uint32_t ph[kRB][2], pwh[2], pwl[2];
         float psum = 0.f;
 #pragma unroll
-        for (int k2 = 0; k2 < 4; ++k2) {
-            float p0 = (m_new == -INFINITY || x[2 * k2] == -INFINITY) ? 0.f : exp2f(x[2 * k2] - m_new);
-            float p1 = (m_new == -INFINITY || x[2 * k2 + 1] == -INFINITY) ? 0.f : exp2f(x[2 * k2 + 1] - m_new);
-            psum += p0 + p1;
-            const uint32_t h0 = bf16_rne(p0), h1 = bf16_rne(p1);
-            const float r0 = p0 - __uint_as_float(h0 << 16), r1 = p1 - __uint_as_float(h1 << 16);
-            ph[k2] = pack2(h0, h1);
-            pl[k2] = pack2(bf16_rne(r0), bf16_rne(r1));
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        const u32x4 phv = {ph[0], ph[1], ph[2], ph[3]};
-        const u32x4 plv = {pl[0], pl[1], pl[2], pl[3]};
-        // P^T fragment's K set for lane group g: entries {4g..4g+3} of block 0, then of block 1
+        for (int j = 0; j <= kRB; ++j) {
+            float p[4];
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
-            const uint16_t* vr = vt + vt_at(16 * db + r, 0);
-            const uint2 a0 = *reinterpret_cast<const uint2*>(vr + 4 * g);
-            const uint2 a1 = *reinterpret_cast<const uint2*>(vr + 16 + 4 * g);
-            const u32x4 af = {a0.x, a0.y, a1.x, a1.y};
-            f32x4 acc = o[db] * alpha;
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
-                                                          __builtin_bit_cast(bf16x8, phv), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af),
-                                                          __builtin_bit_cast(bf16x8, plv), acc, 0, 0, 0);
-            o[db] = acc;
+            for (int ii = 0; ii < 4; ++ii) {
+                p[ii] = __builtin_amdgcn_exp2f(x[j][ii] - m_new);  // masked: exp2(-inf) = 0
+                psum += p[ii];
+            }
+            if (j < kRB) {
+                ph[j][0] = f16pair(p[0], p[1]);
+                ph[j][1] = f16pair(p[2], p[3]);
+            } else {
+                uint32_t h[4], lo[4];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    h[ii] = bf16_rne(p[ii]);
+                    lo[ii] = bf16_rne(p[ii] - __uint_as_float(h[ii] << 16));
+                }
+                pwh[0] = pack2(h[0], h[1]);
+                pwh[1] = pack2(h[2], h[3]);
+                pwl[0] = pack2(lo[0], lo[1]);
+                pwl[1] = pack2(lo[2], lo[3]);
+            }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        cur[0] = nxt[0];
-        cur[1] = nxt[1];
+        l_run += psum;
+
+        // ---- P.V over FP4 block pairs (K = 32 entries: 16 of each block) ----
+#pragma unroll
+        for (int pp = 0; pp < kRB / 2; ++pp) {
+            if (b0 + 2 * pp >= nb4) break;  // wave-uniform
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                *reinterpret_cast<u32x4*>(tile + st_off + 16 * s) = kf[2 * pp][s];
+                *reinterpret_cast<u32x4*>(tile + 16 * kRowB + st_off + 16 * s) = kf[2 * pp + 1][s];
+            }
+            wave_lds_sync();
+            const u32x4 pf = {ph[2 * pp][0], ph[2 * pp][1], ph[2 * pp + 1][0], ph[2 * pp + 1][1]};
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const s16x4 a0 = lds_tr16(tile + tr_off + 32 * db);
+                const s16x4 a1 = lds_tr16(tile + 16 * kRowB + tr_off + 32 * db);
+                const u32x2 u0 = __builtin_bit_cast(u32x2, a0), u1 = __builtin_bit_cast(u32x2, a1);
+                const u32x4 af = {u0[0], u0[1], u1[0], u1[1]};
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af),
+                                                               __builtin_bit_cast(f16x8, pf), o[db], 0, 0, 0);
+            }
+            wave_lds_sync();
+        }
+        // ---- P.V over the window block (K = 16 entries) ----
+        if (wblk) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) *reinterpret_cast<u32x4*>(tile + st_off + 16 * s) = wf[s];
+            wave_lds_sync();
+            const u32x2 hv2 = {pwh[0], pwh[1]}, lv2 = {pwl[0], pwl[1]};
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const s16x4 a = lds_tr16(tile + tr_off + 32 * db);
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, hv2), o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, lv2), o[db], 0, 0, 0);
+            }
+            wave_lds_sync();
+        }
     }
-    // per-head sums of this wave (the 4 lane groups hold different entries of head r)
+
+    // ---- merge the eight waves ----
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
     if (g == 0) {
         s_m[wave][r] = m_run;
         s_l[wave][r] = l_run;
     }
-    __syncthreads();  // all waves done with their V^T tiles
-    // merge: each wave's O^T goes to LDS as [head][128] fp32 (reusing the V^T space)
-    float* ob = reinterpret_cast<float*>(&s_vt[0][0]) + wave * (kNH * kD);
     {
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, s_m[w][r]);
-        const float f = (m_run == -INFINITY) ? 0.f : exp2f(m_run - M);
+        // this wave's O^T (dims 16db + 4g + ii of head r) -> rows [head][dim] inside its own tile
+        float* ob = reinterpret_cast<float*>(tile);
 #pragma unroll
         for (int db = 0; db < 8; ++db)
-            *reinterpret_cast<float4*>(&ob[r * kD + 16 * db + 4 * g]) =
-                make_float4(o[db][0] * f, o[db][1] * f, o[db][2] * f, o[db][3] * f);
+            *reinterpret_cast<f32x4*>(&ob[r * kOStride + 16 * db + 4 * g]) = o[db];
     }
     __syncthreads();
-    const float* all = reinterpret_cast<const float*>(&s_vt[0][0]);
-    for (int x = t; x < kNH * kD; x += kAttNT) {
-        const int h = x / kD;
-        if (h >= n_heads) break;
+    const int h = t >> 5;
+    const int d0 = 4 * (t & 31);
+    if (h < n_heads) {
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, s_m[w][h]);
-        float L = 0.f, O = 0.f;
+        float L = 0.f;
+        f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < kAttWaves; ++w) {
-            const float f = (s_m[w][h] == -INFINITY) ? 0.f : exp2f(s_m[w][h] - M);
+            const float f = (s_m[w][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
             L = fmaf(s_l[w][h], f, L);
-            O += all[w * kNH * kD + x];
+            O += f * *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(s_tile[w]) + h * kOStride + d0);
         }
-        out[(int64_t)i * n_heads * kD + x] = L > 0.f ? O / L : 0.f;
+        const f32x4 res = L > 0.f ? O / L : f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(out + ((int64_t)i * n_heads + h) * kD + d0) = res;
     }
 }
 

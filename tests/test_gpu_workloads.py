@@ -75,7 +75,10 @@ def _run(wid, queries, steps=2):
 
 def test_workload0_single_4k():
     r, worst = _run(0, [0])
-    assert worst < 1e-5
+    # FP4 entries' probabilities are rounded to f16 (relative error <= 2^-11 each) before P.V,
+    # so one query's error is bounded by ~2^-11 * max|V|: far inside the 2e-3 bar, and a dropped
+    # entry or wrong scale would exceed it
+    assert worst < 5e-4
 
 
 def test_workload1_batch32_64k_8layers():
