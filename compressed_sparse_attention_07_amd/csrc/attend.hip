@@ -108,6 +108,10 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// kFp4: top_k > 0 (the FP4 cache is read); kWin: window > 0 and the window store has rows.
+// Both are fixed per launch so that every gather below is unconditional (clamped addresses,
+// masked results): loads under branches make the compiler wait on some of them early.
+template <bool kFp4, bool kWin>
 __global__ __launch_bounds__(kAttNT) void k_attend(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len, int32_t max_len, int64_t cache_rows,
@@ -125,27 +129,62 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
     const int n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
     const int wc = min(window, n);
     const int64_t row0 = n > 0 ? kv_row0[i] : 0;
-    const bool win_ok = wc > 0 && swa_rows > 0;
+    const bool win_ok = kWin && wc > 0;
     const int64_t wrow0 = win_ok ? swa_row0[i] : 0;
-    const int nb4 = n > 0 ? (top_k + 15) >> 4 : 0;  // FP4 blocks (none when nothing is visible)
-    const int nbw = win_ok ? (wc + 15) >> 4 : 0;    // window blocks
+    const int nb4 = (kFp4 && n > 0) ? (top_k + 15) >> 4 : 0;  // FP4 blocks (none when nothing is visible)
+    const int nbw = win_ok ? (wc + 15) >> 4 : 0;              // window blocks
     const int rounds = max((nb4 + kRoundFp4 - 1) / kRoundFp4, (nbw + kRoundWin - 1) / kRoundWin);
 
-    // Q^T fragments of head r, channels 32g + 8s .. + 7: bf16 as given, and f16 scaled by 2^qe
+    // ---- the round's index and window gathers: round 0's go out before the query is read ----
+    int pos[kRB];     // selected positions of this lane's entry in each FP4 block (-1: none)
+    u32x4 wf[4];      // window entry: channels [32g, 32g+32) as bf16
+    bool wvalid = false;
+    auto issue_round = [&](int R) {
+        const int b0 = R * kRoundFp4 + wave * kRB;
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) {
+            const int e = 16 * (b0 + j) + r;
+            pos[j] = (b0 + j < nb4 && e < top_k) ? idx[(int64_t)i * top_k + e] : -1;
+        }
+        const int wb = R * kRoundWin + wave;
+        int64_t sr = -1;
+        const int ew = 16 * wb + r;
+        if (wb < nbw && ew < wc) {
+            const int p = n - wc + ew;
+            sr = wrow0 + (p % swa_cap);
+            if (sr >= swa_rows) sr = -1;
+        }
+        wvalid = sr >= 0;
+        // rows of absent entries are clamped to row 0 (kWin: the store has rows) and masked
+        const uint4* src = reinterpret_cast<const uint4*>(swa + (wvalid ? sr : 0) * kD + 32 * g);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint4 v = kWin ? src[s] : make_uint4(0, 0, 0, 0);
+            wf[s] = u32x4{v.x, v.y, v.z, v.w};
+        }
+    };
+    issue_round(0);
+
+    // Q^T fragments of head r, channels 32g + 8s .. + 7: bf16 as given (loaded now), and f16
+    // scaled by 2^qe (converted while round 0's gathers are in flight)
     u32x4 qb[4], qh[4];
-    float cf4;  // logit multiplier of the f16 contraction: scale_log2 * 2^-qe
+    float cf4 = 0.f;  // logit multiplier of the f16 contraction: scale_log2 * 2^-qe
     {
         const bool hv = r < n_heads;
         const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)i * n_heads + (hv ? r : 0)) * kD + 32 * g);
-        float amax = 0.f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const uint4 v = hv ? qp[s] : make_uint4(0, 0, 0, 0);
             qb[s] = u32x4{v.x, v.y, v.z, v.w};
+        }
+    }
+    auto convert_q = [&]() {
+        float amax = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 amax = fmaxf(amax, fmaxf(fabsf(bf16lo(qb[s][c])), fabsf(bf16hi(qb[s][c]))));
-        }
         amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
         int ex = 0;
@@ -157,7 +196,7 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
             for (int c = 0; c < 4; ++c)
                 qh[s][c] = f16pair(ldexpf(bf16lo(qb[s][c]), qe), ldexpf(bf16hi(qb[s][c]), qe));
         cf4 = scale_log2 * ldexpf(1.f, -qe);
-    }
+    };
 
     float m_run = -INFINITY;  // running max (log2 units) of head r over this wave's entries
     float l_run = 0.f;        // this lane's share of the running sum
@@ -170,35 +209,10 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
     const int tr_off = (4 * g + (r >> 2)) * kRowB + 8 * (r & 3);
 
     for (int R = 0; R < rounds; ++R) {
-        // ---- every gather of the round, issued before any wait ----
+        if (R > 0) issue_round(R);
         const int b0 = R * kRoundFp4 + wave * kRB;
-        int pos[kRB];
-#pragma unroll
-        for (int j = 0; j < kRB; ++j) {
-            const int e = 16 * (b0 + j) + r;
-            pos[j] = (b0 + j < nb4 && e < top_k) ? idx[(int64_t)i * top_k + e] : -1;
-        }
         const int wb = R * kRoundWin + wave;
         const bool wblk = wb < nbw;
-        u32x4 wf[4];
-        bool wvalid = false;
-        {
-            int64_t sr = -1;
-            const int ew = 16 * wb + r;
-            if (wblk && ew < wc) {
-                const int p = n - wc + ew;
-                sr = wrow0 + (p % swa_cap);
-                if (sr >= swa_rows) sr = -1;
-            }
-            wvalid = sr >= 0;
-            // rows of absent entries are clamped to row 0 and masked (win_ok: the store has rows)
-            const uint4* src = reinterpret_cast<const uint4*>(swa + (wvalid ? sr : 0) * kD + 32 * g);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint4 v = win_ok ? src[s] : make_uint4(0, 0, 0, 0);
-                wf[s] = u32x4{v.x, v.y, v.z, v.w};
-            }
-        }
         uint4 cw[kRB];
         uint32_t sw[kRB];
         uint32_t vb[kRB];  // validity of the 16 entries of each block (bit e)
@@ -207,11 +221,16 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
             // inside the loop n > 0, so row0 is a cache row: absent entries read it and are masked
             const bool ok = pos[j] >= 0 && pos[j] < n;
             const int64_t cr = row0 + (ok ? pos[j] : 0);
-            cw[j] = top_k > 0 ? *reinterpret_cast<const uint4*>(codes + cr * 64 + 16 * g) : make_uint4(0, 0, 0, 0);
-            sw[j] = top_k > 0 ? (uint32_t)*reinterpret_cast<const uint16_t*>(scales + cr * 8 + 2 * g) : 0u;
+            cw[j] = kFp4 ? *reinterpret_cast<const uint4*>(codes + cr * 64 + 16 * g) : make_uint4(0, 0, 0, 0);
+            sw[j] = kFp4 ? (uint32_t)*reinterpret_cast<const uint16_t*>(scales + cr * 8 + 2 * g) : 0u;
             vb[j] = (uint32_t)__ballot(ok) & 0xffffu;
         }
         const uint32_t vbw = (uint32_t)__ballot(wvalid) & 0xffffu;
+        // keep every gather above this point: the scheduler would otherwise sink some of them
+        // below the first wait and pay a second memory latency
+        __builtin_amdgcn_sched_barrier(0);
+        if (R == 0) convert_q();
+        __builtin_amdgcn_sched_barrier(0);
 
         // ---- logits of the whole round ----
         u32x4 kf[kRB][4];
@@ -362,7 +381,10 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
                          int top_k, const uint16_t* swa, const int64_t* swa_row0, int swa_cap, int64_t swa_rows,
                          int window, int n_heads, float softmax_scale, float* out, hipStream_t stream) {
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(k_attend, dim3(n_q), dim3(kAttNT), 0, stream, q, codes, scales, kv_row0, kv_len, max_len,
+    const bool fp4 = top_k > 0, win = window > 0 && swa_rows > 0;
+    auto kern = fp4 ? (win ? k_attend<true, true> : k_attend<true, false>)
+                    : (win ? k_attend<false, true> : k_attend<false, false>);
+    hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, q, codes, scales, kv_row0, kv_len, max_len,
                        cache_rows, idx, top_k, swa, swa_row0, swa_cap, swa_rows, window, n_heads, scale_log2, out);
     return hipGetLastError();
 }

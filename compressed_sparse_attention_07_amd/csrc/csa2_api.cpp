@@ -111,8 +111,7 @@ IndexWs carve_reindex(void* ws, int n_q, int top_k, int pool_blocks, size_t* use
     w.hist = c.take<uint32_t>(hist_bytes(n_q) / 4);
     w.meta = c.take<Thresh>((size_t)n_q * 2);
     w.keys = c.take<uint32_t>((size_t)n_q * pool_blocks * 8);
-    w.sure_idx = c.take<int32_t>((size_t)n_q * top_k);
-    w.cand_idx = c.take<uint64_t>((size_t)n_q * pool_blocks * 8);
+    (void)top_k;
     *used = c.off;
     return w;
 }

@@ -86,17 +86,28 @@ __device__ __forceinline__ int32_t eff_len(const int32_t* kv_len, const int64_t*
     return (int32_t)n;
 }
 
+// Inclusive prefix sum across a wave64 with DPP moves (no LDS round trips): Hillis-Steele
+// within each 16-lane row (row_shr 1, 2, 4, 8), then row 0's total into row 1 and row 2's
+// into row 3 (row_bcast:15), then the total of rows 0-1 into rows 2-3 (row_bcast:31).  Lanes
+// without a source add the `old` operand, 0.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
 // Block-wide exclusive scan of one int per thread (blockDim.x == NT).  `sh` holds NT/64 ints.
-template <int NT>
+// TAIL_SYNC = false leaves out the closing barrier: the caller must pass a barrier before
+// anything writes `sh` again.
+template <int NT, bool TAIL_SYNC = true>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_inclusive_scan(v);
     if (lane == kWave - 1) sh[wid] = x;
     __syncthreads();
     int wbase = 0, tot = 0;
@@ -106,7 +117,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) 
         if (w < wid) wbase += s;
         tot += s;
     }
-    __syncthreads();
+    if (TAIL_SYNC) __syncthreads();
     total = tot;
     return wbase + x - v;
 }
@@ -187,15 +198,9 @@ __device__ inline void find_threshold(const uint32_t* hist, int k, int* sh_scan,
         local += (int)h[j];
     }
     int total;
-    int above = block_exclusive_scan<NT>(local, sh_scan, total);
-    if (t == 0) {
-        out->digit = -1;
-        out->above = total;
-        out->in_bucket = 0;
-        out->total = total;
-    }
-    __syncthreads();
-    if (total > k) {
+    // no closing barrier: the barrier below separates these reads of sh_scan from later writes
+    int above = block_exclusive_scan<NT, false>(local, sh_scan, total);
+    if (total > k) {  // uniform: exactly one thread holds the crossing bin
         int a = above;
 #pragma unroll
         for (int j = 0; j < BPT; ++j) {
@@ -204,9 +209,15 @@ __device__ inline void find_threshold(const uint32_t* hist, int k, int* sh_scan,
                 out->digit = kHistBins - 1 - (BPT * t + j);
                 out->above = a;
                 out->in_bucket = c;
+                out->total = total;
             }
             a += c;
         }
+    } else if (t == 0) {
+        out->digit = -1;
+        out->above = total;
+        out->in_bucket = 0;
+        out->total = total;
     }
     __syncthreads();
 }

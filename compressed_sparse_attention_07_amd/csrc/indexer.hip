@@ -661,111 +661,118 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     }
 }
 
-struct ReindexList {
-    const uint64_t* c;  // composites with the candidate element id in place of the position
-    const int32_t* pool;
-    __device__ __forceinline__ uint64_t operator()(int e) const {
-        const uint64_t v = c[e];
-        const uint32_t el = composite_pos(v);
-        return composite((uint32_t)(v >> 32), (uint32_t)(pool[el >> 3] * 8 + (el & 7)));
-    }
-};
-
 // ----------------------------------------------------------------------------------------
 // Reindex, kernel 2: one workgroup per query selects Top-K among the pool's positions.
-// Each thread holds a contiguous run of candidate elements in registers; since the pool is
-// ascending, element order is position order, so the output is written in order with one
-// block scan (no sort).
+// The pool is ascending, so element order is position order: the ranking (score desc,
+// position asc) is "every key above the K-th largest key T, then the keys equal to T in
+// element order".  T is found by radix passes over the keys alone (the first digit's
+// histogram comes from the score kernel; at most two more passes over the keys held in
+// registers), and ties at T are ranked by one block scan, so no composite sort is needed.
+// Each thread holds whole pool blocks (a multiple of 8 consecutive elements).
 // ----------------------------------------------------------------------------------------
-constexpr int kReEPT = 32;  // elements per thread at pool_blocks = 4096
+constexpr int kReMaxEPT = 32;  // elements per thread at pool_blocks = 4096
 
+// EPT: elements per thread (8, 16 or 32; a multiple of 8, so threads hold whole pool blocks).
+template <int EPT>
 __global__ __launch_bounds__(kSelNT) void k_idx_reindex_select(const int32_t* __restrict__ pool, int pool_blocks,
                                                                int top_k, IndexWs ws,
                                                                int32_t* __restrict__ idx_out) {
-    __shared__ SelLds U;
+    __shared__ uint32_t s_hist[2][kHistBins];
+    __shared__ uint32_t s_cand[kSelNT * EPT];  // keys of the first-digit bucket
+    __shared__ int s_scan[kSelNT / kWave];
     __shared__ Thresh sh_th;
     const int i = blockIdx.x;
     const int t = threadIdx.x;
     const int n_elem = pool_blocks * 8;
-    const int ept = (((n_elem + kSelNT - 1) / kSelNT) + 3) & ~3;  // multiple of 4, <= 32
-    const int e0 = t * ept;
+    const int e0 = t * EPT;
     const int32_t* qpool = pool + (int64_t)i * pool_blocks;
     const uint32_t* keys = ws.keys + (int64_t)i * n_elem;
     uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
 
-    uint32_t kv[kReEPT];
+    uint32_t kv[EPT];
+    int32_t pb[EPT / 8];  // pool blocks of this thread's elements
 #pragma unroll
-    for (int j = 0; j < kReEPT; j += 4) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (j < ept && e0 + j + 3 < n_elem) {
-            v = *reinterpret_cast<const uint4*>(keys + e0 + j);
-        } else if (j < ept) {
-            v.x = e0 + j < n_elem ? keys[e0 + j] : 0u;
-            v.y = e0 + j + 1 < n_elem ? keys[e0 + j + 1] : 0u;
-            v.z = e0 + j + 2 < n_elem ? keys[e0 + j + 2] : 0u;
-            v.w = e0 + j + 3 < n_elem ? keys[e0 + j + 3] : 0u;
+    for (int j = 0; j < EPT; j += 8) {
+        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+        int32_t blk = -1;
+        if (e0 + j < n_elem) {  // n_elem is a multiple of 8: the whole block is there
+            a = *reinterpret_cast<const uint4*>(keys + e0 + j);
+            b = *reinterpret_cast<const uint4*>(keys + e0 + j + 4);
+            blk = qpool[(e0 + j) >> 3];
         }
-        kv[j] = v.x;
-        kv[j + 1] = v.y;
-        kv[j + 2] = v.z;
-        kv[j + 3] = v.w;
+        kv[j] = a.x; kv[j + 1] = a.y; kv[j + 2] = a.z; kv[j + 3] = a.w;
+        kv[j + 4] = b.x; kv[j + 5] = b.y; kv[j + 6] = b.z; kv[j + 7] = b.w;
+        pb[j >> 3] = blk;
     }
-    find_threshold<kSelNT>(gh, top_k, U.small.R.scan, &sh_th);
-    const Thresh th = sh_th;
-    const int need = top_k - th.above;
-    uint64_t thr = ~0ull;
-    if (need > 0 && th.in_bucket > 0) {
-        if (th.in_bucket <= kSortCap) {
-            SmallSel& W = U.small;
-            if (t == 0) W.cnt = 0;
-            __syncthreads();
+    for (int b = t; b < 2 * kHistBins; b += kSelNT) (&s_hist[0][0])[b] = 0u;
+    // first digit: histogram accumulated by the score kernel (its barriers also cover the
+    // clearing above)
+    find_threshold<kSelNT>(gh, top_k, s_scan, &sh_th);
+    Thresh th = sh_th;
+    uint32_t T = 1u;           // selected: key > T, or key == T among the first need_eq of them
+    int need_eq = INT32_MAX;   // (keys are >= 1 for every valid element; 0 marks padding)
+    if (th.digit >= 0) {
+        int need = top_k - th.above;  // 1 <= need <= inb
+        int inb = th.in_bucket;
+        uint32_t prefix = (uint32_t)th.digit;
+        int pbits = kHistBits;
+        if (inb > need) {
+            // compact the bucket's keys to LDS (order is irrelevant: only T is sought)
+            uint32_t in_mask = 0u;
 #pragma unroll
-            for (int j = 0; j < kReEPT; ++j) {
-                const int e = e0 + j;
-                if (j < ept && kv[j] != 0u && (int)(kv[j] >> 21) == th.digit)
-                    W.cand[atomicAdd(&W.cnt, 1)] = composite(kv[j], (uint32_t)(qpool[e >> 3] * 8 + (e & 7)));
+            for (int j = 0; j < EPT; ++j) in_mask |= (uint32_t)((kv[j] >> (32 - kHistBits)) == prefix) << j;
+            int m;
+            int off = block_exclusive_scan<kSelNT>(__popc(in_mask), s_scan, m);
+#pragma unroll
+            for (int j = 0; j < EPT; ++j)
+                if ((in_mask >> j) & 1u) s_cand[off++] = kv[j];
+            __syncthreads();
+            // at most two more radix passes (11 and 10 bits) over the m bucket keys
+            int hb = 0;
+            while (pbits < 32 && inb > need) {
+                const int w = min(kHistBits, 32 - pbits);
+                const int shift = 32 - pbits - w;
+                for (int e = t; e < m; e += kSelNT) {
+                    const uint32_t v = s_cand[e];
+                    if ((v >> (32 - pbits)) == prefix) atomicAdd(&s_hist[hb][(v >> shift) & ((1u << w) - 1u)], 1u);
+                }
+                __syncthreads();
+                find_threshold<kSelNT>(s_hist[hb], need, s_scan, &sh_th);
+                th = sh_th;  // inb > need, so a digit is found
+                prefix = (prefix << w) | (uint32_t)th.digit;
+                need -= th.above;
+                inb = th.in_bucket;
+                pbits += w;
+                hb ^= 1;     // the other histogram is still clear
             }
-            __syncthreads();
-            thr = lds_radix_threshold<kSelNT>(W.cand, th.in_bucket, need, th.digit, W.R);
-        } else {
-            // wide tie band: spill the bucket to the workspace and narrow it there
-            uint64_t* cand = ws.cand_idx + (int64_t)i * n_elem;
-            SelectShared& S = U.big;
-            if (t == 0) S.cnt = 0;
-            __syncthreads();
+        }
+        T = prefix << (32 - pbits);  // lowest key with the final prefix
+        need_eq = inb == need ? INT32_MAX : need;  // the whole bucket, or `need` keys equal to T
+    }
+    // one scan of (keys > T, keys == T) counts ranks the ties at T in element order and
+    // places every selected element (keys above T number < top_k <= 4096, ties <= 32768:
+    // packed 16 + 16 bits)
+    int n_gt = 0, n_eq = 0;
 #pragma unroll
-            for (int j = 0; j < kReEPT; ++j) {
-                const int e = e0 + j;
-                if (j < ept && kv[j] != 0u && (int)(kv[j] >> 21) == th.digit)
-                    cand[atomicAdd(&S.cnt, 1)] = composite(kv[j], (uint32_t)e);
-            }
-            __syncthreads();
-            thr = wg_threshold<kSelNT>(ReindexList{cand, qpool}, th.in_bucket, need, th.digit, S);
+    for (int j = 0; j < EPT; ++j) {
+        if (kv[j] != 0u) {
+            n_gt += kv[j] > T ? 1 : 0;
+            n_eq += kv[j] == T ? 1 : 0;
         }
     }
-    // ordered output: selected = above the bucket, or in it with composite >= thr
-    int cnt = 0;
-    uint32_t selmask = 0u;
-#pragma unroll
-    for (int j = 0; j < kReEPT; ++j) {
-        const int e = e0 + j;
-        bool sel = false;
-        if (j < ept && kv[j] != 0u) {
-            const int dg = (int)(kv[j] >> 21);
-            sel = dg > th.digit ||
-                  (dg == th.digit && composite(kv[j], (uint32_t)(qpool[e >> 3] * 8 + (e & 7))) >= thr);
-        }
-        selmask |= (uint32_t)sel << j;
-        cnt += sel;
-    }
-    int total;
-    int off = block_exclusive_scan<kSelNT>(cnt, U.small.R.scan, total);
+    int tot_pk;
+    const uint32_t pk = (uint32_t)block_exclusive_scan<kSelNT>((int)(((uint32_t)n_gt << 16) | (uint32_t)n_eq),
+                                                              s_scan, tot_pk);
+    int eq_rank = (int)(pk & 0xffffu);
+    int off = (int)(pk >> 16) + min(eq_rank, need_eq);
+    const int total = (int)((uint32_t)tot_pk >> 16) + min((int)((uint32_t)tot_pk & 0xffffu), need_eq);
     int32_t* out = idx_out + (int64_t)i * top_k;
 #pragma unroll
-    for (int j = 0; j < kReEPT; ++j) {
-        if ((selmask >> j) & 1u) {
-            const int e = e0 + j;
-            out[off++] = qpool[e >> 3] * 8 + (e & 7);
+    for (int j = 0; j < EPT; ++j) {
+        if (kv[j] != 0u) {
+            bool sel = kv[j] > T;
+            if (kv[j] == T) sel = eq_rank++ < need_eq;
+            if (sel) out[off++] = pb[j >> 3] * 8 + (j & 7);
         }
     }
     for (int j = total + t; j < top_k; j += kSelNT) out[j] = -1;
@@ -828,8 +835,9 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const uin
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_idx_reindex_select, dim3(n_q), dim3(kSelNT), 0, stream, pool, pool_blocks, top_k, ws,
-                       idx_out);
+    const int ept = (pool_blocks * 8 + kSelNT - 1) / kSelNT;
+    auto sel = ept <= 8 ? k_idx_reindex_select<8> : ept <= 16 ? k_idx_reindex_select<16> : k_idx_reindex_select<32>;
+    hipLaunchKernelGGL(sel, dim3(n_q), dim3(kSelNT), 0, stream, pool, pool_blocks, top_k, ws, idx_out);
     return hipGetLastError();
 }
 
