@@ -159,12 +159,15 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
                                                       const int32_t* __restrict__ kv_len, int n_q, int32_t max_len,
                                                       int64_t cache_rows, int grid_tiles, int grid_ftiles,
                                                       IndexWs ws) {
-    __shared__ int sh_scan[16];
+    __shared__ int sh_scan[kPrepNT / kWave];
+    __shared__ int s_ts[kPrepNT + 1];  // first scan tile of each query of the chunk, then the end
+    __shared__ int s_fs[kPrepNT + 1];  // same for filter tiles
     const int t = threadIdx.x;
     const int cap_s = grid_tiles - n_q, cap_f = grid_ftiles - n_q;
     int run_s = 0, run_f = 0;
     for (int base = 0; base < n_q; base += kPrepNT) {
         const int i = base + t;
+        const int cnt = min(kPrepNT, n_q - base);
         int n = 0, xs = 0, xf = 0;
         if (i < n_q) {
             n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
@@ -186,9 +189,33 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
             m.fntiles = 1 + (f1 - f0);
             m.n = (int)min((int64_t)n, min((int64_t)m.ntiles * kFullTile, (int64_t)m.fntiles * kFilterTile));
             ws.qmeta[i] = m;
-            for (int k = 0; k < m.ntiles; ++k) ws.tmap[m.start + k] = i;
-            for (int k = 0; k < m.fntiles; ++k) ws.fmap[m.fstart + k] = i;
+            // consecutive queries own consecutive tile runs (every query has at least one)
+            s_ts[t] = m.start;
+            s_fs[t] = m.fstart;
+            if (t == cnt - 1) {
+                s_ts[cnt] = m.start + m.ntiles;
+                s_fs[cnt] = m.fstart + m.fntiles;
+            }
         }
+        __syncthreads();
+        // tile -> query maps, written by every thread (largest q with s_ts[q] <= tile)
+        for (int k = s_ts[0] + t; k < s_ts[cnt]; k += kPrepNT) {
+            int lo = 0, hi = cnt - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_ts[mid] <= k) lo = mid; else hi = mid - 1;
+            }
+            ws.tmap[k] = base + lo;
+        }
+        for (int k = s_fs[0] + t; k < s_fs[cnt]; k += kPrepNT) {
+            int lo = 0, hi = cnt - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_fs[mid] <= k) lo = mid; else hi = mid - 1;
+            }
+            ws.fmap[k] = base + lo;
+        }
+        __syncthreads();  // s_ts / s_fs are rewritten by the next chunk
         run_s = min(run_s + tot_s, cap_s + 1);
         run_f = min(run_f + tot_f, cap_f + 1);
     }
