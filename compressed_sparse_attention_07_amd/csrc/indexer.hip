@@ -36,19 +36,21 @@ namespace csa2 {
 
 constexpr int kScoreNT = 256;
 // Scan-kernel shape (compile-time; the defaults are the tuned ones):
-//   CSA2_SCAN_TILE  positions per workgroup, CSA2_SCAN_U  16-row groups per load batch of a wave,
-//   CSA2_SCAN_NT    non-temporal key loads,  CSA2_SCAN_PIPE  prefetch the next batch while computing.
+//   CSA2_SCAN_TILE  positions per tile of the tile map,
+//   CSA2_SCAN_U     64-position steps per load batch (each lane has 2U 16-byte loads in flight),
+//   CSA2_SCAN_NT    streaming (slc) key loads,
+//   CSA2_SCAN_WGS_PER_CU  resident workgroups of the persistent scan per compute unit.
 #ifndef CSA2_SCAN_TILE
 #define CSA2_SCAN_TILE 2048
 #endif
 #ifndef CSA2_SCAN_U
-#define CSA2_SCAN_U 4
+#define CSA2_SCAN_U 8
 #endif
 #ifndef CSA2_SCAN_NT
 #define CSA2_SCAN_NT 0
 #endif
-#ifndef CSA2_SCAN_PIPE
-#define CSA2_SCAN_PIPE 0
+#ifndef CSA2_SCAN_WGS_PER_CU
+#define CSA2_SCAN_WGS_PER_CU 64
 #endif
 constexpr int kFullTile = CSA2_SCAN_TILE;       // positions per Full-scan workgroup
 constexpr int kFullTileBlocks = kFullTile / 8;  // 256 blocks
@@ -76,74 +78,82 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                           false);
 }
 
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+constexpr int kBufWord3 = 0x00020000;  // gfx9 buffer resource word 3: raw 32-bit-format access
+
+// Raw buffer view of `bytes` bytes at p (offsets at or past `bytes` read as zero).  Both
+// arguments must be the same in every lane; they are passed through readfirstlane so the
+// descriptor is built in scalar registers (a descriptor the compiler thinks may vary across
+// lanes costs a waterfall loop per load).
+__device__ __forceinline__ BufRsrc tile_rsrc(const void* p, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
+}
+
+__device__ __forceinline__ uint4 buf_ld16(BufRsrc rs, int voff, int soff) {
 #if CSA2_SCAN_NT
-    typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-    const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
+    constexpr int aux = 2;  // slc: streaming
 #else
-    return *reinterpret_cast<const uint4*>(p);
+    constexpr int aux = 0;
 #endif
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, aux);
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
-__device__ __forceinline__ float quad_sum(float v) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
-    return v;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{v.x, v.y, v.z, v.w});
 }
 
-// This lane's share of the query: heads h < HI, dims [8j, 8j+8) and [32+8j, 32+8j+8).
-template <int HI>
-struct QSlice {
-    uint32_t a[HI][4];
-    uint32_t b[HI][4];
-    float w[HI];
+// Decode and Reindex scoring on MFMA: for 16 positions at a time,
+//   D[head][pos] = Q . K^T  on v_mfma_f32_16x16x32_bf16 (two k-steps cover the 64 channels),
+// with the query's heads on the M rows (zero-padded to 16) and the 16 positions on N.  Lane
+// (g, r) = (lane / 16, lane % 16) supplies head r of Q and position r of K^T with channels
+// 32s + 8g .. 32s + 8g + 7 (one 16-byte load per k-step), and its accumulator holds heads
+// 4g .. 4g + 3 at position r, so lanes 0..15 hold all four heads of their position and the
+// ReLU-weighted head sum needs no cross-lane reduction (heads 4..7 sit in lanes 16..31).
+struct QFrag {
+    bf16x8_t a[2];  // head r, channels 32s + 8g .. + 7
+    float w[4];     // weights of heads 4g .. 4g + 3 (0 past n_heads)
 };
 
-template <int HI>
-__device__ __forceinline__ void load_qslice(QSlice<HI>& qs, const uint16_t* q, const float* w, int n_heads,
-                                            int j) {
+__device__ __forceinline__ void load_qfrag(QFrag& qf, const uint16_t* q, const float* w, int n_heads, int lane) {
+    const int g = lane >> 4, r = lane & 15;
+    const bool hv = r < n_heads;
+    const uint16_t* qp = q + (hv ? r : 0) * 64 + 8 * g;
 #pragma unroll
-    for (int h = 0; h < HI; ++h) {
-        if (h < n_heads) {
-            const uint4 va = *reinterpret_cast<const uint4*>(q + h * 64 + 8 * j);
-            const uint4 vb = *reinterpret_cast<const uint4*>(q + h * 64 + 32 + 8 * j);
-            qs.a[h][0] = va.x; qs.a[h][1] = va.y; qs.a[h][2] = va.z; qs.a[h][3] = va.w;
-            qs.b[h][0] = vb.x; qs.b[h][1] = vb.y; qs.b[h][2] = vb.z; qs.b[h][3] = vb.w;
-            qs.w[h] = w[h];
-        } else {
+    for (int s2 = 0; s2 < 2; ++s2)
+        qf.a[s2] = as_bf16x8(hv ? *reinterpret_cast<const uint4*>(qp + 32 * s2) : make_uint4(0, 0, 0, 0));
 #pragma unroll
-            for (int k = 0; k < 4; ++k) { qs.a[h][k] = 0u; qs.b[h][k] = 0u; }
-            qs.w[h] = 0.0f;
-        }
-    }
+    for (int i = 0; i < 4; ++i) qf.w[i] = (4 * g + i < n_heads) ? w[4 * g + i] : 0.f;
 }
 
-// Score of the row whose two 16-byte slices this lane holds (all 4 lanes of the quad return it).
+// Score of position r in lanes 0..15 (kb: the lane's two 16-byte slices of that position).
 template <int HI>
-__device__ __forceinline__ float row_score(const uint4& A, const uint4& B, const QSlice<HI>& qs) {
-    float s = 0.0f;
+__device__ __forceinline__ float mfma_score(const QFrag& qf, const uint4& k0, const uint4& k1) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.a[0], as_bf16x8(k0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.a[1], as_bf16x8(k1), acc, 0, 0, 0);
+    float s = 0.f;
 #pragma unroll
-    for (int h = 0; h < HI; ++h) {
-        float d = 0.0f;
-        d = dot2(A.x, qs.a[h][0], d);
-        d = dot2(A.y, qs.a[h][1], d);
-        d = dot2(A.z, qs.a[h][2], d);
-        d = dot2(A.w, qs.a[h][3], d);
-        d = dot2(B.x, qs.b[h][0], d);
-        d = dot2(B.y, qs.b[h][1], d);
-        d = dot2(B.z, qs.b[h][2], d);
-        d = dot2(B.w, qs.b[h][3], d);
-        d = quad_sum(d);
-        s = fmaf(qs.w[h], fmaxf(d, 0.0f), s);
-    }
+    for (int i = 0; i < 4; ++i) s = fmaf(qf.w[i], fmaxf(acc[i], 0.f), s);
+    if (HI > 4) s += __shfl_down(s, 16, kWave);  // heads 4..7 from lanes 16..31
     return s;
 }
 
-__device__ __forceinline__ uint32_t max_over_8_quads(uint32_t k) {
-    k = max(k, (uint32_t)__shfl_xor((int)k, 4, kWave));
-    k = max(k, (uint32_t)__shfl_xor((int)k, 8, kWave));
-    k = max(k, (uint32_t)__shfl_xor((int)k, 16, kWave));
+// Largest key of each aligned group of 8 lanes within lanes 0..15, in lanes 4 and 12
+// (quad butterflies, then row_ror:4 brings the quad just below).
+__device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t k) {
+    k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0xB1, 0xF, 0xF, true));
+    k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x4E, 0xF, 0xF, true));
+    k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x124, 0xF, 0xF, true));
     return k;
 }
 
@@ -227,6 +237,10 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
 // ----------------------------------------------------------------------------------------
 // Full mode, kernel 1: scores -> keys, block-max keys, first-digit histograms
 // ----------------------------------------------------------------------------------------
+// Persistent: the grid holds a few workgroups per CU and workgroup g streams the contiguous
+// tile range [g * T / G, (g + 1) * T / G) of the tile map, so the per-tile set-up (tile map,
+// query slice) is paid once per query rather than once per 256 KB tile, and the first-digit
+// histograms go to the workspace only when the query changes.
 template <int HI>
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
@@ -235,91 +249,99 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     __shared__ uint32_t sh_hist[kHistBins];
     __shared__ uint32_t sh_bhist[kHistBins];
 
-    const int i = ws.tmap[blockIdx.x];
-    if (i < 0) return;
-    const QMeta qm = ws.qmeta[i];
     const int t = threadIdx.x;
     const int lane = __lane_id();
     const int wid = t / kWave;
-    const int j = lane & 3;
+    const int g = lane >> 4, r = lane & 15;
     const bool want_pool = pool_blocks > 0;
+    const int tb = (int)((int64_t)blockIdx.x * grid_tiles / gridDim.x);
+    const int te = (int)((int64_t)(blockIdx.x + 1) * grid_tiles / gridDim.x);
 
     for (int b = t; b < kHistBins; b += kScoreNT) {
         sh_hist[b] = 0u;
         sh_bhist[b] = 0u;
     }
-    QSlice<HI> qs;
-    load_qslice<HI>(qs, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, j);
-    __syncthreads();
-
-    const int n = qm.n;
-    const int64_t row0 = kv_row0[i];
-    const int64_t key_base = (int64_t)qm.start * kFullTile;
-    const int p_wave = ((int)blockIdx.x - qm.start) * kFullTile + wid * (kFullTile / 4);
-
-    constexpr int U = CSA2_SCAN_U;
-    constexpr int kBatch = 16 * U;  // rows per wave per batch
-    uint4 A[U], B[U];
-#if CSA2_SCAN_PIPE
-    uint4 A2[U], B2[U];
-#endif
-    auto load_batch = [&](int base, uint4 (&a)[U], uint4 (&bb)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = base + 16 * u + (lane >> 2);
-            const int pc = p < n ? p : n - 1;
-            const uint16_t* row = k_idx + (row0 + pc) * 64;
-            a[u] = ld16(row + 8 * j);
-            bb[u] = ld16(row + 32 + 8 * j);
-        }
-    };
-    auto compute_batch = [&](int base, const uint4 (&a)[U], const uint4 (&bb)[U]) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int p = base + 16 * u + (lane >> 2);
-            const float s = row_score<HI>(a[u], bb[u], qs);
-            const uint32_t key = p < n ? score_key(s) : 0u;
-            if (j == 0 && p < n) {
-                ws.keys[key_base + p] = key;
-                atomicAdd(&sh_hist[key >> 21], 1u);
+    int cur = -1;  // query whose counts the LDS histograms hold
+    QMeta qm{};
+    int64_t row0 = 0;
+    QFrag qf;
+    // add the LDS histograms of query `cur` to the workspace and clear them (after a barrier)
+    auto flush = [&]() {
+        uint32_t* gh = ws.hist + (int64_t)cur * 2 * kHistBins;
+        for (int b = t; b < kHistBins; b += kScoreNT) {
+            const uint32_t h = sh_hist[b];
+            if (h) {
+                atomicAdd(&gh[b], h);
+                sh_hist[b] = 0u;
             }
             if (want_pool) {
-                const uint32_t bk = max_over_8_quads(key);
-                if ((lane & 31) == 0 && p < n) {
-                    ws.bkeys[key_base / 8 + (p >> 3)] = bk;
-                    atomicAdd(&sh_bhist[bk >> 21], 1u);
+                const uint32_t hb = sh_bhist[b];
+                if (hb) {
+                    atomicAdd(&gh[kHistBins + b], hb);
+                    sh_bhist[b] = 0u;
                 }
             }
         }
     };
-#if CSA2_SCAN_PIPE
-    if (p_wave < n) load_batch(p_wave, A, B);
-    for (int b = 0; b < kFullTile / 4; b += 2 * kBatch) {
-        const int base = p_wave + b;
-        if (base >= n) break;
-        if (base + kBatch < n) load_batch(base + kBatch, A2, B2);
-        compute_batch(base, A, B);
-        if (base + kBatch >= n) break;
-        if (base + 2 * kBatch < n && b + 2 * kBatch < kFullTile / 4) load_batch(base + 2 * kBatch, A, B);
-        compute_batch(base + kBatch, A2, B2);
-    }
-#else
-    for (int b = 0; b < kFullTile / 4; b += kBatch) {
-        const int base = p_wave + b;
-        if (base >= n) break;
-        load_batch(base, A, B);
-        compute_batch(base, A, B);
-    }
-#endif
-    __syncthreads();
-    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
-    for (int b = t; b < kHistBins; b += kScoreNT) {
-        const uint32_t h = sh_hist[b];
-        if (h) atomicAdd(&gh[b], h);
-        if (want_pool) {
-            const uint32_t hb = sh_bhist[b];
-            if (hb) atomicAdd(&gh[kHistBins + b], hb);
+
+    // one step = 64 consecutive positions of the workgroup (16 per wave); U steps per batch
+    constexpr int U = CSA2_SCAN_U;
+    for (int tile = tb; tile < te; ++tile) {
+        const int i = ws.tmap[tile];
+        if (i < 0) break;  // unused tiles sit at the end of the map
+        if (i != cur) {
+            __syncthreads();  // every wave's counts of `cur` are in LDS (and the clearing above)
+            if (cur >= 0) {
+                flush();
+                __syncthreads();
+            }
+            cur = i;
+            qm = ws.qmeta[i];
+            row0 = kv_row0[i];
+            load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
         }
+        const int n = qm.n;
+        const int64_t key_base = (int64_t)qm.start * kFullTile;
+        const int p_tile = (tile - qm.start) * kFullTile;
+        if (p_tile >= n) continue;
+        // buffer view of this tile's rows: one 32-bit lane offset for every load (the step goes
+        // in the scalar offset) and rows past the sequence read as zeros
+        const BufRsrc rs = tile_rsrc(k_idx + (row0 + p_tile) * 64, min(n - p_tile, kFullTile) * 128);
+        const int voff = (16 * wid + r) * 128 + 16 * g;
+        for (int b = 0; b < kFullTile; b += 64 * U) {
+            const int pb = p_tile + b;
+            if (pb >= n) break;
+            uint4 kb[U][2];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                kb[u][0] = buf_ld16(rs, voff, (b + 64 * u) * 128);
+                kb[u][1] = buf_ld16(rs, voff + 64, (b + 64 * u) * 128);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p0 = pb + 64 * u + 16 * wid;  // first of this wave's 16 positions
+                const int p = p0 + r;
+                const float sc = mfma_score<HI>(qf, kb[u][0], kb[u][1]);
+                const bool mine = g == 0 && p < n;
+                const uint32_t key = mine ? score_key(sc) : 0u;
+                if (mine) {
+                    ws.keys[key_base + p] = key;
+                    atomicAdd(&sh_hist[key >> 21], 1u);
+                }
+                if (want_pool) {
+                    const uint32_t bk = max_over_8_lanes(key);
+                    const int pblk = p0 + (r & 8);  // the 8-position pool block of lanes 4 / 12
+                    if (g == 0 && (r & 7) == 4 && pblk < n) {
+                        ws.bkeys[key_base / 8 + (pblk >> 3)] = bk;
+                        atomicAdd(&sh_bhist[bk >> 21], 1u);
+                    }
+                }
+            }
+        }
+    }
+    if (cur >= 0) {
+        __syncthreads();
+        flush();
     }
 }
 
@@ -335,13 +357,6 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
 constexpr int kPfQ = 16;       // queries per workgroup
 constexpr int kPfPos = 4096;   // positions per workgroup (1,024 per wave)
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    return __builtin_bit_cast(bf16x8_t, u32x4_t{v.x, v.y, v.z, v.w});
-}
 
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
@@ -637,47 +652,50 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     const int t = threadIdx.x;
     const int lane = __lane_id();
     const int wid = t / kWave;
-    const int j = lane & 3;
+    const int g = lane >> 4, r = lane & 15;
     const int n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
-    const int64_t row0 = kv_row0[i];
+    const int64_t row0 = n > 0 ? kv_row0[i] : 0;
     const int n_elem = pool_blocks * 8;
     const int32_t* qpool = pool + (int64_t)i * pool_blocks;
     uint32_t* keys = ws.keys + (int64_t)i * n_elem;
 
     for (int b = t; b < kHistBins; b += kScoreNT) sh_hist[b] = 0u;
-    QSlice<HI> qs;
-    load_qslice<HI>(qs, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, j);
+    QFrag qf;
+    load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
     __syncthreads();
 
-    const int e_wave = blockIdx.x * kReindexTile + wid * (kReindexTile / 4);
-    for (int b = 0; b < kReindexTile / 4; b += 64) {
-        uint4 A[4], B[4];
-        bool valid[4];
+    // one MFMA unit = two pool slots (16 positions): lanes r < 8 take slot 2m, r >= 8 slot 2m + 1;
+    // this wave takes units m0 + 4u of the workgroup's kReindexTile / 16 units
+    constexpr int kUnits = kReindexTile / 16 / 4;  // units per wave
+    const int m0 = blockIdx.x * (kReindexTile / 16) + wid;
+    int blk[kUnits];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = e_wave + b + 16 * u + (lane >> 2);
-            const int slot = e >> 3;
-            const int blk = slot < pool_blocks ? qpool[slot] : -1;
-            const int64_t p = (int64_t)blk * 8 + (e & 7);
-            valid[u] = blk >= 0 && p < n;
-            if (valid[u]) {
-                const uint16_t* row = k_idx + (row0 + p) * 64;
-                A[u] = *reinterpret_cast<const uint4*>(row + 8 * j);
-                B[u] = *reinterpret_cast<const uint4*>(row + 32 + 8 * j);
-            } else {
-                A[u] = make_uint4(0, 0, 0, 0);
-                B[u] = make_uint4(0, 0, 0, 0);
-            }
+    for (int u = 0; u < kUnits; ++u) {
+        const int slot = 2 * (m0 + 4 * u) + (r >> 3);
+        blk[u] = slot < pool_blocks ? qpool[slot] : -1;
+    }
+    uint4 kb[kUnits][2];
+    if (n > 0) {
+        // absent rows read the sequence's first row (n > 0) and are masked below
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+            const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
+            const bool ok = blk[u] >= 0 && p < n;
+            const uint16_t* row = k_idx + (row0 + (ok ? p : 0)) * 64 + 8 * g;
+            kb[u][0] = *reinterpret_cast<const uint4*>(row);
+            kb[u][1] = *reinterpret_cast<const uint4*>(row + 32);
         }
+    }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int e = e_wave + b + 16 * u + (lane >> 2);
-            const float s = row_score<HI>(A[u], B[u], qs);
-            const uint32_t key = valid[u] ? score_key(s) : 0u;
-            if (j == 0 && e < n_elem) {
-                keys[e] = key;
-                if (key) atomicAdd(&sh_hist[key >> 21], 1u);
-            }
+    for (int u = 0; u < kUnits; ++u) {
+        const int slot = 2 * (m0 + 4 * u) + (r >> 3);
+        const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
+        const bool ok = n > 0 && blk[u] >= 0 && p < n;
+        const float sc = n > 0 ? mfma_score<HI>(qf, kb[u][0], kb[u][1]) : 0.f;
+        const uint32_t key = ok ? score_key(sc) : 0u;
+        if (g == 0 && slot < pool_blocks) {
+            keys[slot * 8 + (r & 7)] = key;
+            if (key) atomicAdd(&sh_hist[key >> 21], 1u);
         }
     }
     __syncthreads();
@@ -809,6 +827,24 @@ __global__ __launch_bounds__(kSelNT) void k_idx_reindex_select(const int32_t* __
 // ----------------------------------------------------------------------------------------
 // host launchers
 // ----------------------------------------------------------------------------------------
+// Workgroups of the persistent scan: a fixed number per compute unit of the current device
+// (looked up once per device).
+static int scan_workgroups() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached[dev] = cus * CSA2_SCAN_WGS_PER_CU;
+    }
+    return cached[dev];
+}
+
+// ----------------------------------------------------------------------------------------
+// (launchers)
+// ----------------------------------------------------------------------------------------
 // phase: 1 = prep + scan kernels, 2 = filter + select kernels, 3 = all.
 // prefill != 0: every query reads the same sequence (kv_row0[0]) and no pool is asked for, so
 // the scores come from the MFMA kernel.
@@ -825,12 +861,11 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16
             const dim3 grid((unsigned)((max_len + kPfPos - 1) / kPfPos), (unsigned)((n_q + kPfQ - 1) / kPfQ));
             hipLaunchKernelGGL(k_idx_score_prefill, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, n_q,
                                cache_rows, n_heads, ws);
-        } else if (n_heads <= 4) {
-            hipLaunchKernelGGL(k_idx_score_full<4>, dim3(grid_tiles), dim3(kScoreNT), 0, stream, q_idx, w, k_idx,
-                               kv_row0, kv_len, n_q, max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
         } else {
-            hipLaunchKernelGGL(k_idx_score_full<8>, dim3(grid_tiles), dim3(kScoreNT), 0, stream, q_idx, w, k_idx,
-                               kv_row0, kv_len, n_q, max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
+            const int wgs = min(grid_tiles, scan_workgroups());
+            auto kern = n_heads <= 4 ? k_idx_score_full<4> : k_idx_score_full<8>;
+            hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, kv_len, n_q,
+                               max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
         }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
