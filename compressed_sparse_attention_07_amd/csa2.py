@@ -24,6 +24,7 @@ SIZE_MAX = (1 << 64) - 1  # csa2_workspace_bytes: sizes out of range
 EXPORTS = (
     "fp4_kv_append",
     "csa2_index_full",
+    "csa2_index_full_prep",
     "csa2_index_full_scan",
     "csa2_index_full_select",
     "csa2_index_reindex",
@@ -65,7 +66,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
         L.fp4_kv_append.argtypes = [vp, i64, i32, vp, i64, vp, vp, i64, vp]
-        for name in ("csa2_index_full", "csa2_index_full_scan", "csa2_index_full_select"):
+        for name in ("csa2_index_full", "csa2_index_full_prep", "csa2_index_full_scan", "csa2_index_full_select"):
             getattr(L, name).argtypes = [vp, vp, vp, SeqsC, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
             getattr(L, name).restype = ctypes.c_int
         L.csa2_index_reindex.argtypes = [vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
@@ -162,6 +163,13 @@ def csa2_index_full(q_idx, w, k_idx, seqs: Seqs, top_k: int, pool_blocks: int, i
     n_heads = q_idx.shape[1]
     _check("csa2_index_full", lib().csa2_index_full(
         _ptr(q_idx), _ptr(w), _ptr(k_idx), seqs.c(), n_heads, top_k, block, pool_blocks, shared_kv,
+        _ptr(idx_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def csa2_index_full_prep(q_idx, w, k_idx, seqs: Seqs, top_k: int, pool_blocks: int, idx_out, pool_out, ws,
+                         block: int = BLOCK, shared_kv: int = 0, stream=None) -> None:
+    _check("csa2_index_full_prep", lib().csa2_index_full_prep(
+        _ptr(q_idx), _ptr(w), _ptr(k_idx), seqs.c(), q_idx.shape[1], top_k, block, pool_blocks, shared_kv,
         _ptr(idx_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 

@@ -204,21 +204,28 @@ int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
                     int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
                     int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
     return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
-                            ws, ws_bytes, stream, 3);
+                            ws, ws_bytes, stream, 7);
 }
 
-int csa2_index_full_scan(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
+int csa2_index_full_prep(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
                          int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
                          int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
     return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
                             ws, ws_bytes, stream, 1);
 }
 
+int csa2_index_full_scan(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
+                         int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
+                         int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
+    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
+                            ws, ws_bytes, stream, 2);
+}
+
 int csa2_index_full_select(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
                            int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
                            int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
     return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
-                            ws, ws_bytes, stream, 2);
+                            ws, ws_bytes, stream, 4);
 }
 
 int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,

@@ -845,9 +845,10 @@ static int scan_workgroups() {
 // ----------------------------------------------------------------------------------------
 // (launchers)
 // ----------------------------------------------------------------------------------------
-// phase: 1 = prep + scan kernels, 2 = filter + select kernels, 3 = all.
+// phase bits: 1 = prep kernel (per-query metadata and tile maps), 2 = scan kernel,
+// 4 = filter + select kernels; 7 = all.
 // prefill != 0: every query reads the same sequence (kv_row0[0]) and no pool is asked for, so
-// the scores come from the MFMA kernel.
+// the scores come from the MFMA kernel that tiles 16 queries x 16 positions.
 hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
                              const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
                              int grid_tiles, int grid_ftiles, int top_k, int pool_blocks, int prefill,
@@ -857,6 +858,8 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16
                            grid_tiles, grid_ftiles, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    }
+    if (phase & 2) {
         if (prefill) {
             const dim3 grid((unsigned)((max_len + kPfPos - 1) / kPfPos), (unsigned)((n_q + kPfQ - 1) / kPfQ));
             hipLaunchKernelGGL(k_idx_score_prefill, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, n_q,
@@ -867,10 +870,10 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16
             hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, kv_len, n_q,
                                max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
         }
-        e = hipGetLastError();
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (phase & 2) {
+    if (phase & 4) {
         hipLaunchKernelGGL(k_idx_filter_full, dim3(grid_ftiles), dim3(kScoreNT), 0, stream, kv_row0, kv_len, n_q,
                            max_len, cache_rows, grid_tiles, grid_ftiles, top_k, pool_blocks, ws);
         hipError_t e = hipGetLastError();

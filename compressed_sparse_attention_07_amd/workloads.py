@@ -225,10 +225,12 @@ class Runner:
             if L.mode == "F":
                 want_pool = wl.pool_blocks if (self.pool is not None and not pool_built) else 0
                 pool = self.pool if want_pool else None
+                shared = 1 if wl.prefill_chunk else 0   # a prefill chunk: all queries read one sequence
+                C.csa2_index_full_prep(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
+                                       self.ws_full, shared_kv=shared, stream=stream)
                 if scan_events is not None:
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record()
-                shared = 1 if wl.prefill_chunk else 0   # a prefill chunk: all queries read one sequence
                 C.csa2_index_full_scan(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
                                        self.ws_full, shared_kv=shared, stream=stream)
                 if scan_events is not None:

@@ -128,9 +128,9 @@ int fp4_kv_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64_t* 
  *   pool_out device int32 [n_q, pool_blocks] or NULL when pool_blocks == 0: block
  *           ids under (block max desc, block asc), ascending, -1 padded.
  * Score of position p: sum_h w[h] * max(0, q_h . k_p), accumulated in fp32; with
- * integer-valued inputs and |score| < 2^24 it is exact.  The scan is on vector
- * ALUs when n_q is small; a prefill chunk (shared_kv != 0: every query has the same
- * kv_row0) may use the MFMA path.  n_q == 0 is a no-op.
+ * integer-valued inputs and |score| < 2^24 it is exact.  Scores are MFMA
+ * contractions: heads x positions per query, or, for a prefill chunk (shared_kv != 0:
+ * every query has the same kv_row0), queries x positions.  n_q == 0 is a no-op.
  */
 int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
                     int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
@@ -138,13 +138,18 @@ int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
                     size_t ws_bytes, void* stream);
 
 /*
- * The two halves of csa2_index_full, for callers that time or schedule them apart:
+ * The three parts of csa2_index_full, for callers that time or schedule them apart:
+ * _prep writes per-query metadata and the tile maps to the workspace (one kernel);
  * _scan scores every visible position (fused block maxima and first-digit
  * histograms, one kernel); _select compacts the threshold buckets and writes idx_out
  * and pool_out (two kernels: a filter over all positions, then one workgroup per
- * query and output).  Call _select after _scan, on the same stream, with
- * identical arguments and workspace; together they equal one csa2_index_full call.
+ * query and output).  Call them in this order, on the same stream, with identical
+ * arguments and workspace; together they equal one csa2_index_full call.
  */
+int csa2_index_full_prep(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
+                         int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
+                         int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws,
+                         size_t ws_bytes, void* stream);
 int csa2_index_full_scan(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
                          int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
                          int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws,
