@@ -29,7 +29,10 @@ design notes of this repository):
   * ties in every ranking go to the lower position (or block) index;
   * selection outputs are in ascending index order, padded with -1;
   * attention is one softmax over the selected entries followed by the window
-    entries (no de-duplication), with keys equal to values.
+    entries (no de-duplication), with keys equal to values;
+  * an FP8 window stores each value as the nearest E4M3 ('fn') value, ties to even,
+    saturating at +-448 (the format has no infinity), with the value's sign bit and no
+    scale; a replay start s limits a query's window to positions >= s.
 """
 from __future__ import annotations
 
@@ -222,6 +225,37 @@ def index_reindex(q_bf16, w, k_bf16_seq, n: int, pool: np.ndarray, top_k: int, b
 # ---------------------------------------------------------------------------
 
 
+def e4m3_quantize(x_bf16: np.ndarray) -> np.ndarray:
+    """bf16 bits (any shape) -> E4M3 ('fn') bytes ([Article] section XI: the recent-window cache
+    stays at FP8).  Each value becomes the nearest finite E4M3 value (distances |v - |x|| are
+    exact in fp64), ties to the even code; magnitudes beyond 448 saturate to 448; bit 7 is
+    the input's sign bit (so -0 -> 0x80)."""
+    xb = np.asarray(x_bf16, dtype=np.uint16)
+    # saturate first: past 448 the distances below would no longer be exact in fp64
+    mag = np.minimum(np.abs(bf16_to_f64(xb)), 448.0).ravel()
+    out = np.empty(mag.shape, dtype=np.uint8)
+    for c0 in range(0, mag.size, 1 << 15):       # chunks only bound host memory
+        a = mag[c0:c0 + (1 << 15)]
+        out[c0:c0 + a.size] = _nearest_even(np.abs(E4M3_NONNEG[None, :] - a[:, None]))
+    sign = ((xb >> 15) & 1).astype(np.uint8).ravel()
+    return (out | (sign << 7)).reshape(xb.shape)
+
+
+def e4m3_dequantize(codes: np.ndarray) -> np.ndarray:
+    """fp64 values of E4M3 ('fn') bytes."""
+    table = np.array([e4m3_value(k) for k in range(256)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8)]
+
+
+def _attend_rows(q: np.ndarray, kv: np.ndarray, softmax_scale: float) -> np.ndarray:
+    """Softmax attention of the [H, D] query over the rows of kv (keys = values), fp64."""
+    logits = (q @ kv.T) * softmax_scale              # [H, E]
+    logits -= logits.max(axis=1, keepdims=True)
+    p = np.exp(logits)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ kv
+
+
 def attend(q_bf16: np.ndarray, codes_seq: np.ndarray, scales_seq: np.ndarray, n: int,
            idx: np.ndarray, swa_bf16: np.ndarray, swa_row0: int, swa_cap: int,
            window: int, softmax_scale: float) -> np.ndarray:
@@ -246,11 +280,46 @@ def attend(q_bf16: np.ndarray, codes_seq: np.ndarray, scales_seq: np.ndarray, n:
     if not rows:
         return np.zeros_like(q)
     kv = np.concatenate(rows, axis=0)                # [E, D]
-    logits = (q @ kv.T) * softmax_scale              # [H, E]
-    logits -= logits.max(axis=1, keepdims=True)
-    p = np.exp(logits)
-    p /= p.sum(axis=1, keepdims=True)
-    return p @ kv
+    return _attend_rows(q, kv, softmax_scale)
+
+
+def window_positions(n: int, window: int, replay_start: int = 0) -> list:
+    """Window of the query that sees [0, n): positions [max(replay_start, n - window), n)
+    ([Article] section XII, SWA Bounded Replay: a query at position i attends window keys
+    in [max(s, i - win + 1), i]; the decode query is position i = n - 1)."""
+    return list(range(max(0, replay_start, n - window), n))
+
+
+def attend_fp8_window(q_bf16: np.ndarray, codes_seq: np.ndarray, scales_seq: np.ndarray, n: int,
+                      idx: np.ndarray, swa_e4m3: np.ndarray, swa_row0: int, swa_cap: int,
+                      window: int, softmax_scale: float, replay_start: int = 0) -> np.ndarray:
+    """As attend(), with the window read from an E4M3 store ([Article] section XI) and limited
+    by a replay start ([Article] section XII): the window is window_positions(n, window,
+    replay_start); position p at row swa_row0 + (p mod swa_cap)."""
+    q = bf16_to_f64(q_bf16)
+    sel = [int(j) for j in np.asarray(idx).ravel() if 0 <= int(j) < n]
+    win = window_positions(n, window, replay_start)
+    rows = []
+    if sel:
+        rows.append(fp4_dequantize(codes_seq[sel], scales_seq[sel]))
+    if win:
+        rows.append(e4m3_dequantize(swa_e4m3[[swa_row0 + (p % swa_cap) for p in win]]))
+    if not rows:
+        return np.zeros_like(q)
+    return _attend_rows(q, np.concatenate(rows, axis=0), softmax_scale)
+
+
+def attended_max_abs_fp8(codes_seq, scales_seq, n, idx, swa_e4m3, swa_row0, swa_cap, window,
+                         replay_start=0) -> float:
+    """max |v| over the entries attend_fp8_window attends to."""
+    sel = [int(j) for j in np.asarray(idx).ravel() if 0 <= int(j) < n]
+    m = 0.0
+    if sel:
+        m = max(m, float(np.abs(fp4_dequantize(codes_seq[sel], scales_seq[sel])).max()))
+    win = window_positions(n, window, replay_start)
+    if win:
+        m = max(m, float(np.abs(e4m3_dequantize(swa_e4m3[[swa_row0 + (p % swa_cap) for p in win]])).max()))
+    return m
 
 
 def attended_max_abs(codes_seq, scales_seq, n, idx, swa_bf16, swa_row0, swa_cap, window) -> float:
