@@ -23,12 +23,14 @@ SIZE_MAX = (1 << 64) - 1  # csa2_workspace_bytes: sizes out of range
 
 EXPORTS = (
     "fp4_kv_append",
+    "fp8_window_append",
     "csa2_index_full",
     "csa2_index_full_prep",
     "csa2_index_full_scan",
     "csa2_index_full_select",
     "csa2_index_reindex",
     "csa2_attend",
+    "csa2_attend_fp8win",
     "csa2_workspace_bytes",
     "csa2_workspace_init",
     "csa2_status_string",
@@ -71,14 +73,17 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = ctypes.c_int
         L.csa2_index_reindex.argtypes = [vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
         L.csa2_attend.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, i32, f32, vp, vp, sz, vp]
+        L.fp8_window_append.argtypes = [vp, i64, i32, vp, i64, vp, i64, vp]
+        L.csa2_attend_fp8win.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp,
+                                         sz, vp]
         L.csa2_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
         L.csa2_workspace_bytes.restype = sz
         L.csa2_workspace_init.argtypes = [vp, sz, vp]
         L.csa2_status_string.argtypes = [ctypes.c_int]
         L.csa2_status_string.restype = ctypes.c_char_p
         L.csa2_version.argtypes = []
-        for name in ("fp4_kv_append", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
-                     "csa2_workspace_init", "csa2_version"):
+        for name in ("fp4_kv_append", "fp8_window_append", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
+                     "csa2_attend_fp8win", "csa2_workspace_init", "csa2_version"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -137,6 +142,13 @@ def fp4_kv_append(x, codes, scales, dst_rows=None, row0: int = 0, stream=None) -
     n_tok, dim = x.shape
     _check("fp4_kv_append", lib().fp4_kv_append(_ptr(x), n_tok, dim, _ptr(dst_rows), row0, _ptr(codes),
                                                 _ptr(scales), codes.shape[0], _stream(stream)))
+
+
+def fp8_window_append(x, out, dst_rows=None, row0: int = 0, stream=None) -> None:
+    """Convert x (bf16 [n_tok, dim]) to E4M3 bytes in rows of an FP8 window store (uint8 [rows, dim])."""
+    n_tok, dim = x.shape
+    _check("fp8_window_append", lib().fp8_window_append(_ptr(x), n_tok, dim, _ptr(dst_rows), row0, _ptr(out),
+                                                        out.shape[0], _stream(stream)))
 
 
 def csa2_workspace_bytes(op: int, n_q: int, total_len_ub: int = 0, max_len_ub: int = 0, top_k: int = 0,
@@ -204,3 +216,14 @@ def csa2_attend(q, codes, scales, seqs: Seqs, idx, swa, swa_row0, swa_cap: int, 
         _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa), _ptr(swa_row0), swa_cap,
         swa_rows, window, n_heads, ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws), ws.numel(),
         _stream(stream)))
+
+
+def csa2_attend_fp8win(q, codes, scales, seqs: Seqs, idx, swa8, swa_row0, swa_cap: int, window: int,
+                       softmax_scale: float, out, ws, replay_start=None, stream=None) -> None:
+    n_heads = q.shape[1]
+    top_k = idx.shape[1] if idx is not None else 0
+    swa_rows = swa8.shape[0] if swa8 is not None else 0
+    _check("csa2_attend_fp8win", lib().csa2_attend_fp8win(
+        _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa8), _ptr(swa_row0), swa_cap,
+        swa_rows, window, _ptr(replay_start), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws),
+        ws.numel(), _stream(stream)))

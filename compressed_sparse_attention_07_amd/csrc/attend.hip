@@ -52,6 +52,7 @@ static_assert(kNH * kOStride * 4 <= kTileB, "a wave's merge rows fit in its tile
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -111,12 +112,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 // kFp4: top_k > 0 (the FP4 cache is read); kWin: window > 0 and the window store has rows.
 // Both are fixed per launch so that every gather below is unconditional (clamped addresses,
 // masked results): loads under branches make the compiler wait on some of them early.
-template <bool kFp4, bool kWin>
+// kW8: the window store holds E4M3 bytes ([Article] section XI keeps the recent-window cache
+// in FP8); they are converted to f16 exactly and take the FP4 entries' f16 path.
+// replay (may be NULL): per-query replay start s; the window then holds only positions >= s
+// ([Article] section XII, SWA Bounded Replay).
+template <bool kFp4, bool kWin, bool kW8>
 __global__ __launch_bounds__(kAttNT) void k_attend(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len, int32_t max_len, int64_t cache_rows,
-    const int32_t* __restrict__ idx, int top_k, const uint16_t* __restrict__ swa, const int64_t* __restrict__ swa_row0,
-    int swa_cap, int64_t swa_rows, int window, int n_heads, float scale_log2, float* __restrict__ out) {
+    const int32_t* __restrict__ idx, int top_k, const void* __restrict__ swa, const int64_t* __restrict__ swa_row0,
+    int swa_cap, int64_t swa_rows, int window, const int64_t* __restrict__ replay, int n_heads, float scale_log2,
+    float* __restrict__ out) {
     __shared__ __align__(16) uint8_t s_tile[kAttWaves][kTileB];
     __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
 
@@ -127,7 +133,11 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
     const int g = l >> 4;   // lane group
     const int r = l & 15;   // row / column within the 16
     const int n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
-    const int wc = min(window, n);
+    int wc = min(window, n);  // window = the last wc positions of [0, n)
+    if (replay != nullptr) {
+        const int64_t s0 = replay[i] > 0 ? replay[i] : 0;
+        wc = (int)max((int64_t)0, min((int64_t)wc, (int64_t)n - s0));
+    }
     const int64_t row0 = n > 0 ? kv_row0[i] : 0;
     const bool win_ok = kWin && wc > 0;
     const int64_t wrow0 = win_ok ? swa_row0[i] : 0;
@@ -137,7 +147,7 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
 
     // ---- the round's index and window gathers: round 0's go out before the query is read ----
     int pos[kRB];     // selected positions of this lane's entry in each FP4 block (-1: none)
-    u32x4 wf[4];      // window entry: channels [32g, 32g+32) as bf16
+    u32x4 wf[4];      // window entry: channels [32g, 32g+32) as bf16 (E4M3: wf[0..1] hold them)
     bool wvalid = false;
     auto issue_round = [&](int R) {
         const int b0 = R * kRoundFp4 + wave * kRB;
@@ -156,11 +166,22 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
         }
         wvalid = sr >= 0;
         // rows of absent entries are clamped to row 0 (kWin: the store has rows) and masked
-        const uint4* src = reinterpret_cast<const uint4*>(swa + (wvalid ? sr : 0) * kD + 32 * g);
+        const int64_t wr = wvalid ? sr : 0;
+        if constexpr (kW8) {
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(swa) + wr * kD + 32 * g);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const uint4 v = kWin ? src[s] : make_uint4(0, 0, 0, 0);
-            wf[s] = u32x4{v.x, v.y, v.z, v.w};
+            for (int s = 0; s < 2; ++s) {
+                const uint4 v = kWin ? src[s] : make_uint4(0, 0, 0, 0);
+                wf[s] = u32x4{v.x, v.y, v.z, v.w};
+            }
+            wf[2] = wf[3] = u32x4{0u, 0u, 0u, 0u};
+        } else {
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(swa) + wr * kD + 32 * g);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint4 v = kWin ? src[s] : make_uint4(0, 0, 0, 0);
+                wf[s] = u32x4{v.x, v.y, v.z, v.w};
+            }
         }
     };
     issue_round(0);
@@ -246,10 +267,29 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
             sa[j] = acc;
         }
         f32x4 swc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kW8) {
+            // E4M3 -> f16 (exact): fragment s = channels 32g + 8s .. + 7 = bytes 8s .. 8s + 7
+            u32x4 wh[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            swc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[s]),
-                                                          __builtin_bit_cast(bf16x8, qb[s]), swc, 0, 0, 0);
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t d0 = wf[s >> 1][2 * (s & 1)], d1 = wf[s >> 1][2 * (s & 1) + 1];
+                wh[s] = u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, false)),
+                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d0, 1.0f, true)),
+                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, false)),
+                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d1, 1.0f, true))};
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                wf[s] = wh[s];
+                swc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, wf[s]),
+                                                             __builtin_bit_cast(f16x8, qh[s]), swc, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                swc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[s]),
+                                                              __builtin_bit_cast(bf16x8, qb[s]), swc, 0, 0, 0);
+        }
         // logits of head r for entries 4g + ii of each block (log2 units), masked
         float x[kRB + 1][4];
         float mx = -INFINITY;
@@ -259,7 +299,7 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
             for (int ii = 0; ii < 4; ++ii) {
                 const uint32_t bits = j < kRB ? vb[j] : vbw;
                 const bool ok = (bits >> (4 * g + ii)) & 1u;
-                const float v = j < kRB ? sa[j][ii] * cf4 : swc[ii] * scale_log2;
+                const float v = j < kRB ? sa[j][ii] * cf4 : swc[ii] * (kW8 ? cf4 : scale_log2);
                 x[j][ii] = ok ? v : -INFINITY;
                 mx = fmaxf(mx, x[j][ii]);
             }
@@ -275,7 +315,7 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
             for (int db = 0; db < 8; ++db) o[db] *= alpha;
         }
         m_run = m_new;
-        // probabilities: f16 for FP4 entries, bf16 hi + lo for window entries
+        // probabilities: f16 for FP4 (and E4M3 window) entries, bf16 hi + lo for bf16 window entries
         uint32_t ph[kRB][2], pwh[2], pwl[2];
         float psum = 0.f;
 #pragma unroll
@@ -289,6 +329,10 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
             if (j < kRB) {
                 ph[j][0] = f16pair(p[0], p[1]);
                 ph[j][1] = f16pair(p[2], p[3]);
+            } else if (kW8) {
+                pwh[0] = f16pair(p[0], p[1]);
+                pwh[1] = f16pair(p[2], p[3]);
+                pwl[0] = pwl[1] = 0u;
             } else {
                 uint32_t h[4], lo[4];
 #pragma unroll
@@ -335,8 +379,13 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
                 const s16x4 a = lds_tr16(tile + tr_off + 32 * db);
-                o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, hv2), o[db], 0, 0, 0);
-                o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, lv2), o[db], 0, 0, 0);
+                if constexpr (kW8) {
+                    o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                                  __builtin_bit_cast(f16x4, hv2), o[db], 0, 0, 0);
+                } else {
+                    o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, hv2), o[db], 0, 0, 0);
+                    o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4, lv2), o[db], 0, 0, 0);
+                }
             }
             wave_lds_sync();
         }
@@ -376,16 +425,24 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
     }
 }
 
+// window_fp8: the window store holds E4M3 bytes; replay: per-query replay starts or NULL.
 hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const int64_t* kv_row0,
                          const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
-                         int top_k, const uint16_t* swa, const int64_t* swa_row0, int swa_cap, int64_t swa_rows,
-                         int window, int n_heads, float softmax_scale, float* out, hipStream_t stream) {
+                         int top_k, const void* swa, int window_fp8, const int64_t* swa_row0, int swa_cap,
+                         int64_t swa_rows, int window, const int64_t* replay, int n_heads, float softmax_scale,
+                         float* out, hipStream_t stream) {
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
     const bool fp4 = top_k > 0, win = window > 0 && swa_rows > 0;
-    auto kern = fp4 ? (win ? k_attend<true, true> : k_attend<true, false>)
-                    : (win ? k_attend<false, true> : k_attend<false, false>);
+    decltype(&k_attend<true, true, false>) kern;
+    if (window_fp8)
+        kern = fp4 ? (win ? k_attend<true, true, true> : k_attend<true, false, true>)
+                   : (win ? k_attend<false, true, true> : k_attend<false, false, true>);
+    else
+        kern = fp4 ? (win ? k_attend<true, true, false> : k_attend<true, false, false>)
+                   : (win ? k_attend<false, true, false> : k_attend<false, false, false>);
     hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, q, codes, scales, kv_row0, kv_len, max_len,
-                       cache_rows, idx, top_k, swa, swa_row0, swa_cap, swa_rows, window, n_heads, scale_log2, out);
+                       cache_rows, idx, top_k, swa, swa_row0, swa_cap, swa_rows, window, replay, n_heads, scale_log2,
+                       out);
     return hipGetLastError();
 }
 

@@ -51,10 +51,13 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const uin
                                 const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
                                 const int32_t* pool, int pool_blocks, int top_k, const IndexWs& ws, int32_t* idx_out,
                                 hipStream_t stream);
+hipError_t launch_fp8_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
+                           uint8_t* out, int64_t cap_rows, hipStream_t stream);
 hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const int64_t* kv_row0,
                          const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
-                         int top_k, const uint16_t* swa, const int64_t* swa_row0, int swa_cap, int64_t swa_rows,
-                         int window, int n_heads, float softmax_scale, float* out, hipStream_t stream);
+                         int top_k, const void* swa, int window_fp8, const int64_t* swa_row0, int swa_cap,
+                         int64_t swa_rows, int window, const int64_t* replay, int n_heads, float softmax_scale,
+                         float* out, hipStream_t stream);
 hipError_t launch_zero(void* ws, size_t bytes, hipStream_t stream);
 
 namespace {
@@ -143,6 +146,18 @@ int fp4_kv_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64_t* 
     if (n_tok > ((int64_t)1 << 40)) return CSA2_ERR_SHAPE;
     if (dst_rows == nullptr && (row0 < 0 || row0 > cap_rows || n_tok > cap_rows - row0)) return CSA2_ERR_CAPACITY;
     return launch_status(launch_fp4_pack(x, n_tok, dim, dst_rows, row0, codes, scales, cap_rows,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int fp8_window_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64_t* dst_rows, int64_t row0,
+                      uint8_t* out, int64_t cap_rows, void* stream) {
+    if (n_tok < 0 || dim <= 0 || dim % 8 != 0 || dim > 1024 || cap_rows < 0) return CSA2_ERR_SHAPE;
+    if (n_tok == 0) return CSA2_OK;
+    if (x == nullptr || out == nullptr) return CSA2_ERR_NULL;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(out) & 7u) != 0) return CSA2_ERR_SHAPE;
+    if (n_tok > ((int64_t)1 << 40)) return CSA2_ERR_SHAPE;
+    if (dst_rows == nullptr && (row0 < 0 || row0 > cap_rows || n_tok > cap_rows - row0)) return CSA2_ERR_CAPACITY;
+    return launch_status(launch_fp8_pack(x, n_tok, dim, dst_rows, row0, out, cap_rows,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -250,10 +265,10 @@ int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_
                                               static_cast<hipStream_t>(stream)));
 }
 
-int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs, const int32_t* idx,
-                int32_t top_k, const uint16_t* swa, const int64_t* swa_row0, int32_t swa_cap, int64_t swa_rows,
-                int32_t window, int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes,
-                void* stream) {
+static int attend_common(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const csa2_seqs& seqs,
+                         const int32_t* idx, int32_t top_k, const void* swa, int window_fp8, const int64_t* swa_row0,
+                         int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay, int32_t n_heads,
+                         float softmax_scale, float* out, void* stream) {
     int st = check_seqs(seqs);
     if (st) return st;
     if (top_k < 0 || top_k > CSA2_MAX_SELECT || window < 0 || window > CSA2_MAX_WINDOW || n_heads < 1 ||
@@ -269,11 +284,30 @@ int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, 
     if (!aligned16(q) || (codes && !aligned16(codes)) || (swa && !aligned16(swa)) ||
         (scales && (reinterpret_cast<uintptr_t>(scales) & 1u)))
         return CSA2_ERR_SHAPE;
+    return launch_status(launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
+                                       seqs.cache_rows, idx, top_k, swa, window_fp8, swa_row0,
+                                       window > 0 ? swa_cap : 1, swa_rows, window, replay, n_heads, softmax_scale,
+                                       out, static_cast<hipStream_t>(stream)));
+}
+
+int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs, const int32_t* idx,
+                int32_t top_k, const uint16_t* swa, const int64_t* swa_row0, int32_t swa_cap, int64_t swa_rows,
+                int32_t window, int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                void* stream) {
     (void)ws;
     (void)ws_bytes;
-    return launch_status(launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
-                                       seqs.cache_rows, idx, top_k, swa, swa_row0, window > 0 ? swa_cap : 1, swa_rows,
-                                       window, n_heads, softmax_scale, out, static_cast<hipStream_t>(stream)));
+    return attend_common(q, codes, scales, seqs, idx, top_k, swa, 0, swa_row0, swa_cap, swa_rows, window, nullptr,
+                         n_heads, softmax_scale, out, stream);
+}
+
+int csa2_attend_fp8win(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
+                       const int32_t* idx, int32_t top_k, const uint8_t* swa, const int64_t* swa_row0,
+                       int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay_start,
+                       int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    return attend_common(q, codes, scales, seqs, idx, top_k, swa, 1, swa_row0, swa_cap, swa_rows, window,
+                         replay_start, n_heads, softmax_scale, out, stream);
 }
 
 int csa2_workspace_init(void* ws, size_t bytes, void* stream) {

@@ -100,4 +100,57 @@ hipError_t launch_fp4_pack(const uint16_t* x, int64_t n_tok, int dim, const int6
     return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------------------
+// FP8 window store ([Article] section XI: the recent-window cache stays at FP8): each bf16
+// value becomes the nearest E4M3 ("fn") value, ties to even, saturating at 448 (the format
+// has no infinity), keeping the value's sign bit.  Exact integer rounding of the bf16
+// fields: normal E4M3 targets round the 7-bit mantissa to 3 bits (a carry moves into the
+// exponent by plain addition: codes are ordered like values); below 2^-6 the code is the
+// subnormal count RNE(|x| * 2^9), exact in fp32.  One thread converts 8 channels.
+// ----------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t e4m3_code_of_bf16(uint32_t b) {
+    const uint32_t a = b & 0x7fffu;
+    uint32_t c;
+    if (a >= 0x43E0u) {  // |x| >= 448 (and inf): saturate
+        c = 0x7Eu;
+    } else if (a >= 0x3C80u) {  // |x| >= 2^-6: normal target, biased exponent (a >> 7) - 120
+        const uint32_t m3 = (a >> 4) & 7u, r = a & 0xFu;
+        const uint32_t up = (r > 8u || (r == 8u && (m3 & 1u))) ? 1u : 0u;
+        c = ((((a >> 7) - 120u) << 3) | m3) + up;  // < 0x7F: a < 0x43E0 leaves m3 + up <= 6 at exponent 15
+    } else {
+        c = (uint32_t)__builtin_rintf(__uint_as_float(a << 16) * 512.0f);  // 0..8, 8 = 2^-6 = code 0x08
+    }
+    return c | ((b >> 8) & 0x80u);
+}
+
+__global__ __launch_bounds__(256) void k_fp8_pack(const uint16_t* __restrict__ x, int64_t n_tok, int dim,
+                                                  const int64_t* __restrict__ dst_rows, int64_t row0,
+                                                  uint8_t* __restrict__ out, int64_t cap_rows) {
+    const int octs = dim >> 3;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= n_tok * octs) return;
+    const int64_t t = gid / octs;
+    const int k = (int)(gid - t * octs);
+    const int64_t row = dst_rows ? dst_rows[t] : row0 + t;
+    if (row < 0 || row >= cap_rows) return;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + t * dim + k * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        lo |= (e4m3_code_of_bf16(w[j] & 0xffffu) | (e4m3_code_of_bf16(w[j] >> 16) << 8)) << (16 * j);
+        hi |= (e4m3_code_of_bf16(w[j + 2] & 0xffffu) | (e4m3_code_of_bf16(w[j + 2] >> 16) << 8)) << (16 * j);
+    }
+    *reinterpret_cast<uint2*>(out + row * dim + k * 8) = make_uint2(lo, hi);
+}
+
+hipError_t launch_fp8_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
+                           uint8_t* out, int64_t cap_rows, hipStream_t stream) {
+    const int64_t total = n_tok * (dim >> 3);
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(k_fp8_pack, dim3((unsigned)blocks), dim3(256), 0, stream, x, n_tok, dim, dst_rows, row0, out,
+                       cap_rows);
+    return hipGetLastError();
+}
+
 }  // namespace csa2

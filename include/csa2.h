@@ -112,6 +112,20 @@ int fp4_kv_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64_t* 
                   int64_t row0, uint8_t* codes, uint8_t* scales, int64_t cap_rows, void* stream);
 
 /*
+ * fp8_window_append -- write bf16 vectors into an FP8 window store.
+ * [Article] section XI (the recent-window cache stays at FP8, E4M3).
+ *
+ *   x        device bf16 [n_tok, dim], 16-byte aligned; dim % 8 == 0, <= 1024.
+ *   dst_rows device int64 [n_tok] or NULL (rows row0 .. row0 + n_tok - 1).
+ *   out      device uint8 [cap_rows, dim], 8-byte aligned: E4M3 ("fn") bytes.
+ * Each value becomes the nearest E4M3 value, ties to even, saturating at +-448 (the
+ * format has no infinity), with the value's sign bit; no scale.  Rows outside
+ * [0, cap_rows) named by dst_rows are skipped.  n_tok == 0 is a no-op.
+ */
+int fp8_window_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64_t* dst_rows,
+                      int64_t row0, uint8_t* out, int64_t cap_rows, void* stream);
+
+/*
  * csa2_index_full -- Full-mode indexer for n_q queries.
  * [Article] section IX (the Full layer scores every causally visible position,
  * scores 8-position blocks by their best position and keeps the winning blocks as
@@ -203,6 +217,25 @@ int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, 
                 const int32_t* idx, int32_t top_k, const uint16_t* swa, const int64_t* swa_row0,
                 int32_t swa_cap, int64_t swa_rows, int32_t window, int32_t n_heads,
                 float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_attend_fp8win -- csa2_attend with the pages' window format and replay bound.
+ * [Article] section XI (the recent-window cache stays at FP8) and section XII (SWA
+ * Bounded Replay: for a replay starting at position s, the query at position i
+ * attends window keys in [max(s, i - win + 1), i]).
+ *
+ *   swa           device uint8 [swa_rows, CSA2_KV_DIM]: E4M3 bytes written by
+ *                 fp8_window_append (the codes 0x7f / 0xff, NaN, are never written).
+ *   replay_start  device int64 [n_q] or NULL (no bound): query i's window is
+ *                 positions [max(replay_start[i], N_i - window, 0), N_i).
+ * Every other argument, the layouts, the errors and the output are those of
+ * csa2_attend.  Window values and FP4 values enter the contractions exactly (f16).
+ */
+int csa2_attend_fp8win(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
+                       const int32_t* idx, int32_t top_k, const uint8_t* swa, const int64_t* swa_row0,
+                       int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay_start,
+                       int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /*
  * Workspace bytes for one call of `op` (CSA2_OP_*) with these sizes; SIZE_MAX if the
