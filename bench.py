@@ -10,7 +10,8 @@ Prints ONE JSON line.  `value` is decode tokens/s of the batched 64K-context wor
 captured in HIP graphs (the host issues one launch per step); the 1M-context workload (8 x 2^20,
 20 layers) is reported in the same line under "also".  `roofline` covers the dominant kernel
 (the Full-mode scan), timed with HIP events around each of its launches in K eager steps.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.  The 64K workload
+`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.  "also" further
+holds the 1M-context workload with the pages' FP8 window store and SWA Bounded Replay starts.  The 64K workload
 rotates two device copies of its inputs so that no step re-reads data a 256 MiB last-level
 cache could still hold.
 
@@ -242,7 +243,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=1)
-    ap.add_argument("--also", type=str, default="2")
+    ap.add_argument("--also", type=str, default="2,5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench")

@@ -40,6 +40,10 @@ class Workload:
     prefill_chunk: int = 0         # > 0: a prefill chunk of this many new tokens on a `context` cache
     ragged: tuple | None = None    # (lo, hi) for log-uniform per-sequence lengths
     appends: bool = True           # decode appends the new token's KV (one vector per owned set)
+    window_fp8: bool = False       # window stores hold E4M3 bytes ([Article] XI) and attention takes
+                                   # per-sequence replay starts ([Article] XII): even sequences replay
+                                   # their last replay_tail positions, odd ones have no bound
+    replay_tail: int = 64
 
     def lengths(self) -> np.ndarray:
         if self.ragged:
@@ -60,6 +64,7 @@ WORKLOADS = {
     2: Workload(2, "decode_b8_1m_20layers", 8, 1 << 20, c2_layers(20), 2048),
     3: Workload(3, "prefill_4096_on_128k", 1, 131072, "F", 0, prefill_chunk=4096, appends=True),
     4: Workload(4, "decode_b64_ragged_1k_1m_4layers", 64, None, "FUFU", 0, ragged=(1024, 1 << 20)),
+    5: Workload(5, "decode_b8_1m_20layers_fp8win_replay", 8, 1 << 20, c2_layers(20), 2048, window_fp8=True),
 }
 
 
@@ -82,7 +87,7 @@ class Layer:
     mode: str
     kv_set: int
     q: torch.Tensor                  # bf16 [n_q, H, 128]
-    swa: torch.Tensor                # bf16 [n_q * swa_cap, 128]
+    swa: torch.Tensor                # bf16 [n_q * swa_cap, 128], or E4M3 bytes when the window is FP8
     q_idx: torch.Tensor | None = None
     w: torch.Tensor | None = None
     idx: torch.Tensor | None = None  # output of F/R layers
@@ -168,7 +173,12 @@ class Runner:
             q = synth.normal_bf16(wid, synth.T_Q, (self.n_q, wl.heads, 128), seq=l)
             ssig = synth.channel_sigma(wid, synth.T_SWA_SIGMA, 128, seq=l)
             swa = synth.kv_bf16(wid, synth.T_SWA, self.n_q_swa() * self.swa_cap, 128, ssig, seq=l)
-            L = Layer(m, cur_set, bf16_dev(q, device), bf16_dev(swa, device))
+            swa_dev = bf16_dev(swa, device)
+            if wl.window_fp8:  # the window store is written by the library's FP8 append
+                swa8 = torch.empty(swa_dev.shape, dtype=torch.uint8, device=device)
+                C.fp8_window_append(swa_dev, swa8)
+                swa_dev = swa8
+            L = Layer(m, cur_set, bf16_dev(q, device), swa_dev)
             if m in "FR":
                 qi = synth.int_bf16(wid, synth.T_IDX_Q, (self.n_q, wl.idx_heads, 64), seq=l)
                 w = synth.int_weights(wid, synth.T_IDX_W, (self.n_q, wl.idx_heads), seq=l)
@@ -194,6 +204,12 @@ class Runner:
             self.swa_row0 = torch.arange(self.n_q, dtype=torch.int64, device=device) * self.swa_cap
         self.pool = torch.empty((self.n_q, max(wl.pool_blocks, 1)), dtype=torch.int32, device=device) \
             if wl.pool_blocks else None
+        # replay starts of the FP8-window workload: even sequences replayed their last replay_tail positions
+        self.replay = None
+        if wl.window_fp8:
+            rs = np.where(np.arange(self.n_q) % 2 == 0, np.maximum(q_len - wl.replay_tail, 0), 0).astype(np.int64)
+            self.replay_host = rs
+            self.replay = torch.from_numpy(rs).to(device)
         # workspaces: one per op kind (each op's prefix is sized by n_q)
         self.ws_full = C.alloc_workspace(C.csa2_workspace_bytes(
             C.OP_INDEX_FULL, self.n_q, self.seqs.total_len_ub, self.seqs.max_len_ub, wl.top_k, wl.pool_blocks))
@@ -246,8 +262,13 @@ class Runner:
                 idx = L.idx
             else:
                 idx = self.layers[L.idx_src].idx
-            C.csa2_attend(L.q, st.codes, st.scales, self.seqs, idx, L.swa, self.swa_row0, self.swa_cap, wl.window,
-                          self.scale, L.out, self.ws_att, stream=stream)
+            if wl.window_fp8:
+                C.csa2_attend_fp8win(L.q, st.codes, st.scales, self.seqs, idx, L.swa, self.swa_row0, self.swa_cap,
+                                     wl.window, self.scale, L.out, self.ws_att, replay_start=self.replay,
+                                     stream=stream)
+            else:
+                C.csa2_attend(L.q, st.codes, st.scales, self.seqs, idx, L.swa, self.swa_row0, self.swa_cap,
+                              wl.window, self.scale, L.out, self.ws_att, stream=stream)
 
     def capture(self):
         """Capture one step per KV copy into HIP graphs (torch.cuda.CUDAGraph on torch's current
@@ -285,6 +306,10 @@ class Runner:
                 cand = self.n_q * min(wl.pool_blocks * 8, int(self.q_len.max()))
                 out["index_reindex"] += cand * 128
             win = np.minimum(self.q_len, wl.window)
+            win_bytes = 256                                         # bf16 window entry
+            if wl.window_fp8:
+                win = np.minimum(win, self.q_len - self.replay_host)
+                win_bytes = 128                                     # E4M3 window entry
             sel = np.minimum(self.q_len, wl.top_k)
-            out["attend"] += int(sel.sum()) * 72 + int(win.sum()) * 256 + self.n_q * wl.heads * 128 * (2 + 4)
+            out["attend"] += int(sel.sum()) * 72 + int(win.sum()) * win_bytes + self.n_q * wl.heads * 128 * (2 + 4)
         return out

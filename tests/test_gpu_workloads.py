@@ -56,9 +56,18 @@ def _check_step(r, queries, rows_sample=2000):
             for j in (int(j) for j in idx_ref if j >= 0):
                 codes[j], scales[j] = caches[cur][j]
             swa_row0 = 0 if wl.prefill_chunk else i * r.swa_cap
-            ref = O.attend(h["q"][l][i], codes, scales, n, idx_ref, h["swa"][l], swa_row0, r.swa_cap, wl.window,
-                           r.scale)
-            vmax = O.attended_max_abs(codes, scales, n, idx_ref, h["swa"][l], swa_row0, r.swa_cap, wl.window)
+            if wl.window_fp8:
+                swa8 = O.e4m3_quantize(h["swa"][l][swa_row0:swa_row0 + r.swa_cap])
+                assert np.array_equal(L.swa[swa_row0:swa_row0 + r.swa_cap].cpu().numpy(), swa8), f"fp8 window {l}"
+                rs = int(r.replay_host[i])
+                ref = O.attend_fp8_window(h["q"][l][i], codes, scales, n, idx_ref, swa8, 0, r.swa_cap, wl.window,
+                                          r.scale, replay_start=rs)
+                vmax = O.attended_max_abs_fp8(codes, scales, n, idx_ref, swa8, 0, r.swa_cap, wl.window,
+                                              replay_start=rs)
+            else:
+                ref = O.attend(h["q"][l][i], codes, scales, n, idx_ref, h["swa"][l], swa_row0, r.swa_cap,
+                               wl.window, r.scale)
+                vmax = O.attended_max_abs(codes, scales, n, idx_ref, h["swa"][l], swa_row0, r.swa_cap, wl.window)
             err = float(np.abs(L.out[i].cpu().numpy().astype(np.float64) - ref).max())
             assert err <= ATT_TOL * vmax, (l, i, err, vmax)
             worst = max(worst, err / vmax)
@@ -87,6 +96,11 @@ def test_workload1_batch32_64k_8layers():
 
 def test_workload2_batch8_1m_20layers():
     _run(2, [0, 5])
+
+
+def test_workload5_fp8_window_with_replay():
+    # query 0 replays its last 64 positions (even), query 5 has no replay bound (odd)
+    _run(5, [0, 5])
 
 
 def test_workload3_prefill_4096_on_128k():
