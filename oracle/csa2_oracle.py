@@ -32,7 +32,12 @@ design notes of this repository):
     entries (no de-duplication), with keys equal to values;
   * an FP8 window stores each value as the nearest E4M3 ('fn') value, ties to even,
     saturating at +-448 (the format has no infinity), with the value's sign bit and no
-    scale; a replay start s limits a query's window to positions >= s.
+    scale; a replay start s limits a query's window to positions >= s;
+  * MXFP4 indexer keys (E2M1 + one E8M0 byte per 32 channels) follow the microscaling
+    conversion: the block's scale is 2^(floor(log2 amax) - 2) (2 = the exponent of E2M1's
+    largest value 6), its code clamped to [1, 254] (so an all-zero or vanishing block uses
+    2^-126), each element the E2M1 value nearest to x / scale (ties to even, beyond 6 -> 6)
+    with x's sign bit.
 """
 from __future__ import annotations
 
@@ -217,6 +222,89 @@ def index_reindex(q_bf16, w, k_bf16_seq, n: int, pool: np.ndarray, top_k: int, b
     cand = np.array(sorted(p for b in blocks for p in range(b * block, b * block + block) if p < n),
                     dtype=np.int64)
     s = index_scores(q_bf16, w, k_bf16_seq[cand]) if cand.size else np.zeros(0)
+    return select_top(s, cand, top_k)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 indexer keys ([Article] sections VII and XI: indexer K in MXFP4, E2M1 elements with
+# one E8M0 scale byte per 32 channels)
+# ---------------------------------------------------------------------------
+
+
+def mxfp4_quantize(x_bf16: np.ndarray, block: int = 32):
+    """bf16 bits [T, D] (D % 32 == 0) -> (codes uint8 [T, D/2], scales uint8 [T, D/32]).
+
+    Scale of a 32-channel block: X = 2^e with e = floor(log2 amax) - 2, its E8M0 code e + 127
+    clamped to [1, 254] (an all-zero block gets code 1).  Element: the E2M1 magnitude nearest
+    to |x| / X (ties to the even code, beyond 6 -> 6) with x's sign bit.  Distances
+    |m X - |x|| are exact in fp64 (X is a power of two, m has two significant bits).
+    Byte i of a row holds channel 2i in its low nibble and 2i + 1 in its high nibble."""
+    x_bf16 = np.asarray(x_bf16, dtype=np.uint16)
+    T, D = x_bf16.shape
+    assert D % block == 0
+    if T > 4096:                                   # row chunks only bound host memory
+        parts = [mxfp4_quantize(x_bf16[r0:r0 + 4096], block) for r0 in range(0, T, 4096)]
+        return np.concatenate([a for a, _ in parts]), np.concatenate([b for _, b in parts])
+    x = bf16_to_f64(x_bf16).reshape(T, D // block, block)
+    sign = ((x_bf16 >> 15) & 1).astype(np.uint8).reshape(T, D // block, block)
+    amax = np.abs(x).max(axis=-1)                                  # [T, G]
+    _, ex = np.frexp(amax)                                         # amax = m 2^ex, m in [0.5, 1)
+    e = np.where(amax > 0, ex - 1 - 2, -127)                       # floor(log2 amax) - 2
+    code = np.clip(e + 127, 1, 254).astype(np.uint8)
+    X = np.ldexp(1.0, code.astype(np.int64) - 127)                 # [T, G]
+    dist = np.abs(E2M1_MAGNITUDES[None, None, None, :] * X[..., None, None] - np.abs(x)[..., None])
+    mag = _nearest_even(dist).astype(np.uint8)
+    c = ((sign << 3) | mag).reshape(T, D)
+    packed = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    return packed, code
+
+
+def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """fp64 values E2M1(code) * 2^(scale - 127)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    T, D = codes.shape[0], codes.shape[1] * 2
+    c = np.empty((T, D), dtype=np.uint8)
+    c[:, 0::2] = codes & 0xF
+    c[:, 1::2] = codes >> 4
+    table = np.array([e2m1_value(k) for k in range(16)], dtype=np.float64)
+    X = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    return table[c] * np.repeat(X, block, axis=1)
+
+
+def mxfp4_entry_bytes(dim: int, block: int = 32) -> int:
+    """Bytes per MXFP4 key: 4 bits per value plus one E8M0 byte per block."""
+    return dim // 2 + dim // block
+
+
+def index_scores_f64(q_bf16: np.ndarray, w: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """index_scores with the keys given as fp64 values (e.g. dequantised MXFP4 keys)."""
+    q = bf16_to_f64(q_bf16)
+    dots = np.asarray(k, dtype=np.float64) @ q.T
+    return np.maximum(dots, 0.0) @ np.asarray(w, dtype=np.float64)
+
+
+def index_full_mx(q_bf16, w, k_codes_seq, k_scales_seq, n: int, top_k: int, block: int = 8,
+                  pool_blocks: int = 0):
+    """index_full over MXFP4 keys: the same scores and selection on the dequantised keys."""
+    s = index_scores_f64(q_bf16, w, mxfp4_dequantize(k_codes_seq[:n], k_scales_seq[:n])) if n > 0 \
+        else np.zeros(0)
+    idx = select_top(s, np.arange(n), top_k)
+    pool = None
+    if pool_blocks > 0:
+        bm = block_max(s, block) if n > 0 else np.zeros(0)
+        pool = select_top(bm, np.arange(bm.shape[0]), pool_blocks)
+    return idx, pool
+
+
+def index_reindex_mx(q_bf16, w, k_codes_seq, k_scales_seq, n: int, pool: np.ndarray, top_k: int,
+                     block: int = 8):
+    """index_reindex over MXFP4 keys."""
+    blocks = np.asarray(pool, dtype=np.int64)
+    blocks = blocks[blocks >= 0]
+    cand = np.array(sorted(p for b in blocks for p in range(b * block, b * block + block) if p < n),
+                    dtype=np.int64)
+    s = index_scores_f64(q_bf16, w, mxfp4_dequantize(k_codes_seq[cand], k_scales_seq[cand])) \
+        if cand.size else np.zeros(0)
     return select_top(s, cand, top_k)
 
 
