@@ -29,6 +29,10 @@ EXPORTS = (
     "csa2_index_full_scan",
     "csa2_index_full_select",
     "csa2_index_reindex",
+    "mxfp4_key_append",
+    "csa2_index_full_mx",
+    "csa2_index_full_mx_scan",
+    "csa2_index_reindex_mx",
     "csa2_attend",
     "csa2_attend_fp8win",
     "csa2_workspace_bytes",
@@ -74,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.csa2_index_reindex.argtypes = [vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
         L.csa2_attend.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, i32, f32, vp, vp, sz, vp]
         L.fp8_window_append.argtypes = [vp, i64, i32, vp, i64, vp, i64, vp]
+        L.mxfp4_key_append.argtypes = [vp, i64, i32, vp, i64, vp, vp, i64, vp]
+        for name in ("csa2_index_full_mx", "csa2_index_full_mx_scan"):
+            getattr(L, name).argtypes = [vp, vp, vp, vp, SeqsC, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
+        L.csa2_index_reindex_mx.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
         L.csa2_attend_fp8win.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp,
                                          sz, vp]
         L.csa2_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
@@ -83,7 +91,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_status_string.restype = ctypes.c_char_p
         L.csa2_version.argtypes = []
         for name in ("fp4_kv_append", "fp8_window_append", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
-                     "csa2_attend_fp8win", "csa2_workspace_init", "csa2_version"):
+                     "csa2_attend_fp8win", "csa2_workspace_init", "csa2_version", "mxfp4_key_append",
+                     "csa2_index_full_mx", "csa2_index_full_mx_scan", "csa2_index_reindex_mx"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -227,3 +236,31 @@ def csa2_attend_fp8win(q, codes, scales, seqs: Seqs, idx, swa8, swa_row0, swa_ca
         _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa8), _ptr(swa_row0), swa_cap,
         swa_rows, window, _ptr(replay_start), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws),
         ws.numel(), _stream(stream)))
+
+
+def mxfp4_key_append(x, codes, scales, dst_rows=None, row0: int = 0, stream=None) -> None:
+    """Quantise x (bf16 [n_tok, dim]) into MXFP4 key rows (codes uint8 [rows, dim/2], scales uint8 [rows, dim/32])."""
+    n_tok, dim = x.shape
+    _check("mxfp4_key_append", lib().mxfp4_key_append(_ptr(x), n_tok, dim, _ptr(dst_rows), row0, _ptr(codes),
+                                                      _ptr(scales), codes.shape[0], _stream(stream)))
+
+
+def csa2_index_full_mx(q_idx, w, k_codes, k_scales, seqs: Seqs, top_k: int, pool_blocks: int, idx_out, pool_out,
+                       ws, block: int = BLOCK, shared_kv: int = 0, stream=None) -> None:
+    _check("csa2_index_full_mx", lib().csa2_index_full_mx(
+        _ptr(q_idx), _ptr(w), _ptr(k_codes), _ptr(k_scales), seqs.c(), q_idx.shape[1], top_k, block, pool_blocks,
+        shared_kv, _ptr(idx_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def csa2_index_full_mx_scan(q_idx, w, k_codes, k_scales, seqs: Seqs, top_k: int, pool_blocks: int, idx_out,
+                            pool_out, ws, block: int = BLOCK, shared_kv: int = 0, stream=None) -> None:
+    _check("csa2_index_full_mx_scan", lib().csa2_index_full_mx_scan(
+        _ptr(q_idx), _ptr(w), _ptr(k_codes), _ptr(k_scales), seqs.c(), q_idx.shape[1], top_k, block, pool_blocks,
+        shared_kv, _ptr(idx_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def csa2_index_reindex_mx(q_idx, w, k_codes, k_scales, seqs: Seqs, pool, top_k: int, idx_out, ws,
+                          block: int = BLOCK, stream=None) -> None:
+    _check("csa2_index_reindex_mx", lib().csa2_index_reindex_mx(
+        _ptr(q_idx), _ptr(w), _ptr(k_codes), _ptr(k_scales), seqs.c(), q_idx.shape[1], _ptr(pool), pool.shape[1],
+        block, top_k, _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))

@@ -43,14 +43,17 @@ struct IndexWs {
 
 hipError_t launch_fp4_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
                            uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream);
-hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
-                             const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
-                             int grid_tiles, int grid_ftiles, int top_k, int pool_blocks, int prefill,
-                             const IndexWs& ws, int32_t* idx_out, int32_t* pool_out, int phase, hipStream_t stream);
-hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
-                                const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
-                                const int32_t* pool, int pool_blocks, int top_k, const IndexWs& ws, int32_t* idx_out,
-                                hipStream_t stream);
+hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
+                             const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
+                             int64_t cache_rows, int n_heads, int grid_tiles, int grid_ftiles, int top_k,
+                             int pool_blocks, int prefill, const IndexWs& ws, int32_t* idx_out, int32_t* pool_out,
+                             int phase, hipStream_t stream);
+hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
+                                const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
+                                int64_t cache_rows, int n_heads, const int32_t* pool, int pool_blocks, int top_k,
+                                const IndexWs& ws, int32_t* idx_out, hipStream_t stream);
+hipError_t launch_mx_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
+                          uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream);
 hipError_t launch_fp8_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
                            uint8_t* out, int64_t cap_rows, hipStream_t stream);
 hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const int64_t* kv_row0,
@@ -188,9 +191,10 @@ size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32
     }
 }
 
-static int index_full_phase(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const csa2_seqs& seqs,
-                            int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
-                            int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream, int phase) {
+static int index_full_phase(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
+                            const csa2_seqs& seqs, int32_t n_heads, int32_t top_k, int32_t block,
+                            int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws,
+                            size_t ws_bytes, void* stream, int phase) {
     int st = check_seqs(seqs);
     if (st) return st;
     if (n_heads < 1 || n_heads > CSA2_MAX_IDX_HEADS || top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 ||
@@ -199,8 +203,10 @@ static int index_full_phase(const uint16_t* q_idx, const float* w, const uint16_
     if (block != CSA2_BLOCK) return CSA2_ERR_UNSUPPORTED;
     if (seqs.n_q == 0) return CSA2_OK;
     if (q_idx == nullptr || w == nullptr || k_idx == nullptr || idx_out == nullptr) return CSA2_ERR_NULL;
+    if (mx && k_sc == nullptr) return CSA2_ERR_NULL;
     if (pool_blocks > 0 && pool_out == nullptr) return CSA2_ERR_NULL;
-    if (!aligned16(q_idx) || !aligned16(k_idx)) return CSA2_ERR_SHAPE;
+    if (!aligned16(q_idx) || !aligned16(k_idx) || (mx && (reinterpret_cast<uintptr_t>(k_sc) & 1u)))
+        return CSA2_ERR_SHAPE;
     const int64_t tiles = full_grid_tiles(seqs.n_q, seqs.total_len_ub, seqs.max_len_ub);
     const int64_t ftiles = full_grid_tiles(seqs.n_q, seqs.total_len_ub, seqs.max_len_ub, kFilterTile);
     if (tiles > kMaxTiles) return CSA2_ERR_SHAPE;
@@ -209,43 +215,46 @@ static int index_full_phase(const uint16_t* q_idx, const float* w, const uint16_
     if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return CSA2_ERR_WORKSPACE;
     const IndexWs wsp = carve_full(ws, seqs.n_q, tiles, ftiles, top_k, pool_blocks, &need);
     // prefill chunk: the MFMA scoring kernel (shared sequence, at most 4 heads, no pool, >= 16 queries)
-    const int prefill = (shared_kv != 0 && pool_blocks == 0 && n_heads <= 4 && seqs.n_q >= 16) ? 1 : 0;
-    return launch_status(launch_index_full(q_idx, w, k_idx, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
-                                           seqs.cache_rows, n_heads, (int)tiles, (int)ftiles, top_k, pool_blocks,
-                                           prefill, wsp, idx_out, pool_out, phase, static_cast<hipStream_t>(stream)));
+    // (MXFP4 keys always take the per-query scan)
+    const int prefill = (!mx && shared_kv != 0 && pool_blocks == 0 && n_heads <= 4 && seqs.n_q >= 16) ? 1 : 0;
+    return launch_status(launch_index_full(q_idx, w, k_idx, k_sc, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
+                                           seqs.max_len_ub, seqs.cache_rows, n_heads, (int)tiles, (int)ftiles, top_k,
+                                           pool_blocks, prefill, wsp, idx_out, pool_out, phase,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
                     int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
                     int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
-    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
-                            ws, ws_bytes, stream, 7);
+    return index_full_phase(q_idx, w, k_idx, nullptr, 0, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out,
+                            pool_out, ws, ws_bytes, stream, 7);
 }
 
 int csa2_index_full_prep(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
                          int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
                          int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
-    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
-                            ws, ws_bytes, stream, 1);
+    return index_full_phase(q_idx, w, k_idx, nullptr, 0, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out,
+                            pool_out, ws, ws_bytes, stream, 1);
 }
 
 int csa2_index_full_scan(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
                          int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
                          int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
-    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
-                            ws, ws_bytes, stream, 2);
+    return index_full_phase(q_idx, w, k_idx, nullptr, 0, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out,
+                            pool_out, ws, ws_bytes, stream, 2);
 }
 
 int csa2_index_full_select(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
                            int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks, int32_t shared_kv,
                            int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes, void* stream) {
-    return index_full_phase(q_idx, w, k_idx, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out, pool_out,
-                            ws, ws_bytes, stream, 4);
+    return index_full_phase(q_idx, w, k_idx, nullptr, 0, seqs, n_heads, top_k, block, pool_blocks, shared_kv, idx_out,
+                            pool_out, ws, ws_bytes, stream, 4);
 }
 
-int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
-                       const int32_t* pool, int32_t pool_blocks, int32_t block, int32_t top_k, int32_t* idx_out,
-                       void* ws, size_t ws_bytes, void* stream) {
+static int index_reindex_common(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
+                                const csa2_seqs& seqs, int32_t n_heads, const int32_t* pool, int32_t pool_blocks,
+                                int32_t block, int32_t top_k, int32_t* idx_out, void* ws, size_t ws_bytes,
+                                void* stream) {
     int st = check_seqs(seqs);
     if (st) return st;
     if (n_heads < 1 || n_heads > CSA2_MAX_IDX_HEADS || top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 1 ||
@@ -255,14 +264,58 @@ int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_
     if (seqs.n_q == 0) return CSA2_OK;
     if (q_idx == nullptr || w == nullptr || k_idx == nullptr || pool == nullptr || idx_out == nullptr)
         return CSA2_ERR_NULL;
-    if (!aligned16(q_idx) || !aligned16(k_idx)) return CSA2_ERR_SHAPE;
+    if (mx && k_sc == nullptr) return CSA2_ERR_NULL;
+    if (!aligned16(q_idx) || !aligned16(k_idx) || (mx && (reinterpret_cast<uintptr_t>(k_sc) & 1u)))
+        return CSA2_ERR_SHAPE;
     size_t need = 0;
     carve_reindex(nullptr, seqs.n_q, top_k, pool_blocks, &need);
     if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return CSA2_ERR_WORKSPACE;
     const IndexWs wsp = carve_reindex(ws, seqs.n_q, top_k, pool_blocks, &need);
-    return launch_status(launch_index_reindex(q_idx, w, k_idx, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
-                                              seqs.cache_rows, n_heads, pool, pool_blocks, top_k, wsp, idx_out,
-                                              static_cast<hipStream_t>(stream)));
+    return launch_status(launch_index_reindex(q_idx, w, k_idx, k_sc, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
+                                              seqs.max_len_ub, seqs.cache_rows, n_heads, pool, pool_blocks, top_k,
+                                              wsp, idx_out, static_cast<hipStream_t>(stream)));
+}
+
+int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
+                       const int32_t* pool, int32_t pool_blocks, int32_t block, int32_t top_k, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, void* stream) {
+    return index_reindex_common(q_idx, w, k_idx, nullptr, 0, seqs, n_heads, pool, pool_blocks, block, top_k, idx_out,
+                                ws, ws_bytes, stream);
+}
+
+int mxfp4_key_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64_t* dst_rows, int64_t row0,
+                     uint8_t* codes, uint8_t* scales, int64_t cap_rows, void* stream) {
+    if (n_tok < 0 || dim <= 0 || dim % 32 != 0 || dim > 1024 || cap_rows < 0) return CSA2_ERR_SHAPE;
+    if (n_tok == 0) return CSA2_OK;
+    if (x == nullptr || codes == nullptr || scales == nullptr) return CSA2_ERR_NULL;
+    if (!aligned16(x) || !aligned16(codes)) return CSA2_ERR_SHAPE;
+    if (n_tok > ((int64_t)1 << 40)) return CSA2_ERR_SHAPE;
+    if (dst_rows == nullptr && (row0 < 0 || row0 > cap_rows || n_tok > cap_rows - row0)) return CSA2_ERR_CAPACITY;
+    return launch_status(launch_mx_pack(x, n_tok, dim, dst_rows, row0, codes, scales, cap_rows,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int csa2_index_full_mx(const uint16_t* q_idx, const float* w, const uint8_t* k_codes, const uint8_t* k_scales,
+                       csa2_seqs seqs, int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
+                       int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes,
+                       void* stream) {
+    return index_full_phase(q_idx, w, k_codes, k_scales, 1, seqs, n_heads, top_k, block, pool_blocks, shared_kv,
+                            idx_out, pool_out, ws, ws_bytes, stream, 7);
+}
+
+int csa2_index_full_mx_scan(const uint16_t* q_idx, const float* w, const uint8_t* k_codes, const uint8_t* k_scales,
+                            csa2_seqs seqs, int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
+                            int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes,
+                            void* stream) {
+    return index_full_phase(q_idx, w, k_codes, k_scales, 1, seqs, n_heads, top_k, block, pool_blocks, shared_kv,
+                            idx_out, pool_out, ws, ws_bytes, stream, 2);
+}
+
+int csa2_index_reindex_mx(const uint16_t* q_idx, const float* w, const uint8_t* k_codes, const uint8_t* k_scales,
+                          csa2_seqs seqs, int32_t n_heads, const int32_t* pool, int32_t pool_blocks, int32_t block,
+                          int32_t top_k, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+    return index_reindex_common(q_idx, w, k_codes, k_scales, 1, seqs, n_heads, pool, pool_blocks, block, top_k,
+                                idx_out, ws, ws_bytes, stream);
 }
 
 static int attend_common(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const csa2_seqs& seqs,

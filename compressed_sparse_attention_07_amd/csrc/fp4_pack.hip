@@ -101,6 +101,66 @@ hipError_t launch_fp4_pack(const uint16_t* x, int64_t n_tok, int dim, const int6
 }
 
 // ----------------------------------------------------------------------------------------
+// MXFP4 indexer keys ([Article] sections VII and XI: indexer K in MXFP4, E2M1 elements with
+// one E8M0 scale per 32 channels).  Microscaling conversion: the block's scale is
+// X = 2^(floor(log2 amax) - 2), i.e. E8M0 code = (bf16 exponent field of amax) - 2, clamped to
+// [1, 254]; each element is the E2M1 value nearest to x / X, ties to even, saturating at 6,
+// decided by the same exact threshold compares as the KV packer (X is a power of two, so
+// every threshold times X is exact).  One thread packs one 32-channel block: 64 B in,
+// 16 B of codes and 1 scale byte out.
+// ----------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_mx_pack(const uint16_t* __restrict__ x, int64_t n_tok, int dim,
+                                                 const int64_t* __restrict__ dst_rows, int64_t row0,
+                                                 uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                 int64_t cap_rows) {
+    const int blocks = dim >> 5;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= n_tok * blocks) return;
+    const int64_t t = gid / blocks;
+    const int b = (int)(gid - t * blocks);
+    const int64_t row = dst_rows ? dst_rows[t] : row0 + t;
+    if (row < 0 || row >= cap_rows) return;
+
+    const uint4* src = reinterpret_cast<const uint4*>(x + t * dim + b * 32);
+    uint32_t w[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint4 v = src[k];
+        w[4 * k] = v.x; w[4 * k + 1] = v.y; w[4 * k + 2] = v.z; w[4 * k + 3] = v.w;
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        am = max(am, w[k] & 0x7fffu);
+        am = max(am, (w[k] >> 16) & 0x7fffu);
+    }
+    const int code = min(254, max(1, (int)(am >> 7) - 2));
+    const float X = __uint_as_float((uint32_t)code << 23);  // 2^(code - 127), a normal float
+    uint32_t out[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t o = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t v = w[4 * k + j];
+            o |= (e2m1_code(v & 0xffffu, X) | (e2m1_code(v >> 16, X) << 4)) << (8 * j);
+        }
+        out[k] = o;
+    }
+    *reinterpret_cast<uint4*>(codes + row * (dim >> 1) + b * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+    scales[row * blocks + b] = (uint8_t)code;
+}
+
+hipError_t launch_mx_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
+                          uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream) {
+    const int64_t total = n_tok * (dim >> 5);
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(k_mx_pack, dim3((unsigned)blocks), dim3(256), 0, stream, x, n_tok, dim, dst_rows, row0, codes,
+                       scales, cap_rows);
+    return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------
 // FP8 window store ([Article] section XI: the recent-window cache stays at FP8): each bf16
 // value becomes the nearest E4M3 ("fn") value, ties to even, saturating at 448 (the format
 // has no infinity), keeping the value's sign bit.  Exact integer rounding of the bf16

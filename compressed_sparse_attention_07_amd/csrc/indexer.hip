@@ -148,6 +148,27 @@ __device__ __forceinline__ float mfma_score(const QFrag& qf, const uint4& k0, co
     return s;
 }
 
+// MXFP4 keys (E2M1 + one E8M0 scale per 32 channels): k-step s of the contraction covers
+// exactly scale block s, so lane (g, r)'s 8 channels of k-step s are the 4 code bytes
+// 16s + 4g .. 16s + 4g + 3 of position r.  The hardware conversion applies the power-of-two
+// scale exactly (its scale operand carries only an exponent): E2M1 x 2^(code - 127) -> bf16.
+__device__ __forceinline__ uint4 mx_frag(uint32_t dw, uint32_t code) {
+    const float sc = __uint_as_float(code << 23);  // 2^(code - 127); written codes are >= 1
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 2)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 3)));
+}
+
+__device__ __forceinline__ uint32_t buf_ld4(BufRsrc rs, int voff, int soff) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
+}
+
+__device__ __forceinline__ uint32_t buf_ld2(BufRsrc rs, int voff, int soff) {
+    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0);
+}
+
 // Largest key of each aligned group of 8 lanes within lanes 0..15, in lanes 4 and 12
 // (quad butterflies, then row_ror:4 brings the quad just below).
 __device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t k) {
@@ -241,11 +262,13 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
 // tile range [g * T / G, (g + 1) * T / G) of the tile map, so the per-tile set-up (tile map,
 // query slice) is paid once per query rather than once per 256 KB tile, and the first-digit
 // histograms go to the workspace only when the query changes.
-template <int HI>
+// MX: keys are MXFP4 (k_idx = code bytes [rows, 32], k_sc = E8M0 bytes [rows, 2]) instead of
+// bf16 (k_idx = [rows, 64] bf16, k_sc unused).
+template <int HI, bool MX>
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len, int n_q, int32_t max_len,
-    int64_t cache_rows, int n_heads, int grid_tiles, int pool_blocks, IndexWs ws) {
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx,
+    const uint8_t* __restrict__ k_sc, const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len,
+    int n_q, int32_t max_len, int64_t cache_rows, int n_heads, int grid_tiles, int pool_blocks, IndexWs ws) {
     __shared__ uint32_t sh_hist[kHistBins];
     __shared__ uint32_t sh_bhist[kHistBins];
 
@@ -306,21 +329,36 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
         if (p_tile >= n) continue;
         // buffer view of this tile's rows: one 32-bit lane offset for every load (the step goes
         // in the scalar offset) and rows past the sequence read as zeros
-        const BufRsrc rs = tile_rsrc(k_idx + (row0 + p_tile) * 64, min(n - p_tile, kFullTile) * 128);
-        const int voff = (16 * wid + r) * 128 + 16 * g;
+        const int rows_here = min(n - p_tile, kFullTile);
+        constexpr int kRowB = MX ? 32 : 128;  // key bytes per position (codes only for MXFP4)
+        const BufRsrc rs = tile_rsrc(static_cast<const uint8_t*>(k_idx) + (row0 + p_tile) * kRowB, rows_here * kRowB);
+        const BufRsrc rss = tile_rsrc(MX ? k_sc + (row0 + p_tile) * 2 : nullptr, MX ? rows_here * 2 : 0);
+        const int voff = (16 * wid + r) * kRowB + (MX ? 4 : 16) * g;
+        const int voff_s = (16 * wid + r) * 2;
         for (int b = 0; b < kFullTile; b += 64 * U) {
             const int pb = p_tile + b;
             if (pb >= n) break;
             uint4 kb[U][2];
+            uint32_t kc[U][2], ks[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                kb[u][0] = buf_ld16(rs, voff, (b + 64 * u) * 128);
-                kb[u][1] = buf_ld16(rs, voff + 64, (b + 64 * u) * 128);
+                if constexpr (MX) {
+                    kc[u][0] = buf_ld4(rs, voff, (b + 64 * u) * kRowB);
+                    kc[u][1] = buf_ld4(rs, voff + 16, (b + 64 * u) * kRowB);
+                    ks[u] = buf_ld2(rss, voff_s, (b + 64 * u) * 2);
+                } else {
+                    kb[u][0] = buf_ld16(rs, voff, (b + 64 * u) * kRowB);
+                    kb[u][1] = buf_ld16(rs, voff + 64, (b + 64 * u) * kRowB);
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int p0 = pb + 64 * u + 16 * wid;  // first of this wave's 16 positions
                 const int p = p0 + r;
+                if constexpr (MX) {
+                    kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
+                    kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
+                }
                 const float sc = mfma_score<HI>(qf, kb[u][0], kb[u][1]);
                 const bool mine = g == 0 && p < n;
                 const uint32_t key = mine ? score_key(sc) : 0u;
@@ -641,11 +679,12 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
 // ----------------------------------------------------------------------------------------
 // Reindex, kernel 1: score the pool's positions with this layer's query
 // ----------------------------------------------------------------------------------------
-template <int HI>
+template <int HI, bool MX>
 __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len, int32_t max_len, int64_t cache_rows,
-    int n_heads, const int32_t* __restrict__ pool, int pool_blocks, IndexWs ws) {
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx,
+    const uint8_t* __restrict__ k_sc, const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len,
+    int32_t max_len, int64_t cache_rows, int n_heads, const int32_t* __restrict__ pool, int pool_blocks,
+    IndexWs ws) {
     __shared__ uint32_t sh_hist[kHistBins];
 
     const int i = blockIdx.y;
@@ -675,15 +714,31 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
         blk[u] = slot < pool_blocks ? qpool[slot] : -1;
     }
     uint4 kb[kUnits][2];
+    uint32_t kc[kUnits][2], ks[kUnits];
     if (n > 0) {
         // absent rows read the sequence's first row (n > 0) and are masked below
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) {
             const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
             const bool ok = blk[u] >= 0 && p < n;
-            const uint16_t* row = k_idx + (row0 + (ok ? p : 0)) * 64 + 8 * g;
-            kb[u][0] = *reinterpret_cast<const uint4*>(row);
-            kb[u][1] = *reinterpret_cast<const uint4*>(row + 32);
+            const int64_t kr = row0 + (ok ? p : 0);
+            if constexpr (MX) {
+                const uint8_t* row = static_cast<const uint8_t*>(k_idx) + kr * 32 + 4 * g;
+                kc[u][0] = *reinterpret_cast<const uint32_t*>(row);
+                kc[u][1] = *reinterpret_cast<const uint32_t*>(row + 16);
+                ks[u] = *reinterpret_cast<const uint16_t*>(k_sc + kr * 2);
+            } else {
+                const uint16_t* row = static_cast<const uint16_t*>(k_idx) + kr * 64 + 8 * g;
+                kb[u][0] = *reinterpret_cast<const uint4*>(row);
+                kb[u][1] = *reinterpret_cast<const uint4*>(row + 32);
+            }
+        }
+        if constexpr (MX) {
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) {
+                kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
+                kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
+            }
         }
     }
 #pragma unroll
@@ -849,10 +904,12 @@ static int scan_workgroups() {
 // 4 = filter + select kernels; 7 = all.
 // prefill != 0: every query reads the same sequence (kv_row0[0]) and no pool is asked for, so
 // the scores come from the MFMA kernel that tiles 16 queries x 16 positions.
-hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
-                             const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
-                             int grid_tiles, int grid_ftiles, int top_k, int pool_blocks, int prefill,
-                             const IndexWs& ws, int32_t* idx_out, int32_t* pool_out, int phase, hipStream_t stream) {
+// mx != 0: k_idx holds MXFP4 code bytes and k_sc their E8M0 scales (never with prefill).
+hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
+                             const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
+                             int64_t cache_rows, int n_heads, int grid_tiles, int grid_ftiles, int top_k,
+                             int pool_blocks, int prefill, const IndexWs& ws, int32_t* idx_out, int32_t* pool_out,
+                             int phase, hipStream_t stream) {
     if (phase & 1) {
         hipLaunchKernelGGL(k_idx_prep, dim3(1), dim3(kPrepNT), 0, stream, kv_row0, kv_len, n_q, max_len, cache_rows,
                            grid_tiles, grid_ftiles, ws);
@@ -862,13 +919,14 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16
     if (phase & 2) {
         if (prefill) {
             const dim3 grid((unsigned)((max_len + kPfPos - 1) / kPfPos), (unsigned)((n_q + kPfQ - 1) / kPfQ));
-            hipLaunchKernelGGL(k_idx_score_prefill, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, n_q,
-                               cache_rows, n_heads, ws);
+            hipLaunchKernelGGL(k_idx_score_prefill, grid, dim3(kScoreNT), 0, stream, q_idx, w,
+                               static_cast<const uint16_t*>(k_idx), kv_row0, n_q, cache_rows, n_heads, ws);
         } else {
             const int wgs = min(grid_tiles, scan_workgroups());
-            auto kern = n_heads <= 4 ? k_idx_score_full<4> : k_idx_score_full<8>;
-            hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, kv_len, n_q,
-                               max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
+            auto kern = mx ? (n_heads <= 4 ? k_idx_score_full<4, true> : k_idx_score_full<8, true>)
+                           : (n_heads <= 4 ? k_idx_score_full<4, false> : k_idx_score_full<8, false>);
+            hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, q_idx, w, k_idx, k_sc, kv_row0, kv_len,
+                               n_q, max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -885,19 +943,16 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const uint16
     return hipSuccess;
 }
 
-hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, const int64_t* kv_row0,
-                                const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, int n_heads,
-                                const int32_t* pool, int pool_blocks, int top_k, const IndexWs& ws, int32_t* idx_out,
-                                hipStream_t stream) {
+hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
+                                const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
+                                int64_t cache_rows, int n_heads, const int32_t* pool, int pool_blocks, int top_k,
+                                const IndexWs& ws, int32_t* idx_out, hipStream_t stream) {
     const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
     dim3 grid(chunks, n_q);
-    if (n_heads <= 4) {
-        hipLaunchKernelGGL(k_idx_reindex_score<4>, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, kv_len,
-                           max_len, cache_rows, n_heads, pool, pool_blocks, ws);
-    } else {
-        hipLaunchKernelGGL(k_idx_reindex_score<8>, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, kv_row0, kv_len,
-                           max_len, cache_rows, n_heads, pool, pool_blocks, ws);
-    }
+    auto kern = mx ? (n_heads <= 4 ? k_idx_reindex_score<4, true> : k_idx_reindex_score<8, true>)
+                   : (n_heads <= 4 ? k_idx_reindex_score<4, false> : k_idx_reindex_score<8, false>);
+    hipLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, k_sc, kv_row0, kv_len, max_len,
+                       cache_rows, n_heads, pool, pool_blocks, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ept = (pool_blocks * 8 + kSelNT - 1) / kSelNT;

@@ -174,6 +174,47 @@ int csa2_index_full_select(const uint16_t* q_idx, const float* w, const uint16_t
                            size_t ws_bytes, void* stream);
 
 /*
+ * MXFP4 indexer keys.  [Article] sections VII and XI: indexer K is stored in MXFP4, E2M1
+ * elements with one E8M0 scale byte per 32 channels (34 B per 64-channel key instead of
+ * 128 B in bf16).
+ *
+ * mxfp4_key_append -- quantise bf16 keys into MXFP4 rows.
+ *   x        device bf16 [n_tok, dim], finite values, 16-byte aligned; dim % 32 == 0, <= 1024.
+ *   dst_rows device int64 [n_tok] or NULL (rows row0 .. row0 + n_tok - 1).
+ *   codes    device uint8 [cap_rows, dim/2], 16-byte aligned: byte j holds channel 2j in its
+ *            low nibble, 2j+1 in its high nibble (E2M1, sign bit 3).
+ *   scales   device uint8 [cap_rows, dim/32]: E8M0 byte e of channels [32b, 32b+32),
+ *            value 2^(e - 127).
+ * Per block: e = (exponent of the largest |x|) - 2, clamped to [1, 254] (so the largest
+ * value lands in [4, 8) before rounding); each code is the E2M1 value nearest to x / 2^(e-127),
+ * ties to even, saturating at 6, with x's sign bit.  Rows outside [0, cap_rows) named by
+ * dst_rows are skipped.
+ *
+ * csa2_index_full_mx / csa2_index_full_mx_scan / csa2_index_reindex_mx -- csa2_index_full,
+ * its scan part and csa2_index_reindex with MXFP4 keys: k_codes device uint8
+ * [seqs.cache_rows, 32] (16-byte aligned) and k_scales device uint8 [seqs.cache_rows, 2]
+ * (2-byte aligned), written by mxfp4_key_append with dim = CSA2_IDX_DIM.  Scores are those of
+ * the dequantised keys (integer keys in [-4, 4] are exact, so selections equal the bf16-key
+ * ones).  csa2_index_full_prep and csa2_index_full_select read no keys and serve both key
+ * formats.  A prefill chunk (shared_kv != 0) is scanned per query.  Arguments, workspace,
+ * outputs and errors are otherwise those of the bf16-key calls.
+ */
+int mxfp4_key_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64_t* dst_rows,
+                     int64_t row0, uint8_t* codes, uint8_t* scales, int64_t cap_rows, void* stream);
+int csa2_index_full_mx(const uint16_t* q_idx, const float* w, const uint8_t* k_codes,
+                       const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, int32_t top_k,
+                       int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
+                       int32_t* pool_out, void* ws, size_t ws_bytes, void* stream);
+int csa2_index_full_mx_scan(const uint16_t* q_idx, const float* w, const uint8_t* k_codes,
+                            const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, int32_t top_k,
+                            int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
+                            int32_t* pool_out, void* ws, size_t ws_bytes, void* stream);
+int csa2_index_reindex_mx(const uint16_t* q_idx, const float* w, const uint8_t* k_codes,
+                          const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, const int32_t* pool,
+                          int32_t pool_blocks, int32_t block, int32_t top_k, int32_t* idx_out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
  * csa2_index_reindex -- Reindex-mode indexer: this layer's own query scored against
  * the Full layer's keys, over the positions of the pool's blocks only.
  * [Article] sections VIII-IX (Reindex reuses main KV and indexer K, runs its own

@@ -1,0 +1,148 @@
+"""GPU parity of the MXFP4 indexer keys ([Article] sections VII and XI: indexer K in MXFP4,
+E2M1 + one E8M0 scale per 32 channels), through the C ABI, against the CPU oracle: codes and
+scales bit-exact; Full and Reindex selections over MXFP4 keys bit-exact (their scores are
+exact in fp32 for the keys used here)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from compressed_sparse_attention_07_amd import csa2 as C
+from compressed_sparse_attention_07_amd import synth
+
+from gpu_helpers import DEV, IndexCase, bf16_tensor
+
+pytestmark = pytest.mark.gpu
+W_MX = 400
+
+
+def _append(x_bits, dim=64, dst_rows=None, cap=None):
+    n = x_bits.shape[0]
+    cap = n if cap is None else cap
+    codes = torch.full((cap, dim // 2), 0x55, dtype=torch.uint8, device=DEV)
+    scales = torch.full((cap, dim // 32), 0x55, dtype=torch.uint8, device=DEV)
+    C.mxfp4_key_append(bf16_tensor(x_bits), codes, scales,
+                       dst_rows=None if dst_rows is None else torch.from_numpy(dst_rows).to(DEV))
+    torch.cuda.synchronize()
+    return codes, scales
+
+
+@pytest.mark.parametrize("dim", [64, 128, 32])
+def test_mxfp4_append_bit_exact_workload_values(dim):
+    x = synth.kv_bf16(W_MX, synth.T_KV, 5000, dim, synth.channel_sigma(W_MX, synth.T_KV_SIGMA, dim))
+    codes, scales = _append(x, dim)
+    rc, rs = O.mxfp4_quantize(x)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+def test_mxfp4_append_special_blocks():
+    rows = np.zeros((12, 64), dtype=np.float32)
+    rows[1, :3] = [-4.0, 2.5, -1.25]          # exact ties to even
+    rows[2, 0] = 7.0                          # saturation
+    rows[3, :2] = [3.0, 0.1]
+    rows[4, 0] = 1e-38                        # exponent below the clamp
+    rows[5, 5] = -0.0
+    rows[6, :] = np.linspace(-100, 100, 64)
+    rows[7, 0] = 3.0e38                       # a huge block
+    rows[8, 0] = -3.0e38                      # (inputs are finite: no inf or NaN)
+    rows[9, :] = 2.0 ** -130                  # bf16 subnormals
+    rows[10, :32] = 5.0                       # 5 = 4 + half step at X = 1: ties to 4
+    rows[11, 32:] = -6.5
+    bits = synth.f32_to_bf16_bits(rows)
+    codes, scales = _append(bits)
+    rc, rs = O.mxfp4_quantize(bits)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+
+
+def test_mxfp4_append_scattered_rows():
+    x = synth.int_bf16(W_MX + 1, synth.T_IDX_K, (30, 64))
+    rows = np.array([3, 29, -1, 0, 50] + list(range(5, 29)) + [1], dtype=np.int64)   # distinct rows
+    codes, scales = _append(x, dst_rows=rows, cap=30)
+    rc, rs = O.mxfp4_quantize(x)
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    for t, r in enumerate(rows):
+        if 0 <= r < 30:
+            assert np.array_equal(c[r], rc[t]) and np.array_equal(s[r], rs[t])
+
+
+class MxCase(IndexCase):
+    """IndexCase whose keys are also stored as MXFP4 (packed on the GPU, checked bit-exact).
+    scale_rows: every key row is multiplied by its own power of two 2^K, K in [-60, 60], so the
+    E8M0 codes span a wide range while every score stays an exact fp32 value."""
+
+    def __init__(self, *a, scale_rows=False, **kw):
+        super().__init__(*a, **kw)
+        if scale_rows:
+            K = np.random.default_rng(self.rows).integers(-60, 61, size=self.rows)
+            f = synth.bf16_bits_to_f32(self.k) * np.ldexp(np.float32(1.0), K)[:, None].astype(np.float32)
+            self.k = synth.f32_to_bf16_bits(f)
+            self.k_dev = bf16_tensor(self.k)
+        self.kc_ref, self.ks_ref = O.mxfp4_quantize(self.k)
+        self.kc, self.ks = _append(self.k)
+        assert np.array_equal(self.kc.cpu().numpy(), self.kc_ref)
+        assert np.array_equal(self.ks.cpu().numpy(), self.ks_ref)
+
+    def run_full_mx(self, top_k, pool_blocks):
+        n_q = len(self.lengths)
+        ws = C.alloc_workspace(C.csa2_workspace_bytes(C.OP_INDEX_FULL, n_q, self.seqs.total_len_ub,
+                                                      self.seqs.max_len_ub, top_k, pool_blocks))
+        idx = torch.full((n_q, top_k), -7, dtype=torch.int32, device=DEV)
+        pool = torch.full((n_q, max(pool_blocks, 1)), -7, dtype=torch.int32, device=DEV) if pool_blocks else None
+        C.csa2_index_full_mx(self.q_dev, self.w_dev, self.kc, self.ks, self.seqs, top_k, pool_blocks, idx, pool, ws)
+        torch.cuda.synchronize()
+        return idx, pool
+
+    def run_reindex_mx(self, pool, top_k, q_dev=None, w_dev=None):
+        n_q = len(self.lengths)
+        ws = C.alloc_workspace(C.csa2_workspace_bytes(C.OP_INDEX_REINDEX, n_q, 0, 0, top_k, pool.shape[1]))
+        idx = torch.full((n_q, top_k), -7, dtype=torch.int32, device=DEV)
+        C.csa2_index_reindex_mx(self.q_dev if q_dev is None else q_dev, self.w_dev if w_dev is None else w_dev,
+                                self.kc, self.ks, self.seqs, pool, top_k, idx, ws)
+        torch.cuda.synchronize()
+        return idx
+
+    def oracle_full_mx(self, i, top_k, pool_blocks):
+        r0, n = int(self.row0[i]), int(self.lengths[i])
+        return O.index_full_mx(self.q[i], self.w[i], self.kc_ref[r0:r0 + max(n, 0)], self.ks_ref[r0:r0 + max(n, 0)],
+                               n, top_k, 8, pool_blocks)
+
+
+RAGGED = [0, 1, 7, 9, 511, 513, 2047, 2049, 4101, 20000, 70000]
+
+
+@pytest.mark.parametrize("scale_rows", [False, True])
+def test_index_full_mx_bit_exact(scale_rows):
+    case = MxCase(W_MX + 2, RAGGED, n_heads=4, scale_rows=scale_rows)
+    idx, pool = case.run_full_mx(512, 300)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for i in range(len(RAGGED)):
+        ri, rp = case.oracle_full_mx(i, 512, 300)
+        assert np.array_equal(idx[i], ri), (i, RAGGED[i])
+        assert np.array_equal(pool[i], rp), (i, RAGGED[i])
+    if not scale_rows:       # integer keys are exact: the same selection as bf16 keys
+        idx_b, pool_b, _ = case.run_full(512, 300)
+        assert np.array_equal(idx_b.cpu().numpy(), idx) and np.array_equal(pool_b.cpu().numpy(), pool)
+
+
+def test_index_full_mx_eight_heads_and_small_k():
+    case = MxCase(W_MX + 3, [100, 5000, 33], n_heads=8)
+    idx, _ = case.run_full_mx(7, 0)
+    idx = idx.cpu().numpy()
+    for i in range(3):
+        assert np.array_equal(idx[i], case.oracle_full_mx(i, 7, 0)[0]), i
+
+
+def test_index_reindex_mx_bit_exact():
+    lengths = [4096, 65536, 777, 30001]
+    case = MxCase(W_MX + 4, lengths, n_heads=4, scale_rows=True)
+    idx_f, pool = case.run_full_mx(512, 2048)
+    pool_np = pool.cpu().numpy()
+    q2 = synth.int_bf16(W_MX + 4, synth.T_IDX_Q, (len(lengths), 4, 64), seq=9)
+    w2 = synth.int_weights(W_MX + 4, synth.T_IDX_W, (len(lengths), 4), seq=9)
+    idx2 = case.run_reindex_mx(pool, 512, q_dev=bf16_tensor(q2), w_dev=torch.from_numpy(w2).to(DEV)).cpu().numpy()
+    for i in range(len(lengths)):
+        r0, n = int(case.row0[i]), int(lengths[i])
+        ref = O.index_reindex_mx(q2[i], w2[i], case.kc_ref[r0:r0 + n], case.ks_ref[r0:r0 + n], n, pool_np[i], 512, 8)
+        assert np.array_equal(idx2[i], ref), i
