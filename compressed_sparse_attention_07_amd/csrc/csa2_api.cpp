@@ -11,7 +11,7 @@ namespace csa2 {
 
 // ---- mirrored from the kernels (kept in one place here) ----
 #ifndef CSA2_SCAN_TILE
-#define CSA2_SCAN_TILE 2048
+#define CSA2_SCAN_TILE 4096
 #endif
 constexpr int kFullTile = CSA2_SCAN_TILE;  // must match the scan kernel's tile
 constexpr int kFilterTile = 16384;

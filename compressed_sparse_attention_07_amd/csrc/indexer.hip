@@ -13,15 +13,17 @@
 // Score of position p for one query: sum_h w_h * max(0, q_h . k_p)  (fp32; exact for
 // integer-valued inputs below 2^24).
 //
-// Decode scan (VALU; 4 bytes of arithmetic per byte moved is far below the fp32 ridge,
-// so the scan is HBM-bound and stays off the matrix cores):
-//   * 4 lanes share one 128-byte key row: lane j loads bytes [16j,16j+16) and
-//     [64+16j, 64+16j+16), so one wave instruction moves 16 rows (2 KiB over two loads)
-//     and each 128-byte line is consumed whole by one wave;
-//   * each lane does 8 v_dot2_f32_bf16 per head, two DPP adds finish the row's dot;
-//   * the row's key (order-preserving u32 of the score) is stored; the 8-row block
-//     maximum and the top-11-bit histogram of both are fused in (LDS histograms,
-//     flushed with integer atomics).
+// Decode scan (HBM-bound: 4 flop per key byte for bf16 keys): the dot products run on MFMA
+// (v_mfma_f32_16x16x32_bf16), which leaves the vector ALUs to the per-position epilogue:
+//   * bf16 keys: 4 lanes share one 128-byte key row (lane group g loads bytes [16g, 16g+16)
+//     and [64+16g, 64+16g+16)), so one wave instruction moves 16 whole rows; heads sit on the
+//     MFMA's M rows and 16 positions on N, so lanes 0..15 end with one score each;
+//   * MXFP4 keys (34 bytes per position, so the epilogue rather than HBM sets the pace): the
+//     lane-per-position layout, 64 positions per wave step with a score in every lane, each
+//     lane converting its own row with the hardware E2M1 -> bf16 conversion;
+//   * the row's key (order-preserving u32 of the score) is stored; the 8-row block maximum
+//     and the top-11-bit histogram of both are fused in (LDS histograms, flushed with
+//     integer atomics).
 // Kernels hand data to each other only across kernel boundaries (no device-scope fences
 // inside a kernel: on a multi-XCD part such a fence writes back the L2).
 //   Full:    scan (keys, block-max keys, histograms)
@@ -30,6 +32,8 @@
 //               threshold-bucket candidates to a candidate list, one global atomic per list)
 //            -> select (one workgroup per query and list: exact order inside the bucket).
 //   Reindex: score (pool positions) -> select (one workgroup per query).
+#include <type_traits>
+
 #include "csa2_device.hpp"
 
 namespace csa2 {
@@ -41,7 +45,7 @@ constexpr int kScoreNT = 256;
 //   CSA2_SCAN_NT    streaming (slc) key loads,
 //   CSA2_SCAN_WGS_PER_CU  resident workgroups of the persistent scan per compute unit.
 #ifndef CSA2_SCAN_TILE
-#define CSA2_SCAN_TILE 2048
+#define CSA2_SCAN_TILE 4096
 #endif
 #ifndef CSA2_SCAN_U
 #define CSA2_SCAN_U 8
@@ -50,23 +54,31 @@ constexpr int kScoreNT = 256;
 #define CSA2_SCAN_NT 0
 #endif
 #ifndef CSA2_SCAN_WGS_PER_CU
-#define CSA2_SCAN_WGS_PER_CU 64
+#define CSA2_SCAN_WGS_PER_CU 4
+#endif
+//   CSA2_SCAN_U_LP  256-position steps per load batch in the lane-per-position layout,
+//   CSA2_SCAN_LP_BF16  bf16 keys also take the lane-per-position layout (MXFP4 keys always do).
+#ifndef CSA2_SCAN_U_LP
+#define CSA2_SCAN_U_LP 4
+#endif
+#ifndef CSA2_SCAN_LP_BF16
+#define CSA2_SCAN_LP_BF16 0
 #endif
 constexpr int kFullTile = CSA2_SCAN_TILE;       // positions per Full-scan workgroup
-constexpr int kFullTileBlocks = kFullTile / 8;  // 256 blocks
+constexpr int kFullTileBlocks = kFullTile / 8;
 constexpr int kReindexTile = 512;               // pool positions (64 blocks) per Reindex workgroup
-constexpr int kFilterTile = 16384;              // positions per filter workgroup (8 scan tiles)
+constexpr int kFilterTile = 16384;              // positions per filter workgroup (4 scan tiles)
 
 struct IndexWs {
     uint32_t* ctrl;      // [n_q][kCtlSlots]          self-cleaning counters
     uint32_t* hist;      // [n_q][2][2048]            self-cleaning histograms
     Thresh* meta;        // [n_q][2]
-    uint32_t* keys;      // [grid_tiles * 2048]       per-position keys (Full) / per-candidate keys (Reindex)
-    uint32_t* bkeys;     // [grid_tiles * 256]        per-block max keys
+    uint32_t* keys;      // [grid_tiles * kFullTile]  per-position keys (Full) / per-candidate keys (Reindex)
+    uint32_t* bkeys;     // [grid_tiles * kFullTile / 8] per-block max keys
     int32_t* sure_idx;   // [n_q][top_k]
     int32_t* sure_pool;  // [n_q][pool_blocks]
-    uint64_t* cand_idx;  // [grid_tiles * 2048]       threshold-bucket composites
-    uint64_t* cand_pool; // [grid_tiles * 256]
+    uint64_t* cand_idx;  // [grid_tiles * kFullTile]  threshold-bucket composites
+    uint64_t* cand_pool; // [grid_tiles * kFullTile / 8]
     QMeta* qmeta;        // [n_q]                      per-query length and tile ranges (prep kernel)
     int32_t* tmap;       // [grid_tiles]               scan tile -> query (-1: unused)
     int32_t* fmap;       // [grid_ftiles]              filter tile -> query (-1: unused)
@@ -135,6 +147,35 @@ __device__ __forceinline__ void load_qfrag(QFrag& qf, const uint16_t* q, const f
     for (int i = 0; i < 4; ++i) qf.w[i] = (4 * g + i < n_heads) ? w[4 * g + i] : 0.f;
 }
 
+// Lane-per-position layout (at most 4 indexer heads): 64 positions per wave step, lane l
+// holding position l.  Eight k-steps of 8 channels each cover the 64 channels; in k-step s,
+// lane (g, r) supplies channels 8s .. 8s + 7 of its own position as column r, K slots
+// 8g .. 8g + 7 of B, and A is block-diagonal: row 4g + h holds head h's channels 8s .. 8s + 7
+// in K slots 8g .. 8g + 7 and zeros elsewhere.  Then D[4g + h][r] sums only lane group g's
+// slots, i.e. head h times the position of lane 16g + r, and the accumulator of lane l ends
+// up with all four heads of ITS position: every lane carries a score (the M rows and K slots
+// spent on zeros are the price, the same MFMA count as the layout above).
+struct QFragLP {
+    bf16x8_t a[8];  // k-step s: head (r & 3)'s channels 8s .. 8s + 7 when r / 4 == g, else zeros
+    float w[4];     // weights of heads 0 .. 3 (0 past n_heads)
+};
+
+__device__ __forceinline__ void load_qfrag_lp(QFragLP& qf, const uint16_t* q, const float* w, int n_heads,
+                                              int lane) {
+    const int g = lane >> 4, r = lane & 15, h = r & 3;
+    const bool on = (r >> 2) == g && h < n_heads;
+    const uint16_t* qp = q + (on ? h : 0) * 64;
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+        qf.a[s2] = as_bf16x8(on ? *reinterpret_cast<const uint4*>(qp + 8 * s2) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qf.w[i] = i < n_heads ? w[i] : 0.f;
+}
+
+__device__ __forceinline__ float relu(float x) {
+    return __builtin_elementwise_maximum(x, 0.f);  // one v_maximum3_f32 (fmaxf adds a canonicalize)
+}
+
 // Score of position r in lanes 0..15 (kb: the lane's two 16-byte slices of that position).
 template <int HI>
 __device__ __forceinline__ float mfma_score(const QFrag& qf, const uint4& k0, const uint4& k1) {
@@ -181,7 +222,7 @@ __device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t k) {
 
 // ----------------------------------------------------------------------------------------
 // Full mode, kernel 0: per-query metadata.  Query i owns max(1, ceil(n_i / tile)) consecutive
-// scan tiles (2,048 positions) and filter tiles (16,384), clamped so the map fits the grids the
+// scan tiles (kFullTile positions) and filter tiles (16,384), clamped so the map fits the grids the
 // host sized from its bounds (every query keeps at least one tile of each).  One workgroup.
 // ----------------------------------------------------------------------------------------
 constexpr int kPrepNT = 1024;
@@ -260,11 +301,15 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
 // ----------------------------------------------------------------------------------------
 // Persistent: the grid holds a few workgroups per CU and workgroup g streams the contiguous
 // tile range [g * T / G, (g + 1) * T / G) of the tile map, so the per-tile set-up (tile map,
-// query slice) is paid once per query rather than once per 256 KB tile, and the first-digit
+// query slice) is paid once per query rather than once per tile, and the first-digit
 // histograms go to the workspace only when the query changes.
 // MX: keys are MXFP4 (k_idx = code bytes [rows, 32], k_sc = E8M0 bytes [rows, 2]) instead of
 // bf16 (k_idx = [rows, 64] bf16, k_sc unused).
-template <int HI, bool MX>
+// LP: the lane-per-position layout (QFragLP; at most 4 heads): a wave step covers 64
+// positions with one score per lane, so the per-position epilogue (ReLU-weighted head sum,
+// key, stores, histogram atomics, block maximum) costs a quarter of the instructions of the
+// 16-position layout; the lane reads its own row (16-byte loads, 32 B per MXFP4 row).
+template <int HI, bool MX, bool LP>
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx,
     const uint8_t* __restrict__ k_sc, const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len,
@@ -284,10 +329,11 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
         sh_hist[b] = 0u;
         sh_bhist[b] = 0u;
     }
+    static_assert(!LP || HI == 4, "the lane-per-position layout holds 4 heads");
     int cur = -1;  // query whose counts the LDS histograms hold
     QMeta qm{};
     int64_t row0 = 0;
-    QFrag qf;
+    std::conditional_t<LP, QFragLP, QFrag> qf;
     // add the LDS histograms of query `cur` to the workspace and clear them (after a barrier)
     auto flush = [&]() {
         uint32_t* gh = ws.hist + (int64_t)cur * 2 * kHistBins;
@@ -321,7 +367,10 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
             cur = i;
             qm = ws.qmeta[i];
             row0 = kv_row0[i];
-            load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
+            if constexpr (LP)
+                load_qfrag_lp(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
+            else
+                load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
         }
         const int n = qm.n;
         const int64_t key_base = (int64_t)qm.start * kFullTile;
@@ -333,45 +382,99 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
         constexpr int kRowB = MX ? 32 : 128;  // key bytes per position (codes only for MXFP4)
         const BufRsrc rs = tile_rsrc(static_cast<const uint8_t*>(k_idx) + (row0 + p_tile) * kRowB, rows_here * kRowB);
         const BufRsrc rss = tile_rsrc(MX ? k_sc + (row0 + p_tile) * 2 : nullptr, MX ? rows_here * 2 : 0);
-        const int voff = (16 * wid + r) * kRowB + (MX ? 4 : 16) * g;
-        const int voff_s = (16 * wid + r) * 2;
-        for (int b = 0; b < kFullTile; b += 64 * U) {
-            const int pb = p_tile + b;
-            if (pb >= n) break;
-            uint4 kb[U][2];
-            uint32_t kc[U][2], ks[U];
+        if constexpr (LP) {
+            // one step = 256 consecutive positions of the workgroup (64 per wave, one per lane)
+            constexpr int UL = CSA2_SCAN_U_LP;
+            constexpr int kLd = kRowB / 16;  // 16-byte loads per row
+            const int voff = (64 * wid + lane) * kRowB;
+            const int voff_s = (64 * wid + lane) * 2;
+            for (int b = 0; b < kFullTile; b += 256 * UL) {
+                const int pb = p_tile + b;
+                if (pb >= n) break;
+                uint4 kr[UL][kLd];
+                uint32_t ks[UL];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if constexpr (MX) {
-                    kc[u][0] = buf_ld4(rs, voff, (b + 64 * u) * kRowB);
-                    kc[u][1] = buf_ld4(rs, voff + 16, (b + 64 * u) * kRowB);
-                    ks[u] = buf_ld2(rss, voff_s, (b + 64 * u) * 2);
-                } else {
-                    kb[u][0] = buf_ld16(rs, voff, (b + 64 * u) * kRowB);
-                    kb[u][1] = buf_ld16(rs, voff + 64, (b + 64 * u) * kRowB);
+                for (int u = 0; u < UL; ++u) {
+#pragma unroll
+                    for (int j = 0; j < kLd; ++j) kr[u][j] = buf_ld16(rs, voff + 16 * j, (b + 256 * u) * kRowB);
+                    if constexpr (MX) ks[u] = buf_ld2(rss, voff_s, (b + 256 * u) * 2);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // every load of the batch goes out first
+#pragma unroll
+                for (int u = 0; u < UL; ++u) {
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s2 = 0; s2 < 8; ++s2) {
+                        uint4 kf;
+                        if constexpr (MX) {  // k-step s2 lies in scale block s2 / 4
+                            const uint4& c = kr[u][s2 >> 2];
+                            const uint32_t dw = (s2 & 3) == 0 ? c.x : (s2 & 3) == 1 ? c.y : (s2 & 3) == 2 ? c.z : c.w;
+                            kf = mx_frag(dw, s2 < 4 ? (ks[u] & 0xffu) : (ks[u] >> 8));
+                        } else {
+                            kf = kr[u][s2];
+                        }
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.a[s2], as_bf16x8(kf), acc, 0, 0, 0);
+                    }
+                    float sc = 0.f;
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) sc = fmaf(qf.w[h], relu(acc[h]), sc);
+                    const int p = pb + 256 * u + 64 * wid + lane;
+                    const bool mine = p < n;
+                    const uint32_t key = mine ? score_key(sc) : 0u;
+                    if (mine) {
+                        ws.keys[key_base + p] = key;
+                        atomicAdd(&sh_hist[key >> 21], 1u);
+                    }
+                    if (want_pool) {
+                        const uint32_t bk = max_over_8_lanes(key);  // lanes 8k + 4: block of lanes 8k .. 8k + 7
+                        if ((lane & 7) == 4 && p - 4 < n) {
+                            ws.bkeys[key_base / 8 + ((p - 4) >> 3)] = bk;
+                            atomicAdd(&sh_bhist[bk >> 21], 1u);
+                        }
+                    }
                 }
             }
+        } else {
+            const int voff = (16 * wid + r) * kRowB + (MX ? 4 : 16) * g;
+            const int voff_s = (16 * wid + r) * 2;
+            for (int b = 0; b < kFullTile; b += 64 * U) {
+                const int pb = p_tile + b;
+                if (pb >= n) break;
+                uint4 kb[U][2];
+                uint32_t kc[U][2], ks[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int p0 = pb + 64 * u + 16 * wid;  // first of this wave's 16 positions
-                const int p = p0 + r;
-                if constexpr (MX) {
-                    kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
-                    kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
+                for (int u = 0; u < U; ++u) {
+                    if constexpr (MX) {
+                        kc[u][0] = buf_ld4(rs, voff, (b + 64 * u) * kRowB);
+                        kc[u][1] = buf_ld4(rs, voff + 16, (b + 64 * u) * kRowB);
+                        ks[u] = buf_ld2(rss, voff_s, (b + 64 * u) * 2);
+                    } else {
+                        kb[u][0] = buf_ld16(rs, voff, (b + 64 * u) * kRowB);
+                        kb[u][1] = buf_ld16(rs, voff + 64, (b + 64 * u) * kRowB);
+                    }
                 }
-                const float sc = mfma_score<HI>(qf, kb[u][0], kb[u][1]);
-                const bool mine = g == 0 && p < n;
-                const uint32_t key = mine ? score_key(sc) : 0u;
-                if (mine) {
-                    ws.keys[key_base + p] = key;
-                    atomicAdd(&sh_hist[key >> 21], 1u);
-                }
-                if (want_pool) {
-                    const uint32_t bk = max_over_8_lanes(key);
-                    const int pblk = p0 + (r & 8);  // the 8-position pool block of lanes 4 / 12
-                    if (g == 0 && (r & 7) == 4 && pblk < n) {
-                        ws.bkeys[key_base / 8 + (pblk >> 3)] = bk;
-                        atomicAdd(&sh_bhist[bk >> 21], 1u);
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int p0 = pb + 64 * u + 16 * wid;  // first of this wave's 16 positions
+                    const int p = p0 + r;
+                    if constexpr (MX) {
+                        kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
+                        kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
+                    }
+                    const float sc = mfma_score<HI>(qf, kb[u][0], kb[u][1]);
+                    const bool mine = g == 0 && p < n;
+                    const uint32_t key = mine ? score_key(sc) : 0u;
+                    if (mine) {
+                        ws.keys[key_base + p] = key;
+                        atomicAdd(&sh_hist[key >> 21], 1u);
+                    }
+                    if (want_pool) {
+                        const uint32_t bk = max_over_8_lanes(key);
+                        const int pblk = p0 + (r & 8);  // the 8-position pool block of lanes 4 / 12
+                        if (g == 0 && (r & 7) == 4 && pblk < n) {
+                            ws.bkeys[key_base / 8 + (pblk >> 3)] = bk;
+                            atomicAdd(&sh_bhist[bk >> 21], 1u);
+                        }
                     }
                 }
             }
@@ -923,8 +1026,9 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
                                static_cast<const uint16_t*>(k_idx), kv_row0, n_q, cache_rows, n_heads, ws);
         } else {
             const int wgs = min(grid_tiles, scan_workgroups());
-            auto kern = mx ? (n_heads <= 4 ? k_idx_score_full<4, true> : k_idx_score_full<8, true>)
-                           : (n_heads <= 4 ? k_idx_score_full<4, false> : k_idx_score_full<8, false>);
+            auto kern = mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true> : k_idx_score_full<8, true, false>)
+                           : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0>
+                                           : k_idx_score_full<8, false, false>);
             hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, q_idx, w, k_idx, k_sc, kv_row0, kv_len,
                                n_q, max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
         }

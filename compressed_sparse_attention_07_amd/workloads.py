@@ -1,5 +1,8 @@
-"""The five CSA2 workloads this library is built and measured on, and a driver that runs one
-decode step (or one prefill chunk) of a workload through the C ABI.
+"""The CSA2 workloads this library is built and measured on, and a driver that runs one decode
+step (or one prefill chunk) of a workload through the C ABI.  Workloads 0-4 are the five
+configurations of the problem statement; 5-7 are the 1M-context decode with the pages' storage
+formats of section XI of [Article]: an FP8 window store with SWA Bounded Replay starts (5),
+MXFP4 indexer keys (6), and both (7).
 
 Mode schedule ([Article] "DeepSeek-V4.1-Flash: Pushing KV Cache Compression to 890 Bytes per
 Token", section VIII, and the [Summary] page's Technical Approach):
@@ -44,6 +47,8 @@ class Workload:
                                    # per-sequence replay starts ([Article] XII): even sequences replay
                                    # their last replay_tail positions, odd ones have no bound
     replay_tail: int = 64
+    keys_mx: bool = False          # indexer keys stored as MXFP4 ([Article] XI: E2M1 + E8M0 per 32
+                                   # channels); the step also appends each new token's key
 
     def lengths(self) -> np.ndarray:
         if self.ragged:
@@ -65,6 +70,9 @@ WORKLOADS = {
     3: Workload(3, "prefill_4096_on_128k", 1, 131072, "F", 0, prefill_chunk=4096, appends=True),
     4: Workload(4, "decode_b64_ragged_1k_1m_4layers", 64, None, "FUFU", 0, ragged=(1024, 1 << 20)),
     5: Workload(5, "decode_b8_1m_20layers_fp8win_replay", 8, 1 << 20, c2_layers(20), 2048, window_fp8=True),
+    6: Workload(6, "decode_b8_1m_20layers_mxkeys", 8, 1 << 20, c2_layers(20), 2048, keys_mx=True),
+    7: Workload(7, "decode_b8_1m_20layers_mxkeys_fp8win_replay", 8, 1 << 20, c2_layers(20), 2048,
+                window_fp8=True, keys_mx=True),
 }
 
 
@@ -74,12 +82,21 @@ def bf16_dev(bits: np.ndarray, device="cuda") -> torch.Tensor:
 
 @dataclass
 class KvSet:
-    """One owned main-KV set (FP4) plus its indexer keys, sequences back to back."""
+    """One owned main-KV set (FP4) plus its indexer keys, sequences back to back.  The keys are
+    bf16 rows (k_idx) or MXFP4 rows (k_codes [rows, 32] + k_scales [rows, 2]), never both."""
     codes: torch.Tensor
     scales: torch.Tensor
-    k_idx: torch.Tensor
+    k_idx: torch.Tensor | None
     x_new: torch.Tensor       # bf16 [B, 128]: the step's new token per sequence (post-RoPE)
     new_rows: torch.Tensor    # int64 [B]: row each new token is written to
+    k_codes: torch.Tensor | None = None
+    k_scales: torch.Tensor | None = None
+    k_new: torch.Tensor | None = None    # bf16 [B, 64]: the step's new indexer key (MXFP4 sets)
+
+    def clone(self) -> "KvSet":
+        c = lambda t: None if t is None else t.clone()
+        return KvSet(self.codes.clone(), self.scales.clone(), c(self.k_idx), self.x_new, self.new_rows,
+                     c(self.k_codes), c(self.k_scales), self.k_new)
 
 
 @dataclass
@@ -146,22 +163,36 @@ class Runner:
             # the cache before the step: every row but the new tokens' rows
             x_dev = bf16_dev(x, device)
             C.fp4_kv_append(x_dev, codes, scales)
-            x_new = x_dev[torch.from_numpy(new_rows).to(device)].contiguous()
+            new_rows_t = torch.from_numpy(new_rows).to(device)
+            x_new = x_dev[new_rows_t].contiguous()
             del x_dev
-            self.sets.append(KvSet(codes, scales, bf16_dev(k, device), x_new, torch.from_numpy(new_rows).to(device)))
+            k_dev = bf16_dev(k, device)
+            if wl.keys_mx:   # keys written by the library's MXFP4 append; the bf16 rows are dropped
+                kc = torch.empty((total_rows, 32), dtype=torch.uint8, device=device)
+                ks = torch.empty((total_rows, 2), dtype=torch.uint8, device=device)
+                C.mxfp4_key_append(k_dev, kc, ks)
+                st = KvSet(codes, scales, None, x_new, new_rows_t, kc, ks, k_dev[new_rows_t].contiguous())
+            else:
+                st = KvSet(codes, scales, k_dev, x_new, new_rows_t)
+            del k_dev
+            self.sets.append(st)
             if self.host is not None:
                 self.host.setdefault("x", []).append(x)
                 self.host.setdefault("k_idx", []).append(k)
                 self.host.setdefault("new_rows", []).append(new_rows)
             del x, k
         # Scramble the new tokens' rows so the step's append is what makes them correct.
+        # (An MXFP4 key row becomes +6 * 2^10 in every channel: a large score, so a missing key
+        # append would change the selection.)
         for st in self.sets:
             st.codes[st.new_rows] = 0xEE
             st.scales[st.new_rows] = 0x77
+            if st.k_codes is not None:
+                st.k_codes[st.new_rows] = 0x77
+                st.k_scales[st.new_rows] = 127 + 10
         self.copies = [self.sets]
         for _ in range(1, copies):
-            self.copies.append([KvSet(st.codes.clone(), st.scales.clone(), st.k_idx.clone(), st.x_new, st.new_rows)
-                                for st in self.sets])
+            self.copies.append([st.clone() for st in self.sets])
         self._next_copy = 0
         # layers
         self.swa_cap = wl.window + (wl.prefill_chunk or 0)
@@ -235,6 +266,8 @@ class Runner:
         if wl.appends:
             for st in self.sets:
                 C.fp4_kv_append(st.x_new, st.codes, st.scales, dst_rows=st.new_rows, stream=stream)
+                if wl.keys_mx:
+                    C.mxfp4_key_append(st.k_new, st.k_codes, st.k_scales, dst_rows=st.new_rows, stream=stream)
         pool_built = False
         for L in self.layers:
             st = self.sets[L.kv_set]
@@ -242,23 +275,32 @@ class Runner:
                 want_pool = wl.pool_blocks if (self.pool is not None and not pool_built) else 0
                 pool = self.pool if want_pool else None
                 shared = 1 if wl.prefill_chunk else 0   # a prefill chunk: all queries read one sequence
-                C.csa2_index_full_prep(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
+                keys = st.k_codes if wl.keys_mx else st.k_idx    # prep and select read no keys
+                C.csa2_index_full_prep(L.q_idx, L.w, keys, self.seqs, wl.top_k, want_pool, L.idx, pool,
                                        self.ws_full, shared_kv=shared, stream=stream)
                 if scan_events is not None:
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record()
-                C.csa2_index_full_scan(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
-                                       self.ws_full, shared_kv=shared, stream=stream)
+                if wl.keys_mx:
+                    C.csa2_index_full_mx_scan(L.q_idx, L.w, st.k_codes, st.k_scales, self.seqs, wl.top_k, want_pool,
+                                              L.idx, pool, self.ws_full, shared_kv=shared, stream=stream)
+                else:
+                    C.csa2_index_full_scan(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
+                                           self.ws_full, shared_kv=shared, stream=stream)
                 if scan_events is not None:
                     e1.record()
                     scan_events.append((e0, e1))
-                C.csa2_index_full_select(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
+                C.csa2_index_full_select(L.q_idx, L.w, keys, self.seqs, wl.top_k, want_pool, L.idx, pool,
                                          self.ws_full, shared_kv=shared, stream=stream)
                 pool_built = pool_built or want_pool > 0
                 idx = L.idx
             elif L.mode == "R":
-                C.csa2_index_reindex(L.q_idx, L.w, st.k_idx, self.seqs, self.pool, wl.top_k, L.idx, self.ws_re,
-                                     stream=stream)
+                if wl.keys_mx:
+                    C.csa2_index_reindex_mx(L.q_idx, L.w, st.k_codes, st.k_scales, self.seqs, self.pool, wl.top_k,
+                                            L.idx, self.ws_re, stream=stream)
+                else:
+                    C.csa2_index_reindex(L.q_idx, L.w, st.k_idx, self.seqs, self.pool, wl.top_k, L.idx, self.ws_re,
+                                         stream=stream)
                 idx = L.idx
             else:
                 idx = self.layers[L.idx_src].idx
@@ -296,15 +338,16 @@ class Runner:
         n_sum = int(self.q_len.sum())
         out = {"append": 0, "index_full": 0, "index_reindex": 0, "attend": 0}
         n_sets = len(self.sets)
+        key_bytes = 34 if wl.keys_mx else 128                     # MXFP4 or bf16 indexer key
         if wl.appends:
             toks = (wl.prefill_chunk or self.n_q) * n_sets
-            out["append"] = toks * (256 + 72)
+            out["append"] = toks * (256 + 72 + ((128 + 34) if wl.keys_mx else 0))
         for L in self.layers:
             if L.mode == "F":
-                out["index_full"] += n_sum * 128                   # every visible indexer key, once
+                out["index_full"] += n_sum * key_bytes             # every visible indexer key, once
             elif L.mode == "R":
                 cand = self.n_q * min(wl.pool_blocks * 8, int(self.q_len.max()))
-                out["index_reindex"] += cand * 128
+                out["index_reindex"] += cand * key_bytes
             win = np.minimum(self.q_len, wl.window)
             win_bytes = 256                                         # bf16 window entry
             if wl.window_fp8:

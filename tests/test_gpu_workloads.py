@@ -1,6 +1,7 @@
-"""Parity at the full sizes of the five workloads, in the launch configuration the benchmark
-times (workloads.Runner.step), checked on sampled outputs the CPU oracle computes one by one:
-FP4 rows bit-exact, Top-K indices and pools bit-exact, attention within 2e-3 * max|V|."""
+"""Parity at the full sizes of the workloads, in the launch configuration the benchmark times
+(workloads.Runner.step), checked on sampled outputs the CPU oracle computes one by one: FP4 rows,
+E4M3 window bytes and MXFP4 key rows bit-exact, Top-K indices and pools bit-exact, attention
+within 2e-3 * max|V|."""
 import numpy as np
 import pytest
 import torch
@@ -24,6 +25,10 @@ def _check_step(r, queries, rows_sample=2000):
         c_ref, s_ref = O.fp4_quantize(h["x"][s][rows])
         assert np.array_equal(st.codes[rows_t].cpu().numpy(), c_ref), f"codes set {s}"
         assert np.array_equal(st.scales[rows_t].cpu().numpy(), s_ref), f"scales set {s}"
+        if wl.keys_mx:
+            kc_ref, ks_ref = O.mxfp4_quantize(h["k_idx"][s][rows])
+            assert np.array_equal(st.k_codes[rows_t].cpu().numpy(), kc_ref), f"mx key codes set {s}"
+            assert np.array_equal(st.k_scales[rows_t].cpu().numpy(), ks_ref), f"mx key scales set {s}"
     worst = 0.0
     for i in queries:
         r0, n = int(r.q_row0[i]), int(r.q_len[i])
@@ -32,14 +37,23 @@ def _check_step(r, queries, rows_sample=2000):
         for l, L in enumerate(r.layers):
             if L.mode == "F":
                 cur += 1
-                idx_ref, p = O.index_full(h["q_idx"][l][i], h["w"][l][i], h["k_idx"][cur][r0:r0 + n], n, wl.top_k,
-                                          8, wl.pool_blocks if (pool_ref is None and wl.pool_blocks) else 0)
+                want = wl.pool_blocks if (pool_ref is None and wl.pool_blocks) else 0
+                if wl.keys_mx:    # the oracle's own MXFP4 keys of this sequence
+                    kc_seq, ks_seq = O.mxfp4_quantize(h["k_idx"][cur][r0:r0 + n])
+                    idx_ref, p = O.index_full_mx(h["q_idx"][l][i], h["w"][l][i], kc_seq, ks_seq, n, wl.top_k, 8, want)
+                else:
+                    idx_ref, p = O.index_full(h["q_idx"][l][i], h["w"][l][i], h["k_idx"][cur][r0:r0 + n], n,
+                                              wl.top_k, 8, want)
                 if p is not None:
                     pool_ref = p
                     assert np.array_equal(r.pool[i].cpu().numpy(), pool_ref), f"pool q{i}"
             elif L.mode == "R":
-                idx_ref = O.index_reindex(h["q_idx"][l][i], h["w"][l][i], h["k_idx"][cur][r0:r0 + n], n, pool_ref,
-                                          wl.top_k, 8)
+                if wl.keys_mx:
+                    idx_ref = O.index_reindex_mx(h["q_idx"][l][i], h["w"][l][i], kc_seq, ks_seq, n, pool_ref,
+                                                 wl.top_k, 8)
+                else:
+                    idx_ref = O.index_reindex(h["q_idx"][l][i], h["w"][l][i], h["k_idx"][cur][r0:r0 + n], n,
+                                              pool_ref, wl.top_k, 8)
             if L.mode in "FR":
                 assert np.array_equal(L.idx[i].cpu().numpy(), idx_ref), f"idx layer {l} q{i}"
             # attention over this layer's selection (Reuse: the inherited one)
@@ -101,6 +115,15 @@ def test_workload2_batch8_1m_20layers():
 def test_workload5_fp8_window_with_replay():
     # query 0 replays its last 64 positions (even), query 5 has no replay bound (odd)
     _run(5, [0, 5])
+
+
+def test_workload6_mxfp4_indexer_keys():
+    # one query: the oracle quantises that sequence's 2^20 keys (about 20 s on one core)
+    _run(6, [3])
+
+
+def test_workload7_mxfp4_keys_fp8_window_with_replay():
+    _run(7, [6])
 
 
 def test_workload3_prefill_4096_on_128k():
