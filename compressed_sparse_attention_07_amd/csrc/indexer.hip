@@ -494,11 +494,17 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
 // the scan's 16-byte slices.  The accumulator of lane (g, r) holds queries 4g+i at position r;
 // the lane folds its four heads (ReLU, weights), writes the keys and counts first digits in
 // an LDS histogram (two 16-bit counters per word: a workgroup counts at most kPfPos per bin).
+// POOL: every query also gets its own block pool ([Article] IX, applied per query of the
+// chunk): the lanes of one 16-lane row hold one query's 16 consecutive positions, so the
+// 8-position block maximum is the decode scan's DPP step.  The block keys are counted by
+// k_idx_block_hist afterwards, which keeps this kernel's LDS at one histogram (a second one
+// would halve the resident workgroups).
 // ----------------------------------------------------------------------------------------
 constexpr int kPfQ = 16;       // queries per workgroup
 constexpr int kPfPos = 4096;   // positions per workgroup (1,024 per wave)
 
 
+template <bool POOL>
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, IndexWs ws) {
@@ -590,12 +596,18 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
             for (int i = 0; i < 4; ++i) {
                 float sc = 0.f;
 #pragma unroll
-                for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], fmaxf(acc[h][i], 0.f), sc);
-                if (p < nq[i]) {
-                    const uint32_t key = score_key(sc);
+                for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], relu(acc[h][i]), sc);
+                const bool ok = p < nq[i];
+                const uint32_t key = ok ? score_key(sc) : 0u;
+                if (ok) {
                     ws.keys[bq[i] + p] = key;
                     const uint32_t bin = key >> 21;
                     atomicAdd(&sh_hist[4 * g + i][bin >> 1], 1u << (16 * (bin & 1)));
+                }
+                if constexpr (POOL) {
+                    const uint32_t bk = max_over_8_lanes(key);      // lanes 4 / 12 of the row
+                    const int pblk = base + 16 * u + (r & 8);
+                    if ((r & 7) == 4 && pblk < nq[i]) ws.bkeys[bq[i] / 8 + (pblk >> 3)] = bk;
                 }
             }
         }
@@ -609,6 +621,34 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
         if (v & 0xffffu) atomicAdd(&gh[2 * wd], v & 0xffffu);
         if (v >> 16) atomicAdd(&gh[2 * wd + 1], v >> 16);
     }
+}
+
+// First-digit histogram of each query's block-max keys (prefill chunk with pools): workgroup
+// (x, i) counts blocks [x * kBhChunk, (x + 1) * kBhChunk) of query i in LDS and adds them to
+// the query's block histogram.
+constexpr int kBhChunk = 8192;
+
+__global__ __launch_bounds__(kScoreNT) void k_idx_block_hist(const int64_t* __restrict__ kv_row0, int64_t cache_rows,
+                                                             IndexWs ws) {
+    __shared__ uint32_t sh[kHistBins];
+    const int t = threadIdx.x;
+    const int i = blockIdx.y;
+    const int64_t row0 = kv_row0[0];
+    const int64_t row_room = (row0 >= 0 && row0 <= cache_rows) ? cache_rows - row0 : 0;
+    const QMeta qm = ws.qmeta[i];
+    const int n = (int)min((int64_t)qm.n, row_room);  // the positions the scoring kernel wrote
+    const int nb = (n + 7) >> 3;
+    const int b0 = blockIdx.x * kBhChunk;
+    if (b0 >= nb) return;  // uniform
+    for (int b = t; b < kHistBins; b += kScoreNT) sh[b] = 0u;
+    __syncthreads();
+    const uint32_t* bk = ws.bkeys + (int64_t)qm.start * kFullTile / 8;
+    const int b1 = min(nb, b0 + kBhChunk);
+    for (int b = b0 + t; b < b1; b += kScoreNT) atomicAdd(&sh[bk[b] >> 21], 1u);
+    __syncthreads();
+    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins + kHistBins;
+    for (int b = t; b < kHistBins; b += kScoreNT)
+        if (sh[b]) atomicAdd(&gh[b], sh[b]);
 }
 
 // Compact one workgroup's share of a key array: elements whose first digit is above the threshold
@@ -1005,8 +1045,8 @@ static int scan_workgroups() {
 // ----------------------------------------------------------------------------------------
 // phase bits: 1 = prep kernel (per-query metadata and tile maps), 2 = scan kernel,
 // 4 = filter + select kernels; 7 = all.
-// prefill != 0: every query reads the same sequence (kv_row0[0]) and no pool is asked for, so
-// the scores come from the MFMA kernel that tiles 16 queries x 16 positions.
+// prefill != 0: every query reads the same sequence (kv_row0[0]), so the scores come from the
+// MFMA kernel that tiles 16 queries x 16 positions (with per-query block pools when asked).
 // mx != 0: k_idx holds MXFP4 code bytes and k_sc their E8M0 scales (never with prefill).
 hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
                              const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
@@ -1020,11 +1060,18 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
         if (e != hipSuccess) return e;
     }
     if (phase & 2) {
-        if (prefill) {
+        if (prefill && max_len > 0) {  // (no visible position anywhere: nothing to score)
             const dim3 grid((unsigned)((max_len + kPfPos - 1) / kPfPos), (unsigned)((n_q + kPfQ - 1) / kPfQ));
-            hipLaunchKernelGGL(k_idx_score_prefill, grid, dim3(kScoreNT), 0, stream, q_idx, w,
-                               static_cast<const uint16_t*>(k_idx), kv_row0, n_q, cache_rows, n_heads, ws);
-        } else {
+            hipLaunchKernelGGL(pool_blocks > 0 ? k_idx_score_prefill<true> : k_idx_score_prefill<false>, grid,
+                               dim3(kScoreNT), 0, stream, q_idx, w, static_cast<const uint16_t*>(k_idx), kv_row0, n_q,
+                               cache_rows, n_heads, ws);
+            if (pool_blocks > 0) {
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                const dim3 bgrid((unsigned)(((max_len + 7) / 8 + kBhChunk - 1) / kBhChunk), (unsigned)n_q);
+                hipLaunchKernelGGL(k_idx_block_hist, bgrid, dim3(kScoreNT), 0, stream, kv_row0, cache_rows, ws);
+            }
+        } else if (!prefill) {
             const int wgs = min(grid_tiles, scan_workgroups());
             auto kern = mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true> : k_idx_score_full<8, true, false>)
                            : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0>

@@ -2,7 +2,8 @@
 step (or one prefill chunk) of a workload through the C ABI.  Workloads 0-4 are the five
 configurations of the problem statement; 5-7 are the 1M-context decode with the pages' storage
 formats of section XI of [Article]: an FP8 window store with SWA Bounded Replay starts (5),
-MXFP4 indexer keys (6), and both (7).
+MXFP4 indexer keys (6), and both (7); 8 is a prefill chunk through a Full layer that gives every
+query token its own block pool, two Reindex layers inside those pools and a Reuse layer.
 
 Mode schedule ([Article] "DeepSeek-V4.1-Flash: Pushing KV Cache Compression to 890 Bytes per
 Token", section VIII, and the [Summary] page's Technical Approach):
@@ -73,6 +74,7 @@ WORKLOADS = {
     6: Workload(6, "decode_b8_1m_20layers_mxkeys", 8, 1 << 20, c2_layers(20), 2048, keys_mx=True),
     7: Workload(7, "decode_b8_1m_20layers_mxkeys_fp8win_replay", 8, 1 << 20, c2_layers(20), 2048,
                 window_fp8=True, keys_mx=True),
+    8: Workload(8, "prefill_4096_on_128k_4layers", 1, 131072, "FRRU", 2048, prefill_chunk=4096, appends=True),
 }
 
 

@@ -140,7 +140,10 @@ int fp8_window_append(const uint16_t* x, int64_t n_tok, int32_t dim, const int64
  *   idx_out device int32 [n_q, top_k]: the top_k positions under (score desc,
  *           position asc), written in ascending order, -1 padded when N_i < top_k.
  *   pool_out device int32 [n_q, pool_blocks] or NULL when pool_blocks == 0: block
- *           ids under (block max desc, block asc), ascending, -1 padded.
+ *           ids under (block max desc, block asc), ascending, -1 padded.  Each query
+ *           gets the pool of its own visible positions: in a decode batch that is the
+ *           sequence's shared pool; in a prefill chunk every query token has its own
+ *           (the Reindex layers of the chunk select inside each token's pool).
  * Score of position p: sum_h w[h] * max(0, q_h . k_p), accumulated in fp32; with
  * integer-valued inputs and |score| < 2^24 it is exact.  Scores are MFMA
  * contractions: heads x positions per query, or, for a prefill chunk (shared_kv != 0:

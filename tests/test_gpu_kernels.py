@@ -184,6 +184,37 @@ def test_index_prefill_mfma_arbitrary_lengths_and_ties():
         assert np.array_equal(idx_m[t], ri), t
 
 
+@pytest.mark.parametrize("pool_blocks", [300, 1, 2048])
+def test_index_prefill_mfma_per_query_pools(pool_blocks):
+    # a prefill chunk with pools: every query token gets the pool of its own visible positions
+    # (partial last blocks included), bit-exact against the oracle and the per-query decode path;
+    # then a Reindex layer over those per-query pools
+    lengths = [0, 1, 9, 4096, 4097, 9000, 3, 12345, 8191, 8192, 8193, 50, 7777, 2, 1000, 6000, 12000, 5]
+    case = SharedIndexCase(W_T + 60, 12345, lengths, n_heads=4)
+    idx_m, pool_m, _ = case.run_full(512, pool_blocks, shared_kv=1)
+    idx_v, pool_v, _ = case.run_full(512, pool_blocks, shared_kv=0)
+    idx_m, pool_m = idx_m.cpu().numpy(), pool_m.cpu().numpy()
+    assert np.array_equal(idx_m, idx_v.cpu().numpy()) and np.array_equal(pool_m, pool_v.cpu().numpy())
+    for t in range(len(lengths)):
+        ri, rp = case.oracle_full(t, 512, pool_blocks)
+        assert np.array_equal(idx_m[t], ri), t
+        assert np.array_equal(pool_m[t], rp), t
+    q2 = synth.int_bf16(W_T + 60, synth.T_IDX_Q, (len(lengths), 4, 64), seq=3)
+    w2 = synth.int_weights(W_T + 60, synth.T_IDX_W, (len(lengths), 4), seq=3)
+    idx2, _ = case.run_reindex(torch.from_numpy(pool_m).to(DEV), 512, q_dev=bf16_tensor(q2),
+                               w_dev=torch.from_numpy(w2).to(DEV))
+    idx2 = idx2.cpu().numpy()
+    for t in range(len(lengths)):
+        assert np.array_equal(idx2[t], case.oracle_reindex(t, pool_m[t], 512, q=q2[t], w=w2[t])), t
+
+
+def test_index_prefill_nothing_visible():
+    # a chunk of 16 queries that see no position at all: every output is -1 padding
+    case = SharedIndexCase(W_T + 61, 64, [0] * 16, n_heads=4)
+    idx, pool, _ = case.run_full(512, 300, shared_kv=1)
+    assert (idx.cpu().numpy() == -1).all() and (pool.cpu().numpy() == -1).all()
+
+
 # ---------------------------------------------------------------- Reindex mode
 def test_index_reindex_bit_exact_and_invariant():
     lengths = [4096, 65536, 777, 100, 30001]

@@ -133,6 +133,14 @@ def test_workload3_prefill_4096_on_128k():
     _check_step(r, [0, 1, 2047, 4095], rows_sample=500)
 
 
+def test_workload8_prefill_with_per_query_pools_and_reindex():
+    r = W.Runner(W.WORKLOADS[8], keep_host=True)
+    r.step()
+    torch.cuda.synchronize()
+    # first, second, middle and last token of the chunk: each has its own pool
+    _check_step(r, [0, 1, 2047, 4095], rows_sample=500)
+
+
 def test_workload4_ragged_64_sequences():
     r = W.Runner(W.WORKLOADS[4], keep_host=True)
     r.step()
