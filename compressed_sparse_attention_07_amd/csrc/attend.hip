@@ -62,6 +62,23 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
 
+// Element i of a small per-query array through the vector memory path (a raw buffer load):
+// vector loads are counted in order, so a wait for these leaves later loads in flight, while
+// a wait for a scalar load waits for every scalar load, kernel arguments included.
+__device__ __forceinline__ int64_t vload_i64(const int64_t* p, int i) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int64_t*>(p), (short)0, 0x7fffffff, 0x00020000);
+    typedef int i32x2_t __attribute__((ext_vector_type(2)));
+    const i32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, 0, i * 8, 0);
+    return (int64_t)(((uint64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0]);
+}
+
+__device__ __forceinline__ int32_t vload_i32(const int32_t* p, int i) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p), (short)0, 0x7fffffff, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, 0, i * 4, 0);
+}
+
 __device__ __forceinline__ uint32_t bf16_rne(float v) {
     uint32_t b = __float_as_uint(v);
     return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
@@ -132,30 +149,63 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
     const int l = t & 63;
     const int g = l >> 4;   // lane group
     const int r = l & 15;   // row / column within the 16
-    const int n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
-    int wc = min(window, n);  // window = the last wc positions of [0, n)
-    if (replay != nullptr) {
-        const int64_t s0 = replay[i] > 0 ? replay[i] : 0;
-        wc = (int)max((int64_t)0, min((int64_t)wc, (int64_t)n - s0));
-    }
-    const int64_t row0 = n > 0 ? kv_row0[i] : 0;
-    const bool win_ok = kWin && wc > 0;
-    const int64_t wrow0 = win_ok ? swa_row0[i] : 0;
-    const int nb4 = (kFp4 && n > 0) ? (top_k + 15) >> 4 : 0;  // FP4 blocks (none when nothing is visible)
-    const int nbw = win_ok ? (wc + 15) >> 4 : 0;              // window blocks
-    const int rounds = max((nb4 + kRoundFp4 - 1) / kRoundFp4, (nbw + kRoundWin - 1) / kRoundWin);
-
-    // ---- the round's index and window gathers: round 0's go out before the query is read ----
+    // ---- first level of loads: everything that needs only the query number goes out at once
+    // (the length and rows, the round-0 indices, the query), so the kernel pays one memory
+    // latency before the gathers rather than one per dependent load.  The per-query values
+    // go first, as vector loads (counted in order: waiting for them leaves the index and query
+    // loads in flight); absent arrays are replaced by a valid one whose value is unused. ----
+    int32_t len_raw = vload_i32(kv_len, i);
+    int64_t row0_raw = vload_i64(kv_row0, i);
+    int64_t wrow0_raw = vload_i64(kWin ? swa_row0 : kv_row0, i);
+    int64_t replay_raw = vload_i64(replay != nullptr ? replay : kv_row0, i);  // replay[i] when given
     int pos[kRB];     // selected positions of this lane's entry in each FP4 block (-1: none)
-    u32x4 wf[4];      // window entry: channels [32g, 32g+32) as bf16 (E4M3: wf[0..1] hold them)
-    bool wvalid = false;
-    auto issue_round = [&](int R) {
+    // indices of one round (lanes past top_k read entry 0 and are masked; a length of 0 masks
+    // every position later)
+    auto issue_idx = [&](int R) {
         const int b0 = R * kRoundFp4 + wave * kRB;
 #pragma unroll
         for (int j = 0; j < kRB; ++j) {
             const int e = 16 * (b0 + j) + r;
-            pos[j] = (b0 + j < nb4 && e < top_k) ? idx[(int64_t)i * top_k + e] : -1;
+            const int v = kFp4 ? idx[(int64_t)i * top_k + (e < top_k ? e : 0)] : -1;
+            pos[j] = e < top_k ? v : -1;
         }
+    };
+    issue_idx(0);
+    // Q^T fragments of head r, channels 32g + 8s .. + 7: bf16 as given (loaded now), and f16
+    // scaled by 2^qe (converted while round 0's gathers are in flight).  Rows r >= n_heads
+    // repeat head 0: every head's softmax is its own and only heads < n_heads are written.
+    u32x4 qb[4], qh[4];
+    float cf4 = 0.f;  // logit multiplier of the f16 contraction: scale_log2 * 2^-qe
+    {
+        const uint4* qp =
+            reinterpret_cast<const uint4*>(q + ((int64_t)i * n_heads + (r < n_heads ? r : 0)) * kD + 32 * g);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint4 v = qp[s];
+            qb[s] = u32x4{v.x, v.y, v.z, v.w};
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // an empty statement that takes and returns the four per-query values: every use of them
+    // comes after it, so no wait for them is placed in front of the index and query loads
+    asm volatile("" : "+v"(len_raw), "+v"(row0_raw), "+v"(wrow0_raw), "+v"(replay_raw));
+
+    const int n = eff_len_of(len_raw, row0_raw, max_len, cache_rows);
+    // window = the last wc positions of [0, n), none before the replay start (branch-free, so
+    // the replay load stays with the first level)
+    const int64_t s0 = (replay != nullptr && replay_raw > 0) ? replay_raw : 0;
+    const int wc = (int)max((int64_t)0, min((int64_t)min(window, n), (int64_t)n - s0));
+    const int64_t row0 = n > 0 ? row0_raw : 0;
+    const bool win_ok = kWin && wc > 0;
+    const int64_t wrow0 = win_ok ? wrow0_raw : 0;
+    const int nb4 = (kFp4 && n > 0) ? (top_k + 15) >> 4 : 0;  // FP4 blocks (none when nothing is visible)
+    const int nbw = win_ok ? (wc + 15) >> 4 : 0;              // window blocks
+    const int rounds = max((nb4 + kRoundFp4 - 1) / kRoundFp4, (nbw + kRoundWin - 1) / kRoundWin);
+
+    // ---- the round's window gathers (second level: they need the length) ----
+    u32x4 wf[4];      // window entry: channels [32g, 32g+32) as bf16 (E4M3: wf[0..1] hold them)
+    bool wvalid = false;
+    auto issue_win = [&](int R) {
         const int wb = R * kRoundWin + wave;
         int64_t sr = -1;
         const int ew = 16 * wb + r;
@@ -184,21 +234,8 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
             }
         }
     };
-    issue_round(0);
+    issue_win(0);
 
-    // Q^T fragments of head r, channels 32g + 8s .. + 7: bf16 as given (loaded now), and f16
-    // scaled by 2^qe (converted while round 0's gathers are in flight)
-    u32x4 qb[4], qh[4];
-    float cf4 = 0.f;  // logit multiplier of the f16 contraction: scale_log2 * 2^-qe
-    {
-        const bool hv = r < n_heads;
-        const uint4* qp = reinterpret_cast<const uint4*>(q + ((int64_t)i * n_heads + (hv ? r : 0)) * kD + 32 * g);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const uint4 v = hv ? qp[s] : make_uint4(0, 0, 0, 0);
-            qb[s] = u32x4{v.x, v.y, v.z, v.w};
-        }
-    }
     auto convert_q = [&]() {
         float amax = 0.f;
 #pragma unroll
@@ -230,7 +267,10 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
     const int tr_off = (4 * g + (r >> 2)) * kRowB + 8 * (r & 3);
 
     for (int R = 0; R < rounds; ++R) {
-        if (R > 0) issue_round(R);
+        if (R > 0) {
+            issue_idx(R);
+            issue_win(R);
+        }
         const int b0 = R * kRoundFp4 + wave * kRB;
         const int wb = R * kRoundWin + wave;
         const bool wblk = wb < nbw;

@@ -75,15 +75,17 @@ __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v &
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Valid length of query i: kv_len clamped to [0, max_len] and to the rows after kv_row0.
-__device__ __forceinline__ int32_t eff_len(const int32_t* kv_len, const int64_t* kv_row0, int i,
-                                           int32_t max_len, int64_t cache_rows) {
-    int64_t n = kv_len[i];
-    int64_t r0 = kv_row0[i];
+__device__ __forceinline__ int32_t eff_len_of(int64_t n, int64_t r0, int32_t max_len, int64_t cache_rows) {
     if (n < 0) n = 0;
     if (n > max_len) n = max_len;
     if (r0 < 0 || r0 > cache_rows) return 0;
     if (n > cache_rows - r0) n = cache_rows - r0;
     return (int32_t)n;
+}
+
+__device__ __forceinline__ int32_t eff_len(const int32_t* kv_len, const int64_t* kv_row0, int i,
+                                           int32_t max_len, int64_t cache_rows) {
+    return eff_len_of(kv_len[i], kv_row0[i], max_len, cache_rows);
 }
 
 // Inclusive prefix sum across a wave64 with DPP moves (no LDS round trips): Hillis-Steele
