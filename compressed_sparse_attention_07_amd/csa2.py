@@ -35,6 +35,7 @@ EXPORTS = (
     "csa2_index_reindex_mx",
     "csa2_attend",
     "csa2_attend_fp8win",
+    "csa2_reindex_attend",
     "csa2_workspace_bytes",
     "csa2_workspace_init",
     "csa2_status_string",
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_index_reindex_mx.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
         L.csa2_attend_fp8win.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp,
                                          sz, vp]
+        L.csa2_reindex_attend.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp,
+                                          i32, i64, i32, vp, i32, f32, vp, vp, sz, vp]
         L.csa2_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
         L.csa2_workspace_bytes.restype = sz
         L.csa2_workspace_init.argtypes = [vp, sz, vp]
@@ -92,7 +95,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_version.argtypes = []
         for name in ("fp4_kv_append", "fp8_window_append", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
                      "csa2_attend_fp8win", "csa2_workspace_init", "csa2_version", "mxfp4_key_append",
-                     "csa2_index_full_mx", "csa2_index_full_mx_scan", "csa2_index_reindex_mx"):
+                     "csa2_index_full_mx", "csa2_index_full_mx_scan", "csa2_index_reindex_mx", "csa2_reindex_attend"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -235,6 +238,19 @@ def csa2_attend_fp8win(q, codes, scales, seqs: Seqs, idx, swa8, swa_row0, swa_ca
     _check("csa2_attend_fp8win", lib().csa2_attend_fp8win(
         _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa8), _ptr(swa_row0), swa_cap,
         swa_rows, window, _ptr(replay_start), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws),
+        ws.numel(), _stream(stream)))
+
+
+def csa2_reindex_attend(q_idx, w, k_idx, k_scales, seqs: Seqs, pool, top_k: int, idx_out, q, codes, scales, swa,
+                        swa_row0, swa_cap: int, window: int, softmax_scale: float, out, ws, window_fp8: bool = False,
+                        replay_start=None, block: int = BLOCK, stream=None) -> None:
+    """One Reindex layer: selection inside the pool (bf16 keys, or MXFP4 keys when k_scales is
+    given) and the attention over it; idx_out and out as from the two separate calls."""
+    swa_rows = swa.shape[0] if swa is not None else 0
+    _check("csa2_reindex_attend", lib().csa2_reindex_attend(
+        _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scales), seqs.c(), q_idx.shape[1], _ptr(pool), pool.shape[1], block,
+        top_k, _ptr(idx_out), _ptr(q), _ptr(codes), _ptr(scales), _ptr(swa), 1 if window_fp8 else 0, _ptr(swa_row0),
+        swa_cap, swa_rows, window, _ptr(replay_start), q.shape[1], ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws),
         ws.numel(), _stream(stream)))
 
 

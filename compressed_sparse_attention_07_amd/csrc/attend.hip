@@ -35,6 +35,7 @@
 // B = Q^T); the S^T accumulator is already the B operand layout P^T needs for
 // O^T[dim][head] += V^T . P^T, so P never leaves registers.
 #include "csa2_device.hpp"
+#include "reindex_select.hpp"
 
 namespace csa2 {
 
@@ -133,17 +134,59 @@ __device__ __forceinline__ void wave_lds_sync() {
 // in FP8); they are converted to f16 exactly and take the FP4 entries' f16 path.
 // replay (may be NULL): per-query replay start s; the window then holds only positions >= s
 // ([Article] section XII, SWA Bounded Replay).
-template <bool kFp4, bool kWin, bool kW8>
-__global__ __launch_bounds__(kAttNT) void k_attend(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-    const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len, int32_t max_len, int64_t cache_rows,
-    const int32_t* __restrict__ idx, int top_k, const void* __restrict__ swa, const int64_t* __restrict__ swa_row0,
-    int swa_cap, int64_t swa_rows, int window, const int64_t* __restrict__ replay, int n_heads, float scale_log2,
-    float* __restrict__ out) {
-    __shared__ __align__(16) uint8_t s_tile[kAttWaves][kTileB];
-    __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
+struct AttendArgs {
+    const uint16_t* q;
+    const uint8_t* codes;
+    const uint8_t* scales;
+    const int64_t* kv_row0;
+    const int32_t* kv_len;
+    int32_t max_len;
+    int64_t cache_rows;
+    const int32_t* idx;  // [n_q, top_k] (the standalone kernel reads it; the fused one has it in LDS)
+    int top_k;
+    const void* swa;
+    const int64_t* swa_row0;
+    int swa_cap;
+    int64_t swa_rows;
+    int window;
+    const int64_t* replay;
+    int n_heads;
+    float scale_log2;
+    float* out;
+};
 
-    const int i = blockIdx.x;
+// LDS of one attention workgroup: per-wave tiles (P.V operands, then the merge rows) and the
+// per-wave softmax statistics.
+struct AttendLds {
+    uint8_t* tile;            // [kAttWaves][kTileB], 16-byte aligned
+    float (*m)[kNH];          // [kAttWaves][kNH]
+    float (*l)[kNH];
+};
+
+// The attention of query i (one workgroup of kAttNT threads); idx_row = the query's top_k
+// selected positions (global memory or LDS).
+template <bool kFp4, bool kWin, bool kW8>
+__device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const int32_t* idx_row, const AttendLds& lds) {
+    const uint16_t* __restrict__ q = a.q;
+    const uint8_t* __restrict__ codes = a.codes;
+    const uint8_t* __restrict__ scales = a.scales;
+    const int64_t* __restrict__ kv_row0 = a.kv_row0;
+    const int32_t* __restrict__ kv_len = a.kv_len;
+    const int32_t max_len = a.max_len;
+    const int64_t cache_rows = a.cache_rows;
+    const int top_k = a.top_k;
+    const void* __restrict__ swa = a.swa;
+    const int64_t* __restrict__ swa_row0 = a.swa_row0;
+    const int swa_cap = a.swa_cap;
+    const int64_t swa_rows = a.swa_rows;
+    const int window = a.window;
+    const int64_t* __restrict__ replay = a.replay;
+    const int n_heads = a.n_heads;
+    const float scale_log2 = a.scale_log2;
+    float* __restrict__ out = a.out;
+    float (*s_m)[kNH] = lds.m;
+    float (*s_l)[kNH] = lds.l;
+
     const int t = threadIdx.x;
     const int wave = t >> 6;
     const int l = t & 63;
@@ -166,7 +209,7 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
 #pragma unroll
         for (int j = 0; j < kRB; ++j) {
             const int e = 16 * (b0 + j) + r;
-            const int v = kFp4 ? idx[(int64_t)i * top_k + (e < top_k ? e : 0)] : -1;
+            const int v = kFp4 ? idx_row[e < top_k ? e : 0] : -1;
             pos[j] = e < top_k ? v : -1;
         }
     };
@@ -261,7 +304,7 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
     f32x4 o[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint8_t* tile = s_tile[wave];
+    uint8_t* tile = lds.tile + wave * kTileB;
     // tile addresses: row-major store of this lane's entry r; transposed read of rows 4g + r/4
     const int st_off = r * kRowB + 64 * g;
     const int tr_off = (4 * g + (r >> 2)) * kRowB + 8 * (r & 3);
@@ -458,11 +501,42 @@ __global__ __launch_bounds__(kAttNT) void k_attend(
         for (int w = 0; w < kAttWaves; ++w) {
             const float f = (s_m[w][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
             L = fmaf(s_l[w][h], f, L);
-            O += f * *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(s_tile[w]) + h * kOStride + d0);
+            O += f * *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds.tile + w * kTileB) +
+                                                    h * kOStride + d0);
         }
         const f32x4 res = L > 0.f ? O / L : f32x4{0.f, 0.f, 0.f, 0.f};
         *reinterpret_cast<f32x4*>(out + ((int64_t)i * n_heads + h) * kD + d0) = res;
     }
+}
+
+template <bool kFp4, bool kWin, bool kW8>
+__global__ __launch_bounds__(kAttNT) void k_attend(AttendArgs a) {
+    __shared__ __align__(16) uint8_t s_tile[kAttWaves * kTileB];
+    __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
+    const int i = blockIdx.x;
+    attend_query<kFp4, kWin, kW8>(i, a, a.idx + (int64_t)i * a.top_k, AttendLds{s_tile, s_m, s_l});
+}
+
+// Reindex layer, second kernel: the query's selection inside its pool (reindex_select_query,
+// over the keys the Reindex scoring kernel wrote), kept in LDS and written to idx_out for the
+// Reuse layers that follow, then the attention over it, in one workgroup: the selection's
+// output never makes a round trip through memory and the layer saves a kernel launch.  The
+// selection's candidate buffer and the attention's tiles share one LDS area.
+template <int EPT, bool kWin, bool kW8>
+__global__ __launch_bounds__(kAttNT) void k_reindex_attend(const int32_t* __restrict__ pool, int pool_blocks,
+                                                           IndexWs ws, int32_t* __restrict__ idx_out, AttendArgs a) {
+    constexpr int kCandB = kAttNT * EPT * 4;
+    __shared__ __align__(16) uint8_t s_area[kCandB > kAttWaves * kTileB ? kCandB : kAttWaves * kTileB];
+    __shared__ uint32_t s_hist[2][kHistBins];
+    __shared__ int32_t s_idx[kMaxSelect];
+    __shared__ int s_scan[kAttNT / kWave];
+    __shared__ Thresh sh_th;
+    __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
+    const int i = blockIdx.x;
+    reindex_select_query<kAttNT, EPT>(i, pool, pool_blocks, a.top_k, ws, idx_out, s_idx, s_hist,
+                                      reinterpret_cast<uint32_t*>(s_area), s_scan, &sh_th);
+    __syncthreads();  // the selection is in s_idx; the candidate area becomes the tiles
+    attend_query<true, kWin, kW8>(i, a, s_idx, AttendLds{s_area, s_m, s_l});
 }
 
 // window_fp8: the window store holds E4M3 bytes; replay: per-query replay starts or NULL.
@@ -480,9 +554,34 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
     else
         kern = fp4 ? (win ? k_attend<true, true, false> : k_attend<true, false, false>)
                    : (win ? k_attend<false, true, false> : k_attend<false, false, false>);
-    hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, q, codes, scales, kv_row0, kv_len, max_len,
-                       cache_rows, idx, top_k, swa, swa_row0, swa_cap, swa_rows, window, replay, n_heads, scale_log2,
-                       out);
+    const AttendArgs a{q,          codes,    scales, kv_row0, kv_len, max_len,   cache_rows, idx, top_k, swa,
+                       swa_row0,   swa_cap,  swa_rows, window, replay,  n_heads, scale_log2, out};
+    hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, a);
+    return hipGetLastError();
+}
+
+// The fused Reindex selection + attention (after the Reindex scoring kernel); pool_blocks * 8
+// must be at most kAttNT * 32.
+hipError_t launch_reindex_attend(const int32_t* pool, int pool_blocks, const IndexWs& ws, int32_t* idx_out,
+                                 const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
+                                 int64_t cache_rows, int top_k, const void* swa, int window_fp8,
+                                 const int64_t* swa_row0, int swa_cap, int64_t swa_rows, int window,
+                                 const int64_t* replay, int n_heads, float softmax_scale, float* out,
+                                 hipStream_t stream) {
+    const float scale_log2 = softmax_scale * 1.4426950408889634f;
+    const bool win = window > 0 && swa_rows > 0;
+    const bool small = pool_blocks * 8 <= kAttNT * 16;
+    decltype(&k_reindex_attend<32, true, false>) kern;
+    if (window_fp8)
+        kern = small ? (win ? k_reindex_attend<16, true, true> : k_reindex_attend<16, false, true>)
+                     : (win ? k_reindex_attend<32, true, true> : k_reindex_attend<32, false, true>);
+    else
+        kern = small ? (win ? k_reindex_attend<16, true, false> : k_reindex_attend<16, false, false>)
+                     : (win ? k_reindex_attend<32, true, false> : k_reindex_attend<32, false, false>);
+    const AttendArgs a{q,          codes,    scales, kv_row0, kv_len, max_len,   cache_rows, nullptr, top_k, swa,
+                       swa_row0,   swa_cap,  swa_rows, window, replay,  n_heads, scale_log2, out};
+    hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, pool, pool_blocks, ws, idx_out, a);
     return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ constexpr int kFullTile = CSA2_SCAN_TILE;  // must match the scan kernel's tile
 constexpr int kFilterTile = 16384;
 constexpr int kHistBins = 2048;
 constexpr size_t kAlign = 256;
+constexpr int kFusedMaxPoolElems = 512 * 32;  // pool positions the fused Reindex selection + attention takes
 
 struct Thresh {
     int32_t digit, above, in_bucket, total;
@@ -51,7 +52,14 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
 hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
                                 int64_t cache_rows, int n_heads, const int32_t* pool, int pool_blocks, int top_k,
-                                const IndexWs& ws, int32_t* idx_out, hipStream_t stream);
+                                const IndexWs& ws, int32_t* idx_out, int select, hipStream_t stream);
+hipError_t launch_reindex_attend(const int32_t* pool, int pool_blocks, const IndexWs& ws, int32_t* idx_out,
+                                 const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
+                                 int64_t cache_rows, int top_k, const void* swa, int window_fp8,
+                                 const int64_t* swa_row0, int swa_cap, int64_t swa_rows, int window,
+                                 const int64_t* replay, int n_heads, float softmax_scale, float* out,
+                                 hipStream_t stream);
 hipError_t launch_mx_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
                           uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream);
 hipError_t launch_fp8_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
@@ -251,10 +259,10 @@ int csa2_index_full_select(const uint16_t* q_idx, const float* w, const uint16_t
                             pool_out, ws, ws_bytes, stream, 4);
 }
 
-static int index_reindex_common(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
-                                const csa2_seqs& seqs, int32_t n_heads, const int32_t* pool, int32_t pool_blocks,
-                                int32_t block, int32_t top_k, int32_t* idx_out, void* ws, size_t ws_bytes,
-                                void* stream) {
+// Checks of a Reindex call (everything but n_q == 0, which the callers handle first).
+static int check_reindex(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
+                         const csa2_seqs& seqs, int32_t n_heads, const int32_t* pool, int32_t pool_blocks,
+                         int32_t block, int32_t top_k, int32_t* idx_out, void* ws, size_t ws_bytes) {
     int st = check_seqs(seqs);
     if (st) return st;
     if (n_heads < 1 || n_heads > CSA2_MAX_IDX_HEADS || top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 1 ||
@@ -270,10 +278,21 @@ static int index_reindex_common(const uint16_t* q_idx, const float* w, const voi
     size_t need = 0;
     carve_reindex(nullptr, seqs.n_q, top_k, pool_blocks, &need);
     if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return CSA2_ERR_WORKSPACE;
+    return CSA2_OK;
+}
+
+static int index_reindex_common(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
+                                const csa2_seqs& seqs, int32_t n_heads, const int32_t* pool, int32_t pool_blocks,
+                                int32_t block, int32_t top_k, int32_t* idx_out, void* ws, size_t ws_bytes,
+                                void* stream) {
+    const int st = check_reindex(q_idx, w, k_idx, k_sc, mx, seqs, n_heads, pool, pool_blocks, block, top_k, idx_out,
+                                 ws, ws_bytes);
+    if (st || seqs.n_q == 0) return st;
+    size_t need = 0;
     const IndexWs wsp = carve_reindex(ws, seqs.n_q, top_k, pool_blocks, &need);
     return launch_status(launch_index_reindex(q_idx, w, k_idx, k_sc, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
                                               seqs.max_len_ub, seqs.cache_rows, n_heads, pool, pool_blocks, top_k,
-                                              wsp, idx_out, static_cast<hipStream_t>(stream)));
+                                              wsp, idx_out, 1, static_cast<hipStream_t>(stream)));
 }
 
 int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
@@ -318,10 +337,10 @@ int csa2_index_reindex_mx(const uint16_t* q_idx, const float* w, const uint8_t* 
                                 idx_out, ws, ws_bytes, stream);
 }
 
-static int attend_common(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const csa2_seqs& seqs,
-                         const int32_t* idx, int32_t top_k, const void* swa, int window_fp8, const int64_t* swa_row0,
-                         int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay, int32_t n_heads,
-                         float softmax_scale, float* out, void* stream) {
+// Checks of an attention call (everything but n_q == 0, which the callers handle first).
+static int check_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const csa2_seqs& seqs,
+                        const int32_t* idx, int32_t top_k, const void* swa, const int64_t* swa_row0, int32_t swa_cap,
+                        int64_t swa_rows, int32_t window, int32_t n_heads, float softmax_scale, const float* out) {
     int st = check_seqs(seqs);
     if (st) return st;
     if (top_k < 0 || top_k > CSA2_MAX_SELECT || window < 0 || window > CSA2_MAX_WINDOW || n_heads < 1 ||
@@ -337,6 +356,16 @@ static int attend_common(const uint16_t* q, const uint8_t* codes, const uint8_t*
     if (!aligned16(q) || (codes && !aligned16(codes)) || (swa && !aligned16(swa)) ||
         (scales && (reinterpret_cast<uintptr_t>(scales) & 1u)))
         return CSA2_ERR_SHAPE;
+    return CSA2_OK;
+}
+
+static int attend_common(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const csa2_seqs& seqs,
+                         const int32_t* idx, int32_t top_k, const void* swa, int window_fp8, const int64_t* swa_row0,
+                         int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay, int32_t n_heads,
+                         float softmax_scale, float* out, void* stream) {
+    const int st = check_attend(q, codes, scales, seqs, idx, top_k, swa, swa_row0, swa_cap, swa_rows, window, n_heads,
+                                softmax_scale, out);
+    if (st || seqs.n_q == 0) return st;
     return launch_status(launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
                                        seqs.cache_rows, idx, top_k, swa, window_fp8, swa_row0,
                                        window > 0 ? swa_cap : 1, swa_rows, window, replay, n_heads, softmax_scale,
@@ -361,6 +390,40 @@ int csa2_attend_fp8win(const uint16_t* q, const uint8_t* codes, const uint8_t* s
     (void)ws_bytes;
     return attend_common(q, codes, scales, seqs, idx, top_k, swa, 1, swa_row0, swa_cap, swa_rows, window,
                          replay_start, n_heads, softmax_scale, out, stream);
+}
+
+int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
+                        csa2_seqs seqs, int32_t idx_heads, const int32_t* pool, int32_t pool_blocks, int32_t block,
+                        int32_t top_k, int32_t* idx_out, const uint16_t* q, const uint8_t* codes,
+                        const uint8_t* scales, const void* swa, int32_t window_fp8, const int64_t* swa_row0,
+                        int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay_start,
+                        int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+    const int mx = k_scales != nullptr ? 1 : 0;
+    if (window_fp8 != 0 && window_fp8 != 1) return CSA2_ERR_SHAPE;
+    int st = check_reindex(q_idx, w, k_idx, k_scales, mx, seqs, idx_heads, pool, pool_blocks, block, top_k, idx_out,
+                           ws, ws_bytes);
+    if (st) return st;
+    st = check_attend(q, codes, scales, seqs, idx_out, top_k, swa, swa_row0, swa_cap, swa_rows, window, n_heads,
+                      softmax_scale, out);
+    if (st || seqs.n_q == 0) return st;
+    size_t need = 0;
+    const IndexWs wsp = carve_reindex(ws, seqs.n_q, top_k, pool_blocks, &need);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool fused = pool_blocks * 8 <= kFusedMaxPoolElems;
+    hipError_t e = launch_index_reindex(q_idx, w, k_idx, k_scales, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
+                                        seqs.max_len_ub, seqs.cache_rows, idx_heads, pool, pool_blocks, top_k, wsp,
+                                        idx_out, fused ? 0 : 1, s);
+    if (e != hipSuccess) return CSA2_ERR_LAUNCH;
+    if (fused)
+        e = launch_reindex_attend(pool, pool_blocks, wsp, idx_out, q, codes, scales, seqs.kv_row0, seqs.kv_len,
+                                  seqs.n_q, seqs.max_len_ub, seqs.cache_rows, top_k, swa, window_fp8, swa_row0,
+                                  window > 0 ? swa_cap : 1, swa_rows, window, replay_start, n_heads, softmax_scale,
+                                  out, s);
+    else
+        e = launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub, seqs.cache_rows,
+                          idx_out, top_k, swa, window_fp8, swa_row0, window > 0 ? swa_cap : 1, swa_rows, window,
+                          replay_start, n_heads, softmax_scale, out, s);
+    return launch_status(e);
 }
 
 int csa2_workspace_init(void* ws, size_t bytes, void* stream) {

@@ -49,6 +49,22 @@ struct Thresh {
     int32_t total;      // valid elements
 };
 
+// Workspace views of the Full / Reindex indexer (carved by the host from one caller buffer).
+struct IndexWs {
+    uint32_t* ctrl;      // [n_q][kCtlSlots]          self-cleaning counters
+    uint32_t* hist;      // [n_q][2][2048]            self-cleaning histograms
+    Thresh* meta;        // [n_q][2]
+    uint32_t* keys;      // [grid_tiles * kFullTile]  per-position keys (Full) / per-candidate keys (Reindex)
+    uint32_t* bkeys;     // [grid_tiles * kFullTile / 8] per-block max keys
+    int32_t* sure_idx;   // [n_q][top_k]
+    int32_t* sure_pool;  // [n_q][pool_blocks]
+    uint64_t* cand_idx;  // [grid_tiles * kFullTile]  threshold-bucket composites
+    uint64_t* cand_pool; // [grid_tiles * kFullTile / 8]
+    QMeta* qmeta;        // [n_q]                      per-query length and tile ranges (prep kernel)
+    int32_t* tmap;       // [grid_tiles]               scan tile -> query (-1: unused)
+    int32_t* fmap;       // [grid_ftiles]              filter tile -> query (-1: unused)
+};
+
 __device__ __forceinline__ uint32_t score_key(float s) {
     s = s + 0.0f;  // -0 -> +0 so both zeros share one key
     uint32_t b = __float_as_uint(s);

@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "csa2_device.hpp"
+#include "reindex_select.hpp"
 
 namespace csa2 {
 
@@ -69,20 +70,6 @@ constexpr int kFullTileBlocks = kFullTile / 8;
 constexpr int kReindexTile = 512;               // pool positions (64 blocks) per Reindex workgroup
 constexpr int kFilterTile = 16384;              // positions per filter workgroup (4 scan tiles)
 
-struct IndexWs {
-    uint32_t* ctrl;      // [n_q][kCtlSlots]          self-cleaning counters
-    uint32_t* hist;      // [n_q][2][2048]            self-cleaning histograms
-    Thresh* meta;        // [n_q][2]
-    uint32_t* keys;      // [grid_tiles * kFullTile]  per-position keys (Full) / per-candidate keys (Reindex)
-    uint32_t* bkeys;     // [grid_tiles * kFullTile / 8] per-block max keys
-    int32_t* sure_idx;   // [n_q][top_k]
-    int32_t* sure_pool;  // [n_q][pool_blocks]
-    uint64_t* cand_idx;  // [grid_tiles * kFullTile]  threshold-bucket composites
-    uint64_t* cand_pool; // [grid_tiles * kFullTile / 8]
-    QMeta* qmeta;        // [n_q]                      per-query length and tile ranges (prep kernel)
-    int32_t* tmap;       // [grid_tiles]               scan tile -> query (-1: unused)
-    int32_t* fmap;       // [grid_ftiles]              filter tile -> query (-1: unused)
-};
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -924,102 +911,8 @@ __global__ __launch_bounds__(kSelNT) void k_idx_reindex_select(const int32_t* __
     __shared__ uint32_t s_cand[kSelNT * EPT];  // keys of the first-digit bucket
     __shared__ int s_scan[kSelNT / kWave];
     __shared__ Thresh sh_th;
-    const int i = blockIdx.x;
-    const int t = threadIdx.x;
-    const int n_elem = pool_blocks * 8;
-    const int e0 = t * EPT;
-    const int32_t* qpool = pool + (int64_t)i * pool_blocks;
-    const uint32_t* keys = ws.keys + (int64_t)i * n_elem;
-    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
-
-    uint32_t kv[EPT];
-    int32_t pb[EPT / 8];  // pool blocks of this thread's elements
-#pragma unroll
-    for (int j = 0; j < EPT; j += 8) {
-        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-        int32_t blk = -1;
-        if (e0 + j < n_elem) {  // n_elem is a multiple of 8: the whole block is there
-            a = *reinterpret_cast<const uint4*>(keys + e0 + j);
-            b = *reinterpret_cast<const uint4*>(keys + e0 + j + 4);
-            blk = qpool[(e0 + j) >> 3];
-        }
-        kv[j] = a.x; kv[j + 1] = a.y; kv[j + 2] = a.z; kv[j + 3] = a.w;
-        kv[j + 4] = b.x; kv[j + 5] = b.y; kv[j + 6] = b.z; kv[j + 7] = b.w;
-        pb[j >> 3] = blk;
-    }
-    for (int b = t; b < 2 * kHistBins; b += kSelNT) (&s_hist[0][0])[b] = 0u;
-    // first digit: histogram accumulated by the score kernel (its barriers also cover the
-    // clearing above)
-    find_threshold<kSelNT>(gh, top_k, s_scan, &sh_th);
-    Thresh th = sh_th;
-    uint32_t T = 1u;           // selected: key > T, or key == T among the first need_eq of them
-    int need_eq = INT32_MAX;   // (keys are >= 1 for every valid element; 0 marks padding)
-    if (th.digit >= 0) {
-        int need = top_k - th.above;  // 1 <= need <= inb
-        int inb = th.in_bucket;
-        uint32_t prefix = (uint32_t)th.digit;
-        int pbits = kHistBits;
-        if (inb > need) {
-            // compact the bucket's keys to LDS (order is irrelevant: only T is sought)
-            uint32_t in_mask = 0u;
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) in_mask |= (uint32_t)((kv[j] >> (32 - kHistBits)) == prefix) << j;
-            int m;
-            int off = block_exclusive_scan<kSelNT>(__popc(in_mask), s_scan, m);
-#pragma unroll
-            for (int j = 0; j < EPT; ++j)
-                if ((in_mask >> j) & 1u) s_cand[off++] = kv[j];
-            __syncthreads();
-            // at most two more radix passes (11 and 10 bits) over the m bucket keys
-            int hb = 0;
-            while (pbits < 32 && inb > need) {
-                const int w = min(kHistBits, 32 - pbits);
-                const int shift = 32 - pbits - w;
-                for (int e = t; e < m; e += kSelNT) {
-                    const uint32_t v = s_cand[e];
-                    if ((v >> (32 - pbits)) == prefix) atomicAdd(&s_hist[hb][(v >> shift) & ((1u << w) - 1u)], 1u);
-                }
-                __syncthreads();
-                find_threshold<kSelNT>(s_hist[hb], need, s_scan, &sh_th);
-                th = sh_th;  // inb > need, so a digit is found
-                prefix = (prefix << w) | (uint32_t)th.digit;
-                need -= th.above;
-                inb = th.in_bucket;
-                pbits += w;
-                hb ^= 1;     // the other histogram is still clear
-            }
-        }
-        T = prefix << (32 - pbits);  // lowest key with the final prefix
-        need_eq = inb == need ? INT32_MAX : need;  // the whole bucket, or `need` keys equal to T
-    }
-    // one scan of (keys > T, keys == T) counts ranks the ties at T in element order and
-    // places every selected element (keys above T number < top_k <= 4096, ties <= 32768:
-    // packed 16 + 16 bits)
-    int n_gt = 0, n_eq = 0;
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        if (kv[j] != 0u) {
-            n_gt += kv[j] > T ? 1 : 0;
-            n_eq += kv[j] == T ? 1 : 0;
-        }
-    }
-    int tot_pk;
-    const uint32_t pk = (uint32_t)block_exclusive_scan<kSelNT>((int)(((uint32_t)n_gt << 16) | (uint32_t)n_eq),
-                                                              s_scan, tot_pk);
-    int eq_rank = (int)(pk & 0xffffu);
-    int off = (int)(pk >> 16) + min(eq_rank, need_eq);
-    const int total = (int)((uint32_t)tot_pk >> 16) + min((int)((uint32_t)tot_pk & 0xffffu), need_eq);
-    int32_t* out = idx_out + (int64_t)i * top_k;
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-        if (kv[j] != 0u) {
-            bool sel = kv[j] > T;
-            if (kv[j] == T) sel = eq_rank++ < need_eq;
-            if (sel) out[off++] = pb[j >> 3] * 8 + (j & 7);
-        }
-    }
-    for (int j = total + t; j < top_k; j += kSelNT) out[j] = -1;
-    for (int b = t; b < kHistBins; b += kSelNT) gh[b] = 0u;
+    reindex_select_query<kSelNT, EPT>(blockIdx.x, pool, pool_blocks, top_k, ws, idx_out, nullptr, s_hist, s_cand,
+                                      s_scan, &sh_th);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1094,10 +987,11 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
     return hipSuccess;
 }
 
+// select == 0: the scoring kernel only (the fused selection + attention kernel follows).
 hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
                                 int64_t cache_rows, int n_heads, const int32_t* pool, int pool_blocks, int top_k,
-                                const IndexWs& ws, int32_t* idx_out, hipStream_t stream) {
+                                const IndexWs& ws, int32_t* idx_out, int select, hipStream_t stream) {
     const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
     dim3 grid(chunks, n_q);
     auto kern = mx ? (n_heads <= 4 ? k_idx_reindex_score<4, true> : k_idx_reindex_score<8, true>)
@@ -1105,7 +999,7 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
     hipLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, k_sc, kv_row0, kv_len, max_len,
                        cache_rows, n_heads, pool, pool_blocks, ws);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !select) return e;
     const int ept = (pool_blocks * 8 + kSelNT - 1) / kSelNT;
     auto sel = ept <= 8 ? k_idx_reindex_select<8> : ept <= 16 ? k_idx_reindex_select<16> : k_idx_reindex_select<32>;
     hipLaunchKernelGGL(sel, dim3(n_q), dim3(kSelNT), 0, stream, pool, pool_blocks, top_k, ws, idx_out);

@@ -1,0 +1,130 @@
+// Reindex-mode selection of one query, shared by the selection kernel and the fused
+// selection + attention kernel (one workgroup of NT threads; EPT pool elements per thread).
+//
+// Article "DeepSeek-V4.1-Flash: Pushing KV Cache Compression to 890 Bytes per Token", section
+// IX: a Reindex layer takes its own Top-K inside the shared pool.  The pool is ascending, so
+// element order is position order: the K-th largest key T comes from the first-digit
+// histogram the scoring kernel built plus at most two radix passes over the bucket's keys
+// (compacted to LDS first), and one packed (greater-than-T, equal-to-T) block scan ranks the
+// ties at T and places every selected element in ascending position order.
+#pragma once
+
+#include "csa2_device.hpp"
+
+namespace csa2 {
+
+// Writes the query's selection to idx_out[i * top_k ..] and, when lds_idx is given, to that
+// LDS row as well (entries past the selection: -1).  Every thread of the workgroup must call
+// it; it ends with the selection written (the caller synchronises before reading lds_idx).
+template <int NT, int EPT>
+__device__ __forceinline__ void reindex_select_query(int i, const int32_t* __restrict__ pool, int pool_blocks,
+                                                     int top_k, const IndexWs& ws, int32_t* __restrict__ idx_out,
+                                                     int32_t* lds_idx, uint32_t (*s_hist)[kHistBins],
+                                                     uint32_t* s_cand, int* s_scan, Thresh* sh_th_p) {
+    Thresh& sh_th = *sh_th_p;
+    const int t = threadIdx.x;
+    const int n_elem = pool_blocks * 8;
+    const int e0 = t * EPT;
+    const int32_t* qpool = pool + (int64_t)i * pool_blocks;
+    const uint32_t* keys = ws.keys + (int64_t)i * n_elem;
+    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
+
+    uint32_t kv[EPT];
+    int32_t pb[EPT / 8];  // pool blocks of this thread's elements
+#pragma unroll
+    for (int j = 0; j < EPT; j += 8) {
+        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+        int32_t blk = -1;
+        if (e0 + j < n_elem) {  // n_elem is a multiple of 8: the whole block is there
+            a = *reinterpret_cast<const uint4*>(keys + e0 + j);
+            b = *reinterpret_cast<const uint4*>(keys + e0 + j + 4);
+            blk = qpool[(e0 + j) >> 3];
+        }
+        kv[j] = a.x; kv[j + 1] = a.y; kv[j + 2] = a.z; kv[j + 3] = a.w;
+        kv[j + 4] = b.x; kv[j + 5] = b.y; kv[j + 6] = b.z; kv[j + 7] = b.w;
+        pb[j >> 3] = blk;
+    }
+    for (int b = t; b < 2 * kHistBins; b += NT) (&s_hist[0][0])[b] = 0u;
+    // first digit: histogram accumulated by the score kernel (its barriers also cover the
+    // clearing above)
+    find_threshold<NT>(gh, top_k, s_scan, &sh_th);
+    Thresh th = sh_th;
+    uint32_t T = 1u;           // selected: key > T, or key == T among the first need_eq of them
+    int need_eq = INT32_MAX;   // (keys are >= 1 for every valid element; 0 marks padding)
+    if (th.digit >= 0) {
+        int need = top_k - th.above;  // 1 <= need <= inb
+        int inb = th.in_bucket;
+        uint32_t prefix = (uint32_t)th.digit;
+        int pbits = kHistBits;
+        if (inb > need) {
+            // compact the bucket's keys to LDS (order is irrelevant: only T is sought)
+            uint32_t in_mask = 0u;
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) in_mask |= (uint32_t)((kv[j] >> (32 - kHistBits)) == prefix) << j;
+            int m;
+            int off = block_exclusive_scan<NT>(__popc(in_mask), s_scan, m);
+#pragma unroll
+            for (int j = 0; j < EPT; ++j)
+                if ((in_mask >> j) & 1u) s_cand[off++] = kv[j];
+            __syncthreads();
+            // at most two more radix passes (11 and 10 bits) over the m bucket keys
+            int hb = 0;
+            while (pbits < 32 && inb > need) {
+                const int w = min(kHistBits, 32 - pbits);
+                const int shift = 32 - pbits - w;
+                for (int e = t; e < m; e += NT) {
+                    const uint32_t v = s_cand[e];
+                    if ((v >> (32 - pbits)) == prefix) atomicAdd(&s_hist[hb][(v >> shift) & ((1u << w) - 1u)], 1u);
+                }
+                __syncthreads();
+                find_threshold<NT>(s_hist[hb], need, s_scan, &sh_th);
+                th = sh_th;  // inb > need, so a digit is found
+                prefix = (prefix << w) | (uint32_t)th.digit;
+                need -= th.above;
+                inb = th.in_bucket;
+                pbits += w;
+                hb ^= 1;     // the other histogram is still clear
+            }
+        }
+        T = prefix << (32 - pbits);  // lowest key with the final prefix
+        need_eq = inb == need ? INT32_MAX : need;  // the whole bucket, or `need` keys equal to T
+    }
+    // one scan of (keys > T, keys == T) counts ranks the ties at T in element order and
+    // places every selected element (keys above T number < top_k <= 4096, ties <= 32768:
+    // packed 16 + 16 bits)
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        if (kv[j] != 0u) {
+            n_gt += kv[j] > T ? 1 : 0;
+            n_eq += kv[j] == T ? 1 : 0;
+        }
+    }
+    int tot_pk;
+    const uint32_t pk = (uint32_t)block_exclusive_scan<NT>((int)(((uint32_t)n_gt << 16) | (uint32_t)n_eq),
+                                                              s_scan, tot_pk);
+    int eq_rank = (int)(pk & 0xffffu);
+    int off = (int)(pk >> 16) + min(eq_rank, need_eq);
+    const int total = (int)((uint32_t)tot_pk >> 16) + min((int)((uint32_t)tot_pk & 0xffffu), need_eq);
+    int32_t* out = idx_out + (int64_t)i * top_k;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        if (kv[j] != 0u) {
+            bool sel = kv[j] > T;
+            if (kv[j] == T) sel = eq_rank++ < need_eq;
+            if (sel) {
+                const int32_t v = pb[j >> 3] * 8 + (j & 7);
+                out[off] = v;
+                if (lds_idx != nullptr) lds_idx[off] = v;
+                ++off;
+            }
+        }
+    }
+    for (int j = total + t; j < top_k; j += NT) {
+        out[j] = -1;
+        if (lds_idx != nullptr) lds_idx[j] = -1;
+    }
+    for (int b = t; b < kHistBins; b += NT) gh[b] = 0u;
+}
+
+}  // namespace csa2

@@ -118,11 +118,15 @@ class Runner:
     """Device state of one workload and its step.  host copies of the inputs are kept in
     `self.host` when keep_host=True (for the oracle checks in tests and the bench baseline)."""
 
-    def __init__(self, wl: Workload, device="cuda", keep_host=False, seed=0, copies=1):
+    def __init__(self, wl: Workload, device="cuda", keep_host=False, seed=0, copies=1, fused_reindex=False):
         """copies > 1 keeps that many device copies of the KV sets (identical values); step() then
         rotates through them so consecutive steps never re-read a set that a last-level cache
-        could still hold."""
+        could still hold.  fused_reindex: Reindex layers run as csa2_reindex_attend (two
+        kernels) rather than csa2_index_reindex + csa2_attend (three).  Off by default: on
+        the decode workloads the fused form measured 1-2 % slower per step (its selection runs
+        with half the threads of the standalone one, which outweighs the saved launch)."""
         self.wl = wl
+        self.fused_reindex = fused_reindex
         self.device = device
         self.host = {} if keep_host else None
         B = wl.batch
@@ -296,6 +300,13 @@ class Runner:
                                          self.ws_full, shared_kv=shared, stream=stream)
                 pool_built = pool_built or want_pool > 0
                 idx = L.idx
+            elif L.mode == "R" and self.fused_reindex:
+                C.csa2_reindex_attend(L.q_idx, L.w, st.k_codes if wl.keys_mx else st.k_idx,
+                                      st.k_scales if wl.keys_mx else None, self.seqs, self.pool, wl.top_k, L.idx, L.q,
+                                      st.codes, st.scales, L.swa, self.swa_row0, self.swa_cap, wl.window, self.scale,
+                                      L.out, self.ws_re, window_fp8=wl.window_fp8, replay_start=self.replay,
+                                      stream=stream)
+                continue
             elif L.mode == "R":
                 if wl.keys_mx:
                     C.csa2_index_reindex_mx(L.q_idx, L.w, st.k_codes, st.k_scales, self.seqs, self.pool, wl.top_k,

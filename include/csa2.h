@@ -282,6 +282,34 @@ int csa2_attend_fp8win(const uint16_t* q, const uint8_t* codes, const uint8_t* s
                        void* stream);
 
 /*
+ * csa2_reindex_attend -- one Reindex layer: csa2_index_reindex (or _mx) followed by
+ * csa2_attend (or _fp8win) over the selection it produced, in two kernels instead of
+ * three.  [Article] sections VIII-IX (a Reindex layer selects its own Top-K inside the
+ * shared pool) and section VI (the layer then attends its selection plus its window).
+ *
+ *   q_idx, w, pool, pool_blocks, block, top_k, idx_out, ws, ws_bytes: as for
+ *           csa2_index_reindex (CSA2_OP_INDEX_REINDEX workspace); idx_heads is its n_heads.
+ *   k_idx, k_scales  k_scales == NULL: bf16 keys [seqs.cache_rows, CSA2_IDX_DIM];
+ *           otherwise MXFP4 keys as for csa2_index_reindex_mx (k_idx = the code bytes).
+ *   q, codes, scales, swa, swa_row0, swa_cap, swa_rows, window, n_heads, softmax_scale,
+ *   out: as for csa2_attend; window_fp8 = 0: swa holds bf16, 1: E4M3 bytes.
+ *   replay_start  device int64 [n_q] or NULL: as for csa2_attend_fp8win (either format).
+ * idx_out receives the selection (a Reuse layer that follows attends with it) and out
+ * the attention, both equal to those of the two separate calls.  With pool_blocks * 8
+ * <= 16,384 the selection and the attention run in one workgroup per query (the
+ * selection never goes back through memory before the attention reads it); larger
+ * pools take the separate selection and attention kernels.  All arguments are checked
+ * before anything is launched; the errors are those of the two separate calls.
+ */
+int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
+                        csa2_seqs seqs, int32_t idx_heads, const int32_t* pool, int32_t pool_blocks,
+                        int32_t block, int32_t top_k, int32_t* idx_out, const uint16_t* q,
+                        const uint8_t* codes, const uint8_t* scales, const void* swa, int32_t window_fp8,
+                        const int64_t* swa_row0, int32_t swa_cap, int64_t swa_rows, int32_t window,
+                        const int64_t* replay_start, int32_t n_heads, float softmax_scale, float* out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Workspace bytes for one call of `op` (CSA2_OP_*) with these sizes; SIZE_MAX if the
  * sizes are out of range, 0 if the call needs no workspace.  For CSA2_OP_ATTEND pass the
  * window length in `pool_blocks` (attention needs no workspace: it returns 0); for

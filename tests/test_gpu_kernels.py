@@ -248,6 +248,40 @@ def test_index_reindex_pool_with_padding_and_out_of_range_blocks():
         assert np.array_equal(idx[i], case.oracle_reindex(i, pool[i], 100)), i
 
 
+@pytest.mark.parametrize("pool_blocks,top_k,window", [(2048, 512, 128), (300, 64, 0), (3000, 512, 128), (1, 4, 16)])
+def test_reindex_attend_equals_separate_calls_and_oracle(pool_blocks, top_k, window):
+    # csa2_reindex_attend (fused selection + attention for pools of <= 2,048 blocks, the
+    # separate kernels above that) against csa2_index_reindex followed by csa2_attend: the
+    # same indices and bit-identical outputs; indices and outputs also against the oracle
+    lengths = [40000, 777, 0, 16, 25001]
+    ic = IndexCase(W_T + 70, lengths, n_heads=4)
+    ac = AttendCase(W_T + 70, lengths, n_heads=16, window=max(window, 1), swa_cap=128)
+    _, pool, _ = ic.run_full(512, pool_blocks)
+    q2 = synth.int_bf16(W_T + 70, synth.T_IDX_Q, (len(lengths), 4, 64), seq=5)
+    w2 = synth.int_weights(W_T + 70, synth.T_IDX_W, (len(lengths), 4), seq=5)
+    q2_dev, w2_dev = bf16_tensor(q2), torch.from_numpy(w2).to(DEV)
+    idx_a, _ = ic.run_reindex(pool, top_k, q_dev=q2_dev, w_dev=w2_dev)
+    idx_a = idx_a.cpu().numpy()
+    scale = 1 / np.sqrt(128)
+    n_q = len(lengths)
+    out_a = torch.empty((n_q, 16, 128), dtype=torch.float32, device=DEV)
+    C.csa2_attend(ac.q_dev, ac.codes, ac.scales, ac.seqs, torch.from_numpy(idx_a).to(DEV), ac.swa_dev,
+                  ac.swa_row0_dev, ac.swa_cap, window, scale, out_a, C.alloc_workspace(0))
+    ws = C.alloc_workspace(C.csa2_workspace_bytes(C.OP_INDEX_REINDEX, n_q, 0, 0, top_k, pool_blocks))
+    idx_b = torch.full((n_q, top_k), -7, dtype=torch.int32, device=DEV)
+    out_b = torch.full((n_q, 16, 128), float("nan"), dtype=torch.float32, device=DEV)
+    C.csa2_reindex_attend(q2_dev, w2_dev, ic.k_dev, None, ic.seqs, pool, top_k, idx_b, ac.q_dev, ac.codes, ac.scales,
+                          ac.swa_dev, ac.swa_row0_dev, ac.swa_cap, window, scale, out_b, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx_b.cpu().numpy(), idx_a)
+    assert np.array_equal(out_b.cpu().numpy(), out_a.cpu().numpy())
+    pool_np = pool.cpu().numpy()
+    for i in range(n_q):
+        assert np.array_equal(idx_a[i], ic.oracle_reindex(i, pool_np[i], top_k, q=q2[i], w=w2[i])), i
+    ac.window = window
+    ac.check(out_b.cpu().numpy(), idx_a, scale)
+
+
 # ---------------------------------------------------------------- attention
 def test_attend_selected_plus_window():
     lengths = [4096, 300, 130, 5000]

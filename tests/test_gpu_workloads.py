@@ -126,6 +126,25 @@ def test_workload7_mxfp4_keys_fp8_window_with_replay():
     _run(7, [6])
 
 
+@pytest.mark.parametrize("wid", [1, 7])
+def test_fused_reindex_layers_equal_separate_calls(wid):
+    # the fused Reindex selection + attention gives the separate calls' indices and outputs
+    # exactly (the same arithmetic in the same order); the separate calls are checked against
+    # the oracle by the workload tests above
+    outs = []
+    for fused in (True, False):
+        r = W.Runner(W.WORKLOADS[wid], fused_reindex=fused)
+        r.step()
+        torch.cuda.synchronize()
+        outs.append([(L.idx.cpu().numpy() if L.idx is not None else None, L.out.cpu().numpy()) for L in r.layers])
+        del r
+        torch.cuda.empty_cache()
+    for l, ((ia, oa), (ib, ob)) in enumerate(zip(*outs)):
+        if ia is not None:
+            assert np.array_equal(ia, ib), l
+        assert np.array_equal(oa, ob), l
+
+
 def test_workload3_prefill_4096_on_128k():
     r = W.Runner(W.WORKLOADS[3], keep_host=True)
     r.step()
