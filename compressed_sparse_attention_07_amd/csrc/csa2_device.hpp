@@ -372,6 +372,87 @@ __device__ void sort_write_ascending(uint32_t* sel, int total, int k, int32_t* o
     for (int j = E * NT + t; j < k; j += NT) out[j] = -1;
 }
 
+// Ascending output of `total` distinct values sel[0..total) (LDS) to out[0..k), -1 padded,
+// without a sort network: one counting pass over kAscB buckets of the values' range
+// [vmin, vmax] (bucket = (v - vmin) >> shift), an exclusive scan of the counts, a scatter into
+// bucket order, then each value's place inside its bucket by counting the bucket's smaller
+// values.  Distinct values keep a bucket of width 2^shift at <= 2^shift values, so the last
+// step costs at most total * 2^shift comparisons (2^shift = 512 for a 2^20 range).
+// scratch: >= 2 * kAscB + total words of LDS; sh_scan: NT / 64 ints; sh_mm: 2 words.
+constexpr int kAscB = 2048;
+
+template <int NT>
+__device__ void bucket_write_ascending(const uint32_t* sel, int total, int k, int32_t* out, uint32_t* scratch,
+                                       int* sh_scan, uint32_t* sh_mm) {
+    static_assert(kAscB % NT == 0, "buckets per thread");
+    constexpr int BPT = kAscB / NT;
+    const int t = threadIdx.x;
+    uint32_t* cnt = scratch;              // counts, then bucket starts
+    uint32_t* fill = scratch + kAscB;     // values placed per bucket
+    uint32_t* grp = scratch + 2 * kAscB;  // the values grouped by bucket
+    if (t == 0) {
+        sh_mm[0] = 0xffffffffu;
+        sh_mm[1] = 0u;
+    }
+    for (int b = t; b < kAscB; b += NT) {
+        cnt[b] = 0u;
+        fill[b] = 0u;
+    }
+    __syncthreads();
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    for (int j = t; j < total; j += NT) {
+        lo = min(lo, sel[j]);
+        hi = max(hi, sel[j]);
+    }
+    // wave reduction first: a thousand LDS atomics on one address serialise
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, kWave));
+        hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, kWave));
+    }
+    if ((t & (kWave - 1)) == 0 && lo != 0xffffffffu) {
+        atomicMin(&sh_mm[0], lo);
+        atomicMax(&sh_mm[1], hi);
+    }
+    __syncthreads();
+    const uint32_t vmin = sh_mm[0];
+    const uint32_t range = total > 0 ? sh_mm[1] - vmin : 0u;
+    int shift = 0;
+    while ((range >> shift) >= (uint32_t)kAscB) ++shift;
+    for (int j = t; j < total; j += NT) atomicAdd(&cnt[(sel[j] - vmin) >> shift], 1u);
+    __syncthreads();
+    uint32_t c[BPT];
+    int run = 0;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+        c[b] = cnt[BPT * t + b];
+        run += (int)c[b];
+    }
+    int tot;
+    int base = block_exclusive_scan<NT>(run, sh_scan, tot);
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+        cnt[BPT * t + b] = (uint32_t)base;
+        base += (int)c[b];
+    }
+    __syncthreads();
+    for (int j = t; j < total; j += NT) {
+        const uint32_t v = sel[j];
+        const uint32_t b = (v - vmin) >> shift;
+        grp[cnt[b] + atomicAdd(&fill[b], 1u)] = v;
+    }
+    __syncthreads();
+    for (int j = t; j < total; j += NT) {
+        const uint32_t v = grp[j];
+        const uint32_t b = (v - vmin) >> shift;
+        const int s0 = (int)cnt[b], s1 = s0 + (int)fill[b];
+        int rank = 0;
+        for (int e = s0; e < s1; ++e) rank += grp[e] < v ? 1 : 0;
+        out[s0 + rank] = (int32_t)v;
+    }
+    for (int j = total + t; j < k; j += NT) out[j] = -1;
+}
+
 // Write the `total` distinct positions in sel[] (LDS) to out[0..k) in ascending order, -1 padded:
 // each position's slot is the number of smaller positions (no sort network, no barriers).
 template <int NT>

@@ -735,15 +735,15 @@ union SelLds {
     SmallSel small;
 };
 
-// Ascending output of up to kMaxSelect selected positions (sel[] in LDS, >= kMaxSelect words).
-__device__ __forceinline__ void sort_out(uint32_t* sel, int total, int k, int32_t* out) {
-    if (total <= kSelNT) {
-        sort_write_ascending<kSelNT, 1>(sel, total, k, out);
-    } else if (total <= 2 * kSelNT) {
-        sort_write_ascending<kSelNT, 2>(sel, total, k, out);
-    } else {
-        sort_write_ascending<kSelNT, 4>(sel, total, k, out);
-    }
+// Ascending output of up to kMaxSelect selected positions (sel[] in LDS).
+struct AscLds {
+    uint32_t scratch[2 * kAscB + kMaxSelect];
+    int scan[kSelNT / kWave];
+    uint32_t mm[2];
+};
+
+__device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, int32_t* out, AscLds& A) {
+    bucket_write_ascending<kSelNT>(sel, total, k, out, A.scratch, A.scan, A.mm);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -759,6 +759,7 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
                                                             int32_t* __restrict__ idx_out,
                                                             int32_t* __restrict__ pool_out) {
     __shared__ SelLds U;
+    __shared__ AscLds A;
     __shared__ Thresh sh_th;
     const int i = blockIdx.x;
     const int which = blockIdx.y;  // 0: positions, 1: pool blocks
@@ -786,7 +787,7 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
         for (int e = t; e < th.in_bucket; e += kSelNT)
             if (W.cand[e] >= thr) W.sel[atomicAdd(&W.cnt, 1)] = composite_pos(W.cand[e]);
         __syncthreads();
-        sort_out(W.sel, W.cnt, k, out);
+        sort_out(W.sel, W.cnt, k, out, A);
     } else {
         SelectShared& S = U.big;
         const uint64_t thr = wg_threshold<kSelNT>(CompositeList{cand}, th.in_bucket, need, th.digit, S);
@@ -797,7 +798,7 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
         for (int e = t; e < th.in_bucket; e += kSelNT)
             if (cand[e] >= thr) sel[atomicAdd(&S.cnt, 1)] = composite_pos(cand[e]);
         __syncthreads();
-        sort_out(sel, S.cnt, k, out);
+        sort_out(sel, S.cnt, k, out, A);
     }
     for (int b = t; b < kHistBins; b += kSelNT) gh[b] = 0u;
     if (t == 0) {
