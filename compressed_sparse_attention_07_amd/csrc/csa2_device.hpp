@@ -16,7 +16,7 @@ namespace csa2 {
 constexpr int kWave = 64;
 constexpr int kHistBits = 11;                 // first radix digit = top 11 key bits
 constexpr int kHistBins = 1 << kHistBits;     // 2048
-constexpr int kSortCap = 4096;                // largest candidate set sorted in LDS
+constexpr int kSortCap = 8192;                // largest candidate set selected in LDS
 constexpr int kMaxSelect = 4096;
 
 // Per-query self-cleaning counters at the start of the workspace (16 x u32 = 64 B).
@@ -252,6 +252,75 @@ struct RadixShared {
     int scan[16];
     int digit, above, inb;
 };
+
+// Key-only threshold among m composites in LDS whose keys all lie in first-digit bucket d1:
+// the need-th largest KEY, by at most two more radix passes (the key's remaining 21 bits).
+// take_eq < 0: every composite with key >= t is selected (exactly `need` of them).  Otherwise
+// the key t itself is the threshold: keys above t are selected, and of the n_tie composites
+// with key == t the take_eq lowest positions (the caller orders those few ties itself).
+struct KeyThr {
+    uint32_t t;
+    int take_eq;
+    int n_tie;
+};
+
+template <int NT>
+__device__ KeyThr lds_key_threshold(const uint64_t* c, int m, int need, int d1, RadixShared& R) {
+    constexpr int BPT = kHistBins / NT;
+    const int t = threadIdx.x;
+    uint32_t prefix = (uint32_t)d1;
+    int pbits = kHistBits;
+    int matching = m;
+    while (pbits < 32 && matching > need) {
+        const int w = (32 - pbits) >= kHistBits ? kHistBits : (32 - pbits);
+        const int shift = 32 - pbits - w;
+        for (int b = t; b < kHistBins; b += NT) R.hist[b] = 0u;
+        __syncthreads();
+        for (int e = t; e < m; e += NT) {
+            const uint32_t key = (uint32_t)(c[e] >> 32);
+            if ((key >> (32 - pbits)) == prefix) atomicAdd(&R.hist[(key >> shift) & ((1u << w) - 1)], 1u);
+        }
+        __syncthreads();
+        const int nb = 1 << w;
+        uint32_t h[BPT];
+        int local = 0;
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            const int b = nb - 1 - (BPT * t + j);
+            h[j] = b >= 0 ? R.hist[b] : 0u;
+            local += (int)h[j];
+        }
+        int tot;
+        int a = block_exclusive_scan<NT>(local, R.scan, tot);
+#pragma unroll
+        for (int j = 0; j < BPT; ++j) {
+            const int cnt = (int)h[j];
+            if (a < need && a + cnt >= need) {
+                R.digit = nb - 1 - (BPT * t + j);
+                R.above = a;
+                R.inb = cnt;
+            }
+            a += cnt;
+        }
+        __syncthreads();
+        prefix = (prefix << w) | (uint32_t)R.digit;
+        pbits += w;
+        need -= R.above;
+        matching = R.inb;
+        __syncthreads();
+    }
+    KeyThr r;
+    if (matching > need) {  // all 32 key bits fixed: ties at the threshold key
+        r.t = prefix;
+        r.take_eq = need;
+        r.n_tie = matching;
+    } else {
+        r.t = prefix << (32 - pbits);
+        r.take_eq = -1;
+        r.n_tie = 0;
+    }
+    return r;
+}
 
 template <int NT>
 __device__ uint64_t lds_radix_threshold(const uint64_t* c, int m, int need, int d1, RadixShared& R) {

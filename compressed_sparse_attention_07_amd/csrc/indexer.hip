@@ -729,11 +729,14 @@ struct SmallSel {
     uint32_t sel[kMaxSelect + 4];
     RadixShared R;
     int cnt;
+    int nt;
 };
 union SelLds {
     SelectShared big;
     SmallSel small;
 };
+
+constexpr int kTieCap = 1024;  // equal keys at the threshold ordered by direct counting
 
 // Ascending output of up to kMaxSelect selected positions (sel[] in LDS).
 struct AscLds {
@@ -779,15 +782,51 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
         SmallSel& W = U.small;
         for (int e = t; e < th.in_bucket; e += kSelNT) W.cand[e] = cand[e];
         for (int j = t; j < n_sure; j += kSelNT) W.sel[j] = (uint32_t)sure[j];
-        if (t == 0) W.cnt = n_sure;
+        if (t == 0) {
+            W.cnt = n_sure;
+            W.nt = 0;
+        }
         __syncthreads();
-        const uint64_t thr = (need > 0 && th.in_bucket > 0)
-                                 ? lds_radix_threshold<kSelNT>(W.cand, th.in_bucket, need, th.digit, W.R)
-                                 : ~0ull;
-        for (int e = t; e < th.in_bucket; e += kSelNT)
-            if (W.cand[e] >= thr) W.sel[atomicAdd(&W.cnt, 1)] = composite_pos(W.cand[e]);
-        __syncthreads();
-        sort_out(W.sel, W.cnt, k, out, A);
+        // the threshold KEY first (at most two passes); ties at it are ordered by position below
+        const bool any = need > 0 && th.in_bucket > 0;
+        const KeyThr kt = any ? lds_key_threshold<kSelNT>(W.cand, th.in_bucket, need, th.digit, W.R)
+                              : KeyThr{0u, -1, 0};
+        const bool ranked = any && kt.take_eq >= 0;  // only take_eq of the n_tie equal keys go
+        int total;
+        if (ranked && kt.n_tie > kTieCap) {
+            // many equal keys at the threshold: radix passes over the composites' position bits
+            const uint64_t thr = lds_radix_threshold<kSelNT>(W.cand, th.in_bucket, need, th.digit, W.R);
+            for (int e = t; e < th.in_bucket; e += kSelNT)
+                if (W.cand[e] >= thr) W.sel[atomicAdd(&W.cnt, 1)] = composite_pos(W.cand[e]);
+            __syncthreads();
+            total = W.cnt;
+        } else {
+            uint32_t* ties = A.scratch;  // free until the ascending output
+            for (int e = t; e < th.in_bucket; e += kSelNT) {
+                const uint64_t c = W.cand[e];
+                const uint32_t key = (uint32_t)(c >> 32);
+                if (any && (ranked ? key > kt.t : key >= kt.t))
+                    W.sel[atomicAdd(&W.cnt, 1)] = composite_pos(c);
+                else if (ranked && key == kt.t)
+                    ties[atomicAdd(&W.nt, 1)] = composite_pos(c);
+            }
+            __syncthreads();
+            total = W.cnt;
+            if (ranked) {
+                // each tie's place among the ties by position (distinct positions): the take_eq
+                // lowest follow the keys above the threshold
+                const int nt = W.nt;
+                for (int j = t; j < nt; j += kSelNT) {
+                    const uint32_t p = ties[j];
+                    int rank = 0;
+                    for (int e = 0; e < nt; ++e) rank += ties[e] < p ? 1 : 0;
+                    if (rank < kt.take_eq) W.sel[total + rank] = p;
+                }
+                total += kt.take_eq;
+                __syncthreads();
+            }
+        }
+        sort_out(W.sel, total, k, out, A);
     } else {
         SelectShared& S = U.big;
         const uint64_t thr = wg_threshold<kSelNT>(CompositeList{cand}, th.in_bucket, need, th.digit, S);
