@@ -145,17 +145,19 @@ def test_index_full_tie_heavy_and_repeatable():
         assert np.array_equal(first[1][i], rp)
 
 
-def test_index_full_all_equal_scores_takes_lowest_positions():
-    # every score is 0: the whole context is one tie band (larger than the LDS sort)
-    lengths = [50000, 9000]
+@pytest.mark.parametrize("lengths,pool_blocks", [([50000, 9000], 2048), ([5000, 800, 513], 50)])
+def test_index_full_all_equal_scores_takes_lowest_positions(lengths, pool_blocks):
+    # every score is 0: the whole context is one tie band.  50,000 / 9,000: larger than the LDS
+    # candidate set; 5,000 / 1,125 blocks: in LDS with more ties than are ordered directly;
+    # 800 / 513 positions and 100 / 65 blocks: ties ordered directly by position
     case = IndexCase(W_T + 2, lengths, n_heads=4, kfill=0)
-    idx, pool, _ = case.run_full(512, 2048)
+    idx, pool, _ = case.run_full(512, pool_blocks)
     idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
-    for i in range(2):
+    for i in range(len(lengths)):
         assert np.array_equal(idx[i], np.arange(512))
         nb = -(-lengths[i] // 8)
-        assert np.array_equal(pool[i], np.arange(2048) if nb >= 2048 else
-                              np.concatenate([np.arange(nb), -np.ones(2048 - nb, int)]))
+        assert np.array_equal(pool[i], np.arange(pool_blocks) if nb >= pool_blocks else
+                              np.concatenate([np.arange(nb), -np.ones(pool_blocks - nb, int)]))
 
 
 # ---------------------------------------------------------------- prefill chunk (MFMA scoring)
