@@ -489,13 +489,26 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
 // ----------------------------------------------------------------------------------------
 constexpr int kPfQ = 16;       // queries per workgroup
 constexpr int kPfPos = 4096;   // positions per workgroup (1,024 per wave)
+// What a pass of the prefill scoring kernel produces.  A chunk's selection runs it twice:
+// kPfHist (first-digit histograms, and the block keys when pools are asked for), then, once
+// k_idx_prefill_thresh has put every query's threshold bucket in the workspace, kPfCompact:
+// the same scores again, with only the positions at or above the bucket written, straight into
+// the lists the selection reads.  Scores are recomputed rather than stored: a chunk has
+// 4,096 x ~133K (query, position) pairs, and a 4-byte key for each (2.2 GB out and back in)
+// costs several times the MFMA work.
+constexpr int kPfHist = 1, kPfCompact = 2;
+constexpr int kPfBuf = 256;    // positions of one query a workgroup gathers in LDS before writing
 
 
-template <bool POOL>
+template <bool POOL, int MODE>
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, IndexWs ws) {
-    __shared__ uint32_t sh_hist[kPfQ][kHistBins / 2];
+    const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, int top_k, IndexWs ws) {
+    constexpr bool kCompact = MODE == kPfCompact;
+    __shared__ uint32_t sh_hist[kCompact ? 1 : kPfQ][kHistBins / 2];
+    __shared__ uint64_t sh_buf[kCompact ? kPfQ : 1][kCompact ? kPfBuf : 1];  // selected entries per query
+    __shared__ int sh_cnt[kPfQ];
+    __shared__ int sh_thr[kPfQ];
     __shared__ int sh_n[kPfQ];
     __shared__ int64_t sh_base[kPfQ];
     const int t = threadIdx.x;
@@ -517,13 +530,17 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
         }
         sh_n[t] = n;
         sh_base[t] = base;
+        sh_cnt[t] = 0;
+        // threshold bucket of the query (k_idx_prefill_thresh); -1: every position is kept
+        sh_thr[t] = (kCompact && q < n_q) ? ws.meta[2 * q].digit : 0;
     }
     __syncthreads();
     int n_max = 0;
 #pragma unroll
     for (int k = 0; k < kPfQ; ++k) n_max = max(n_max, sh_n[k]);
     if (p_wg >= n_max) return;  // uniform: nothing visible in this position chunk
-    for (int k = t; k < kPfQ * kHistBins / 2; k += kScoreNT) (&sh_hist[0][0])[k] = 0u;
+    if constexpr (!kCompact)
+        for (int k = t; k < kPfQ * kHistBins / 2; k += kScoreNT) (&sh_hist[0][0])[k] = 0u;
     // A fragments: query q0 + r, head h, channels 32s + 8g .. +8 ; weights of queries q0 + 4g + i
     bf16x8_t qa[4][2];
     float wq[4][4];
@@ -541,12 +558,13 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
             wq[i][h] = (qi < n_q && h < n_heads) ? w[(int64_t)qi * n_heads + h] : 0.f;
         }
     }
-    int nq[4];
+    int nq[4], thr[4];
     int64_t bq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         nq[i] = sh_n[4 * g + i];
         bq[i] = sh_base[4 * g + i];
+        thr[i] = sh_thr[4 * g + i];
     }
     __syncthreads();
 
@@ -586,12 +604,31 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
                 for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], relu(acc[h][i]), sc);
                 const bool ok = p < nq[i];
                 const uint32_t key = ok ? score_key(sc) : 0u;
-                if (ok) {
-                    ws.keys[bq[i] + p] = key;
+                if constexpr (kCompact) {
+                    // at or above the query's threshold bucket: a sure position (above) or a
+                    // candidate (in it), gathered in LDS (candidate keys are never 0; a sure
+                    // entry is the bare position)
+                    const int dg = (int)(key >> 21);
+                    if (ok && dg >= thr[i]) {
+                        const int ql = 4 * g + i;
+                        const uint64_t e = dg > thr[i] ? (uint64_t)(uint32_t)p : composite(key, (uint32_t)p);
+                        const int slot = atomicAdd(&sh_cnt[ql], 1);
+                        if (slot < kPfBuf) {
+                            sh_buf[ql][slot] = e;
+                        } else {  // more than the buffer holds (heavy ties): straight to the list
+                            const int q = q0 + ql;
+                            uint32_t* ctrl = ws.ctrl + (int64_t)q * kCtlSlots;
+                            if (dg > thr[i])
+                                ws.sure_idx[(int64_t)q * top_k + atomicAdd(ctrl + kCtlSureIdx, 1u)] = p;
+                            else
+                                ws.cand_idx[bq[i] + atomicAdd(ctrl + kCtlCandIdx, 1u)] = e;
+                        }
+                    }
+                } else if (ok) {
                     const uint32_t bin = key >> 21;
                     atomicAdd(&sh_hist[4 * g + i][bin >> 1], 1u << (16 * (bin & 1)));
                 }
-                if constexpr (POOL) {
+                if constexpr (POOL && !kCompact) {
                     const uint32_t bk = max_over_8_lanes(key);      // lanes 4 / 12 of the row
                     const int pblk = base + 16 * u + (r & 8);
                     if ((r & 7) == 4 && pblk < nq[i]) ws.bkeys[bq[i] / 8 + (pblk >> 3)] = bk;
@@ -600,14 +637,58 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
         }
     }
     __syncthreads();
-    for (int k = t; k < kPfQ * kHistBins / 2; k += kScoreNT) {
-        const int ql = k / (kHistBins / 2), wd = k % (kHistBins / 2);
-        const uint32_t v = sh_hist[ql][wd];
-        if (v == 0u || q0 + ql >= n_q) continue;
-        uint32_t* gh = ws.hist + (int64_t)(q0 + ql) * 2 * kHistBins;
-        if (v & 0xffffu) atomicAdd(&gh[2 * wd], v & 0xffffu);
-        if (v >> 16) atomicAdd(&gh[2 * wd + 1], v >> 16);
+    if constexpr (kCompact) {
+        // each wave writes the gathered entries of four queries: one reservation per list and
+        // query, places from ballots (no LDS atomics)
+        for (int ql = wid; ql < kPfQ; ql += kScoreNT / kWave) {
+            const int q = q0 + ql;
+            const int nb = min(sh_cnt[ql], kPfBuf);
+            if (q >= n_q || nb == 0) continue;
+            int ns = 0;
+            for (int j0 = 0; j0 < nb; j0 += kWave) {
+                const int j = j0 + lane;
+                ns += __popcll(__ballot(j < nb && (sh_buf[ql][j] >> 32) == 0ull));
+            }
+            uint32_t* ctrl = ws.ctrl + (int64_t)q * kCtlSlots;
+            int bs = 0, bc = 0;
+            if (lane == 0) {
+                if (ns) bs = (int)atomicAdd(ctrl + kCtlSureIdx, (uint32_t)ns);
+                if (nb - ns) bc = (int)atomicAdd(ctrl + kCtlCandIdx, (uint32_t)(nb - ns));
+            }
+            bs = __builtin_amdgcn_readfirstlane(bs);
+            bc = __builtin_amdgcn_readfirstlane(bc);
+            for (int j0 = 0; j0 < nb; j0 += kWave) {
+                const int j = j0 + lane;
+                const uint64_t e = j < nb ? sh_buf[ql][j] : 0ull;
+                const bool is_s = j < nb && (e >> 32) == 0ull, is_c = j < nb && (e >> 32) != 0ull;
+                const uint64_t ms = __ballot(is_s), mc = __ballot(is_c);
+                const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+                if (is_s) ws.sure_idx[(int64_t)q * top_k + bs + __popcll(ms & below)] = (int32_t)(uint32_t)e;
+                if (is_c) ws.cand_idx[sh_base[ql] + bc + __popcll(mc & below)] = e;
+                bs += __popcll(ms);
+                bc += __popcll(mc);
+            }
+        }
+    } else {
+        for (int k = t; k < kPfQ * kHistBins / 2; k += kScoreNT) {
+            const int ql = k / (kHistBins / 2), wd = k % (kHistBins / 2);
+            const uint32_t v = sh_hist[ql][wd];
+            if (v == 0u || q0 + ql >= n_q) continue;
+            uint32_t* gh = ws.hist + (int64_t)(q0 + ql) * 2 * kHistBins;
+            if (v & 0xffffu) atomicAdd(&gh[2 * wd], v & 0xffffu);
+            if (v >> 16) atomicAdd(&gh[2 * wd + 1], v >> 16);
+        }
     }
+}
+
+// Prefill chunk: every query's threshold bucket for its Top-K from the finished position
+// histogram (one workgroup per query), for the compacting scoring pass.
+__global__ __launch_bounds__(kScoreNT) void k_idx_prefill_thresh(int top_k, IndexWs ws) {
+    __shared__ int sh_scan[kScoreNT / kWave];
+    __shared__ Thresh sh_th;
+    const int i = blockIdx.x;
+    find_threshold_256(ws.hist + (int64_t)i * 2 * kHistBins, top_k, sh_scan, &sh_th);
+    if (threadIdx.x == 0) ws.meta[2 * i] = sh_th;
 }
 
 // First-digit histogram of each query's block-max keys (prefill chunk with pools): workgroup
@@ -684,7 +765,8 @@ __device__ void wg_compact(const uint32_t* keys, int e_begin, int e_end, const T
 __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __restrict__ kv_row0,
                                                               const int32_t* __restrict__ kv_len, int n_q,
                                                               int32_t max_len, int64_t cache_rows, int grid_tiles,
-                                                              int grid_ftiles, int top_k, int pool_blocks, IndexWs ws) {
+                                                              int grid_ftiles, int top_k, int pool_blocks, int pos_done,
+                                                              IndexWs ws) {
     __shared__ int sh_scan[8];
     __shared__ int sh_base[2];
     __shared__ Thresh sh_th;
@@ -698,13 +780,15 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __r
     uint32_t* ctrl = ws.ctrl + (int64_t)i * kCtlSlots;
     const uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
 
-    find_threshold_256(gh, top_k, sh_scan, &sh_th);
-    const Thresh th = sh_th;
-    __syncthreads();
-    const int p0 = fchunk * kFilterTile;
-    wg_compact<kFilterTile / kScoreNT>(ws.keys + key_base, p0, min(n, p0 + kFilterTile), th,
-                                       ws.sure_idx + (int64_t)i * top_k, ctrl + kCtlSureIdx, ws.cand_idx + key_base,
-                                       ctrl + kCtlCandIdx, sh_scan, sh_base);
+    if (!pos_done) {  // (a prefill chunk's compacting pass wrote the position lists already)
+        find_threshold_256(gh, top_k, sh_scan, &sh_th);
+        const Thresh th = sh_th;
+        __syncthreads();
+        const int p0 = fchunk * kFilterTile;
+        wg_compact<kFilterTile / kScoreNT>(ws.keys + key_base, p0, min(n, p0 + kFilterTile), th,
+                                           ws.sure_idx + (int64_t)i * top_k, ctrl + kCtlSureIdx,
+                                           ws.cand_idx + key_base, ctrl + kCtlCandIdx, sh_scan, sh_base);
+    }
     if (pool_blocks > 0) {
         find_threshold_256(gh + kHistBins, pool_blocks, sh_scan, &sh_th);
         const Thresh tp = sh_th;
@@ -995,15 +1079,24 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
     if (phase & 2) {
         if (prefill && max_len > 0) {  // (no visible position anywhere: nothing to score)
             const dim3 grid((unsigned)((max_len + kPfPos - 1) / kPfPos), (unsigned)((n_q + kPfQ - 1) / kPfQ));
-            hipLaunchKernelGGL(pool_blocks > 0 ? k_idx_score_prefill<true> : k_idx_score_prefill<false>, grid,
-                               dim3(kScoreNT), 0, stream, q_idx, w, static_cast<const uint16_t*>(k_idx), kv_row0, n_q,
-                               cache_rows, n_heads, ws);
+            const uint16_t* kb = static_cast<const uint16_t*>(k_idx);
+            auto k_hist = pool_blocks > 0 ? k_idx_score_prefill<true, kPfHist> : k_idx_score_prefill<false, kPfHist>;
+            hipLaunchKernelGGL(k_hist, grid, dim3(kScoreNT), 0, stream, q_idx, w, kb, kv_row0, n_q, cache_rows, n_heads,
+                               top_k, ws);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
             if (pool_blocks > 0) {
-                hipError_t e = hipGetLastError();
-                if (e != hipSuccess) return e;
                 const dim3 bgrid((unsigned)(((max_len + 7) / 8 + kBhChunk - 1) / kBhChunk), (unsigned)n_q);
                 hipLaunchKernelGGL(k_idx_block_hist, bgrid, dim3(kScoreNT), 0, stream, kv_row0, cache_rows, ws);
+                e = hipGetLastError();
+                if (e != hipSuccess) return e;
             }
+            hipLaunchKernelGGL(k_idx_prefill_thresh, dim3(n_q), dim3(kScoreNT), 0, stream, top_k, ws);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            auto k_compact = k_idx_score_prefill<false, kPfCompact>;
+            hipLaunchKernelGGL(k_compact, grid, dim3(kScoreNT), 0, stream, q_idx, w, kb, kv_row0, n_q, cache_rows,
+                               n_heads, top_k, ws);
         } else if (!prefill) {
             const int wgs = min(grid_tiles, scan_workgroups());
             auto kern = mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true> : k_idx_score_full<8, true, false>)
@@ -1016,10 +1109,12 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
         if (e != hipSuccess) return e;
     }
     if (phase & 4) {
-        hipLaunchKernelGGL(k_idx_filter_full, dim3(grid_ftiles), dim3(kScoreNT), 0, stream, kv_row0, kv_len, n_q,
-                           max_len, cache_rows, grid_tiles, grid_ftiles, top_k, pool_blocks, ws);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (!prefill || pool_blocks > 0) {  // a prefill chunk's position lists are written by its scan
+            hipLaunchKernelGGL(k_idx_filter_full, dim3(grid_ftiles), dim3(kScoreNT), 0, stream, kv_row0, kv_len, n_q,
+                               max_len, cache_rows, grid_tiles, grid_ftiles, top_k, pool_blocks, prefill, ws);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         hipLaunchKernelGGL(k_idx_select_full, dim3(n_q, pool_blocks > 0 ? 2 : 1), dim3(kSelNT), 0, stream, kv_row0,
                            kv_len, n_q, max_len, cache_rows, grid_tiles, top_k, pool_blocks, ws, idx_out, pool_out);
         return hipGetLastError();
