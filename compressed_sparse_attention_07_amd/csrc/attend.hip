@@ -520,22 +520,19 @@ __global__ __launch_bounds__(kAttNT) void k_attend(AttendArgs a) {
 // Reindex layer, second kernel: the query's selection inside its pool (reindex_select_query,
 // over the keys the Reindex scoring kernel wrote), kept in LDS and written to idx_out for the
 // Reuse layers that follow, then the attention over it, in one workgroup: the selection's
-// output never makes a round trip through memory and the layer saves a kernel launch.  The
-// selection's candidate buffer and the attention's tiles share one LDS area.
+// output never makes a round trip through memory and the layer saves a kernel launch.
 template <int EPT, bool kWin, bool kW8>
 __global__ __launch_bounds__(kAttNT) void k_reindex_attend(const int32_t* __restrict__ pool, int pool_blocks,
                                                            IndexWs ws, int32_t* __restrict__ idx_out, AttendArgs a) {
-    constexpr int kCandB = kAttNT * EPT * 4;
-    __shared__ __align__(16) uint8_t s_area[kCandB > kAttWaves * kTileB ? kCandB : kAttWaves * kTileB];
+    __shared__ __align__(16) uint8_t s_area[kAttWaves * kTileB];
     __shared__ uint32_t s_hist[2][kHistBins];
     __shared__ int32_t s_idx[kMaxSelect];
     __shared__ int s_scan[kAttNT / kWave];
     __shared__ Thresh sh_th;
     __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
     const int i = blockIdx.x;
-    reindex_select_query<kAttNT, EPT>(i, pool, pool_blocks, a.top_k, ws, idx_out, s_idx, s_hist,
-                                      reinterpret_cast<uint32_t*>(s_area), s_scan, &sh_th);
-    __syncthreads();  // the selection is in s_idx; the candidate area becomes the tiles
+    reindex_select_query<kAttNT, EPT>(i, pool, pool_blocks, a.top_k, ws, idx_out, s_idx, s_hist, s_scan, &sh_th);
+    __syncthreads();  // the selection is in s_idx
     attend_query<true, kWin, kW8>(i, a, s_idx, AttendLds{s_area, s_m, s_l});
 }
 

@@ -1032,11 +1032,10 @@ __global__ __launch_bounds__(kSelNT) void k_idx_reindex_select(const int32_t* __
                                                                int top_k, IndexWs ws,
                                                                int32_t* __restrict__ idx_out) {
     __shared__ uint32_t s_hist[2][kHistBins];
-    __shared__ uint32_t s_cand[kSelNT * EPT];  // keys of the first-digit bucket
     __shared__ int s_scan[kSelNT / kWave];
     __shared__ Thresh sh_th;
-    reindex_select_query<kSelNT, EPT>(blockIdx.x, pool, pool_blocks, top_k, ws, idx_out, nullptr, s_hist, s_cand,
-                                      s_scan, &sh_th);
+    reindex_select_query<kSelNT, EPT>(blockIdx.x, pool, pool_blocks, top_k, ws, idx_out, nullptr, s_hist, s_scan,
+                                      &sh_th);
 }
 
 // ----------------------------------------------------------------------------------------

@@ -5,7 +5,7 @@
 // IX: a Reindex layer takes its own Top-K inside the shared pool.  The pool is ascending, so
 // element order is position order: the K-th largest key T comes from the first-digit
 // histogram the scoring kernel built plus at most two radix passes over the bucket's keys
-// (compacted to LDS first), and one packed (greater-than-T, equal-to-T) block scan ranks the
+// (in registers), and one packed (greater-than-T, equal-to-T) block scan ranks the
 // ties at T and places every selected element in ascending position order.
 #pragma once
 
@@ -19,8 +19,8 @@ namespace csa2 {
 template <int NT, int EPT>
 __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __restrict__ pool, int pool_blocks,
                                                      int top_k, const IndexWs& ws, int32_t* __restrict__ idx_out,
-                                                     int32_t* lds_idx, uint32_t (*s_hist)[kHistBins],
-                                                     uint32_t* s_cand, int* s_scan, Thresh* sh_th_p) {
+                                                     int32_t* lds_idx, uint32_t (*s_hist)[kHistBins], int* s_scan,
+                                                     Thresh* sh_th_p) {
     Thresh& sh_th = *sh_th_p;
     const int t = threadIdx.x;
     const int n_elem = pool_blocks * 8;
@@ -57,25 +57,16 @@ __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __res
         uint32_t prefix = (uint32_t)th.digit;
         int pbits = kHistBits;
         if (inb > need) {
-            // compact the bucket's keys to LDS (order is irrelevant: only T is sought)
-            uint32_t in_mask = 0u;
-#pragma unroll
-            for (int j = 0; j < EPT; ++j) in_mask |= (uint32_t)((kv[j] >> (32 - kHistBits)) == prefix) << j;
-            int m;
-            int off = block_exclusive_scan<NT>(__popc(in_mask), s_scan, m);
-#pragma unroll
-            for (int j = 0; j < EPT; ++j)
-                if ((in_mask >> j) & 1u) s_cand[off++] = kv[j];
-            __syncthreads();
-            // at most two more radix passes (11 and 10 bits) over the m bucket keys
+            // at most two more radix passes (11 and 10 bits) over the bucket's keys, straight
+            // from the registers (a pass costs EPT compares per thread; no compaction)
             int hb = 0;
             while (pbits < 32 && inb > need) {
                 const int w = min(kHistBits, 32 - pbits);
                 const int shift = 32 - pbits - w;
-                for (int e = t; e < m; e += NT) {
-                    const uint32_t v = s_cand[e];
-                    if ((v >> (32 - pbits)) == prefix) atomicAdd(&s_hist[hb][(v >> shift) & ((1u << w) - 1u)], 1u);
-                }
+#pragma unroll
+                for (int j = 0; j < EPT; ++j)
+                    if (kv[j] != 0u && (kv[j] >> (32 - pbits)) == prefix)
+                        atomicAdd(&s_hist[hb][(kv[j] >> shift) & ((1u << w) - 1u)], 1u);
                 __syncthreads();
                 find_threshold<NT>(s_hist[hb], need, s_scan, &sh_th);
                 th = sh_th;  // inb > need, so a digit is found
