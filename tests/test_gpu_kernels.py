@@ -210,6 +210,18 @@ def test_index_prefill_mfma_per_query_pools(pool_blocks):
         assert np.array_equal(idx2[t], case.oracle_reindex(t, pool_m[t], 512, q=q2[t], w=w2[t])), t
 
 
+def test_index_prefill_all_equal_scores_takes_lowest_positions():
+    # every score is 0: every visible position of every token is in the threshold bucket, so
+    # the compacting pass overflows its per-token LDS buffer and writes the rest directly
+    lengths = [3000 + 7 * t for t in range(32)]
+    case = SharedIndexCase(W_T + 62, 3300, lengths, n_heads=4, qlo=0, qhi=0)
+    idx, pool, _ = case.run_full(512, 100, shared_kv=1)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for t in range(len(lengths)):
+        assert np.array_equal(idx[t], np.arange(512)), t
+        assert np.array_equal(pool[t], np.arange(100)), t
+
+
 def test_index_prefill_nothing_visible():
     # a chunk of 16 queries that see no position at all: every output is -1 padding
     case = SharedIndexCase(W_T + 61, 64, [0] * 16, n_heads=4)
