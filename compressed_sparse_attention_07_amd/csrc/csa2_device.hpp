@@ -88,8 +88,6 @@ __device__ __forceinline__ int pow2_ceil(int n) {
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
-
 // Valid length of query i: kv_len clamped to [0, max_len] and to the rows after kv_row0.
 __device__ __forceinline__ int32_t eff_len_of(int64_t n, int64_t r0, int32_t max_len, int64_t cache_rows) {
     if (n < 0) n = 0;
@@ -138,68 +136,6 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) 
     if (TAIL_SYNC) __syncthreads();
     total = tot;
     return wbase + x - v;
-}
-
-// Ragged tile map: query i owns T_i = max(1, ceil(n_i / CH)) consecutive tiles of the grid,
-// clamped so that the whole map fits `grid_tiles` (every query keeps at least one tile).
-// Every workgroup derives the same map; this one returns the query that owns tile `tile`.
-struct TileInfo {
-    int32_t q;       // query index, -1 if the tile is unused
-    int32_t chunk;   // tile index within the query
-    int32_t start;   // first tile of the query
-    int32_t ntiles;  // tiles of the query
-    int32_t n;       // clamped visible length
-};
-
-// With want_query < 0: find the query owning tile `tile`.  With want_query >= 0: return the
-// map entry of that query (chunk = 0).
-template <int NT>
-__device__ TileInfo tile_map(const int32_t* kv_len, const int64_t* kv_row0, int n_q, int32_t max_len,
-                             int64_t cache_rows, int ch, int grid_tiles, int tile, int want_query, int* sh_scan,
-                             TileInfo* sh_out) {
-    const int extra_cap = grid_tiles - n_q;  // tiles beyond one per query
-    if (threadIdx.x == 0) sh_out->q = -1;
-    int run = 0;  // raw prefix of extra tiles before this chunk of queries
-    for (int base = 0; base < n_q; base += NT) {
-        int i = base + (int)threadIdx.x;
-        int n = 0, x = 0;
-        if (i < n_q) {
-            n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
-            int t = (int)(((int64_t)n + ch - 1) / ch);
-            x = t > 1 ? t - 1 : 0;
-        }
-        int tot;
-        int ex = block_exclusive_scan<NT>(x, sh_scan, tot);
-        if (i < n_q) {
-            int p0 = min(extra_cap, run + ex);
-            int p1 = min(extra_cap, run + ex + x);
-            int start = i + p0;
-            int nt = 1 + (p1 - p0);
-            bool hit = want_query >= 0 ? (i == want_query) : (tile >= start && tile < start + nt);
-            if (hit) {
-                TileInfo ti;
-                ti.q = i;
-                ti.chunk = want_query >= 0 ? 0 : tile - start;
-                ti.start = start;
-                ti.ntiles = nt;
-                ti.n = min(n, nt * ch);
-                *sh_out = ti;
-            }
-        }
-        run += tot;
-        if (run > extra_cap) run = extra_cap + 1;  // saturate (keeps ints small)
-    }
-    __syncthreads();
-    TileInfo r = *sh_out;
-    __syncthreads();
-    return r;
-}
-
-template <int NT>
-__device__ __forceinline__ TileInfo tile_lookup(const int32_t* kv_len, const int64_t* kv_row0, int n_q,
-                                                int32_t max_len, int64_t cache_rows, int ch, int grid_tiles, int tile,
-                                                int* sh_scan, TileInfo* sh_out) {
-    return tile_map<NT>(kv_len, kv_row0, n_q, max_len, cache_rows, ch, grid_tiles, tile, -1, sh_scan, sh_out);
 }
 
 // Search a 2048-bin histogram (counts of the top key digit) from the top for the bucket
@@ -371,76 +307,6 @@ __device__ uint64_t lds_radix_threshold(const uint64_t* c, int m, int need, int 
     return pbits >= 64 ? prefix : (prefix << (64 - pbits));
 }
 
-// Ascending bitonic sort of n <= E*NT 32-bit values held E per thread (element e = E*t + i), padded
-// with 0xffffffff.  Partners within a thread or a wave are exchanged in registers and with
-// cross-lane shuffles; only partners in another wave go through LDS (xchg, E*NT words) with
-// workgroup barriers.
-template <int NT, int E>
-__device__ void regs_bitonic_asc(uint32_t (&x)[E], int n, uint32_t* xchg) {
-    const int t = threadIdx.x;
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            if (stride < E) {
-#pragma unroll
-                for (int i = 0; i < E; ++i) {
-                    const int j = i ^ stride;
-                    if (j > i) {
-                        const int e = E * t + i;
-                        const bool asc = (e & size) == 0;
-                        const uint32_t a = x[i], b = x[j];
-                        x[i] = asc ? min(a, b) : max(a, b);
-                        x[j] = asc ? max(a, b) : min(a, b);
-                    }
-                }
-            } else if (stride / E < kWave) {
-                const int lx = stride / E;
-                const bool lower = (t & lx) == 0;
-#pragma unroll
-                for (int i = 0; i < E; ++i) {
-                    const uint32_t y = (uint32_t)__shfl_xor((int)x[i], lx, kWave);
-                    const int e = E * t + i;
-                    const bool asc = (e & size) == 0;
-                    x[i] = (lower == asc) ? min(x[i], y) : max(x[i], y);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < E; ++i) xchg[E * t + i] = x[i];
-                __syncthreads();
-#pragma unroll
-                for (int i = 0; i < E; ++i) {
-                    const int e = E * t + i;
-                    const uint32_t y = xchg[e ^ stride];
-                    const bool asc = (e & size) == 0;
-                    const bool lower = (e & stride) == 0;
-                    x[i] = (lower == asc) ? min(x[i], y) : max(x[i], y);
-                }
-                __syncthreads();
-            }
-        }
-    }
-}
-
-// Write the `total` (<= E*NT) distinct values of sel[] (LDS) to out[0..k) in ascending order,
-// -1 padded.  sel[] is also used as the exchange buffer of the sort.
-template <int NT, int E>
-__device__ void sort_write_ascending(uint32_t* sel, int total, int k, int32_t* out) {
-    const int t = threadIdx.x;
-    uint32_t x[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-        const int e = E * t + i;
-        x[i] = e < total ? sel[e] : 0xffffffffu;
-    }
-    __syncthreads();
-    regs_bitonic_asc<NT, E>(x, pow2_ceil(total > 1 ? total : 2), sel);
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-        const int e = E * t + i;
-        if (e < k) out[e] = e < total ? (int32_t)x[i] : -1;
-    }
-    for (int j = E * NT + t; j < k; j += NT) out[j] = -1;
-}
-
 // Ascending output of `total` distinct values sel[0..total) (LDS) to out[0..k), -1 padded,
 // without a sort network: one counting pass over kAscB buckets of the values' range
 // [vmin, vmax] (bucket = (v - vmin) >> shift), an exclusive scan of the counts, a scatter into
@@ -522,25 +388,6 @@ __device__ void bucket_write_ascending(const uint32_t* sel, int total, int k, in
     for (int j = total + t; j < k; j += NT) out[j] = -1;
 }
 
-// Write the `total` distinct positions in sel[] (LDS) to out[0..k) in ascending order, -1 padded:
-// each position's slot is the number of smaller positions (no sort network, no barriers).
-template <int NT>
-__device__ void write_ascending(const uint32_t* sel, int total, int k, int32_t* out) {
-    const int t = threadIdx.x;
-    for (int j = t; j < total; j += NT) {
-        const uint32_t p = sel[j];
-        int slot = 0;
-        int i = 0;
-        for (; i + 4 <= total; i += 4) {
-            const uint4 v = *reinterpret_cast<const uint4*>(sel + i);
-            slot += (v.x < p) + (v.y < p) + (v.z < p) + (v.w < p);
-        }
-        for (; i < total; ++i) slot += sel[i] < p;
-        out[slot] = (int32_t)p;
-    }
-    for (int j = total + t; j < k; j += NT) out[j] = -1;
-}
-
 // Bitonic sort of n (power of two, <= kSortCap) 64-bit values in LDS, descending.
 template <int NT>
 __device__ inline void bitonic_desc_u64(uint64_t* a, int n) {
@@ -560,27 +407,6 @@ __device__ inline void bitonic_desc_u64(uint64_t* a, int n) {
         }
     }
 }
-
-// Bitonic sort of n (power of two) 32-bit values in LDS, ascending.
-template <int NT>
-__device__ inline void bitonic_asc_u32(uint32_t* a, int n) {
-    for (int size = 2; size <= n; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = threadIdx.x; t < (n >> 1); t += NT) {
-                int lo = 2 * t - (t & (stride - 1));
-                int hi = lo + stride;
-                bool asc = ((lo & size) == 0);
-                uint32_t x = a[lo], y = a[hi];
-                if ((x > y) == asc) {
-                    a[lo] = y;
-                    a[hi] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
 
 // LDS working set of one workgroup-level selection.
 struct SelectShared {

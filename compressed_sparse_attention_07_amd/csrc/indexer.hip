@@ -66,16 +66,9 @@ constexpr int kScoreNT = 256;
 #define CSA2_SCAN_LP_BF16 0
 #endif
 constexpr int kFullTile = CSA2_SCAN_TILE;       // positions per Full-scan workgroup
-constexpr int kFullTileBlocks = kFullTile / 8;
 constexpr int kReindexTile = 512;               // pool positions (64 blocks) per Reindex workgroup
 constexpr int kFilterTile = 16384;              // positions per filter workgroup (4 scan tiles)
 
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
-                                          false);
-}
 
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
 constexpr int kBufWord3 = 0x00020000;  // gfx9 buffer resource word 3: raw 32-bit-format access
