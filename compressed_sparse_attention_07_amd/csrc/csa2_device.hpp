@@ -140,17 +140,22 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int& total) 
 
 // Search a 2048-bin histogram (counts of the top key digit) from the top for the bucket
 // holding the k-th largest element.  NT threads (a divisor of 2048).  Result in *out (shared).
+// hist_load reads thread t's bins (h[j] is bin kHistBins - 1 - (kHistBins / NT * t + j)) and
+// find_threshold_regs searches them, so a caller can issue other loads in between.
 template <int NT>
-__device__ inline void find_threshold(const uint32_t* hist, int k, int* sh_scan, Thresh* out) {
+__device__ inline void hist_load(const uint32_t* hist, uint32_t (&h)[kHistBins / NT]) {
+    constexpr int BPT = kHistBins / NT;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) h[j] = hist[kHistBins - 1 - (BPT * (int)threadIdx.x + j)];
+}
+
+template <int NT>
+__device__ inline void find_threshold_regs(const uint32_t (&h)[kHistBins / NT], int k, int* sh_scan, Thresh* out) {
     constexpr int BPT = kHistBins / NT;  // bins per thread, highest bins to thread 0
     const int t = threadIdx.x;
-    uint32_t h[BPT];
     int local = 0;
 #pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-        h[j] = hist[kHistBins - 1 - (BPT * t + j)];
-        local += (int)h[j];
-    }
+    for (int j = 0; j < BPT; ++j) local += (int)h[j];
     int total;
     // no closing barrier: the barrier below separates these reads of sh_scan from later writes
     int above = block_exclusive_scan<NT, false>(local, sh_scan, total);
@@ -174,6 +179,13 @@ __device__ inline void find_threshold(const uint32_t* hist, int k, int* sh_scan,
         out->total = total;
     }
     __syncthreads();
+}
+
+template <int NT>
+__device__ inline void find_threshold(const uint32_t* hist, int k, int* sh_scan, Thresh* out) {
+    uint32_t h[kHistBins / NT];
+    hist_load<NT>(hist, h);
+    find_threshold_regs<NT>(h, k, sh_scan, out);
 }
 
 __device__ inline void find_threshold_256(const uint32_t* hist, int k, int* sh_scan, Thresh* out) {

@@ -712,86 +712,181 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_block_hist(const int64_t* __re
         if (sh[b]) atomicAdd(&gh[b], sh[b]);
 }
 
-// Compact one workgroup's share of a key array: elements whose first digit is above the threshold
-// bucket go to sure[] (positions), elements in the bucket to cand[] (composites).  Two passes over
-// the keys (count, then write) so each list costs one global atomic per workgroup.
-template <int PER>
-__device__ void wg_compact(const uint32_t* keys, int e_begin, int e_end, const Thresh& th, int32_t* sure,
-                           uint32_t* sure_ctr, uint64_t* cand, uint32_t* cand_ctr, int* sh_scan, int* sh_base) {
-    const int t = threadIdx.x;
-    uint32_t kv[PER];
+// ----------------------------------------------------------------------------------------
+// Splitting a query's keys by the threshold bucket (the filter kernel, and the selection
+// kernel for short contexts).  A workgroup of NT threads holds U quads of keys per thread,
+// element e = e0 + 4 (u NT + t) + c; a zero key is padding.
+// ----------------------------------------------------------------------------------------
+
+// Loads keys[e0, e_end) (e0 a multiple of 4; the array is readable up to e_end rounded up to 4).
+// Quads at or past e_end read as zero through the buffer bound; the rest of a partial last quad
+// is cleared by mask_quads once the loads are waited for.
+template <int NT, int U>
+__device__ __forceinline__ void load_quads(uint4 (&q)[U], const uint32_t* keys, int e0, int e_end) {
+    const int n = e_end > e0 ? e_end - e0 : 0;
+    const BufRsrc rs = tile_rsrc(keys + e0, ((n + 3) & ~3) * 4);
+#pragma unroll
+    for (int u = 0; u < U; ++u) q[u] = buf_ld16(rs, 16 * (u * NT + (int)threadIdx.x), 0);
+}
+
+template <int NT, int U>
+__device__ __forceinline__ void mask_quads(uint4 (&q)[U], int e0, int e_end) {
+    if ((e_end - e0) & 3) {  // uniform
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int rem = e_end - (e0 + 4 * (u * NT + (int)threadIdx.x));
+            q[u].y = rem > 1 ? q[u].y : 0u;
+            q[u].z = rem > 2 ? q[u].z : 0u;
+            q[u].w = rem > 3 ? q[u].w : 0u;
+        }
+    }
+}
+
+// Key bounds of a threshold bucket: above it key > gt, in it lo <= key <= gt (digit -1: every
+// nonzero key is above).
+struct KeySplit {
+    uint32_t gt, lo;
+};
+__device__ __forceinline__ KeySplit key_split(const Thresh& th) {
+    return KeySplit{th.digit >= 0 ? ((uint32_t)th.digit << 21) | 0x1fffffu : 0u,
+                    th.digit > 0 ? (uint32_t)th.digit << 21 : 1u};
+}
+
+// (above, in bucket) counts of this thread's keys packed as above << 16 | in bucket
+template <int U>
+__device__ __forceinline__ int count_quads(const uint4 (&q)[U], KeySplit ks) {
     int ns = 0, nc = 0;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = e_begin + u * kScoreNT + t;
-        kv[u] = e < e_end ? keys[e] : 0u;
-    }
+    for (int u = 0; u < U; ++u) {
+        const uint32_t v4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int dg = (int)(kv[u] >> 21);
-        ns += (kv[u] != 0u && dg > th.digit);
-        nc += (kv[u] != 0u && dg == th.digit);
+        for (int c = 0; c < 4; ++c) {
+            ns += v4[c] > ks.gt ? 1 : 0;
+            nc += v4[c] >= ks.lo && v4[c] <= ks.gt ? 1 : 0;
+        }
     }
-    int tot_s, tot_c;
-    int off_s = block_exclusive_scan<kScoreNT>(ns, sh_scan, tot_s);
-    int off_c = block_exclusive_scan<kScoreNT>(nc, sh_scan, tot_c);
-    if (t == 0) {
-        sh_base[0] = tot_s ? (int)atomicAdd(sure_ctr, (uint32_t)tot_s) : 0;
-        sh_base[1] = tot_c ? (int)atomicAdd(cand_ctr, (uint32_t)tot_c) : 0;
+    return (ns << 16) | nc;
+}
+
+// Writes this thread's above-bucket elements to sure[os..] and in-bucket composites to
+// cand[oc..] (entries at or past cap_s / cap_c are dropped: the histogram the offsets come
+// from counted the same keys, so none is).  Sure entries go out as 32-bit element indices.
+template <int NT, int U, typename SureT>
+__device__ __forceinline__ void write_quads(uint4 (&q)[U], KeySplit ks, int e0, int os, int oc, SureT* sure,
+                                            int cap_s, uint64_t* cand, int cap_c) {
+    // (the tests are recomputed here rather than 2 x 4U lane masks kept alive from the count)
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" : "+v"(q[u].x), "+v"(q[u].y), "+v"(q[u].z), "+v"(q[u].w));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t v4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t e = (uint32_t)(e0 + 4 * (u * NT + (int)threadIdx.x) + c);
+            if (v4[c] > ks.gt) {
+                if ((unsigned)os < (unsigned)cap_s) sure[os] = (SureT)e;
+                ++os;
+            } else if (v4[c] >= ks.lo) {
+                if ((unsigned)oc < (unsigned)cap_c) cand[oc] = composite(v4[c], e);
+                ++oc;
+            }
+        }
+    }
+}
+
+// Two block-wide exclusive scans at once (one barrier).  `sh` holds 2 NT/64 ints.
+template <int NT>
+__device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* sh, int& ea, int& eb, int& ta, int& tb) {
+    constexpr int NW = NT / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const int xa = wave_inclusive_scan(a), xb = wave_inclusive_scan(b);
+    if (lane == kWave - 1) {
+        sh[wid] = xa;
+        sh[NW + wid] = xb;
     }
     __syncthreads();
-    off_s += sh_base[0];
-    off_c += sh_base[1];
+    int wa = 0, wb = 0, sa = 0, sb = 0;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int e = e_begin + u * kScoreNT + t;
-        const int dg = (int)(kv[u] >> 21);
-        if (kv[u] != 0u && dg > th.digit) sure[off_s++] = e;
-        if (kv[u] != 0u && dg == th.digit) cand[off_c++] = composite(kv[u], (uint32_t)e);
+    for (int w = 0; w < NW; ++w) {
+        const int va = sh[w], vb = sh[NW + w];
+        if (w < wid) {
+            wa += va;
+            wb += vb;
+        }
+        sa += va;
+        sb += vb;
     }
     __syncthreads();
+    ea = wa + xa - a;
+    eb = wb + xb - b;
+    ta = sa;
+    tb = sb;
 }
 
 // ----------------------------------------------------------------------------------------
-// Full mode, kernel 2: thresholds from the histograms, compaction of the keys
+// Full mode, kernel 2: thresholds from the histograms, compaction of the keys.  One workgroup
+// per filter tile (kFilterTile positions and their blocks) of a query.  Both histograms and
+// all keys of the tile are requested before the first wait; both lists are split in one pass,
+// with one global counter atomic per list and workgroup.
 // ----------------------------------------------------------------------------------------
+constexpr int kFiltU = kFilterTile / (4 * kScoreNT);       // position quads per thread
+constexpr int kFiltUB = kFilterTile / 8 / (4 * kScoreNT);  // block quads per thread
+
 __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __restrict__ kv_row0,
                                                               const int32_t* __restrict__ kv_len, int n_q,
                                                               int32_t max_len, int64_t cache_rows, int grid_tiles,
                                                               int grid_ftiles, int top_k, int pool_blocks, int pos_done,
                                                               IndexWs ws) {
-    __shared__ int sh_scan[8];
-    __shared__ int sh_base[2];
-    __shared__ Thresh sh_th;
+    __shared__ int sh_scan[2 * kScoreNT / kWave];
+    __shared__ int sh_base[4];
+    __shared__ Thresh sh_th[2];
 
     const int i = ws.fmap[blockIdx.x];
     if (i < 0) return;
+    const int t = threadIdx.x;
     const QMeta qm = ws.qmeta[i];
     const int n = qm.n;
+    const int nb = (n + 7) >> 3;
     const int fchunk = (int)blockIdx.x - qm.fstart;
     const int64_t key_base = (int64_t)qm.start * kFullTile;
     uint32_t* ctrl = ws.ctrl + (int64_t)i * kCtlSlots;
     const uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
+    // (a prefill chunk's compacting pass wrote the position lists already: pos_done)
+    const bool do_pos = !pos_done, do_pool = pool_blocks > 0;
+    const int p0 = fchunk * kFilterTile, p1 = do_pos ? min(n, p0 + kFilterTile) : p0;
+    const int b0 = fchunk * (kFilterTile / 8), b1 = do_pool ? min(nb, b0 + kFilterTile / 8) : b0;
 
-    if (!pos_done) {  // (a prefill chunk's compacting pass wrote the position lists already)
-        find_threshold_256(gh, top_k, sh_scan, &sh_th);
-        const Thresh th = sh_th;
-        __syncthreads();
-        const int p0 = fchunk * kFilterTile;
-        wg_compact<kFilterTile / kScoreNT>(ws.keys + key_base, p0, min(n, p0 + kFilterTile), th,
-                                           ws.sure_idx + (int64_t)i * top_k, ctrl + kCtlSureIdx,
-                                           ws.cand_idx + key_base, ctrl + kCtlCandIdx, sh_scan, sh_base);
+    uint32_t h0[kHistBins / kScoreNT], h1[kHistBins / kScoreNT];
+    if (do_pos) hist_load<kScoreNT>(gh, h0);
+    else
+        for (auto& x : h0) x = 0u;
+    if (do_pool) hist_load<kScoreNT>(gh + kHistBins, h1);
+    else
+        for (auto& x : h1) x = 0u;
+    uint4 kq[kFiltU], bq[kFiltUB];
+    load_quads<kScoreNT>(kq, ws.keys + key_base, p0, p1);
+    load_quads<kScoreNT>(bq, ws.bkeys + key_base / 8, b0, b1);
+    find_threshold_regs<kScoreNT>(h0, top_k, sh_scan, &sh_th[0]);
+    find_threshold_regs<kScoreNT>(h1, max(pool_blocks, 1), sh_scan, &sh_th[1]);
+    const KeySplit s0 = key_split(sh_th[0]), s1 = key_split(sh_th[1]);
+    mask_quads<kScoreNT>(kq, p0, p1);
+    mask_quads<kScoreNT>(bq, b0, b1);
+    int e0, e1, t0, t1;  // packed above << 16 | in bucket (a tile has at most 16,384 of each)
+    block_exclusive_scan2<kScoreNT>(count_quads(kq, s0), count_quads(bq, s1), sh_scan, e0, e1, t0, t1);
+    if (t < 4) {
+        const int cnt = t == 0 ? t0 >> 16 : t == 1 ? t0 & 0xffff : t == 2 ? t1 >> 16 : t1 & 0xffff;
+        const int slot = t == 0 ? kCtlSureIdx : t == 1 ? kCtlCandIdx : t == 2 ? kCtlSurePool : kCtlCandPool;
+        sh_base[t] = cnt ? (int)atomicAdd(ctrl + slot, (uint32_t)cnt) : 0;
     }
-    if (pool_blocks > 0) {
-        find_threshold_256(gh + kHistBins, pool_blocks, sh_scan, &sh_th);
-        const Thresh tp = sh_th;
-        __syncthreads();
-        const int nb = (n + 7) >> 3;
-        const int b0 = fchunk * (kFilterTile / 8);
-        wg_compact<kFilterTile / 8 / kScoreNT>(ws.bkeys + key_base / 8, b0, min(nb, b0 + kFilterTile / 8), tp,
-                                               ws.sure_pool + (int64_t)i * pool_blocks, ctrl + kCtlSurePool,
-                                               ws.cand_pool + key_base / 8, ctrl + kCtlCandPool, sh_scan, sh_base);
-    }
+    __syncthreads();
+    if (do_pos)
+        write_quads<kScoreNT>(kq, s0, p0, sh_base[0] + (e0 >> 16), sh_base[1] + (e0 & 0xffff),
+                              ws.sure_idx + (int64_t)i * top_k, top_k, ws.cand_idx + key_base, n);
+    if (do_pool)
+        write_quads<kScoreNT>(bq, s1, b0, sh_base[2] + (e1 >> 16), sh_base[3] + (e1 & 0xffff),
+                              ws.sure_pool + (int64_t)i * pool_blocks, pool_blocks, ws.cand_pool + key_base / 8,
+                              nb);
 }
 
 struct CompositeList {
@@ -815,6 +910,11 @@ union SelLds {
 
 constexpr int kTieCap = 1024;  // equal keys at the threshold ordered by direct counting
 
+// Decode contexts up to this length skip the filter kernel: the selection workgroup reads the
+// query's keys itself (kSelScanU four-key loads per thread, issued before the threshold search).
+constexpr int kSelScanMax = 16384;
+constexpr int kSelScanU = kSelScanMax / (4 * kSelNT);
+
 // Ascending output of up to kMaxSelect selected positions (sel[] in LDS).
 struct AscLds {
     uint32_t scratch[2 * kAscB + kMaxSelect];
@@ -830,12 +930,14 @@ __device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, 
 // Full mode, kernel 3: exact selection inside the threshold bucket; one workgroup per
 // (query, list).  The bucket's candidates normally fit in LDS: radix passes there find the
 // threshold, and each selected position's output slot is its rank among the selected.
+// scan_keys != 0 (decode, every context <= kSelScanMax): the filter kernel did not run and this
+// workgroup splits the query's keys into the above-bucket and in-bucket lists itself.
 // Leaves the histograms and counters of the query zero for the next call.
 // ----------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __restrict__ kv_row0,
                                                             const int32_t* __restrict__ kv_len, int n_q,
                                                             int32_t max_len, int64_t cache_rows, int grid_tiles,
-                                                            int top_k, int pool_blocks, IndexWs ws,
+                                                            int top_k, int pool_blocks, int scan_keys, IndexWs ws,
                                                             int32_t* __restrict__ idx_out,
                                                             int32_t* __restrict__ pool_out) {
     __shared__ SelLds U;
@@ -844,21 +946,44 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
     const int i = blockIdx.x;
     const int which = blockIdx.y;  // 0: positions, 1: pool blocks
     const int t = threadIdx.x;
-    const int64_t key_base = (int64_t)ws.qmeta[i].start * kFullTile;
+    const QMeta qm = ws.qmeta[i];
+    const int64_t key_base = (int64_t)qm.start * kFullTile;
     uint32_t* ctrl = ws.ctrl + (int64_t)i * kCtlSlots;
     uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins + which * kHistBins;
     const int k = which ? pool_blocks : top_k;
-    const uint64_t* cand = which ? ws.cand_pool + key_base / 8 : ws.cand_idx + key_base;
-    const int32_t* sure = which ? ws.sure_pool + (int64_t)i * pool_blocks : ws.sure_idx + (int64_t)i * top_k;
+    uint64_t* cand = which ? ws.cand_pool + key_base / 8 : ws.cand_idx + key_base;
+    int32_t* sure = which ? ws.sure_pool + (int64_t)i * pool_blocks : ws.sure_idx + (int64_t)i * top_k;
     int32_t* out = which ? pool_out + (int64_t)i * pool_blocks : idx_out + (int64_t)i * top_k;
-    find_threshold<kSelNT>(gh, k, U.small.R.scan, &sh_th);
+    uint32_t h[kHistBins / kSelNT];
+    hist_load<kSelNT>(gh, h);
+    // the keys, requested behind the histogram so that waiting for it leaves them in flight
+    uint4 kq[kSelScanU];
+    const int n_elem = scan_keys ? (which ? (qm.n + 7) >> 3 : qm.n) : 0;
+    if (scan_keys) load_quads<kSelNT>(kq, which ? ws.bkeys + key_base / 8 : ws.keys + key_base, 0, n_elem);
+    find_threshold_regs<kSelNT>(h, k, U.small.R.scan, &sh_th);
     const Thresh th = sh_th;
     const int need = k - th.above;
     const int n_sure = min(th.above, k);
-    if (th.in_bucket <= kSortCap) {
+    const bool small = th.in_bucket <= kSortCap;
+    if (scan_keys) {
+        // above the bucket -> sure list, in the bucket -> candidate composites; in LDS when the
+        // bucket fits there, else in the query's global lists for the large-bucket path
+        const KeySplit ks = key_split(th);
+        mask_quads<kSelNT>(kq, 0, n_elem);
+        int tot;  // sure and candidates <= kSelScanMax each: 16 + 16 bits
+        const int pk = block_exclusive_scan<kSelNT>(count_quads(kq, ks), U.small.R.scan, tot);
+        if (small)
+            write_quads<kSelNT>(kq, ks, 0, pk >> 16, pk & 0xffff, U.small.sel, k, U.small.cand, kSortCap);
+        else
+            write_quads<kSelNT>(kq, ks, 0, pk >> 16, pk & 0xffff, sure, k, cand, n_elem);
+        __syncthreads();
+    }
+    if (small) {
         SmallSel& W = U.small;
-        for (int e = t; e < th.in_bucket; e += kSelNT) W.cand[e] = cand[e];
-        for (int j = t; j < n_sure; j += kSelNT) W.sel[j] = (uint32_t)sure[j];
+        if (!scan_keys) {
+            for (int e = t; e < th.in_bucket; e += kSelNT) W.cand[e] = cand[e];
+            for (int j = t; j < n_sure; j += kSelNT) W.sel[j] = (uint32_t)sure[j];
+        }
         if (t == 0) {
             W.cnt = n_sure;
             W.nt = 0;
@@ -1101,14 +1226,17 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
         if (e != hipSuccess) return e;
     }
     if (phase & 4) {
-        if (!prefill || pool_blocks > 0) {  // a prefill chunk's position lists are written by its scan
+        // short decode contexts: the selection workgroups read the keys themselves
+        const int scan_keys = !prefill && max_len <= kSelScanMax ? 1 : 0;
+        if ((!prefill || pool_blocks > 0) && !scan_keys) {  // a prefill chunk's position lists are written by its scan
             hipLaunchKernelGGL(k_idx_filter_full, dim3(grid_ftiles), dim3(kScoreNT), 0, stream, kv_row0, kv_len, n_q,
                                max_len, cache_rows, grid_tiles, grid_ftiles, top_k, pool_blocks, prefill, ws);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
         hipLaunchKernelGGL(k_idx_select_full, dim3(n_q, pool_blocks > 0 ? 2 : 1), dim3(kSelNT), 0, stream, kv_row0,
-                           kv_len, n_q, max_len, cache_rows, grid_tiles, top_k, pool_blocks, ws, idx_out, pool_out);
+                           kv_len, n_q, max_len, cache_rows, grid_tiles, top_k, pool_blocks, scan_keys, ws, idx_out,
+                           pool_out);
         return hipGetLastError();
     }
     return hipSuccess;

@@ -115,6 +115,32 @@ def test_index_full_bit_exact_ragged(top_k, pool_blocks, n_heads):
             assert np.array_equal(pool[i], rp), (i, RAGGED[i])
 
 
+# every context <= 16,384: the selection workgroups split the keys themselves (no filter kernel)
+RAGGED_SHORT = [0, 1, 7, 8, 9, 511, 512, 513, 2047, 2048, 2049, 4101, 16383, 16384]
+
+
+@pytest.mark.parametrize("top_k,pool_blocks,n_heads", [(512, 256, 4), (2048, 2048, 4), (3, 1, 1)])
+def test_index_full_bit_exact_short_contexts(top_k, pool_blocks, n_heads):
+    case = IndexCase(W_T + 70 + top_k, RAGGED_SHORT, n_heads=n_heads)
+    idx, pool, _ = case.run_full(top_k, pool_blocks)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for i in range(len(RAGGED_SHORT)):
+        ri, rp = case.oracle_full(i, top_k, pool_blocks)
+        assert np.array_equal(idx[i], ri), (i, RAGGED_SHORT[i])
+        assert np.array_equal(pool[i], rp), (i, RAGGED_SHORT[i])
+
+
+def test_index_full_tie_heavy_short_contexts():
+    lengths = [3000, 16384, 12345, 5]
+    case = IndexCase(W_T + 71, lengths, n_heads=4, qlo=0, qhi=1)   # scores in a narrow integer range
+    idx, pool, _ = case.run_full(512, 700)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for i in range(len(lengths)):
+        ri, rp = case.oracle_full(i, 512, 700)
+        assert np.array_equal(idx[i], ri), i
+        assert np.array_equal(pool[i], rp), i
+
+
 def test_index_full_many_queries():
     # more queries than one workgroup's scan width: the ragged tile map is built in chunks
     lengths = list(np.random.default_rng(21).integers(0, 5000, size=300))
@@ -145,11 +171,13 @@ def test_index_full_tie_heavy_and_repeatable():
         assert np.array_equal(first[1][i], rp)
 
 
-@pytest.mark.parametrize("lengths,pool_blocks", [([50000, 9000], 2048), ([5000, 800, 513], 50)])
+@pytest.mark.parametrize("lengths,pool_blocks", [([50000, 9000], 2048), ([5000, 800, 513], 50),
+                                                 ([12000, 16384, 600], 2048)])
 def test_index_full_all_equal_scores_takes_lowest_positions(lengths, pool_blocks):
     # every score is 0: the whole context is one tie band.  50,000 / 9,000: larger than the LDS
     # candidate set; 5,000 / 1,125 blocks: in LDS with more ties than are ordered directly;
-    # 800 / 513 positions and 100 / 65 blocks: ties ordered directly by position
+    # 800 / 513 positions and 100 / 65 blocks: ties ordered directly by position; 12,000 and
+    # 16,384 (contexts the selection workgroup splits itself): larger than the LDS set
     case = IndexCase(W_T + 2, lengths, n_heads=4, kfill=0)
     idx, pool, _ = case.run_full(512, pool_blocks)
     idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
