@@ -14,7 +14,7 @@ namespace csa2 {
 #define CSA2_SCAN_TILE 4096
 #endif
 constexpr int kFullTile = CSA2_SCAN_TILE;  // must match the scan kernel's tile
-constexpr int kFilterTile = 16384;
+constexpr int kFilterTile = 8192;
 constexpr int kHistBins = 2048;
 constexpr size_t kAlign = 256;
 constexpr int kFusedMaxPoolElems = 512 * 32;  // pool positions the fused Reindex selection + attention takes

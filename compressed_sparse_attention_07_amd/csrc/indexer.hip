@@ -67,7 +67,7 @@ constexpr int kScoreNT = 256;
 #endif
 constexpr int kFullTile = CSA2_SCAN_TILE;       // positions per Full-scan workgroup
 constexpr int kReindexTile = 512;               // pool positions (64 blocks) per Reindex workgroup
-constexpr int kFilterTile = 16384;              // positions per filter workgroup (4 scan tiles)
+constexpr int kFilterTile = 8192;               // positions per filter workgroup (2 scan tiles)
 
 
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
@@ -202,7 +202,7 @@ __device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t k) {
 
 // ----------------------------------------------------------------------------------------
 // Full mode, kernel 0: per-query metadata.  Query i owns max(1, ceil(n_i / tile)) consecutive
-// scan tiles (kFullTile positions) and filter tiles (16,384), clamped so the map fits the grids the
+// scan tiles (kFullTile positions) and filter tiles (kFilterTile), clamped so the map fits the grids the
 // host sized from its bounds (every query keeps at least one tile of each).  One workgroup.
 // ----------------------------------------------------------------------------------------
 constexpr int kPrepNT = 1024;
@@ -831,7 +831,7 @@ __device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* sh, int
 // with one global counter atomic per list and workgroup.
 // ----------------------------------------------------------------------------------------
 constexpr int kFiltU = kFilterTile / (4 * kScoreNT);       // position quads per thread
-constexpr int kFiltUB = kFilterTile / 8 / (4 * kScoreNT);  // block quads per thread
+constexpr int kFiltUB = (kFilterTile / 8 + 4 * kScoreNT - 1) / (4 * kScoreNT);  // block quads per thread
 
 __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __restrict__ kv_row0,
                                                               const int32_t* __restrict__ kv_len, int n_q,
@@ -872,7 +872,7 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __r
     const KeySplit s0 = key_split(sh_th[0]), s1 = key_split(sh_th[1]);
     mask_quads<kScoreNT>(kq, p0, p1);
     mask_quads<kScoreNT>(bq, b0, b1);
-    int e0, e1, t0, t1;  // packed above << 16 | in bucket (a tile has at most 16,384 of each)
+    int e0, e1, t0, t1;  // packed above << 16 | in bucket (a tile has at most kFilterTile of each)
     block_exclusive_scan2<kScoreNT>(count_quads(kq, s0), count_quads(bq, s1), sh_scan, e0, e1, t0, t1);
     if (t < 4) {
         const int cnt = t == 0 ? t0 >> 16 : t == 1 ? t0 & 0xffff : t == 2 ? t1 >> 16 : t1 & 0xffff;
