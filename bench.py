@@ -146,7 +146,12 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
         "input_copies": copies,
     }
     if wl.prefill_chunk:
-        # a prefill chunk's scan is one dense contraction (all queries x all visible positions x heads x 64)
+        # A prefill chunk's per-query key bytes are re-reads of one shared key array (from the
+        # caches), not HBM traffic, so no HBM rate is derived from them; its scan is one dense
+        # contraction (all queries x all visible positions x heads x 64) priced against MFMA.
+        for k in ("alg_gbps_step", "scan_gbps"):
+            res[k] = None
+        res["hbm_note"] = "prefill: MFMA-bound; per-query key bytes are cache re-reads, no HBM rate given"
         flops = 2.0 * 64 * wl.idx_heads * float(r.q_len.sum())
         tflops = flops / scan_avg_s / 1e12
         res["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -276,7 +281,8 @@ def main() -> int:
         rr, res = measure(w, max(3, args.steps // 2), args.warmup, copies=2 if w in (0, 1) else 1)
         del rr
         torch.cuda.empty_cache()
-        res["step_frac_of_hbm_peak"] = round(res["alg_gbps_step"] / HBM_PEAK_GBPS, 4)
+        res["step_frac_of_hbm_peak"] = (round(res["alg_gbps_step"] / HBM_PEAK_GBPS, 4)
+                                        if res["alg_gbps_step"] is not None else None)
         also.append(res)
 
     line = {
@@ -294,13 +300,14 @@ def main() -> int:
         "data": "synthetic",
         "config": main_res["config"],
         "roofline": main_res["roofline"],
-        "step_alg_gbps": round(main_res["alg_gbps_step"], 1),
+        "step_alg_gbps": (round(main_res["alg_gbps_step"], 1) if main_res["alg_gbps_step"] is not None else None),
         "eager_tokens_per_s": round(main_res["eager_tokens_per_s"], 1),
         "input_copies": main_res["input_copies"],
         "timing": "value: K replays of the step captured in HIP graphs; roofline: HIP events around "
                   "each Full-scan kernel launch (csa2_index_full_scan) in K eager steps issued behind a "
                   "GPU-side wait (no host gaps inside an event pair)",
-        "step_frac_of_hbm_peak": round(main_res["alg_gbps_step"] / HBM_PEAK_GBPS, 4),
+        "step_frac_of_hbm_peak": (round(main_res["alg_gbps_step"] / HBM_PEAK_GBPS, 4)
+                                  if main_res["alg_gbps_step"] is not None else None),
         "cpu_baseline": cpu,
         "also": also,
     }

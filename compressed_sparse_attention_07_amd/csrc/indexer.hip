@@ -204,12 +204,36 @@ __device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t k) {
 // Full mode, kernel 0: per-query metadata.  Query i owns max(1, ceil(n_i / tile)) consecutive
 // scan tiles (kFullTile positions) and filter tiles (kFilterTile), clamped so the map fits the grids the
 // host sized from its bounds (every query keeps at least one tile of each).  One workgroup.
+// maps: which tile -> query maps the following kernels read (kMapScan: the decode scan's,
+// kMapFilter: the filter pass's); the per-query metadata is always written.
 // ----------------------------------------------------------------------------------------
 constexpr int kPrepNT = 1024;
+constexpr int kMapScan = 1, kMapFilter = 2;
+
+// Tile -> query map of one chunk of cnt queries (first tiles s[0..cnt), end s[cnt]).  Few
+// queries with long runs: every thread fills tiles and finds each one's query by binary
+// search, so the work is spread evenly; many queries (short runs): each thread writes its own
+// query's run, no search.
+__device__ __forceinline__ void fill_tile_map(int32_t* __restrict__ map, const int* s, int cnt, int base) {
+    const int t = threadIdx.x;
+    if (cnt > kPrepNT / 4) {
+        if (t < cnt)
+            for (int k = s[t]; k < s[t + 1]; ++k) map[k] = base + t;
+        return;
+    }
+    for (int k = s[0] + t; k < s[cnt]; k += kPrepNT) {
+        int lo = 0, hi = cnt - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s[mid] <= k) lo = mid; else hi = mid - 1;
+        }
+        map[k] = base + lo;
+    }
+}
 
 __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict__ kv_row0,
                                                       const int32_t* __restrict__ kv_len, int n_q, int32_t max_len,
-                                                      int64_t cache_rows, int grid_tiles, int grid_ftiles,
+                                                      int64_t cache_rows, int grid_tiles, int grid_ftiles, int maps,
                                                       IndexWs ws) {
     __shared__ int sh_scan[kPrepNT / kWave];
     __shared__ int s_ts[kPrepNT + 1];  // first scan tile of each query of the chunk, then the end
@@ -250,30 +274,18 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
             }
         }
         __syncthreads();
-        // tile -> query maps, written by every thread (largest q with s_ts[q] <= tile)
-        for (int k = s_ts[0] + t; k < s_ts[cnt]; k += kPrepNT) {
-            int lo = 0, hi = cnt - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_ts[mid] <= k) lo = mid; else hi = mid - 1;
-            }
-            ws.tmap[k] = base + lo;
-        }
-        for (int k = s_fs[0] + t; k < s_fs[cnt]; k += kPrepNT) {
-            int lo = 0, hi = cnt - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_fs[mid] <= k) lo = mid; else hi = mid - 1;
-            }
-            ws.fmap[k] = base + lo;
-        }
+        // tile -> query maps (tile k belongs to the largest q with s[q] <= k)
+        if (maps & kMapScan) fill_tile_map(ws.tmap, s_ts, cnt, base);
+        if (maps & kMapFilter) fill_tile_map(ws.fmap, s_fs, cnt, base);
         __syncthreads();  // s_ts / s_fs are rewritten by the next chunk
         run_s = min(run_s + tot_s, cap_s + 1);
         run_f = min(run_f + tot_f, cap_f + 1);
     }
     const int used_s = n_q + min(cap_s, run_s), used_f = n_q + min(cap_f, run_f);
-    for (int k = used_s + t; k < grid_tiles; k += kPrepNT) ws.tmap[k] = -1;
-    for (int k = used_f + t; k < grid_ftiles; k += kPrepNT) ws.fmap[k] = -1;
+    if (maps & kMapScan)
+        for (int k = used_s + t; k < grid_tiles; k += kPrepNT) ws.tmap[k] = -1;
+    if (maps & kMapFilter)
+        for (int k = used_f + t; k < grid_ftiles; k += kPrepNT) ws.fmap[k] = -1;
 }
 
 // ----------------------------------------------------------------------------------------
@@ -493,10 +505,23 @@ constexpr int kPfHist = 1, kPfCompact = 2;
 constexpr int kPfBuf = 256;    // positions of one query a workgroup gathers in LDS before writing
 
 
+// Work items (position chunk x, query group y) are numbered chunk-major and split into kXcds
+// contiguous slices, one per XCD: workgroups are handed to the XCDs in turn (workgroup b to
+// XCD b mod kXcds), so workgroup b takes item (b mod kXcds) * per_xcd + b / kXcds.  The
+// workgroups resident on one XCD then read the same few key chunks (512 KB each), which stay
+// in that XCD's 4 MB L2 across all query groups instead of being fetched again for every
+// group from the last-level cache.  (Only the speed depends on the hand-out order.)
+constexpr int kXcds = 8;
+
+__host__ __device__ __forceinline__ int pf_items_per_xcd(int n_px, int n_qg) {
+    return (n_px * n_qg + kXcds - 1) / kXcds;
+}
+
 template <bool POOL, int MODE>
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, int top_k, IndexWs ws) {
+    const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, int top_k, int n_px, int n_qg,
+    IndexWs ws) {
     constexpr bool kCompact = MODE == kPfCompact;
     __shared__ uint32_t sh_hist[kCompact ? 1 : kPfQ][kHistBins / 2];
     __shared__ uint64_t sh_buf[kCompact ? kPfQ : 1][kCompact ? kPfBuf : 1];  // selected entries per query
@@ -508,8 +533,10 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
     const int lane = __lane_id();
     const int wid = t / kWave;
     const int g = lane >> 4, r = lane & 15;
-    const int q0 = blockIdx.y * kPfQ;
-    const int p_wg = blockIdx.x * kPfPos;
+    const int item = (int)(blockIdx.x % kXcds) * pf_items_per_xcd(n_px, n_qg) + (int)(blockIdx.x / kXcds);
+    if (item >= n_px * n_qg) return;  // uniform: the grid is rounded up to a multiple of kXcds
+    const int q0 = (item % n_qg) * kPfQ;
+    const int p_wg = (item / n_qg) * kPfPos;
     const int64_t row0 = kv_row0[0];
     const int64_t row_room = (row0 >= 0 && row0 <= cache_rows) ? cache_rows - row0 : 0;
     if (t < kPfQ) {
@@ -1187,19 +1214,25 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
                              int64_t cache_rows, int n_heads, int grid_tiles, int grid_ftiles, int top_k,
                              int pool_blocks, int prefill, const IndexWs& ws, int32_t* idx_out, int32_t* pool_out,
                              int phase, hipStream_t stream) {
+    // short decode contexts: the selection workgroups read the keys themselves (no filter pass)
+    const int scan_keys = !prefill && max_len <= kSelScanMax ? 1 : 0;
+    const bool filter = (!prefill || pool_blocks > 0) && !scan_keys;  // a prefill chunk's position lists
+                                                                      // are written by its scan
     if (phase & 1) {
+        const int maps = (prefill ? 0 : kMapScan) | (filter ? kMapFilter : 0);
         hipLaunchKernelGGL(k_idx_prep, dim3(1), dim3(kPrepNT), 0, stream, kv_row0, kv_len, n_q, max_len, cache_rows,
-                           grid_tiles, grid_ftiles, ws);
+                           grid_tiles, grid_ftiles, maps, ws);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (phase & 2) {
         if (prefill && max_len > 0) {  // (no visible position anywhere: nothing to score)
-            const dim3 grid((unsigned)((max_len + kPfPos - 1) / kPfPos), (unsigned)((n_q + kPfQ - 1) / kPfQ));
+            const int n_px = (max_len + kPfPos - 1) / kPfPos, n_qg = (n_q + kPfQ - 1) / kPfQ;
+            const dim3 grid((unsigned)(kXcds * pf_items_per_xcd(n_px, n_qg)));
             const uint16_t* kb = static_cast<const uint16_t*>(k_idx);
             auto k_hist = pool_blocks > 0 ? k_idx_score_prefill<true, kPfHist> : k_idx_score_prefill<false, kPfHist>;
             hipLaunchKernelGGL(k_hist, grid, dim3(kScoreNT), 0, stream, q_idx, w, kb, kv_row0, n_q, cache_rows, n_heads,
-                               top_k, ws);
+                               top_k, n_px, n_qg, ws);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             if (pool_blocks > 0) {
@@ -1213,7 +1246,7 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
             if (e != hipSuccess) return e;
             auto k_compact = k_idx_score_prefill<false, kPfCompact>;
             hipLaunchKernelGGL(k_compact, grid, dim3(kScoreNT), 0, stream, q_idx, w, kb, kv_row0, n_q, cache_rows,
-                               n_heads, top_k, ws);
+                               n_heads, top_k, n_px, n_qg, ws);
         } else if (!prefill) {
             const int wgs = min(grid_tiles, scan_workgroups());
             auto kern = mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true> : k_idx_score_full<8, true, false>)
@@ -1226,9 +1259,7 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
         if (e != hipSuccess) return e;
     }
     if (phase & 4) {
-        // short decode contexts: the selection workgroups read the keys themselves
-        const int scan_keys = !prefill && max_len <= kSelScanMax ? 1 : 0;
-        if ((!prefill || pool_blocks > 0) && !scan_keys) {  // a prefill chunk's position lists are written by its scan
+        if (filter) {
             hipLaunchKernelGGL(k_idx_filter_full, dim3(grid_ftiles), dim3(kScoreNT), 0, stream, kv_row0, kv_len, n_q,
                                max_len, cache_rows, grid_tiles, grid_ftiles, top_k, pool_blocks, prefill, ws);
             hipError_t e = hipGetLastError();
