@@ -588,12 +588,17 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
     }
     __syncthreads();
 
+    // positions below n_min are visible to every query of the workgroup (0 when the workgroup
+    // holds fewer than kPfQ queries: the missing ones must never count as visible)
+    int n_min = INT32_MAX;
+#pragma unroll
+    for (int k = 0; k < kPfQ; ++k) n_min = min(n_min, q0 + k < n_q ? sh_n[k] : 0);
+
     const int p_wave = p_wg + wid * (kPfPos / 4);
-    constexpr int TB = 4;  // 16-position tiles per load batch
-    for (int b = 0; b < kPfPos / 4; b += 16 * TB) {
-        const int base = p_wave + b;
-        if (base >= n_max) break;
-        uint4 kb[TB][2];
+    constexpr int TB = 4;          // 16-position tiles per load batch
+    constexpr int kBatch = 16 * TB;
+    // key rows of one batch (rows past the longest visible length read as zero)
+    auto load_batch = [&](uint4 (&kb)[TB][2], int base) {
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
             const int p = base + 16 * u + r;
@@ -606,6 +611,11 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
                 kb[u][1] = make_uint4(0, 0, 0, 0);
             }
         }
+    };
+    // scores of one batch; ALL: every position of the batch is visible to all 16 queries, so
+    // no per-query length test (and no branch around the histogram update) is needed
+    auto score_batch = [&](const uint4 (&kb)[TB][2], int base, auto all_tag) {
+        constexpr bool ALL = decltype(all_tag)::value;
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
             f32x4_t acc[4];
@@ -622,7 +632,7 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
                 float sc = 0.f;
 #pragma unroll
                 for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], relu(acc[h][i]), sc);
-                const bool ok = p < nq[i];
+                const bool ok = ALL || p < nq[i];
                 const uint32_t key = ok ? score_key(sc) : 0u;
                 if constexpr (kCompact) {
                     // at or above the query's threshold bucket: a sure position (above) or a
@@ -655,6 +665,19 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
                 }
             }
         }
+    };
+    auto score_any = [&](const uint4 (&kb)[TB][2], int base) {
+        if (base + kBatch <= n_min)
+            score_batch(kb, base, std::true_type{});
+        else
+            score_batch(kb, base, std::false_type{});
+    };
+    for (int b = 0; b < kPfPos / 4; b += kBatch) {
+        const int base = p_wave + b;
+        if (base >= n_max) break;
+        uint4 kb[TB][2];
+        load_batch(kb, base);
+        score_any(kb, base);
     }
     __syncthreads();
     if constexpr (kCompact) {
