@@ -38,7 +38,8 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 METRIC = "CSA2 decode tokens/s at 64K & 1M ctx; KV gather GB/s vs HBM peak"
 SCAN_KERNEL = "k_idx_score_full"
-SCAN_SOURCES = ["compressed_sparse_attention_07_amd/csrc/indexer.hip",
+SCAN_SOURCES = ["compressed_sparse_attention_07_amd/csrc/scan_full.hpp",
+                "compressed_sparse_attention_07_amd/csrc/scan_common.hpp",
                 "compressed_sparse_attention_07_amd/csrc/csa2_device.hpp"]
 
 

@@ -36,169 +36,10 @@
 
 #include "csa2_device.hpp"
 #include "reindex_select.hpp"
+#include "scan_common.hpp"
+#include "scan_full.hpp"
 
 namespace csa2 {
-
-constexpr int kScoreNT = 256;
-// Scan-kernel shape (compile-time; the defaults are the tuned ones):
-//   CSA2_SCAN_TILE  positions per tile of the tile map,
-//   CSA2_SCAN_U     64-position steps per load batch (each lane has 2U 16-byte loads in flight),
-//   CSA2_SCAN_NT    streaming (slc) key loads,
-//   CSA2_SCAN_WGS_PER_CU  resident workgroups of the persistent scan per compute unit.
-#ifndef CSA2_SCAN_TILE
-#define CSA2_SCAN_TILE 4096
-#endif
-#ifndef CSA2_SCAN_U
-#define CSA2_SCAN_U 8
-#endif
-#ifndef CSA2_SCAN_NT
-#define CSA2_SCAN_NT 0
-#endif
-#ifndef CSA2_SCAN_WGS_PER_CU
-#define CSA2_SCAN_WGS_PER_CU 4
-#endif
-//   CSA2_SCAN_U_LP  256-position steps per load batch in the lane-per-position layout,
-//   CSA2_SCAN_LP_BF16  bf16 keys also take the lane-per-position layout (MXFP4 keys always do).
-#ifndef CSA2_SCAN_U_LP
-#define CSA2_SCAN_U_LP 4
-#endif
-#ifndef CSA2_SCAN_LP_BF16
-#define CSA2_SCAN_LP_BF16 0
-#endif
-constexpr int kFullTile = CSA2_SCAN_TILE;       // positions per Full-scan workgroup
-constexpr int kReindexTile = 512;               // pool positions (64 blocks) per Reindex workgroup
-constexpr int kFilterTile = 8192;               // positions per filter workgroup (2 scan tiles)
-
-
-typedef __amdgpu_buffer_rsrc_t BufRsrc;
-constexpr int kBufWord3 = 0x00020000;  // gfx9 buffer resource word 3: raw 32-bit-format access
-
-// Raw buffer view of `bytes` bytes at p (offsets at or past `bytes` read as zero).  Both
-// arguments must be the same in every lane; they are passed through readfirstlane so the
-// descriptor is built in scalar registers (a descriptor the compiler thinks may vary across
-// lanes costs a waterfall loop per load).
-__device__ __forceinline__ BufRsrc tile_rsrc(const void* p, int bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-    void* base = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
-}
-
-__device__ __forceinline__ uint4 buf_ld16(BufRsrc rs, int voff, int soff) {
-#if CSA2_SCAN_NT
-    constexpr int aux = 2;  // slc: streaming
-#else
-    constexpr int aux = 0;
-#endif
-    typedef int i32x4 __attribute__((ext_vector_type(4)));
-    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, aux);
-    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-}
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    return __builtin_bit_cast(bf16x8_t, u32x4_t{v.x, v.y, v.z, v.w});
-}
-
-// Decode and Reindex scoring on MFMA: for 16 positions at a time,
-//   D[head][pos] = Q . K^T  on v_mfma_f32_16x16x32_bf16 (two k-steps cover the 64 channels),
-// with the query's heads on the M rows (zero-padded to 16) and the 16 positions on N.  Lane
-// (g, r) = (lane / 16, lane % 16) supplies head r of Q and position r of K^T with channels
-// 32s + 8g .. 32s + 8g + 7 (one 16-byte load per k-step), and its accumulator holds heads
-// 4g .. 4g + 3 at position r, so lanes 0..15 hold all four heads of their position and the
-// ReLU-weighted head sum needs no cross-lane reduction (heads 4..7 sit in lanes 16..31).
-struct QFrag {
-    bf16x8_t a[2];  // head r, channels 32s + 8g .. + 7
-    float w[4];     // weights of heads 4g .. 4g + 3 (0 past n_heads)
-};
-
-__device__ __forceinline__ void load_qfrag(QFrag& qf, const uint16_t* q, const float* w, int n_heads, int lane) {
-    const int g = lane >> 4, r = lane & 15;
-    const bool hv = r < n_heads;
-    const uint16_t* qp = q + (hv ? r : 0) * 64 + 8 * g;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-        qf.a[s2] = as_bf16x8(hv ? *reinterpret_cast<const uint4*>(qp + 32 * s2) : make_uint4(0, 0, 0, 0));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qf.w[i] = (4 * g + i < n_heads) ? w[4 * g + i] : 0.f;
-}
-
-// Lane-per-position layout (at most 4 indexer heads): 64 positions per wave step, lane l
-// holding position l.  Eight k-steps of 8 channels each cover the 64 channels; in k-step s,
-// lane (g, r) supplies channels 8s .. 8s + 7 of its own position as column r, K slots
-// 8g .. 8g + 7 of B, and A is block-diagonal: row 4g + h holds head h's channels 8s .. 8s + 7
-// in K slots 8g .. 8g + 7 and zeros elsewhere.  Then D[4g + h][r] sums only lane group g's
-// slots, i.e. head h times the position of lane 16g + r, and the accumulator of lane l ends
-// up with all four heads of ITS position: every lane carries a score (the M rows and K slots
-// spent on zeros are the price, the same MFMA count as the layout above).
-struct QFragLP {
-    bf16x8_t a[8];  // k-step s: head (r & 3)'s channels 8s .. 8s + 7 when r / 4 == g, else zeros
-    float w[4];     // weights of heads 0 .. 3 (0 past n_heads)
-};
-
-__device__ __forceinline__ void load_qfrag_lp(QFragLP& qf, const uint16_t* q, const float* w, int n_heads,
-                                              int lane) {
-    const int g = lane >> 4, r = lane & 15, h = r & 3;
-    const bool on = (r >> 2) == g && h < n_heads;
-    const uint16_t* qp = q + (on ? h : 0) * 64;
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2)
-        qf.a[s2] = as_bf16x8(on ? *reinterpret_cast<const uint4*>(qp + 8 * s2) : make_uint4(0, 0, 0, 0));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qf.w[i] = i < n_heads ? w[i] : 0.f;
-}
-
-__device__ __forceinline__ float relu(float x) {
-    return __builtin_elementwise_maximum(x, 0.f);  // one v_maximum3_f32 (fmaxf adds a canonicalize)
-}
-
-// Score of position r in lanes 0..15 (kb: the lane's two 16-byte slices of that position).
-template <int HI>
-__device__ __forceinline__ float mfma_score(const QFrag& qf, const uint4& k0, const uint4& k1) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.a[0], as_bf16x8(k0), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.a[1], as_bf16x8(k1), acc, 0, 0, 0);
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(qf.w[i], fmaxf(acc[i], 0.f), s);
-    if (HI > 4) s += __shfl_down(s, 16, kWave);  // heads 4..7 from lanes 16..31
-    return s;
-}
-
-// MXFP4 keys (E2M1 + one E8M0 scale per 32 channels): k-step s of the contraction covers
-// exactly scale block s, so lane (g, r)'s 8 channels of k-step s are the 4 code bytes
-// 16s + 4g .. 16s + 4g + 3 of position r.  The hardware conversion applies the power-of-two
-// scale exactly (its scale operand carries only an exponent): E2M1 x 2^(code - 127) -> bf16.
-__device__ __forceinline__ uint4 mx_frag(uint32_t dw, uint32_t code) {
-    const float sc = __uint_as_float(code << 23);  // 2^(code - 127); written codes are >= 1
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 0)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 1)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 2)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(dw, sc, 3)));
-}
-
-__device__ __forceinline__ uint32_t buf_ld4(BufRsrc rs, int voff, int soff) {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, 0);
-}
-
-__device__ __forceinline__ uint32_t buf_ld2(BufRsrc rs, int voff, int soff) {
-    return (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, 0);
-}
-
-// Largest key of each aligned group of 8 lanes within lanes 0..15, in lanes 4 and 12
-// (quad butterflies, then row_ror:4 brings the quad just below).
-__device__ __forceinline__ uint32_t max_over_8_lanes(uint32_t k) {
-    k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0xB1, 0xF, 0xF, true));
-    k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x4E, 0xF, 0xF, true));
-    k = max(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x124, 0xF, 0xF, true));
-    return k;
-}
-
 
 // ----------------------------------------------------------------------------------------
 // Full mode, kernel 0: per-query metadata.  Query i owns max(1, ceil(n_i / tile)) consecutive
@@ -286,196 +127,6 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
         for (int k = used_s + t; k < grid_tiles; k += kPrepNT) ws.tmap[k] = -1;
     if (maps & kMapFilter)
         for (int k = used_f + t; k < grid_ftiles; k += kPrepNT) ws.fmap[k] = -1;
-}
-
-// ----------------------------------------------------------------------------------------
-// Full mode, kernel 1: scores -> keys, block-max keys, first-digit histograms
-// ----------------------------------------------------------------------------------------
-// Persistent: the grid holds a few workgroups per CU and workgroup g streams the contiguous
-// tile range [g * T / G, (g + 1) * T / G) of the tile map, so the per-tile set-up (tile map,
-// query slice) is paid once per query rather than once per tile, and the first-digit
-// histograms go to the workspace only when the query changes.
-// MX: keys are MXFP4 (k_idx = code bytes [rows, 32], k_sc = E8M0 bytes [rows, 2]) instead of
-// bf16 (k_idx = [rows, 64] bf16, k_sc unused).
-// LP: the lane-per-position layout (QFragLP; at most 4 heads): a wave step covers 64
-// positions with one score per lane, so the per-position epilogue (ReLU-weighted head sum,
-// key, stores, histogram atomics, block maximum) costs a quarter of the instructions of the
-// 16-position layout; the lane reads its own row (16-byte loads, 32 B per MXFP4 row).
-template <int HI, bool MX, bool LP>
-__global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx,
-    const uint8_t* __restrict__ k_sc, const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len,
-    int n_q, int32_t max_len, int64_t cache_rows, int n_heads, int grid_tiles, int pool_blocks, IndexWs ws) {
-    __shared__ uint32_t sh_hist[kHistBins];
-    __shared__ uint32_t sh_bhist[kHistBins];
-
-    const int t = threadIdx.x;
-    const int lane = __lane_id();
-    const int wid = t / kWave;
-    const int g = lane >> 4, r = lane & 15;
-    const bool want_pool = pool_blocks > 0;
-    const int tb = (int)((int64_t)blockIdx.x * grid_tiles / gridDim.x);
-    const int te = (int)((int64_t)(blockIdx.x + 1) * grid_tiles / gridDim.x);
-
-    for (int b = t; b < kHistBins; b += kScoreNT) {
-        sh_hist[b] = 0u;
-        sh_bhist[b] = 0u;
-    }
-    static_assert(!LP || HI == 4, "the lane-per-position layout holds 4 heads");
-    int cur = -1;  // query whose counts the LDS histograms hold
-    QMeta qm{};
-    int64_t row0 = 0;
-    std::conditional_t<LP, QFragLP, QFrag> qf;
-    // add the LDS histograms of query `cur` to the workspace and clear them (after a barrier)
-    auto flush = [&]() {
-        uint32_t* gh = ws.hist + (int64_t)cur * 2 * kHistBins;
-        for (int b = t; b < kHistBins; b += kScoreNT) {
-            const uint32_t h = sh_hist[b];
-            if (h) {
-                atomicAdd(&gh[b], h);
-                sh_hist[b] = 0u;
-            }
-            if (want_pool) {
-                const uint32_t hb = sh_bhist[b];
-                if (hb) {
-                    atomicAdd(&gh[kHistBins + b], hb);
-                    sh_bhist[b] = 0u;
-                }
-            }
-        }
-    };
-
-    // one step = 64 consecutive positions of the workgroup (16 per wave); U steps per batch
-    constexpr int U = CSA2_SCAN_U;
-    for (int tile = tb; tile < te; ++tile) {
-        const int i = ws.tmap[tile];
-        if (i < 0) break;  // unused tiles sit at the end of the map
-        if (i != cur) {
-            __syncthreads();  // every wave's counts of `cur` are in LDS (and the clearing above)
-            if (cur >= 0) {
-                flush();
-                __syncthreads();
-            }
-            cur = i;
-            qm = ws.qmeta[i];
-            row0 = kv_row0[i];
-            if constexpr (LP)
-                load_qfrag_lp(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
-            else
-                load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
-        }
-        const int n = qm.n;
-        const int64_t key_base = (int64_t)qm.start * kFullTile;
-        const int p_tile = (tile - qm.start) * kFullTile;
-        if (p_tile >= n) continue;
-        // buffer view of this tile's rows: one 32-bit lane offset for every load (the step goes
-        // in the scalar offset) and rows past the sequence read as zeros
-        const int rows_here = min(n - p_tile, kFullTile);
-        constexpr int kRowB = MX ? 32 : 128;  // key bytes per position (codes only for MXFP4)
-        const BufRsrc rs = tile_rsrc(static_cast<const uint8_t*>(k_idx) + (row0 + p_tile) * kRowB, rows_here * kRowB);
-        const BufRsrc rss = tile_rsrc(MX ? k_sc + (row0 + p_tile) * 2 : nullptr, MX ? rows_here * 2 : 0);
-        if constexpr (LP) {
-            // one step = 256 consecutive positions of the workgroup (64 per wave, one per lane)
-            constexpr int UL = CSA2_SCAN_U_LP;
-            constexpr int kLd = kRowB / 16;  // 16-byte loads per row
-            const int voff = (64 * wid + lane) * kRowB;
-            const int voff_s = (64 * wid + lane) * 2;
-            for (int b = 0; b < kFullTile; b += 256 * UL) {
-                const int pb = p_tile + b;
-                if (pb >= n) break;
-                uint4 kr[UL][kLd];
-                uint32_t ks[UL];
-#pragma unroll
-                for (int u = 0; u < UL; ++u) {
-#pragma unroll
-                    for (int j = 0; j < kLd; ++j) kr[u][j] = buf_ld16(rs, voff + 16 * j, (b + 256 * u) * kRowB);
-                    if constexpr (MX) ks[u] = buf_ld2(rss, voff_s, (b + 256 * u) * 2);
-                }
-                __builtin_amdgcn_sched_barrier(0);  // every load of the batch goes out first
-#pragma unroll
-                for (int u = 0; u < UL; ++u) {
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s2 = 0; s2 < 8; ++s2) {
-                        uint4 kf;
-                        if constexpr (MX) {  // k-step s2 lies in scale block s2 / 4
-                            const uint4& c = kr[u][s2 >> 2];
-                            const uint32_t dw = (s2 & 3) == 0 ? c.x : (s2 & 3) == 1 ? c.y : (s2 & 3) == 2 ? c.z : c.w;
-                            kf = mx_frag(dw, s2 < 4 ? (ks[u] & 0xffu) : (ks[u] >> 8));
-                        } else {
-                            kf = kr[u][s2];
-                        }
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.a[s2], as_bf16x8(kf), acc, 0, 0, 0);
-                    }
-                    float sc = 0.f;
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) sc = fmaf(qf.w[h], relu(acc[h]), sc);
-                    const int p = pb + 256 * u + 64 * wid + lane;
-                    const bool mine = p < n;
-                    const uint32_t key = mine ? score_key(sc) : 0u;
-                    if (mine) {
-                        ws.keys[key_base + p] = key;
-                        atomicAdd(&sh_hist[key >> 21], 1u);
-                    }
-                    if (want_pool) {
-                        const uint32_t bk = max_over_8_lanes(key);  // lanes 8k + 4: block of lanes 8k .. 8k + 7
-                        if ((lane & 7) == 4 && p - 4 < n) {
-                            ws.bkeys[key_base / 8 + ((p - 4) >> 3)] = bk;
-                            atomicAdd(&sh_bhist[bk >> 21], 1u);
-                        }
-                    }
-                }
-            }
-        } else {
-            const int voff = (16 * wid + r) * kRowB + (MX ? 4 : 16) * g;
-            const int voff_s = (16 * wid + r) * 2;
-            for (int b = 0; b < kFullTile; b += 64 * U) {
-                const int pb = p_tile + b;
-                if (pb >= n) break;
-                uint4 kb[U][2];
-                uint32_t kc[U][2], ks[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if constexpr (MX) {
-                        kc[u][0] = buf_ld4(rs, voff, (b + 64 * u) * kRowB);
-                        kc[u][1] = buf_ld4(rs, voff + 16, (b + 64 * u) * kRowB);
-                        ks[u] = buf_ld2(rss, voff_s, (b + 64 * u) * 2);
-                    } else {
-                        kb[u][0] = buf_ld16(rs, voff, (b + 64 * u) * kRowB);
-                        kb[u][1] = buf_ld16(rs, voff + 64, (b + 64 * u) * kRowB);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int p0 = pb + 64 * u + 16 * wid;  // first of this wave's 16 positions
-                    const int p = p0 + r;
-                    if constexpr (MX) {
-                        kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
-                        kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
-                    }
-                    const float sc = mfma_score<HI>(qf, kb[u][0], kb[u][1]);
-                    const bool mine = g == 0 && p < n;
-                    const uint32_t key = mine ? score_key(sc) : 0u;
-                    if (mine) {
-                        ws.keys[key_base + p] = key;
-                        atomicAdd(&sh_hist[key >> 21], 1u);
-                    }
-                    if (want_pool) {
-                        const uint32_t bk = max_over_8_lanes(key);
-                        const int pblk = p0 + (r & 8);  // the 8-position pool block of lanes 4 / 12
-                        if (g == 0 && (r & 7) == 4 && pblk < n) {
-                            ws.bkeys[key_base / 8 + (pblk >> 3)] = bk;
-                            atomicAdd(&sh_bhist[bk >> 21], 1u);
-                        }
-                    }
-                }
-            }
-        }
-    }
-    if (cur >= 0) {
-        __syncthreads();
-        flush();
-    }
 }
 
 // ----------------------------------------------------------------------------------------

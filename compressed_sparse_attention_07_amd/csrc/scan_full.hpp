@@ -1,0 +1,202 @@
+// Full-mode decode scan kernel (k_idx_score_full): every visible position's indexer score,
+// its order-preserving key, the 8-position block-max key and both first-digit histograms.
+//
+// Article "DeepSeek-V4.1-Flash: Pushing KV Cache Compression to 890 Bytes per Token", section
+// IX: the Full layer scores all causally visible positions and ranks 8-position blocks by
+// their maximum score.
+#pragma once
+
+#include "scan_common.hpp"
+
+namespace csa2 {
+// ----------------------------------------------------------------------------------------
+// Full mode, kernel 1: scores -> keys, block-max keys, first-digit histograms
+// ----------------------------------------------------------------------------------------
+// Persistent: the grid holds a few workgroups per CU and workgroup g streams the contiguous
+// tile range [g * T / G, (g + 1) * T / G) of the tile map, so the per-tile set-up (tile map,
+// query slice) is paid once per query rather than once per tile, and the first-digit
+// histograms go to the workspace only when the query changes.
+// MX: keys are MXFP4 (k_idx = code bytes [rows, 32], k_sc = E8M0 bytes [rows, 2]) instead of
+// bf16 (k_idx = [rows, 64] bf16, k_sc unused).
+// LP: the lane-per-position layout (QFragLP; at most 4 heads): a wave step covers 64
+// positions with one score per lane, so the per-position epilogue (ReLU-weighted head sum,
+// key, stores, histogram atomics, block maximum) costs a quarter of the instructions of the
+// 16-position layout; the lane reads its own row (16-byte loads, 32 B per MXFP4 row).
+template <int HI, bool MX, bool LP>
+__global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx,
+    const uint8_t* __restrict__ k_sc, const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len,
+    int n_q, int32_t max_len, int64_t cache_rows, int n_heads, int grid_tiles, int pool_blocks, IndexWs ws) {
+    __shared__ uint32_t sh_hist[kHistBins];
+    __shared__ uint32_t sh_bhist[kHistBins];
+
+    const int t = threadIdx.x;
+    const int lane = __lane_id();
+    const int wid = t / kWave;
+    const int g = lane >> 4, r = lane & 15;
+    const bool want_pool = pool_blocks > 0;
+    const int tb = (int)((int64_t)blockIdx.x * grid_tiles / gridDim.x);
+    const int te = (int)((int64_t)(blockIdx.x + 1) * grid_tiles / gridDim.x);
+
+    for (int b = t; b < kHistBins; b += kScoreNT) {
+        sh_hist[b] = 0u;
+        sh_bhist[b] = 0u;
+    }
+    static_assert(!LP || HI == 4, "the lane-per-position layout holds 4 heads");
+    int cur = -1;  // query whose counts the LDS histograms hold
+    QMeta qm{};
+    int64_t row0 = 0;
+    std::conditional_t<LP, QFragLP, QFrag> qf;
+    // add the LDS histograms of query `cur` to the workspace and clear them (after a barrier)
+    auto flush = [&]() {
+        uint32_t* gh = ws.hist + (int64_t)cur * 2 * kHistBins;
+        for (int b = t; b < kHistBins; b += kScoreNT) {
+            const uint32_t h = sh_hist[b];
+            if (h) {
+                atomicAdd(&gh[b], h);
+                sh_hist[b] = 0u;
+            }
+            if (want_pool) {
+                const uint32_t hb = sh_bhist[b];
+                if (hb) {
+                    atomicAdd(&gh[kHistBins + b], hb);
+                    sh_bhist[b] = 0u;
+                }
+            }
+        }
+    };
+
+    // one step = 64 consecutive positions of the workgroup (16 per wave); U steps per batch
+    constexpr int U = CSA2_SCAN_U;
+    for (int tile = tb; tile < te; ++tile) {
+        const int i = ws.tmap[tile];
+        if (i < 0) break;  // unused tiles sit at the end of the map
+        if (i != cur) {
+            __syncthreads();  // every wave's counts of `cur` are in LDS (and the clearing above)
+            if (cur >= 0) {
+                flush();
+                __syncthreads();
+            }
+            cur = i;
+            qm = ws.qmeta[i];
+            row0 = kv_row0[i];
+            if constexpr (LP)
+                load_qfrag_lp(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
+            else
+                load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
+        }
+        const int n = qm.n;
+        const int64_t key_base = (int64_t)qm.start * kFullTile;
+        const int p_tile = (tile - qm.start) * kFullTile;
+        if (p_tile >= n) continue;
+        // buffer view of this tile's rows: one 32-bit lane offset for every load (the step goes
+        // in the scalar offset) and rows past the sequence read as zeros
+        const int rows_here = min(n - p_tile, kFullTile);
+        constexpr int kRowB = MX ? 32 : 128;  // key bytes per position (codes only for MXFP4)
+        const BufRsrc rs = tile_rsrc(static_cast<const uint8_t*>(k_idx) + (row0 + p_tile) * kRowB, rows_here * kRowB);
+        const BufRsrc rss = tile_rsrc(MX ? k_sc + (row0 + p_tile) * 2 : nullptr, MX ? rows_here * 2 : 0);
+        if constexpr (LP) {
+            // one step = 256 consecutive positions of the workgroup (64 per wave, one per lane)
+            constexpr int UL = CSA2_SCAN_U_LP;
+            constexpr int kLd = kRowB / 16;  // 16-byte loads per row
+            const int voff = (64 * wid + lane) * kRowB;
+            const int voff_s = (64 * wid + lane) * 2;
+            for (int b = 0; b < kFullTile; b += 256 * UL) {
+                const int pb = p_tile + b;
+                if (pb >= n) break;
+                uint4 kr[UL][kLd];
+                uint32_t ks[UL];
+#pragma unroll
+                for (int u = 0; u < UL; ++u) {
+#pragma unroll
+                    for (int j = 0; j < kLd; ++j) kr[u][j] = buf_ld16(rs, voff + 16 * j, (b + 256 * u) * kRowB);
+                    if constexpr (MX) ks[u] = buf_ld2(rss, voff_s, (b + 256 * u) * 2);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // every load of the batch goes out first
+#pragma unroll
+                for (int u = 0; u < UL; ++u) {
+                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s2 = 0; s2 < 8; ++s2) {
+                        uint4 kf;
+                        if constexpr (MX) {  // k-step s2 lies in scale block s2 / 4
+                            const uint4& c = kr[u][s2 >> 2];
+                            const uint32_t dw = (s2 & 3) == 0 ? c.x : (s2 & 3) == 1 ? c.y : (s2 & 3) == 2 ? c.z : c.w;
+                            kf = mx_frag(dw, s2 < 4 ? (ks[u] & 0xffu) : (ks[u] >> 8));
+                        } else {
+                            kf = kr[u][s2];
+                        }
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.a[s2], as_bf16x8(kf), acc, 0, 0, 0);
+                    }
+                    float sc = 0.f;
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) sc = fmaf(qf.w[h], relu(acc[h]), sc);
+                    const int p = pb + 256 * u + 64 * wid + lane;
+                    const bool mine = p < n;
+                    const uint32_t key = mine ? score_key(sc) : 0u;
+                    if (mine) {
+                        ws.keys[key_base + p] = key;
+                        atomicAdd(&sh_hist[key >> 21], 1u);
+                    }
+                    if (want_pool) {
+                        const uint32_t bk = max_over_8_lanes(key);  // lanes 8k + 4: block of lanes 8k .. 8k + 7
+                        if ((lane & 7) == 4 && p - 4 < n) {
+                            ws.bkeys[key_base / 8 + ((p - 4) >> 3)] = bk;
+                            atomicAdd(&sh_bhist[bk >> 21], 1u);
+                        }
+                    }
+                }
+            }
+        } else {
+            const int voff = (16 * wid + r) * kRowB + (MX ? 4 : 16) * g;
+            const int voff_s = (16 * wid + r) * 2;
+            for (int b = 0; b < kFullTile; b += 64 * U) {
+                const int pb = p_tile + b;
+                if (pb >= n) break;
+                uint4 kb[U][2];
+                uint32_t kc[U][2], ks[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if constexpr (MX) {
+                        kc[u][0] = buf_ld4(rs, voff, (b + 64 * u) * kRowB);
+                        kc[u][1] = buf_ld4(rs, voff + 16, (b + 64 * u) * kRowB);
+                        ks[u] = buf_ld2(rss, voff_s, (b + 64 * u) * 2);
+                    } else {
+                        kb[u][0] = buf_ld16(rs, voff, (b + 64 * u) * kRowB);
+                        kb[u][1] = buf_ld16(rs, voff + 64, (b + 64 * u) * kRowB);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int p0 = pb + 64 * u + 16 * wid;  // first of this wave's 16 positions
+                    const int p = p0 + r;
+                    if constexpr (MX) {
+                        kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
+                        kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
+                    }
+                    const float sc = mfma_score<HI>(qf, kb[u][0], kb[u][1]);
+                    const bool mine = g == 0 && p < n;
+                    const uint32_t key = mine ? score_key(sc) : 0u;
+                    if (mine) {
+                        ws.keys[key_base + p] = key;
+                        atomicAdd(&sh_hist[key >> 21], 1u);
+                    }
+                    if (want_pool) {
+                        const uint32_t bk = max_over_8_lanes(key);
+                        const int pblk = p0 + (r & 8);  // the 8-position pool block of lanes 4 / 12
+                        if (g == 0 && (r & 7) == 4 && pblk < n) {
+                            ws.bkeys[key_base / 8 + (pblk >> 3)] = bk;
+                            atomicAdd(&sh_bhist[bk >> 21], 1u);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    if (cur >= 0) {
+        __syncthreads();
+        flush();
+    }
+}
+
+}  // namespace csa2
