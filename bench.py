@@ -40,7 +40,8 @@ METRIC = "CSA2 decode tokens/s at 64K & 1M ctx; KV gather GB/s vs HBM peak"
 SCAN_KERNEL = "k_idx_score_full"
 SCAN_SOURCES = ["compressed_sparse_attention_07_amd/csrc/scan_full.hpp",
                 "compressed_sparse_attention_07_amd/csrc/scan_common.hpp",
-                "compressed_sparse_attention_07_amd/csrc/csa2_device.hpp"]
+                "compressed_sparse_attention_07_amd/csrc/csa2_device.hpp",
+                "compressed_sparse_attention_07_amd/build.py"]  # (compiler flags change the code too)
 
 
 def source_sha(paths) -> str:

@@ -284,7 +284,10 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
 #pragma unroll
                 for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], relu(acc[h][i]), sc);
                 const bool ok = ALL || p < nq[i];
-                const uint32_t key = ok ? score_key(sc) : 0u;
+                // the sum starts from +0, so it is never -0 and score_key's normalisation is not
+                // needed: flip every bit of a negative score, only the sign bit of the others
+                const uint32_t sb = __float_as_uint(sc);
+                const uint32_t key = ok ? sb ^ ((uint32_t)((int32_t)sb >> 31) | 0x80000000u) : 0u;
                 if constexpr (kCompact) {
                     // at or above the query's threshold bucket: a sure position (above) or a
                     // candidate (in it), gathered in LDS (candidate keys are never 0; a sure
@@ -306,8 +309,11 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
                         }
                     }
                 } else if (ok) {
-                    const uint32_t bin = key >> 21;
-                    atomicAdd(&sh_hist[4 * g + i][bin >> 1], 1u << (16 * (bin & 1)));
+                    // first digit = key >> 21; two 16-bit counters per word: word digit >> 1,
+                    // half digit & 1 (an increment of 1 or 1 << 16)
+                    const uint32_t word = (key >> 22) & 0x3ffu;
+                    const uint32_t half = (key >> 21) & 1u;
+                    atomicAdd(&sh_hist[4 * g + i][word], 1u + half * 0xffffu);
                 }
                 if constexpr (POOL && !kCompact) {
                     const uint32_t bk = max_over_8_lanes(key);      // lanes 4 / 12 of the row
