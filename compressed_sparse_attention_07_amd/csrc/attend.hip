@@ -528,10 +528,12 @@ __global__ __launch_bounds__(kAttNT) void k_reindex_attend(const int32_t* __rest
     __shared__ uint32_t s_hist[2][kHistBins];
     __shared__ int32_t s_idx[kMaxSelect];
     __shared__ int s_scan[kAttNT / kWave];
+    __shared__ uint32_t s_or[2];
     __shared__ Thresh sh_th;
     __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
     const int i = blockIdx.x;
-    reindex_select_query<kAttNT, EPT>(i, pool, pool_blocks, a.top_k, ws, idx_out, s_idx, s_hist, s_scan, &sh_th);
+    reindex_select_query<kAttNT, EPT>(i, pool, pool_blocks, a.top_k, ws, idx_out, s_idx, s_hist, s_scan, s_or,
+                                      &sh_th);
     __syncthreads();  // the selection is in s_idx
     attend_query<true, kWin, kW8>(i, a, s_idx, AttendLds{s_area, s_m, s_l});
 }

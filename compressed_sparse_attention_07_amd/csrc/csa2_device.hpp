@@ -199,6 +199,7 @@ struct RadixShared {
     uint32_t hist[kHistBins];
     int scan[16];
     int digit, above, inb;
+    uint32_t low_or;  // OR of the bucket's key bits below the current digit
 };
 
 // Key-only threshold among m composites in LDS whose keys all lie in first-digit bucket d1:
@@ -219,16 +220,27 @@ __device__ KeyThr lds_key_threshold(const uint64_t* c, int m, int need, int d1, 
     uint32_t prefix = (uint32_t)d1;
     int pbits = kHistBits;
     int matching = m;
-    while (pbits < 32 && matching > need) {
+    bool low_zero = false;  // every key of the bucket has zeros below the digit just taken
+    while (pbits < 32 && matching > need && !low_zero) {
         const int w = (32 - pbits) >= kHistBits ? kHistBits : (32 - pbits);
         const int shift = 32 - pbits - w;
         for (int b = t; b < kHistBins; b += NT) R.hist[b] = 0u;
+        if (t == 0) R.low_or = 0u;
         __syncthreads();
+        uint32_t low = 0u;
         for (int e = t; e < m; e += NT) {
             const uint32_t key = (uint32_t)(c[e] >> 32);
-            if ((key >> (32 - pbits)) == prefix) atomicAdd(&R.hist[(key >> shift) & ((1u << w) - 1)], 1u);
+            if ((key >> (32 - pbits)) == prefix) {
+                atomicAdd(&R.hist[(key >> shift) & ((1u << w) - 1)], 1u);
+                low |= key & ((1u << shift) - 1u);
+            }
         }
+        if (low != 0u) atomicOr(&R.low_or, low);
         __syncthreads();
+        // when no key of the bucket has a bit below this digit, every key of the sub-bucket the
+        // digit selects is the same key: a further pass could not split it (the ties at that
+        // key are ordered by position, as after a pass over all 32 bits)
+        low_zero = R.low_or == 0u;
         const int nb = 1 << w;
         uint32_t h[BPT];
         int local = 0;
@@ -258,8 +270,8 @@ __device__ KeyThr lds_key_threshold(const uint64_t* c, int m, int need, int d1, 
         __syncthreads();
     }
     KeyThr r;
-    if (matching > need) {  // all 32 key bits fixed: ties at the threshold key
-        r.t = prefix;
+    if (matching > need) {  // ties at the threshold key (all 32 bits fixed, or the bits left are 0)
+        r.t = prefix << (32 - pbits);
         r.take_eq = need;
         r.n_tie = matching;
     } else {

@@ -858,9 +858,10 @@ __global__ __launch_bounds__(kSelNT) void k_idx_reindex_select(const int32_t* __
                                                                int32_t* __restrict__ idx_out) {
     __shared__ uint32_t s_hist[2][kHistBins];
     __shared__ int s_scan[kSelNT / kWave];
+    __shared__ uint32_t s_or[2];
     __shared__ Thresh sh_th;
     reindex_select_query<kSelNT, EPT>(blockIdx.x, pool, pool_blocks, top_k, ws, idx_out, nullptr, s_hist, s_scan,
-                                      &sh_th);
+                                      s_or, &sh_th);
 }
 
 // ----------------------------------------------------------------------------------------

@@ -20,7 +20,7 @@ template <int NT, int EPT>
 __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __restrict__ pool, int pool_blocks,
                                                      int top_k, const IndexWs& ws, int32_t* __restrict__ idx_out,
                                                      int32_t* lds_idx, uint32_t (*s_hist)[kHistBins], int* s_scan,
-                                                     Thresh* sh_th_p) {
+                                                     uint32_t* s_or, Thresh* sh_th_p) {
     Thresh& sh_th = *sh_th_p;
     const int t = threadIdx.x;
     const int n_elem = pool_blocks * 8;
@@ -45,6 +45,7 @@ __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __res
         pb[j >> 3] = blk;
     }
     for (int b = t; b < 2 * kHistBins; b += NT) (&s_hist[0][0])[b] = 0u;
+    if (t < 2) s_or[t] = 0u;
     // first digit: histogram accumulated by the score kernel (its barriers also cover the
     // clearing above)
     find_threshold<NT>(gh, top_k, s_scan, &sh_th);
@@ -60,14 +61,22 @@ __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __res
             // at most two more radix passes (11 and 10 bits) over the bucket's keys, straight
             // from the registers (a pass costs EPT compares per thread; no compaction)
             int hb = 0;
-            while (pbits < 32 && inb > need) {
+            bool low_zero = false;  // every key of the bucket has zeros below the digit just taken
+            while (pbits < 32 && inb > need && !low_zero) {
                 const int w = min(kHistBits, 32 - pbits);
                 const int shift = 32 - pbits - w;
+                uint32_t low = 0u;
 #pragma unroll
                 for (int j = 0; j < EPT; ++j)
-                    if (kv[j] != 0u && (kv[j] >> (32 - pbits)) == prefix)
+                    if (kv[j] != 0u && (kv[j] >> (32 - pbits)) == prefix) {
                         atomicAdd(&s_hist[hb][(kv[j] >> shift) & ((1u << w) - 1u)], 1u);
+                        low |= kv[j] & ((1u << shift) - 1u);
+                    }
+                if (low != 0u) atomicOr(&s_or[hb], low);
                 __syncthreads();
+                // no key of the bucket has a bit below this digit: every key of the sub-bucket
+                // the digit selects equals T, so a further pass could not split it
+                low_zero = s_or[hb] == 0u;
                 find_threshold<NT>(s_hist[hb], need, s_scan, &sh_th);
                 th = sh_th;  // inb > need, so a digit is found
                 prefix = (prefix << w) | (uint32_t)th.digit;
