@@ -238,6 +238,23 @@ def test_index_prefill_mfma_per_query_pools(pool_blocks):
         assert np.array_equal(idx2[t], case.oracle_reindex(t, pool_m[t], 512, q=q2[t], w=w2[t])), t
 
 
+def test_index_prefill_fractional_and_negative_weights():
+    # the prefill scoring passes build the key from the score without the -0 step (a sum started
+    # from +0 is never -0): scores of both signs with bits below the integer part, exact in fp32
+    C_, T = 9000, 48
+    case = SharedIndexCase(W_T + 83, C_ + T, C_ + 1 + np.arange(T), n_heads=4)
+    m = np.random.default_rng(83).integers(-256, 257, size=case.w.shape)
+    m[m == 0] = 3
+    case.w = (m / 64.0).astype(np.float32)
+    case.w_dev = torch.from_numpy(case.w).to(DEV)
+    idx_m, pool_m, _ = case.run_full(512, 300, shared_kv=1)
+    idx_m, pool_m = idx_m.cpu().numpy(), pool_m.cpu().numpy()
+    for t in range(T):
+        ri, rp = case.oracle_full(t, 512, 300)
+        assert np.array_equal(idx_m[t], ri), t
+        assert np.array_equal(pool_m[t], rp), t
+
+
 def test_index_prefill_all_equal_scores_takes_lowest_positions():
     # every score is 0: every visible position of every token is in the threshold bucket, so
     # the compacting pass overflows its per-token LDS buffer and writes the rest directly
@@ -274,6 +291,35 @@ def test_index_reindex_bit_exact_and_invariant():
     for i in range(len(lengths)):
         ref = case.oracle_reindex(i, pool_np[i], 512, q=q2[i], w=w2[i])
         assert np.array_equal(idx2[i], ref), i
+
+
+@pytest.mark.parametrize("negative", [False, True])
+def test_index_fractional_weights_full_and_reindex(negative):
+    # weights m / 64 (|m| <= 256): every score is still exact in fp32 and fp64 (at most 20
+    # significant bits), but keys now carry bits below the integer part, so the radix passes
+    # cannot stop early on all-zero low bits; negative weights give negative scores (keys with
+    # every bit flipped)
+    lengths = [70000, 20000, 4096, 9]
+    case = IndexCase(W_T + 80 + int(negative), lengths, n_heads=4)
+    r = np.random.default_rng(80 + int(negative))
+    lo = -256 if negative else 1
+    m = r.integers(lo, 257, size=case.w.shape)
+    m[m == 0] = 1
+    case.w = (m / 64.0).astype(np.float32)
+    case.w_dev = torch.from_numpy(case.w).to(DEV)
+    idx_f, pool, _ = case.run_full(512, 2048)
+    idx_f, pool_np = idx_f.cpu().numpy(), pool.cpu().numpy()
+    for i in range(len(lengths)):
+        ri, rp = case.oracle_full(i, 512, 2048)
+        assert np.array_equal(idx_f[i], ri), i
+        assert np.array_equal(pool_np[i], rp), i
+    q2 = synth.int_bf16(W_T + 82, synth.T_IDX_Q, (len(lengths), 4, 64), seq=5)
+    w2 = (r.integers(lo, 257, size=(len(lengths), 4)) / 64.0).astype(np.float32)
+    w2[w2 == 0] = 1.0
+    idx2, _ = case.run_reindex(pool, 512, q_dev=bf16_tensor(q2), w_dev=torch.from_numpy(w2).to(DEV))
+    idx2 = idx2.cpu().numpy()
+    for i in range(len(lengths)):
+        assert np.array_equal(idx2[i], case.oracle_reindex(i, pool_np[i], 512, q=q2[i], w=w2[i])), i
 
 
 def test_index_reindex_pool_with_padding_and_out_of_range_blocks():
