@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
 // of Q_h and position r of K^T with channels 32s + 8g .. 32s + 8g + 7, so its key loads are
 // the scan's 16-byte slices.  The accumulator of lane (g, r) holds queries 4g+i at position r;
 // the lane folds its four heads (ReLU, weights), writes the keys and counts first digits in
-// an LDS histogram (two 16-bit counters per word: a workgroup counts at most kPfPos per bin).
+// an LDS histogram (two 16-bit counters per word, digits d and d + 1024: a workgroup counts at most kPfPos per bin).
 // POOL: every query also gets its own block pool ([Article] IX, applied per query of the
 // chunk): the lanes of one 16-lane row hold one query's 16 consecutive positions, so the
 // 8-position block maximum is the decode scan's DPP step.  The block keys are counted by
@@ -309,10 +309,12 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
                         }
                     }
                 } else if (ok) {
-                    // first digit = key >> 21; two 16-bit counters per word: word digit >> 1,
-                    // half digit & 1 (an increment of 1 or 1 << 16)
-                    const uint32_t word = (key >> 22) & 0x3ffu;
-                    const uint32_t half = (key >> 21) & 1u;
+                    // first digit = key >> 21; two 16-bit counters per word: digit d and
+                    // d + 1024 share word d & 1023 (the key's top bit picks the half: an
+                    // increment of 1 or 1 << 16), so neighbouring digits, which the scores of
+                    // nearby positions often take, update different words
+                    const uint32_t word = (key >> 21) & 0x3ffu;
+                    const uint32_t half = key >> 31;
                     atomicAdd(&sh_hist[4 * g + i][word], 1u + half * 0xffffu);
                 }
                 if constexpr (POOL && !kCompact) {
@@ -375,8 +377,8 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
             const uint32_t v = sh_hist[ql][wd];
             if (v == 0u || q0 + ql >= n_q) continue;
             uint32_t* gh = ws.hist + (int64_t)(q0 + ql) * 2 * kHistBins;
-            if (v & 0xffffu) atomicAdd(&gh[2 * wd], v & 0xffffu);
-            if (v >> 16) atomicAdd(&gh[2 * wd + 1], v >> 16);
+            if (v & 0xffffu) atomicAdd(&gh[wd], v & 0xffffu);
+            if (v >> 16) atomicAdd(&gh[wd + kHistBins / 2], v >> 16);
         }
     }
 }
