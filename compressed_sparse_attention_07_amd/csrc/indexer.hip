@@ -760,15 +760,36 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
 // ----------------------------------------------------------------------------------------
 // Reindex, kernel 1: score the pool's positions with this layer's query
 // ----------------------------------------------------------------------------------------
+// Workgroup b scores chunk group `chunk` (cpw x kReindexTile pool slots) of query i.  When the
+// group count is a multiple of kXcds, XCD x (the XCD workgroup b runs on is b mod kXcds) takes the x-th
+// eighth of every query's pool: a pool is ascending, so that eighth covers about one eighth of
+// the query's positions, and where queries read the same sequence (the tokens of a prefill
+// chunk) one XCD's workgroups read one eighth of its keys, a share that stays in the XCD's L2.
+__device__ __forceinline__ void reindex_item(int b, int chunks, int& i, int& chunk) {
+    if (chunks % kXcds == 0) {
+        const int per = chunks / kXcds, j = b / kXcds;
+        i = j / per;
+        chunk = (b % kXcds) * per + j % per;
+    } else {
+        i = b / chunks;
+        chunk = b % chunks;
+    }
+}
+
+// cpw: chunks per workgroup (a divisor of the chunk count).  Many queries (a prefill chunk's
+// tokens): each workgroup scores cpw consecutive chunks of its query and adds its first-digit
+// counts to the query's histogram once, which divides the global atomics by cpw.
 template <int HI, bool MX>
 __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx,
     const uint8_t* __restrict__ k_sc, const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len,
-    int32_t max_len, int64_t cache_rows, int n_heads, const int32_t* __restrict__ pool, int pool_blocks,
+    int32_t max_len, int64_t cache_rows, int n_heads, const int32_t* __restrict__ pool, int pool_blocks, int cpw,
     IndexWs ws) {
     __shared__ uint32_t sh_hist[kHistBins];
 
-    const int i = blockIdx.y;
+    const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
+    int i, grp;
+    reindex_item((int)blockIdx.x, chunks / cpw, i, grp);
     const int t = threadIdx.x;
     const int lane = __lane_id();
     const int wid = t / kWave;
@@ -785,55 +806,57 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     __syncthreads();
 
     // one MFMA unit = two pool slots (16 positions): lanes r < 8 take slot 2m, r >= 8 slot 2m + 1;
-    // this wave takes units m0 + 4u of the workgroup's kReindexTile / 16 units
+    // this wave takes units m0 + 4u of the chunk's kReindexTile / 16 units
     constexpr int kUnits = kReindexTile / 16 / 4;  // units per wave
-    const int m0 = blockIdx.x * (kReindexTile / 16) + wid;
-    int blk[kUnits];
-#pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-        const int slot = 2 * (m0 + 4 * u) + (r >> 3);
-        blk[u] = slot < pool_blocks ? qpool[slot] : -1;
-    }
-    uint4 kb[kUnits][2];
-    uint32_t kc[kUnits][2], ks[kUnits];
-    if (n > 0) {
-        // absent rows read the sequence's first row (n > 0) and are masked below
+    for (int chunk = grp * cpw; chunk < (grp + 1) * cpw; ++chunk) {
+        const int m0 = chunk * (kReindexTile / 16) + wid;
+        int blk[kUnits];
 #pragma unroll
         for (int u = 0; u < kUnits; ++u) {
-            const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
-            const bool ok = blk[u] >= 0 && p < n;
-            const int64_t kr = row0 + (ok ? p : 0);
-            if constexpr (MX) {
-                const uint8_t* row = static_cast<const uint8_t*>(k_idx) + kr * 32 + 4 * g;
-                kc[u][0] = *reinterpret_cast<const uint32_t*>(row);
-                kc[u][1] = *reinterpret_cast<const uint32_t*>(row + 16);
-                ks[u] = *reinterpret_cast<const uint16_t*>(k_sc + kr * 2);
-            } else {
-                const uint16_t* row = static_cast<const uint16_t*>(k_idx) + kr * 64 + 8 * g;
-                kb[u][0] = *reinterpret_cast<const uint4*>(row);
-                kb[u][1] = *reinterpret_cast<const uint4*>(row + 32);
-            }
+            const int slot = 2 * (m0 + 4 * u) + (r >> 3);
+            blk[u] = slot < pool_blocks ? qpool[slot] : -1;
         }
-        if constexpr (MX) {
+        uint4 kb[kUnits][2];
+        uint32_t kc[kUnits][2], ks[kUnits];
+        if (n > 0) {
+            // absent rows read the sequence's first row (n > 0) and are masked below
 #pragma unroll
             for (int u = 0; u < kUnits; ++u) {
-                kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
-                kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
+                const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
+                const bool ok = blk[u] >= 0 && p < n;
+                const int64_t kr = row0 + (ok ? p : 0);
+                if constexpr (MX) {
+                    const uint8_t* row = static_cast<const uint8_t*>(k_idx) + kr * 32 + 4 * g;
+                    kc[u][0] = *reinterpret_cast<const uint32_t*>(row);
+                    kc[u][1] = *reinterpret_cast<const uint32_t*>(row + 16);
+                    ks[u] = *reinterpret_cast<const uint16_t*>(k_sc + kr * 2);
+                } else {
+                    const uint16_t* row = static_cast<const uint16_t*>(k_idx) + kr * 64 + 8 * g;
+                    kb[u][0] = *reinterpret_cast<const uint4*>(row);
+                    kb[u][1] = *reinterpret_cast<const uint4*>(row + 32);
+                }
+            }
+            if constexpr (MX) {
+#pragma unroll
+                for (int u = 0; u < kUnits; ++u) {
+                    kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
+                    kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
+                }
             }
         }
-    }
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
-        const int slot = 2 * (m0 + 4 * u) + (r >> 3);
-        const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
-        const bool ok = n > 0 && blk[u] >= 0 && p < n;
-        const float sc = n > 0 ? mfma_score<HI>(qf, kb[u][0], kb[u][1]) : 0.f;
-        const uint32_t key = ok ? score_key(sc) : 0u;
-        if (g == 0 && slot < pool_blocks) {
-            keys[slot * 8 + (r & 7)] = key;
-            if (key) atomicAdd(&sh_hist[key >> 21], 1u);
+        for (int u = 0; u < kUnits; ++u) {
+            const int slot = 2 * (m0 + 4 * u) + (r >> 3);
+            const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
+            const bool ok = n > 0 && blk[u] >= 0 && p < n;
+            const float sc = n > 0 ? mfma_score<HI>(qf, kb[u][0], kb[u][1]) : 0.f;
+            const uint32_t key = ok ? score_key(sc) : 0u;
+            if (g == 0 && slot < pool_blocks) {
+                keys[slot * 8 + (r & 7)] = key;
+                if (key) atomicAdd(&sh_hist[key >> 21], 1u);
+            }
         }
-    }
+    }  // chunks of this workgroup
     __syncthreads();
     uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
     for (int b = t; b < kHistBins; b += kScoreNT) {
@@ -962,11 +985,14 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
                                 int64_t cache_rows, int n_heads, const int32_t* pool, int pool_blocks, int top_k,
                                 const IndexWs& ws, int32_t* idx_out, int select, hipStream_t stream) {
     const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
-    dim3 grid(chunks, n_q);
+    // many queries (>= 512: a prefill chunk): a whole pool of 32 chunks per workgroup, one histogram
+    // flush per query instead of one per chunk
+    const int cpw = (n_q >= 512 && chunks % 32 == 0) ? 32 : 1;
+    const dim3 grid((unsigned)(chunks / cpw * n_q));  // (query, chunk group) items, see reindex_item
     auto kern = mx ? (n_heads <= 4 ? k_idx_reindex_score<4, true> : k_idx_reindex_score<8, true>)
                    : (n_heads <= 4 ? k_idx_reindex_score<4, false> : k_idx_reindex_score<8, false>);
     hipLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, k_sc, kv_row0, kv_len, max_len,
-                       cache_rows, n_heads, pool, pool_blocks, ws);
+                       cache_rows, n_heads, pool, pool_blocks, cpw, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !select) return e;
     const int ept = (pool_blocks * 8 + kSelNT - 1) / kSelNT;
