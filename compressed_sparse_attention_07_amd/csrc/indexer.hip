@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
 // would halve the resident workgroups).
 // ----------------------------------------------------------------------------------------
 constexpr int kPfQ = 16;       // queries per workgroup
-constexpr int kPfPos = 4096;   // positions per workgroup (1,024 per wave)
+constexpr int kPfPos = 8192;   // positions per workgroup (2,048 per wave)
 // What a pass of the prefill scoring kernel produces.  A chunk's selection runs it twice:
 // kPfHist (first-digit histograms, and the block keys when pools are asked for), then, once
 // k_idx_prefill_thresh has put every query's threshold bucket in the workspace, kPfCompact:
