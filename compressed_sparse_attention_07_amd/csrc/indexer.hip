@@ -954,12 +954,21 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
             hipLaunchKernelGGL(k_compact, grid, dim3(kScoreNT), 0, stream, q_idx, w, kb, kv_row0, n_q, cache_rows,
                                n_heads, top_k, n_px, n_qg, ws);
         } else if (!prefill) {
-            const int wgs = min(grid_tiles, scan_workgroups());
-            auto kern = mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true> : k_idx_score_full<8, true, false>)
-                           : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0>
-                                           : k_idx_score_full<8, false, false>);
+            // tiles split into 2 or 4 units while the host's tile bound leaves the grid half empty
+            int sub_log2 = 0;
+            while (sub_log2 < 2 && ((int64_t)grid_tiles << (sub_log2 + 1)) <= scan_workgroups()) ++sub_log2;
+            const int wgs = (int)std::min<int64_t>((int64_t)grid_tiles << sub_log2, scan_workgroups());
+            auto kern = sub_log2 == 0
+                            ? (mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true, false>
+                                                  : k_idx_score_full<8, true, false, false>)
+                                  : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0, false>
+                                                  : k_idx_score_full<8, false, false, false>))
+                            : (mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true, true>
+                                                  : k_idx_score_full<8, true, false, true>)
+                                  : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0, true>
+                                                  : k_idx_score_full<8, false, false, true>));
             hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, q_idx, w, k_idx, k_sc, kv_row0, kv_len,
-                               n_q, max_len, cache_rows, n_heads, grid_tiles, pool_blocks, ws);
+                               n_q, max_len, cache_rows, n_heads, grid_tiles, sub_log2, pool_blocks, ws);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -13,20 +13,25 @@ namespace csa2 {
 // Full mode, kernel 1: scores -> keys, block-max keys, first-digit histograms
 // ----------------------------------------------------------------------------------------
 // Persistent: the grid holds a few workgroups per CU and workgroup g streams the contiguous
-// tile range [g * T / G, (g + 1) * T / G) of the tile map, so the per-tile set-up (tile map,
-// query slice) is paid once per query rather than once per tile, and the first-digit
-// histograms go to the workspace only when the query changes.
+// range [g * U / G, (g + 1) * U / G) of U work units, so the per-tile set-up (tile map, query
+// slice) is paid once per query rather than once per tile, and the first-digit histograms go
+// to the workspace only when the query changes.  A unit is one of the T tiles of the map, or,
+// when the host's tile bound is small next to the grid, one of S = 2 or 4 equal position
+// ranges of a tile (U = T * S, S = 1 << sub_log2), so a short context is not streamed by a
+// single workgroup.
 // MX: keys are MXFP4 (k_idx = code bytes [rows, 32], k_sc = E8M0 bytes [rows, 2]) instead of
 // bf16 (k_idx = [rows, 64] bf16, k_sc unused).
 // LP: the lane-per-position layout (QFragLP; at most 4 heads): a wave step covers 64
 // positions with one score per lane, so the per-position epilogue (ReLU-weighted head sum,
 // key, stores, histogram atomics, block maximum) costs a quarter of the instructions of the
 // 16-position layout; the lane reads its own row (16-byte loads, 32 B per MXFP4 row).
-template <int HI, bool MX, bool LP>
+// SPLIT: sub_log2 is honoured (false: one unit per tile, the loop bounds fold to constants).
+template <int HI, bool MX, bool LP, bool SPLIT>
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx,
     const uint8_t* __restrict__ k_sc, const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len,
-    int n_q, int32_t max_len, int64_t cache_rows, int n_heads, int grid_tiles, int pool_blocks, IndexWs ws) {
+    int n_q, int32_t max_len, int64_t cache_rows, int n_heads, int grid_tiles, int sub_log2, int pool_blocks,
+    IndexWs ws) {
     __shared__ uint32_t sh_hist[kHistBins];
     __shared__ uint32_t sh_bhist[kHistBins];
 
@@ -35,8 +40,11 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     const int wid = t / kWave;
     const int g = lane >> 4, r = lane & 15;
     const bool want_pool = pool_blocks > 0;
-    const int tb = (int)((int64_t)blockIdx.x * grid_tiles / gridDim.x);
-    const int te = (int)((int64_t)(blockIdx.x + 1) * grid_tiles / gridDim.x);
+    if constexpr (!SPLIT) sub_log2 = 0;
+    const int64_t units = (int64_t)grid_tiles << sub_log2;
+    const int ub = (int)((int64_t)blockIdx.x * units / gridDim.x);
+    const int ue = (int)((int64_t)(blockIdx.x + 1) * units / gridDim.x);
+    const int unit_len = kFullTile >> sub_log2;  // positions per unit
 
     for (int b = t; b < kHistBins; b += kScoreNT) {
         sh_hist[b] = 0u;
@@ -68,7 +76,11 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
 
     // one step = 64 consecutive positions of the workgroup (16 per wave); U steps per batch
     constexpr int U = CSA2_SCAN_U;
-    for (int tile = tb; tile < te; ++tile) {
+    static_assert((kFullTile / 4) % (64 * U) == 0 && (kFullTile / 4) % (256 * CSA2_SCAN_U_LP) == 0,
+                  "a quarter tile holds whole load batches");
+    for (int unit = ub; unit < ue; ++unit) {
+        const int tile = unit >> sub_log2;
+        const int b_lo = (unit & ((1 << sub_log2) - 1)) * unit_len, b_hi = b_lo + unit_len;
         const int i = ws.tmap[tile];
         if (i < 0) break;  // unused tiles sit at the end of the map
         if (i != cur) {
@@ -101,7 +113,7 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
             constexpr int kLd = kRowB / 16;  // 16-byte loads per row
             const int voff = (64 * wid + lane) * kRowB;
             const int voff_s = (64 * wid + lane) * 2;
-            for (int b = 0; b < kFullTile; b += 256 * UL) {
+            for (int b = b_lo; b < b_hi; b += 256 * UL) {
                 const int pb = p_tile + b;
                 if (pb >= n) break;
                 uint4 kr[UL][kLd];
@@ -150,7 +162,7 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
         } else {
             const int voff = (16 * wid + r) * kRowB + (MX ? 4 : 16) * g;
             const int voff_s = (16 * wid + r) * 2;
-            for (int b = 0; b < kFullTile; b += 64 * U) {
+            for (int b = b_lo; b < b_hi; b += 64 * U) {
                 const int pb = p_tile + b;
                 if (pb >= n) break;
                 uint4 kb[U][2];
