@@ -255,6 +255,21 @@ def test_index_prefill_fractional_and_negative_weights():
         assert np.array_equal(pool_m[t], rp), t
 
 
+def test_index_reindex_many_queries_whole_pool_per_workgroup():
+    # >= 512 queries with 2,048-block pools: each Reindex workgroup scores a whole pool and adds
+    # its counts to the query's histogram once; every token checked against the oracle
+    T = 600
+    lengths = np.random.default_rng(90).integers(1, 20000, size=T)
+    case = SharedIndexCase(W_T + 90, 20000, lengths, n_heads=4)
+    _, pool, _ = case.run_full(512, 2048, shared_kv=1)
+    q2 = synth.int_bf16(W_T + 90, synth.T_IDX_Q, (T, 4, 64), seq=7)
+    w2 = synth.int_weights(W_T + 90, synth.T_IDX_W, (T, 4), seq=7)
+    idx2, _ = case.run_reindex(pool, 512, q_dev=bf16_tensor(q2), w_dev=torch.from_numpy(w2).to(DEV))
+    idx2, pool_np = idx2.cpu().numpy(), pool.cpu().numpy()
+    for t in range(T):
+        assert np.array_equal(idx2[t], case.oracle_reindex(t, pool_np[t], 512, q=q2[t], w=w2[t])), t
+
+
 def test_index_prefill_all_equal_scores_takes_lowest_positions():
     # every score is 0: every visible position of every token is in the threshold bucket, so
     # the compacting pass overflows its per-token LDS buffer and writes the rest directly
