@@ -541,12 +541,19 @@ __device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* sh, int
 // ----------------------------------------------------------------------------------------
 constexpr int kFiltU = kFilterTile / (4 * kScoreNT);       // position quads per thread
 constexpr int kFiltUB = (kFilterTile / 8 + 4 * kScoreNT - 1) / (4 * kScoreNT);  // block quads per thread
+// POOL_ONLY (a prefill chunk with pools: its compacting scoring pass wrote the position lists
+// already): only the block list is split, and the first workgroup of every kPoolGroup filter
+// tiles of a query takes all their blocks (the others return at once), so a query's ~17 tiles
+// need 3 workgroups, each loading the block histogram once for 8,192 blocks.
+constexpr int kPoolGroup = 8;
 
+template <bool POOL_ONLY>
 __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __restrict__ kv_row0,
                                                               const int32_t* __restrict__ kv_len, int n_q,
                                                               int32_t max_len, int64_t cache_rows, int grid_tiles,
-                                                              int grid_ftiles, int top_k, int pool_blocks, int pos_done,
-                                                              IndexWs ws) {
+                                                              int grid_ftiles, int top_k, int pool_blocks, IndexWs ws) {
+    constexpr int UP = POOL_ONLY ? 1 : kFiltU;                      // position quads per thread
+    constexpr int UB = POOL_ONLY ? kPoolGroup * kFiltUB : kFiltUB;  // block quads per thread
     __shared__ int sh_scan[2 * kScoreNT / kWave];
     __shared__ int sh_base[4];
     __shared__ Thresh sh_th[2];
@@ -558,13 +565,14 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __r
     const int n = qm.n;
     const int nb = (n + 7) >> 3;
     const int fchunk = (int)blockIdx.x - qm.fstart;
+    if (POOL_ONLY && fchunk % kPoolGroup != 0) return;  // uniform: the group's first workgroup takes its blocks
     const int64_t key_base = (int64_t)qm.start * kFullTile;
     uint32_t* ctrl = ws.ctrl + (int64_t)i * kCtlSlots;
     const uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
-    // (a prefill chunk's compacting pass wrote the position lists already: pos_done)
-    const bool do_pos = !pos_done, do_pool = pool_blocks > 0;
+    const bool do_pos = !POOL_ONLY, do_pool = pool_blocks > 0;
     const int p0 = fchunk * kFilterTile, p1 = do_pos ? min(n, p0 + kFilterTile) : p0;
-    const int b0 = fchunk * (kFilterTile / 8), b1 = do_pool ? min(nb, b0 + kFilterTile / 8) : b0;
+    const int b0 = fchunk * (kFilterTile / 8);
+    const int b1 = do_pool ? min(nb, b0 + (POOL_ONLY ? kPoolGroup : 1) * (kFilterTile / 8)) : b0;
 
     uint32_t h0[kHistBins / kScoreNT], h1[kHistBins / kScoreNT];
     if (do_pos) hist_load<kScoreNT>(gh, h0);
@@ -573,13 +581,15 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __r
     if (do_pool) hist_load<kScoreNT>(gh + kHistBins, h1);
     else
         for (auto& x : h1) x = 0u;
-    uint4 kq[kFiltU], bq[kFiltUB];
-    load_quads<kScoreNT>(kq, ws.keys + key_base, p0, p1);
+    uint4 kq[UP], bq[UB];
+    if constexpr (!POOL_ONLY) load_quads<kScoreNT>(kq, ws.keys + key_base, p0, p1);
     load_quads<kScoreNT>(bq, ws.bkeys + key_base / 8, b0, b1);
-    find_threshold_regs<kScoreNT>(h0, top_k, sh_scan, &sh_th[0]);
+    if constexpr (!POOL_ONLY) find_threshold_regs<kScoreNT>(h0, top_k, sh_scan, &sh_th[0]);
     find_threshold_regs<kScoreNT>(h1, max(pool_blocks, 1), sh_scan, &sh_th[1]);
-    const KeySplit s0 = key_split(sh_th[0]), s1 = key_split(sh_th[1]);
-    mask_quads<kScoreNT>(kq, p0, p1);
+    const KeySplit s0 = POOL_ONLY ? KeySplit{0xffffffffu, 0xffffffffu} : key_split(sh_th[0]);
+    const KeySplit s1 = key_split(sh_th[1]);
+    if constexpr (POOL_ONLY) kq[0] = make_uint4(0, 0, 0, 0);  // no positions (keys 0 fall in no list)
+    else mask_quads<kScoreNT>(kq, p0, p1);
     mask_quads<kScoreNT>(bq, b0, b1);
     int e0, e1, t0, t1;  // packed above << 16 | in bucket (a tile has at most kFilterTile of each)
     block_exclusive_scan2<kScoreNT>(count_quads(kq, s0), count_quads(bq, s1), sh_scan, e0, e1, t0, t1);
@@ -975,8 +985,10 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
     }
     if (phase & 4) {
         if (filter) {
-            hipLaunchKernelGGL(k_idx_filter_full, dim3(grid_ftiles), dim3(kScoreNT), 0, stream, kv_row0, kv_len, n_q,
-                               max_len, cache_rows, grid_tiles, grid_ftiles, top_k, pool_blocks, prefill, ws);
+            // (a prefill chunk's compacting pass wrote the position lists: only the block list is left)
+            hipLaunchKernelGGL(prefill ? k_idx_filter_full<true> : k_idx_filter_full<false>, dim3(grid_ftiles),
+                               dim3(kScoreNT), 0, stream, kv_row0, kv_len, n_q, max_len, cache_rows, grid_tiles,
+                               grid_ftiles, top_k, pool_blocks, ws);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
