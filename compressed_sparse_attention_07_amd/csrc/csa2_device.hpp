@@ -432,9 +432,10 @@ __device__ inline void bitonic_desc_u64(uint64_t* a, int n) {
     }
 }
 
-// LDS working set of one workgroup-level selection.
-struct SelectShared {
-    uint64_t buf[kSortCap];     // candidate composites, then reused for the output positions
+// LDS working set of one workgroup-level selection (CAP: candidates sorted in LDS, a power of 2).
+template <int CAP>
+struct SelectSharedT {
+    uint64_t buf[CAP];          // candidate composites, then reused for the output positions
     uint32_t hist[kHistBins];
     int scan[16];
     int cnt;
@@ -442,13 +443,14 @@ struct SelectShared {
     int above;
     int inb;
 };
+using SelectShared = SelectSharedT<kSortCap>;
 
 // The need-th largest of `count` candidate composites (src(e), e in [0, count)) whose keys all
 // start with the 11-bit digit `d1`, for candidate sets of any size: 11-bit radix passes over
 // the (global) list narrow the set until it fits in LDS, where it is sorted.  NT threads.
 // Returns the threshold composite (exactly `need` candidates are >= it), ~0 if need <= 0.
-template <int NT, class Src>
-__device__ uint64_t wg_threshold(const Src& src, int count, int need, int d1, SelectShared& S) {
+template <int NT, class Src, int CAP>
+__device__ uint64_t wg_threshold(const Src& src, int count, int need, int d1, SelectSharedT<CAP>& S) {
     const int t = threadIdx.x;
     constexpr int BPT = kHistBins / NT;
     uint64_t thr = ~0ull;
@@ -456,7 +458,7 @@ __device__ uint64_t wg_threshold(const Src& src, int count, int need, int d1, Se
     uint64_t prefix = (uint64_t)(uint32_t)d1;
     int pbits = kHistBits;
     int matching = count;
-    while (matching > kSortCap && pbits < 64) {
+    while (matching > CAP && pbits < 64) {
         const int w = (64 - pbits) >= kHistBits ? kHistBits : (64 - pbits);
         const int shift = 64 - pbits - w;
         for (int b = t; b < kHistBins; b += NT) S.hist[b] = 0;

@@ -614,17 +614,20 @@ struct CompositeList {
 };
 
 constexpr int kSelNT = 1024;  // threads of the per-query selection workgroups
+constexpr int kSelNTMany = 512, kSortCapMany = 2048;  // the same for a prefill chunk's many queries
 
+template <int CAP>
 struct SmallSel {
-    uint64_t cand[kSortCap];
+    uint64_t cand[CAP];
     uint32_t sel[kMaxSelect + 4];
     RadixShared R;
     int cnt;
     int nt;
 };
+template <int CAP>
 union SelLds {
-    SelectShared big;
-    SmallSel small;
+    SelectSharedT<CAP> big;
+    SmallSel<CAP> small;
 };
 
 constexpr int kTieCap = 1024;  // equal keys at the threshold ordered by direct counting
@@ -632,17 +635,20 @@ constexpr int kTieCap = 1024;  // equal keys at the threshold ordered by direct 
 // Decode contexts up to this length skip the filter kernel: the selection workgroup reads the
 // query's keys itself (kSelScanU four-key loads per thread, issued before the threshold search).
 constexpr int kSelScanMax = 16384;
-constexpr int kSelScanU = kSelScanMax / (4 * kSelNT);
+template <int NT>
+constexpr int sel_scan_u() { return kSelScanMax / (4 * NT); }  // four-key loads per thread
 
 // Ascending output of up to kMaxSelect selected positions (sel[] in LDS).
+template <int NT>
 struct AscLds {
     uint32_t scratch[2 * kAscB + kMaxSelect];
-    int scan[kSelNT / kWave];
+    int scan[NT / kWave];
     uint32_t mm[2];
 };
 
-__device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, int32_t* out, AscLds& A) {
-    bucket_write_ascending<kSelNT>(sel, total, k, out, A.scratch, A.scan, A.mm);
+template <int NT>
+__device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, int32_t* out, AscLds<NT>& A) {
+    bucket_write_ascending<NT>(sel, total, k, out, A.scratch, A.scan, A.mm);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -652,15 +658,19 @@ __device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, 
 // scan_keys != 0 (decode, every context <= kSelScanMax): the filter kernel did not run and this
 // workgroup splits the query's keys into the above-bucket and in-bucket lists itself.
 // Leaves the histograms and counters of the query zero for the next call.
+// NT threads; CAP: largest threshold bucket selected in LDS (larger ones take the global-list
+// radix path).  Decode: 1,024 threads, 8,192; a prefill chunk's thousands of queries: 512 and
+// 2,048, which halves the LDS so that two workgroups share a compute unit.
 // ----------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __restrict__ kv_row0,
+template <int NT, int CAP>
+__global__ __launch_bounds__(NT) void k_idx_select_full(const int64_t* __restrict__ kv_row0,
                                                             const int32_t* __restrict__ kv_len, int n_q,
                                                             int32_t max_len, int64_t cache_rows, int grid_tiles,
                                                             int top_k, int pool_blocks, int scan_keys, IndexWs ws,
                                                             int32_t* __restrict__ idx_out,
                                                             int32_t* __restrict__ pool_out) {
-    __shared__ SelLds U;
-    __shared__ AscLds A;
+    __shared__ SelLds<CAP> U;
+    __shared__ AscLds<NT> A;
     __shared__ Thresh sh_th;
     const int i = blockIdx.x;
     const int which = blockIdx.y;  // 0: positions, 1: pool blocks
@@ -673,35 +683,38 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
     uint64_t* cand = which ? ws.cand_pool + key_base / 8 : ws.cand_idx + key_base;
     int32_t* sure = which ? ws.sure_pool + (int64_t)i * pool_blocks : ws.sure_idx + (int64_t)i * top_k;
     int32_t* out = which ? pool_out + (int64_t)i * pool_blocks : idx_out + (int64_t)i * top_k;
-    uint32_t h[kHistBins / kSelNT];
-    hist_load<kSelNT>(gh, h);
+    uint32_t h[kHistBins / NT];
+    hist_load<NT>(gh, h);
     // the keys, requested behind the histogram so that waiting for it leaves them in flight
-    uint4 kq[kSelScanU];
+    // (the key-splitting path exists in the decode variant only; the prefill one never takes it)
+    constexpr bool kSplit = NT == kSelNT;
+    if constexpr (!kSplit) scan_keys = 0;
+    uint4 kq[kSplit ? sel_scan_u<NT>() : 1];
     const int n_elem = scan_keys ? (which ? (qm.n + 7) >> 3 : qm.n) : 0;
-    if (scan_keys) load_quads<kSelNT>(kq, which ? ws.bkeys + key_base / 8 : ws.keys + key_base, 0, n_elem);
-    find_threshold_regs<kSelNT>(h, k, U.small.R.scan, &sh_th);
+    if (scan_keys) load_quads<NT>(kq, which ? ws.bkeys + key_base / 8 : ws.keys + key_base, 0, n_elem);
+    find_threshold_regs<NT>(h, k, U.small.R.scan, &sh_th);
     const Thresh th = sh_th;
     const int need = k - th.above;
     const int n_sure = min(th.above, k);
-    const bool small = th.in_bucket <= kSortCap;
+    const bool small = th.in_bucket <= CAP;
     if (scan_keys) {
         // above the bucket -> sure list, in the bucket -> candidate composites; in LDS when the
         // bucket fits there, else in the query's global lists for the large-bucket path
         const KeySplit ks = key_split(th);
-        mask_quads<kSelNT>(kq, 0, n_elem);
+        mask_quads<NT>(kq, 0, n_elem);
         int tot;  // sure and candidates <= kSelScanMax each: 16 + 16 bits
-        const int pk = block_exclusive_scan<kSelNT>(count_quads(kq, ks), U.small.R.scan, tot);
+        const int pk = block_exclusive_scan<NT>(count_quads(kq, ks), U.small.R.scan, tot);
         if (small)
-            write_quads<kSelNT>(kq, ks, 0, pk >> 16, pk & 0xffff, U.small.sel, k, U.small.cand, kSortCap);
+            write_quads<NT>(kq, ks, 0, pk >> 16, pk & 0xffff, U.small.sel, k, U.small.cand, CAP);
         else
-            write_quads<kSelNT>(kq, ks, 0, pk >> 16, pk & 0xffff, sure, k, cand, n_elem);
+            write_quads<NT>(kq, ks, 0, pk >> 16, pk & 0xffff, sure, k, cand, n_elem);
         __syncthreads();
     }
     if (small) {
-        SmallSel& W = U.small;
+        SmallSel<CAP>& W = U.small;
         if (!scan_keys) {
-            for (int e = t; e < th.in_bucket; e += kSelNT) W.cand[e] = cand[e];
-            for (int j = t; j < n_sure; j += kSelNT) W.sel[j] = (uint32_t)sure[j];
+            for (int e = t; e < th.in_bucket; e += NT) W.cand[e] = cand[e];
+            for (int j = t; j < n_sure; j += NT) W.sel[j] = (uint32_t)sure[j];
         }
         if (t == 0) {
             W.cnt = n_sure;
@@ -710,20 +723,20 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
         __syncthreads();
         // the threshold KEY first (at most two passes); ties at it are ordered by position below
         const bool any = need > 0 && th.in_bucket > 0;
-        const KeyThr kt = any ? lds_key_threshold<kSelNT>(W.cand, th.in_bucket, need, th.digit, W.R)
+        const KeyThr kt = any ? lds_key_threshold<NT>(W.cand, th.in_bucket, need, th.digit, W.R)
                               : KeyThr{0u, -1, 0};
         const bool ranked = any && kt.take_eq >= 0;  // only take_eq of the n_tie equal keys go
         int total;
         if (ranked && kt.n_tie > kTieCap) {
             // many equal keys at the threshold: radix passes over the composites' position bits
-            const uint64_t thr = lds_radix_threshold<kSelNT>(W.cand, th.in_bucket, need, th.digit, W.R);
-            for (int e = t; e < th.in_bucket; e += kSelNT)
+            const uint64_t thr = lds_radix_threshold<NT>(W.cand, th.in_bucket, need, th.digit, W.R);
+            for (int e = t; e < th.in_bucket; e += NT)
                 if (W.cand[e] >= thr) W.sel[atomicAdd(&W.cnt, 1)] = composite_pos(W.cand[e]);
             __syncthreads();
             total = W.cnt;
         } else {
             uint32_t* ties = A.scratch;  // free until the ascending output
-            for (int e = t; e < th.in_bucket; e += kSelNT) {
+            for (int e = t; e < th.in_bucket; e += NT) {
                 const uint64_t c = W.cand[e];
                 const uint32_t key = (uint32_t)(c >> 32);
                 if (any && (ranked ? key > kt.t : key >= kt.t))
@@ -737,7 +750,7 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
                 // each tie's place among the ties by position (distinct positions): the take_eq
                 // lowest follow the keys above the threshold
                 const int nt = W.nt;
-                for (int j = t; j < nt; j += kSelNT) {
+                for (int j = t; j < nt; j += NT) {
                     const uint32_t p = ties[j];
                     int rank = 0;
                     for (int e = 0; e < nt; ++e) rank += ties[e] < p ? 1 : 0;
@@ -749,18 +762,18 @@ __global__ __launch_bounds__(kSelNT) void k_idx_select_full(const int64_t* __res
         }
         sort_out(W.sel, total, k, out, A);
     } else {
-        SelectShared& S = U.big;
-        const uint64_t thr = wg_threshold<kSelNT>(CompositeList{cand}, th.in_bucket, need, th.digit, S);
+        SelectSharedT<CAP>& S = U.big;
+        const uint64_t thr = wg_threshold<NT>(CompositeList{cand}, th.in_bucket, need, th.digit, S);
         uint32_t* sel = reinterpret_cast<uint32_t*>(S.buf);
         if (t == 0) S.cnt = 0;
         __syncthreads();
-        for (int j = t; j < n_sure; j += kSelNT) sel[atomicAdd(&S.cnt, 1)] = (uint32_t)sure[j];
-        for (int e = t; e < th.in_bucket; e += kSelNT)
+        for (int j = t; j < n_sure; j += NT) sel[atomicAdd(&S.cnt, 1)] = (uint32_t)sure[j];
+        for (int e = t; e < th.in_bucket; e += NT)
             if (cand[e] >= thr) sel[atomicAdd(&S.cnt, 1)] = composite_pos(cand[e]);
         __syncthreads();
         sort_out(sel, S.cnt, k, out, A);
     }
-    for (int b = t; b < kHistBins; b += kSelNT) gh[b] = 0u;
+    for (int b = t; b < kHistBins; b += NT) gh[b] = 0u;
     if (t == 0) {
         ctrl[which ? kCtlSurePool : kCtlSureIdx] = 0u;
         ctrl[which ? kCtlCandPool : kCtlCandIdx] = 0u;
@@ -992,7 +1005,9 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(k_idx_select_full, dim3(n_q, pool_blocks > 0 ? 2 : 1), dim3(kSelNT), 0, stream, kv_row0,
+        const bool many = prefill && n_q >= 512;
+        auto selk = many ? k_idx_select_full<kSelNTMany, kSortCapMany> : k_idx_select_full<kSelNT, kSortCap>;
+        hipLaunchKernelGGL(selk, dim3(n_q, pool_blocks > 0 ? 2 : 1), dim3(many ? kSelNTMany : kSelNT), 0, stream, kv_row0,
                            kv_len, n_q, max_len, cache_rows, grid_tiles, top_k, pool_blocks, scan_keys, ws, idx_out,
                            pool_out);
         return hipGetLastError();

@@ -270,10 +270,13 @@ def test_index_reindex_many_queries_whole_pool_per_workgroup():
         assert np.array_equal(idx2[t], case.oracle_reindex(t, pool_np[t], 512, q=q2[t], w=w2[t])), t
 
 
-def test_index_prefill_all_equal_scores_takes_lowest_positions():
+@pytest.mark.parametrize("tokens", [32, 600])
+def test_index_prefill_all_equal_scores_takes_lowest_positions(tokens):
     # every score is 0: every visible position of every token is in the threshold bucket, so
-    # the compacting pass overflows its per-token LDS buffer and writes the rest directly
-    lengths = [3000 + 7 * t for t in range(32)]
+    # the compacting pass overflows its per-token LDS buffer and writes the rest directly; with
+    # 600 tokens the selection runs its many-query form, whose LDS holds 2,048 candidates, so
+    # these buckets (3,000+ positions) take its global-list path
+    lengths = [3000 + 7 * (t % 40) for t in range(tokens)]
     case = SharedIndexCase(W_T + 62, 3300, lengths, n_heads=4, qlo=0, qhi=0)
     idx, pool, _ = case.run_full(512, 100, shared_kv=1)
     idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
