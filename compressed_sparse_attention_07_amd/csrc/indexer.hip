@@ -900,16 +900,17 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
 constexpr int kReMaxEPT = 32;  // elements per thread at pool_blocks = 4096
 
 // EPT: elements per thread (8, 16 or 32; a multiple of 8, so threads hold whole pool blocks).
-template <int EPT>
-__global__ __launch_bounds__(kSelNT) void k_idx_reindex_select(const int32_t* __restrict__ pool, int pool_blocks,
-                                                               int top_k, IndexWs ws,
-                                                               int32_t* __restrict__ idx_out) {
+// NT threads: 1,024 (decode), or 256 with EPT = 64 for a prefill chunk's many queries (more,
+// smaller workgroups per compute unit).
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void k_idx_reindex_select(const int32_t* __restrict__ pool, int pool_blocks,
+                                                           int top_k, IndexWs ws, int32_t* __restrict__ idx_out) {
     __shared__ uint32_t s_hist[2][kHistBins];
-    __shared__ int s_scan[kSelNT / kWave];
+    __shared__ int s_scan[NT / kWave];
     __shared__ uint32_t s_or[2];
     __shared__ Thresh sh_th;
-    reindex_select_query<kSelNT, EPT>(blockIdx.x, pool, pool_blocks, top_k, ws, idx_out, nullptr, s_hist, s_scan,
-                                      s_or, &sh_th);
+    reindex_select_query<NT, EPT>(blockIdx.x, pool, pool_blocks, top_k, ws, idx_out, nullptr, s_hist, s_scan, s_or,
+                                  &sh_th);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1031,8 +1032,15 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
                        cache_rows, n_heads, pool, pool_blocks, cpw, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !select) return e;
+    if (n_q >= 512 && pool_blocks * 8 <= 256 * 64) {
+        hipLaunchKernelGGL((k_idx_reindex_select<256, 64>), dim3(n_q), dim3(256), 0, stream, pool, pool_blocks, top_k,
+                           ws, idx_out);
+        return hipGetLastError();
+    }
     const int ept = (pool_blocks * 8 + kSelNT - 1) / kSelNT;
-    auto sel = ept <= 8 ? k_idx_reindex_select<8> : ept <= 16 ? k_idx_reindex_select<16> : k_idx_reindex_select<32>;
+    auto sel = ept <= 8    ? k_idx_reindex_select<kSelNT, 8>
+               : ept <= 16 ? k_idx_reindex_select<kSelNT, 16>
+                           : k_idx_reindex_select<kSelNT, 32>;
     hipLaunchKernelGGL(sel, dim3(n_q), dim3(kSelNT), 0, stream, pool, pool_blocks, top_k, ws, idx_out);
     return hipGetLastError();
 }
