@@ -151,7 +151,7 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
         # A prefill chunk's per-query key bytes are re-reads of one shared key array (from the
         # caches), not HBM traffic, so no HBM rate is derived from them; its scan is one dense
         # contraction (all queries x all visible positions x heads x 64) priced against MFMA.
-        for k in ("alg_gbps_step", "scan_gbps"):
+        for k in ("alg_gbps_step", "scan_gbps", "alg_bytes_per_step", "scan_alg_bytes_per_launch"):
             res[k] = None
         res["hbm_note"] = "prefill: MFMA-bound; per-query key bytes are cache re-reads, no HBM rate given"
         flops = 2.0 * 64 * wl.idx_heads * float(r.q_len.sum())
