@@ -13,11 +13,13 @@ captured in HIP graphs (the host issues one launch per step); the 1M-context wor
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.  "also" further
 holds the 1M-context workload in the pages' storage formats: an FP8 window store with SWA Bounded
 Replay starts, MXFP4 indexer keys, and both together; and the two prefill chunks (one Full
-layer; Full with per-token pools + 2 Reindex + 1 Reuse), as chunk tokens/s.  The 64K workload
+layer; Full with per-token pools + 2 Reindex + 1 Reuse), as chunk tokens/s; the single 4K-context
+sequence; and the ragged mix of 64 sequences (1K to 1M contexts, F U F U, two appends per
+sequence and step).  The 64K workload
 rotates two device copies of its inputs so that no step re-reads data a 256 MiB last-level
 cache could still hold.
 
-  python bench.py [--steps K] [--warmup W] [--workload 1] [--also 2,5,6,7,3,8] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload 1] [--also 2,5,6,7,3,8,0,4] [--no-cpu-baseline]
   python bench.py --mode copy      # plain 1 GiB device copy, for counter calibration
 """
 from __future__ import annotations
@@ -252,7 +254,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=1)
-    ap.add_argument("--also", type=str, default="2,5,6,7,3,8")
+    ap.add_argument("--also", type=str, default="2,5,6,7,3,8,0,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
