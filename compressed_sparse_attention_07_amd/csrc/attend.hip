@@ -172,8 +172,8 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
     const uint8_t* __restrict__ scales = a.scales;
     const int64_t* __restrict__ kv_row0 = a.kv_row0;
     const int32_t* __restrict__ kv_len = a.kv_len;
-    const int32_t max_len = a.max_len;
-    const int64_t cache_rows = a.cache_rows;
+    int32_t max_len = a.max_len;     // (made opaque below, after the first level of loads)
+    int64_t cache_rows = a.cache_rows;
     const int top_k = a.top_k;
     const void* __restrict__ swa = a.swa;
     const int64_t* __restrict__ swa_row0 = a.swa_row0;
@@ -232,6 +232,9 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
     // an empty statement that takes and returns the four per-query values: every use of them
     // comes after it, so no wait for them is placed in front of the index and query loads
     asm volatile("" : "+v"(len_raw), "+v"(row0_raw), "+v"(wrow0_raw), "+v"(replay_raw));
+    // the same for the bounds (kernel arguments not preloaded into SGPRs): their loads are not
+    // waited for in front of the first level
+    asm volatile("" : "+s"(max_len), "+s"(cache_rows));
 
     const int n = eff_len_of(len_raw, row0_raw, max_len, cache_rows);
     // window = the last wc positions of [0, n), none before the replay start (branch-free, so
@@ -509,12 +512,22 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
     }
 }
 
+// The arguments one by one (not the AttendArgs block), those of the first level of loads first:
+// the leading ones are preloaded into SGPRs at launch, so those loads need no scalar load of
+// the argument block before them.
 template <bool kFp4, bool kWin, bool kW8>
-__global__ __launch_bounds__(kAttNT) void k_attend(AttendArgs a) {
+__global__ __launch_bounds__(kAttNT) void k_attend(const int32_t* kv_len, const int64_t* kv_row0,
+                                                   const int64_t* swa_row0, const int64_t* replay, const int32_t* idx,
+                                                   const uint16_t* q, int top_k, int n_heads, int32_t max_len,
+                                                   int64_t cache_rows, const uint8_t* codes, const uint8_t* scales,
+                                                   const void* swa, int swa_cap, int64_t swa_rows, int window,
+                                                   float scale_log2, float* out) {
     __shared__ __align__(16) uint8_t s_tile[kAttWaves * kTileB];
     __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
+    const AttendArgs a{q,        codes,    scales, kv_row0, kv_len, max_len, cache_rows, idx,     top_k, swa,
+                       swa_row0, swa_cap,  swa_rows, window, replay, n_heads, scale_log2, out};
     const int i = blockIdx.x;
-    attend_query<kFp4, kWin, kW8>(i, a, a.idx + (int64_t)i * a.top_k, AttendLds{s_tile, s_m, s_l});
+    attend_query<kFp4, kWin, kW8>(i, a, idx + (int64_t)i * top_k, AttendLds{s_tile, s_m, s_l});
 }
 
 // Reindex layer, second kernel: the query's selection inside its pool (reindex_select_query,
@@ -553,9 +566,8 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
     else
         kern = fp4 ? (win ? k_attend<true, true, false> : k_attend<true, false, false>)
                    : (win ? k_attend<false, true, false> : k_attend<false, false, false>);
-    const AttendArgs a{q,          codes,    scales, kv_row0, kv_len, max_len,   cache_rows, idx, top_k, swa,
-                       swa_row0,   swa_cap,  swa_rows, window, replay,  n_heads, scale_log2, out};
-    hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, a);
+    hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, kv_len, kv_row0, swa_row0, replay, idx, q, top_k,
+                       n_heads, max_len, cache_rows, codes, scales, swa, swa_cap, swa_rows, window, scale_log2, out);
     return hipGetLastError();
 }
 
