@@ -804,10 +804,11 @@ __device__ __forceinline__ void reindex_item(int b, int chunks, int& i, int& chu
 // counts to the query's histogram once, which divides the global atomics by cpw.
 template <int HI, bool MX>
 __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx,
-    const uint8_t* __restrict__ k_sc, const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len,
-    int32_t max_len, int64_t cache_rows, int n_heads, const int32_t* __restrict__ pool, int pool_blocks, int cpw,
+    const int32_t* __restrict__ pool, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
+    const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len, int pool_blocks, int n_heads, int cpw,
+    int32_t max_len, const void* __restrict__ k_idx, const uint8_t* __restrict__ k_sc, int64_t cache_rows,
     IndexWs ws) {
+    // (the leading arguments, everything the first loads need, are preloaded into SGPRs)
     __shared__ uint32_t sh_hist[kHistBins];
 
     const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
@@ -902,13 +903,19 @@ constexpr int kReMaxEPT = 32;  // elements per thread at pool_blocks = 4096
 // EPT: elements per thread (8, 16 or 32; a multiple of 8, so threads hold whole pool blocks).
 // NT threads: 1,024 (decode), or 256 with EPT = 64 for a prefill chunk's many queries (more,
 // smaller workgroups per compute unit).
+// The workspace's key and histogram areas come as arguments of their own, ahead of the rest, so
+// that they are preloaded into SGPRs with the pool: the first loads need nothing else.
 template <int NT, int EPT>
-__global__ __launch_bounds__(NT) void k_idx_reindex_select(const int32_t* __restrict__ pool, int pool_blocks,
-                                                           int top_k, IndexWs ws, int32_t* __restrict__ idx_out) {
+__global__ __launch_bounds__(NT) void k_idx_reindex_select(uint32_t* __restrict__ keys, uint32_t* __restrict__ hist,
+                                                           const int32_t* __restrict__ pool, int pool_blocks,
+                                                           int top_k, int32_t* __restrict__ idx_out) {
     __shared__ uint32_t s_hist[2][kHistBins];
     __shared__ int s_scan[NT / kWave];
     __shared__ uint32_t s_or[2];
     __shared__ Thresh sh_th;
+    IndexWs ws{};
+    ws.keys = keys;
+    ws.hist = hist;
     reindex_select_query<NT, EPT>(blockIdx.x, pool, pool_blocks, top_k, ws, idx_out, nullptr, s_hist, s_scan, s_or,
                                   &sh_th);
 }
@@ -1028,20 +1035,20 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
     const dim3 grid((unsigned)(chunks / cpw * n_q));  // (query, chunk group) items, see reindex_item
     auto kern = mx ? (n_heads <= 4 ? k_idx_reindex_score<4, true> : k_idx_reindex_score<8, true>)
                    : (n_heads <= 4 ? k_idx_reindex_score<4, false> : k_idx_reindex_score<8, false>);
-    hipLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, q_idx, w, k_idx, k_sc, kv_row0, kv_len, max_len,
-                       cache_rows, n_heads, pool, pool_blocks, cpw, ws);
+    hipLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, pool, q_idx, w, kv_row0, kv_len, pool_blocks, n_heads,
+                       cpw, max_len, k_idx, k_sc, cache_rows, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !select) return e;
     if (n_q >= 512 && pool_blocks * 8 <= 256 * 64) {
-        hipLaunchKernelGGL((k_idx_reindex_select<256, 64>), dim3(n_q), dim3(256), 0, stream, pool, pool_blocks, top_k,
-                           ws, idx_out);
+        hipLaunchKernelGGL((k_idx_reindex_select<256, 64>), dim3(n_q), dim3(256), 0, stream, ws.keys, ws.hist, pool,
+                           pool_blocks, top_k, idx_out);
         return hipGetLastError();
     }
     const int ept = (pool_blocks * 8 + kSelNT - 1) / kSelNT;
     auto sel = ept <= 8    ? k_idx_reindex_select<kSelNT, 8>
                : ept <= 16 ? k_idx_reindex_select<kSelNT, 16>
                            : k_idx_reindex_select<kSelNT, 32>;
-    hipLaunchKernelGGL(sel, dim3(n_q), dim3(kSelNT), 0, stream, pool, pool_blocks, top_k, ws, idx_out);
+    hipLaunchKernelGGL(sel, dim3(n_q), dim3(kSelNT), 0, stream, ws.keys, ws.hist, pool, pool_blocks, top_k, idx_out);
     return hipGetLastError();
 }
 
