@@ -33,8 +33,9 @@ FLAGS = [
 # Per-source additions.  indexer.hip: MFMA results in ordinary VGPRs (no accumulation registers),
 # so the scoring epilogues read them without a copy per value.
 EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
-         # both: a kernel's leading scalar and pointer arguments preloaded into SGPRs at launch
-         "attend.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+         # all three: a kernel's leading scalar and pointer arguments preloaded into SGPRs at launch
+         "attend.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+         "fp4_pack.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def _compile(src: str) -> str:

@@ -548,10 +548,16 @@ constexpr int kFiltUB = (kFilterTile / 8 + 4 * kScoreNT - 1) / (4 * kScoreNT);  
 constexpr int kPoolGroup = 8;
 
 template <bool POOL_ONLY>
-__global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(const int64_t* __restrict__ kv_row0,
-                                                              const int32_t* __restrict__ kv_len, int n_q,
-                                                              int32_t max_len, int64_t cache_rows, int grid_tiles,
-                                                              int grid_ftiles, int top_k, int pool_blocks, IndexWs ws) {
+// The workspace areas of the first loads (tile map, query metadata, histograms, keys) come as
+// leading arguments of their own, preloaded into SGPRs at launch; ws supplies the rest.
+__global__ __launch_bounds__(kScoreNT) void k_idx_filter_full(int32_t* fmap, QMeta* qmeta, uint32_t* hist,
+                                                              uint32_t* keys, uint32_t* bkeys, int top_k,
+                                                              int pool_blocks, IndexWs ws) {
+    ws.fmap = fmap;
+    ws.qmeta = qmeta;
+    ws.hist = hist;
+    ws.keys = keys;
+    ws.bkeys = bkeys;
     constexpr int UP = POOL_ONLY ? 1 : kFiltU;                      // position quads per thread
     constexpr int UB = POOL_ONLY ? kPoolGroup * kFiltUB : kFiltUB;  // block quads per thread
     __shared__ int sh_scan[2 * kScoreNT / kWave];
@@ -663,12 +669,15 @@ __device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, 
 // 2,048, which halves the LDS so that two workgroups share a compute unit.
 // ----------------------------------------------------------------------------------------
 template <int NT, int CAP>
-__global__ __launch_bounds__(NT) void k_idx_select_full(const int64_t* __restrict__ kv_row0,
-                                                            const int32_t* __restrict__ kv_len, int n_q,
-                                                            int32_t max_len, int64_t cache_rows, int grid_tiles,
-                                                            int top_k, int pool_blocks, int scan_keys, IndexWs ws,
-                                                            int32_t* __restrict__ idx_out,
-                                                            int32_t* __restrict__ pool_out) {
+// (as in the filter pass: the first loads' workspace areas lead the arguments, preloaded)
+__global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* hist, uint32_t* keys, uint32_t* bkeys,
+                                                        int top_k, int pool_blocks, int scan_keys, IndexWs ws,
+                                                        int32_t* __restrict__ idx_out,
+                                                        int32_t* __restrict__ pool_out) {
+    ws.qmeta = qmeta;
+    ws.hist = hist;
+    ws.keys = keys;
+    ws.bkeys = bkeys;
     __shared__ SelLds<CAP> U;
     __shared__ AscLds<NT> A;
     __shared__ Thresh sh_th;
@@ -1008,16 +1017,15 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
         if (filter) {
             // (a prefill chunk's compacting pass wrote the position lists: only the block list is left)
             hipLaunchKernelGGL(prefill ? k_idx_filter_full<true> : k_idx_filter_full<false>, dim3(grid_ftiles),
-                               dim3(kScoreNT), 0, stream, kv_row0, kv_len, n_q, max_len, cache_rows, grid_tiles,
-                               grid_ftiles, top_k, pool_blocks, ws);
+                               dim3(kScoreNT), 0, stream, ws.fmap, ws.qmeta, ws.hist, ws.keys, ws.bkeys, top_k,
+                               pool_blocks, ws);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
         const bool many = prefill && n_q >= 512;
         auto selk = many ? k_idx_select_full<kSelNTMany, kSortCapMany> : k_idx_select_full<kSelNT, kSortCap>;
-        hipLaunchKernelGGL(selk, dim3(n_q, pool_blocks > 0 ? 2 : 1), dim3(many ? kSelNTMany : kSelNT), 0, stream, kv_row0,
-                           kv_len, n_q, max_len, cache_rows, grid_tiles, top_k, pool_blocks, scan_keys, ws, idx_out,
-                           pool_out);
+        hipLaunchKernelGGL(selk, dim3(n_q, pool_blocks > 0 ? 2 : 1), dim3(many ? kSelNTMany : kSelNT), 0, stream,
+                           ws.qmeta, ws.hist, ws.keys, ws.bkeys, top_k, pool_blocks, scan_keys, ws, idx_out, pool_out);
         return hipGetLastError();
     }
     return hipSuccess;
