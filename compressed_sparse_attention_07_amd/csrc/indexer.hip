@@ -1007,8 +1007,8 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
                                                   : k_idx_score_full<8, true, false, true>)
                                   : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0, true>
                                                   : k_idx_score_full<8, false, false, true>));
-            hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, q_idx, w, k_idx, k_sc, kv_row0, kv_len,
-                               n_q, max_len, cache_rows, n_heads, grid_tiles, sub_log2, pool_blocks, ws);
+            hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, ws.tmap, ws.qmeta, kv_row0, q_idx, w, k_idx,
+                               grid_tiles, sub_log2, n_heads, k_sc, pool_blocks, ws);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

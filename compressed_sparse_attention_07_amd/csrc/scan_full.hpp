@@ -27,11 +27,14 @@ namespace csa2 {
 // 16-position layout; the lane reads its own row (16-byte loads, 32 B per MXFP4 row).
 // SPLIT: sub_log2 is honoured (false: one unit per tile, the loop bounds fold to constants).
 template <int HI, bool MX, bool LP, bool SPLIT>
+// Arguments: the tile map and everything the first loads of a tile need lead (preloaded into
+// SGPRs at launch); ws supplies the output areas.
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
-    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx,
-    const uint8_t* __restrict__ k_sc, const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len,
-    int n_q, int32_t max_len, int64_t cache_rows, int n_heads, int grid_tiles, int sub_log2, int pool_blocks,
-    IndexWs ws) {
+    int32_t* tmap, QMeta* qmeta, const int64_t* __restrict__ kv_row0, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w, const void* __restrict__ k_idx, int grid_tiles, int sub_log2, int n_heads,
+    const uint8_t* __restrict__ k_sc, int pool_blocks, IndexWs ws) {
+    ws.tmap = tmap;
+    ws.qmeta = qmeta;
     __shared__ uint32_t sh_hist[kHistBins];
     __shared__ uint32_t sh_bhist[kHistBins];
 
