@@ -26,9 +26,9 @@ namespace csa2 {
 // key, stores, histogram atomics, block maximum) costs a quarter of the instructions of the
 // 16-position layout; the lane reads its own row (16-byte loads, 32 B per MXFP4 row).
 // SPLIT: sub_log2 is honoured (false: one unit per tile, the loop bounds fold to constants).
-template <int HI, bool MX, bool LP, bool SPLIT>
 // Arguments: the tile map and everything the first loads of a tile need lead (preloaded into
 // SGPRs at launch); ws supplies the output areas.
+template <int HI, bool MX, bool LP, bool SPLIT>
 __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     int32_t* tmap, QMeta* qmeta, const int64_t* __restrict__ kv_row0, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w, const void* __restrict__ k_idx, int grid_tiles, int sub_log2, int n_heads,
