@@ -153,6 +153,19 @@ def test_index_full_many_queries():
         assert np.array_equal(pool[i], rp), i
 
 
+def test_index_full_more_queries_than_one_prep_chunk():
+    # 1,300 decode queries: the metadata kernel handles them in chunks of 1,024 (tile runs carried
+    # across chunks), with every context short enough for the filter-free selection
+    lengths = list(np.random.default_rng(23).integers(0, 2500, size=1300))
+    case = IndexCase(W_T + 11, lengths, n_heads=4)
+    idx, pool, _ = case.run_full(64, 16)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for i in list(range(0, 1300, 13)) + [1023, 1024, 1025, 1299]:
+        ri, rp = case.oracle_full(i, 64, 16)
+        assert np.array_equal(idx[i], ri), i
+        assert np.array_equal(pool[i], rp), i
+
+
 def test_index_full_tie_heavy_and_repeatable():
     lengths = [3000, 70000, 12345]
     case = IndexCase(W_T + 1, lengths, n_heads=4, qlo=0, qhi=1)   # scores in a narrow integer range
