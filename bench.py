@@ -9,7 +9,8 @@ Prints ONE JSON line.  `value` is decode tokens/s of the batched 64K-context wor
 (32 sequences x 65,536 positions, 8 layers F R R R U U U U), timed over K replays of the step
 captured in HIP graphs (the host issues one launch per step); the 1M-context workload (8 x 2^20,
 20 layers) is reported in the same line under "also".  `roofline` covers the dominant kernel
-(the Full-mode scan), timed with HIP events around each of its launches in K eager steps.
+(the Full-mode scan), timed with HIP events its own launches record at the kernel's start and end,
+in K eager steps.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.  "also" further
 holds the 1M-context workload in the pages' storage formats: an FP8 window store with SWA Bounded
 Replay starts, MXFP4 indexer keys, and both together; and the two prefill chunks (one Full
@@ -89,7 +90,7 @@ def gpu_busy_wait(torch, seconds: float) -> None:
 
 
 def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
-    """Eager pass (HIP events around every Full scan launch -> the scan kernel's average duration),
+    """Eager pass (HIP events recorded by every Full scan launch -> the scan kernel's average duration),
     then the timed region proper: `steps` replays of the step captured in HIP graphs."""
     import torch
     from compressed_sparse_attention_07_amd import workloads as W
@@ -112,8 +113,8 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
         r.step()
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t0
-    # the same steps again with events around each Full-scan launch; a GPU-side wait in front lets
-    # the host issue every step before the GPU starts, so no event pair spans an idle gap
+    # the same steps again with each Full-scan launch recording its start and end into an event
+    # pair; a GPU-side wait in front lets the host issue every step before the GPU starts
     gpu_busy_wait(torch, 1.5 * steps * t_host + 2e-3)
     for _ in range(steps):
         r.step(scan_events=ev)
@@ -307,9 +308,9 @@ def main() -> int:
         "step_alg_gbps": (round(main_res["alg_gbps_step"], 1) if main_res["alg_gbps_step"] is not None else None),
         "eager_tokens_per_s": round(main_res["eager_tokens_per_s"], 1),
         "input_copies": main_res["input_copies"],
-        "timing": "value: K replays of the step captured in HIP graphs; roofline: HIP events around "
-                  "each Full-scan kernel launch (csa2_index_full_scan) in K eager steps issued behind a "
-                  "GPU-side wait (no host gaps inside an event pair)",
+        "timing": "value: K replays of the step captured in HIP graphs; roofline: HIP events recorded by "
+                  "each Full-scan kernel's own launch at its start and end (csa2_index_full_scan_timed), "
+                  "in K eager steps issued behind a GPU-side wait",
         "step_frac_of_hbm_peak": (round(main_res["alg_gbps_step"] / HBM_PEAK_GBPS, 4)
                                   if main_res["alg_gbps_step"] is not None else None),
         "cpu_baseline": cpu,

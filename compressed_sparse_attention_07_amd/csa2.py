@@ -32,6 +32,7 @@ EXPORTS = (
     "mxfp4_key_append",
     "csa2_index_full_mx",
     "csa2_index_full_mx_scan",
+    "csa2_index_full_scan_timed",
     "csa2_index_reindex_mx",
     "csa2_attend",
     "csa2_attend_fp8win",
@@ -83,6 +84,8 @@ def lib() -> ctypes.CDLL:
         for name in ("csa2_index_full_mx", "csa2_index_full_mx_scan"):
             getattr(L, name).argtypes = [vp, vp, vp, vp, SeqsC, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
         L.csa2_index_reindex_mx.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
+        L.csa2_index_full_scan_timed.argtypes = [vp, vp, vp, vp, SeqsC, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp,
+                                                 vp, vp]
         L.csa2_attend_fp8win.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp,
                                          sz, vp]
         L.csa2_reindex_attend.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp,
@@ -95,7 +98,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_version.argtypes = []
         for name in ("fp4_kv_append", "fp8_window_append", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
                      "csa2_attend_fp8win", "csa2_workspace_init", "csa2_version", "mxfp4_key_append",
-                     "csa2_index_full_mx", "csa2_index_full_mx_scan", "csa2_index_reindex_mx", "csa2_reindex_attend"):
+                     "csa2_index_full_mx", "csa2_index_full_mx_scan", "csa2_index_reindex_mx", "csa2_reindex_attend",
+                     "csa2_index_full_scan_timed"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -273,6 +277,18 @@ def csa2_index_full_mx_scan(q_idx, w, k_codes, k_scales, seqs: Seqs, top_k: int,
     _check("csa2_index_full_mx_scan", lib().csa2_index_full_mx_scan(
         _ptr(q_idx), _ptr(w), _ptr(k_codes), _ptr(k_scales), seqs.c(), q_idx.shape[1], top_k, block, pool_blocks,
         shared_kv, _ptr(idx_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def csa2_index_full_scan_timed(q_idx, w, k_idx, k_scales, seqs: Seqs, top_k: int, pool_blocks: int, idx_out,
+                               pool_out, ws, start_event, stop_event, block: int = BLOCK, shared_kv: int = 0,
+                               stream=None) -> None:
+    """The scan phase (k_scales None: bf16 keys; else MXFP4 codes in k_idx) with the scan kernel's
+    start and end recorded into two torch.cuda.Event objects (recorded once already, so that
+    their HIP events exist)."""
+    _check("csa2_index_full_scan_timed", lib().csa2_index_full_scan_timed(
+        _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scales), seqs.c(), q_idx.shape[1], top_k, block, pool_blocks,
+        shared_kv, _ptr(idx_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream(stream),
+        ctypes.c_void_p(start_event.cuda_event), ctypes.c_void_p(stop_event.cuda_event)))
 
 
 def csa2_index_reindex_mx(q_idx, w, k_codes, k_scales, seqs: Seqs, pool, top_k: int, idx_out, ws,

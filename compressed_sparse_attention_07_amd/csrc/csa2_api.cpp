@@ -48,7 +48,8 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
                              const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
                              int64_t cache_rows, int n_heads, int grid_tiles, int grid_ftiles, int top_k,
                              int pool_blocks, int prefill, const IndexWs& ws, int32_t* idx_out, int32_t* pool_out,
-                             int phase, hipStream_t stream);
+                             int phase, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                             hipEvent_t ev_stop = nullptr);
 hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
                                 int64_t cache_rows, int n_heads, const int32_t* pool, int pool_blocks, int top_k,
@@ -202,7 +203,8 @@ size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32
 static int index_full_phase(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
                             const csa2_seqs& seqs, int32_t n_heads, int32_t top_k, int32_t block,
                             int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws,
-                            size_t ws_bytes, void* stream, int phase) {
+                            size_t ws_bytes, void* stream, int phase, void* ev_start = nullptr,
+                            void* ev_stop = nullptr) {
     int st = check_seqs(seqs);
     if (st) return st;
     if (n_heads < 1 || n_heads > CSA2_MAX_IDX_HEADS || top_k < 1 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 ||
@@ -228,7 +230,8 @@ static int index_full_phase(const uint16_t* q_idx, const float* w, const void* k
     return launch_status(launch_index_full(q_idx, w, k_idx, k_sc, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
                                            seqs.max_len_ub, seqs.cache_rows, n_heads, (int)tiles, (int)ftiles, top_k,
                                            pool_blocks, prefill, wsp, idx_out, pool_out, phase,
-                                           static_cast<hipStream_t>(stream)));
+                                           static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_start),
+                                           static_cast<hipEvent_t>(ev_stop)));
 }
 
 int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
@@ -328,6 +331,15 @@ int csa2_index_full_mx_scan(const uint16_t* q_idx, const float* w, const uint8_t
                             void* stream) {
     return index_full_phase(q_idx, w, k_codes, k_scales, 1, seqs, n_heads, top_k, block, pool_blocks, shared_kv,
                             idx_out, pool_out, ws, ws_bytes, stream, 2);
+}
+
+int csa2_index_full_scan_timed(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
+                               csa2_seqs seqs, int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
+                               int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes,
+                               void* stream, void* start_event, void* stop_event) {
+    return index_full_phase(q_idx, w, k_idx, k_scales, k_scales != nullptr ? 1 : 0, seqs, n_heads, top_k, block,
+                            pool_blocks, shared_kv, idx_out, pool_out, ws, ws_bytes, stream, 2, start_event,
+                            stop_event);
 }
 
 int csa2_index_reindex_mx(const uint16_t* q_idx, const float* w, const uint8_t* k_codes, const uint8_t* k_scales,

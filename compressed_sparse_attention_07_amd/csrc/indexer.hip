@@ -34,6 +34,8 @@
 //   Reindex: score (pool positions) -> select (one workgroup per query).
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "csa2_device.hpp"
 #include "reindex_select.hpp"
 #include "scan_common.hpp"
@@ -959,7 +961,7 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
                              const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
                              int64_t cache_rows, int n_heads, int grid_tiles, int grid_ftiles, int top_k,
                              int pool_blocks, int prefill, const IndexWs& ws, int32_t* idx_out, int32_t* pool_out,
-                             int phase, hipStream_t stream) {
+                             int phase, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
     // short decode contexts: the selection workgroups read the keys themselves (no filter pass)
     const int scan_keys = !prefill && max_len <= kSelScanMax ? 1 : 0;
     const bool filter = (!prefill || pool_blocks > 0) && !scan_keys;  // a prefill chunk's position lists
@@ -972,6 +974,12 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
         if (e != hipSuccess) return e;
     }
     if (phase & 2) {
+        // ev_start / ev_stop (may be null): the decode scan kernel's own start and end are recorded
+        // into them by its launch; a prefill chunk's scoring kernels are bracketed by records
+        if (prefill && ev_start != nullptr) {
+            hipError_t e = hipEventRecord(ev_start, stream);
+            if (e != hipSuccess) return e;
+        }
         if (prefill && max_len > 0) {  // (no visible position anywhere: nothing to score)
             const int n_px = (max_len + kPfPos - 1) / kPfPos, n_qg = (n_q + kPfQ - 1) / kPfQ;
             const dim3 grid((unsigned)(kXcds * pf_items_per_xcd(n_px, n_qg)));
@@ -1007,8 +1015,16 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
                                                   : k_idx_score_full<8, true, false, true>)
                                   : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0, true>
                                                   : k_idx_score_full<8, false, false, true>));
-            hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, ws.tmap, ws.qmeta, kv_row0, q_idx, w, k_idx,
-                               grid_tiles, sub_log2, n_heads, k_sc, pool_blocks, ws);
+            if (ev_start != nullptr || ev_stop != nullptr)
+                hipExtLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, ev_start, ev_stop, 0, ws.tmap, ws.qmeta,
+                                      kv_row0, q_idx, w, k_idx, grid_tiles, sub_log2, n_heads, k_sc, pool_blocks, ws);
+            else
+                hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, ws.tmap, ws.qmeta, kv_row0, q_idx, w,
+                                   k_idx, grid_tiles, sub_log2, n_heads, k_sc, pool_blocks, ws);
+        }
+        if (prefill && ev_stop != nullptr) {
+            hipError_t e = hipEventRecord(ev_stop, stream);
+            if (e != hipSuccess) return e;
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -285,17 +285,21 @@ class Runner:
                 C.csa2_index_full_prep(L.q_idx, L.w, keys, self.seqs, wl.top_k, want_pool, L.idx, pool,
                                        self.ws_full, shared_kv=shared, stream=stream)
                 if scan_events is not None:
+                    # the scan kernel's own start and end, recorded by its launch (the two records
+                    # here only create the events)
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record()
-                if wl.keys_mx:
+                    e1.record()
+                    C.csa2_index_full_scan_timed(L.q_idx, L.w, st.k_codes if wl.keys_mx else st.k_idx,
+                                                 st.k_scales if wl.keys_mx else None, self.seqs, wl.top_k, want_pool,
+                                                 L.idx, pool, self.ws_full, e0, e1, shared_kv=shared, stream=stream)
+                    scan_events.append((e0, e1))
+                elif wl.keys_mx:
                     C.csa2_index_full_mx_scan(L.q_idx, L.w, st.k_codes, st.k_scales, self.seqs, wl.top_k, want_pool,
                                               L.idx, pool, self.ws_full, shared_kv=shared, stream=stream)
                 else:
                     C.csa2_index_full_scan(L.q_idx, L.w, st.k_idx, self.seqs, wl.top_k, want_pool, L.idx, pool,
                                            self.ws_full, shared_kv=shared, stream=stream)
-                if scan_events is not None:
-                    e1.record()
-                    scan_events.append((e0, e1))
                 C.csa2_index_full_select(L.q_idx, L.w, keys, self.seqs, wl.top_k, want_pool, L.idx, pool,
                                          self.ws_full, shared_kv=shared, stream=stream)
                 pool_built = pool_built or want_pool > 0

@@ -213,6 +213,21 @@ int csa2_index_full_mx_scan(const uint16_t* q_idx, const float* w, const uint8_t
                             const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, int32_t top_k,
                             int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
                             int32_t* pool_out, void* ws, size_t ws_bytes, void* stream);
+/*
+ * csa2_index_full_scan_timed -- csa2_index_full_scan (k_scales == NULL: bf16 keys k_idx) or
+ * csa2_index_full_mx_scan (k_scales != NULL: MXFP4 code bytes k_idx and their E8M0 scales), with
+ * the scan kernel's own start and end recorded into two caller events, for timing that kernel
+ * alone (the Full-mode scan of Article "DeepSeek-V4.1-Flash: Pushing KV Cache Compression to 890
+ * Bytes per Token", section IX).  start_event, stop_event: hipEvent_t created by the caller (either
+ * may be NULL: not recorded); the decode scan records them through its launch, a prefill chunk's
+ * scoring kernels are bracketed by two event records on `stream`.  Arguments, workspace, outputs
+ * and errors are those of the untimed calls; on an error nothing is launched or recorded.
+ */
+int csa2_index_full_scan_timed(const uint16_t* q_idx, const float* w, const void* k_idx,
+                               const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, int32_t top_k,
+                               int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
+                               int32_t* pool_out, void* ws, size_t ws_bytes, void* stream,
+                               void* start_event, void* stop_event);
 int csa2_index_reindex_mx(const uint16_t* q_idx, const float* w, const uint8_t* k_codes,
                           const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, const int32_t* pool,
                           int32_t pool_blocks, int32_t block, int32_t top_k, int32_t* idx_out, void* ws,

@@ -166,6 +166,28 @@ def test_index_full_more_queries_than_one_prep_chunk():
         assert np.array_equal(pool[i], rp), i
 
 
+def test_index_full_timed_scan_equals_single_call():
+    # prep -> timed scan (the kernel records its start and end into two events) -> select gives
+    # exactly the single call's selection, and the events bracket a positive interval
+    lengths = [70000, 20000, 4096, 0, 9]
+    case = IndexCase(W_T + 12, lengths, n_heads=4)
+    idx_ref, pool_ref, _ = case.run_full(512, 300)
+    n_q = len(lengths)
+    ws = C.alloc_workspace(C.csa2_workspace_bytes(C.OP_INDEX_FULL, n_q, case.seqs.total_len_ub,
+                                                  case.seqs.max_len_ub, 512, 300))
+    idx = torch.full((n_q, 512), -7, dtype=torch.int32, device=DEV)
+    pool = torch.full((n_q, 300), -7, dtype=torch.int32, device=DEV)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    C.csa2_index_full_prep(case.q_dev, case.w_dev, case.k_dev, case.seqs, 512, 300, idx, pool, ws)
+    C.csa2_index_full_scan_timed(case.q_dev, case.w_dev, case.k_dev, None, case.seqs, 512, 300, idx, pool, ws, e0, e1)
+    C.csa2_index_full_select(case.q_dev, case.w_dev, case.k_dev, case.seqs, 512, 300, idx, pool, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_ref) and torch.equal(pool, pool_ref)
+    assert e0.elapsed_time(e1) > 0.0
+
+
 def test_index_full_tie_heavy_and_repeatable():
     lengths = [3000, 70000, 12345]
     case = IndexCase(W_T + 1, lengths, n_heads=4, qlo=0, qhi=1)   # scores in a narrow integer range
