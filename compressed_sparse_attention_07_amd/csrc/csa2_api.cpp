@@ -337,6 +337,11 @@ int csa2_index_full_scan_timed(const uint16_t* q_idx, const float* w, const void
                                csa2_seqs seqs, int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
                                int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes,
                                void* stream, void* start_event, void* stop_event) {
+    if (start_event != nullptr || stop_event != nullptr) {  // timing launches are not for graph capture
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess) return CSA2_ERR_LAUNCH;
+        if (cap != hipStreamCaptureStatusNone) return CSA2_ERR_UNSUPPORTED;
+    }
     return index_full_phase(q_idx, w, k_idx, k_scales, k_scales != nullptr ? 1 : 0, seqs, n_heads, top_k, block,
                             pool_blocks, shared_kv, idx_out, pool_out, ws, ws_bytes, stream, 2, start_event,
                             stop_event);

@@ -220,8 +220,9 @@ int csa2_index_full_mx_scan(const uint16_t* q_idx, const float* w, const uint8_t
  * alone (the Full-mode scan of Article "DeepSeek-V4.1-Flash: Pushing KV Cache Compression to 890
  * Bytes per Token", section IX).  start_event, stop_event: hipEvent_t created by the caller (either
  * may be NULL: not recorded); the decode scan records them through its launch, a prefill chunk's
- * scoring kernels are bracketed by two event records on `stream`.  Arguments, workspace, outputs
- * and errors are those of the untimed calls; on an error nothing is launched or recorded.
+ * scoring kernels are bracketed by two event records on `stream`.  With an event given, a stream
+ * under graph capture is refused (CSA2_ERR_UNSUPPORTED).  Arguments, workspace, outputs and errors
+ * are otherwise those of the untimed calls; on an error nothing is launched or recorded.
  */
 int csa2_index_full_scan_timed(const uint16_t* q_idx, const float* w, const void* k_idx,
                                const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, int32_t top_k,
