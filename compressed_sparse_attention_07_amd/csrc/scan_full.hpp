@@ -149,14 +149,17 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
                     const int p = pb + 256 * u + 64 * wid + lane;
                     const bool mine = p < n;
                     const uint32_t key = mine ? score_key(sc) : 0u;
+                    // (non-temporal stores here: with 34-byte MXFP4 rows the key writes are an eighth
+                    // of the traffic, and streaming them past the caches measured 11 % faster; the
+                    // bf16 layout below measured slower with them)
                     if (mine) {
-                        ws.keys[key_base + p] = key;
+                        __builtin_nontemporal_store(key, &ws.keys[key_base + p]);
                         atomicAdd(&sh_hist[key >> 21], 1u);
                     }
                     if (want_pool) {
                         const uint32_t bk = max_over_8_lanes(key);  // lanes 8k + 4: block of lanes 8k .. 8k + 7
                         if ((lane & 7) == 4 && p - 4 < n) {
-                            ws.bkeys[key_base / 8 + ((p - 4) >> 3)] = bk;
+                            __builtin_nontemporal_store(bk, &ws.bkeys[key_base / 8 + ((p - 4) >> 3)]);
                             atomicAdd(&sh_bhist[bk >> 21], 1u);
                         }
                     }
