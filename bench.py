@@ -166,7 +166,8 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
     else:
         res["roofline"] = {"bound": "hbm", "achieved": round(res["scan_gbps"], 1), "peak": HBM_PEAK_GBPS,
                            "unit": "GB/s", "frac": round(res["scan_gbps"] / HBM_PEAK_GBPS, 4),
-                           "traffic": read_traffic(wl.name), "kernel": SCAN_KERNEL,
+                           "traffic": read_traffic(wl.name),
+                           "kernel": SCAN_KERNEL + ("_self" if wl.batch <= 64 else ""),
                            "alg_bytes_per_launch": int(scan_bytes_per_launch),
                            "avg_launch_us": round(scan_avg_s * 1e6, 2)}
     res["config"] = {"workload": wl.name, "batch": wl.batch, "context": wl.context, "layers": wl.layers,

@@ -966,7 +966,10 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
     const int scan_keys = !prefill && max_len <= kSelScanMax ? 1 : 0;
     const bool filter = (!prefill || pool_blocks > 0) && !scan_keys;  // a prefill chunk's position lists
                                                                       // are written by its scan
-    if (phase & 1) {
+    // decode calls of at most one wave of queries: the scan derives the metadata itself and
+    // writes what the filter and selection read, so the metadata kernel is not launched
+    const bool self_meta = !prefill && n_q <= kWave;
+    if ((phase & 1) && !self_meta) {
         const int maps = (prefill ? 0 : kMapScan) | (filter ? kMapFilter : 0);
         hipLaunchKernelGGL(k_idx_prep, dim3(1), dim3(kPrepNT), 0, stream, kv_row0, kv_len, n_q, max_len, cache_rows,
                            grid_tiles, grid_ftiles, maps, ws);
@@ -1006,21 +1009,41 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
             int sub_log2 = 0;
             while (sub_log2 < 2 && ((int64_t)grid_tiles << (sub_log2 + 1)) <= scan_workgroups()) ++sub_log2;
             const int wgs = (int)std::min<int64_t>((int64_t)grid_tiles << sub_log2, scan_workgroups());
-            auto kern = sub_log2 == 0
-                            ? (mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true, false>
-                                                  : k_idx_score_full<8, true, false, false>)
-                                  : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0, false>
-                                                  : k_idx_score_full<8, false, false, false>))
-                            : (mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true, true>
-                                                  : k_idx_score_full<8, true, false, true>)
-                                  : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0, true>
-                                                  : k_idx_score_full<8, false, false, true>));
-            if (ev_start != nullptr || ev_stop != nullptr)
-                hipExtLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, ev_start, ev_stop, 0, ws.tmap, ws.qmeta,
-                                      kv_row0, q_idx, w, k_idx, grid_tiles, sub_log2, n_heads, k_sc, pool_blocks, ws);
-            else
-                hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, ws.tmap, ws.qmeta, kv_row0, q_idx, w,
-                                   k_idx, grid_tiles, sub_log2, n_heads, k_sc, pool_blocks, ws);
+            // (kernel variants: key format, head count, lane-per-position layout, split tiles)
+            if (self_meta) {
+                auto pick = [&](auto split) {
+                    constexpr bool S = decltype(split)::value;
+                    return mx ? (n_heads <= 4 ? k_idx_score_full_self<4, true, true, S>
+                                              : k_idx_score_full_self<8, true, false, S>)
+                              : (n_heads <= 4 ? k_idx_score_full_self<4, false, CSA2_SCAN_LP_BF16 != 0, S>
+                                              : k_idx_score_full_self<8, false, false, S>);
+                };
+                auto kern = sub_log2 == 0 ? pick(std::false_type{}) : pick(std::true_type{});
+                const int fmap_out = filter ? 1 : 0;
+                if (ev_start != nullptr || ev_stop != nullptr)
+                    hipExtLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, ev_start, ev_stop, 0, kv_len,
+                                               kv_row0, n_q, max_len, q_idx, w, k_idx, grid_tiles, sub_log2, cache_rows,
+                                               n_heads, k_sc, pool_blocks, grid_ftiles, fmap_out, ws);
+                else
+                    hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, kv_len, kv_row0, n_q, max_len,
+                                       q_idx, w, k_idx, grid_tiles, sub_log2, cache_rows, n_heads, k_sc, pool_blocks,
+                                       grid_ftiles, fmap_out, ws);
+            } else {
+                auto pick = [&](auto split) {
+                    constexpr bool S = decltype(split)::value;
+                    return mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true, S> : k_idx_score_full<8, true, false, S>)
+                              : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0, S>
+                                              : k_idx_score_full<8, false, false, S>);
+                };
+                auto kern = sub_log2 == 0 ? pick(std::false_type{}) : pick(std::true_type{});
+                if (ev_start != nullptr || ev_stop != nullptr)
+                    hipExtLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, ev_start, ev_stop, 0,
+                                               ws.tmap, ws.qmeta, kv_row0, q_idx, w, k_idx, grid_tiles, sub_log2, n_heads,
+                                               k_sc, pool_blocks, ws);
+                else
+                    hipLaunchKernelGGL(kern, dim3(wgs), dim3(kScoreNT), 0, stream, ws.tmap, ws.qmeta, kv_row0, q_idx, w,
+                                       k_idx, grid_tiles, sub_log2, n_heads, k_sc, pool_blocks, ws);
+            }
         }
         if (prefill && ev_stop != nullptr) {
             hipError_t e = hipEventRecord(ev_stop, stream);

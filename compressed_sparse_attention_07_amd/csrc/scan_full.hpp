@@ -26,15 +26,20 @@ namespace csa2 {
 // key, stores, histogram atomics, block maximum) costs a quarter of the instructions of the
 // 16-position layout; the lane reads its own row (16-byte loads, 32 B per MXFP4 row).
 // SPLIT: sub_log2 is honoured (false: one unit per tile, the loop bounds fold to constants).
-// Arguments: the tile map and everything the first loads of a tile need lead (preloaded into
-// SGPRs at launch); ws supplies the output areas.
-template <int HI, bool MX, bool LP, bool SPLIT>
-__global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
-    int32_t* tmap, QMeta* qmeta, const int64_t* __restrict__ kv_row0, const uint16_t* __restrict__ q_idx,
+// SELF: no metadata kernel ran before (decode calls of at most 64 queries).  Every wave
+// derives the per-query tile runs itself, lane i holding query i's, with the same rule as
+// k_idx_prep (max(1, ceil(n_i / tile)) consecutive tiles per query, clamped to the host's
+// grid bound), finds a tile's query by a ballot over the run starts, and the workgroups write
+// the per-query metadata and the filter pass's tile map for the kernels that follow.  One
+// dependent load (length and rows) then precedes the first key loads, instead of two (tile
+// map, then metadata), and the metadata kernel's launch is saved.
+template <int HI, bool MX, bool LP, bool SPLIT, bool SELF>
+__device__ __forceinline__ void score_full_body(
+    const int32_t* __restrict__ tmap, QMeta* __restrict__ qmeta, const int64_t* __restrict__ kv_row0,
+    const int32_t* __restrict__ kv_len,
+    int n_q, int32_t max_len, int64_t cache_rows, int grid_ftiles, int fmap_out, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w, const void* __restrict__ k_idx, int grid_tiles, int sub_log2, int n_heads,
-    const uint8_t* __restrict__ k_sc, int pool_blocks, IndexWs ws) {
-    ws.tmap = tmap;
-    ws.qmeta = qmeta;
+    const uint8_t* __restrict__ k_sc, int pool_blocks, const IndexWs& ws) {
     __shared__ uint32_t sh_hist[kHistBins];
     __shared__ uint32_t sh_bhist[kHistBins];
 
@@ -48,6 +53,49 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     const int ub = (int)((int64_t)blockIdx.x * units / gridDim.x);
     const int ue = (int)((int64_t)(blockIdx.x + 1) * units / gridDim.x);
     const int unit_len = kFullTile >> sub_log2;  // positions per unit
+
+    // SELF: lane i's copy of query i's metadata (lanes past n_q: a start no tile reaches)
+    int lm_n = 0, lm_start = INT32_MAX, lm_ntiles = 0, lm_fstart = INT32_MAX, lm_fntiles = 0;
+    int64_t lrow0 = 0;
+    int used_s = 0, used_f = 0;  // scan / filter tiles owned by some query; the rest of each bound is unused
+    if constexpr (SELF) {
+        // the lengths and rows come in through scalar loads (uniform addresses), 8 queries per
+        // round, and lane i keeps query i's: every wave of the grid reads the same few lines, and
+        // the scalar caches absorb that, where vector loads from thousands of waves queue at
+        // the same L2 lines (measured ~10 us later first key loads on a grid of 1,024 workgroups)
+        int32_t len = 0;
+        for (int q0 = 0; q0 < n_q; q0 += 8) {
+            int32_t lq[8];
+            int64_t rq[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int q = min(q0 + j, n_q - 1);
+                lq[j] = kv_len[q];
+                rq[j] = kv_row0[q];
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (lane == q0 + j) {
+                    len = lq[j];
+                    lrow0 = rq[j];
+                }
+        }
+        const int n = lane < n_q ? eff_len_of(len, lrow0, max_len, cache_rows) : 0;
+        const int ts = (int)(((int64_t)n + kFullTile - 1) / kFullTile);
+        const int tf = (int)(((int64_t)n + kFilterTile - 1) / kFilterTile);
+        const int xs = ts > 1 ? ts - 1 : 0, xf = tf > 1 ? tf - 1 : 0;  // tiles beyond each query's first
+        const int in_s = wave_inclusive_scan(xs), in_f = wave_inclusive_scan(xf);
+        const int cap_s = grid_tiles - n_q, cap_f = grid_ftiles - n_q;
+        const int p0 = min(cap_s, in_s - xs), p1 = min(cap_s, in_s);
+        const int f0 = min(cap_f, in_f - xf), f1 = min(cap_f, in_f);
+        lm_start = lane < n_q ? lane + p0 : INT32_MAX;
+        lm_ntiles = 1 + (p1 - p0);
+        lm_fstart = lane < n_q ? lane + f0 : INT32_MAX;
+        lm_fntiles = 1 + (f1 - f0);
+        lm_n = (int)min((int64_t)n, min((int64_t)lm_ntiles * kFullTile, (int64_t)lm_fntiles * kFilterTile));
+        used_s = n_q + min(cap_s, __builtin_amdgcn_readlane(in_s, 63));
+        used_f = n_q + min(cap_f, __builtin_amdgcn_readlane(in_f, 63));
+    }
 
     for (int b = t; b < kHistBins; b += kScoreNT) {
         sh_hist[b] = 0u;
@@ -84,8 +132,15 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
     for (int unit = ub; unit < ue; ++unit) {
         const int tile = unit >> sub_log2;
         const int b_lo = (unit & ((1 << sub_log2) - 1)) * unit_len, b_hi = b_lo + unit_len;
-        const int i = ws.tmap[tile];
-        if (i < 0) break;  // unused tiles sit at the end of the map
+        int i;
+        if constexpr (SELF) {
+            if (tile >= used_s) break;  // unused tiles sit at the end of the grid bound
+            // the owner is the last query whose run starts at or before the tile (starts ascend)
+            i = 63 - __builtin_clzll(__ballot(lm_start <= tile));
+        } else {
+            i = tmap[tile];
+            if (i < 0) break;  // unused tiles sit at the end of the map
+        }
         if (i != cur) {
             __syncthreads();  // every wave's counts of `cur` are in LDS (and the clearing above)
             if (cur >= 0) {
@@ -93,8 +148,15 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
                 __syncthreads();
             }
             cur = i;
-            qm = ws.qmeta[i];
-            row0 = kv_row0[i];
+            if constexpr (SELF) {
+                qm.n = __builtin_amdgcn_readlane(lm_n, i);
+                qm.start = __builtin_amdgcn_readlane(lm_start, i);
+                row0 = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(lrow0 >> 32), i) << 32) |
+                                 (uint32_t)__builtin_amdgcn_readlane((int)lrow0, i));
+            } else {
+                qm = qmeta[i];
+                row0 = kv_row0[i];
+            }
             if constexpr (LP)
                 load_qfrag_lp(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
             else
@@ -215,6 +277,54 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
         __syncthreads();
         flush();
     }
+    if constexpr (SELF) {
+        // what k_idx_prep would have written for the kernels that follow: the per-query
+        // metadata (first workgroup) and the filter pass's tile -> query map (one entry per
+        // thread, from the first workgroups on)
+        if (blockIdx.x == 0 && t < n_q) {
+            int4* m = reinterpret_cast<int4*>(qmeta + t);  // QMeta: n, start, ntiles, fstart, fntiles, pad
+            m[0] = make_int4(lm_n, lm_start, lm_ntiles, lm_fstart);
+            m[1] = make_int4(lm_fntiles, 0, 0, 0);
+        }
+        if (fmap_out) {
+            for (int k0 = blockIdx.x * kScoreNT; k0 < grid_ftiles; k0 += gridDim.x * kScoreNT) {  // (uniform)
+                const int k = k0 + t;
+                // last query whose filter run starts at or before k (binary lifting over the lanes'
+                // ascending starts; lanes past n_q hold INT32_MAX; every lane takes part)
+                int lo = 0;
+                for (int step = 32; step > 0; step >>= 1) {
+                    const int fs = __shfl(lm_fstart, lo + step);
+                    if (fs <= k) lo += step;
+                }
+                if (k < grid_ftiles) ws.fmap[k] = k < used_f ? lo : -1;
+            }
+        }
+    }
+}
+
+// Tile map and metadata from k_idx_prep.  The tile map and everything the first loads of a
+// tile need lead the arguments (preloaded into SGPRs at launch); ws supplies the output areas.
+template <int HI, bool MX, bool LP, bool SPLIT>
+__global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
+    const int32_t* tmap, QMeta* qmeta, const int64_t* __restrict__ kv_row0, const uint16_t* __restrict__ q_idx,
+    const float* __restrict__ w, const void* __restrict__ k_idx, int grid_tiles, int sub_log2, int n_heads,
+    const uint8_t* __restrict__ k_sc, int pool_blocks, IndexWs ws) {
+    score_full_body<HI, MX, LP, SPLIT, false>(tmap, qmeta, kv_row0, nullptr, 0, 0, 0, 0, 0, q_idx, w, k_idx,
+                                              grid_tiles, sub_log2, n_heads, k_sc, pool_blocks, ws);
+}
+
+// Metadata derived in the kernel (at most 64 queries, no metadata kernel before it): the
+// lengths, rows and query count lead the arguments, so the first loads wait on nothing else.
+// fmap_out != 0: the filter pass runs next and reads its tile map from ws.fmap.
+template <int HI, bool MX, bool LP, bool SPLIT>
+__global__ __launch_bounds__(kScoreNT) void k_idx_score_full_self(
+    const int32_t* __restrict__ kv_len, const int64_t* __restrict__ kv_row0, int n_q, int32_t max_len,
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int grid_tiles,
+    int sub_log2, int64_t cache_rows, int n_heads, const uint8_t* __restrict__ k_sc, int pool_blocks,
+    int grid_ftiles, int fmap_out, IndexWs ws) {
+    score_full_body<HI, MX, LP, SPLIT, true>(nullptr, ws.qmeta, kv_row0, kv_len, n_q, max_len, cache_rows,
+                                             grid_ftiles, fmap_out, q_idx, w, k_idx, grid_tiles, sub_log2, n_heads,
+                                             k_sc, pool_blocks, ws);
 }
 
 }  // namespace csa2

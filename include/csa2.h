@@ -157,8 +157,10 @@ int csa2_index_full(const uint16_t* q_idx, const float* w, const uint16_t* k_idx
 /*
  * The three parts of csa2_index_full, for callers that time or schedule them apart:
  * _prep writes per-query metadata and the tile maps the later kernels read to the
- * workspace (one kernel); _scan scores every visible position (fused block maxima and
- * first-digit histograms, one kernel); _select compacts the threshold buckets and writes
+ * workspace (one kernel; a decode call of at most 64 queries launches nothing here, its
+ * scan kernel derives the metadata itself and writes what the later kernels read);
+ * _scan scores every visible position (fused block maxima and first-digit histograms,
+ * one kernel); _select compacts the threshold buckets and writes
  * idx_out and pool_out (two kernels: a filter over all positions, then one workgroup per
  * query and output; decode calls whose contexts are all at most 16,384 positions skip
  * the filter, the selection workgroups then read the keys themselves).  Call them in this order, on the same stream, with identical

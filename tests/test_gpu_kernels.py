@@ -166,6 +166,23 @@ def test_index_full_more_queries_than_one_prep_chunk():
         assert np.array_equal(pool[i], rp), i
 
 
+@pytest.mark.parametrize("n_q", [64, 65])
+def test_index_full_one_wave_of_queries_and_one_more(n_q):
+    # 64 decode queries: the scan derives the tile runs itself and writes the metadata and the
+    # filter map the later kernels read; 65: the metadata kernel does.  Both bit-exact, with
+    # empty, single-tile and many-filter-tile contexts in one call.
+    rng = np.random.default_rng(27 + n_q)
+    lengths = [int(x) for x in rng.integers(0, 9000, size=n_q)]
+    lengths[0], lengths[5], lengths[31], lengths[n_q - 1] = 0, 41000, 0, 70001
+    case = IndexCase(W_T + 13 + n_q, lengths, n_heads=4)
+    idx, pool, _ = case.run_full(512, 300)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for i in sorted({0, 1, 5, 30, 31, 32, 62, 63, n_q - 1} | set(range(0, n_q, 9))):
+        ri, rp = case.oracle_full(i, 512, 300)
+        assert np.array_equal(idx[i], ri), (n_q, i, lengths[i])
+        assert np.array_equal(pool[i], rp), (n_q, i, lengths[i])
+
+
 def test_index_full_timed_scan_equals_single_call():
     # prep -> timed scan (the kernel records its start and end into two events) -> select gives
     # exactly the single call's selection, and the events bracket a positive interval
