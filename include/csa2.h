@@ -242,10 +242,16 @@ int csa2_index_reindex_mx(const uint16_t* q_idx, const float* w, const uint8_t* 
  * [Article] sections VIII-IX (Reindex reuses main KV and indexer K, runs its own
  * selection inside the shared pool); [Summary] Technical Approach.
  *
- *   pool    device int32 [n_q, pool_blocks]: block ids from csa2_index_full; -1
- *           entries and ids whose positions fall outside [0, N_i) contribute nothing.
+ *   pool    device int32 [n_q, pool_blocks]: block ids in ascending order, as
+ *           csa2_index_full writes them; -1 entries (anywhere in the row) and ids whose
+ *           positions fall outside [0, N_i) contribute nothing.
  *   Other arguments as in csa2_index_full.  idx_out gets the top_k candidate
  *   positions under (score desc, position asc), ascending, -1 padded.
+ * The kernels take a pool row's element order for position order (ties at the threshold
+ * score go to the earlier element, and idx_out lists the selection in element order), which
+ * is what the ranking above needs when the row is ascending.  A row in any other order is not
+ * an error: its selection is the top_k candidates under (score desc, element order asc),
+ * written in element order.
  */
 int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
                        int32_t n_heads, const int32_t* pool, int32_t pool_blocks, int32_t block,

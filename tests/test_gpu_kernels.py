@@ -247,7 +247,7 @@ def test_index_prefill_mfma_causal_bit_exact(n_heads, top_k):
     C_, T = 5900, 100
     case = SharedIndexCase(W_T + 40 + n_heads, C_ + T, C_ + 1 + np.arange(T), n_heads=n_heads)
     idx_m, _, _ = case.run_full(top_k, 0, shared_kv=1)
-    idx_v, _, _ = case.run_full(top_k, 0, shared_kv=0)          # decode VALU path on the same data
+    idx_v, _, _ = case.run_full(top_k, 0, shared_kv=0)          # per-query decode path on the same data
     idx_m, idx_v = idx_m.cpu().numpy(), idx_v.cpu().numpy()
     assert np.array_equal(idx_m, idx_v)
     for t in list(range(0, T, 9)) + [T - 1]:
@@ -404,6 +404,19 @@ def test_index_reindex_pool_with_padding_and_out_of_range_blocks():
     idx = idx.cpu().numpy()
     for i in range(2):
         assert np.array_equal(idx[i], case.oracle_reindex(i, pool[i], 100)), i
+
+
+def test_index_reindex_unsorted_pool_follows_element_order():
+    # The header documents an ascending pool (as csa2_index_full writes it); for a row in any
+    # other order the selection is the top_k candidates under (score desc, element order asc),
+    # written in element order.  Scores from {-1, 0, 1} inputs tie a lot, so the order decides.
+    case = IndexCase(W_T + 6, [4000], n_heads=4, qlo=-1, qhi=1)
+    blocks = np.random.default_rng(6).permutation(500)[:64].astype(np.int32)   # not ascending
+    idx, _ = case.run_reindex(torch.from_numpy(blocks[None].copy()).to(DEV), 100)
+    cand = np.concatenate([b * 8 + np.arange(8) for b in blocks])
+    s = O.index_scores(case.q[0], case.w[0], case.k[cand])
+    chosen = np.sort(np.lexsort((np.arange(cand.size), -s))[:100])           # element positions
+    assert np.array_equal(idx.cpu().numpy()[0], cand[chosen])
 
 
 @pytest.mark.parametrize("pool_blocks,top_k,window", [(2048, 512, 128), (300, 64, 0), (3000, 512, 128), (1, 4, 16)])
