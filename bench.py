@@ -1,24 +1,27 @@
 """Benchmark of the CSA2 hot path on one MI355X.
 
-A step = one decode step of a workload: the step's FP4 append for every owned KV set, then
-every layer in order (Full: scan + select; Reindex; Reuse: none), each followed by its
-gather-dequant attention.  Inputs are synthetic and already resident in HBM when the timed
+A step = one decode step of a workload: the step's own token written to every owned KV set (FP4
+row + indexer key, one launch per set), then every layer in order (Full: scan + select; Reindex;
+Reuse: none), each followed by its gather-dequant attention, which also writes that layer's own
+window entry for the token.  Inputs are synthetic and already resident in HBM when the timed
 region starts.
 
 Prints ONE JSON line.  `value` is decode tokens/s of the batched 64K-context workload
 (32 sequences x 65,536 positions, 8 layers F R R R U U U U), timed over K replays of the step
 captured in HIP graphs (the host issues one launch per step); the 1M-context workload (8 x 2^20,
-20 layers) is reported in the same line under "also".  `roofline` covers the dominant kernel
-(the Full-mode scan), timed with HIP events its own launches record at the kernel's start and end,
-in K eager steps.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.  "also" further
-holds the 1M-context workload in the pages' storage formats: an FP8 window store with SWA Bounded
-Replay starts, MXFP4 indexer keys, and both together; and the two prefill chunks (one Full
-layer; Full with per-token pools + 2 Reindex + 1 Reuse), as chunk tokens/s; the single 4K-context
-sequence; and the ragged mix of 64 sequences (1K to 1M contexts, F U F U, two appends per
-sequence and step).  The 64K workload
-rotates two device copies of its inputs so that no step re-reads data a 256 MiB last-level
-cache could still hold.
+20 layers) is reported in the same line under "also".  `kernels` lists the step's timed kernels
+(the Full scan, the Reindex selection pair, the attention), each timed with HIP events its own
+launches record at the kernel's start and end in K eager steps, with its share of the step, its
+algorithmic GB/s and its fraction of HBM peak; `roofline` is the entry with the largest share.
+`kv_gather` is the attention's cache gathers (72 B per selected FP4 entry, 256 B per bf16 window
+entry) per launch over the attention kernel's duration.  `bulk_append` times fp4_kv_append of
+2^20 tokens; `stream_ceiling` a plain 1 GiB device copy and a 1 GiB read-only reduction (torch),
+the rates this HBM delivers in practice.  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload on the host's cores.  "also" further holds the 1M-context workload in
+the pages' storage formats (FP8 window with SWA Bounded Replay, MXFP4 indexer keys, both), the two
+prefill chunks (chunk tokens/s, MFMA roofline of the scoring), the single 4K-context sequence and
+the ragged mix of 64 sequences.  The 64K workload rotates two device copies of its inputs so that
+no step re-reads data a 256 MiB last-level cache could still hold.
 
   python bench.py [--steps K] [--warmup W] [--workload 1] [--also 2,5,6,7,3,8,0,4] [--no-cpu-baseline]
   python bench.py --mode copy      # plain 1 GiB device copy, for counter calibration
@@ -26,11 +29,11 @@ cache could still hold.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -40,37 +43,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 METRIC = "CSA2 decode tokens/s at 64K & 1M ctx; KV gather GB/s vs HBM peak"
-SCAN_KERNEL = "k_idx_score_full"
-SCAN_SOURCES = ["compressed_sparse_attention_07_amd/csrc/scan_full.hpp",
-                "compressed_sparse_attention_07_amd/csrc/scan_common.hpp",
-                "compressed_sparse_attention_07_amd/csrc/csa2_device.hpp",
-                "compressed_sparse_attention_07_amd/build.py"]  # (compiler flags change the code too)
-
-
-def source_sha(paths) -> str:
-    h = hashlib.sha256()
-    for p in paths:
-        h.update(open(os.path.join(ROOT, p), "rb").read())
-    return h.hexdigest()[:16]
-
-
-def read_traffic(workload_name: str):
-    """HBM bytes per scan launch from the committed counter summary, if it was taken on the
-    current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{SCAN_KERNEL}_{workload_name}.md")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    for line in open(path):
-        if ":" in line and line.strip().startswith("- "):
-            k, v = line.strip()[2:].split(":", 1)
-            kv[k.strip()] = v.strip().strip("`")
-    if kv.get("source_sha256") != source_sha(SCAN_SOURCES):
-        return None
-    try:
-        return float(kv["hbm_bytes_per_dispatch"])
-    except (KeyError, ValueError):
-        return None
+DTYPE = "f16/bf16 MFMA, fp32 accumulate"
+STORAGE = ("main KV FP4 (E2M1 + E4M3 per 16 ch); indexer keys bf16 (MXFP4 in the mxkeys workloads); "
+           "window bf16 (E4M3 in the fp8win workloads); scores, softmax and outputs fp32")
+KERNEL_NAMES = {"scan": "k_idx_score_full", "reindex": "k_idx_reindex_score + k_idx_reindex_select",
+                "attend": "k_attend"}
 
 
 _SLEEP_CYCLES_PER_S = None
@@ -90,7 +67,7 @@ def gpu_busy_wait(torch, seconds: float) -> None:
 
 
 def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
-    """Eager pass (HIP events recorded by every Full scan launch -> the scan kernel's average duration),
+    """Eager pass with every timed kernel recording its own start and end (average durations),
     then the timed region proper: `steps` replays of the step captured in HIP graphs."""
     import torch
     from compressed_sparse_attention_07_amd import workloads as W
@@ -106,20 +83,20 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
         r.step()
     t_host = (time.perf_counter() - t_host) / max(warmup, 1)  # host time to issue one step (upper bound)
     torch.cuda.synchronize()
-    # eager steps, scan kernel timed with events on the stream it runs on
-    ev = []
     t0 = time.perf_counter()
     for _ in range(steps):
         r.step()
     torch.cuda.synchronize()
     eager_s = time.perf_counter() - t0
-    # the same steps again with each Full-scan launch recording its start and end into an event
-    # pair; a GPU-side wait in front lets the host issue every step before the GPU starts
+    # the same steps again with the timed kernels recording their own start and end; a GPU-side
+    # wait in front lets the host issue every step before the GPU starts
+    timing = {}
     gpu_busy_wait(torch, 1.5 * steps * t_host + 2e-3)
     for _ in range(steps):
-        r.step(scan_events=ev)
+        r.step(timing=timing)
     torch.cuda.synchronize()
-    scan_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_us = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) * 1e3 for k, v in timing.items()}
+    per_step = {k: len(v) / steps for k, v in timing.items()}
     # graph replays: the timed region
     graphs = r.capture()
     for k in range(warmup):
@@ -133,9 +110,7 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
     del graphs
     tokens_per_step = wl.prefill_chunk or wl.batch
     alg = r.algorithmic_bytes()
-    n_full = wl.layers.count("F")
-    scan_bytes_per_launch = alg["index_full"] / max(n_full, 1)
-    scan_avg_s = float(np.mean(scan_ms)) / 1e3
+    kb = r.kernel_bytes()
     ms_step = elapsed * 1e3 / steps
     res = {
         "workload": wl.name,
@@ -144,36 +119,104 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
         "eager_tokens_per_s": tokens_per_step * steps / eager_s,
         "alg_bytes_per_step": int(sum(alg.values())),
         "alg_gbps_step": sum(alg.values()) / (ms_step / 1e3) / 1e9,
-        "scan_avg_us": scan_avg_s * 1e6,
-        "scan_alg_bytes_per_launch": int(scan_bytes_per_launch),
-        "scan_gbps": scan_bytes_per_launch / scan_avg_s / 1e9,
-        "scan_launches_timed": len(scan_ms),
         "input_copies": copies,
     }
+    kernels = []
+    for k in ("scan", "reindex", "attend"):
+        if k not in avg_us:
+            continue
+        e = {"kernel": KERNEL_NAMES[k], "family": k, "avg_launch_us": round(avg_us[k], 2),
+             "launches_per_step": per_step[k], "share_of_step": round(avg_us[k] * per_step[k] / (ms_step * 1e3), 4)}
+        if not wl.prefill_chunk:
+            gbps = kb[k] / (avg_us[k] / 1e6) / 1e9
+            e.update({"alg_bytes_per_launch": kb[k], "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+        kernels.append(e)
+    res["kernels"] = kernels
+    if "attend" in avg_us and not wl.prefill_chunk:
+        g = kb["kv_gather"] / (avg_us["attend"] / 1e6) / 1e9
+        res["kv_gather"] = {"gbps": round(g, 1), "frac": round(g / HBM_PEAK_GBPS, 4),
+                            "bytes_per_launch": kb["kv_gather"], "avg_launch_us": round(avg_us["attend"], 2)}
     if wl.prefill_chunk:
         # A prefill chunk's per-query key bytes are re-reads of one shared key array (from the
-        # caches), not HBM traffic, so no HBM rate is derived from them; its scan is one dense
+        # caches), not HBM traffic, so no HBM rate is derived from them; its scoring is one dense
         # contraction (all queries x all visible positions x heads x 64) priced against MFMA.
-        for k in ("alg_gbps_step", "scan_gbps", "alg_bytes_per_step", "scan_alg_bytes_per_launch"):
+        for k in ("alg_gbps_step", "alg_bytes_per_step"):
             res[k] = None
         res["hbm_note"] = "prefill: MFMA-bound; per-query key bytes are cache re-reads, no HBM rate given"
         flops = 2.0 * 64 * wl.idx_heads * float(r.q_len.sum())
-        tflops = flops / scan_avg_s / 1e12
+        scan_s = avg_us["scan"] / 1e6
+        tflops = flops / scan_s / 1e12
         res["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                           "kernel": "k_idx_score_prefill", "alg_flops_per_launch": flops,
-                           "avg_launch_us": round(scan_avg_s * 1e6, 2)}
+                           "kernel": "k_idx_score_prefill (both passes)", "alg_flops_per_launch": flops,
+                           "avg_launch_us": round(avg_us["scan"], 2)}
     else:
-        res["roofline"] = {"bound": "hbm", "achieved": round(res["scan_gbps"], 1), "peak": HBM_PEAK_GBPS,
-                           "unit": "GB/s", "frac": round(res["scan_gbps"] / HBM_PEAK_GBPS, 4),
-                           "traffic": read_traffic(wl.name),
-                           "kernel": SCAN_KERNEL + ("_self" if wl.batch <= 64 else ""),
-                           "alg_bytes_per_launch": int(scan_bytes_per_launch),
-                           "avg_launch_us": round(scan_avg_s * 1e6, 2)}
+        dom = max(kernels, key=lambda e: e["share_of_step"])
+        res["roofline"] = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": dom["frac"], "traffic": None, "kernel": dom["kernel"],
+                           "share_of_step": dom["share_of_step"], "alg_bytes_per_launch": dom["alg_bytes_per_launch"],
+                           "avg_launch_us": dom["avg_launch_us"]}
     res["config"] = {"workload": wl.name, "batch": wl.batch, "context": wl.context, "layers": wl.layers,
                      "top_k": wl.top_k, "pool_blocks": wl.pool_blocks, "window": wl.window,
                      "query_heads": wl.heads, "indexer_heads": wl.idx_heads}
     return r, res
+
+
+def bulk_append(reps: int = 10) -> dict:
+    """fp4_kv_append of 2^20 post-RoPE tokens (128 channels) in one call, timed with events around
+    each call; two input copies alternate so no call re-reads a 256 MiB last-level cache."""
+    import torch
+    from compressed_sparse_attention_07_amd import csa2 as C, synth
+
+    n = 1 << 20
+    sig = synth.channel_sigma(4, synth.T_KV_SIGMA, 128, seq=99)
+    xs = [torch.from_numpy(synth.kv_bf16(4, synth.T_KV, n, 128, sig, seq=99 + k).view(np.int16))
+          .view(torch.bfloat16).cuda() for k in range(2)]
+    codes = torch.empty((n, 64), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, 8), dtype=torch.uint8, device="cuda")
+    for k in range(2):
+        C.fp4_kv_append(xs[k], codes, scales)
+    torch.cuda.synchronize()
+    ms = []
+    for k in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        C.fp4_kv_append(xs[k % 2], codes, scales)
+        b.record()
+        ms.append((a, b))
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ms])) * 1e3
+    nbytes = n * (256 + 72)
+    gbps = nbytes / (us / 1e6) / 1e9
+    return {"tokens": n, "avg_call_us": round(us, 2), "alg_bytes": nbytes, "gbps": round(gbps, 1),
+            "frac": round(gbps / HBM_PEAK_GBPS, 4), "kernel": "k_fp4_pack128",
+            "timing": "events recorded around each call on its stream (2 alternating inputs)"}
+
+
+def stream_ceiling() -> dict:
+    """What the HBM delivers to plain streaming kernels in this run: a 1 GiB device copy (read +
+    write) and a 1 GiB read-only reduction, both torch kernels, best of 5."""
+    import torch
+    nbytes = 1 << 30
+    x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, moved in (("copy", lambda: y.copy_(x), 2 * nbytes), ("read", lambda: x.sum(), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        best = 1e9
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b) / 1e3)
+        out[f"{name}_gbps"] = round(moved / best / 1e9, 1)
+    out["frac_of_peak"] = {k: round(v / HBM_PEAK_GBPS, 4) for k, v in out.items()}
+    del x, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def _oracle_step(O, r, i, caches, select_only=False):
@@ -202,16 +245,21 @@ def _oracle_step(O, r, i, caches, select_only=False):
 
 def cpu_baseline(r, n_seq: int, min_seconds: float = 10.0) -> dict:
     """The CPU oracle, as it stands, on n_seq sequences of the workload's decode step, repeated
-    until at least min_seconds of CPU time have been measured."""
+    until at least min_seconds of wall time have been measured.  The sequences are independent:
+    one worker thread per host core of this process's affinity set takes them from a pool (BLAS
+    held to one thread per worker; numpy releases the interpreter lock in its array kernels, the
+    oracle's Python loops do not, so the threads overlap only partly)."""
     import oracle as O
     from threadpoolctl import threadpool_limits
 
     h = r.host
+    workers = max(1, min(len(os.sched_getaffinity(0)), n_seq))
     with threadpool_limits(limits=1):
         # Cache state before the step (exists before a step, so not timed): the oracle's own
         # quantisation of the rows this step attends, found by an untimed selection pass.
         caches = [[None] * n_seq for _ in r.sets]
-        for i in range(n_seq):
+
+        def prepare(i):
             r0, n = int(r.q_row0[i]), int(r.q_len[i])
             used = _oracle_step(O, r, i, None, select_only=True)
             for s in range(len(r.sets)):
@@ -221,16 +269,19 @@ def cpu_baseline(r, n_seq: int, min_seconds: float = 10.0) -> dict:
                 if rows.size:
                     codes[rows], scales[rows] = O.fp4_quantize(h["x"][s][r0 + rows])
                 caches[s][i] = (codes, scales)
-        reps, t = 0, 0.0
-        while t < min_seconds:
-            t0 = time.perf_counter()
-            for i in range(n_seq):
-                _oracle_step(O, r, i, caches)
-            t += time.perf_counter() - t0
-            reps += 1
-    return {"value": reps * n_seq / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(prepare, range(n_seq)))
+            reps, t = 0, 0.0
+            while t < min_seconds:
+                t0 = time.perf_counter()
+                list(ex.map(lambda i: _oracle_step(O, r, i, caches), range(n_seq)))
+                t += time.perf_counter() - t0
+                reps += 1
+    return {"value": reps * n_seq / t, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": f"{reps} x the decode step of {n_seq} of {r.wl.batch} sequences of {r.wl.name} "
-                      f"(all {len(r.wl.layers)} layers), {t:.1f} s on 1 host thread"}
+                      f"(all {len(r.wl.layers)} layers), {t:.1f} s wall on {workers} worker threads "
+                      f"(one per core of the affinity set)"}
 
 
 def copy_mode(nbytes: int = 1 << 30, reps: int = 5) -> None:
@@ -258,6 +309,7 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--also", type=str, default="2,5,6,7,3,8,0,4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the bulk append and streaming ceilings")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     ap.add_argument("--mode", choices=["bench", "copy"], default="bench")
     args = ap.parse_args()
@@ -280,8 +332,16 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(r, min(args.cpu_seqs, r.wl.batch))
+        print(f"[bench] cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads", file=sys.stderr,
+              flush=True)
     del r
     torch.cuda.empty_cache()
+    extras = {}
+    if not args.no_extras:
+        extras["bulk_append"] = bulk_append()
+        extras["stream_ceiling"] = stream_ceiling()
+        print(f"[bench] bulk append {extras['bulk_append']['gbps']} GB/s, ceiling {extras['stream_ceiling']}",
+              file=sys.stderr, flush=True)
     also = []
     for w in [int(x) for x in args.also.split(",") if x.strip()]:
         rr, res = measure(w, max(3, args.steps // 2), args.warmup, copies=2 if w in (0, 1) else 1)
@@ -290,6 +350,7 @@ def main() -> int:
         res["step_frac_of_hbm_peak"] = (round(res["alg_gbps_step"] / HBM_PEAK_GBPS, 4)
                                         if res["alg_gbps_step"] is not None else None)
         also.append(res)
+        print(f"[bench] {res['workload']}: {res['ms_per_step']:.4f} ms/step", file=sys.stderr, flush=True)
 
     line = {
         "metric": METRIC,
@@ -302,18 +363,22 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": DTYPE,
+        "storage": STORAGE,
         "data": "synthetic",
         "config": main_res["config"],
         "roofline": main_res["roofline"],
+        "kernels": main_res["kernels"],
+        "kv_gather": main_res.get("kv_gather"),
         "step_alg_gbps": (round(main_res["alg_gbps_step"], 1) if main_res["alg_gbps_step"] is not None else None),
-        "eager_tokens_per_s": round(main_res["eager_tokens_per_s"], 1),
-        "input_copies": main_res["input_copies"],
-        "timing": "value: K replays of the step captured in HIP graphs; roofline: HIP events recorded by "
-                  "each Full-scan kernel's own launch at its start and end (csa2_index_full_scan_timed), "
-                  "in K eager steps issued behind a GPU-side wait",
         "step_frac_of_hbm_peak": (round(main_res["alg_gbps_step"] / HBM_PEAK_GBPS, 4)
                                   if main_res["alg_gbps_step"] is not None else None),
+        "eager_tokens_per_s": round(main_res["eager_tokens_per_s"], 1),
+        "input_copies": main_res["input_copies"],
+        "timing": "value: K replays of the step captured in HIP graphs; kernels and roofline: HIP events that "
+                  "each timed kernel's own launch records at its start and end (csa2_timing.h), in K eager "
+                  "steps issued behind a GPU-side wait",
+        **extras,
         "cpu_baseline": cpu,
         "also": also,
     }

@@ -33,10 +33,14 @@ EXPORTS = (
     "csa2_index_full_mx",
     "csa2_index_full_mx_scan",
     "csa2_index_full_scan_timed",
+    "csa2_index_reindex_timed",
+    "csa2_attend_timed",
     "csa2_index_reindex_mx",
     "csa2_attend",
     "csa2_attend_fp8win",
     "csa2_reindex_attend",
+    "csa2_token_append",
+    "csa2_window_append",
     "csa2_workspace_bytes",
     "csa2_workspace_init",
     "csa2_status_string",
@@ -78,7 +82,7 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).argtypes = [vp, vp, vp, SeqsC, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
             getattr(L, name).restype = ctypes.c_int
         L.csa2_index_reindex.argtypes = [vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
-        L.csa2_attend.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, i32, f32, vp, vp, sz, vp]
+        L.csa2_attend.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp]
         L.fp8_window_append.argtypes = [vp, i64, i32, vp, i64, vp, i64, vp]
         L.mxfp4_key_append.argtypes = [vp, i64, i32, vp, i64, vp, vp, i64, vp]
         for name in ("csa2_index_full_mx", "csa2_index_full_mx_scan"):
@@ -86,10 +90,15 @@ def lib() -> ctypes.CDLL:
         L.csa2_index_reindex_mx.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
         L.csa2_index_full_scan_timed.argtypes = [vp, vp, vp, vp, SeqsC, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp,
                                                  vp, vp]
-        L.csa2_attend_fp8win.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp,
-                                         sz, vp]
+        L.csa2_attend_fp8win.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, vp, i32, f32, vp,
+                                         vp]
         L.csa2_reindex_attend.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp,
-                                          i32, i64, i32, vp, i32, f32, vp, vp, sz, vp]
+                                          i32, i64, i32, vp, vp, i32, f32, vp, vp, sz, vp]
+        L.csa2_token_append.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, vp]
+        L.csa2_index_reindex_timed.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp, vp, vp]
+        L.csa2_attend_timed.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp, vp,
+                                        vp]
+        L.csa2_window_append.argtypes = [vp, i64, vp, i64, vp, i32, i64, vp]
         L.csa2_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
         L.csa2_workspace_bytes.restype = sz
         L.csa2_workspace_init.argtypes = [vp, sz, vp]
@@ -99,7 +108,8 @@ def lib() -> ctypes.CDLL:
         for name in ("fp4_kv_append", "fp8_window_append", "csa2_index_full", "csa2_index_reindex", "csa2_attend",
                      "csa2_attend_fp8win", "csa2_workspace_init", "csa2_version", "mxfp4_key_append",
                      "csa2_index_full_mx", "csa2_index_full_mx_scan", "csa2_index_reindex_mx", "csa2_reindex_attend",
-                     "csa2_index_full_scan_timed"):
+                     "csa2_index_full_scan_timed", "csa2_token_append", "csa2_window_append",
+                     "csa2_index_reindex_timed", "csa2_attend_timed"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -224,38 +234,54 @@ def csa2_index_reindex(q_idx, w, k_idx, seqs: Seqs, pool, top_k: int, idx_out, w
 
 
 def csa2_attend(q, codes, scales, seqs: Seqs, idx, swa, swa_row0, swa_cap: int, window: int,
-                softmax_scale: float, out, ws, stream=None) -> None:
+                softmax_scale: float, out, win_new=None, stream=None) -> None:
+    """Attention over the selected FP4 entries and the bf16 window; win_new (bf16 [n_q, 128] or
+    None): the new token's window vector, attended as position N - 1 and written to its row."""
     n_heads = q.shape[1]
     top_k = idx.shape[1] if idx is not None else 0
     swa_rows = swa.shape[0] if swa is not None else 0
     _check("csa2_attend", lib().csa2_attend(
         _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa), _ptr(swa_row0), swa_cap,
-        swa_rows, window, n_heads, ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws), ws.numel(),
-        _stream(stream)))
+        swa_rows, window, _ptr(win_new), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _stream(stream)))
 
 
 def csa2_attend_fp8win(q, codes, scales, seqs: Seqs, idx, swa8, swa_row0, swa_cap: int, window: int,
-                       softmax_scale: float, out, ws, replay_start=None, stream=None) -> None:
+                       softmax_scale: float, out, replay_start=None, win_new=None, stream=None) -> None:
     n_heads = q.shape[1]
     top_k = idx.shape[1] if idx is not None else 0
     swa_rows = swa8.shape[0] if swa8 is not None else 0
     _check("csa2_attend_fp8win", lib().csa2_attend_fp8win(
         _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa8), _ptr(swa_row0), swa_cap,
-        swa_rows, window, _ptr(replay_start), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws),
-        ws.numel(), _stream(stream)))
+        swa_rows, window, _ptr(replay_start), _ptr(win_new), n_heads, ctypes.c_float(softmax_scale), _ptr(out),
+        _stream(stream)))
 
 
 def csa2_reindex_attend(q_idx, w, k_idx, k_scales, seqs: Seqs, pool, top_k: int, idx_out, q, codes, scales, swa,
                         swa_row0, swa_cap: int, window: int, softmax_scale: float, out, ws, window_fp8: bool = False,
-                        replay_start=None, block: int = BLOCK, stream=None) -> None:
-    """One Reindex layer: selection inside the pool (bf16 keys, or MXFP4 keys when k_scales is
-    given) and the attention over it; idx_out and out as from the two separate calls."""
+                        replay_start=None, win_new=None, block: int = BLOCK, stream=None) -> None:
+    """One Reindex layer in one kernel: selection inside the pool (bf16 keys, or MXFP4 keys when
+    k_scales is given) and the attention over it; idx_out and out as from the separate calls."""
     swa_rows = swa.shape[0] if swa is not None else 0
     _check("csa2_reindex_attend", lib().csa2_reindex_attend(
         _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scales), seqs.c(), q_idx.shape[1], _ptr(pool), pool.shape[1], block,
         top_k, _ptr(idx_out), _ptr(q), _ptr(codes), _ptr(scales), _ptr(swa), 1 if window_fp8 else 0, _ptr(swa_row0),
-        swa_cap, swa_rows, window, _ptr(replay_start), q.shape[1], ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws),
-        ws.numel(), _stream(stream)))
+        swa_cap, swa_rows, window, _ptr(replay_start), _ptr(win_new), q.shape[1], ctypes.c_float(softmax_scale),
+        _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def csa2_token_append(x, dst_rows, codes, scales, k_new=None, k_idx=None, k_scales=None, stream=None) -> None:
+    """The step's own token of a Full layer's set: x (bf16 [n_tok, 128]) into the FP4 cache and
+    k_new (bf16 [n_tok, 64]) into the key cache (bf16 rows, or MXFP4 when k_scales is given)."""
+    _check("csa2_token_append", lib().csa2_token_append(
+        _ptr(x), _ptr(k_new), x.shape[0], _ptr(dst_rows), _ptr(codes), _ptr(scales), _ptr(k_idx), _ptr(k_scales),
+        codes.shape[0], _stream(stream)))
+
+
+def csa2_window_append(x, out, dst_rows=None, row0: int = 0, window_fp8: bool = False, stream=None) -> None:
+    """Window vectors (bf16 [n_tok, 128]) into a window store (bf16 rows, or E4M3 bytes)."""
+    _check("csa2_window_append", lib().csa2_window_append(
+        _ptr(x), x.shape[0], _ptr(dst_rows), row0, _ptr(out), 1 if window_fp8 else 0, out.shape[0],
+        _stream(stream)))
 
 
 def mxfp4_key_append(x, codes, scales, dst_rows=None, row0: int = 0, stream=None) -> None:
@@ -289,6 +315,31 @@ def csa2_index_full_scan_timed(q_idx, w, k_idx, k_scales, seqs: Seqs, top_k: int
         _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scales), seqs.c(), q_idx.shape[1], top_k, block, pool_blocks,
         shared_kv, _ptr(idx_out), _ptr(pool_out), _ptr(ws), ws.numel(), _stream(stream),
         ctypes.c_void_p(start_event.cuda_event), ctypes.c_void_p(stop_event.cuda_event)))
+
+
+def _event(e):
+    return ctypes.c_void_p(e.cuda_event) if e is not None else None
+
+
+def csa2_index_reindex_timed(q_idx, w, k_idx, k_scales, seqs: Seqs, pool, top_k: int, idx_out, ws, start_event,
+                             stop_event, block: int = BLOCK, stream=None) -> None:
+    """csa2_index_reindex (or _mx with k_scales) with the scoring kernel's start and the selection
+    kernel's end recorded into two torch.cuda.Event objects (recorded once already)."""
+    _check("csa2_index_reindex_timed", lib().csa2_index_reindex_timed(
+        _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scales), seqs.c(), q_idx.shape[1], _ptr(pool), pool.shape[1], block,
+        top_k, _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream), _event(start_event), _event(stop_event)))
+
+
+def csa2_attend_timed(q, codes, scales, seqs: Seqs, idx, swa, swa_row0, swa_cap: int, window: int,
+                      softmax_scale: float, out, start_event, stop_event, win_new=None, stream=None) -> None:
+    """csa2_attend with the attention kernel's own start and end recorded into two torch events."""
+    n_heads = q.shape[1]
+    top_k = idx.shape[1] if idx is not None else 0
+    swa_rows = swa.shape[0] if swa is not None else 0
+    _check("csa2_attend_timed", lib().csa2_attend_timed(
+        _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa), _ptr(swa_row0), swa_cap,
+        swa_rows, window, _ptr(win_new), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _stream(stream),
+        _event(start_event), _event(stop_event)))
 
 
 def csa2_index_reindex_mx(q_idx, w, k_codes, k_scales, seqs: Seqs, pool, top_k: int, idx_out, ws,

@@ -34,7 +34,13 @@
 // Logits use S^T[entry][head] = K . Q^T (A = 16 entries x 32 channels from registers,
 // B = Q^T); the S^T accumulator is already the B operand layout P^T needs for
 // O^T[dim][head] += V^T . P^T, so P never leaves registers.
+#include <hip/hip_ext.h>
+
+#include <type_traits>
+
 #include "csa2_device.hpp"
+#include "pack_common.hpp"
+#include "reindex_score.hpp"
 #include "reindex_select.hpp"
 
 namespace csa2 {
@@ -134,6 +140,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 // in FP8); they are converted to f16 exactly and take the FP4 entries' f16 path.
 // replay (may be NULL): per-query replay start s; the window then holds only positions >= s
 // ([Article] section XII, SWA Bounded Replay).
+// win_new (may be NULL): the step's own window vector per query (bf16 [n_q, 128]): every layer
+// computes its own window entry for the new token ([Article] section VI).  The kernel attends it
+// as position N - 1 of the window straight from win_new (the store's row for that position is
+// never read) and writes it to that row (converted to E4M3 for an FP8 store) once everything
+// else is done.
 struct AttendArgs {
     const uint16_t* q;
     const uint8_t* codes;
@@ -153,6 +164,7 @@ struct AttendArgs {
     int n_heads;
     float scale_log2;
     float* out;
+    const uint16_t* win_new;
 };
 
 // LDS of one attention workgroup: per-wave tiles (P.V operands, then the merge rows) and the
@@ -201,6 +213,10 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
     int64_t row0_raw = vload_i64(kv_row0, i);
     int64_t wrow0_raw = vload_i64(kWin ? swa_row0 : kv_row0, i);
     int64_t replay_raw = vload_i64(replay != nullptr ? replay : kv_row0, i);  // replay[i] when given
+    const uint16_t* __restrict__ win_new = a.win_new;
+    const bool has_new = kWin && win_new != nullptr;
+    // channels 2l, 2l + 1 of the query's new window vector (the E4M3 exchange and the final store)
+    uint32_t nwv = has_new ? *reinterpret_cast<const uint32_t*>(win_new + (int64_t)i * kD + 2 * l) : 0u;
     int pos[kRB];     // selected positions of this lane's entry in each FP4 block (-1: none)
     // indices of one round (lanes past top_k read entry 0 and are masked; a length of 0 masks
     // every position later)
@@ -231,7 +247,7 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
     __builtin_amdgcn_sched_barrier(0);
     // an empty statement that takes and returns the four per-query values: every use of them
     // comes after it, so no wait for them is placed in front of the index and query loads
-    asm volatile("" : "+v"(len_raw), "+v"(row0_raw), "+v"(wrow0_raw), "+v"(replay_raw));
+    asm volatile("" : "+v"(len_raw), "+v"(row0_raw), "+v"(wrow0_raw), "+v"(replay_raw), "+v"(nwv));
     // the same for the bounds (kernel arguments not preloaded into SGPRs): their loads are not
     // waited for in front of the first level
     asm volatile("" : "+s"(max_len), "+s"(cache_rows));
@@ -251,6 +267,8 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
     // ---- the round's window gathers (second level: they need the length) ----
     u32x4 wf[4];      // window entry: channels [32g, 32g+32) as bf16 (E4M3: wf[0..1] hold them)
     bool wvalid = false;
+    bool wnew = false;       // this lane's window entry is position n - 1, taken from win_new
+    bool wnew_wave = false;  // this wave's window block of the round holds that entry
     auto issue_win = [&](int R) {
         const int wb = R * kRoundWin + wave;
         int64_t sr = -1;
@@ -261,6 +279,8 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
             if (sr >= swa_rows) sr = -1;
         }
         wvalid = sr >= 0;
+        wnew = has_new && wvalid && ew == wc - 1;
+        wnew_wave = has_new && wb < nbw && (wc - 1) >> 4 == wb;
         // rows of absent entries are clamped to row 0 (kWin: the store has rows) and masked
         const int64_t wr = wvalid ? sr : 0;
         if constexpr (kW8) {
@@ -272,7 +292,9 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
             }
             wf[2] = wf[3] = u32x4{0u, 0u, 0u, 0u};
         } else {
-            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(swa) + wr * kD + 32 * g);
+            // the new entry comes from win_new (same layout as a store row)
+            const uint16_t* row = wnew ? win_new + (int64_t)i * kD : static_cast<const uint16_t*>(swa) + wr * kD;
+            const uint4* src = reinterpret_cast<const uint4*>(row + 32 * g);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const uint4 v = kWin ? src[s] : make_uint4(0, 0, 0, 0);
@@ -338,6 +360,23 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
         __builtin_amdgcn_sched_barrier(0);
         if (R == 0) convert_q();
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kW8) {
+            // E4M3 store: the wave holding the new entry converts its vector (two channels per
+            // lane, from the first-level load) through its tile; the entry's lanes take their 32
+            // channels from there in place of the store row
+            if (wnew_wave) {
+                const uint32_t e = e4m3_code_of_bf16(nwv & 0xffffu) | (e4m3_code_of_bf16(nwv >> 16) << 8);
+                *reinterpret_cast<uint16_t*>(tile + 2 * l) = (uint16_t)e;
+                wave_lds_sync();
+                const uint4 v0 = *reinterpret_cast<const uint4*>(tile + 32 * g);
+                const uint4 v1 = *reinterpret_cast<const uint4*>(tile + 32 * g + 16);
+                if (wnew) {
+                    wf[0] = u32x4{v0.x, v0.y, v0.z, v0.w};
+                    wf[1] = u32x4{v1.x, v1.y, v1.z, v1.w};
+                }
+                wave_lds_sync();
+            }
+        }
 
         // ---- logits of the whole round ----
         u32x4 kf[kRB][4];
@@ -510,6 +549,18 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
         const f32x4 res = L > 0.f ? O / L : f32x4{0.f, 0.f, 0.f, 0.f};
         *reinterpret_cast<f32x4*>(out + ((int64_t)i * n_heads + h) * kD + d0) = res;
     }
+    // the new window entry into its store row, after every read of the store by this query
+    // (wave 0, two channels per lane); whether or not the replay bound lets it be attended
+    if (has_new && wave == 0 && n > 0) {
+        const int64_t wr = wrow0_raw + ((n - 1) % swa_cap);
+        if (wr >= 0 && wr < swa_rows) {
+            if constexpr (kW8)
+                *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(const_cast<void*>(swa)) + wr * kD + 2 * l) =
+                    (uint16_t)(e4m3_code_of_bf16(nwv & 0xffffu) | (e4m3_code_of_bf16(nwv >> 16) << 8));
+            else
+                *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(const_cast<void*>(swa)) + wr * kD + 2 * l) = nwv;
+        }
+    }
 }
 
 // The arguments one by one (not the AttendArgs block), those of the first level of loads first:
@@ -521,33 +572,85 @@ __global__ __launch_bounds__(kAttNT) void k_attend(const int32_t* kv_len, const 
                                                    const uint16_t* q, int top_k, int n_heads, int32_t max_len,
                                                    int64_t cache_rows, const uint8_t* codes, const uint8_t* scales,
                                                    const void* swa, int swa_cap, int64_t swa_rows, int window,
-                                                   float scale_log2, float* out) {
+                                                   float scale_log2, float* out, const uint16_t* win_new) {
     __shared__ __align__(16) uint8_t s_tile[kAttWaves * kTileB];
     __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
-    const AttendArgs a{q,        codes,    scales, kv_row0, kv_len, max_len, cache_rows, idx,     top_k, swa,
-                       swa_row0, swa_cap,  swa_rows, window, replay, n_heads, scale_log2, out};
+    const AttendArgs a{q,        codes,   scales,   kv_row0, kv_len, max_len, cache_rows, idx,   top_k,
+                       swa,      swa_row0, swa_cap, swa_rows, window, replay, n_heads,   scale_log2, out,
+                       win_new};
     const int i = blockIdx.x;
     attend_query<kFp4, kWin, kW8>(i, a, idx + (int64_t)i * top_k, AttendLds{s_tile, s_m, s_l});
 }
 
-// Reindex layer, second kernel: the query's selection inside its pool (reindex_select_query,
-// over the keys the Reindex scoring kernel wrote), kept in LDS and written to idx_out for the
-// Reuse layers that follow, then the attention over it, in one workgroup: the selection's
-// output never makes a round trip through memory and the layer saves a kernel launch.
-template <int EPT, bool kWin, bool kW8>
-__global__ __launch_bounds__(kAttNT) void k_reindex_attend(const int32_t* __restrict__ pool, int pool_blocks,
-                                                           IndexWs ws, int32_t* __restrict__ idx_out, AttendArgs a) {
+// One Reindex layer in one kernel ([Article] sections VIII-IX: the layer scores its own indexer
+// query against the Full layer's keys inside the shared pool and takes its own Top-K there;
+// section VI: it then attends its selection plus its window).
+//   Every workgroup scores one kReindexTile chunk of one query's pool (as k_idx_reindex_score,
+//   with 8 waves), writes the keys with agent-scope stores and adds its first-digit counts to
+//   the query's histogram; once its stores and atomics have completed it takes a ticket from
+//   the query's counter.  The workgroup holding the last ticket of its query is the only one
+//   that goes on: it resets the counter, selects the query's Top-K from the keys and the
+//   histogram (agent-scope loads: the other chunks were scored on other XCDs in this same
+//   kernel), keeps the selection in LDS, writes it to idx_out for the Reuse layers that follow,
+//   and runs the attention over it.  No workgroup waits for another: the last to finish
+//   does the rest, so the kernel cannot stall on scheduling order.
+// The selection is that of k_idx_reindex_select and the attention that of k_attend, so the
+// results equal the separate kernels' bit for bit.
+constexpr int kLayerMaxTopK = 1024;  // selected entries kept in LDS
+
+template <int HI, bool MX, int EPT, bool kWin, bool kW8>
+__global__ __launch_bounds__(kAttNT) void k_reindex_layer(const int32_t* __restrict__ pool,
+                                                          const uint16_t* __restrict__ q_idx,
+                                                          const float* __restrict__ w, const int64_t* __restrict__ kv_row0,
+                                                          const int32_t* __restrict__ kv_len, int pool_blocks,
+                                                          int idx_heads, int32_t max_len, const void* __restrict__ k_idx,
+                                                          const uint8_t* __restrict__ k_sc, int64_t cache_rows, IndexWs ws,
+                                                          int32_t* __restrict__ idx_out, AttendArgs a) {
+    // s_area: the scoring histogram, then the selection's two radix histograms, then the
+    // attention's per-wave tiles
     __shared__ __align__(16) uint8_t s_area[kAttWaves * kTileB];
-    __shared__ uint32_t s_hist[2][kHistBins];
-    __shared__ int32_t s_idx[kMaxSelect];
+    __shared__ int32_t s_idx[kLayerMaxTopK];
     __shared__ int s_scan[kAttNT / kWave];
     __shared__ uint32_t s_or[2];
     __shared__ Thresh sh_th;
     __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
-    const int i = blockIdx.x;
-    reindex_select_query<kAttNT, EPT>(i, pool, pool_blocks, a.top_k, ws, idx_out, s_idx, s_hist, s_scan, s_or,
-                                      &sh_th);
-    __syncthreads();  // the selection is in s_idx
+    __shared__ uint32_t s_ticket;
+    static_assert(2 * kHistBins * 4 <= kAttWaves * kTileB, "selection histograms fit the tile area");
+
+    const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
+    int i, chunk;
+    reindex_item((int)blockIdx.x, chunks, i, chunk);
+    const int t = threadIdx.x;
+    const int n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
+    const int64_t row0 = n > 0 ? kv_row0[i] : 0;
+    const int n_elem = pool_blocks * 8;
+    uint32_t* sh_hist = reinterpret_cast<uint32_t*>(s_area);
+    for (int b = t; b < kHistBins; b += kAttNT) sh_hist[b] = 0u;
+    QFrag qf;
+    load_qfrag(qf, q_idx + (int64_t)i * idx_heads * 64, w + (int64_t)i * idx_heads, idx_heads, t & (kWave - 1));
+    __syncthreads();
+    reindex_score_chunks<HI, MX, kAttWaves, true>(chunk, chunk + 1, n, row0, pool + (int64_t)i * pool_blocks,
+                                                  pool_blocks, qf, k_idx, k_sc, ws.keys + (int64_t)i * n_elem, sh_hist);
+    __syncthreads();
+    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
+    for (int b = t; b < kHistBins; b += kAttNT) {
+        const uint32_t h = sh_hist[b];
+        if (h) atomicAdd(&gh[b], h);
+    }
+    // every key store and histogram atomic of this thread has completed (gfx9 counts stores and
+    // atomics in vmcnt); the barrier then covers the whole workgroup before the ticket
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    uint32_t* ctr = ws.ctrl + (int64_t)i * kCtlSlots + kCtlScoreDone;
+    if (t == 0) s_ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_ticket != (uint32_t)(chunks - 1)) return;  // uniform across the workgroup
+    if (t == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::: "memory");  // nothing below moves above the ticket
+
+    reindex_select_query<kAttNT, EPT, true>(i, pool, pool_blocks, a.top_k, ws, idx_out, s_idx,
+                                            reinterpret_cast<uint32_t(*)[kHistBins]>(s_area), s_scan, s_or, &sh_th);
+    __syncthreads();  // the selection is in s_idx; the histogram area is free for the tiles
     attend_query<true, kWin, kW8>(i, a, s_idx, AttendLds{s_area, s_m, s_l});
 }
 
@@ -556,7 +659,8 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
                          const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
                          int top_k, const void* swa, int window_fp8, const int64_t* swa_row0, int swa_cap,
                          int64_t swa_rows, int window, const int64_t* replay, int n_heads, float softmax_scale,
-                         float* out, hipStream_t stream) {
+                         float* out, const uint16_t* win_new, hipStream_t stream, hipEvent_t ev_start,
+                         hipEvent_t ev_stop) {
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
     const bool fp4 = top_k > 0, win = window > 0 && swa_rows > 0;
     decltype(&k_attend<true, true, false>) kern;
@@ -566,33 +670,55 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
     else
         kern = fp4 ? (win ? k_attend<true, true, false> : k_attend<true, false, false>)
                    : (win ? k_attend<false, true, false> : k_attend<false, false, false>);
-    hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, kv_len, kv_row0, swa_row0, replay, idx, q, top_k,
-                       n_heads, max_len, cache_rows, codes, scales, swa, swa_cap, swa_rows, window, scale_log2, out);
+    // ev_start / ev_stop (may be null): the kernel's own start and end, recorded by its launch
+    if (ev_start != nullptr || ev_stop != nullptr)
+        hipExtLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, ev_start, ev_stop, 0, kv_len, kv_row0, swa_row0,
+                              replay, idx, q, top_k, n_heads, max_len, cache_rows, codes, scales, swa, swa_cap, swa_rows,
+                              window, scale_log2, out, win_new);
+    else
+        hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, kv_len, kv_row0, swa_row0, replay, idx, q, top_k,
+                           n_heads, max_len, cache_rows, codes, scales, swa, swa_cap, swa_rows, window, scale_log2, out,
+                           win_new);
     return hipGetLastError();
 }
 
-// The fused Reindex selection + attention (after the Reindex scoring kernel); pool_blocks * 8
-// must be at most kAttNT * 32.
-hipError_t launch_reindex_attend(const int32_t* pool, int pool_blocks, const IndexWs& ws, int32_t* idx_out,
-                                 const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
-                                 int64_t cache_rows, int top_k, const void* swa, int window_fp8,
-                                 const int64_t* swa_row0, int swa_cap, int64_t swa_rows, int window,
-                                 const int64_t* replay, int n_heads, float softmax_scale, float* out,
-                                 hipStream_t stream) {
+// The one-kernel Reindex layer: pool_blocks * 8 <= kAttNT * 32 and top_k <= kLayerMaxTopK (the
+// caller checks both).  mx: MXFP4 keys (k_idx = code bytes, k_sc = E8M0 scales).
+hipError_t launch_reindex_layer(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
+                                int idx_heads, const int32_t* pool, int pool_blocks, const IndexWs& ws,
+                                int32_t* idx_out, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
+                                int64_t cache_rows, int top_k, const void* swa, int window_fp8,
+                                const int64_t* swa_row0, int swa_cap, int64_t swa_rows, int window,
+                                const int64_t* replay, int n_heads, float softmax_scale, float* out,
+                                const uint16_t* win_new, hipStream_t stream) {
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
     const bool win = window > 0 && swa_rows > 0;
-    const bool small = pool_blocks * 8 <= kAttNT * 16;
-    decltype(&k_reindex_attend<32, true, false>) kern;
-    if (window_fp8)
-        kern = small ? (win ? k_reindex_attend<16, true, true> : k_reindex_attend<16, false, true>)
-                     : (win ? k_reindex_attend<32, true, true> : k_reindex_attend<32, false, true>);
-    else
-        kern = small ? (win ? k_reindex_attend<16, true, false> : k_reindex_attend<16, false, false>)
-                     : (win ? k_reindex_attend<32, true, false> : k_reindex_attend<32, false, false>);
-    const AttendArgs a{q,          codes,    scales, kv_row0, kv_len, max_len,   cache_rows, nullptr, top_k, swa,
-                       swa_row0,   swa_cap,  swa_rows, window, replay,  n_heads, scale_log2, out};
-    hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, pool, pool_blocks, ws, idx_out, a);
+    const int ept = (pool_blocks * 8 + kAttNT - 1) / kAttNT;
+    using K = decltype(&k_reindex_layer<4, false, 8, true, false>);
+    // variants: indexer heads (<= 4 or <= 8), key format, elements per thread, window presence, window format
+    auto pick_w = [&](auto hi, auto mxv, auto e) -> K {
+        constexpr int HI = decltype(hi)::value;
+        constexpr bool MX = decltype(mxv)::value;
+        constexpr int E = decltype(e)::value;
+        if (window_fp8) return win ? k_reindex_layer<HI, MX, E, true, true> : k_reindex_layer<HI, MX, E, false, true>;
+        return win ? k_reindex_layer<HI, MX, E, true, false> : k_reindex_layer<HI, MX, E, false, false>;
+    };
+    auto pick_e = [&](auto hi, auto mxv) -> K {
+        if (ept <= 8) return pick_w(hi, mxv, std::integral_constant<int, 8>{});
+        if (ept <= 16) return pick_w(hi, mxv, std::integral_constant<int, 16>{});
+        return pick_w(hi, mxv, std::integral_constant<int, 32>{});
+    };
+    auto pick_m = [&](auto hi) -> K {
+        return mx ? pick_e(hi, std::true_type{}) : pick_e(hi, std::false_type{});
+    };
+    const K kern = idx_heads <= 4 ? pick_m(std::integral_constant<int, 4>{}) : pick_m(std::integral_constant<int, 8>{});
+    const AttendArgs a{q,        codes,   scales,   kv_row0, kv_len, max_len, cache_rows, nullptr,    top_k,
+                       swa,      swa_row0, swa_cap, swa_rows, window, replay, n_heads,   scale_log2, out,
+                       win_new};
+    const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(chunks * n_q)), dim3(kAttNT), 0, stream, pool, q_idx, w, kv_row0, kv_len,
+                       pool_blocks, idx_heads, max_len, k_idx, k_sc, cache_rows, ws, idx_out, a);
     return hipGetLastError();
 }
 

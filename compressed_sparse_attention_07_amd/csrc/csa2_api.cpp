@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "csa2.h"
+#include "csa2_timing.h"
 
 namespace csa2 {
 
@@ -17,7 +18,8 @@ constexpr int kFullTile = CSA2_SCAN_TILE;  // must match the scan kernel's tile
 constexpr int kFilterTile = 8192;
 constexpr int kHistBins = 2048;
 constexpr size_t kAlign = 256;
-constexpr int kFusedMaxPoolElems = 512 * 32;  // pool positions the fused Reindex selection + attention takes
+constexpr int kLayerMaxPoolElems = 512 * 32;  // pool positions the one-kernel Reindex layer takes
+constexpr int kLayerMaxTopK = 1024;          // selected entries it keeps in LDS
 
 struct Thresh {
     int32_t digit, above, in_bucket, total;
@@ -53,14 +55,21 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
 hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
                                 int64_t cache_rows, int n_heads, const int32_t* pool, int pool_blocks, int top_k,
-                                const IndexWs& ws, int32_t* idx_out, int select, hipStream_t stream);
-hipError_t launch_reindex_attend(const int32_t* pool, int pool_blocks, const IndexWs& ws, int32_t* idx_out,
-                                 const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
-                                 int64_t cache_rows, int top_k, const void* swa, int window_fp8,
-                                 const int64_t* swa_row0, int swa_cap, int64_t swa_rows, int window,
-                                 const int64_t* replay, int n_heads, float softmax_scale, float* out,
-                                 hipStream_t stream);
+                                const IndexWs& ws, int32_t* idx_out, int select, hipStream_t stream,
+                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+hipError_t launch_reindex_layer(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
+                                int idx_heads, const int32_t* pool, int pool_blocks, const IndexWs& ws,
+                                int32_t* idx_out, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
+                                int64_t cache_rows, int top_k, const void* swa, int window_fp8,
+                                const int64_t* swa_row0, int swa_cap, int64_t swa_rows, int window,
+                                const int64_t* replay, int n_heads, float softmax_scale, float* out,
+                                const uint16_t* win_new, hipStream_t stream);
+hipError_t launch_token_append(const uint16_t* x, const uint16_t* k_new, int64_t n_tok, const int64_t* dst_rows,
+                               uint8_t* codes, uint8_t* scales, void* k_idx, uint8_t* k_scales, int64_t cap_rows,
+                               hipStream_t stream);
+hipError_t launch_row_copy(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
+                           uint16_t* out, int64_t cap_rows, hipStream_t stream);
 hipError_t launch_mx_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
                           uint8_t* codes, uint8_t* scales, int64_t cap_rows, hipStream_t stream);
 hipError_t launch_fp8_pack(const uint16_t* x, int64_t n_tok, int dim, const int64_t* dst_rows, int64_t row0,
@@ -69,7 +78,8 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
                          const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
                          int top_k, const void* swa, int window_fp8, const int64_t* swa_row0, int swa_cap,
                          int64_t swa_rows, int window, const int64_t* replay, int n_heads, float softmax_scale,
-                         float* out, hipStream_t stream);
+                         float* out, const uint16_t* win_new, hipStream_t stream, hipEvent_t ev_start = nullptr,
+                         hipEvent_t ev_stop = nullptr);
 hipError_t launch_zero(void* ws, size_t bytes, hipStream_t stream);
 
 namespace {
@@ -287,7 +297,7 @@ static int check_reindex(const uint16_t* q_idx, const float* w, const void* k_id
 static int index_reindex_common(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
                                 const csa2_seqs& seqs, int32_t n_heads, const int32_t* pool, int32_t pool_blocks,
                                 int32_t block, int32_t top_k, int32_t* idx_out, void* ws, size_t ws_bytes,
-                                void* stream) {
+                                void* stream, void* ev_start = nullptr, void* ev_stop = nullptr) {
     const int st = check_reindex(q_idx, w, k_idx, k_sc, mx, seqs, n_heads, pool, pool_blocks, block, top_k, idx_out,
                                  ws, ws_bytes);
     if (st || seqs.n_q == 0) return st;
@@ -295,7 +305,8 @@ static int index_reindex_common(const uint16_t* q_idx, const float* w, const voi
     const IndexWs wsp = carve_reindex(ws, seqs.n_q, top_k, pool_blocks, &need);
     return launch_status(launch_index_reindex(q_idx, w, k_idx, k_sc, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
                                               seqs.max_len_ub, seqs.cache_rows, n_heads, pool, pool_blocks, top_k,
-                                              wsp, idx_out, 1, static_cast<hipStream_t>(stream)));
+                                              wsp, idx_out, 1, static_cast<hipStream_t>(stream),
+                                              static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)));
 }
 
 int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
@@ -333,18 +344,33 @@ int csa2_index_full_mx_scan(const uint16_t* q_idx, const float* w, const uint8_t
                             idx_out, pool_out, ws, ws_bytes, stream, 2);
 }
 
+// Timed launches record into caller events; they are refused on a stream under graph capture.
+static int refuse_capture(void* stream, void* ev_start, void* ev_stop) {
+    if (ev_start == nullptr && ev_stop == nullptr) return CSA2_OK;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess) return CSA2_ERR_LAUNCH;
+    return cap != hipStreamCaptureStatusNone ? CSA2_ERR_UNSUPPORTED : CSA2_OK;
+}
+
 int csa2_index_full_scan_timed(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
                                csa2_seqs seqs, int32_t n_heads, int32_t top_k, int32_t block, int32_t pool_blocks,
                                int32_t shared_kv, int32_t* idx_out, int32_t* pool_out, void* ws, size_t ws_bytes,
                                void* stream, void* start_event, void* stop_event) {
-    if (start_event != nullptr || stop_event != nullptr) {  // timing launches are not for graph capture
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cap) != hipSuccess) return CSA2_ERR_LAUNCH;
-        if (cap != hipStreamCaptureStatusNone) return CSA2_ERR_UNSUPPORTED;
-    }
+    const int st = refuse_capture(stream, start_event, stop_event);
+    if (st) return st;
     return index_full_phase(q_idx, w, k_idx, k_scales, k_scales != nullptr ? 1 : 0, seqs, n_heads, top_k, block,
                             pool_blocks, shared_kv, idx_out, pool_out, ws, ws_bytes, stream, 2, start_event,
                             stop_event);
+}
+
+int csa2_index_reindex_timed(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
+                             csa2_seqs seqs, int32_t n_heads, const int32_t* pool, int32_t pool_blocks, int32_t block,
+                             int32_t top_k, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream,
+                             void* start_event, void* stop_event) {
+    const int st = refuse_capture(stream, start_event, stop_event);
+    if (st) return st;
+    return index_reindex_common(q_idx, w, k_idx, k_scales, k_scales != nullptr ? 1 : 0, seqs, n_heads, pool,
+                                pool_blocks, block, top_k, idx_out, ws, ws_bytes, stream, start_event, stop_event);
 }
 
 int csa2_index_reindex_mx(const uint16_t* q_idx, const float* w, const uint8_t* k_codes, const uint8_t* k_scales,
@@ -357,7 +383,8 @@ int csa2_index_reindex_mx(const uint16_t* q_idx, const float* w, const uint8_t* 
 // Checks of an attention call (everything but n_q == 0, which the callers handle first).
 static int check_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const csa2_seqs& seqs,
                         const int32_t* idx, int32_t top_k, const void* swa, const int64_t* swa_row0, int32_t swa_cap,
-                        int64_t swa_rows, int32_t window, int32_t n_heads, float softmax_scale, const float* out) {
+                        int64_t swa_rows, int32_t window, int32_t n_heads, float softmax_scale, const float* out,
+                        const uint16_t* win_new) {
     int st = check_seqs(seqs);
     if (st) return st;
     if (top_k < 0 || top_k > CSA2_MAX_SELECT || window < 0 || window > CSA2_MAX_WINDOW || n_heads < 1 ||
@@ -371,7 +398,7 @@ static int check_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* 
     if (top_k > 0 && (codes == nullptr || scales == nullptr || idx == nullptr)) return CSA2_ERR_NULL;
     if (window > 0 && (swa == nullptr || swa_row0 == nullptr)) return CSA2_ERR_NULL;
     if (!aligned16(q) || (codes && !aligned16(codes)) || (swa && !aligned16(swa)) ||
-        (scales && (reinterpret_cast<uintptr_t>(scales) & 1u)))
+        (scales && (reinterpret_cast<uintptr_t>(scales) & 1u)) || (win_new && !aligned16(win_new)))
         return CSA2_ERR_SHAPE;
     return CSA2_OK;
 }
@@ -379,68 +406,107 @@ static int check_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* 
 static int attend_common(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const csa2_seqs& seqs,
                          const int32_t* idx, int32_t top_k, const void* swa, int window_fp8, const int64_t* swa_row0,
                          int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay, int32_t n_heads,
-                         float softmax_scale, float* out, void* stream) {
+                         float softmax_scale, float* out, const uint16_t* win_new, void* stream,
+                         void* ev_start = nullptr, void* ev_stop = nullptr) {
     const int st = check_attend(q, codes, scales, seqs, idx, top_k, swa, swa_row0, swa_cap, swa_rows, window, n_heads,
-                                softmax_scale, out);
+                                softmax_scale, out, win_new);
     if (st || seqs.n_q == 0) return st;
     return launch_status(launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
                                        seqs.cache_rows, idx, top_k, swa, window_fp8, swa_row0,
                                        window > 0 ? swa_cap : 1, swa_rows, window, replay, n_heads, softmax_scale,
-                                       out, static_cast<hipStream_t>(stream)));
+                                       out, window > 0 ? win_new : nullptr, static_cast<hipStream_t>(stream),
+                                       static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)));
 }
 
 int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs, const int32_t* idx,
-                int32_t top_k, const uint16_t* swa, const int64_t* swa_row0, int32_t swa_cap, int64_t swa_rows,
-                int32_t window, int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                int32_t top_k, uint16_t* swa, const int64_t* swa_row0, int32_t swa_cap, int64_t swa_rows,
+                int32_t window, const uint16_t* win_new, int32_t n_heads, float softmax_scale, float* out,
                 void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     return attend_common(q, codes, scales, seqs, idx, top_k, swa, 0, swa_row0, swa_cap, swa_rows, window, nullptr,
-                         n_heads, softmax_scale, out, stream);
+                         n_heads, softmax_scale, out, win_new, stream);
+}
+
+int csa2_attend_timed(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
+                      const int32_t* idx, int32_t top_k, uint16_t* swa, const int64_t* swa_row0, int32_t swa_cap,
+                      int64_t swa_rows, int32_t window, const uint16_t* win_new, int32_t n_heads, float softmax_scale,
+                      float* out, void* stream, void* start_event, void* stop_event) {
+    const int st = refuse_capture(stream, start_event, stop_event);
+    if (st) return st;
+    return attend_common(q, codes, scales, seqs, idx, top_k, swa, 0, swa_row0, swa_cap, swa_rows, window, nullptr,
+                         n_heads, softmax_scale, out, win_new, stream, start_event, stop_event);
 }
 
 int csa2_attend_fp8win(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
-                       const int32_t* idx, int32_t top_k, const uint8_t* swa, const int64_t* swa_row0,
-                       int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay_start,
-                       int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
+                       const int32_t* idx, int32_t top_k, uint8_t* swa, const int64_t* swa_row0, int32_t swa_cap,
+                       int64_t swa_rows, int32_t window, const int64_t* replay_start, const uint16_t* win_new,
+                       int32_t n_heads, float softmax_scale, float* out, void* stream) {
     return attend_common(q, codes, scales, seqs, idx, top_k, swa, 1, swa_row0, swa_cap, swa_rows, window,
-                         replay_start, n_heads, softmax_scale, out, stream);
+                         replay_start, n_heads, softmax_scale, out, win_new, stream);
 }
 
 int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
                         csa2_seqs seqs, int32_t idx_heads, const int32_t* pool, int32_t pool_blocks, int32_t block,
                         int32_t top_k, int32_t* idx_out, const uint16_t* q, const uint8_t* codes,
-                        const uint8_t* scales, const void* swa, int32_t window_fp8, const int64_t* swa_row0,
+                        const uint8_t* scales, void* swa, int32_t window_fp8, const int64_t* swa_row0,
                         int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay_start,
-                        int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
+                        const uint16_t* win_new, int32_t n_heads, float softmax_scale, float* out, void* ws,
+                        size_t ws_bytes, void* stream) {
     const int mx = k_scales != nullptr ? 1 : 0;
     if (window_fp8 != 0 && window_fp8 != 1) return CSA2_ERR_SHAPE;
     int st = check_reindex(q_idx, w, k_idx, k_scales, mx, seqs, idx_heads, pool, pool_blocks, block, top_k, idx_out,
                            ws, ws_bytes);
     if (st) return st;
     st = check_attend(q, codes, scales, seqs, idx_out, top_k, swa, swa_row0, swa_cap, swa_rows, window, n_heads,
-                      softmax_scale, out);
+                      softmax_scale, out, win_new);
     if (st || seqs.n_q == 0) return st;
     size_t need = 0;
     const IndexWs wsp = carve_reindex(ws, seqs.n_q, top_k, pool_blocks, &need);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const bool fused = pool_blocks * 8 <= kFusedMaxPoolElems;
+    const uint16_t* wn = window > 0 ? win_new : nullptr;
+    if (pool_blocks * 8 <= kLayerMaxPoolElems && top_k <= kLayerMaxTopK)
+        return launch_status(launch_reindex_layer(q_idx, w, k_idx, k_scales, mx, idx_heads, pool, pool_blocks, wsp,
+                                                  idx_out, q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q,
+                                                  seqs.max_len_ub, seqs.cache_rows, top_k, swa, window_fp8, swa_row0,
+                                                  window > 0 ? swa_cap : 1, swa_rows, window, replay_start, n_heads,
+                                                  softmax_scale, out, wn, s));
     hipError_t e = launch_index_reindex(q_idx, w, k_idx, k_scales, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
                                         seqs.max_len_ub, seqs.cache_rows, idx_heads, pool, pool_blocks, top_k, wsp,
-                                        idx_out, fused ? 0 : 1, s);
+                                        idx_out, 1, s);
     if (e != hipSuccess) return CSA2_ERR_LAUNCH;
-    if (fused)
-        e = launch_reindex_attend(pool, pool_blocks, wsp, idx_out, q, codes, scales, seqs.kv_row0, seqs.kv_len,
-                                  seqs.n_q, seqs.max_len_ub, seqs.cache_rows, top_k, swa, window_fp8, swa_row0,
-                                  window > 0 ? swa_cap : 1, swa_rows, window, replay_start, n_heads, softmax_scale,
-                                  out, s);
-    else
-        e = launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub, seqs.cache_rows,
-                          idx_out, top_k, swa, window_fp8, swa_row0, window > 0 ? swa_cap : 1, swa_rows, window,
-                          replay_start, n_heads, softmax_scale, out, s);
+    e = launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub, seqs.cache_rows,
+                      idx_out, top_k, swa, window_fp8, swa_row0, window > 0 ? swa_cap : 1, swa_rows, window,
+                      replay_start, n_heads, softmax_scale, out, wn, s);
     return launch_status(e);
+}
+
+int csa2_token_append(const uint16_t* x, const uint16_t* k_new, int64_t n_tok, const int64_t* dst_rows,
+                      uint8_t* codes, uint8_t* scales, void* k_idx, uint8_t* k_scales, int64_t cap_rows,
+                      void* stream) {
+    if (n_tok < 0 || cap_rows < 0 || n_tok > ((int64_t)1 << 40)) return CSA2_ERR_SHAPE;
+    if (n_tok == 0) return CSA2_OK;
+    if (x == nullptr || dst_rows == nullptr || codes == nullptr || scales == nullptr) return CSA2_ERR_NULL;
+    if (k_new != nullptr && k_idx == nullptr) return CSA2_ERR_NULL;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(codes) & 7u) != 0 || (k_new && !aligned16(k_new)) ||
+        (k_new && !aligned16(k_idx)))
+        return CSA2_ERR_SHAPE;
+    return launch_status(launch_token_append(x, k_new, n_tok, dst_rows, codes, scales, k_new ? k_idx : nullptr,
+                                             k_scales, cap_rows, static_cast<hipStream_t>(stream)));
+}
+
+int csa2_window_append(const uint16_t* x, int64_t n_tok, const int64_t* dst_rows, int64_t row0, void* out,
+                       int32_t window_fp8, int64_t cap_rows, void* stream) {
+    if (n_tok < 0 || cap_rows < 0 || n_tok > ((int64_t)1 << 40) || (window_fp8 != 0 && window_fp8 != 1))
+        return CSA2_ERR_SHAPE;
+    if (n_tok == 0) return CSA2_OK;
+    if (x == nullptr || out == nullptr) return CSA2_ERR_NULL;
+    if (!aligned16(x) || !aligned16(out)) return CSA2_ERR_SHAPE;
+    if (dst_rows == nullptr && (row0 < 0 || row0 > cap_rows || n_tok > cap_rows - row0)) return CSA2_ERR_CAPACITY;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (window_fp8)
+        return launch_status(launch_fp8_pack(x, n_tok, CSA2_KV_DIM, dst_rows, row0, static_cast<uint8_t*>(out),
+                                             cap_rows, s));
+    return launch_status(launch_row_copy(x, n_tok, CSA2_KV_DIM, dst_rows, row0, static_cast<uint16_t*>(out), cap_rows,
+                                         s));
 }
 
 int csa2_workspace_init(void* ws, size_t bytes, void* stream) {

@@ -38,6 +38,7 @@
 
 #include "csa2_device.hpp"
 #include "reindex_select.hpp"
+#include "reindex_score.hpp"
 #include "scan_common.hpp"
 #include "scan_full.hpp"
 
@@ -164,7 +165,6 @@ constexpr int kPfBuf = 256;    // positions of one query a workgroup gathers in 
 // workgroups resident on one XCD then read the same few key chunks (512 KB each), which stay
 // in that XCD's 4 MB L2 across all query groups instead of being fetched again for every
 // group from the last-level cache.  (Only the speed depends on the hand-out order.)
-constexpr int kXcds = 8;
 
 __host__ __device__ __forceinline__ int pf_items_per_xcd(int n_px, int n_qg) {
     return (n_px * n_qg + kXcds - 1) / kXcds;
@@ -794,22 +794,8 @@ __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* 
 // ----------------------------------------------------------------------------------------
 // Reindex, kernel 1: score the pool's positions with this layer's query
 // ----------------------------------------------------------------------------------------
-// Workgroup b scores chunk group `chunk` (cpw x kReindexTile pool slots) of query i.  When the
-// group count is a multiple of kXcds, XCD x (the XCD workgroup b runs on is b mod kXcds) takes the x-th
-// eighth of every query's pool: a pool is ascending, so that eighth covers about one eighth of
-// the query's positions, and where queries read the same sequence (the tokens of a prefill
-// chunk) one XCD's workgroups read one eighth of its keys, a share that stays in the XCD's L2.
-__device__ __forceinline__ void reindex_item(int b, int chunks, int& i, int& chunk) {
-    if (chunks % kXcds == 0) {
-        const int per = chunks / kXcds, j = b / kXcds;
-        i = j / per;
-        chunk = (b % kXcds) * per + j % per;
-    } else {
-        i = b / chunks;
-        chunk = b % chunks;
-    }
-}
-
+// Workgroup b scores chunk group `grp` (cpw chunks of kReindexTile pool slots) of query i; the
+// items are sliced per XCD as reindex_item describes.
 // cpw: chunks per workgroup (a divisor of the chunk count).  Many queries (a prefill chunk's
 // tokens): each workgroup scores cpw consecutive chunks of its query and adds its first-digit
 // counts to the query's histogram once, which divides the global atomics by cpw.
@@ -827,71 +813,17 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     reindex_item((int)blockIdx.x, chunks / cpw, i, grp);
     const int t = threadIdx.x;
     const int lane = __lane_id();
-    const int wid = t / kWave;
-    const int g = lane >> 4, r = lane & 15;
     const int n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
     const int64_t row0 = n > 0 ? kv_row0[i] : 0;
     const int n_elem = pool_blocks * 8;
-    const int32_t* qpool = pool + (int64_t)i * pool_blocks;
-    uint32_t* keys = ws.keys + (int64_t)i * n_elem;
 
     for (int b = t; b < kHistBins; b += kScoreNT) sh_hist[b] = 0u;
     QFrag qf;
     load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
     __syncthreads();
-
-    // one MFMA unit = two pool slots (16 positions): lanes r < 8 take slot 2m, r >= 8 slot 2m + 1;
-    // this wave takes units m0 + 4u of the chunk's kReindexTile / 16 units
-    constexpr int kUnits = kReindexTile / 16 / 4;  // units per wave
-    for (int chunk = grp * cpw; chunk < (grp + 1) * cpw; ++chunk) {
-        const int m0 = chunk * (kReindexTile / 16) + wid;
-        int blk[kUnits];
-#pragma unroll
-        for (int u = 0; u < kUnits; ++u) {
-            const int slot = 2 * (m0 + 4 * u) + (r >> 3);
-            blk[u] = slot < pool_blocks ? qpool[slot] : -1;
-        }
-        uint4 kb[kUnits][2];
-        uint32_t kc[kUnits][2], ks[kUnits];
-        if (n > 0) {
-            // absent rows read the sequence's first row (n > 0) and are masked below
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) {
-                const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
-                const bool ok = blk[u] >= 0 && p < n;
-                const int64_t kr = row0 + (ok ? p : 0);
-                if constexpr (MX) {
-                    const uint8_t* row = static_cast<const uint8_t*>(k_idx) + kr * 32 + 4 * g;
-                    kc[u][0] = *reinterpret_cast<const uint32_t*>(row);
-                    kc[u][1] = *reinterpret_cast<const uint32_t*>(row + 16);
-                    ks[u] = *reinterpret_cast<const uint16_t*>(k_sc + kr * 2);
-                } else {
-                    const uint16_t* row = static_cast<const uint16_t*>(k_idx) + kr * 64 + 8 * g;
-                    kb[u][0] = *reinterpret_cast<const uint4*>(row);
-                    kb[u][1] = *reinterpret_cast<const uint4*>(row + 32);
-                }
-            }
-            if constexpr (MX) {
-#pragma unroll
-                for (int u = 0; u < kUnits; ++u) {
-                    kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
-                    kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnits; ++u) {
-            const int slot = 2 * (m0 + 4 * u) + (r >> 3);
-            const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
-            const bool ok = n > 0 && blk[u] >= 0 && p < n;
-            const float sc = n > 0 ? mfma_score<HI>(qf, kb[u][0], kb[u][1]) : 0.f;
-            const uint32_t key = ok ? score_key(sc) : 0u;
-            if (g == 0 && slot < pool_blocks) {
-                keys[slot * 8 + (r & 7)] = key;
-                if (key) atomicAdd(&sh_hist[key >> 21], 1u);
-            }
-        }
-    }  // chunks of this workgroup
+    reindex_score_chunks<HI, MX, kScoreNT / kWave, false>(grp * cpw, (grp + 1) * cpw, n, row0,
+                                                          pool + (int64_t)i * pool_blocks, pool_blocks, qf, k_idx,
+                                                          k_sc, ws.keys + (int64_t)i * n_elem, sh_hist);
     __syncthreads();
     uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
     for (int b = t; b < kHistBins; b += kScoreNT) {
@@ -1070,11 +1002,12 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
     return hipSuccess;
 }
 
-// select == 0: the scoring kernel only (the fused selection + attention kernel follows).
+// select == 0: the scoring kernel only.
 hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
                                 int64_t cache_rows, int n_heads, const int32_t* pool, int pool_blocks, int top_k,
-                                const IndexWs& ws, int32_t* idx_out, int select, hipStream_t stream) {
+                                const IndexWs& ws, int32_t* idx_out, int select, hipStream_t stream,
+                                hipEvent_t ev_start, hipEvent_t ev_stop) {
     const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
     // many queries (>= 512: a prefill chunk): a whole pool of 32 chunks per workgroup, one histogram
     // flush per query instead of one per chunk
@@ -1082,21 +1015,31 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
     const dim3 grid((unsigned)(chunks / cpw * n_q));  // (query, chunk group) items, see reindex_item
     auto kern = mx ? (n_heads <= 4 ? k_idx_reindex_score<4, true> : k_idx_reindex_score<8, true>)
                    : (n_heads <= 4 ? k_idx_reindex_score<4, false> : k_idx_reindex_score<8, false>);
-    hipLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, pool, q_idx, w, kv_row0, kv_len, pool_blocks, n_heads,
-                       cpw, max_len, k_idx, k_sc, cache_rows, ws);
+    // ev_start / ev_stop (may be null): the scoring kernel's start and the selection kernel's end,
+    // recorded by their launches
+    if (ev_start != nullptr)
+        hipExtLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, ev_start, nullptr, 0, pool, q_idx, w, kv_row0,
+                              kv_len, pool_blocks, n_heads, cpw, max_len, k_idx, k_sc, cache_rows, ws);
+    else
+        hipLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, pool, q_idx, w, kv_row0, kv_len, pool_blocks,
+                           n_heads, cpw, max_len, k_idx, k_sc, cache_rows, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !select) return e;
-    if (n_q >= 512 && pool_blocks * 8 <= 256 * 64) {
-        hipLaunchKernelGGL((k_idx_reindex_select<256, 64>), dim3(n_q), dim3(256), 0, stream, ws.keys, ws.hist, pool,
-                           pool_blocks, top_k, idx_out);
+    auto launch_sel = [&](auto kernel, int nt) {
+        if (ev_stop != nullptr)
+            hipExtLaunchKernelGGL(kernel, dim3(n_q), dim3(nt), 0, stream, nullptr, ev_stop, 0, ws.keys, ws.hist, pool,
+                                  pool_blocks, top_k, idx_out);
+        else
+            hipLaunchKernelGGL(kernel, dim3(n_q), dim3(nt), 0, stream, ws.keys, ws.hist, pool, pool_blocks, top_k,
+                               idx_out);
         return hipGetLastError();
-    }
+    };
+    if (n_q >= 512 && pool_blocks * 8 <= 256 * 64) return launch_sel(k_idx_reindex_select<256, 64>, 256);
     const int ept = (pool_blocks * 8 + kSelNT - 1) / kSelNT;
     auto sel = ept <= 8    ? k_idx_reindex_select<kSelNT, 8>
                : ept <= 16 ? k_idx_reindex_select<kSelNT, 16>
                            : k_idx_reindex_select<kSelNT, 32>;
-    hipLaunchKernelGGL(sel, dim3(n_q), dim3(kSelNT), 0, stream, ws.keys, ws.hist, pool, pool_blocks, top_k, idx_out);
-    return hipGetLastError();
+    return launch_sel(sel, kSelNT);
 }
 
 }  // namespace csa2

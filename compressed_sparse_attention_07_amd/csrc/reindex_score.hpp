@@ -1,0 +1,102 @@
+// Reindex-mode scoring of pool positions, shared by the standalone scoring kernel and the
+// one-kernel Reindex layer.
+//
+// Article "DeepSeek-V4.1-Flash: Pushing KV Cache Compression to 890 Bytes per Token", sections
+// VIII-IX: a Reindex layer scores its own indexer query against the Full layer's keys, over the
+// positions of the shared pool's blocks only.
+#pragma once
+
+#include "scan_common.hpp"
+
+namespace csa2 {
+
+constexpr int kXcds = 8;  // workgroup b runs on XCD b mod 8
+
+// Workgroup b scores chunk group `chunk` of query i.  When the group count is a multiple of
+// kXcds, XCD x takes the x-th eighth of every query's pool: a pool is ascending, so that eighth
+// covers about one eighth of the query's positions, and where queries read the same sequence
+// (the tokens of a prefill chunk) one XCD's workgroups read one eighth of its keys, a share
+// that stays in the XCD's L2.
+__device__ __forceinline__ void reindex_item(int b, int chunks, int& i, int& chunk) {
+    if (chunks % kXcds == 0) {
+        const int per = chunks / kXcds, j = b / kXcds;
+        i = j / per;
+        chunk = (b % kXcds) * per + j % per;
+    } else {
+        i = b / chunks;
+        chunk = b % chunks;
+    }
+}
+
+// Scores the pool slots of chunks [c0, c1) (kReindexTile positions each) of one query with NW
+// waves: one MFMA unit = two pool slots (16 positions, 1 KiB of contiguous bf16 keys each),
+// lanes r < 8 taking slot 2m and r >= 8 slot 2m + 1; wave wid takes units m0 + NW u.  Writes
+// each position's order-preserving key (0 for positions outside [0, n) or -1 slots) to keys
+// [slot * 8 + p % 8] and counts the first digit of every nonzero key in sh_hist (LDS).
+// COHERENT: the keys are written with agent-scope stores (written through to memory), for a
+// workgroup of another XCD that reads them inside the same kernel.
+template <int HI, bool MX, int NW, bool COHERENT>
+__device__ __forceinline__ void reindex_score_chunks(int c0, int c1, int n, int64_t row0,
+                                                     const int32_t* __restrict__ qpool, int pool_blocks,
+                                                     const QFrag& qf, const void* __restrict__ k_idx,
+                                                     const uint8_t* __restrict__ k_sc, uint32_t* __restrict__ keys,
+                                                     uint32_t* sh_hist) {
+    const int lane = __lane_id();
+    const int wid = threadIdx.x / kWave;
+    const int g = lane >> 4, r = lane & 15;
+    constexpr int kUnits = kReindexTile / 16 / NW;  // units per wave per chunk
+    for (int chunk = c0; chunk < c1; ++chunk) {
+        const int m0 = chunk * (kReindexTile / 16) + wid;
+        int blk[kUnits];
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+            const int slot = 2 * (m0 + NW * u) + (r >> 3);
+            blk[u] = slot < pool_blocks ? qpool[slot] : -1;
+        }
+        uint4 kb[kUnits][2];
+        uint32_t kc[kUnits][2], ks[kUnits];
+        if (n > 0) {
+            // absent rows read the sequence's first row (n > 0) and are masked below
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) {
+                const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
+                const bool ok = blk[u] >= 0 && p < n;
+                const int64_t kr = row0 + (ok ? p : 0);
+                if constexpr (MX) {
+                    const uint8_t* row = static_cast<const uint8_t*>(k_idx) + kr * 32 + 4 * g;
+                    kc[u][0] = *reinterpret_cast<const uint32_t*>(row);
+                    kc[u][1] = *reinterpret_cast<const uint32_t*>(row + 16);
+                    ks[u] = *reinterpret_cast<const uint16_t*>(k_sc + kr * 2);
+                } else {
+                    const uint16_t* row = static_cast<const uint16_t*>(k_idx) + kr * 64 + 8 * g;
+                    kb[u][0] = *reinterpret_cast<const uint4*>(row);
+                    kb[u][1] = *reinterpret_cast<const uint4*>(row + 32);
+                }
+            }
+            if constexpr (MX) {
+#pragma unroll
+                for (int u = 0; u < kUnits; ++u) {
+                    kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
+                    kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnits; ++u) {
+            const int slot = 2 * (m0 + NW * u) + (r >> 3);
+            const int64_t p = (int64_t)blk[u] * 8 + (r & 7);
+            const bool ok = n > 0 && blk[u] >= 0 && p < n;
+            const float sc = n > 0 ? mfma_score<HI>(qf, kb[u][0], kb[u][1]) : 0.f;
+            const uint32_t key = ok ? score_key(sc) : 0u;
+            if (g == 0 && slot < pool_blocks) {
+                if constexpr (COHERENT)
+                    __hip_atomic_store(&keys[slot * 8 + (r & 7)], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else
+                    keys[slot * 8 + (r & 7)] = key;
+                if (key) atomicAdd(&sh_hist[key >> 21], 1u);
+            }
+        }
+    }
+}
+
+}  // namespace csa2

@@ -41,6 +41,7 @@ T_SWA_SIGMA = 8
 T_LEN = 9
 T_NEW_KV = 10
 T_MISC = 11
+T_SWA_NEW = 12   # the decode step's own window vector per layer
 
 KV_CLIP = 26.0
 

@@ -93,7 +93,7 @@ class KvSet:
     new_rows: torch.Tensor    # int64 [B]: row each new token is written to
     k_codes: torch.Tensor | None = None
     k_scales: torch.Tensor | None = None
-    k_new: torch.Tensor | None = None    # bf16 [B, 64]: the step's new indexer key (MXFP4 sets)
+    k_new: torch.Tensor | None = None    # bf16 [B, 64]: the step's new indexer key
 
     def clone(self) -> "KvSet":
         c = lambda t: None if t is None else t.clone()
@@ -107,6 +107,9 @@ class Layer:
     kv_set: int
     q: torch.Tensor                  # bf16 [n_q, H, 128]
     swa: torch.Tensor                # bf16 [n_q * swa_cap, 128], or E4M3 bytes when the window is FP8
+    win_new: torch.Tensor | None = None   # decode: bf16 [n_q, 128], the step's own window vector per query
+    win_chunk: torch.Tensor | None = None  # prefill: bf16 [T, 128], the chunk's window vectors
+    win_rows: torch.Tensor | None = None   # prefill: int64 [T], their store rows
     q_idx: torch.Tensor | None = None
     w: torch.Tensor | None = None
     idx: torch.Tensor | None = None  # output of F/R layers
@@ -121,10 +124,10 @@ class Runner:
     def __init__(self, wl: Workload, device="cuda", keep_host=False, seed=0, copies=1, fused_reindex=False):
         """copies > 1 keeps that many device copies of the KV sets (identical values); step() then
         rotates through them so consecutive steps never re-read a set that a last-level cache
-        could still hold.  fused_reindex: Reindex layers run as csa2_reindex_attend (two
-        kernels) rather than csa2_index_reindex + csa2_attend (three).  Off by default: on
-        the decode workloads the fused form measured 1-2 % slower per step (its selection runs
-        with half the threads of the standalone one, which outweighs the saved launch)."""
+        could still hold.  fused_reindex: Reindex layers run as csa2_reindex_attend (one kernel)
+        rather than csa2_index_reindex + csa2_attend (three).  Off by default: on the decode
+        workloads the one-kernel form measured slower per step (the in-kernel hand-off from the
+        scoring workgroups to the selecting one costs more than a kernel boundary)."""
         self.wl = wl
         self.fused_reindex = fused_reindex
         self.device = device
@@ -173,13 +176,14 @@ class Runner:
             x_new = x_dev[new_rows_t].contiguous()
             del x_dev
             k_dev = bf16_dev(k, device)
+            k_new = k_dev[new_rows_t].contiguous()
             if wl.keys_mx:   # keys written by the library's MXFP4 append; the bf16 rows are dropped
                 kc = torch.empty((total_rows, 32), dtype=torch.uint8, device=device)
                 ks = torch.empty((total_rows, 2), dtype=torch.uint8, device=device)
                 C.mxfp4_key_append(k_dev, kc, ks)
-                st = KvSet(codes, scales, None, x_new, new_rows_t, kc, ks, k_dev[new_rows_t].contiguous())
+                st = KvSet(codes, scales, None, x_new, new_rows_t, kc, ks, k_new)
             else:
-                st = KvSet(codes, scales, k_dev, x_new, new_rows_t)
+                st = KvSet(codes, scales, k_dev, x_new, new_rows_t, k_new=k_new)
             del k_dev
             self.sets.append(st)
             if self.host is not None:
@@ -188,14 +192,16 @@ class Runner:
                 self.host.setdefault("new_rows", []).append(new_rows)
             del x, k
         # Scramble the new tokens' rows so the step's append is what makes them correct.
-        # (An MXFP4 key row becomes +6 * 2^10 in every channel: a large score, so a missing key
-        # append would change the selection.)
+        # (A key row becomes +6 * 2^10 (MXFP4) or 100 (bf16) in every channel: a large score, so a
+        # missing key write would change the selection.)
         for st in self.sets:
             st.codes[st.new_rows] = 0xEE
             st.scales[st.new_rows] = 0x77
             if st.k_codes is not None:
                 st.k_codes[st.new_rows] = 0x77
                 st.k_scales[st.new_rows] = 127 + 10
+            if st.k_idx is not None:
+                st.k_idx[st.new_rows] = 100.0
         self.copies = [self.sets]
         for _ in range(1, copies):
             self.copies.append([st.clone() for st in self.sets])
@@ -210,12 +216,32 @@ class Runner:
             q = synth.normal_bf16(wid, synth.T_Q, (self.n_q, wl.heads, 128), seq=l)
             ssig = synth.channel_sigma(wid, synth.T_SWA_SIGMA, 128, seq=l)
             swa = synth.kv_bf16(wid, synth.T_SWA, self.n_q_swa() * self.swa_cap, 128, ssig, seq=l)
-            swa_dev = bf16_dev(swa, device)
+            # The rows the step writes (decode: each query's position N - 1; prefill: the chunk's
+            # own positions) hold the step's vectors in the host copy (the store after the step)
+            # and a marker on the device until the step writes them (bf16 1000 / E4M3 448: a
+            # missing write would dominate the attention).
+            if wl.prefill_chunk:
+                new_pos = wl.context + np.arange(wl.prefill_chunk, dtype=np.int64)
+                new_row = new_pos % self.swa_cap
+                win_vec = swa[new_row]
+            else:
+                new_row = np.arange(self.n_q, dtype=np.int64) * self.swa_cap + (q_len - 1) % self.swa_cap
+                win_vec = synth.kv_bf16(wid, synth.T_SWA_NEW, self.n_q, 128, ssig, seq=l)
+                swa[new_row] = win_vec
+            self.win_rows_host = new_row                                  # the same rows in every layer
+            swa_before = swa.copy()
+            swa_before[new_row] = 0x447A                                  # bf16 1000.0
+            swa_dev = bf16_dev(swa_before, device)
             if wl.window_fp8:  # the window store is written by the library's FP8 append
                 swa8 = torch.empty(swa_dev.shape, dtype=torch.uint8, device=device)
                 C.fp8_window_append(swa_dev, swa8)
                 swa_dev = swa8
             L = Layer(m, cur_set, bf16_dev(q, device), swa_dev)
+            if wl.prefill_chunk:
+                L.win_chunk = bf16_dev(win_vec, device)
+                L.win_rows = torch.from_numpy(new_row).to(device)
+            else:
+                L.win_new = bf16_dev(win_vec, device)
             if m in "FR":
                 qi = synth.int_bf16(wid, synth.T_IDX_Q, (self.n_q, wl.idx_heads, 64), seq=l)
                 w = synth.int_weights(wid, synth.T_IDX_W, (self.n_q, wl.idx_heads), seq=l)
@@ -252,31 +278,42 @@ class Runner:
             C.OP_INDEX_FULL, self.n_q, self.seqs.total_len_ub, self.seqs.max_len_ub, wl.top_k, wl.pool_blocks))
         self.ws_re = C.alloc_workspace(C.csa2_workspace_bytes(
             C.OP_INDEX_REINDEX, self.n_q, 0, 0, wl.top_k, max(wl.pool_blocks, 1))) if "R" in wl.layers else None
-        self.ws_att = C.alloc_workspace(C.csa2_workspace_bytes(C.OP_ATTEND, self.n_q, 0, 0, wl.top_k, wl.window))
         self.scale = 1.0 / math.sqrt(128.0)
         torch.cuda.synchronize()
 
     def n_q_swa(self) -> int:
         return 1 if self.wl.prefill_chunk else self.n_q
 
-    def step(self, stream=None, scan_events=None, copy=None) -> None:
+    def step(self, stream=None, timing=None, copy=None) -> None:
         """One pass of the hot path: append the step's KV, then every layer in order.
-        scan_events: optional list; a (start, end) torch.cuda.Event pair recorded around each
-        Full-mode scan kernel is appended to it (for timing that kernel inside a timed loop).
+        timing: optional dict; the Full-mode scan ("scan"), each separate Reindex selection
+        ("reindex": scoring start to selection end) and each bf16-window attention ("attend") then
+        record their kernels' own start and end into a torch.cuda.Event pair appended to
+        timing[kind] (for timing those kernels inside a timed loop; not for graph capture).
         copy: which device copy of the KV sets to use (default: the next one in rotation)."""
         wl = self.wl
         if copy is None:
             copy = self._next_copy
             self._next_copy = (self._next_copy + 1) % len(self.copies)
         self.sets = self.copies[copy]
-        if wl.appends:
+        if wl.appends:   # the step's own token: FP4 KV row and indexer key row of every owned set
             for st in self.sets:
-                C.fp4_kv_append(st.x_new, st.codes, st.scales, dst_rows=st.new_rows, stream=stream)
-                if wl.keys_mx:
-                    C.mxfp4_key_append(st.k_new, st.k_codes, st.k_scales, dst_rows=st.new_rows, stream=stream)
+                C.csa2_token_append(st.x_new, st.new_rows, st.codes, st.scales, k_new=st.k_new,
+                                    k_idx=st.k_codes if wl.keys_mx else st.k_idx,
+                                    k_scales=st.k_scales if wl.keys_mx else None, stream=stream)
+        def ev_pair(kind):
+            # the two records only create the events; the kernels' launches record into them
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            e1.record()
+            timing.setdefault(kind, []).append((e0, e1))
+            return e0, e1
+
         pool_built = False
         for L in self.layers:
             st = self.sets[L.kv_set]
+            if L.win_chunk is not None:   # a prefill chunk's own window entries, before they are read
+                C.csa2_window_append(L.win_chunk, L.swa, dst_rows=L.win_rows, window_fp8=wl.window_fp8, stream=stream)
             if L.mode == "F":
                 want_pool = wl.pool_blocks if (self.pool is not None and not pool_built) else 0
                 pool = self.pool if want_pool else None
@@ -284,16 +321,11 @@ class Runner:
                 keys = st.k_codes if wl.keys_mx else st.k_idx    # prep and select read no keys
                 C.csa2_index_full_prep(L.q_idx, L.w, keys, self.seqs, wl.top_k, want_pool, L.idx, pool,
                                        self.ws_full, shared_kv=shared, stream=stream)
-                if scan_events is not None:
-                    # the scan kernel's own start and end, recorded by its launch (the two records
-                    # here only create the events)
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                    e1.record()
+                if timing is not None:
+                    e0, e1 = ev_pair("scan")
                     C.csa2_index_full_scan_timed(L.q_idx, L.w, st.k_codes if wl.keys_mx else st.k_idx,
                                                  st.k_scales if wl.keys_mx else None, self.seqs, wl.top_k, want_pool,
                                                  L.idx, pool, self.ws_full, e0, e1, shared_kv=shared, stream=stream)
-                    scan_events.append((e0, e1))
                 elif wl.keys_mx:
                     C.csa2_index_full_mx_scan(L.q_idx, L.w, st.k_codes, st.k_scales, self.seqs, wl.top_k, want_pool,
                                               L.idx, pool, self.ws_full, shared_kv=shared, stream=stream)
@@ -309,8 +341,14 @@ class Runner:
                                       st.k_scales if wl.keys_mx else None, self.seqs, self.pool, wl.top_k, L.idx, L.q,
                                       st.codes, st.scales, L.swa, self.swa_row0, self.swa_cap, wl.window, self.scale,
                                       L.out, self.ws_re, window_fp8=wl.window_fp8, replay_start=self.replay,
-                                      stream=stream)
+                                      win_new=L.win_new, stream=stream)
                 continue
+            elif L.mode == "R" and timing is not None:
+                e0, e1 = ev_pair("reindex")
+                C.csa2_index_reindex_timed(L.q_idx, L.w, st.k_codes if wl.keys_mx else st.k_idx,
+                                           st.k_scales if wl.keys_mx else None, self.seqs, self.pool, wl.top_k, L.idx,
+                                           self.ws_re, e0, e1, stream=stream)
+                idx = L.idx
             elif L.mode == "R":
                 if wl.keys_mx:
                     C.csa2_index_reindex_mx(L.q_idx, L.w, st.k_codes, st.k_scales, self.seqs, self.pool, wl.top_k,
@@ -323,11 +361,15 @@ class Runner:
                 idx = self.layers[L.idx_src].idx
             if wl.window_fp8:
                 C.csa2_attend_fp8win(L.q, st.codes, st.scales, self.seqs, idx, L.swa, self.swa_row0, self.swa_cap,
-                                     wl.window, self.scale, L.out, self.ws_att, replay_start=self.replay,
+                                     wl.window, self.scale, L.out, replay_start=self.replay, win_new=L.win_new,
                                      stream=stream)
+            elif timing is not None:
+                e0, e1 = ev_pair("attend")
+                C.csa2_attend_timed(L.q, st.codes, st.scales, self.seqs, idx, L.swa, self.swa_row0, self.swa_cap,
+                                    wl.window, self.scale, L.out, e0, e1, win_new=L.win_new, stream=stream)
             else:
                 C.csa2_attend(L.q, st.codes, st.scales, self.seqs, idx, L.swa, self.swa_row0, self.swa_cap,
-                              wl.window, self.scale, L.out, self.ws_att, stream=stream)
+                              wl.window, self.scale, L.out, win_new=L.win_new, stream=stream)
 
     def capture(self):
         """Capture one step per KV copy into HIP graphs (torch.cuda.CUDAGraph on torch's current
@@ -349,6 +391,27 @@ class Runner:
         return graphs
 
     # ---- accounting of the bytes the method itself must move per step ----
+    def kernel_bytes(self) -> dict:
+        """Algorithmic bytes of ONE launch of each timed kernel family: "scan" (every visible key
+        once), "reindex" (scoring: every pool position's key, plus its 4-B order key written and
+        read back by the selection), "attend" (72 B per selected FP4 entry + one window entry per
+        window position + the query, the new window vector read and written, the output), and
+        "kv_gather" (the attention's cache gathers alone: selected entries and window entries)."""
+        wl = self.wl
+        key_bytes = 34 if wl.keys_mx else 128
+        win_entry = 128 if wl.window_fp8 else 256
+        win = np.minimum(self.q_len, wl.window)
+        if wl.window_fp8:
+            win = np.minimum(win, self.q_len - self.replay_host)
+        sel = np.minimum(self.q_len, wl.top_k)
+        gather = int(sel.sum()) * 72 + int(win.sum()) * win_entry
+        new_vec = 0 if wl.prefill_chunk else self.n_q * (256 + win_entry)
+        cand = self.n_q * min(wl.pool_blocks * 8, int(self.q_len.max())) if wl.pool_blocks else 0
+        return {"scan": int(self.q_len.sum()) * key_bytes,
+                "reindex": cand * (key_bytes + 8),
+                "attend": gather + self.n_q * wl.heads * 128 * (2 + 4) + new_vec,
+                "kv_gather": gather}
+
     def algorithmic_bytes(self) -> dict:
         """Bytes per step by kernel family (see the design notes for the per-unit figures)."""
         wl = self.wl
@@ -356,9 +419,12 @@ class Runner:
         out = {"append": 0, "index_full": 0, "index_reindex": 0, "attend": 0}
         n_sets = len(self.sets)
         key_bytes = 34 if wl.keys_mx else 128                     # MXFP4 or bf16 indexer key
-        if wl.appends:
+        win_entry = 128 if wl.window_fp8 else 256                    # E4M3 or bf16 window entry
+        if wl.appends:   # per token and owned set: KV in + FP4 out, key in + key out
             toks = (wl.prefill_chunk or self.n_q) * n_sets
-            out["append"] = toks * (256 + 72 + ((128 + 34) if wl.keys_mx else 0))
+            out["append"] = toks * (256 + 72 + 128 + (34 if wl.keys_mx else 128))
+        # every layer writes its own window entries: the step's token (decode) or the chunk's tokens
+        out["append"] += len(self.layers) * (wl.prefill_chunk or self.n_q) * (256 + win_entry)
         for L in self.layers:
             if L.mode == "F":
                 out["index_full"] += n_sum * key_bytes             # every visible indexer key, once

@@ -28,7 +28,7 @@
  *     skipped, destination rows outside [0, cap_rows) are not written.  Results are
  *     then those of the clamped problem.
  *   - Inputs are finite.  Results are deterministic run to run (no float atomics).
- *   - Workspace: index and attention calls take a caller-owned device workspace of
+ *   - Workspace: index calls take a caller-owned device workspace of
  *     at least csa2_workspace_bytes(...) bytes.  Every workspace starts with the same
  *     prefix for a given n_q: per-query counters (CSA2_CTRL_BYTES(n_q) bytes) and
  *     per-query histograms.  That prefix must be zero when a call starts and every
@@ -215,22 +215,6 @@ int csa2_index_full_mx_scan(const uint16_t* q_idx, const float* w, const uint8_t
                             const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, int32_t top_k,
                             int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
                             int32_t* pool_out, void* ws, size_t ws_bytes, void* stream);
-/*
- * csa2_index_full_scan_timed -- csa2_index_full_scan (k_scales == NULL: bf16 keys k_idx) or
- * csa2_index_full_mx_scan (k_scales != NULL: MXFP4 code bytes k_idx and their E8M0 scales), with
- * the scan kernel's own start and end recorded into two caller events, for timing that kernel
- * alone (the Full-mode scan of Article "DeepSeek-V4.1-Flash: Pushing KV Cache Compression to 890
- * Bytes per Token", section IX).  start_event, stop_event: hipEvent_t created by the caller (either
- * may be NULL: not recorded); the decode scan records them through its launch, a prefill chunk's
- * scoring kernels are bracketed by two event records on `stream`.  With an event given, a stream
- * under graph capture is refused (CSA2_ERR_UNSUPPORTED).  Arguments, workspace, outputs and errors
- * are otherwise those of the untimed calls; on an error nothing is launched or recorded.
- */
-int csa2_index_full_scan_timed(const uint16_t* q_idx, const float* w, const void* k_idx,
-                               const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, int32_t top_k,
-                               int32_t block, int32_t pool_blocks, int32_t shared_kv, int32_t* idx_out,
-                               int32_t* pool_out, void* ws, size_t ws_bytes, void* stream,
-                               void* start_event, void* stop_event);
 int csa2_index_reindex_mx(const uint16_t* q_idx, const float* w, const uint8_t* k_codes,
                           const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, const int32_t* pool,
                           int32_t pool_blocks, int32_t block, int32_t top_k, int32_t* idx_out, void* ws,
@@ -260,10 +244,11 @@ int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_
 /*
  * csa2_attend -- sparse attention of n_q queries over their selected FP4 entries
  * plus their bf16 sliding window.  [Article] section VI ("What one layer looks
- * like": own query, 512 selected entries plus the recent window) and section XI
- * (entries are dequantised before attention).
+ * like": own query, 512 selected entries plus the recent window, and every layer
+ * computes its own window entries) and section XI (entries are dequantised before
+ * attention).
  *
- *   q       device bf16 [n_q, n_heads, CSA2_KV_DIM].
+ *   q       device bf16 [n_q, n_heads, CSA2_KV_DIM], 16-byte aligned.
  *   codes, scales  the FP4 cache ([seqs.cache_rows, 64] and [seqs.cache_rows, 8]).
  *   idx     device int32 [n_q, top_k]: selected positions; entries outside [0, N_i)
  *           (e.g. -1 padding) are skipped.  A Reuse layer passes the idx of the
@@ -273,19 +258,24 @@ int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_
  *   swa_row0 device int64 [n_q]; swa_cap >= window (>= 1); rows outside
  *           [0, swa_rows) are skipped.
  *   window  window length W >= 0: query i attends positions [max(0, N_i - W), N_i).
+ *   win_new device bf16 [n_q, CSA2_KV_DIM] (16-byte aligned) or NULL: the new token's
+ *           own window vector of this layer (decode).  Query i attends it as position
+ *           N_i - 1 (that store row is not read) and the call writes it to that row,
+ *           after its own reads, also when the position falls outside the attended
+ *           window.  Rows written for one query must not be read by another query of
+ *           the same call (decode: one ring per sequence); a prefill chunk writes its
+ *           window rows with csa2_window_append first and passes NULL.
  *   n_heads 1..CSA2_MAX_Q_HEADS.  softmax_scale multiplies q.k.
  *   out     device fp32 [n_q, n_heads, CSA2_KV_DIM].
- *   ws, ws_bytes  unused by this implementation (pass NULL, 0); kept so that a future
- *           split-entry variant can take a workspace without an ABI change.
  *   swa_rows must be below 2^31.
  * Each entry's vector is both key and value.  One softmax runs over the selected
  * entries and the window entries together (no de-duplication).  A query with
- * nothing to attend gets zeros.  n_q == 0 is a no-op.
+ * nothing to attend gets zeros.  n_q == 0 is a no-op.  No workspace.
  */
 int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
-                const int32_t* idx, int32_t top_k, const uint16_t* swa, const int64_t* swa_row0,
-                int32_t swa_cap, int64_t swa_rows, int32_t window, int32_t n_heads,
-                float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+                const int32_t* idx, int32_t top_k, uint16_t* swa, const int64_t* swa_row0,
+                int32_t swa_cap, int64_t swa_rows, int32_t window, const uint16_t* win_new,
+                int32_t n_heads, float softmax_scale, float* out, void* stream);
 
 /*
  * csa2_attend_fp8win -- csa2_attend with the pages' window format and replay bound.
@@ -297,48 +287,86 @@ int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, 
  *                 fp8_window_append (the codes 0x7f / 0xff, NaN, are never written).
  *   replay_start  device int64 [n_q] or NULL (no bound): query i's window is
  *                 positions [max(replay_start[i], N_i - window, 0), N_i).
+ *   win_new       as for csa2_attend (bf16); it is converted to E4M3 as
+ *                 fp8_window_append does, attended in that form and written.
  * Every other argument, the layouts, the errors and the output are those of
  * csa2_attend.  Window values and FP4 values enter the contractions exactly (f16).
  */
 int csa2_attend_fp8win(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
-                       const int32_t* idx, int32_t top_k, const uint8_t* swa, const int64_t* swa_row0,
+                       const int32_t* idx, int32_t top_k, uint8_t* swa, const int64_t* swa_row0,
                        int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay_start,
-                       int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                       const uint16_t* win_new, int32_t n_heads, float softmax_scale, float* out,
                        void* stream);
 
 /*
- * csa2_reindex_attend -- one Reindex layer: csa2_index_reindex (or _mx) followed by
- * csa2_attend (or _fp8win) over the selection it produced, in two kernels instead of
- * three.  [Article] sections VIII-IX (a Reindex layer selects its own Top-K inside the
- * shared pool) and section VI (the layer then attends its selection plus its window).
+ * csa2_reindex_attend -- one Reindex layer in one kernel: csa2_index_reindex (or _mx)
+ * followed by csa2_attend (or _fp8win) over the selection it produced.  [Article]
+ * sections VIII-IX (a Reindex layer selects its own Top-K inside the shared pool) and
+ * section VI (the layer then attends its selection plus its window).
  *
  *   q_idx, w, pool, pool_blocks, block, top_k, idx_out, ws, ws_bytes: as for
  *           csa2_index_reindex (CSA2_OP_INDEX_REINDEX workspace); idx_heads is its n_heads.
  *   k_idx, k_scales  k_scales == NULL: bf16 keys [seqs.cache_rows, CSA2_IDX_DIM];
  *           otherwise MXFP4 keys as for csa2_index_reindex_mx (k_idx = the code bytes).
- *   q, codes, scales, swa, swa_row0, swa_cap, swa_rows, window, n_heads, softmax_scale,
- *   out: as for csa2_attend; window_fp8 = 0: swa holds bf16, 1: E4M3 bytes.
+ *   q, codes, scales, swa, swa_row0, swa_cap, swa_rows, window, win_new, n_heads,
+ *   softmax_scale, out: as for csa2_attend; window_fp8 = 0: swa holds bf16, 1: E4M3 bytes.
  *   replay_start  device int64 [n_q] or NULL: as for csa2_attend_fp8win (either format).
  * idx_out receives the selection (a Reuse layer that follows attends with it) and out
- * the attention, both equal to those of the two separate calls.  With pool_blocks * 8
- * <= 16,384 the selection and the attention run in one workgroup per query (the
- * selection never goes back through memory before the attention reads it); larger
- * pools take the separate selection and attention kernels.  All arguments are checked
- * before anything is launched; the errors are those of the two separate calls.
+ * the attention, both equal to those of the separate calls.  With pool_blocks * 8 <=
+ * 16,384 and top_k <= 1,024 it is one kernel: every workgroup scores one 512-position
+ * chunk of a pool, and the last workgroup of each query to finish (an agent-scope
+ * ticket counter in the workspace) selects and attends; larger sizes take the separate
+ * kernels.  On MI355X the separate calls measured faster (the in-kernel hand-off costs
+ * more than a kernel boundary), so this entry point is the single-launch form for
+ * callers that want one, not the fast path.  All arguments are checked before anything
+ * is launched; the errors are those of the separate calls.
  */
 int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
                         csa2_seqs seqs, int32_t idx_heads, const int32_t* pool, int32_t pool_blocks,
                         int32_t block, int32_t top_k, int32_t* idx_out, const uint16_t* q,
-                        const uint8_t* codes, const uint8_t* scales, const void* swa, int32_t window_fp8,
+                        const uint8_t* codes, const uint8_t* scales, void* swa, int32_t window_fp8,
                         const int64_t* swa_row0, int32_t swa_cap, int64_t swa_rows, int32_t window,
-                        const int64_t* replay_start, int32_t n_heads, float softmax_scale, float* out,
-                        void* ws, size_t ws_bytes, void* stream);
+                        const int64_t* replay_start, const uint16_t* win_new, int32_t n_heads,
+                        float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_token_append -- the decode step's own token for a Full layer's cache set: its
+ * post-RoPE KV vector packed into the FP4 cache (exactly as fp4_kv_append) and its indexer
+ * key written into the key cache, in one launch.  [Article] section VIII (a Full layer
+ * computes its main KV and its indexer key fresh) and section XI (main KV in FP4, indexer
+ * key in MXFP4; the workloads keep bf16 keys).
+ *
+ *   x        device bf16 [n_tok, CSA2_KV_DIM], 16-byte aligned.
+ *   k_new    device bf16 [n_tok, CSA2_IDX_DIM], 16-byte aligned, or NULL (no key written).
+ *   dst_rows device int64 [n_tok]: the row of token t in every cache; rows outside
+ *            [0, cap_rows) are skipped.
+ *   codes, scales  FP4 cache [cap_rows, 64] (8-byte aligned) and [cap_rows, 8].
+ *   k_idx, k_scales  k_scales == NULL: bf16 key cache [cap_rows, CSA2_IDX_DIM]; otherwise
+ *            MXFP4 code bytes [cap_rows, 32] and E8M0 scales [cap_rows, 2] (as
+ *            mxfp4_key_append); k_idx 16-byte aligned.
+ * n_tok == 0 is a no-op.
+ */
+int csa2_token_append(const uint16_t* x, const uint16_t* k_new, int64_t n_tok, const int64_t* dst_rows,
+                      uint8_t* codes, uint8_t* scales, void* k_idx, uint8_t* k_scales, int64_t cap_rows,
+                      void* stream);
+
+/*
+ * csa2_window_append -- write window vectors into a layer's window store ([Article]
+ * section VI: every layer computes its own window entries; section XI: the pages keep
+ * them at FP8).  window_fp8 = 0: bf16 rows (a copy); 1: E4M3 bytes as fp8_window_append.
+ *   x        device bf16 [n_tok, CSA2_KV_DIM], 16-byte aligned.
+ *   dst_rows device int64 [n_tok] or NULL (rows row0 .. row0 + n_tok - 1).
+ *   out      device store [cap_rows, CSA2_KV_DIM] of bf16 or E4M3 bytes, 16-byte aligned.
+ * Rows outside [0, cap_rows) named by dst_rows are skipped.  n_tok == 0 is a no-op.
+ */
+int csa2_window_append(const uint16_t* x, int64_t n_tok, const int64_t* dst_rows, int64_t row0, void* out,
+                       int32_t window_fp8, int64_t cap_rows, void* stream);
 
 /*
  * Workspace bytes for one call of `op` (CSA2_OP_*) with these sizes; SIZE_MAX if the
  * sizes are out of range, 0 if the call needs no workspace.  For CSA2_OP_ATTEND pass the
  * window length in `pool_blocks` (attention needs no workspace: it returns 0); for
- * CSA2_OP_INDEX_REINDEX total_len_ub and max_len_ub are unused.
+ * CSA2_OP_INDEX_REINDEX (also csa2_reindex_attend) total_len_ub and max_len_ub are unused.
  */
 size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32_t max_len_ub,
                             int32_t top_k, int32_t pool_blocks);

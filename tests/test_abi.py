@@ -1,4 +1,4 @@
-"""CPU checks of the C ABI library: it loads, exports every function include/csa2.h declares,
+"""CPU checks of the C ABI library: it loads, exports every function include/*.h declares,
 and rejects bad arguments on the host before any HIP call (no GPU needed: every call here
 fails validation, so nothing is launched)."""
 import ctypes
@@ -10,14 +10,17 @@ import pytest
 from compressed_sparse_attention_07_amd import csa2 as C
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "csa2.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
-    return sorted(set(names))
+    names = set()
+    for hp in HEADERS:
+        text = open(hp).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+([a-z_0-9]+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
@@ -88,9 +91,9 @@ def test_reindex_and_attend_validation():
                                 None) == C.ERR_WORKSPACE
     assert C.csa2_workspace_bytes(C.OP_ATTEND, 2, 0, 0, 512, 128) == 0     # attention needs none
 
-    def att(top_k=512, window=128, cap=128, heads=16, scale=0.1, idx=FAKE, swa=FAKE, swa_rows=1000):
-        return L.csa2_attend(FAKE, FAKE, FAKE, seqs(), idx, top_k, swa, FAKE, cap, swa_rows, window, heads,
-                             ctypes.c_float(scale), FAKE, None, 0, None)
+    def att(top_k=512, window=128, cap=128, heads=16, scale=0.1, idx=FAKE, swa=FAKE, swa_rows=1000, win_new=None):
+        return L.csa2_attend(FAKE, FAKE, FAKE, seqs(), idx, top_k, swa, FAKE, cap, swa_rows, window, win_new, heads,
+                             ctypes.c_float(scale), FAKE, None)
 
     assert att(heads=17) == C.ERR_SHAPE
     assert att(cap=100) == C.ERR_SHAPE          # the window ring must hold the window
@@ -101,6 +104,7 @@ def test_reindex_and_attend_validation():
     assert att(swa_rows=1 << 31) == C.ERR_SHAPE
     assert att(top_k=4097) == C.ERR_SHAPE
     assert att(window=4097, cap=5000) == C.ERR_SHAPE
+    assert att(win_new=ctypes.c_void_p(0x10008)) == C.ERR_SHAPE   # the new window vector must be 16-byte aligned
 
 
 def test_reindex_attend_validation():
@@ -111,7 +115,7 @@ def test_reindex_attend_validation():
     def call(pool_blocks=2048, top_k=512, idx_heads=4, heads=16, window=128, cap=128, fp8=0, k_scales=None,
              idx_out=FAKE, q=FAKE, swa=FAKE, ws_bytes=need_r, s=None):
         return L.csa2_reindex_attend(FAKE, FAKE, FAKE, k_scales, s or seqs(), idx_heads, FAKE, pool_blocks, 8, top_k,
-                                     idx_out, q, FAKE, FAKE, swa, fp8, FAKE, cap, 1000, window, None, heads,
+                                     idx_out, q, FAKE, FAKE, swa, fp8, FAKE, cap, 1000, window, None, None, heads,
                                      ctypes.c_float(0.1), FAKE, FAKE, ws_bytes, None)
 
     assert call(pool_blocks=0) == C.ERR_SHAPE
@@ -125,6 +129,27 @@ def test_reindex_attend_validation():
     assert call(ws_bytes=need_r - 1) == C.ERR_WORKSPACE
     assert call(k_scales=ctypes.c_void_p(0x10001)) == C.ERR_SHAPE    # MXFP4 scales must be 2-byte aligned
     assert call(s=seqs(n_q=0)) == C.OK
+
+
+def test_token_and_window_append_validation():
+    L = C.lib()
+    def tok(n=4, x=FAKE, k_new=None, dst=FAKE, codes=FAKE, scales=FAKE, k_idx=None, cap=100):
+        return L.csa2_token_append(x, k_new, n, dst, codes, scales, k_idx, None, cap, None)
+    assert tok(n=-1) == C.ERR_SHAPE
+    assert tok(n=0, x=None) == C.OK                          # nothing to do
+    assert tok(x=None) == C.ERR_NULL
+    assert tok(dst=None) == C.ERR_NULL                       # the decode step names its rows
+    assert tok(k_new=FAKE, k_idx=None) == C.ERR_NULL         # a key needs its cache
+    assert tok(x=ctypes.c_void_p(0x10008)) == C.ERR_SHAPE    # 16-byte aligned input
+    assert tok(codes=ctypes.c_void_p(0x10004)) == C.ERR_SHAPE
+
+    def win(n=4, x=FAKE, dst=None, row0=0, out=FAKE, fp8=0, cap=100):
+        return L.csa2_window_append(x, n, dst, row0, out, fp8, cap, None)
+    assert win(fp8=2) == C.ERR_SHAPE
+    assert win(out=None) == C.ERR_NULL
+    assert win(row0=98) == C.ERR_CAPACITY                    # rows 98..101 past a 100-row store
+    assert win(out=ctypes.c_void_p(0x10008)) == C.ERR_SHAPE
+    assert win(n=0, x=None) == C.OK
 
 
 def test_workspace_sizes():

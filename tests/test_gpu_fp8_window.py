@@ -60,7 +60,7 @@ class Fp8Case(AttendCase):
         idx = torch.from_numpy(np.ascontiguousarray(idx_np.astype(np.int32))).to(DEV)
         rs = None if replay is None else torch.from_numpy(np.asarray(replay, dtype=np.int64)).to(DEV)
         C.csa2_attend_fp8win(self.q_dev, self.codes, self.scales, self.seqs, idx, self.swa8, self.swa_row0_dev,
-                             self.swa_cap, self.window, scale, out, C.alloc_workspace(0), replay_start=rs)
+                             self.swa_cap, self.window, scale, out, replay_start=rs)
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
@@ -126,3 +126,55 @@ def test_fp8_window_many_queries_several_rounds():
     replay = [int(rng.integers(0, n + 1)) for n in lengths]
     scale = 1 / np.sqrt(128)
     case.check8(case.run8(idx, scale, replay), idx, scale, replay)
+
+
+@pytest.mark.parametrize("window,cap,top_k", [(128, 128, 512), (256, 300, 1024), (16, 16, 16)])
+def test_new_window_vector_attended_and_written(window, cap, top_k):
+    # win_new: the step's own window vector per query ([Article] section VI: every layer computes
+    # its own window entries).  The call attends it as position N - 1 and writes it to that row of
+    # the store (E4M3 for an FP8 store), also when a replay start keeps it out of the window; the
+    # store's old row is never read (it holds a marker here).
+    lengths = [3000, 129, 1, 700, 0, 4096]
+    n_q = len(lengths)
+    for fp8 in (False, True):
+        case = Fp8Case(34, lengths, n_heads=16, window=window, swa_cap=cap)
+        new = synth.kv_bf16(34, synth.T_SWA_NEW, n_q, 128, synth.channel_sigma(34, synth.T_SWA_SIGMA, 128))
+        rows = np.array([i * cap + (n - 1) % cap for i, n in enumerate(lengths) if n > 0])
+        truth = case.swa.copy()
+        truth[rows] = new[[i for i, n in enumerate(lengths) if n > 0]]
+        before = truth.copy()
+        before[rows] = 0x447A                                   # bf16 1000: a marker the call overwrites
+        idx = _idx_for(lengths, top_k, 34)
+        scale = 1 / np.sqrt(128)
+        replay = [2990, 0, 0, 700, 0, 0]                       # query 3's window excludes position N - 1
+        out = torch.full((n_q, 16, 128), float("nan"), dtype=torch.float32, device=DEV)
+        idx_t = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+        if fp8:
+            store = torch.zeros(before.shape, dtype=torch.uint8, device=DEV)
+            C.fp8_window_append(bf16_tensor(before), store)
+            C.csa2_attend_fp8win(case.q_dev, case.codes, case.scales, case.seqs, idx_t, store, case.swa_row0_dev,
+                                 cap, window, scale, out, replay_start=torch.tensor(replay, device=DEV),
+                                 win_new=bf16_tensor(new))
+        else:
+            store = bf16_tensor(before)
+            C.csa2_attend(case.q_dev, case.codes, case.scales, case.seqs, idx_t, store, case.swa_row0_dev, cap,
+                          window, scale, out, win_new=bf16_tensor(new))
+        torch.cuda.synchronize()
+        got_store = store.cpu().numpy() if fp8 else store.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got_store, O.e4m3_quantize(truth) if fp8 else truth), fp8
+        res = out.cpu().numpy()
+        for i, n in enumerate(lengths):
+            r0 = int(case.row0[i])
+            if fp8:
+                s8 = O.e4m3_quantize(truth)
+                ref = O.attend_fp8_window(case.q[i], case.codes_ref[r0:r0 + n], case.scales_ref[r0:r0 + n], n,
+                                          idx[i], s8, i * cap, cap, window, scale, replay_start=replay[i])
+                vmax = O.attended_max_abs_fp8(case.codes_ref[r0:r0 + n], case.scales_ref[r0:r0 + n], n, idx[i],
+                                              s8, i * cap, cap, window, replay_start=replay[i])
+            else:
+                ref = O.attend(case.q[i], case.codes_ref[r0:r0 + n], case.scales_ref[r0:r0 + n], n, idx[i], truth,
+                               i * cap, cap, window, scale)
+                vmax = O.attended_max_abs(case.codes_ref[r0:r0 + n], case.scales_ref[r0:r0 + n], n, idx[i], truth,
+                                          i * cap, cap, window)
+            err = float(np.abs(res[i].astype(np.float64) - ref).max())
+            assert err <= ATT_TOL * vmax if vmax > 0 else err == 0.0, (fp8, i, err, vmax)

@@ -84,6 +84,60 @@ def test_fp4_pack_scatter_rows_and_skips_out_of_range():
             assert np.all(cg[r] == 0xAB) and np.all(sg[r] == 0xCD)
 
 
+@pytest.mark.parametrize("mx", [False, True])
+def test_token_append_kv_and_key_rows(mx):
+    # the decode step's own token of a Full layer's set: FP4 KV row (as fp4_kv_append) and its
+    # indexer key row (a bf16 copy, or MXFP4 as mxfp4_key_append) in one launch; rows outside
+    # the cache are skipped and every other row is left alone
+    n, cap = 37, 300
+    x = synth.kv_bf16(W_T + 7, synth.T_NEW_KV, n, 128, synth.channel_sigma(W_T + 7, synth.T_KV_SIGMA, 128))
+    k = synth.int_bf16(W_T + 7, synth.T_IDX_K, (n, 64), seq=1)
+    rows = np.random.default_rng(7).permutation(cap)[:n].astype(np.int64)
+    rows[3], rows[11] = -1, cap + 5
+    codes = torch.full((cap, 64), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((cap, 8), 0x5A, dtype=torch.uint8, device=DEV)
+    if mx:
+        kc = torch.full((cap, 32), 0x5A, dtype=torch.uint8, device=DEV)
+        ks = torch.full((cap, 2), 0x5A, dtype=torch.uint8, device=DEV)
+        C.csa2_token_append(bf16_tensor(x), torch.from_numpy(rows).to(DEV), codes, scales, k_new=bf16_tensor(k),
+                            k_idx=kc, k_scales=ks)
+    else:
+        kb = torch.full((cap, 64), 0x5A5A, dtype=torch.int16, device=DEV)
+        C.csa2_token_append(bf16_tensor(x), torch.from_numpy(rows).to(DEV), codes, scales, k_new=bf16_tensor(k),
+                            k_idx=kb)
+    torch.cuda.synchronize()
+    c_ref, s_ref = O.fp4_quantize(x)
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    ok = (rows >= 0) & (rows < cap)
+    assert np.array_equal(got_c[rows[ok]], c_ref[ok]) and np.array_equal(got_s[rows[ok]], s_ref[ok])
+    untouched = np.setdiff1d(np.arange(cap), rows[ok])
+    assert (got_c[untouched] == 0x5A).all() and (got_s[untouched] == 0x5A).all()
+    if mx:
+        kc_ref, ks_ref = O.mxfp4_quantize(k)
+        assert np.array_equal(kc.cpu().numpy()[rows[ok]], kc_ref[ok])
+        assert np.array_equal(ks.cpu().numpy()[rows[ok]], ks_ref[ok])
+        assert (kc.cpu().numpy()[untouched] == 0x5A).all()
+    else:
+        got_k = kb.cpu().numpy().view(np.uint16)
+        assert np.array_equal(got_k[rows[ok]], k[ok])
+        assert (got_k[untouched] == 0x5A5A).all()
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_window_append_rows(fp8):
+    x = synth.kv_bf16(W_T + 8, synth.T_SWA, 50, 128, synth.channel_sigma(W_T + 8, synth.T_SWA_SIGMA, 128))
+    rows = np.arange(50, dtype=np.int64)[::-1].copy() * 2
+    rows[0] = 1000                                              # outside: skipped
+    store = torch.zeros((100, 128), dtype=torch.uint8 if fp8 else torch.int16, device=DEV)
+    C.csa2_window_append(bf16_tensor(x), store, dst_rows=torch.from_numpy(rows).to(DEV), window_fp8=fp8)
+    torch.cuda.synchronize()
+    got = store.cpu().numpy()
+    want = O.e4m3_quantize(x) if fp8 else x
+    got = got if fp8 else got.view(np.uint16)
+    assert np.array_equal(got[rows[1:]], want[1:])
+    assert (got[1::2] == 0).all()
+
+
 def test_fp4_pack_row_offset_appends():
     sig = synth.channel_sigma(W_T, synth.T_KV_SIGMA, 128, seq=78)
     x = synth.kv_bf16(W_T, synth.T_KV, 10, 128, sig, seq=78)
@@ -421,9 +475,9 @@ def test_index_reindex_unsorted_pool_follows_element_order():
 
 @pytest.mark.parametrize("pool_blocks,top_k,window", [(2048, 512, 128), (300, 64, 0), (3000, 512, 128), (1, 4, 16)])
 def test_reindex_attend_equals_separate_calls_and_oracle(pool_blocks, top_k, window):
-    # csa2_reindex_attend (fused selection + attention for pools of <= 2,048 blocks, the
-    # separate kernels above that) against csa2_index_reindex followed by csa2_attend: the
-    # same indices and bit-identical outputs; indices and outputs also against the oracle
+    # csa2_reindex_attend (one kernel for pools of <= 2,048 blocks, the separate kernels above
+    # that) against csa2_index_reindex followed by csa2_attend: the same indices and
+    # bit-identical outputs; indices and outputs also against the oracle
     lengths = [40000, 777, 0, 16, 25001]
     ic = IndexCase(W_T + 70, lengths, n_heads=4)
     ac = AttendCase(W_T + 70, lengths, n_heads=16, window=max(window, 1), swa_cap=128)
@@ -437,7 +491,7 @@ def test_reindex_attend_equals_separate_calls_and_oracle(pool_blocks, top_k, win
     n_q = len(lengths)
     out_a = torch.empty((n_q, 16, 128), dtype=torch.float32, device=DEV)
     C.csa2_attend(ac.q_dev, ac.codes, ac.scales, ac.seqs, torch.from_numpy(idx_a).to(DEV), ac.swa_dev,
-                  ac.swa_row0_dev, ac.swa_cap, window, scale, out_a, C.alloc_workspace(0))
+                  ac.swa_row0_dev, ac.swa_cap, window, scale, out_a)
     ws = C.alloc_workspace(C.csa2_workspace_bytes(C.OP_INDEX_REINDEX, n_q, 0, 0, top_k, pool_blocks))
     idx_b = torch.full((n_q, top_k), -7, dtype=torch.int32, device=DEV)
     out_b = torch.full((n_q, 16, 128), float("nan"), dtype=torch.float32, device=DEV)

@@ -33,6 +33,16 @@ def _prefill_tokens(T=4096):
 
 def _check_rows(r, rows_sample):
     wl, h = r.wl, r.host
+    # every layer's window rows the step wrote (decode: position N - 1 of each query's ring;
+    # prefill: the chunk's own positions), bit-exact (E4M3 stores: the oracle's conversion)
+    rows_t = torch.from_numpy(r.win_rows_host).to(r.layers[0].swa.device)
+    for l, L in enumerate(r.layers):
+        want = h["swa"][l][r.win_rows_host]
+        if wl.window_fp8:
+            assert np.array_equal(L.swa[rows_t].cpu().numpy(), O.e4m3_quantize(want)), f"fp8 window rows {l}"
+        else:
+            assert np.array_equal(L.swa[rows_t].view(torch.int16).cpu().numpy().view(np.uint16), want), \
+                f"window rows {l}"
     rng = np.random.default_rng(wl.wid)
     for s, st in enumerate(r.sets):
         rows = np.unique(np.concatenate([h["new_rows"][s], rng.integers(0, r.rows, rows_sample)]))
