@@ -10,7 +10,7 @@ Prints ONE JSON line.  `value` is decode tokens/s of the batched 64K-context wor
 (32 sequences x 65,536 positions, 8 layers F R R R U U U U), timed over K replays of the step
 captured in HIP graphs (the host issues one launch per step); the 1M-context workload (8 x 2^20,
 20 layers) is reported in the same line under "also".  `kernels` lists the step's timed kernels
-(the Full scan, the Reindex selection pair, the attention), each timed with HIP events its own
+(the Full scan, the Reindex scoring and selection, the attention), each timed with HIP events its own
 launches record at the kernel's start and end in K eager steps, with its share of the step, its
 algorithmic GB/s and its fraction of HBM peak; `roofline` is the entry with the largest share.
 `kv_gather` is the attention's cache gathers (72 B per selected FP4 entry, 256 B per bf16 window
@@ -46,8 +46,8 @@ METRIC = "CSA2 decode tokens/s at 64K & 1M ctx; KV gather GB/s vs HBM peak"
 DTYPE = "f16/bf16 MFMA, fp32 accumulate"
 STORAGE = ("main KV FP4 (E2M1 + E4M3 per 16 ch); indexer keys bf16 (MXFP4 in the mxkeys workloads); "
            "window bf16 (E4M3 in the fp8win workloads); scores, softmax and outputs fp32")
-KERNEL_NAMES = {"scan": "k_idx_score_full", "reindex": "k_idx_reindex_score + k_idx_reindex_select",
-                "attend": "k_attend"}
+KERNEL_NAMES = {"scan": "k_idx_score_full", "reindex_score": "k_idx_reindex_score",
+                "reindex_select": "k_idx_reindex_select", "attend": "k_attend"}
 
 
 _SLEEP_CYCLES_PER_S = None
@@ -122,7 +122,7 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
         "input_copies": copies,
     }
     kernels = []
-    for k in ("scan", "reindex", "attend"):
+    for k in ("scan", "reindex_score", "reindex_select", "attend"):
         if k not in avg_us:
             continue
         e = {"kernel": KERNEL_NAMES[k], "family": k, "avg_launch_us": round(avg_us[k], 2),

@@ -95,7 +95,8 @@ def lib() -> ctypes.CDLL:
         L.csa2_reindex_attend.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp,
                                           i32, i64, i32, vp, vp, i32, f32, vp, vp, sz, vp]
         L.csa2_token_append.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, vp]
-        L.csa2_index_reindex_timed.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp, vp, vp]
+        L.csa2_index_reindex_timed.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp, vp, vp,
+                                               vp, vp]
         L.csa2_attend_timed.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp, vp,
                                         vp]
         L.csa2_window_append.argtypes = [vp, i64, vp, i64, vp, i32, i64, vp]
@@ -321,13 +322,14 @@ def _event(e):
     return ctypes.c_void_p(e.cuda_event) if e is not None else None
 
 
-def csa2_index_reindex_timed(q_idx, w, k_idx, k_scales, seqs: Seqs, pool, top_k: int, idx_out, ws, start_event,
-                             stop_event, block: int = BLOCK, stream=None) -> None:
-    """csa2_index_reindex (or _mx with k_scales) with the scoring kernel's start and the selection
-    kernel's end recorded into two torch.cuda.Event objects (recorded once already)."""
+def csa2_index_reindex_timed(q_idx, w, k_idx, k_scales, seqs: Seqs, pool, top_k: int, idx_out, ws, score_events,
+                             select_events, block: int = BLOCK, stream=None) -> None:
+    """csa2_index_reindex (or _mx with k_scales) with the scoring kernel's and the selection
+    kernel's own start and end recorded into two pairs of torch.cuda.Event objects."""
     _check("csa2_index_reindex_timed", lib().csa2_index_reindex_timed(
         _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scales), seqs.c(), q_idx.shape[1], _ptr(pool), pool.shape[1], block,
-        top_k, _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream), _event(start_event), _event(stop_event)))
+        top_k, _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream), _event(score_events[0]), _event(score_events[1]),
+        _event(select_events[0]), _event(select_events[1])))
 
 
 def csa2_attend_timed(q, codes, scales, seqs: Seqs, idx, swa, swa_row0, swa_cap: int, window: int,

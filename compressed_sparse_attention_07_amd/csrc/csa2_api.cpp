@@ -56,7 +56,8 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
                                 int64_t cache_rows, int n_heads, const int32_t* pool, int pool_blocks, int top_k,
                                 const IndexWs& ws, int32_t* idx_out, int select, hipStream_t stream,
-                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                                hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
+                                hipEvent_t ev_sel_start = nullptr, hipEvent_t ev_sel_stop = nullptr);
 hipError_t launch_reindex_layer(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
                                 int idx_heads, const int32_t* pool, int pool_blocks, const IndexWs& ws,
                                 int32_t* idx_out, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
@@ -297,7 +298,8 @@ static int check_reindex(const uint16_t* q_idx, const float* w, const void* k_id
 static int index_reindex_common(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
                                 const csa2_seqs& seqs, int32_t n_heads, const int32_t* pool, int32_t pool_blocks,
                                 int32_t block, int32_t top_k, int32_t* idx_out, void* ws, size_t ws_bytes,
-                                void* stream, void* ev_start = nullptr, void* ev_stop = nullptr) {
+                                void* stream, void* ev_start = nullptr, void* ev_stop = nullptr,
+                                void* ev_sel_start = nullptr, void* ev_sel_stop = nullptr) {
     const int st = check_reindex(q_idx, w, k_idx, k_sc, mx, seqs, n_heads, pool, pool_blocks, block, top_k, idx_out,
                                  ws, ws_bytes);
     if (st || seqs.n_q == 0) return st;
@@ -306,7 +308,9 @@ static int index_reindex_common(const uint16_t* q_idx, const float* w, const voi
     return launch_status(launch_index_reindex(q_idx, w, k_idx, k_sc, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
                                               seqs.max_len_ub, seqs.cache_rows, n_heads, pool, pool_blocks, top_k,
                                               wsp, idx_out, 1, static_cast<hipStream_t>(stream),
-                                              static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)));
+                                              static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop),
+                                              static_cast<hipEvent_t>(ev_sel_start),
+                                              static_cast<hipEvent_t>(ev_sel_stop)));
 }
 
 int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs, int32_t n_heads,
@@ -366,11 +370,13 @@ int csa2_index_full_scan_timed(const uint16_t* q_idx, const float* w, const void
 int csa2_index_reindex_timed(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
                              csa2_seqs seqs, int32_t n_heads, const int32_t* pool, int32_t pool_blocks, int32_t block,
                              int32_t top_k, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream,
-                             void* start_event, void* stop_event) {
-    const int st = refuse_capture(stream, start_event, stop_event);
+                             void* score_start, void* score_stop, void* select_start, void* select_stop) {
+    int st = refuse_capture(stream, score_start, score_stop);
+    if (st == CSA2_OK) st = refuse_capture(stream, select_start, select_stop);
     if (st) return st;
     return index_reindex_common(q_idx, w, k_idx, k_scales, k_scales != nullptr ? 1 : 0, seqs, n_heads, pool,
-                                pool_blocks, block, top_k, idx_out, ws, ws_bytes, stream, start_event, stop_event);
+                                pool_blocks, block, top_k, idx_out, ws, ws_bytes, stream, score_start, score_stop,
+                                select_start, select_stop);
 }
 
 int csa2_index_reindex_mx(const uint16_t* q_idx, const float* w, const uint8_t* k_codes, const uint8_t* k_scales,

@@ -1007,7 +1007,8 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
                                 const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
                                 int64_t cache_rows, int n_heads, const int32_t* pool, int pool_blocks, int top_k,
                                 const IndexWs& ws, int32_t* idx_out, int select, hipStream_t stream,
-                                hipEvent_t ev_start, hipEvent_t ev_stop) {
+                                hipEvent_t ev_start, hipEvent_t ev_stop, hipEvent_t ev_sel_start,
+                                hipEvent_t ev_sel_stop) {
     const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
     // many queries (>= 512: a prefill chunk): a whole pool of 32 chunks per workgroup, one histogram
     // flush per query instead of one per chunk
@@ -1015,10 +1016,10 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
     const dim3 grid((unsigned)(chunks / cpw * n_q));  // (query, chunk group) items, see reindex_item
     auto kern = mx ? (n_heads <= 4 ? k_idx_reindex_score<4, true> : k_idx_reindex_score<8, true>)
                    : (n_heads <= 4 ? k_idx_reindex_score<4, false> : k_idx_reindex_score<8, false>);
-    // ev_start / ev_stop (may be null): the scoring kernel's start and the selection kernel's end,
-    // recorded by their launches
-    if (ev_start != nullptr)
-        hipExtLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, ev_start, nullptr, 0, pool, q_idx, w, kv_row0,
+    // ev_start / ev_stop, ev_sel_start / ev_sel_stop (may be null): the scoring kernel's and the
+    // selection kernel's own start and end, recorded by their launches
+    if (ev_start != nullptr || ev_stop != nullptr)
+        hipExtLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, ev_start, ev_stop, 0, pool, q_idx, w, kv_row0,
                               kv_len, pool_blocks, n_heads, cpw, max_len, k_idx, k_sc, cache_rows, ws);
     else
         hipLaunchKernelGGL(kern, grid, dim3(kScoreNT), 0, stream, pool, q_idx, w, kv_row0, kv_len, pool_blocks,
@@ -1026,9 +1027,9 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !select) return e;
     auto launch_sel = [&](auto kernel, int nt) {
-        if (ev_stop != nullptr)
-            hipExtLaunchKernelGGL(kernel, dim3(n_q), dim3(nt), 0, stream, nullptr, ev_stop, 0, ws.keys, ws.hist, pool,
-                                  pool_blocks, top_k, idx_out);
+        if (ev_sel_start != nullptr || ev_sel_stop != nullptr)
+            hipExtLaunchKernelGGL(kernel, dim3(n_q), dim3(nt), 0, stream, ev_sel_start, ev_sel_stop, 0, ws.keys, ws.hist,
+                                  pool, pool_blocks, top_k, idx_out);
         else
             hipLaunchKernelGGL(kernel, dim3(n_q), dim3(nt), 0, stream, ws.keys, ws.hist, pool, pool_blocks, top_k,
                                idx_out);

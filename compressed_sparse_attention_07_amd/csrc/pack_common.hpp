@@ -51,25 +51,62 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t bits16, float s) {
     return mag | ((bits16 >> 12) & 0x8u);
 }
 
+// E2M1 codes of two bf16 values at once (one per 16-bit half of w) against a group's seven
+// midpoint thresholds T[k] (t_k = m_k * s as a bf16 bit pattern in both halves; all ones for a zero
+// scale, so every magnitude codes 0).  Each t_k has at most 7 significant bits (an E4M3 scale
+// times a midpoint of the E2M1 grid), so it is an exact bf16 value, and for non-negative values
+// the 15-bit patterns order like the values: the comparisons are 16-bit integer ones, two values
+// per instruction.  The seven compares of e2m1_code become a three-level tree: c4 = |x| >= t3,
+// then t5 or t1 (>=), then one of t6, t4, t2, t0 (>); the tie rules are e2m1_code's.
+// Returns the 4-bit codes (sign bit 3) in bits 0..3 and 16..19.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t lt16_mask(uint32_t a, uint32_t b) {  // all ones in a half where a < b
+    const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, a) - __builtin_bit_cast(u16x2_t, b));
+    uint32_t m;
+    // the sign of each 16-bit difference spread over its half (one packed shift; written out
+    // because the compiler otherwise compares and selects each half on its own).  The shift
+    // amount is a register holding 15 in both halves: a packed instruction's high half reads
+    // bits 31..16 of each operand, which an inline constant 15 leaves zero.
+    asm("v_pk_ashrrev_i16 %0, %1, %2" : "=v"(m) : "s"(0x000f000fu), "v"(d));
+    return m;
+}
+
+__device__ __forceinline__ uint32_t pick(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
+
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t w, const uint32_t (&T)[7]) {
+    const uint32_t A = w & 0x7fff7fffu;
+    const uint32_t m4 = lt16_mask(A, T[3]);           // |x| < t3
+    const uint32_t m2 = lt16_mask(A, pick(m4, T[1], T[5]));
+    const uint32_t tl = pick(m4, pick(m2, T[0], T[2]), pick(m2, T[4], T[6]));
+    const uint32_t m1 = lt16_mask(tl, A);             // |x| > the last threshold
+    return (~m4 & 0x00040004u) | (~m2 & 0x00020002u) | (m1 & 0x00010001u) | ((w >> 12) & 0x00080008u);
+}
+
 // One 16-channel FP4 group: w = 8 dwords of bf16 pairs (channel 2k in the low half) ->
 // codes (lo: channels 0..7, hi: 8..15; low nibble = even channel) and the E4M3 scale code.
 __device__ __forceinline__ uint32_t fp4_pack_group(const uint32_t (&w)[8], uint32_t& lo, uint32_t& hi) {
     // amax: bf16 magnitudes order like their 15-bit patterns
     uint32_t am = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        am = max(am, w[k] & 0x7fffu);
-        am = max(am, (w[k] >> 16) & 0x7fffu);
-    }
+    for (int k = 0; k < 8; ++k) am = max(am, max(w[k] & 0x7fffu, (w[k] >> 16) & 0x7fffu));
     const int sc = e4m3_round_amax_over_6(__uint_as_float(am << 16));
     const float s = e4m3_pos_value(sc);
-    lo = 0;
-    hi = 0;
+    constexpr float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+    uint32_t T[7];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        lo |= (e2m1_code(w[k] & 0xffffu, s) | (e2m1_code(w[k] >> 16, s) << 4)) << (8 * k);
-        hi |= (e2m1_code(w[k + 4] & 0xffffu, s) | (e2m1_code(w[k + 4] >> 16, s) << 4)) << (8 * k);
+    for (int k = 0; k < 7; ++k) {
+        const uint32_t b = __float_as_uint(kMid[k] * s) >> 16;  // exact (low half is zero)
+        T[k] = sc == 0 ? 0x7fff7fffu : (b | (b << 16));
     }
+    uint32_t byte[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t c = e2m1_pair(w[k], T);
+        byte[k] = (c | (c >> 12)) & 0xffu;  // channel 2k in the low nibble, 2k + 1 in the high one
+    }
+    lo = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
+    hi = byte[4] | (byte[5] << 8) | (byte[6] << 16) | (byte[7] << 24);
     return (uint32_t)sc;
 }
 

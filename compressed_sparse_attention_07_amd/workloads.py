@@ -286,10 +286,10 @@ class Runner:
 
     def step(self, stream=None, timing=None, copy=None) -> None:
         """One pass of the hot path: append the step's KV, then every layer in order.
-        timing: optional dict; the Full-mode scan ("scan"), each separate Reindex selection
-        ("reindex": scoring start to selection end) and each bf16-window attention ("attend") then
-        record their kernels' own start and end into a torch.cuda.Event pair appended to
-        timing[kind] (for timing those kernels inside a timed loop; not for graph capture).
+        timing: optional dict; the Full-mode scan ("scan"), the two kernels of each separate Reindex
+        selection ("reindex_score", "reindex_select") and each bf16-window attention ("attend") then
+        record their own start and end into a torch.cuda.Event pair appended to timing[kind] (for
+        timing those kernels inside a timed loop; not for graph capture).
         copy: which device copy of the KV sets to use (default: the next one in rotation)."""
         wl = self.wl
         if copy is None:
@@ -344,10 +344,10 @@ class Runner:
                                       win_new=L.win_new, stream=stream)
                 continue
             elif L.mode == "R" and timing is not None:
-                e0, e1 = ev_pair("reindex")
                 C.csa2_index_reindex_timed(L.q_idx, L.w, st.k_codes if wl.keys_mx else st.k_idx,
                                            st.k_scales if wl.keys_mx else None, self.seqs, self.pool, wl.top_k, L.idx,
-                                           self.ws_re, e0, e1, stream=stream)
+                                           self.ws_re, ev_pair("reindex_score"), ev_pair("reindex_select"),
+                                           stream=stream)
                 idx = L.idx
             elif L.mode == "R":
                 if wl.keys_mx:
@@ -392,9 +392,9 @@ class Runner:
 
     # ---- accounting of the bytes the method itself must move per step ----
     def kernel_bytes(self) -> dict:
-        """Algorithmic bytes of ONE launch of each timed kernel family: "scan" (every visible key
-        once), "reindex" (scoring: every pool position's key, plus its 4-B order key written and
-        read back by the selection), "attend" (72 B per selected FP4 entry + one window entry per
+        """Algorithmic bytes of ONE launch of each timed kernel: "scan" (every visible key once),
+        "reindex_score" (every pool position's key read, its 4-B order key written),
+        "reindex_select" (those order keys read back), "attend" (72 B per selected FP4 entry + one window entry per
         window position + the query, the new window vector read and written, the output), and
         "kv_gather" (the attention's cache gathers alone: selected entries and window entries)."""
         wl = self.wl
@@ -408,7 +408,8 @@ class Runner:
         new_vec = 0 if wl.prefill_chunk else self.n_q * (256 + win_entry)
         cand = self.n_q * min(wl.pool_blocks * 8, int(self.q_len.max())) if wl.pool_blocks else 0
         return {"scan": int(self.q_len.sum()) * key_bytes,
-                "reindex": cand * (key_bytes + 8),
+                "reindex_score": cand * (key_bytes + 4),
+                "reindex_select": cand * 4,
                 "attend": gather + self.n_q * wl.heads * 128 * (2 + 4) + new_vec,
                 "kv_gather": gather}
 

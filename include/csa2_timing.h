@@ -33,13 +33,14 @@ int csa2_index_full_scan_timed(const uint16_t* q_idx, const float* w, const void
 
 /*
  * csa2_index_reindex_timed -- csa2_index_reindex (k_scales == NULL) or csa2_index_reindex_mx
- * (MXFP4 keys): [Article] sections VIII-IX.  start_event is recorded at the start of the
- * scoring kernel and stop_event at the end of the selection kernel that follows it.
+ * (MXFP4 keys): [Article] sections VIII-IX.  Two event pairs: the scoring kernel's own start and
+ * end, and the selection kernel's (the kernel that follows it).
  */
 int csa2_index_reindex_timed(const uint16_t* q_idx, const float* w, const void* k_idx,
                              const uint8_t* k_scales, csa2_seqs seqs, int32_t n_heads, const int32_t* pool,
                              int32_t pool_blocks, int32_t block, int32_t top_k, int32_t* idx_out, void* ws,
-                             size_t ws_bytes, void* stream, void* start_event, void* stop_event);
+                             size_t ws_bytes, void* stream, void* score_start, void* score_stop,
+                             void* select_start, void* select_stop);
 
 /*
  * csa2_attend_timed -- csa2_attend (bf16 window store): [Article] sections VI and XI.  The

@@ -50,6 +50,42 @@ def _special_groups():
     return x
 
 
+def test_fp4_pack_every_scale_and_midpoint():
+    # For every E4M3 scale code c (1..126): groups whose largest element is exactly 6 v(c), so
+    # the scale is c, and whose other 15 elements sit on the E2M1 midpoints m v(c) (exact ties)
+    # and one bf16 step to either side, in even and odd channels, with both signs -- every
+    # rounding decision of the packer at every scale, compared with the oracle.
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    rows = []
+    rng = np.random.default_rng(17)
+    for c in range(1, 127):
+        e, m = c >> 3, c & 7
+        v = m * 2.0 ** -9 if e == 0 else 2.0 ** (e - 7) * (1 + m / 8)
+        vals = []
+        for mid in mids:
+            b = int(np.float32(mid * v).view(np.uint32)) >> 16           # exact bf16 threshold
+            vals += [b, b + 1, b - 1]
+        top = int(np.float32(6 * v).view(np.uint32)) >> 16
+        for shift in range(2):                                          # odd / even placement
+            vv = np.array(vals, dtype=np.int64)
+            rng.shuffle(vv)
+            for start in range(0, len(vv), 15):
+                chunk = list(vv[start:start + 15])
+                chunk += [0] * (15 - len(chunk))
+                g = chunk[:shift] + [top] + chunk[shift:]
+                sign = rng.integers(0, 2, 16) << 15
+                rows.append((np.array(g, dtype=np.int64) | sign).astype(np.uint16))
+    x = np.stack(rows)
+    x = np.concatenate([x, np.zeros(((-x.shape[0]) % 8, 16), np.uint16)]).reshape(-1, 128)
+    codes = torch.full((x.shape[0], 64), 0x5A, dtype=torch.uint8, device=DEV)
+    scales = torch.full((x.shape[0], 8), 0x5A, dtype=torch.uint8, device=DEV)
+    C.fp4_kv_append(bf16_tensor(x), codes, scales)
+    torch.cuda.synchronize()
+    c_ref, s_ref = O.fp4_quantize(x)
+    assert np.array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+
+
 def test_fp4_pack_special_groups():
     x = _special_groups()
     x = np.concatenate([x] * 8, axis=1)[:, :128]             # 128 channels per row
