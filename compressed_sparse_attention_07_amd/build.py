@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
-SOURCES = ["fp4_pack.hip", "indexer.hip", "attend.hip", "csa2_api.cpp"]
+SOURCES = ["fp4_pack.hip", "indexer.hip", "attend.hip", "noalloc.hip", "csa2_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -16,7 +16,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcsa2.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_CAPACITY, ERR_LAUNCH = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_CAPACITY, ERR_LAUNCH, ERR_SCRATCH = range(8)
 OP_INDEX_FULL, OP_INDEX_REINDEX, OP_ATTEND = 1, 2, 3
 KV_DIM, IDX_DIM, BLOCK = 128, 64, 8
 SIZE_MAX = (1 << 64) - 1  # csa2_workspace_bytes: sizes out of range
@@ -29,6 +29,7 @@ EXPORTS = (
     "csa2_index_full_scan",
     "csa2_index_full_select",
     "csa2_index_reindex",
+    "csa2_index_reindex_noalloc",
     "mxfp4_key_append",
     "csa2_index_full_mx",
     "csa2_index_full_mx_scan",
@@ -82,6 +83,7 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).argtypes = [vp, vp, vp, SeqsC, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp]
             getattr(L, name).restype = ctypes.c_int
         L.csa2_index_reindex.argtypes = [vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
+        L.csa2_index_reindex_noalloc.argtypes = [vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp]
         L.csa2_attend.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp]
         L.fp8_window_append.argtypes = [vp, i64, i32, vp, i64, vp, i64, vp]
         L.mxfp4_key_append.argtypes = [vp, i64, i32, vp, i64, vp, vp, i64, vp]
@@ -110,7 +112,7 @@ def lib() -> ctypes.CDLL:
                      "csa2_attend_fp8win", "csa2_workspace_init", "csa2_version", "mxfp4_key_append",
                      "csa2_index_full_mx", "csa2_index_full_mx_scan", "csa2_index_reindex_mx", "csa2_reindex_attend",
                      "csa2_index_full_scan_timed", "csa2_token_append", "csa2_window_append",
-                     "csa2_index_reindex_timed", "csa2_attend_timed"):
+                     "csa2_index_reindex_timed", "csa2_attend_timed", "csa2_index_reindex_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -320,6 +322,15 @@ def csa2_index_full_scan_timed(q_idx, w, k_idx, k_scales, seqs: Seqs, top_k: int
 
 def _event(e):
     return ctypes.c_void_p(e.cuda_event) if e is not None else None
+
+
+def csa2_index_reindex_noalloc(q_idx, w, k_idx, seqs: Seqs, pool, top_k: int, idx_out, block: int = BLOCK,
+                               stream=None) -> None:
+    """csa2_index_reindex with the library's static scratch in place of a workspace (n_q <= 64,
+    pool_blocks <= 2048); allocates nothing."""
+    _check("csa2_index_reindex_noalloc", lib().csa2_index_reindex_noalloc(
+        _ptr(q_idx), _ptr(w), _ptr(k_idx), seqs.c(), q_idx.shape[1], _ptr(pool), pool.shape[1], block, top_k,
+        _ptr(idx_out), _stream(stream)))
 
 
 def csa2_index_reindex_timed(q_idx, w, k_idx, k_scales, seqs: Seqs, pool, top_k: int, idx_out, ws, score_events,

@@ -531,6 +531,7 @@ const char* csa2_status_string(int status) {
         case CSA2_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case CSA2_ERR_CAPACITY: return "destination range exceeds capacity";
         case CSA2_ERR_LAUNCH: return "HIP launch failed";
+        case CSA2_ERR_SCRATCH: return "sizes exceed the no-allocation scratch (n_q <= 64, pool_blocks <= 2048)";
         default: return "unknown status";
     }
 }

@@ -55,6 +55,7 @@ extern "C" {
 #define CSA2_ERR_WORKSPACE 4   /* workspace NULL or smaller than csa2_workspace_bytes() */
 #define CSA2_ERR_CAPACITY 5    /* a destination range exceeds the stated capacity */
 #define CSA2_ERR_LAUNCH 6      /* the HIP runtime reported an error at launch */
+#define CSA2_ERR_SCRATCH 7     /* sizes past the no-allocation entry point's built-in scratch */
 
 /* ---- limits of this implementation ---- */
 #define CSA2_KV_DIM 128         /* main-KV latent width = attention head dim */
@@ -65,6 +66,8 @@ extern "C" {
 #define CSA2_MAX_WINDOW 4096    /* sliding-window length */
 #define CSA2_MAX_QUERIES 65535  /* n_q */
 #define CSA2_BLOCK 8            /* positions per pool block */
+#define CSA2_NOALLOC_MAX_QUERIES 64   /* csa2_index_reindex_noalloc: n_q */
+#define CSA2_NOALLOC_MAX_POOL 2048    /* csa2_index_reindex_noalloc: pool_blocks */
 
 /* ---- operation ids for csa2_workspace_bytes ---- */
 #define CSA2_OP_INDEX_FULL 1
@@ -297,6 +300,21 @@ int csa2_attend_fp8win(const uint16_t* q, const uint8_t* codes, const uint8_t* s
                        int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay_start,
                        const uint16_t* win_new, int32_t n_heads, float softmax_scale, float* out,
                        void* stream);
+
+/*
+ * csa2_index_reindex_noalloc -- csa2_index_reindex without a caller workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, serving loops and harnesses that
+ * forbid allocation).  The workspace is a static device array of the library (6 MiB per GPU,
+ * held until the process ends); the call allocates nothing.  Sizes: n_q <= 64 and pool_blocks
+ * <= 2,048 (larger: CSA2_ERR_SCRATCH, nothing launched).  The first call on a device also clears
+ * the array with a kernel on `stream`; every call leaves its counters and histograms zero again.
+ * All calls on one GPU share its array: calls that may overlap on one GPU (other streams, other
+ * host threads) race and must not be issued.  Arguments, outputs and other errors are those of
+ * csa2_index_reindex.
+ */
+int csa2_index_reindex_noalloc(const uint16_t* q_idx, const float* w, const uint16_t* k_idx, csa2_seqs seqs,
+                               int32_t n_heads, const int32_t* pool, int32_t pool_blocks, int32_t block,
+                               int32_t top_k, int32_t* idx_out, void* stream);
 
 /*
  * csa2_reindex_attend -- one Reindex layer in one kernel: csa2_index_reindex (or _mx)

@@ -35,7 +35,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for n in declared_functions():
         assert hasattr(L, n), n
     assert L.csa2_version() == 100
-    for s in range(7):
+    for s in range(8):
         assert L.csa2_status_string(s)
 
 
