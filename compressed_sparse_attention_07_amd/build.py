@@ -35,7 +35,8 @@ FLAGS = [
 EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
          # all three: a kernel's leading scalar and pointer arguments preloaded into SGPRs at launch
          "attend.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
-         "fp4_pack.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+         # fp4_pack.hip: the scale table is built by the compiler (constexpr), which needs more steps
+         "fp4_pack.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16", "-fconstexpr-steps=100000000"]}
 
 
 def _compile(src: str) -> str:

@@ -13,6 +13,68 @@ namespace csa2 {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// The E4M3 scale code of every possible group amax: index = the 15-bit pattern of amax (bf16
+// magnitudes order like their patterns), value = e4m3_round_amax_over_6 of that amax.  Built by
+// the compiler from the same search, so a group's scale is one byte load (from L2 after the
+// first groups) instead of a seven-step search of ~80 instructions per group.
+struct ScaleLut {
+    uint8_t c[32768];
+};
+
+constexpr float e4m3_pos_value_cx(int c) {
+    const int e = c >> 3, m = c & 7;
+    return e == 0 ? (float)m * 0.001953125f
+                  : __builtin_bit_cast(float, (uint32_t)((e + 120) << 23) | (uint32_t)(m << 20));
+}
+
+constexpr ScaleLut make_scale_lut() {
+    ScaleLut t{};
+    for (int a = 0; a < 32768; ++a) {
+        const float amax = __builtin_bit_cast(float, (uint32_t)a << 16);
+        int lo = 0;  // largest code c with 6 v(c) <= amax, then round half to even at the midpoint
+        for (int step = 64; step > 0; step >>= 1) {
+            const int c = lo + step;
+            if (c <= 126 && 6.0f * e4m3_pos_value_cx(c) <= amax) lo = c;
+        }
+        if (lo < 126) {
+            const float th = 3.0f * (e4m3_pos_value_cx(lo) + e4m3_pos_value_cx(lo + 1));
+            if (amax > th || (amax == th && (lo & 1))) lo += 1;
+        }
+        t.c[a] = (uint8_t)lo;
+    }
+    return t;
+}
+
+__device__ constexpr ScaleLut kScaleLut = make_scale_lut();
+
+// One 16-channel FP4 group: w = 8 dwords of bf16 pairs (channel 2k in the low half) ->
+// codes (lo: channels 0..7, hi: 8..15; low nibble = even channel) and the E4M3 scale code.
+__device__ __forceinline__ uint32_t fp4_pack_group(const uint32_t (&w)[8], uint32_t& lo, uint32_t& hi) {
+    // amax: bf16 magnitudes order like their 15-bit patterns
+    uint32_t am = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) am = max(am, max(w[k] & 0x7fffu, (w[k] >> 16) & 0x7fffu));
+    const int sc = kScaleLut.c[am];
+    const float s = e4m3_pos_value(sc);
+    constexpr float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+    uint32_t T[7];
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+        const uint32_t b = __float_as_uint(kMid[k] * s) >> 16;  // exact (low half is zero)
+        T[k] = sc == 0 ? 0x7fff7fffu : (b | (b << 16));
+    }
+    uint32_t byte[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t c = e2m1_pair(w[k], T);
+        byte[k] = (c | (c >> 12)) & 0xffu;  // channel 2k in the low nibble, 2k + 1 in the high one
+    }
+    lo = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
+    hi = byte[4] | (byte[5] << 8) | (byte[6] << 16) | (byte[7] << 24);
+    return (uint32_t)sc;
+}
+
+
 // Generic FP4 pack (any dim % 16 == 0): one thread per 16-channel group, 32 B in, 8 B of codes
 // and 1 B of scale out.
 __global__ __launch_bounds__(256) void k_fp4_pack(const uint16_t* __restrict__ x, int64_t n_tok, int dim,

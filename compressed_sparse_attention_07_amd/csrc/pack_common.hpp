@@ -83,33 +83,6 @@ __device__ __forceinline__ uint32_t e2m1_pair(uint32_t w, const uint32_t (&T)[7]
     return (~m4 & 0x00040004u) | (~m2 & 0x00020002u) | (m1 & 0x00010001u) | ((w >> 12) & 0x00080008u);
 }
 
-// One 16-channel FP4 group: w = 8 dwords of bf16 pairs (channel 2k in the low half) ->
-// codes (lo: channels 0..7, hi: 8..15; low nibble = even channel) and the E4M3 scale code.
-__device__ __forceinline__ uint32_t fp4_pack_group(const uint32_t (&w)[8], uint32_t& lo, uint32_t& hi) {
-    // amax: bf16 magnitudes order like their 15-bit patterns
-    uint32_t am = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) am = max(am, max(w[k] & 0x7fffu, (w[k] >> 16) & 0x7fffu));
-    const int sc = e4m3_round_amax_over_6(__uint_as_float(am << 16));
-    const float s = e4m3_pos_value(sc);
-    constexpr float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-    uint32_t T[7];
-#pragma unroll
-    for (int k = 0; k < 7; ++k) {
-        const uint32_t b = __float_as_uint(kMid[k] * s) >> 16;  // exact (low half is zero)
-        T[k] = sc == 0 ? 0x7fff7fffu : (b | (b << 16));
-    }
-    uint32_t byte[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const uint32_t c = e2m1_pair(w[k], T);
-        byte[k] = (c | (c >> 12)) & 0xffu;  // channel 2k in the low nibble, 2k + 1 in the high one
-    }
-    lo = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
-    hi = byte[4] | (byte[5] << 8) | (byte[6] << 16) | (byte[7] << 24);
-    return (uint32_t)sc;
-}
-
 // One 32-channel MXFP4 block (microscaling conversion): scale X = 2^(floor(log2 amax) - 2), its
 // E8M0 code = (bf16 exponent field of amax) - 2 clamped to [1, 254]; elements nearest to x / X,
 // ties to even, saturating at 6, decided by the threshold compares above (X is a power of two,
