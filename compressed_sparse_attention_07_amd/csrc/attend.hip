@@ -46,6 +46,10 @@
 namespace csa2 {
 
 constexpr int kAttWaves = 8;
+#ifndef CSA2_ATT_SPLIT
+#define CSA2_ATT_SPLIT 4   // workgroups per decode query (output dimensions split): 1, 2, 4 or 8
+#endif
+constexpr int kAttSplitMaxQ = 64;            // decode-sized calls take the split
 constexpr int kAttNT = kAttWaves * 64;
 constexpr int kD = 128;                      // latent / head dim
 constexpr int kNH = 16;                      // heads (padded)
@@ -176,9 +180,16 @@ struct AttendLds {
 };
 
 // The attention of query i (one workgroup of kAttNT threads); idx_row = the query's top_k
-// selected positions (global memory or LDS).
-template <bool kFp4, bool kWin, bool kW8>
-__device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const int32_t* idx_row, const AttendLds& lds) {
+// selected positions (global memory or LDS).  SPLIT > 1: the query's output dimensions are
+// split over SPLIT workgroups and this one, number `part`, produces dimensions
+// [part * 128 / SPLIT, (part + 1) * 128 / SPLIT): every workgroup forms all logits and the same
+// softmax (the same arithmetic in the same order), but P.V, its LDS transposes and the wave merge
+// cover only its share, so no partial result crosses workgroups.
+template <bool kFp4, bool kWin, bool kW8, int SPLIT = 1>
+__device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const int32_t* idx_row, const AttendLds& lds,
+                                             int part = 0) {
+    constexpr int NDB = 8 / SPLIT;  // 16-dimension output blocks of this workgroup
+    static_assert(SPLIT == 1 || SPLIT == 2 || SPLIT == 4 || SPLIT == 8, "split");
     const uint16_t* __restrict__ q = a.q;
     const uint8_t* __restrict__ codes = a.codes;
     const uint8_t* __restrict__ scales = a.scales;
@@ -326,9 +337,11 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
 
     float m_run = -INFINITY;  // running max (log2 units) of head r over this wave's entries
     float l_run = 0.f;        // this lane's share of the running sum
-    f32x4 o[8];
+    f32x4 o[NDB];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int db0 = part * NDB;                                       // first output block
+    const bool g_in = 2 * g + 1 >= db0 && 2 * g < db0 + NDB;          // this lane's channels (blocks 2g, 2g + 1) meet the share
     uint8_t* tile = lds.tile + wave * kTileB;
     // tile addresses: row-major store of this lane's entry r; transposed read of rows 4g + r/4
     const int st_off = r * kRowB + 64 * g;
@@ -437,7 +450,7 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
 #pragma unroll
-            for (int db = 0; db < 8; ++db) o[db] *= alpha;
+            for (int db = 0; db < NDB; ++db) o[db] *= alpha;
         }
         m_run = m_new;
         // probabilities: f16 for FP4 (and E4M3 window) entries, bf16 hi + lo for bf16 window entries
@@ -477,17 +490,19 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
 #pragma unroll
         for (int pp = 0; pp < kRB / 2; ++pp) {
             if (b0 + 2 * pp >= nb4) break;  // wave-uniform
+            if (g_in) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                *reinterpret_cast<u32x4*>(tile + st_off + 16 * s) = kf[2 * pp][s];
-                *reinterpret_cast<u32x4*>(tile + 16 * kRowB + st_off + 16 * s) = kf[2 * pp + 1][s];
+                for (int s = 0; s < 4; ++s) {
+                    *reinterpret_cast<u32x4*>(tile + st_off + 16 * s) = kf[2 * pp][s];
+                    *reinterpret_cast<u32x4*>(tile + 16 * kRowB + st_off + 16 * s) = kf[2 * pp + 1][s];
+                }
             }
             wave_lds_sync();
             const u32x4 pf = {ph[2 * pp][0], ph[2 * pp][1], ph[2 * pp + 1][0], ph[2 * pp + 1][1]};
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const s16x4 a0 = lds_tr16(tile + tr_off + 32 * db);
-                const s16x4 a1 = lds_tr16(tile + 16 * kRowB + tr_off + 32 * db);
+            for (int db = 0; db < NDB; ++db) {
+                const s16x4 a0 = lds_tr16(tile + tr_off + 32 * (db0 + db));
+                const s16x4 a1 = lds_tr16(tile + 16 * kRowB + tr_off + 32 * (db0 + db));
                 const u32x2 u0 = __builtin_bit_cast(u32x2, a0), u1 = __builtin_bit_cast(u32x2, a1);
                 const u32x4 af = {u0[0], u0[1], u1[0], u1[1]};
                 o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af),
@@ -497,13 +512,15 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
         }
         // ---- P.V over the window block (K = 16 entries) ----
         if (wblk) {
+            if (g_in) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) *reinterpret_cast<u32x4*>(tile + st_off + 16 * s) = wf[s];
+                for (int s = 0; s < 4; ++s) *reinterpret_cast<u32x4*>(tile + st_off + 16 * s) = wf[s];
+            }
             wave_lds_sync();
             const u32x2 hv2 = {pwh[0], pwh[1]}, lv2 = {pwl[0], pwl[1]};
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const s16x4 a = lds_tr16(tile + tr_off + 32 * db);
+            for (int db = 0; db < NDB; ++db) {
+                const s16x4 a = lds_tr16(tile + tr_off + 32 * (db0 + db));
                 if constexpr (kW8) {
                     o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
                                                                   __builtin_bit_cast(f16x4, hv2), o[db], 0, 0, 0);
@@ -524,16 +541,17 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
         s_l[wave][r] = l_run;
     }
     {
-        // this wave's O^T (dims 16db + 4g + ii of head r) -> rows [head][dim] inside its own tile
+        // this wave's O^T (dims 16 (db0 + db) + 4g + ii of head r) -> rows [head][dim - 16 db0] of its tile
         float* ob = reinterpret_cast<float*>(tile);
 #pragma unroll
-        for (int db = 0; db < 8; ++db)
+        for (int db = 0; db < NDB; ++db)
             *reinterpret_cast<f32x4*>(&ob[r * kOStride + 16 * db + 4 * g]) = o[db];
     }
     __syncthreads();
-    const int h = t >> 5;
-    const int d0 = 4 * (t & 31);
-    if (h < n_heads) {
+    constexpr int kTpH = 32 / SPLIT;  // threads per head, four dimensions each
+    const int h = t / kTpH;
+    const int d0 = 4 * (t % kTpH);    // within the share
+    if (h < n_heads && t < kNH * kTpH) {
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, s_m[w][h]);
@@ -547,11 +565,11 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
                                                     h * kOStride + d0);
         }
         const f32x4 res = L > 0.f ? O / L : f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(out + ((int64_t)i * n_heads + h) * kD + d0) = res;
+        *reinterpret_cast<f32x4*>(out + ((int64_t)i * n_heads + h) * kD + 16 * db0 + d0) = res;
     }
     // the new window entry into its store row, after every read of the store by this query
     // (wave 0, two channels per lane); whether or not the replay bound lets it be attended
-    if (has_new && wave == 0 && n > 0) {
+    if (has_new && wave == 0 && part == 0 && n > 0) {
         const int64_t wr = wrow0_raw + ((n - 1) % swa_cap);
         if (wr >= 0 && wr < swa_rows) {
             if constexpr (kW8)
@@ -566,7 +584,7 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
 // The arguments one by one (not the AttendArgs block), those of the first level of loads first:
 // the leading ones are preloaded into SGPRs at launch, so those loads need no scalar load of
 // the argument block before them.
-template <bool kFp4, bool kWin, bool kW8>
+template <bool kFp4, bool kWin, bool kW8, int SPLIT>
 __global__ __launch_bounds__(kAttNT) void k_attend(const int32_t* kv_len, const int64_t* kv_row0,
                                                    const int64_t* swa_row0, const int64_t* replay, const int32_t* idx,
                                                    const uint16_t* q, int top_k, int n_heads, int32_t max_len,
@@ -578,8 +596,11 @@ __global__ __launch_bounds__(kAttNT) void k_attend(const int32_t* kv_len, const 
     const AttendArgs a{q,        codes,   scales,   kv_row0, kv_len, max_len, cache_rows, idx,   top_k,
                        swa,      swa_row0, swa_cap, swa_rows, window, replay, n_heads,   scale_log2, out,
                        win_new};
-    const int i = blockIdx.x;
-    attend_query<kFp4, kWin, kW8>(i, a, idx + (int64_t)i * top_k, AttendLds{s_tile, s_m, s_l});
+    // workgroups i and i + n_q * k serve query i (parts k); with n_q a multiple of 8 they run on
+    // one XCD (workgroup b runs on XCD b mod 8), so a query's gathers are shared in its L2
+    const int n_q = (int)gridDim.x / SPLIT;
+    const int i = (int)blockIdx.x % n_q, part = (int)blockIdx.x / n_q;
+    attend_query<kFp4, kWin, kW8, SPLIT>(i, a, idx + (int64_t)i * top_k, AttendLds{s_tile, s_m, s_l}, part);
 }
 
 // One Reindex layer in one kernel ([Article] sections VIII-IX: the layer scores its own indexer
@@ -663,20 +684,30 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
                          hipEvent_t ev_stop) {
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
     const bool fp4 = top_k > 0, win = window > 0 && swa_rows > 0;
-    decltype(&k_attend<true, true, false>) kern;
-    if (window_fp8)
-        kern = fp4 ? (win ? k_attend<true, true, true> : k_attend<true, false, true>)
-                   : (win ? k_attend<false, true, true> : k_attend<false, false, true>);
-    else
-        kern = fp4 ? (win ? k_attend<true, true, false> : k_attend<true, false, false>)
-                   : (win ? k_attend<false, true, false> : k_attend<false, false, false>);
+    // decode batches (at most kAttSplitMaxQ queries) split each query's output dimensions over
+    // CSA2_ATT_SPLIT workgroups; larger calls (a prefill chunk's tokens) already fill the chip
+    const int split = n_q <= kAttSplitMaxQ ? CSA2_ATT_SPLIT : 1;
+    using K = decltype(&k_attend<true, true, false, 1>);
+    auto pick = [&](auto sp) -> K {
+        constexpr int S = decltype(sp)::value;
+        if (window_fp8)
+            return fp4 ? (win ? k_attend<true, true, true, S> : k_attend<true, false, true, S>)
+                       : (win ? k_attend<false, true, true, S> : k_attend<false, false, true, S>);
+        return fp4 ? (win ? k_attend<true, true, false, S> : k_attend<true, false, false, S>)
+                   : (win ? k_attend<false, true, false, S> : k_attend<false, false, false, S>);
+    };
+    const K kern = split == 8   ? pick(std::integral_constant<int, 8>{})
+                   : split == 4 ? pick(std::integral_constant<int, 4>{})
+                   : split == 2 ? pick(std::integral_constant<int, 2>{})
+                                : pick(std::integral_constant<int, 1>{});
+    const dim3 grid((unsigned)(n_q * split));
     // ev_start / ev_stop (may be null): the kernel's own start and end, recorded by its launch
     if (ev_start != nullptr || ev_stop != nullptr)
-        hipExtLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, ev_start, ev_stop, 0, kv_len, kv_row0, swa_row0,
+        hipExtLaunchKernelGGL(kern, grid, dim3(kAttNT), 0, stream, ev_start, ev_stop, 0, kv_len, kv_row0, swa_row0,
                               replay, idx, q, top_k, n_heads, max_len, cache_rows, codes, scales, swa, swa_cap, swa_rows,
                               window, scale_log2, out, win_new);
     else
-        hipLaunchKernelGGL(kern, dim3(n_q), dim3(kAttNT), 0, stream, kv_len, kv_row0, swa_row0, replay, idx, q, top_k,
+        hipLaunchKernelGGL(kern, grid, dim3(kAttNT), 0, stream, kv_len, kv_row0, swa_row0, replay, idx, q, top_k,
                            n_heads, max_len, cache_rows, codes, scales, swa, swa_cap, swa_rows, window, scale_log2, out,
                            win_new);
     return hipGetLastError();
