@@ -29,6 +29,7 @@ no step re-reads data a 256 MiB last-level cache could still hold.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -48,6 +49,46 @@ STORAGE = ("main KV FP4 (E2M1 + E4M3 per 16 ch); indexer keys bf16 (MXFP4 in the
            "window bf16 (E4M3 in the fp8win workloads); scores, softmax and outputs fp32")
 KERNEL_NAMES = {"scan": "k_idx_score_full", "reindex_score": "k_idx_reindex_score",
                 "reindex_select": "k_idx_reindex_select", "attend": "k_attend"}
+
+
+# sources whose text decides each timed kernel's code (compiler flags included): a committed counter
+# summary is used for `traffic` only while these still hash to the value recorded in it
+_COMMON = ["compressed_sparse_attention_07_amd/csrc/csa2_device.hpp", "compressed_sparse_attention_07_amd/build.py"]
+KERNEL_SOURCES = {
+    "scan": ["compressed_sparse_attention_07_amd/csrc/scan_full.hpp",
+             "compressed_sparse_attention_07_amd/csrc/scan_common.hpp"] + _COMMON,
+    "reindex_score": ["compressed_sparse_attention_07_amd/csrc/reindex_score.hpp",
+                      "compressed_sparse_attention_07_amd/csrc/scan_common.hpp"] + _COMMON,
+    "reindex_select": ["compressed_sparse_attention_07_amd/csrc/reindex_select.hpp"] + _COMMON,
+    "attend": ["compressed_sparse_attention_07_amd/csrc/attend.hip",
+               "compressed_sparse_attention_07_amd/csrc/pack_common.hpp"] + _COMMON,
+}
+
+
+def source_sha(family: str) -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES[family]:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(family: str, workload_name: str):
+    """Calibrated HBM bytes per launch of a kernel family from the committed counter summary
+    profiles/traffic_<kernel>_<workload>.md, if it was taken on the current sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_NAMES[family]}_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            kv[k.strip()] = v.strip().strip("`")
+    if kv.get("source_sha256") != source_sha(family):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
 
 
 _SLEEP_CYCLES_PER_S = None
@@ -153,7 +194,8 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
     else:
         dom = max(kernels, key=lambda e: e["share_of_step"])
         res["roofline"] = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": dom["frac"], "traffic": None, "kernel": dom["kernel"],
+                           "frac": dom["frac"], "traffic": read_traffic(dom["family"], wl.name),
+                           "kernel": dom["kernel"],
                            "share_of_step": dom["share_of_step"], "alg_bytes_per_launch": dom["alg_bytes_per_launch"],
                            "avg_launch_us": dom["avg_launch_us"]}
     res["config"] = {"workload": wl.name, "batch": wl.batch, "context": wl.context, "layers": wl.layers,
