@@ -189,7 +189,7 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
         tflops = flops / scan_s / 1e12
         res["roofline"] = {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                           "kernel": "k_idx_score_prefill (both passes)", "alg_flops_per_launch": flops,
+                           "kernel": "k_idx_prefill_sample + k_idx_prefill_thresh + k_idx_prefill_cand", "alg_flops_per_launch": flops,
                            "avg_launch_us": round(avg_us["scan"], 2)}
     else:
         dom = max(kernels, key=lambda e: e["share_of_step"])

@@ -131,12 +131,6 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 // kFp4: top_k > 0 (the FP4 cache is read); kWin: window > 0 and the window store has rows.
 // Both are fixed per launch so that every gather below is unconditional (clamped addresses,
 // masked results): loads under branches make the compiler wait on some of them early.

@@ -235,9 +235,11 @@ static int index_full_phase(const uint16_t* q_idx, const float* w, const void* k
     carve_full(nullptr, seqs.n_q, tiles, ftiles, top_k, pool_blocks, &need);
     if (ws == nullptr || ws_bytes < need || !aligned16(ws)) return CSA2_ERR_WORKSPACE;
     const IndexWs wsp = carve_full(ws, seqs.n_q, tiles, ftiles, top_k, pool_blocks, &need);
-    // prefill chunk: the MFMA scoring kernel (shared sequence, at most 4 heads, >= 16 queries)
+    // prefill chunk: the MFMA scoring kernels (shared sequence, at most 4 heads, >= 16 queries,
+    // positions below 2^26, which its candidate entries pack into 26 bits)
     // (MXFP4 keys always take the per-query scan)
-    const int prefill = (!mx && shared_kv != 0 && n_heads <= 4 && seqs.n_q >= 16) ? 1 : 0;
+    const int prefill =
+        (!mx && shared_kv != 0 && n_heads <= 4 && seqs.n_q >= 16 && seqs.max_len_ub < (1 << 26)) ? 1 : 0;
     return launch_status(launch_index_full(q_idx, w, k_idx, k_sc, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
                                            seqs.max_len_ub, seqs.cache_rows, n_heads, (int)tiles, (int)ftiles, top_k,
                                            pool_blocks, prefill, wsp, idx_out, pool_out, phase,

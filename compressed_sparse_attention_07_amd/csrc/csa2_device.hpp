@@ -71,6 +71,13 @@ __device__ __forceinline__ uint32_t score_key(float s) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// LDS writes of this wave visible to its own later LDS reads (a wave-private buffer).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
     return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - pos);
 }

@@ -133,31 +133,28 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
 }
 
 // ----------------------------------------------------------------------------------------
-// Full mode, kernel 1 (prefill chunk: every query reads the same sequence): the scores of
-// 16 queries x 16 positions per MFMA tile.  For indexer head h, D_h = Q_h . K^T on
-// v_mfma_f32_16x16x32_bf16 (two k-steps cover the 64 channels); lane (g, r) supplies query r
-// of Q_h and position r of K^T with channels 32s + 8g .. 32s + 8g + 7, so its key loads are
-// the scan's 16-byte slices.  The accumulator of lane (g, r) holds queries 4g+i at position r;
-// the lane folds its four heads (ReLU, weights), writes the keys and counts first digits in
-// an LDS histogram (two 16-bit counters per word, digits d and d + 1024: a workgroup counts at most kPfPos per bin).
-// POOL: every query also gets its own block pool ([Article] IX, applied per query of the
-// chunk): the lanes of one 16-lane row hold one query's 16 consecutive positions, so the
-// 8-position block maximum is the decode scan's DPP step.  The block keys are counted by
-// k_idx_block_hist afterwards, which keeps this kernel's LDS at one histogram (a second one
-// would halve the resident workgroups).
+// Full mode, prefill chunk (every query reads the same sequence).  Scores are formed 16 queries
+// x 16 positions per MFMA tile: for indexer head h, D_h = Q_h . K^T on v_mfma_f32_16x16x32_bf16
+// (two k-steps cover the 64 channels); lane (g, r) supplies query r of Q_h and position r of
+// K^T with channels 32s + 8g .. 32s + 8g + 7, so its key loads are the scan's 16-byte slices.
+// The accumulator of lane (g, r) holds queries 4g+i at position r; the lane folds its four
+// heads (ReLU, weights) into the score and its order-preserving key.
+// The chunk's selection takes two passes over the scores:
+//   sample     - k_idx_prefill_sample scores one 16-position tile in kPfStride and counts the
+//                keys' first digits per query (LDS histogram, two 16-bit counters per word);
+//                k_idx_prefill_thresh turns the counts into the query's sampled threshold
+//                digit: the digit holding the K-th largest key of the sample;
+//   candidates - k_idx_prefill_cand scores every position and keeps those whose first digit is
+//                at least the sampled one.  The sample is a subset of the visible positions,
+//                so at least K visible positions reach that digit and the exact Top-K lies
+//                among the candidates, where k_idx_select_cands takes it.  A sample of 1 in
+//                kPfStride keeps about kPfStride x K candidates per query.
+// Scores are recomputed rather than stored: a chunk has 4,096 x ~133K (query, position)
+// pairs, and a 4-byte key for each (2.2 GB out and back in) costs several times the MFMA work.
 // ----------------------------------------------------------------------------------------
-constexpr int kPfQ = 16;       // queries per workgroup
-constexpr int kPfPos = 8192;   // positions per workgroup (2,048 per wave)
-// What a pass of the prefill scoring kernel produces.  A chunk's selection runs it twice:
-// kPfHist (first-digit histograms, and the block keys when pools are asked for), then, once
-// k_idx_prefill_thresh has put every query's threshold bucket in the workspace, kPfCompact:
-// the same scores again, with only the positions at or above the bucket written, straight into
-// the lists the selection reads.  Scores are recomputed rather than stored: a chunk has
-// 4,096 x ~133K (query, position) pairs, and a 4-byte key for each (2.2 GB out and back in)
-// costs several times the MFMA work.
-constexpr int kPfHist = 1, kPfCompact = 2;
-constexpr int kPfBuf = 256;    // positions of one query a workgroup gathers in LDS before writing
-
+constexpr int kPfQ = 16;           // queries per sample workgroup
+constexpr int kPfPos = 32768;      // positions per sample workgroup (8,192 per wave)
+constexpr int kPfStride = 8;       // the sample takes one 16-position tile in kPfStride
 
 // Work items (position chunk x, query group y) are numbered chunk-major and split into kXcds
 // contiguous slices, one per XCD: workgroups are handed to the XCDs in turn (workgroup b to
@@ -170,18 +167,12 @@ __host__ __device__ __forceinline__ int pf_items_per_xcd(int n_px, int n_qg) {
     return (n_px * n_qg + kXcds - 1) / kXcds;
 }
 
-template <bool POOL, int MODE>
-__global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
+__global__ __launch_bounds__(kScoreNT) void k_idx_prefill_sample(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
-    const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, int top_k, int n_px, int n_qg,
+    const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, int n_px, int n_qg,
     IndexWs ws) {
-    constexpr bool kCompact = MODE == kPfCompact;
-    __shared__ uint32_t sh_hist[kCompact ? 1 : kPfQ][kHistBins / 2];
-    __shared__ uint64_t sh_buf[kCompact ? kPfQ : 1][kCompact ? kPfBuf : 1];  // selected entries per query
-    __shared__ int sh_cnt[kPfQ];
-    __shared__ int sh_thr[kPfQ];
+    __shared__ __align__(16) uint32_t sh_hist[kPfQ][kHistBins / 2];
     __shared__ int sh_n[kPfQ];
-    __shared__ int64_t sh_base[kPfQ];
     const int t = threadIdx.x;
     const int lane = __lane_id();
     const int wid = t / kWave;
@@ -194,26 +185,15 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
     const int64_t row_room = (row0 >= 0 && row0 <= cache_rows) ? cache_rows - row0 : 0;
     if (t < kPfQ) {
         const int q = q0 + t;
-        int n = 0;
-        int64_t base = 0;
-        if (q < n_q) {
-            const QMeta m = ws.qmeta[q];
-            n = (int)min((int64_t)m.n, row_room);
-            base = (int64_t)m.start * kFullTile;
-        }
-        sh_n[t] = n;
-        sh_base[t] = base;
-        sh_cnt[t] = 0;
-        // threshold bucket of the query (k_idx_prefill_thresh); -1: every position is kept
-        sh_thr[t] = (kCompact && q < n_q) ? ws.meta[2 * q].digit : 0;
+        sh_n[t] = q < n_q ? (int)min((int64_t)ws.qmeta[q].n, row_room) : 0;
     }
     __syncthreads();
     int n_max = 0;
 #pragma unroll
     for (int k = 0; k < kPfQ; ++k) n_max = max(n_max, sh_n[k]);
     if (p_wg >= n_max) return;  // uniform: nothing visible in this position chunk
-    if constexpr (!kCompact)
-        for (int k = t; k < kPfQ * kHistBins / 2; k += kScoreNT) (&sh_hist[0][0])[k] = 0u;
+    for (int k = t; k < kPfQ * kHistBins / 8; k += kScoreNT)
+        reinterpret_cast<uint4*>(&sh_hist[0][0])[k] = make_uint4(0, 0, 0, 0);
     // A fragments: query q0 + r, head h, channels 32s + 8g .. +8 ; weights of queries q0 + 4g + i
     bf16x8_t qa[4][2];
     float wq[4][4];
@@ -231,14 +211,9 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
             wq[i][h] = (qi < n_q && h < n_heads) ? w[(int64_t)qi * n_heads + h] : 0.f;
         }
     }
-    int nq[4], thr[4];
-    int64_t bq[4];
+    int nq[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        nq[i] = sh_n[4 * g + i];
-        bq[i] = sh_base[4 * g + i];
-        thr[i] = sh_thr[4 * g + i];
-    }
+    for (int i = 0; i < 4; ++i) nq[i] = sh_n[4 * g + i];
     __syncthreads();
 
     // positions below n_min are visible to every query of the workgroup (0 when the workgroup
@@ -248,13 +223,14 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
     for (int k = 0; k < kPfQ; ++k) n_min = min(n_min, q0 + k < n_q ? sh_n[k] : 0);
 
     const int p_wave = p_wg + wid * (kPfPos / 4);
-    constexpr int TB = 4;          // 16-position tiles per load batch
-    constexpr int kBatch = 16 * TB;
+    constexpr int TB = 4;                   // sampled tiles per load batch
+    constexpr int kTs = 16 * kPfStride;     // position step between a batch's tiles
+    constexpr int kBatch = TB * kTs;        // positions a batch spans
     // key rows of one batch (rows past the longest visible length read as zero)
     auto load_batch = [&](uint4 (&kb)[TB][2], int base) {
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
-            const int p = base + 16 * u + r;
+            const int p = base + kTs * u + r;
             if (p < n_max) {
                 const uint16_t* row = k_idx + (row0 + p) * 64 + 8 * g;
                 kb[u][0] = *reinterpret_cast<const uint4*>(row);
@@ -265,8 +241,8 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
             }
         }
     };
-    // scores of one batch; ALL: every position of the batch is visible to all 16 queries, so
-    // no per-query length test (and no branch around the histogram update) is needed
+    // ALL: every position of the batch is visible to all 16 queries, so no per-query length
+    // test (and no branch around the histogram update) is needed
     auto score_batch = [&](const uint4 (&kb)[TB][2], int base, auto all_tag) {
         constexpr bool ALL = decltype(all_tag)::value;
 #pragma unroll
@@ -279,120 +255,292 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_prefill(
                 a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][1], as_bf16x8(kb[u][1]), a, 0, 0, 0);
                 acc[h] = a;
             }
-            const int p = base + 16 * u + r;
+            const int p = base + kTs * u + r;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float sc = 0.f;
 #pragma unroll
                 for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], relu(acc[h][i]), sc);
-                const bool ok = ALL || p < nq[i];
-                // the sum starts from +0, so it is never -0 and score_key's normalisation is not
-                // needed: flip every bit of a negative score, only the sign bit of the others
-                const uint32_t sb = __float_as_uint(sc);
-                const uint32_t key = ok ? sb ^ ((uint32_t)((int32_t)sb >> 31) | 0x80000000u) : 0u;
-                if constexpr (kCompact) {
-                    // at or above the query's threshold bucket: a sure position (above) or a
-                    // candidate (in it), gathered in LDS (candidate keys are never 0; a sure
-                    // entry is the bare position)
-                    const int dg = (int)(key >> 21);
-                    if (ok && dg >= thr[i]) {
-                        const int ql = 4 * g + i;
-                        const uint64_t e = dg > thr[i] ? (uint64_t)(uint32_t)p : composite(key, (uint32_t)p);
-                        const int slot = atomicAdd(&sh_cnt[ql], 1);
-                        if (slot < kPfBuf) {
-                            sh_buf[ql][slot] = e;
-                        } else {  // more than the buffer holds (heavy ties): straight to the list
-                            const int q = q0 + ql;
-                            uint32_t* ctrl = ws.ctrl + (int64_t)q * kCtlSlots;
-                            if (dg > thr[i])
-                                ws.sure_idx[(int64_t)q * top_k + atomicAdd(ctrl + kCtlSureIdx, 1u)] = p;
-                            else
-                                ws.cand_idx[bq[i] + atomicAdd(ctrl + kCtlCandIdx, 1u)] = e;
-                        }
-                    }
-                } else if (ok) {
-                    // first digit = key >> 21; two 16-bit counters per word: digit d and
-                    // d + 1024 share word d & 1023 (the key's top bit picks the half: an
-                    // increment of 1 or 1 << 16), so neighbouring digits, which the scores of
-                    // nearby positions often take, update different words
+                if (ALL || p < nq[i]) {
+                    // the sum starts from +0, so it is never -0: flip every bit of a negative
+                    // score, only the sign bit of the others.  First digit = key >> 21; two
+                    // 16-bit counters per word: digit d and d + 1024 share word d & 1023 (the
+                    // key's top bit picks the half: an increment of 1 or 1 << 16), so
+                    // neighbouring digits, which nearby scores often take, update different words
+                    const uint32_t sb = __float_as_uint(sc);
+                    const uint32_t key = sb ^ ((uint32_t)((int32_t)sb >> 31) | 0x80000000u);
                     const uint32_t word = (key >> 21) & 0x3ffu;
                     const uint32_t half = key >> 31;
                     atomicAdd(&sh_hist[4 * g + i][word], 1u + half * 0xffffu);
                 }
-                if constexpr (POOL && !kCompact) {
-                    const uint32_t bk = max_over_8_lanes(key);      // lanes 4 / 12 of the row
-                    const int pblk = base + 16 * u + (r & 8);
-                    if ((r & 7) == 4 && pblk < nq[i]) ws.bkeys[bq[i] / 8 + (pblk >> 3)] = bk;
-                }
             }
         }
-    };
-    auto score_any = [&](const uint4 (&kb)[TB][2], int base) {
-        if (base + kBatch <= n_min)
-            score_batch(kb, base, std::true_type{});
-        else
-            score_batch(kb, base, std::false_type{});
     };
     for (int b = 0; b < kPfPos / 4; b += kBatch) {
         const int base = p_wave + b;
         if (base >= n_max) break;
         uint4 kb[TB][2];
         load_batch(kb, base);
-        score_any(kb, base);
+        if (base + kBatch - kTs + 16 <= n_min)
+            score_batch(kb, base, std::true_type{});
+        else
+            score_batch(kb, base, std::false_type{});
     }
     __syncthreads();
-    if constexpr (kCompact) {
-        // each wave writes the gathered entries of four queries: one reservation per list and
-        // query, places from ballots (no LDS atomics)
-        for (int ql = wid; ql < kPfQ; ql += kScoreNT / kWave) {
-            const int q = q0 + ql;
-            const int nb = min(sh_cnt[ql], kPfBuf);
-            if (q >= n_q || nb == 0) continue;
-            int ns = 0;
-            for (int j0 = 0; j0 < nb; j0 += kWave) {
-                const int j = j0 + lane;
-                ns += __popcll(__ballot(j < nb && (sh_buf[ql][j] >> 32) == 0ull));
-            }
-            uint32_t* ctrl = ws.ctrl + (int64_t)q * kCtlSlots;
-            int bs = 0, bc = 0;
-            if (lane == 0) {
-                if (ns) bs = (int)atomicAdd(ctrl + kCtlSureIdx, (uint32_t)ns);
-                if (nb - ns) bc = (int)atomicAdd(ctrl + kCtlCandIdx, (uint32_t)(nb - ns));
-            }
-            bs = __builtin_amdgcn_readfirstlane(bs);
-            bc = __builtin_amdgcn_readfirstlane(bc);
-            for (int j0 = 0; j0 < nb; j0 += kWave) {
-                const int j = j0 + lane;
-                const uint64_t e = j < nb ? sh_buf[ql][j] : 0ull;
-                const bool is_s = j < nb && (e >> 32) == 0ull, is_c = j < nb && (e >> 32) != 0ull;
-                const uint64_t ms = __ballot(is_s), mc = __ballot(is_c);
-                const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-                if (is_s) ws.sure_idx[(int64_t)q * top_k + bs + __popcll(ms & below)] = (int32_t)(uint32_t)e;
-                if (is_c) ws.cand_idx[sh_base[ql] + bc + __popcll(mc & below)] = e;
-                bs += __popcll(ms);
-                bc += __popcll(mc);
-            }
-        }
-    } else {
-        for (int k = t; k < kPfQ * kHistBins / 2; k += kScoreNT) {
-            const int ql = k / (kHistBins / 2), wd = k % (kHistBins / 2);
-            const uint32_t v = sh_hist[ql][wd];
-            if (v == 0u || q0 + ql >= n_q) continue;
-            uint32_t* gh = ws.hist + (int64_t)(q0 + ql) * 2 * kHistBins;
-            if (v & 0xffffu) atomicAdd(&gh[wd], v & 0xffffu);
-            if (v >> 16) atomicAdd(&gh[wd + kHistBins / 2], v >> 16);
+    for (int k = t; k < kPfQ * kHistBins / 8; k += kScoreNT) {
+        const int ql = k / (kHistBins / 8);
+        const uint4 v = reinterpret_cast<const uint4*>(&sh_hist[0][0])[k];
+        if ((v.x | v.y | v.z | v.w) == 0u || q0 + ql >= n_q) continue;
+        uint32_t* gh = ws.hist + (int64_t)(q0 + ql) * 2 * kHistBins;
+        const int wd = 4 * (k % (kHistBins / 8));
+        const uint32_t c[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (c[j] & 0xffffu) atomicAdd(&gh[wd + j], c[j] & 0xffffu);
+            if (c[j] >> 16) atomicAdd(&gh[wd + j + kHistBins / 2], c[j] >> 16);
         }
     }
 }
 
-// Prefill chunk: every query's threshold bucket for its Top-K from the finished position
-// histogram (one workgroup per query), for the compacting scoring pass.
+// ----------------------------------------------------------------------------------------
+// Prefill chunk, candidate pass: every visible position of every query is scored, and those
+// whose first key digit reaches the query's sampled threshold digit are kept (see the sample
+// pass above for why the Top-K lies inside them).  A workgroup takes kPcQ = 64 queries (16 per
+// wave, one MFMA tile's worth) and kPcPos positions; the key rows go through LDS in stages of
+// kPcStage positions (the next stage's loads in flight while the current one is scored), so
+// each row is fetched once per 64 queries rather than once per 16.
+// Kept entries are appended to a per-wave LDS ring with one ballot per (tile, query row): no
+// atomics on that path.  When the ring may not take another tile, the wave flushes it:
+// per-query counts reserve room in the queries' global candidate lists (one atomic per query),
+// entries are scattered there as (key, position) composites, and the per-(query, digit) counts
+// are added to the query's position histogram, which then holds exactly the candidates'
+// first-digit counts for the selection.  A ring entry is key << 32 | wave-row << 26 | position
+// (positions below 2^26).
+// POOL: every query's 8-position block maxima go to the block keys as in the sample pass's
+// layout (lanes 4 and 12 of each 16-lane row).
+// ----------------------------------------------------------------------------------------
+constexpr int kPcQ = 64;         // queries per workgroup: 16 per wave
+constexpr int kPcPos = 4096;     // positions per workgroup
+constexpr int kPcStage = 128;    // positions per LDS key stage (8 MFMA tiles)
+constexpr int kPcRowB = 144;     // bytes per staged key row: 128 + 16, which spreads rows over the banks
+constexpr int kPcRing = 512;     // ring entries per wave (a tile adds at most 256)
+constexpr int kPcDW = 16;        // digits at and above the sampled one counted in LDS
+constexpr int kPcMaxPos = 1 << 26;
+
+__host__ __device__ __forceinline__ int pc_items_per_xcd(int n_px, int n_qg) {
+    return (n_px * n_qg + kXcds - 1) / kXcds;
+}
+
+template <bool POOL>
+__global__ __launch_bounds__(kScoreNT) void k_idx_prefill_cand(
+    const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
+    const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, int n_px, int n_qg,
+    IndexWs ws) {
+    __shared__ __align__(16) uint8_t sh_keys[2][kPcStage * kPcRowB];
+    __shared__ uint64_t sh_ring[kScoreNT / kWave][kPcRing];
+    __shared__ uint32_t sh_dcnt[kScoreNT / kWave][16 * kPcDW];   // [wave][row * kPcDW + digit offset]
+    __shared__ uint32_t sh_qcur[kScoreNT / kWave][16];
+    __shared__ int sh_n[kPcQ];
+    __shared__ int sh_thr[kPcQ];
+    __shared__ int64_t sh_base[kPcQ];
+    const int t = threadIdx.x;
+    const int lane = __lane_id();
+    const int wid = t / kWave;
+    const int g = lane >> 4, r = lane & 15;
+    const int item = (int)(blockIdx.x % kXcds) * pc_items_per_xcd(n_px, n_qg) + (int)(blockIdx.x / kXcds);
+    if (item >= n_px * n_qg) return;  // uniform: the grid is rounded up to a multiple of kXcds
+    const int q0 = (item % n_qg) * kPcQ;
+    const int p_wg = (item / n_qg) * kPcPos;
+    const int64_t row0 = kv_row0[0];
+    const int64_t row_room = (row0 >= 0 && row0 <= cache_rows) ? cache_rows - row0 : 0;
+    if (t < kPcQ) {
+        const int q = q0 + t;
+        int n = 0, thr = -1;
+        int64_t base = 0;
+        if (q < n_q) {
+            const QMeta m = ws.qmeta[q];
+            n = (int)min((int64_t)m.n, row_room);
+            base = (int64_t)m.start * kFullTile;
+            thr = ws.meta[2 * q].digit;
+        }
+        sh_n[t] = n;
+        sh_base[t] = base;
+        sh_thr[t] = thr;
+    }
+    for (int k = t; k < (kScoreNT / kWave) * 16 * kPcDW; k += kScoreNT) (&sh_dcnt[0][0])[k] = 0u;
+    __syncthreads();
+    int n_max = 0;
+    for (int k = 0; k < kPcQ; ++k) n_max = max(n_max, sh_n[k]);
+    if (p_wg >= n_max) return;  // uniform: nothing visible in this position chunk
+    const int p_end = min(n_max, p_wg + kPcPos);
+    const int wq0 = wid * 16;  // this wave's first query (within the workgroup)
+    int n_min = INT32_MAX;     // positions below it are visible to all 16 queries of the wave
+    for (int k = 0; k < 16; ++k) n_min = min(n_min, q0 + wq0 + k < n_q ? sh_n[wq0 + k] : 0);
+
+    // A fragments: query q0 + wq0 + r, head h, channels 32s + 8g .. +8; weights, lengths and
+    // threshold keys of the lane's four queries q0 + wq0 + 4g + i
+    bf16x8_t qa[4][2];
+    float wq[4][4];
+    int nq[4];
+    uint32_t tk[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const int q = q0 + wq0 + r;
+        const bool ok = q < n_q && h < n_heads;
+        const uint16_t* qp = q_idx + ((int64_t)(ok ? q : 0) * n_heads + (ok ? h : 0)) * 64 + 8 * g;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+            qa[h][s2] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qp + 32 * s2) : make_uint4(0, 0, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int qi = q0 + wq0 + 4 * g + i;
+            wq[i][h] = (qi < n_q && h < n_heads) ? w[(int64_t)qi * n_heads + h] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        nq[i] = sh_n[wq0 + 4 * g + i];
+        const int d = sh_thr[wq0 + 4 * g + i];
+        tk[i] = d < 0 ? 0u : (uint32_t)d << 21;
+    }
+
+    // ---- the wave's candidate ring ----
+    uint64_t* ring = sh_ring[wid];
+    uint32_t* dcnt = sh_dcnt[wid];
+    uint32_t* qcur = sh_qcur[wid];
+    int ring_n = 0;  // wave-uniform
+    auto flush = [&]() {
+        if (lane < 16) qcur[lane] = 0u;
+        wave_lds_sync();
+        for (int e = lane; e < ring_n; e += kWave) {
+            const uint64_t v = ring[e];
+            const int row = (int)((uint32_t)v >> 26) & 15;
+            const int d = (int)(v >> 53);
+            const int d0 = sh_thr[wq0 + row];
+            atomicAdd(&qcur[row], 1u);
+            if (d0 >= 0 && d - d0 < kPcDW)
+                atomicAdd(&dcnt[row * kPcDW + (d - d0)], 1u);
+            else  // (a digit far above the sampled one, or every position kept)
+                atomicAdd(ws.hist + (int64_t)(q0 + wq0 + row) * 2 * kHistBins + d, 1u);
+        }
+        wave_lds_sync();
+        if (lane < 16) {
+            const uint32_t c = qcur[lane];
+            uint32_t* ctrl = ws.ctrl + (int64_t)(q0 + wq0 + lane) * kCtlSlots;
+            qcur[lane] = c ? atomicAdd(ctrl + kCtlCandIdx, c) : 0u;
+        }
+        for (int k = lane; k < 16 * kPcDW; k += kWave) {
+            const uint32_t c = dcnt[k];
+            if (c) {
+                const int row = k / kPcDW;
+                atomicAdd(ws.hist + (int64_t)(q0 + wq0 + row) * 2 * kHistBins + sh_thr[wq0 + row] + k % kPcDW, c);
+                dcnt[k] = 0u;
+            }
+        }
+        wave_lds_sync();
+        for (int e = lane; e < ring_n; e += kWave) {
+            const uint64_t v = ring[e];
+            const int row = (int)((uint32_t)v >> 26) & 15;
+            const uint32_t slot = atomicAdd(&qcur[row], 1u);
+            ws.cand_idx[sh_base[wq0 + row] + slot] = composite((uint32_t)(v >> 32), (uint32_t)v & (kPcMaxPos - 1));
+        }
+        wave_lds_sync();
+        ring_n = 0;
+    };
+
+    // ---- key stages: thread t moves 64 bytes (row t / 2, half t % 2) ----
+    const int ld_row = t >> 1, ld_half = t & 1;
+    uint4 stg[4];
+    auto load_stage = [&](int ps) {
+        const int p = ps + ld_row;
+        const uint16_t* src = k_idx + (row0 + p) * 64 + 32 * ld_half;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            stg[j] = p < p_end ? *reinterpret_cast<const uint4*>(src + 8 * j) : make_uint4(0, 0, 0, 0);
+    };
+    auto store_stage = [&](int buf) {
+        uint8_t* dst = sh_keys[buf] + ld_row * kPcRowB + 64 * ld_half;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(dst + 16 * j) = stg[j];
+    };
+    // scores of one stage; ALL: every position of the stage is visible to the wave's queries
+    auto score_stage = [&](int buf, int ps, auto all_tag) {
+        constexpr bool ALL = decltype(all_tag)::value;
+        const uint8_t* kb = sh_keys[buf];
+#pragma unroll 2
+        for (int u = 0; u < kPcStage / 16; ++u) {
+            if (ring_n > kPcRing - 256) flush();  // wave-uniform
+            const uint8_t* kr = kb + (16 * u + r) * kPcRowB + 16 * g;
+            const bf16x8_t b0 = as_bf16x8(*reinterpret_cast<const uint4*>(kr));
+            const bf16x8_t b1 = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 64));
+            f32x4_t acc[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][0], b0, a, 0, 0, 0);
+                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][1], b1, a, 0, 0, 0);
+                acc[h] = a;
+            }
+            const int p = ps + 16 * u + r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float sc = 0.f;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], relu(acc[h][i]), sc);
+                const bool ok = ALL || p < nq[i];
+                // the sum starts from +0, so it is never -0: flip every bit of a negative
+                // score, only the sign bit of the others
+                const uint32_t sb = __float_as_uint(sc);
+                const uint32_t key = ok ? sb ^ ((uint32_t)((int32_t)sb >> 31) | 0x80000000u) : 0u;
+                const bool kept = ok && key >= tk[i];
+                const uint64_t m = __ballot(kept);
+                if (m) {  // wave-uniform
+                    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (kept)
+                        ring[ring_n + rank] =
+                            ((uint64_t)key << 32) | ((uint32_t)(4 * g + i) << 26) | (uint32_t)p;
+                    ring_n += __popcll(m);
+                }
+                if constexpr (POOL) {
+                    const uint32_t bk = max_over_8_lanes(key);  // lanes 4 / 12 of the row
+                    const int pblk = ps + 16 * u + (r & 8);
+                    if ((r & 7) == 4 && pblk < nq[i])
+                        ws.bkeys[sh_base[wq0 + 4 * g + i] / 8 + (pblk >> 3)] = bk;
+                }
+            }
+        }
+    };
+
+    load_stage(p_wg);
+    store_stage(0);
+    __syncthreads();
+    int buf = 0;
+    for (int ps = p_wg; ps < p_end; ps += kPcStage) {
+        const bool more = ps + kPcStage < p_end;  // uniform
+        if (more) load_stage(ps + kPcStage);
+        if (ps + kPcStage <= n_min)
+            score_stage(buf, ps, std::true_type{});
+        else
+            score_stage(buf, ps, std::false_type{});
+        if (more) store_stage(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+    }
+    if (ring_n > 0) flush();
+}
+
+// Prefill chunk: every query's sampled threshold digit (the digit holding the K-th largest key
+// of its sample; -1 when the sample holds at most K keys: then every visible position is a
+// candidate), one workgroup per query.  Clears the sample histogram for the next call.
 __global__ __launch_bounds__(kScoreNT) void k_idx_prefill_thresh(int top_k, IndexWs ws) {
     __shared__ int sh_scan[kScoreNT / kWave];
     __shared__ Thresh sh_th;
     const int i = blockIdx.x;
-    find_threshold_256(ws.hist + (int64_t)i * 2 * kHistBins, top_k, sh_scan, &sh_th);
+    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
+    find_threshold_256(gh, top_k, sh_scan, &sh_th);  // (ends with a barrier: every bin is read)
     if (threadIdx.x == 0) ws.meta[2 * i] = sh_th;
+    for (int b = threadIdx.x; b < kHistBins; b += kScoreNT) gh[b] = 0u;
 }
 
 // First-digit histogram of each query's block-max keys (prefill chunk with pools): workgroup
@@ -659,10 +807,58 @@ __device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, 
     bucket_write_ascending<NT>(sel, total, k, out, A.scratch, A.scan, A.mm);
 }
 
+// The LDS part of a selection: W.cand[0, m) holds the threshold bucket's composites (first
+// digit d1) and W.sel[0, W.cnt) the positions already selected (those above the bucket); adds
+// the `need` best of the bucket to W.sel and returns how many W.sel holds.  The threshold KEY
+// comes first (at most two radix passes); equal keys at it are ranked by position.
+template <int NT, int CAP>
+__device__ int select_bucket_lds(SmallSel<CAP>& W, AscLds<NT>& A, int m, int need, int d1) {
+    const int t = threadIdx.x;
+    const bool any = need > 0 && m > 0;
+    const KeyThr kt = any ? lds_key_threshold<NT>(W.cand, m, need, d1, W.R) : KeyThr{0u, -1, 0};
+    const bool ranked = any && kt.take_eq >= 0;  // only take_eq of the n_tie equal keys go
+    int total;
+    if (ranked && kt.n_tie > kTieCap) {
+        // many equal keys at the threshold: radix passes over the composites' position bits
+        const uint64_t thr = lds_radix_threshold<NT>(W.cand, m, need, d1, W.R);
+        for (int e = t; e < m; e += NT)
+            if (W.cand[e] >= thr) W.sel[atomicAdd(&W.cnt, 1)] = composite_pos(W.cand[e]);
+        __syncthreads();
+        total = W.cnt;
+    } else {
+        uint32_t* ties = A.scratch;  // free until the ascending output
+        for (int e = t; e < m; e += NT) {
+            const uint64_t c = W.cand[e];
+            const uint32_t key = (uint32_t)(c >> 32);
+            if (any && (ranked ? key > kt.t : key >= kt.t))
+                W.sel[atomicAdd(&W.cnt, 1)] = composite_pos(c);
+            else if (ranked && key == kt.t)
+                ties[atomicAdd(&W.nt, 1)] = composite_pos(c);
+        }
+        __syncthreads();
+        total = W.cnt;
+        if (ranked) {
+            // each tie's place among the ties by position (distinct positions): the take_eq
+            // lowest follow the keys above the threshold
+            const int nt = W.nt;
+            for (int j = t; j < nt; j += NT) {
+                const uint32_t p = ties[j];
+                int rank = 0;
+                for (int e = 0; e < nt; ++e) rank += ties[e] < p ? 1 : 0;
+                if (rank < kt.take_eq) W.sel[total + rank] = p;
+            }
+            total += kt.take_eq;
+            __syncthreads();
+        }
+    }
+    return total;
+}
+
 // ----------------------------------------------------------------------------------------
 // Full mode, kernel 3: exact selection inside the threshold bucket; one workgroup per
-// (query, list).  The bucket's candidates normally fit in LDS: radix passes there find the
-// threshold, and each selected position's output slot is its rank among the selected.
+// (query, list), list = list0 + blockIdx.y (0: positions, 1: pool blocks).  The bucket's
+// candidates normally fit in LDS: radix passes there find the threshold, and each selected
+// position's output slot is its rank among the selected.
 // scan_keys != 0 (decode, every context <= kSelScanMax): the filter kernel did not run and this
 // workgroup splits the query's keys into the above-bucket and in-bucket lists itself.
 // Leaves the histograms and counters of the query zero for the next call.
@@ -673,7 +869,7 @@ __device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, 
 template <int NT, int CAP>
 // (as in the filter pass: the first loads' workspace areas lead the arguments, preloaded)
 __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* hist, uint32_t* keys, uint32_t* bkeys,
-                                                        int top_k, int pool_blocks, int scan_keys, IndexWs ws,
+                                                        int top_k, int pool_blocks, int scan_keys, int list0, IndexWs ws,
                                                         int32_t* __restrict__ idx_out,
                                                         int32_t* __restrict__ pool_out) {
     ws.qmeta = qmeta;
@@ -684,7 +880,7 @@ __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* 
     __shared__ AscLds<NT> A;
     __shared__ Thresh sh_th;
     const int i = blockIdx.x;
-    const int which = blockIdx.y;  // 0: positions, 1: pool blocks
+    const int which = list0 + (int)blockIdx.y;  // 0: positions, 1: pool blocks
     const int t = threadIdx.x;
     const QMeta qm = ws.qmeta[i];
     const int64_t key_base = (int64_t)qm.start * kFullTile;
@@ -732,45 +928,7 @@ __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* 
             W.nt = 0;
         }
         __syncthreads();
-        // the threshold KEY first (at most two passes); ties at it are ordered by position below
-        const bool any = need > 0 && th.in_bucket > 0;
-        const KeyThr kt = any ? lds_key_threshold<NT>(W.cand, th.in_bucket, need, th.digit, W.R)
-                              : KeyThr{0u, -1, 0};
-        const bool ranked = any && kt.take_eq >= 0;  // only take_eq of the n_tie equal keys go
-        int total;
-        if (ranked && kt.n_tie > kTieCap) {
-            // many equal keys at the threshold: radix passes over the composites' position bits
-            const uint64_t thr = lds_radix_threshold<NT>(W.cand, th.in_bucket, need, th.digit, W.R);
-            for (int e = t; e < th.in_bucket; e += NT)
-                if (W.cand[e] >= thr) W.sel[atomicAdd(&W.cnt, 1)] = composite_pos(W.cand[e]);
-            __syncthreads();
-            total = W.cnt;
-        } else {
-            uint32_t* ties = A.scratch;  // free until the ascending output
-            for (int e = t; e < th.in_bucket; e += NT) {
-                const uint64_t c = W.cand[e];
-                const uint32_t key = (uint32_t)(c >> 32);
-                if (any && (ranked ? key > kt.t : key >= kt.t))
-                    W.sel[atomicAdd(&W.cnt, 1)] = composite_pos(c);
-                else if (ranked && key == kt.t)
-                    ties[atomicAdd(&W.nt, 1)] = composite_pos(c);
-            }
-            __syncthreads();
-            total = W.cnt;
-            if (ranked) {
-                // each tie's place among the ties by position (distinct positions): the take_eq
-                // lowest follow the keys above the threshold
-                const int nt = W.nt;
-                for (int j = t; j < nt; j += NT) {
-                    const uint32_t p = ties[j];
-                    int rank = 0;
-                    for (int e = 0; e < nt; ++e) rank += ties[e] < p ? 1 : 0;
-                    if (rank < kt.take_eq) W.sel[total + rank] = p;
-                }
-                total += kt.take_eq;
-                __syncthreads();
-            }
-        }
+        const int total = select_bucket_lds<NT, CAP>(W, A, th.in_bucket, need, th.digit);
         sort_out(W.sel, total, k, out, A);
     } else {
         SelectSharedT<CAP>& S = U.big;
@@ -789,6 +947,81 @@ __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* 
         ctrl[which ? kCtlSurePool : kCtlSureIdx] = 0u;
         ctrl[which ? kCtlCandPool : kCtlCandIdx] = 0u;
     }
+}
+
+// ----------------------------------------------------------------------------------------
+// Prefill chunk, positions: the exact Top-K of each query among the candidates of the
+// candidate pass (composites at or above its sampled threshold digit; unique composites, so
+// the K largest are the Top-K in (score desc, position asc) order), one workgroup per query.
+// The query's position histogram holds the candidates' first-digit counts (added by the
+// candidate pass), which give the exact threshold bucket; the candidates above it are
+// selected, and those in it go to LDS for select_bucket_lds, or, when more than CAP share the
+// bucket (heavy ties), to the radix passes over the global list.
+// Leaves the query's histogram and candidate counter zero for the next call.
+// ----------------------------------------------------------------------------------------
+template <int NT, int CAP>
+__global__ __launch_bounds__(NT) void k_idx_select_cands(QMeta* qmeta, uint32_t* ctrl_all, uint32_t* hist_all,
+                                                         uint64_t* cand_all, int top_k, int32_t* __restrict__ idx_out) {
+    __shared__ SelLds<CAP> U;
+    __shared__ AscLds<NT> A;
+    __shared__ Thresh sh_th;
+    const int i = blockIdx.x;
+    const int t = threadIdx.x;
+    uint32_t* gh = hist_all + (int64_t)i * 2 * kHistBins;
+    uint32_t h[kHistBins / NT];
+    hist_load<NT>(gh, h);
+    const QMeta qm = qmeta[i];
+    uint32_t* ctrl = ctrl_all + (int64_t)i * kCtlSlots;
+    const uint64_t* cand = cand_all + (int64_t)qm.start * kFullTile;
+    int32_t* out = idx_out + (int64_t)i * top_k;
+    // the candidates are distinct visible positions: at most n of them
+    const int m = (int)min((int64_t)ctrl[kCtlCandIdx], (int64_t)max(qm.n, 0));
+    SmallSel<CAP>& W = U.small;
+    find_threshold_regs<NT>(h, top_k, W.R.scan, &sh_th);
+    const Thresh th = sh_th;
+    if (th.digit < 0) {
+        // at most K candidates: every one is selected
+        const int mk = min(m, top_k);
+        uint32_t* sel = W.sel;
+        for (int e = t; e < mk; e += NT) sel[e] = composite_pos(cand[e]);
+        __syncthreads();
+        sort_out(sel, mk, top_k, out, A);
+    } else if (th.in_bucket <= CAP) {
+        if (t == 0) {
+            W.cnt = 0;
+            W.nt = 0;
+            W.R.inb = 0;  // (counts the bucket's fill until the radix passes)
+        }
+        __syncthreads();
+        for (int e = t; e < m; e += NT) {
+            const uint64_t c = cand[e];
+            const int d = (int)(c >> 53);
+            // (the histogram counts exactly these candidates: the slots stay below above / in_bucket)
+            if (d > th.digit) {
+                const int j = atomicAdd(&W.cnt, 1);
+                if (j < top_k) W.sel[j] = composite_pos(c);
+            } else if (d == th.digit) {
+                const int j = atomicAdd(&W.R.inb, 1);
+                if (j < CAP) W.cand[j] = c;
+            }
+        }
+        __syncthreads();
+        const int total = select_bucket_lds<NT, CAP>(W, A, th.in_bucket, top_k - th.above, th.digit);
+        sort_out(W.sel, total, top_k, out, A);
+    } else {
+        SelectSharedT<CAP>& S = U.big;
+        // the need-th largest of the bucket; every candidate above the bucket exceeds it
+        const uint64_t thr = wg_threshold<NT>(CompositeList{cand}, m, top_k - th.above, th.digit, S);
+        uint32_t* sel = reinterpret_cast<uint32_t*>(S.buf);
+        if (t == 0) S.cnt = 0;
+        __syncthreads();
+        for (int e = t; e < m; e += NT)
+            if (cand[e] >= thr) sel[atomicAdd(&S.cnt, 1)] = composite_pos(cand[e]);
+        __syncthreads();
+        sort_out(sel, S.cnt, top_k, out, A);
+    }
+    for (int b = t; b < kHistBins; b += NT) gh[b] = 0u;
+    if (t == 0) ctrl[kCtlCandIdx] = 0u;
 }
 
 // ----------------------------------------------------------------------------------------
@@ -916,26 +1149,27 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
             if (e != hipSuccess) return e;
         }
         if (prefill && max_len > 0) {  // (no visible position anywhere: nothing to score)
-            const int n_px = (max_len + kPfPos - 1) / kPfPos, n_qg = (n_q + kPfQ - 1) / kPfQ;
-            const dim3 grid((unsigned)(kXcds * pf_items_per_xcd(n_px, n_qg)));
             const uint16_t* kb = static_cast<const uint16_t*>(k_idx);
-            auto k_hist = pool_blocks > 0 ? k_idx_score_prefill<true, kPfHist> : k_idx_score_prefill<false, kPfHist>;
-            hipLaunchKernelGGL(k_hist, grid, dim3(kScoreNT), 0, stream, q_idx, w, kb, kv_row0, n_q, cache_rows, n_heads,
-                               top_k, n_px, n_qg, ws);
+            // the sample, its threshold digits, then every position against them
+            const int s_px = (max_len + kPfPos - 1) / kPfPos, s_qg = (n_q + kPfQ - 1) / kPfQ;
+            hipLaunchKernelGGL(k_idx_prefill_sample, dim3((unsigned)(kXcds * pf_items_per_xcd(s_px, s_qg))),
+                               dim3(kScoreNT), 0, stream, q_idx, w, kb, kv_row0, n_q, cache_rows, n_heads, s_px, s_qg,
+                               ws);
             hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(k_idx_prefill_thresh, dim3(n_q), dim3(kScoreNT), 0, stream, top_k, ws);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int c_px = (max_len + kPcPos - 1) / kPcPos, c_qg = (n_q + kPcQ - 1) / kPcQ;
+            auto k_cand = pool_blocks > 0 ? k_idx_prefill_cand<true> : k_idx_prefill_cand<false>;
+            hipLaunchKernelGGL(k_cand, dim3((unsigned)(kXcds * pc_items_per_xcd(c_px, c_qg))), dim3(kScoreNT), 0,
+                               stream, q_idx, w, kb, kv_row0, n_q, cache_rows, n_heads, c_px, c_qg, ws);
+            e = hipGetLastError();
             if (e != hipSuccess) return e;
             if (pool_blocks > 0) {
                 const dim3 bgrid((unsigned)(((max_len + 7) / 8 + kBhChunk - 1) / kBhChunk), (unsigned)n_q);
                 hipLaunchKernelGGL(k_idx_block_hist, bgrid, dim3(kScoreNT), 0, stream, kv_row0, cache_rows, ws);
-                e = hipGetLastError();
-                if (e != hipSuccess) return e;
             }
-            hipLaunchKernelGGL(k_idx_prefill_thresh, dim3(n_q), dim3(kScoreNT), 0, stream, top_k, ws);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
-            auto k_compact = k_idx_score_prefill<false, kPfCompact>;
-            hipLaunchKernelGGL(k_compact, grid, dim3(kScoreNT), 0, stream, q_idx, w, kb, kv_row0, n_q, cache_rows,
-                               n_heads, top_k, n_px, n_qg, ws);
         } else if (!prefill) {
             // tiles split into 2 or 4 units while the host's tile bound leaves the grid half empty
             int sub_log2 = 0;
@@ -994,9 +1228,20 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
             if (e != hipSuccess) return e;
         }
         const bool many = prefill && n_q >= 512;
+        if (prefill) {
+            // positions: the exact Top-K among each query's candidates; pool blocks (when asked
+            // for): the threshold-bucket selection over the filtered block lists
+            auto candk = many ? k_idx_select_cands<kSelNTMany, kSortCapMany> : k_idx_select_cands<kSelNT, kSortCap>;
+            hipLaunchKernelGGL(candk, dim3(n_q), dim3(many ? kSelNTMany : kSelNT), 0, stream, ws.qmeta, ws.ctrl,
+                               ws.hist, ws.cand_idx, top_k, idx_out);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess || pool_blocks <= 0) return e;
+        }
         auto selk = many ? k_idx_select_full<kSelNTMany, kSortCapMany> : k_idx_select_full<kSelNT, kSortCap>;
-        hipLaunchKernelGGL(selk, dim3(n_q, pool_blocks > 0 ? 2 : 1), dim3(many ? kSelNTMany : kSelNT), 0, stream,
-                           ws.qmeta, ws.hist, ws.keys, ws.bkeys, top_k, pool_blocks, scan_keys, ws, idx_out, pool_out);
+        const int list0 = prefill ? 1 : 0;
+        hipLaunchKernelGGL(selk, dim3(n_q, pool_blocks > 0 && !prefill ? 2 : 1), dim3(many ? kSelNTMany : kSelNT), 0,
+                           stream, ws.qmeta, ws.hist, ws.keys, ws.bkeys, top_k, pool_blocks, scan_keys, list0, ws,
+                           idx_out, pool_out);
         return hipGetLastError();
     }
     return hipSuccess;
