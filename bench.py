@@ -49,6 +49,13 @@ STORAGE = ("main KV FP4 (E2M1 + E4M3 per 16 ch); indexer keys bf16 (MXFP4 in the
            "window bf16 (E4M3 in the fp8win workloads); scores, softmax and outputs fp32")
 KERNEL_NAMES = {"scan": "k_idx_score_full", "reindex_score": "k_idx_reindex_score",
                 "reindex_select": "k_idx_reindex_select", "attend": "k_attend"}
+DECODE_MAX_Q = 64   # attention calls of at most this many queries run k_attend_dec (entries split)
+
+
+def kernel_name(family: str, n_q: int) -> str:
+    if family == "attend" and n_q <= DECODE_MAX_Q:
+        return "k_attend_dec"
+    return KERNEL_NAMES[family]
 
 
 # sources whose text decides each timed kernel's code (compiler flags included): a committed counter
@@ -61,6 +68,8 @@ KERNEL_SOURCES = {
                       "compressed_sparse_attention_07_amd/csrc/scan_common.hpp"] + _COMMON,
     "reindex_select": ["compressed_sparse_attention_07_amd/csrc/reindex_select.hpp"] + _COMMON,
     "attend": ["compressed_sparse_attention_07_amd/csrc/attend.hip",
+               "compressed_sparse_attention_07_amd/csrc/attend_decode.hip",
+               "compressed_sparse_attention_07_amd/csrc/attend_common.hpp",
                "compressed_sparse_attention_07_amd/csrc/pack_common.hpp"] + _COMMON,
 }
 
@@ -72,10 +81,10 @@ def source_sha(family: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(family: str, workload_name: str):
-    """Calibrated HBM bytes per launch of a kernel family from the committed counter summary
+def read_traffic(kernel: str, family: str, workload_name: str):
+    """Calibrated HBM bytes per launch of a kernel from the committed counter summary
     profiles/traffic_<kernel>_<workload>.md, if it was taken on the current sources (else None)."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_NAMES[family]}_{workload_name}.md")
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_name}.md")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -166,7 +175,7 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
     for k in ("scan", "reindex_score", "reindex_select", "attend"):
         if k not in avg_us:
             continue
-        e = {"kernel": KERNEL_NAMES[k], "family": k, "avg_launch_us": round(avg_us[k], 2),
+        e = {"kernel": kernel_name(k, r.n_q), "family": k, "avg_launch_us": round(avg_us[k], 2),
              "launches_per_step": per_step[k], "share_of_step": round(avg_us[k] * per_step[k] / (ms_step * 1e3), 4)}
         if not wl.prefill_chunk:
             gbps = kb[k] / (avg_us[k] / 1e6) / 1e9
@@ -194,7 +203,7 @@ def measure(wid: int, steps: int, warmup: int, keep_host=False, copies=1):
     else:
         dom = max(kernels, key=lambda e: e["share_of_step"])
         res["roofline"] = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": dom["frac"], "traffic": read_traffic(dom["family"], wl.name),
+                           "frac": dom["frac"], "traffic": read_traffic(dom["kernel"], dom["family"], wl.name),
                            "kernel": dom["kernel"],
                            "share_of_step": dom["share_of_step"], "alg_bytes_per_launch": dom["alg_bytes_per_launch"],
                            "avg_launch_us": dom["avg_launch_us"]}

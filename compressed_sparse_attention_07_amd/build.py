@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
-SOURCES = ["fp4_pack.hip", "indexer.hip", "attend.hip", "noalloc.hip", "csa2_api.cpp"]
+SOURCES = ["fp4_pack.hip", "indexer.hip", "attend.hip", "attend_decode.hip", "noalloc.hip", "csa2_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -35,6 +35,7 @@ FLAGS = [
 EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
          # all three: a kernel's leading scalar and pointer arguments preloaded into SGPRs at launch
          "attend.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+         "attend_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-kernarg-preload-count=16"],
          # fp4_pack.hip: the scale table is built by the compiler (constexpr), which needs more steps
          "fp4_pack.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16", "-fconstexpr-steps=100000000"]}
 
@@ -51,7 +52,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]

@@ -84,7 +84,7 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = ctypes.c_int
         L.csa2_index_reindex.argtypes = [vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp]
         L.csa2_index_reindex_noalloc.argtypes = [vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp]
-        L.csa2_attend.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp]
+        L.csa2_attend.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp, sz, vp]
         L.fp8_window_append.argtypes = [vp, i64, i32, vp, i64, vp, i64, vp]
         L.mxfp4_key_append.argtypes = [vp, i64, i32, vp, i64, vp, vp, i64, vp]
         for name in ("csa2_index_full_mx", "csa2_index_full_mx_scan"):
@@ -93,14 +93,14 @@ def lib() -> ctypes.CDLL:
         L.csa2_index_full_scan_timed.argtypes = [vp, vp, vp, vp, SeqsC, i32, i32, i32, i32, i32, vp, vp, vp, sz, vp,
                                                  vp, vp]
         L.csa2_attend_fp8win.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, vp, i32, f32, vp,
-                                         vp]
+                                         vp, sz, vp]
         L.csa2_reindex_attend.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp,
                                           i32, i64, i32, vp, vp, i32, f32, vp, vp, sz, vp]
         L.csa2_token_append.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, vp]
         L.csa2_index_reindex_timed.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp, vp, vp,
                                                vp, vp]
-        L.csa2_attend_timed.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp, vp,
-                                        vp]
+        L.csa2_attend_timed.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp, sz,
+                                        vp, vp, vp]
         L.csa2_window_append.argtypes = [vp, i64, vp, i64, vp, i32, i64, vp]
         L.csa2_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
         L.csa2_workspace_bytes.restype = sz
@@ -236,27 +236,40 @@ def csa2_index_reindex(q_idx, w, k_idx, seqs: Seqs, pool, top_k: int, idx_out, w
         _ptr(idx_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
+def attend_workspace(n_q: int, top_k: int, window: int, device="cuda") -> torch.Tensor:
+    """A zeroed workspace for attention calls of these sizes (16 bytes when none is needed)."""
+    return alloc_workspace(csa2_workspace_bytes(OP_ATTEND, n_q, 0, 0, top_k, window), device)
+
+
+def _attend_ws(ws, q, top_k: int, window: int):
+    # the caller's workspace, or (for one-off calls) a fresh zeroed one of the required size
+    return ws if ws is not None else attend_workspace(q.shape[0], top_k, window, q.device)
+
+
 def csa2_attend(q, codes, scales, seqs: Seqs, idx, swa, swa_row0, swa_cap: int, window: int,
-                softmax_scale: float, out, win_new=None, stream=None) -> None:
+                softmax_scale: float, out, win_new=None, ws=None, stream=None) -> None:
     """Attention over the selected FP4 entries and the bf16 window; win_new (bf16 [n_q, 128] or
     None): the new token's window vector, attended as position N - 1 and written to its row."""
     n_heads = q.shape[1]
     top_k = idx.shape[1] if idx is not None else 0
     swa_rows = swa.shape[0] if swa is not None else 0
+    ws = _attend_ws(ws, q, top_k, window)
     _check("csa2_attend", lib().csa2_attend(
         _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa), _ptr(swa_row0), swa_cap,
-        swa_rows, window, _ptr(win_new), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _stream(stream)))
+        swa_rows, window, _ptr(win_new), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws), ws.numel(),
+        _stream(stream)))
 
 
 def csa2_attend_fp8win(q, codes, scales, seqs: Seqs, idx, swa8, swa_row0, swa_cap: int, window: int,
-                       softmax_scale: float, out, replay_start=None, win_new=None, stream=None) -> None:
+                       softmax_scale: float, out, replay_start=None, win_new=None, ws=None, stream=None) -> None:
     n_heads = q.shape[1]
     top_k = idx.shape[1] if idx is not None else 0
     swa_rows = swa8.shape[0] if swa8 is not None else 0
+    ws = _attend_ws(ws, q, top_k, window)
     _check("csa2_attend_fp8win", lib().csa2_attend_fp8win(
         _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa8), _ptr(swa_row0), swa_cap,
         swa_rows, window, _ptr(replay_start), _ptr(win_new), n_heads, ctypes.c_float(softmax_scale), _ptr(out),
-        _stream(stream)))
+        _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def csa2_reindex_attend(q_idx, w, k_idx, k_scales, seqs: Seqs, pool, top_k: int, idx_out, q, codes, scales, swa,
@@ -344,15 +357,17 @@ def csa2_index_reindex_timed(q_idx, w, k_idx, k_scales, seqs: Seqs, pool, top_k:
 
 
 def csa2_attend_timed(q, codes, scales, seqs: Seqs, idx, swa, swa_row0, swa_cap: int, window: int,
-                      softmax_scale: float, out, start_event, stop_event, win_new=None, stream=None) -> None:
+                      softmax_scale: float, out, start_event, stop_event, win_new=None, ws=None,
+                      stream=None) -> None:
     """csa2_attend with the attention kernel's own start and end recorded into two torch events."""
     n_heads = q.shape[1]
     top_k = idx.shape[1] if idx is not None else 0
     swa_rows = swa.shape[0] if swa is not None else 0
+    ws = _attend_ws(ws, q, top_k, window)
     _check("csa2_attend_timed", lib().csa2_attend_timed(
         _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa), _ptr(swa_row0), swa_cap,
-        swa_rows, window, _ptr(win_new), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _stream(stream),
-        _event(start_event), _event(stop_event)))
+        swa_rows, window, _ptr(win_new), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws), ws.numel(),
+        _stream(stream), _event(start_event), _event(stop_event)))
 
 
 def csa2_index_reindex_mx(q_idx, w, k_codes, k_scales, seqs: Seqs, pool, top_k: int, idx_out, ws,

@@ -38,6 +38,7 @@
 
 #include <type_traits>
 
+#include "attend_common.hpp"
 #include "csa2_device.hpp"
 #include "pack_common.hpp"
 #include "reindex_score.hpp"
@@ -49,87 +50,12 @@ constexpr int kAttWaves = 8;
 #ifndef CSA2_ATT_SPLIT
 #define CSA2_ATT_SPLIT 4   // workgroups per decode query (output dimensions split): 1, 2, 4 or 8
 #endif
-constexpr int kAttSplitMaxQ = 64;            // decode-sized calls take the split
 constexpr int kAttNT = kAttWaves * 64;
-constexpr int kD = 128;                      // latent / head dim
-constexpr int kNH = 16;                      // heads (padded)
 constexpr int kRB = 4;                       // FP4 blocks per wave per round
 constexpr int kRoundFp4 = kAttWaves * kRB;   // FP4 blocks per round (512 entries)
 constexpr int kRoundWin = kAttWaves;         // window blocks per round (128 entries)
-constexpr int kRowB = 288;                   // bytes per tile row: 128 x 16-bit + 32 B skew
-constexpr int kTileB = 32 * kRowB;           // one wave's tile: 32 entries
-constexpr int kOStride = 132;                // floats per head row of the merge buffer
 static_assert(kNH * kOStride * 4 <= kTileB, "a wave's merge rows fit in its tile");
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return lo16 | (hi16 << 16); }
-
-// Element i of a small per-query array through the vector memory path (a raw buffer load):
-// vector loads are counted in order, so a wait for these leaves later loads in flight, while
-// a wait for a scalar load waits for every scalar load, kernel arguments included.
-__device__ __forceinline__ int64_t vload_i64(const int64_t* p, int i) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int64_t*>(p), (short)0, 0x7fffffff, 0x00020000);
-    typedef int i32x2_t __attribute__((ext_vector_type(2)));
-    const i32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, 0, i * 8, 0);
-    return (int64_t)(((uint64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0]);
-}
-
-__device__ __forceinline__ int32_t vload_i32(const int32_t* p, int i) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p), (short)0, 0x7fffffff, 0x00020000);
-    return __builtin_amdgcn_raw_buffer_load_b32(rs, 0, i * 4, 0);
-}
-
-__device__ __forceinline__ uint32_t bf16_rne(float v) {
-    uint32_t b = __float_as_uint(v);
-    return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ uint32_t f16pair(float a, float b) {
-    const f16x2 v = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// Byte Q of w (low nibble = even channel, high nibble = odd channel) as two f16 values times
-// the group scale.  The conversion is given scale 1.0 (its scale operand only carries a power
-// of two); E2M1 x E4M3 needs at most 6 significant bits, so the f16 product is exact.
-template <int Q>
-__device__ __forceinline__ uint32_t fp4_pair_f16(uint32_t w, f16x2 sc) {
-    const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, Q);
-    return __builtin_bit_cast(uint32_t, v * sc);
-}
-
-// One lane's 32 FP4 codes (channels [32g, 32g+32)) and its two E4M3 scale bytes (low 16 bits
-// of sb) -> four f16x8 A fragments (fragment s = channels 32g + 8s .. 32g + 8s + 7).  The
-// hardware E4M3 -> f16 conversion is exact for every finite E4M3 value (the packer never
-// writes the NaN codes 0x7f / 0xff).
-__device__ __forceinline__ void dequant_f16(const uint4 cb, uint32_t sb, u32x4 (&f)[4]) {
-    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
-    const f16x2 sc0 = {sc[0], sc[0]}, sc1 = {sc[1], sc[1]};
-    const uint32_t w[4] = {cb.x, cb.y, cb.z, cb.w};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const f16x2 sc = s < 2 ? sc0 : sc1;
-        f[s][0] = fp4_pair_f16<0>(w[s], sc);
-        f[s][1] = fp4_pair_f16<1>(w[s], sc);
-        f[s][2] = fp4_pair_f16<2>(w[s], sc);
-        f[s][3] = fp4_pair_f16<3>(w[s], sc);
-    }
-}
-
-__device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-}
 
 // kFp4: top_k > 0 (the FP4 cache is read); kWin: window > 0 and the window store has rows.
 // Both are fixed per launch so that every gather below is unconditional (clamped addresses,
@@ -670,12 +596,27 @@ __global__ __launch_bounds__(kAttNT) void k_reindex_layer(const int32_t* __restr
 }
 
 // window_fp8: the window store holds E4M3 bytes; replay: per-query replay starts or NULL.
+hipError_t launch_attend_dec(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const int64_t* kv_row0,
+                             const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
+                             int top_k, const void* swa, int window_fp8, const int64_t* swa_row0, int swa_cap,
+                             int64_t swa_rows, int window, const int64_t* replay, int n_heads, float softmax_scale,
+                             float* out, const uint16_t* win_new, float* part, uint32_t* ctrl, hipStream_t stream,
+                             hipEvent_t ev_start, hipEvent_t ev_stop);
+
+// dec: a decode-sized call (at most kAttSplitMaxQ queries) whose entries are split over
+// workgroups (csrc/attend_decode.hip; part / ctrl: its merge workspace); otherwise one workgroup
+// per query (a prefill chunk's tokens fill the chip), or, for a decode call given no merge
+// workspace, CSA2_ATT_SPLIT workgroups per query splitting the output dimensions.
 hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const int64_t* kv_row0,
                          const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
                          int top_k, const void* swa, int window_fp8, const int64_t* swa_row0, int swa_cap,
                          int64_t swa_rows, int window, const int64_t* replay, int n_heads, float softmax_scale,
-                         float* out, const uint16_t* win_new, hipStream_t stream, hipEvent_t ev_start,
-                         hipEvent_t ev_stop) {
+                         float* out, const uint16_t* win_new, int dec, float* part, uint32_t* ctrl, hipStream_t stream,
+                         hipEvent_t ev_start, hipEvent_t ev_stop) {
+    if (dec && n_q <= kAttSplitMaxQ)
+        return launch_attend_dec(q, codes, scales, kv_row0, kv_len, n_q, max_len, cache_rows, idx, top_k, swa,
+                                 window_fp8, swa_row0, swa_cap, swa_rows, window, replay, n_heads, softmax_scale, out,
+                                 win_new, part, ctrl, stream, ev_start, ev_stop);
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
     const bool fp4 = top_k > 0, win = window > 0 && swa_rows > 0;
     // decode batches (at most kAttSplitMaxQ queries) split each query's output dimensions over

@@ -79,8 +79,11 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
                          const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
                          int top_k, const void* swa, int window_fp8, const int64_t* swa_row0, int swa_cap,
                          int64_t swa_rows, int window, const int64_t* replay, int n_heads, float softmax_scale,
-                         float* out, const uint16_t* win_new, hipStream_t stream, hipEvent_t ev_start = nullptr,
-                         hipEvent_t ev_stop = nullptr);
+                         float* out, const uint16_t* win_new, int dec, float* part, uint32_t* ctrl, hipStream_t stream,
+                         hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+int attend_dec_parts(int top_k, int window);
+int attend_split_max_queries();
+size_t attend_dec_part_bytes();
 hipError_t launch_zero(void* ws, size_t bytes, hipStream_t stream);
 
 namespace {
@@ -138,6 +141,31 @@ IndexWs carve_reindex(void* ws, int n_q, int top_k, int pool_blocks, size_t* use
     w.meta = c.take<Thresh>((size_t)n_q * 2);
     w.keys = c.take<uint32_t>((size_t)n_q * pool_blocks * 8);
     (void)top_k;
+    *used = c.off;
+    return w;
+}
+
+// Attention workspace (decode calls whose entries are split over several workgroups): the
+// common prefix (per-query counters and histograms, so the workspace may be shared with index
+// calls of the same n_q), then one partial per (query, workgroup).  Sized 0 when none is needed.
+struct AttendWs {
+    uint32_t* ctrl;
+    float* part;
+};
+
+bool attend_split(int n_q) { return n_q <= attend_split_max_queries(); }
+
+AttendWs carve_attend(void* ws, int n_q, int top_k, int window, size_t* used) {
+    AttendWs w{nullptr, nullptr};
+    const int parts = attend_dec_parts(top_k, window);
+    if (!attend_split(n_q) || parts <= 1) {
+        *used = 0;
+        return w;
+    }
+    Carve c{static_cast<char*>(ws)};
+    w.ctrl = c.take<uint32_t>(ctrl_bytes(n_q) / 4);
+    (void)c.take<uint32_t>(hist_bytes(n_q) / 4);  // the histogram prefix every workspace has (left zero)
+    w.part = reinterpret_cast<float*>(c.take<uint8_t>((size_t)n_q * parts * attend_dec_part_bytes()));
     *used = c.off;
     return w;
 }
@@ -203,9 +231,10 @@ size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32
             carve_reindex(nullptr, n_q, top_k, pool_blocks, &used);
             return used;
         case CSA2_OP_ATTEND:
-            // top_k = selected slots, pool_blocks = window length; attention needs no workspace
+            // top_k = selected slots, pool_blocks = window length
             if (top_k < 0 || top_k > CSA2_MAX_SELECT || pool_blocks < 0 || pool_blocks > CSA2_MAX_WINDOW) return bad;
-            return 0;
+            carve_attend(nullptr, n_q, top_k, pool_blocks, &used);
+            return used;
         default:
             return bad;
     }
@@ -414,42 +443,47 @@ static int check_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* 
 static int attend_common(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const csa2_seqs& seqs,
                          const int32_t* idx, int32_t top_k, const void* swa, int window_fp8, const int64_t* swa_row0,
                          int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay, int32_t n_heads,
-                         float softmax_scale, float* out, const uint16_t* win_new, void* stream,
-                         void* ev_start = nullptr, void* ev_stop = nullptr) {
+                         float softmax_scale, float* out, const uint16_t* win_new, void* ws, size_t ws_bytes,
+                         void* stream, void* ev_start = nullptr, void* ev_stop = nullptr) {
     const int st = check_attend(q, codes, scales, seqs, idx, top_k, swa, swa_row0, swa_cap, swa_rows, window, n_heads,
                                 softmax_scale, out, win_new);
     if (st || seqs.n_q == 0) return st;
+    size_t need = 0;
+    carve_attend(nullptr, seqs.n_q, top_k, window, &need);
+    if (need > 0 && (ws == nullptr || ws_bytes < need || !aligned16(ws))) return CSA2_ERR_WORKSPACE;
+    const AttendWs aw = carve_attend(ws, seqs.n_q, top_k, window, &need);
     return launch_status(launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
                                        seqs.cache_rows, idx, top_k, swa, window_fp8, swa_row0,
                                        window > 0 ? swa_cap : 1, swa_rows, window, replay, n_heads, softmax_scale,
-                                       out, window > 0 ? win_new : nullptr, static_cast<hipStream_t>(stream),
-                                       static_cast<hipEvent_t>(ev_start), static_cast<hipEvent_t>(ev_stop)));
+                                       out, window > 0 ? win_new : nullptr, 1, aw.part, aw.ctrl,
+                                       static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_start),
+                                       static_cast<hipEvent_t>(ev_stop)));
 }
 
 int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs, const int32_t* idx,
                 int32_t top_k, uint16_t* swa, const int64_t* swa_row0, int32_t swa_cap, int64_t swa_rows,
-                int32_t window, const uint16_t* win_new, int32_t n_heads, float softmax_scale, float* out,
-                void* stream) {
+                int32_t window, const uint16_t* win_new, int32_t n_heads, float softmax_scale, float* out, void* ws,
+                size_t ws_bytes, void* stream) {
     return attend_common(q, codes, scales, seqs, idx, top_k, swa, 0, swa_row0, swa_cap, swa_rows, window, nullptr,
-                         n_heads, softmax_scale, out, win_new, stream);
+                         n_heads, softmax_scale, out, win_new, ws, ws_bytes, stream);
 }
 
 int csa2_attend_timed(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
                       const int32_t* idx, int32_t top_k, uint16_t* swa, const int64_t* swa_row0, int32_t swa_cap,
                       int64_t swa_rows, int32_t window, const uint16_t* win_new, int32_t n_heads, float softmax_scale,
-                      float* out, void* stream, void* start_event, void* stop_event) {
+                      float* out, void* ws, size_t ws_bytes, void* stream, void* start_event, void* stop_event) {
     const int st = refuse_capture(stream, start_event, stop_event);
     if (st) return st;
     return attend_common(q, codes, scales, seqs, idx, top_k, swa, 0, swa_row0, swa_cap, swa_rows, window, nullptr,
-                         n_heads, softmax_scale, out, win_new, stream, start_event, stop_event);
+                         n_heads, softmax_scale, out, win_new, ws, ws_bytes, stream, start_event, stop_event);
 }
 
 int csa2_attend_fp8win(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
                        const int32_t* idx, int32_t top_k, uint8_t* swa, const int64_t* swa_row0, int32_t swa_cap,
                        int64_t swa_rows, int32_t window, const int64_t* replay_start, const uint16_t* win_new,
-                       int32_t n_heads, float softmax_scale, float* out, void* stream) {
+                       int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream) {
     return attend_common(q, codes, scales, seqs, idx, top_k, swa, 1, swa_row0, swa_cap, swa_rows, window,
-                         replay_start, n_heads, softmax_scale, out, win_new, stream);
+                         replay_start, n_heads, softmax_scale, out, win_new, ws, ws_bytes, stream);
 }
 
 int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
@@ -481,9 +515,10 @@ int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx
                                         seqs.max_len_ub, seqs.cache_rows, idx_heads, pool, pool_blocks, top_k, wsp,
                                         idx_out, 1, s);
     if (e != hipSuccess) return CSA2_ERR_LAUNCH;
+    // (no attention workspace here: the decode form that splits the output dimensions)
     e = launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub, seqs.cache_rows,
                       idx_out, top_k, swa, window_fp8, swa_row0, window > 0 ? swa_cap : 1, swa_rows, window,
-                      replay_start, n_heads, softmax_scale, out, wn, s);
+                      replay_start, n_heads, softmax_scale, out, wn, 0, nullptr, nullptr, s);
     return launch_status(e);
 }
 

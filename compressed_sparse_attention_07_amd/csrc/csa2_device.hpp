@@ -18,6 +18,7 @@ constexpr int kHistBits = 11;                 // first radix digit = top 11 key 
 constexpr int kHistBins = 1 << kHistBits;     // 2048
 constexpr int kSortCap = 8192;                // largest candidate set selected in LDS
 constexpr int kMaxSelect = 4096;
+constexpr int kAttSplitMaxQ = 64;           // attention calls up to this many queries are decode-sized
 
 // Per-query self-cleaning counters at the start of the workspace (16 x u32 = 64 B).
 enum CtrlSlot {

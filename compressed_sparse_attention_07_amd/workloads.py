@@ -278,6 +278,7 @@ class Runner:
             C.OP_INDEX_FULL, self.n_q, self.seqs.total_len_ub, self.seqs.max_len_ub, wl.top_k, wl.pool_blocks))
         self.ws_re = C.alloc_workspace(C.csa2_workspace_bytes(
             C.OP_INDEX_REINDEX, self.n_q, 0, 0, wl.top_k, max(wl.pool_blocks, 1))) if "R" in wl.layers else None
+        self.ws_att = C.attend_workspace(self.n_q, wl.top_k, wl.window)
         self.scale = 1.0 / math.sqrt(128.0)
         torch.cuda.synchronize()
 
@@ -362,14 +363,15 @@ class Runner:
             if wl.window_fp8:
                 C.csa2_attend_fp8win(L.q, st.codes, st.scales, self.seqs, idx, L.swa, self.swa_row0, self.swa_cap,
                                      wl.window, self.scale, L.out, replay_start=self.replay, win_new=L.win_new,
-                                     stream=stream)
+                                     ws=self.ws_att, stream=stream)
             elif timing is not None:
                 e0, e1 = ev_pair("attend")
                 C.csa2_attend_timed(L.q, st.codes, st.scales, self.seqs, idx, L.swa, self.swa_row0, self.swa_cap,
-                                    wl.window, self.scale, L.out, e0, e1, win_new=L.win_new, stream=stream)
+                                    wl.window, self.scale, L.out, e0, e1, win_new=L.win_new, ws=self.ws_att,
+                                    stream=stream)
             else:
                 C.csa2_attend(L.q, st.codes, st.scales, self.seqs, idx, L.swa, self.swa_row0, self.swa_cap,
-                              wl.window, self.scale, L.out, win_new=L.win_new, stream=stream)
+                              wl.window, self.scale, L.out, win_new=L.win_new, ws=self.ws_att, stream=stream)
 
     def capture(self):
         """Capture one step per KV copy into HIP graphs (torch.cuda.CUDAGraph on torch's current

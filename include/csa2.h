@@ -28,7 +28,7 @@
  *     skipped, destination rows outside [0, cap_rows) are not written.  Results are
  *     then those of the clamped problem.
  *   - Inputs are finite.  Results are deterministic run to run (no float atomics).
- *   - Workspace: index calls take a caller-owned device workspace of
+ *   - Workspace: index calls and decode-sized attention calls take a caller-owned device workspace of
  *     at least csa2_workspace_bytes(...) bytes.  Every workspace starts with the same
  *     prefix for a given n_q: per-query counters (CSA2_CTRL_BYTES(n_q) bytes) and
  *     per-query histograms.  That prefix must be zero when a call starts and every
@@ -273,12 +273,23 @@ int csa2_index_reindex(const uint16_t* q_idx, const float* w, const uint16_t* k_
  *   swa_rows must be below 2^31.
  * Each entry's vector is both key and value.  One softmax runs over the selected
  * entries and the window entries together (no de-duplication).  A query with
- * nothing to attend gets zeros.  n_q == 0 is a no-op.  No workspace.
+ * nothing to attend gets zeros.  n_q == 0 is a no-op.
+ *   ws, ws_bytes  device workspace of at least
+ *           csa2_workspace_bytes(CSA2_OP_ATTEND, n_q, 0, 0, top_k, window) bytes,
+ *           16-byte aligned, zeroed once (csa2_workspace_init) and left as the call
+ *           leaves it.  Calls of at most 64 queries share each query's entries out
+ *           over several workgroups and merge their softmax partials through it; the
+ *           size is 0 otherwise, and ws may then be NULL.  A workspace smaller than
+ *           required gives CSA2_ERR_WORKSPACE with nothing launched.  Calls that
+ *           overlap in time need separate workspaces.
+ * The result is the same whatever order the workgroups finish in (the partials are
+ * combined in a fixed order).
  */
 int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
                 const int32_t* idx, int32_t top_k, uint16_t* swa, const int64_t* swa_row0,
                 int32_t swa_cap, int64_t swa_rows, int32_t window, const uint16_t* win_new,
-                int32_t n_heads, float softmax_scale, float* out, void* stream);
+                int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                void* stream);
 
 /*
  * csa2_attend_fp8win -- csa2_attend with the pages' window format and replay bound.
@@ -299,7 +310,7 @@ int csa2_attend_fp8win(const uint16_t* q, const uint8_t* codes, const uint8_t* s
                        const int32_t* idx, int32_t top_k, uint8_t* swa, const int64_t* swa_row0,
                        int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay_start,
                        const uint16_t* win_new, int32_t n_heads, float softmax_scale, float* out,
-                       void* stream);
+                       void* ws, size_t ws_bytes, void* stream);
 
 /*
  * csa2_index_reindex_noalloc -- csa2_index_reindex without a caller workspace, for callers that
@@ -329,8 +340,11 @@ int csa2_index_reindex_noalloc(const uint16_t* q_idx, const float* w, const uint
  *   q, codes, scales, swa, swa_row0, swa_cap, swa_rows, window, win_new, n_heads,
  *   softmax_scale, out: as for csa2_attend; window_fp8 = 0: swa holds bf16, 1: E4M3 bytes.
  *   replay_start  device int64 [n_q] or NULL: as for csa2_attend_fp8win (either format).
- * idx_out receives the selection (a Reuse layer that follows attends with it) and out
- * the attention, both equal to those of the separate calls.  With pool_blocks * 8 <=
+ * idx_out receives the selection (a Reuse layer that follows attends with it), equal to
+ * that of csa2_index_reindex, and out the attention over it, within the same tolerance of
+ * the exact result as csa2_attend (its arithmetic is csa2_attend's for calls of more than
+ * 64 queries; for fewer, csa2_attend splits each query's entries over several workgroups
+ * and may round differently).  With pool_blocks * 8 <=
  * 16,384 and top_k <= 1,024 it is one kernel: every workgroup scores one 512-position
  * chunk of a pool, and the last workgroup of each query to finish (an agent-scope
  * ticket counter in the workspace) selects and attends; larger sizes take the separate
@@ -383,7 +397,7 @@ int csa2_window_append(const uint16_t* x, int64_t n_tok, const int64_t* dst_rows
 /*
  * Workspace bytes for one call of `op` (CSA2_OP_*) with these sizes; SIZE_MAX if the
  * sizes are out of range, 0 if the call needs no workspace.  For CSA2_OP_ATTEND pass the
- * window length in `pool_blocks` (attention needs no workspace: it returns 0); for
+ * window length in `pool_blocks` (0 for calls of more than 64 queries); for
  * CSA2_OP_INDEX_REINDEX (also csa2_reindex_attend) total_len_ub and max_len_ub are unused.
  */
 size_t csa2_workspace_bytes(int32_t op, int32_t n_q, int64_t total_len_ub, int32_t max_len_ub,

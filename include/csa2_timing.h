@@ -49,8 +49,8 @@ int csa2_index_reindex_timed(const uint16_t* q_idx, const float* w, const void* 
 int csa2_attend_timed(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs,
                       const int32_t* idx, int32_t top_k, uint16_t* swa, const int64_t* swa_row0,
                       int32_t swa_cap, int64_t swa_rows, int32_t window, const uint16_t* win_new,
-                      int32_t n_heads, float softmax_scale, float* out, void* stream, void* start_event,
-                      void* stop_event);
+                      int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes,
+                      void* stream, void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

@@ -147,7 +147,7 @@ class AttendCase:
         out = torch.full((n_q, self.n_heads, 128), float("nan"), dtype=torch.float32, device=DEV)
         idx = torch.from_numpy(np.ascontiguousarray(idx_np.astype(np.int32))).to(DEV)
         C.csa2_attend(self.q_dev, self.codes, self.scales, self.seqs, idx, self.swa_dev, self.swa_row0_dev,
-                      self.swa_cap, self.window, scale, out)
+                      self.swa_cap, self.window, scale, out, ws=ws)
         torch.cuda.synchronize()
         return out.cpu().numpy(), ws
 

@@ -89,11 +89,17 @@ def test_reindex_and_attend_validation():
     assert L.csa2_index_reindex(FAKE, FAKE, FAKE, seqs(), 4, None, 2048, 8, 512, FAKE, FAKE, need_r, None) == C.ERR_NULL
     assert L.csa2_index_reindex(FAKE, FAKE, FAKE, seqs(), 4, FAKE, 2048, 8, 512, FAKE, FAKE, need_r - 1,
                                 None) == C.ERR_WORKSPACE
-    assert C.csa2_workspace_bytes(C.OP_ATTEND, 2, 0, 0, 512, 128) == 0     # attention needs none
+    need_a = C.csa2_workspace_bytes(C.OP_ATTEND, 2, 0, 0, 512, 128)
+    assert need_a >= 2 * 5 * (16 * 130 * 4)     # five partials of 16 heads x (128 + max + sum) per query
 
-    def att(top_k=512, window=128, cap=128, heads=16, scale=0.1, idx=FAKE, swa=FAKE, swa_rows=1000, win_new=None):
+    def att(top_k=512, window=128, cap=128, heads=16, scale=0.1, idx=FAKE, swa=FAKE, swa_rows=1000, win_new=None,
+            ws=FAKE, ws_bytes=None):
         return L.csa2_attend(FAKE, FAKE, FAKE, seqs(), idx, top_k, swa, FAKE, cap, swa_rows, window, win_new, heads,
-                             ctypes.c_float(scale), FAKE, None)
+                             ctypes.c_float(scale), FAKE, ws, need_a if ws_bytes is None else ws_bytes, None)
+
+    assert att(ws=None) == C.ERR_WORKSPACE
+    assert att(ws_bytes=need_a - 1) == C.ERR_WORKSPACE
+    assert att(ws=ctypes.c_void_p(0x10008)) == C.ERR_WORKSPACE   # 16-byte aligned
 
     assert att(heads=17) == C.ERR_SHAPE
     assert att(cap=100) == C.ERR_SHAPE          # the window ring must hold the window
@@ -161,6 +167,9 @@ def test_workspace_sizes():
     assert C.csa2_workspace_bytes(C.OP_INDEX_FULL, 8, 100, 10, 0, 0) == C.SIZE_MAX
     r = C.csa2_workspace_bytes(C.OP_INDEX_REINDEX, 8, 0, 0, 512, 2048)
     assert r >= 8 * 2048 * 8 * 4          # a 4 B key per pool position
-    assert C.csa2_workspace_bytes(C.OP_ATTEND, 8, 0, 0, 512, 128) == 0
+    a8 = C.csa2_workspace_bytes(C.OP_ATTEND, 8, 0, 0, 512, 128)
+    assert a8 >= 8 * 5 * (16 * 130 * 4) and a8 < C.csa2_workspace_bytes(C.OP_ATTEND, 8, 0, 0, 1024, 128)
+    assert C.csa2_workspace_bytes(C.OP_ATTEND, 65, 0, 0, 512, 128) == 0    # more than 64 queries: no split
+    assert C.csa2_workspace_bytes(C.OP_ATTEND, 8, 0, 0, 64, 0) == 0        # one workgroup covers a query
     assert C.csa2_workspace_bytes(C.OP_ATTEND, 8, 0, 0, 512, 5000) == C.SIZE_MAX
     assert C.csa2_workspace_bytes(99, 8, 0, 0, 1, 1) == C.SIZE_MAX

@@ -185,21 +185,23 @@ def test_workload7_mxfp4_keys_fp8_window_with_replay():
 
 @pytest.mark.parametrize("wid", [1, 7])
 def test_fused_reindex_layers_equal_separate_calls(wid):
-    # the fused Reindex selection + attention gives the separate calls' indices and outputs
-    # exactly (the same arithmetic in the same order); the separate calls are checked against
-    # the oracle by the workload tests above
-    outs = []
+    # the fused Reindex selection + attention gives the separate calls' indices exactly; its
+    # attention (one workgroup per query, where the separate decode call splits each query's
+    # entries over workgroups, so the two may round differently) is checked against the oracle
+    # on strided queries of every layer
+    idxs = []
     for fused in (True, False):
-        r = W.Runner(W.WORKLOADS[wid], fused_reindex=fused)
+        r = W.Runner(W.WORKLOADS[wid], fused_reindex=fused, keep_host=fused)
         r.step()
         torch.cuda.synchronize()
-        outs.append([(L.idx.cpu().numpy() if L.idx is not None else None, L.out.cpu().numpy()) for L in r.layers])
+        idxs.append([L.idx.cpu().numpy() if L.idx is not None else None for L in r.layers])
+        if fused:
+            _check_step(r, [], _strided(r.n_q, 8), rows_sample=200)
         del r
         torch.cuda.empty_cache()
-    for l, ((ia, oa), (ib, ob)) in enumerate(zip(*outs)):
+    for l, (ia, ib) in enumerate(zip(*idxs)):
         if ia is not None:
             assert np.array_equal(ia, ib), l
-        assert np.array_equal(oa, ob), l
 
 
 def test_workload3_prefill_4096_on_128k():
