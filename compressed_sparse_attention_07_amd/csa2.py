@@ -95,7 +95,7 @@ def lib() -> ctypes.CDLL:
         L.csa2_attend_fp8win.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, vp, i32, f32, vp,
                                          vp, sz, vp]
         L.csa2_reindex_attend.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp,
-                                          i32, i64, i32, vp, vp, i32, f32, vp, vp, sz, vp]
+                                          i32, i64, i32, vp, vp, i32, f32, vp, vp, sz, vp, sz, vp]
         L.csa2_token_append.argtypes = [vp, vp, i64, vp, vp, vp, vp, vp, i64, vp]
         L.csa2_index_reindex_timed.argtypes = [vp, vp, vp, vp, SeqsC, i32, vp, i32, i32, i32, vp, vp, sz, vp, vp, vp,
                                                vp, vp]
@@ -274,15 +274,17 @@ def csa2_attend_fp8win(q, codes, scales, seqs: Seqs, idx, swa8, swa_row0, swa_ca
 
 def csa2_reindex_attend(q_idx, w, k_idx, k_scales, seqs: Seqs, pool, top_k: int, idx_out, q, codes, scales, swa,
                         swa_row0, swa_cap: int, window: int, softmax_scale: float, out, ws, window_fp8: bool = False,
-                        replay_start=None, win_new=None, block: int = BLOCK, stream=None) -> None:
-    """One Reindex layer in one kernel: selection inside the pool (bf16 keys, or MXFP4 keys when
-    k_scales is given) and the attention over it; idx_out and out as from the separate calls."""
+                        replay_start=None, win_new=None, att_ws=None, block: int = BLOCK, stream=None) -> None:
+    """One Reindex layer in one call: selection inside the pool (bf16 keys, or MXFP4 keys when
+    k_scales is given) and the attention over it.  att_ws: the attention workspace (None: a
+    fresh one)."""
     swa_rows = swa.shape[0] if swa is not None else 0
+    att_ws = _attend_ws(att_ws, q, top_k, window)
     _check("csa2_reindex_attend", lib().csa2_reindex_attend(
         _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_scales), seqs.c(), q_idx.shape[1], _ptr(pool), pool.shape[1], block,
         top_k, _ptr(idx_out), _ptr(q), _ptr(codes), _ptr(scales), _ptr(swa), 1 if window_fp8 else 0, _ptr(swa_row0),
         swa_cap, swa_rows, window, _ptr(replay_start), _ptr(win_new), q.shape[1], ctypes.c_float(softmax_scale),
-        _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+        _ptr(out), _ptr(ws), ws.numel(), _ptr(att_ws), att_ws.numel(), _stream(stream)))
 
 
 def csa2_token_append(x, dst_rows, codes, scales, k_new=None, k_idx=None, k_scales=None, stream=None) -> None:

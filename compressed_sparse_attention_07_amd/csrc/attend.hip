@@ -41,55 +41,14 @@
 #include "attend_common.hpp"
 #include "csa2_device.hpp"
 #include "pack_common.hpp"
-#include "reindex_score.hpp"
-#include "reindex_select.hpp"
 
 namespace csa2 {
 
 constexpr int kAttWaves = 8;
-#ifndef CSA2_ATT_SPLIT
-#define CSA2_ATT_SPLIT 4   // workgroups per decode query (output dimensions split): 1, 2, 4 or 8
-#endif
 constexpr int kAttNT = kAttWaves * 64;
 constexpr int kRB = 4;                       // FP4 blocks per wave per round
-constexpr int kRoundFp4 = kAttWaves * kRB;   // FP4 blocks per round (512 entries)
-constexpr int kRoundWin = kAttWaves;         // window blocks per round (128 entries)
 static_assert(kNH * kOStride * 4 <= kTileB, "a wave's merge rows fit in its tile");
 
-
-// kFp4: top_k > 0 (the FP4 cache is read); kWin: window > 0 and the window store has rows.
-// Both are fixed per launch so that every gather below is unconditional (clamped addresses,
-// masked results): loads under branches make the compiler wait on some of them early.
-// kW8: the window store holds E4M3 bytes ([Article] section XI keeps the recent-window cache
-// in FP8); they are converted to f16 exactly and take the FP4 entries' f16 path.
-// replay (may be NULL): per-query replay start s; the window then holds only positions >= s
-// ([Article] section XII, SWA Bounded Replay).
-// win_new (may be NULL): the step's own window vector per query (bf16 [n_q, 128]): every layer
-// computes its own window entry for the new token ([Article] section VI).  The kernel attends it
-// as position N - 1 of the window straight from win_new (the store's row for that position is
-// never read) and writes it to that row (converted to E4M3 for an FP8 store) once everything
-// else is done.
-struct AttendArgs {
-    const uint16_t* q;
-    const uint8_t* codes;
-    const uint8_t* scales;
-    const int64_t* kv_row0;
-    const int32_t* kv_len;
-    int32_t max_len;
-    int64_t cache_rows;
-    const int32_t* idx;  // [n_q, top_k] (the standalone kernel reads it; the fused one has it in LDS)
-    int top_k;
-    const void* swa;
-    const int64_t* swa_row0;
-    int swa_cap;
-    int64_t swa_rows;
-    int window;
-    const int64_t* replay;
-    int n_heads;
-    float scale_log2;
-    float* out;
-    const uint16_t* win_new;
-};
 
 // LDS of one attention workgroup: per-wave tiles (P.V operands, then the merge rows) and the
 // per-wave softmax statistics.
@@ -99,27 +58,22 @@ struct AttendLds {
     float (*l)[kNH];
 };
 
-// The attention of query i (one workgroup of kAttNT threads); idx_row = the query's top_k
-// selected positions (global memory or LDS).  SPLIT > 1: the query's output dimensions are
-// split over SPLIT workgroups and this one, number `part`, produces dimensions
-// [part * 128 / SPLIT, (part + 1) * 128 / SPLIT): every workgroup forms all logits and the same
-// softmax (the same arithmetic in the same order), but P.V, its LDS transposes and the wave merge
-// cover only its share, so no partial result crosses workgroups.
-template <bool kFp4, bool kWin, bool kW8, int SPLIT = 1>
+// The attention of query i (one workgroup of WAVES waves; wave w takes RB FP4 blocks and one
+// window block of a round); idx_row = the query's top_k selected positions (global memory or
+// LDS); pre = its first level of loads.
+template <bool kFp4, bool kWin, bool kW8, int WAVES = kAttWaves, int RB = kRB>
 __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const int32_t* idx_row, const AttendLds& lds,
-                                             int part = 0) {
-    constexpr int NDB = 8 / SPLIT;  // 16-dimension output blocks of this workgroup
-    static_assert(SPLIT == 1 || SPLIT == 2 || SPLIT == 4 || SPLIT == 8, "split");
-    const uint16_t* __restrict__ q = a.q;
+                                             AttendPre pre) {
+    constexpr int NDB = 8;  // 16-dimension output blocks
+    constexpr int kRoundFp4 = WAVES * RB;  // FP4 blocks per round
+    constexpr int kRoundWin = WAVES;       // window blocks per round
+    static_assert(RB % 2 == 0, "FP4 blocks go to P.V in pairs");
     const uint8_t* __restrict__ codes = a.codes;
     const uint8_t* __restrict__ scales = a.scales;
-    const int64_t* __restrict__ kv_row0 = a.kv_row0;
-    const int32_t* __restrict__ kv_len = a.kv_len;
     int32_t max_len = a.max_len;     // (made opaque below, after the first level of loads)
     int64_t cache_rows = a.cache_rows;
     const int top_k = a.top_k;
     const void* __restrict__ swa = a.swa;
-    const int64_t* __restrict__ swa_row0 = a.swa_row0;
     const int swa_cap = a.swa_cap;
     const int64_t swa_rows = a.swa_rows;
     const int window = a.window;
@@ -135,46 +89,30 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
     const int l = t & 63;
     const int g = l >> 4;   // lane group
     const int r = l & 15;   // row / column within the 16
-    // ---- first level of loads: everything that needs only the query number goes out at once
-    // (the length and rows, the round-0 indices, the query), so the kernel pays one memory
-    // latency before the gathers rather than one per dependent load.  The per-query values
-    // go first, as vector loads (counted in order: waiting for them leaves the index and query
-    // loads in flight); absent arrays are replaced by a valid one whose value is unused. ----
-    int32_t len_raw = vload_i32(kv_len, i);
-    int64_t row0_raw = vload_i64(kv_row0, i);
-    int64_t wrow0_raw = vload_i64(kWin ? swa_row0 : kv_row0, i);
-    int64_t replay_raw = vload_i64(replay != nullptr ? replay : kv_row0, i);  // replay[i] when given
+    int32_t len_raw = pre.len_raw;
+    int64_t row0_raw = pre.row0_raw, wrow0_raw = pre.wrow0_raw, replay_raw = pre.replay_raw;
+    uint32_t nwv = pre.nwv;
     const uint16_t* __restrict__ win_new = a.win_new;
     const bool has_new = kWin && win_new != nullptr;
-    // channels 2l, 2l + 1 of the query's new window vector (the E4M3 exchange and the final store)
-    uint32_t nwv = has_new ? *reinterpret_cast<const uint32_t*>(win_new + (int64_t)i * kD + 2 * l) : 0u;
-    int pos[kRB];     // selected positions of this lane's entry in each FP4 block (-1: none)
+    int pos[RB];     // selected positions of this lane's entry in each FP4 block (-1: none)
     // indices of one round (lanes past top_k read entry 0 and are masked; a length of 0 masks
     // every position later)
     auto issue_idx = [&](int R) {
-        const int b0 = R * kRoundFp4 + wave * kRB;
+        const int b0 = R * kRoundFp4 + wave * RB;
 #pragma unroll
-        for (int j = 0; j < kRB; ++j) {
+        for (int j = 0; j < RB; ++j) {
             const int e = 16 * (b0 + j) + r;
             const int v = kFp4 ? idx_row[e < top_k ? e : 0] : -1;
             pos[j] = e < top_k ? v : -1;
         }
     };
     issue_idx(0);
-    // Q^T fragments of head r, channels 32g + 8s .. + 7: bf16 as given (loaded now), and f16
-    // scaled by 2^qe (converted while round 0's gathers are in flight).  Rows r >= n_heads
-    // repeat head 0: every head's softmax is its own and only heads < n_heads are written.
+    // Q^T fragments: bf16 as given (pre), and f16 scaled by 2^qe (converted while round 0's
+    // gathers are in flight)
     u32x4 qb[4], qh[4];
     float cf4 = 0.f;  // logit multiplier of the f16 contraction: scale_log2 * 2^-qe
-    {
-        const uint4* qp =
-            reinterpret_cast<const uint4*>(q + ((int64_t)i * n_heads + (r < n_heads ? r : 0)) * kD + 32 * g);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const uint4 v = qp[s];
-            qb[s] = u32x4{v.x, v.y, v.z, v.w};
-        }
-    }
+    for (int s = 0; s < 4; ++s) qb[s] = pre.qb[s];
     __builtin_amdgcn_sched_barrier(0);
     // an empty statement that takes and returns the four per-query values: every use of them
     // comes after it, so no wait for them is placed in front of the index and query loads
@@ -260,8 +198,6 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
     f32x4 o[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int db0 = part * NDB;                                       // first output block
-    const bool g_in = 2 * g + 1 >= db0 && 2 * g < db0 + NDB;          // this lane's channels (blocks 2g, 2g + 1) meet the share
     uint8_t* tile = lds.tile + wave * kTileB;
     // tile addresses: row-major store of this lane's entry r; transposed read of rows 4g + r/4
     const int st_off = r * kRowB + 64 * g;
@@ -272,14 +208,14 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
             issue_idx(R);
             issue_win(R);
         }
-        const int b0 = R * kRoundFp4 + wave * kRB;
+        const int b0 = R * kRoundFp4 + wave * RB;
         const int wb = R * kRoundWin + wave;
         const bool wblk = wb < nbw;
-        uint4 cw[kRB];
-        uint32_t sw[kRB];
-        uint32_t vb[kRB];  // validity of the 16 entries of each block (bit e)
+        uint4 cw[RB];
+        uint32_t sw[RB];
+        uint32_t vb[RB];  // validity of the 16 entries of each block (bit e)
 #pragma unroll
-        for (int j = 0; j < kRB; ++j) {
+        for (int j = 0; j < RB; ++j) {
             // inside the loop n > 0, so row0 is a cache row: absent entries read it and are masked
             const bool ok = pos[j] >= 0 && pos[j] < n;
             const int64_t cr = row0 + (ok ? pos[j] : 0);
@@ -312,10 +248,10 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
         }
 
         // ---- logits of the whole round ----
-        u32x4 kf[kRB][4];
-        f32x4 sa[kRB];
+        u32x4 kf[RB][4];
+        f32x4 sa[RB];
 #pragma unroll
-        for (int j = 0; j < kRB; ++j) {
+        for (int j = 0; j < RB; ++j) {
             dequant_f16(cw[j], sw[j], kf[j]);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -349,15 +285,15 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
                                                               __builtin_bit_cast(bf16x8, qb[s]), swc, 0, 0, 0);
         }
         // logits of head r for entries 4g + ii of each block (log2 units), masked
-        float x[kRB + 1][4];
+        float x[RB + 1][4];
         float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j <= kRB; ++j) {
+        for (int j = 0; j <= RB; ++j) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-                const uint32_t bits = j < kRB ? vb[j] : vbw;
+                const uint32_t bits = j < RB ? vb[j] : vbw;
                 const bool ok = (bits >> (4 * g + ii)) & 1u;
-                const float v = j < kRB ? sa[j][ii] * cf4 : swc[ii] * (kW8 ? cf4 : scale_log2);
+                const float v = j < RB ? sa[j][ii] * cf4 : swc[ii] * (kW8 ? cf4 : scale_log2);
                 x[j][ii] = ok ? v : -INFINITY;
                 mx = fmaxf(mx, x[j][ii]);
             }
@@ -374,17 +310,17 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
         }
         m_run = m_new;
         // probabilities: f16 for FP4 (and E4M3 window) entries, bf16 hi + lo for bf16 window entries
-        uint32_t ph[kRB][2], pwh[2], pwl[2];
+        uint32_t ph[RB][2], pwh[2], pwl[2];
         float psum = 0.f;
 #pragma unroll
-        for (int j = 0; j <= kRB; ++j) {
+        for (int j = 0; j <= RB; ++j) {
             float p[4];
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 p[ii] = __builtin_amdgcn_exp2f(x[j][ii] - m_new);  // masked: exp2(-inf) = 0
                 psum += p[ii];
             }
-            if (j < kRB) {
+            if (j < RB) {
                 ph[j][0] = f16pair(p[0], p[1]);
                 ph[j][1] = f16pair(p[2], p[3]);
             } else if (kW8) {
@@ -408,21 +344,19 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
 
         // ---- P.V over FP4 block pairs (K = 32 entries: 16 of each block) ----
 #pragma unroll
-        for (int pp = 0; pp < kRB / 2; ++pp) {
+        for (int pp = 0; pp < RB / 2; ++pp) {
             if (b0 + 2 * pp >= nb4) break;  // wave-uniform
-            if (g_in) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    *reinterpret_cast<u32x4*>(tile + st_off + 16 * s) = kf[2 * pp][s];
-                    *reinterpret_cast<u32x4*>(tile + 16 * kRowB + st_off + 16 * s) = kf[2 * pp + 1][s];
-                }
+            for (int s = 0; s < 4; ++s) {
+                *reinterpret_cast<u32x4*>(tile + st_off + 16 * s) = kf[2 * pp][s];
+                *reinterpret_cast<u32x4*>(tile + 16 * kRowB + st_off + 16 * s) = kf[2 * pp + 1][s];
             }
             wave_lds_sync();
             const u32x4 pf = {ph[2 * pp][0], ph[2 * pp][1], ph[2 * pp + 1][0], ph[2 * pp + 1][1]};
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const s16x4 a0 = lds_tr16(tile + tr_off + 32 * (db0 + db));
-                const s16x4 a1 = lds_tr16(tile + 16 * kRowB + tr_off + 32 * (db0 + db));
+                const s16x4 a0 = lds_tr16(tile + tr_off + 32 * db);
+                const s16x4 a1 = lds_tr16(tile + 16 * kRowB + tr_off + 32 * db);
                 const u32x2 u0 = __builtin_bit_cast(u32x2, a0), u1 = __builtin_bit_cast(u32x2, a1);
                 const u32x4 af = {u0[0], u0[1], u1[0], u1[1]};
                 o[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, af),
@@ -432,15 +366,13 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
         }
         // ---- P.V over the window block (K = 16 entries) ----
         if (wblk) {
-            if (g_in) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) *reinterpret_cast<u32x4*>(tile + st_off + 16 * s) = wf[s];
-            }
+            for (int s = 0; s < 4; ++s) *reinterpret_cast<u32x4*>(tile + st_off + 16 * s) = wf[s];
             wave_lds_sync();
             const u32x2 hv2 = {pwh[0], pwh[1]}, lv2 = {pwl[0], pwl[1]};
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const s16x4 a = lds_tr16(tile + tr_off + 32 * (db0 + db));
+                const s16x4 a = lds_tr16(tile + tr_off + 32 * db);
                 if constexpr (kW8) {
                     o[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
                                                                   __builtin_bit_cast(f16x4, hv2), o[db], 0, 0, 0);
@@ -461,35 +393,35 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
         s_l[wave][r] = l_run;
     }
     {
-        // this wave's O^T (dims 16 (db0 + db) + 4g + ii of head r) -> rows [head][dim - 16 db0] of its tile
+        // this wave's O^T (dims 16 db + 4g + ii of head r) -> rows [head][dim] of its tile
         float* ob = reinterpret_cast<float*>(tile);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             *reinterpret_cast<f32x4*>(&ob[r * kOStride + 16 * db + 4 * g]) = o[db];
     }
     __syncthreads();
-    constexpr int kTpH = 32 / SPLIT;  // threads per head, four dimensions each
+    constexpr int kTpH = 32;          // threads per head, four dimensions each
     const int h = t / kTpH;
-    const int d0 = 4 * (t % kTpH);    // within the share
+    const int d0 = 4 * (t % kTpH);
     if (h < n_heads && t < kNH * kTpH) {
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kAttWaves; ++w) M = fmaxf(M, s_m[w][h]);
+        for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][h]);
         float L = 0.f;
         f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < kAttWaves; ++w) {
+        for (int w = 0; w < WAVES; ++w) {
             const float f = (s_m[w][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
             L = fmaf(s_l[w][h], f, L);
             O += f * *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds.tile + w * kTileB) +
                                                     h * kOStride + d0);
         }
         const f32x4 res = L > 0.f ? O / L : f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(out + ((int64_t)i * n_heads + h) * kD + 16 * db0 + d0) = res;
+        *reinterpret_cast<f32x4*>(out + ((int64_t)i * n_heads + h) * kD + d0) = res;
     }
     // the new window entry into its store row, after every read of the store by this query
     // (wave 0, two channels per lane); whether or not the replay bound lets it be attended
-    if (has_new && wave == 0 && part == 0 && n > 0) {
+    if (has_new && wave == 0 && n > 0) {
         const int64_t wr = wrow0_raw + ((n - 1) % swa_cap);
         if (wr >= 0 && wr < swa_rows) {
             if constexpr (kW8)
@@ -504,7 +436,7 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
 // The arguments one by one (not the AttendArgs block), those of the first level of loads first:
 // the leading ones are preloaded into SGPRs at launch, so those loads need no scalar load of
 // the argument block before them.
-template <bool kFp4, bool kWin, bool kW8, int SPLIT>
+template <bool kFp4, bool kWin, bool kW8>
 __global__ __launch_bounds__(kAttNT) void k_attend(const int32_t* kv_len, const int64_t* kv_row0,
                                                    const int64_t* swa_row0, const int64_t* replay, const int32_t* idx,
                                                    const uint16_t* q, int top_k, int n_heads, int32_t max_len,
@@ -516,86 +448,10 @@ __global__ __launch_bounds__(kAttNT) void k_attend(const int32_t* kv_len, const 
     const AttendArgs a{q,        codes,   scales,   kv_row0, kv_len, max_len, cache_rows, idx,   top_k,
                        swa,      swa_row0, swa_cap, swa_rows, window, replay, n_heads,   scale_log2, out,
                        win_new};
-    // workgroups i and i + n_q * k serve query i (parts k); with n_q a multiple of 8 they run on
-    // one XCD (workgroup b runs on XCD b mod 8), so a query's gathers are shared in its L2
-    const int n_q = (int)gridDim.x / SPLIT;
-    const int i = (int)blockIdx.x % n_q, part = (int)blockIdx.x / n_q;
-    attend_query<kFp4, kWin, kW8, SPLIT>(i, a, idx + (int64_t)i * top_k, AttendLds{s_tile, s_m, s_l}, part);
+    const int i = (int)blockIdx.x;
+    attend_query<kFp4, kWin, kW8>(i, a, idx + (int64_t)i * top_k, AttendLds{s_tile, s_m, s_l}, attend_pre<kWin>(i, a));
 }
 
-// One Reindex layer in one kernel ([Article] sections VIII-IX: the layer scores its own indexer
-// query against the Full layer's keys inside the shared pool and takes its own Top-K there;
-// section VI: it then attends its selection plus its window).
-//   Every workgroup scores one kReindexTile chunk of one query's pool (as k_idx_reindex_score,
-//   with 8 waves), writes the keys with agent-scope stores and adds its first-digit counts to
-//   the query's histogram; once its stores and atomics have completed it takes a ticket from
-//   the query's counter.  The workgroup holding the last ticket of its query is the only one
-//   that goes on: it resets the counter, selects the query's Top-K from the keys and the
-//   histogram (agent-scope loads: the other chunks were scored on other XCDs in this same
-//   kernel), keeps the selection in LDS, writes it to idx_out for the Reuse layers that follow,
-//   and runs the attention over it.  No workgroup waits for another: the last to finish
-//   does the rest, so the kernel cannot stall on scheduling order.
-// The selection is that of k_idx_reindex_select and the attention that of k_attend, so the
-// results equal the separate kernels' bit for bit.
-constexpr int kLayerMaxTopK = 1024;  // selected entries kept in LDS
-
-template <int HI, bool MX, int EPT, bool kWin, bool kW8>
-__global__ __launch_bounds__(kAttNT) void k_reindex_layer(const int32_t* __restrict__ pool,
-                                                          const uint16_t* __restrict__ q_idx,
-                                                          const float* __restrict__ w, const int64_t* __restrict__ kv_row0,
-                                                          const int32_t* __restrict__ kv_len, int pool_blocks,
-                                                          int idx_heads, int32_t max_len, const void* __restrict__ k_idx,
-                                                          const uint8_t* __restrict__ k_sc, int64_t cache_rows, IndexWs ws,
-                                                          int32_t* __restrict__ idx_out, AttendArgs a) {
-    // s_area: the scoring histogram, then the selection's two radix histograms, then the
-    // attention's per-wave tiles
-    __shared__ __align__(16) uint8_t s_area[kAttWaves * kTileB];
-    __shared__ int32_t s_idx[kLayerMaxTopK];
-    __shared__ int s_scan[kAttNT / kWave];
-    __shared__ uint32_t s_or[2];
-    __shared__ Thresh sh_th;
-    __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
-    __shared__ uint32_t s_ticket;
-    static_assert(2 * kHistBins * 4 <= kAttWaves * kTileB, "selection histograms fit the tile area");
-
-    const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
-    int i, chunk;
-    reindex_item((int)blockIdx.x, chunks, i, chunk);
-    const int t = threadIdx.x;
-    const int n = eff_len(kv_len, kv_row0, i, max_len, cache_rows);
-    const int64_t row0 = n > 0 ? kv_row0[i] : 0;
-    const int n_elem = pool_blocks * 8;
-    uint32_t* sh_hist = reinterpret_cast<uint32_t*>(s_area);
-    for (int b = t; b < kHistBins; b += kAttNT) sh_hist[b] = 0u;
-    QFrag qf;
-    load_qfrag(qf, q_idx + (int64_t)i * idx_heads * 64, w + (int64_t)i * idx_heads, idx_heads, t & (kWave - 1));
-    __syncthreads();
-    reindex_score_chunks<HI, MX, kAttWaves, true>(chunk, chunk + 1, n, row0, pool + (int64_t)i * pool_blocks,
-                                                  pool_blocks, qf, k_idx, k_sc, ws.keys + (int64_t)i * n_elem, sh_hist);
-    __syncthreads();
-    uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
-    for (int b = t; b < kHistBins; b += kAttNT) {
-        const uint32_t h = sh_hist[b];
-        if (h) atomicAdd(&gh[b], h);
-    }
-    // every key store and histogram atomic of this thread has completed (gfx9 counts stores and
-    // atomics in vmcnt); the barrier then covers the whole workgroup before the ticket
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    uint32_t* ctr = ws.ctrl + (int64_t)i * kCtlSlots + kCtlScoreDone;
-    if (t == 0) s_ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (s_ticket != (uint32_t)(chunks - 1)) return;  // uniform across the workgroup
-    if (t == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("" ::: "memory");  // nothing below moves above the ticket
-
-    reindex_select_query<kAttNT, EPT, true>(i, pool, pool_blocks, a.top_k, ws, idx_out, s_idx,
-                                            reinterpret_cast<uint32_t(*)[kHistBins]>(s_area), s_scan, s_or, &sh_th);
-    __syncthreads();  // the selection is in s_idx; the histogram area is free for the tiles
-    attend_query<true, kWin, kW8>(i, a, s_idx, AttendLds{s_area, s_m, s_l});
-}
-
-// window_fp8: the window store holds E4M3 bytes; replay: per-query replay starts or NULL.
 hipError_t launch_attend_dec(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const int64_t* kv_row0,
                              const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
                              int top_k, const void* swa, int window_fp8, const int64_t* swa_row0, int swa_cap,
@@ -603,39 +459,31 @@ hipError_t launch_attend_dec(const uint16_t* q, const uint8_t* codes, const uint
                              float* out, const uint16_t* win_new, float* part, uint32_t* ctrl, hipStream_t stream,
                              hipEvent_t ev_start, hipEvent_t ev_stop);
 
-// dec: a decode-sized call (at most kAttSplitMaxQ queries) whose entries are split over
-// workgroups (csrc/attend_decode.hip; part / ctrl: its merge workspace); otherwise one workgroup
-// per query (a prefill chunk's tokens fill the chip), or, for a decode call given no merge
-// workspace, CSA2_ATT_SPLIT workgroups per query splitting the output dimensions.
+// window_fp8: the window store holds E4M3 bytes; replay: per-query replay starts or NULL.
+// Decode-sized calls (at most kAttSplitMaxQ queries) split each query's entries over workgroups
+// (k_attend_dec, csrc/attend_decode.hip; part / ctrl: its merge workspace); larger calls (a
+// prefill chunk's tokens, which fill the chip by themselves) take one workgroup per query.
 hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const int64_t* kv_row0,
                          const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
                          int top_k, const void* swa, int window_fp8, const int64_t* swa_row0, int swa_cap,
                          int64_t swa_rows, int window, const int64_t* replay, int n_heads, float softmax_scale,
-                         float* out, const uint16_t* win_new, int dec, float* part, uint32_t* ctrl, hipStream_t stream,
+                         float* out, const uint16_t* win_new, float* part, uint32_t* ctrl, hipStream_t stream,
                          hipEvent_t ev_start, hipEvent_t ev_stop) {
-    if (dec && n_q <= kAttSplitMaxQ)
+    if (n_q <= kAttSplitMaxQ)
         return launch_attend_dec(q, codes, scales, kv_row0, kv_len, n_q, max_len, cache_rows, idx, top_k, swa,
                                  window_fp8, swa_row0, swa_cap, swa_rows, window, replay, n_heads, softmax_scale, out,
                                  win_new, part, ctrl, stream, ev_start, ev_stop);
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
     const bool fp4 = top_k > 0, win = window > 0 && swa_rows > 0;
-    // decode batches (at most kAttSplitMaxQ queries) split each query's output dimensions over
-    // CSA2_ATT_SPLIT workgroups; larger calls (a prefill chunk's tokens) already fill the chip
-    const int split = n_q <= kAttSplitMaxQ ? CSA2_ATT_SPLIT : 1;
-    using K = decltype(&k_attend<true, true, false, 1>);
-    auto pick = [&](auto sp) -> K {
-        constexpr int S = decltype(sp)::value;
-        if (window_fp8)
-            return fp4 ? (win ? k_attend<true, true, true, S> : k_attend<true, false, true, S>)
-                       : (win ? k_attend<false, true, true, S> : k_attend<false, false, true, S>);
-        return fp4 ? (win ? k_attend<true, true, false, S> : k_attend<true, false, false, S>)
-                   : (win ? k_attend<false, true, false, S> : k_attend<false, false, false, S>);
-    };
-    const K kern = split == 8   ? pick(std::integral_constant<int, 8>{})
-                   : split == 4 ? pick(std::integral_constant<int, 4>{})
-                   : split == 2 ? pick(std::integral_constant<int, 2>{})
-                                : pick(std::integral_constant<int, 1>{});
-    const dim3 grid((unsigned)(n_q * split));
+    using K = decltype(&k_attend<true, true, false>);
+    K kern;
+    if (window_fp8)
+        kern = fp4 ? (win ? k_attend<true, true, true> : k_attend<true, false, true>)
+                   : (win ? k_attend<false, true, true> : k_attend<false, false, true>);
+    else
+        kern = fp4 ? (win ? k_attend<true, true, false> : k_attend<true, false, false>)
+                   : (win ? k_attend<false, true, false> : k_attend<false, false, false>);
+    const dim3 grid((unsigned)n_q);
     // ev_start / ev_stop (may be null): the kernel's own start and end, recorded by its launch
     if (ev_start != nullptr || ev_stop != nullptr)
         hipExtLaunchKernelGGL(kern, grid, dim3(kAttNT), 0, stream, ev_start, ev_stop, 0, kv_len, kv_row0, swa_row0,
@@ -645,46 +493,6 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
         hipLaunchKernelGGL(kern, grid, dim3(kAttNT), 0, stream, kv_len, kv_row0, swa_row0, replay, idx, q, top_k,
                            n_heads, max_len, cache_rows, codes, scales, swa, swa_cap, swa_rows, window, scale_log2, out,
                            win_new);
-    return hipGetLastError();
-}
-
-// The one-kernel Reindex layer: pool_blocks * 8 <= kAttNT * 32 and top_k <= kLayerMaxTopK (the
-// caller checks both).  mx: MXFP4 keys (k_idx = code bytes, k_sc = E8M0 scales).
-hipError_t launch_reindex_layer(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
-                                int idx_heads, const int32_t* pool, int pool_blocks, const IndexWs& ws,
-                                int32_t* idx_out, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                                const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
-                                int64_t cache_rows, int top_k, const void* swa, int window_fp8,
-                                const int64_t* swa_row0, int swa_cap, int64_t swa_rows, int window,
-                                const int64_t* replay, int n_heads, float softmax_scale, float* out,
-                                const uint16_t* win_new, hipStream_t stream) {
-    const float scale_log2 = softmax_scale * 1.4426950408889634f;
-    const bool win = window > 0 && swa_rows > 0;
-    const int ept = (pool_blocks * 8 + kAttNT - 1) / kAttNT;
-    using K = decltype(&k_reindex_layer<4, false, 8, true, false>);
-    // variants: indexer heads (<= 4 or <= 8), key format, elements per thread, window presence, window format
-    auto pick_w = [&](auto hi, auto mxv, auto e) -> K {
-        constexpr int HI = decltype(hi)::value;
-        constexpr bool MX = decltype(mxv)::value;
-        constexpr int E = decltype(e)::value;
-        if (window_fp8) return win ? k_reindex_layer<HI, MX, E, true, true> : k_reindex_layer<HI, MX, E, false, true>;
-        return win ? k_reindex_layer<HI, MX, E, true, false> : k_reindex_layer<HI, MX, E, false, false>;
-    };
-    auto pick_e = [&](auto hi, auto mxv) -> K {
-        if (ept <= 8) return pick_w(hi, mxv, std::integral_constant<int, 8>{});
-        if (ept <= 16) return pick_w(hi, mxv, std::integral_constant<int, 16>{});
-        return pick_w(hi, mxv, std::integral_constant<int, 32>{});
-    };
-    auto pick_m = [&](auto hi) -> K {
-        return mx ? pick_e(hi, std::true_type{}) : pick_e(hi, std::false_type{});
-    };
-    const K kern = idx_heads <= 4 ? pick_m(std::integral_constant<int, 4>{}) : pick_m(std::integral_constant<int, 8>{});
-    const AttendArgs a{q,        codes,   scales,   kv_row0, kv_len, max_len, cache_rows, nullptr,    top_k,
-                       swa,      swa_row0, swa_cap, swa_rows, window, replay, n_heads,   scale_log2, out,
-                       win_new};
-    const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(chunks * n_q)), dim3(kAttNT), 0, stream, pool, q_idx, w, kv_row0, kv_len,
-                       pool_blocks, idx_heads, max_len, k_idx, k_sc, cache_rows, ws, idx_out, a);
     return hipGetLastError();
 }
 

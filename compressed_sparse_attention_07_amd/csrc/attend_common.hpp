@@ -88,4 +88,73 @@ __device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
+// kFp4: top_k > 0 (the FP4 cache is read); kWin: window > 0 and the window store has rows.
+// Both are fixed per launch so that every gather below is unconditional (clamped addresses,
+// masked results): loads under branches make the compiler wait on some of them early.
+// kW8: the window store holds E4M3 bytes ([Article] section XI keeps the recent-window cache
+// in FP8); they are converted to f16 exactly and take the FP4 entries' f16 path.
+// replay (may be NULL): per-query replay start s; the window then holds only positions >= s
+// ([Article] section XII, SWA Bounded Replay).
+// win_new (may be NULL): the step's own window vector per query (bf16 [n_q, 128]): every layer
+// computes its own window entry for the new token ([Article] section VI).  The kernel attends it
+// as position N - 1 of the window straight from win_new (the store's row for that position is
+// never read) and writes it to that row (converted to E4M3 for an FP8 store) once everything
+// else is done.
+struct AttendArgs {
+    const uint16_t* q;
+    const uint8_t* codes;
+    const uint8_t* scales;
+    const int64_t* kv_row0;
+    const int32_t* kv_len;
+    int32_t max_len;
+    int64_t cache_rows;
+    const int32_t* idx;  // [n_q, top_k]
+    int top_k;
+    const void* swa;
+    const int64_t* swa_row0;
+    int swa_cap;
+    int64_t swa_rows;
+    int window;
+    const int64_t* replay;
+    int n_heads;
+    float scale_log2;
+    float* out;
+    const uint16_t* win_new;
+};
+
+// The first level of loads of query i's attention: everything that needs only the query number
+// (the length and rows, the new window vector, the query), so the kernel pays one memory latency
+// before the gathers rather than one per dependent load.  The per-query values go first, as
+// vector loads (counted in order: waiting for them leaves the later loads in flight); absent
+// arrays are replaced by a valid one whose value is unused.
+struct AttendPre {
+    int32_t len_raw;
+    int64_t row0_raw, wrow0_raw, replay_raw;
+    uint32_t nwv;     // channels 2l, 2l + 1 of the query's new window vector
+    u32x4 qb[4];      // Q^T fragment of head r, channels 32g + 8s .. + 7 (bf16 as given)
+};
+
+template <bool kWin>
+__device__ __forceinline__ AttendPre attend_pre(int i, const AttendArgs& a) {
+    AttendPre p;
+    const int l = threadIdx.x & 63;
+    const int g = l >> 4, r = l & 15;
+    p.len_raw = vload_i32(a.kv_len, i);
+    p.row0_raw = vload_i64(a.kv_row0, i);
+    p.wrow0_raw = vload_i64(kWin ? a.swa_row0 : a.kv_row0, i);
+    p.replay_raw = vload_i64(a.replay != nullptr ? a.replay : a.kv_row0, i);  // replay[i] when given
+    const bool has_new = kWin && a.win_new != nullptr;
+    p.nwv = has_new ? *reinterpret_cast<const uint32_t*>(a.win_new + (int64_t)i * kD + 2 * l) : 0u;
+    // rows r >= n_heads repeat head 0: every head's softmax is its own and only heads < n_heads
+    // are written
+    const uint4* qp = reinterpret_cast<const uint4*>(a.q + ((int64_t)i * a.n_heads + (r < a.n_heads ? r : 0)) * kD +
+                                                     32 * g);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const uint4 v = qp[s];
+        p.qb[s] = u32x4{v.x, v.y, v.z, v.w};
+    }
+    return p;
+}
+
 }  // namespace csa2

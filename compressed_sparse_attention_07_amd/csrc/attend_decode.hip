@@ -46,10 +46,13 @@ constexpr int kPartFloats = kNH * kD + 2 * kNH;    // a workgroup's partial: O [
 constexpr int kMergeBatch = 8;                     // partials the merging workgroup loads per batch
 static_assert(kNH * kOStride * 4 <= kTileB, "a wave's merge rows fit in its tile");
 
-int attend_dec_parts(int top_k, int window) {
+// workgroups per query with nw waves each (one unit of 32 entries per wave)
+inline int dec_parts(int top_k, int window, int nw) {
     const int units = (top_k + kUnitE - 1) / kUnitE + (window + kUnitE - 1) / kUnitE;
-    return (units + kDecWaves - 1) / kDecWaves;
+    return (units + nw - 1) / nw;
 }
+
+int attend_dec_parts(int top_k, int window) { return dec_parts(top_k, window, kDecWaves); }
 
 size_t attend_dec_part_bytes() { return (size_t)kPartFloats * 4; }
 
@@ -69,57 +72,55 @@ constexpr int kSc1 = 16;  // cache-policy operand: sc1 (agent scope)
 // ([Article] section XII, SWA Bounded Replay).
 // win_new (may be NULL): the step's own window vector per query, attended as position N - 1 and
 // written to that store row ([Article] section VI: every layer writes its own window entry).
-// The arguments of the first level of loads lead (preloaded into SGPRs at launch).
-template <bool kFp4, bool kWin, bool kW8>
-__global__ __launch_bounds__(kDecNT) void k_attend_dec(
-    const int32_t* kv_len, const int64_t* kv_row0, const int64_t* swa_row0, const int64_t* replay,
-    const int32_t* idx, const uint16_t* q, const uint16_t* win_new, int top_k, int n_heads, int n_q, int u4,
-    int32_t max_len, int64_t cache_rows, const uint8_t* codes, const uint8_t* scales, const void* swa, int swa_cap,
-    int64_t swa_rows, int window, float scale_log2, float* out, float* part, uint32_t* ctrl) {
-    __shared__ __align__(16) uint8_t s_tile[kDecWaves * kTileB];
-    __shared__ float s_m[kDecWaves][kNH], s_l[kDecWaves][kNH];
-    __shared__ uint32_t s_ticket;
-    const int parts = (int)gridDim.x / n_q;
-    // workgroups i + n_q * s serve query i (with n_q a multiple of 8 they share one XCD)
-    const int i = (int)blockIdx.x % n_q, s = (int)blockIdx.x / n_q;
+// The attention of query i by workgroup part s of `parts` (NW waves, wave w takes unit
+// s * NW + w); idx_row = the query's top_k selected positions (global memory or LDS); pre = the
+// first level of loads (issued by the caller, possibly before other work).
+template <bool kFp4, bool kWin, bool kW8, int NW>
+__device__ __forceinline__ void attend_dec_body(int i, int s, int parts, int u4, const AttendArgs& a,
+                                                const int32_t* idx_row, AttendPre pre, uint8_t* s_tile,
+                                                float (*s_m)[kNH], float (*s_l)[kNH], uint32_t& s_ticket, float* part,
+                                                uint32_t* ctrl) {
+    constexpr int TPH = NW * kWave / kNH;  // merging threads per head
+    constexpr int DPT = kD / TPH;          // dimensions per merging thread
+    static_assert(DPT == 8 || DPT == 2, "merge vector width");
+    const uint8_t* __restrict__ codes = a.codes;
+    const uint8_t* __restrict__ scales = a.scales;
+    int32_t max_len = a.max_len;
+    int64_t cache_rows = a.cache_rows;
+    const int top_k = a.top_k;
+    const void* __restrict__ swa = a.swa;
+    const int swa_cap = a.swa_cap;
+    const int64_t swa_rows = a.swa_rows;
+    const int window = a.window;
+    const int64_t* __restrict__ replay = a.replay;
+    const int n_heads = a.n_heads;
+    const float scale_log2 = a.scale_log2;
+    float* __restrict__ out = a.out;
+    const uint16_t* __restrict__ win_new = a.win_new;
     const int t = threadIdx.x;
     const int wave = t >> 6;
     const int l = t & 63;
     const int g = l >> 4;   // lane group
     const int r = l & 15;   // row / column within the 16
-    const int u = s * kDecWaves + wave;
+    const int u = s * NW + wave;
     const bool is_fp4 = kFp4 && u < u4;  // wave-uniform
     const int uw = u - u4;               // window unit of a non-FP4 wave
 
-    // ---- first level of loads: the per-query values (vector loads, counted in order, so
-    // waiting for them leaves the rest in flight), this wave's indices and the query ----
-    int32_t len_raw = vload_i32(kv_len, i);
-    int64_t row0_raw = vload_i64(kv_row0, i);
-    int64_t wrow0_raw = vload_i64(kWin ? swa_row0 : kv_row0, i);
-    int64_t replay_raw = vload_i64(replay != nullptr ? replay : kv_row0, i);  // replay[i] when given
+    int32_t len_raw = pre.len_raw;
+    int64_t row0_raw = pre.row0_raw, wrow0_raw = pre.wrow0_raw, replay_raw = pre.replay_raw;
+    uint32_t nwv = pre.nwv;
     const bool has_new = kWin && win_new != nullptr;
-    // channels 2l, 2l + 1 of the query's new window vector
-    uint32_t nwv = has_new ? *reinterpret_cast<const uint32_t*>(win_new + (int64_t)i * kD + 2 * l) : 0u;
     int pos[2];  // selected positions of this lane's entry in the unit's two blocks (-1: none)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int e = kUnitE * u + 16 * j + r;
         const bool in = is_fp4 && e < top_k;
-        const int v = kFp4 ? idx[(int64_t)i * top_k + (in ? e : 0)] : -1;
+        const int v = kFp4 ? idx_row[in ? e : 0] : -1;
         pos[j] = in ? v : -1;
     }
-    // Q^T fragments of head r, channels 32g + 8s .. + 7 (rows r >= n_heads repeat head 0: every
-    // head's softmax is its own and only heads < n_heads are written)
     u32x4 qb[4], qh[4];
-    {
-        const uint4* qp =
-            reinterpret_cast<const uint4*>(q + ((int64_t)i * n_heads + (r < n_heads ? r : 0)) * kD + 32 * g);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint4 v = qp[c];
-            qb[c] = u32x4{v.x, v.y, v.z, v.w};
-        }
-    }
+    for (int c = 0; c < 4; ++c) qb[c] = pre.qb[c];
     __builtin_amdgcn_sched_barrier(0);
     // every use of the per-query values comes after this empty statement, so their wait is not
     // placed in front of the index and query loads
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(kDecNT) void k_attend_dec(
         }
     }
 
-    // ---- merge the four waves ----
+    // ---- merge the NW waves ----
     l_w += __shfl_xor(l_w, 16, 64);
     l_w += __shfl_xor(l_w, 32, 64);
     if (g == 0) {
@@ -396,29 +397,34 @@ __global__ __launch_bounds__(kDecNT) void k_attend_dec(
         for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(&ob[r * kOStride + 16 * db + 4 * g]) = o[db];
     }
     __syncthreads();
-    // thread t: head h, dimensions d0 .. d0 + 7
-    const int h = t >> 4;
-    const int d0 = 8 * (t & 15);
+    // thread t: head h, dimensions d0 .. d0 + DPT - 1
+    const int h = t / TPH;
+    const int d0 = DPT * (t % TPH);
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][h]);
     float L = 0.f;
-    f32x4 O0 = {0.f, 0.f, 0.f, 0.f}, O1 = {0.f, 0.f, 0.f, 0.f};
+    float O[DPT];
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
+    for (int k = 0; k < DPT; ++k) O[k] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
         const float f = (s_m[w][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
         L = fmaf(s_l[w][h], f, L);
         const float* ob = reinterpret_cast<const float*>(s_tile + w * kTileB) + h * kOStride + d0;
-        O0 += f * *reinterpret_cast<const f32x4*>(ob);
-        O1 += f * *reinterpret_cast<const f32x4*>(ob + 4);
+#pragma unroll
+        for (int k = 0; k < DPT; ++k) O[k] = fmaf(f, ob[k], O[k]);
     }
     float* op = out + ((int64_t)i * n_heads + h) * kD + d0;
-    if (parts == 1) {
+    auto store_out = [&](const float (&v)[DPT], float lsum) {
         if (h < n_heads) {
-            const float inv = L > 0.f ? 1.f / L : 0.f;
-            *reinterpret_cast<f32x4*>(op) = O0 * inv;
-            *reinterpret_cast<f32x4*>(op + 4) = O1 * inv;
+            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+            for (int k = 0; k < DPT; k += 2) *reinterpret_cast<float2*>(op + k) = make_float2(v[k] * inv, v[k + 1] * inv);
         }
+    };
+    if (parts == 1) {
+        store_out(O, L);
         return;
     }
 
@@ -427,9 +433,11 @@ __global__ __launch_bounds__(kDecNT) void k_attend_dec(
     const __amdgpu_buffer_rsrc_t rs = part_rsrc(qpart);
     {
         const int base = s * kPartFloats;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, O0), rs, 4 * (base + h * kD + d0), 0, kSc1);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, O1), rs, 4 * (base + h * kD + d0 + 4), 0, kSc1);
-        if ((t & 15) == 0) {
+#pragma unroll
+        for (int k = 0; k < DPT; k += 2)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(O[k]), __float_as_uint(O[k + 1])}, rs,
+                                                  4 * (base + h * kD + d0 + k), 0, kSc1);
+        if (t % TPH == 0) {
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), rs, 4 * (base + kNH * kD + h), 0, kSc1);
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(L), rs, 4 * (base + kNH * kD + kNH + h), 0, kSc1);
         }
@@ -448,15 +456,21 @@ __global__ __launch_bounds__(kDecNT) void k_attend_dec(
     // past the last re-read the last one and are masked), so a batch costs one memory round trip;
     // this workgroup's own part is read back too (its stores have completed).
     float Mg = -INFINITY, Lg = 0.f;
-    f32x4 G0 = {0.f, 0.f, 0.f, 0.f}, G1 = {0.f, 0.f, 0.f, 0.f};
+    float G[DPT];
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) G[k] = 0.f;
     for (int b0 = 0; b0 < parts; b0 += kMergeBatch) {
-        float pm[kMergeBatch], pl[kMergeBatch];
-        f32x4 p0[kMergeBatch], p1[kMergeBatch];
+        float pm[kMergeBatch], pl[kMergeBatch], pv[kMergeBatch][DPT];
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) {
             const int base = min(b0 + k, parts - 1) * kPartFloats;
-            p0[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (base + h * kD + d0), 0, kSc1));
-            p1[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 4 * (base + h * kD + d0 + 4), 0, kSc1));
+#pragma unroll
+            for (int c = 0; c < DPT; c += 2) {
+                const u32x2 v = __builtin_bit_cast(u32x2,
+                    __builtin_amdgcn_raw_buffer_load_b64(rs, 4 * (base + h * kD + d0 + c), 0, kSc1));
+                pv[k][c] = __uint_as_float(v[0]);
+                pv[k][c + 1] = __uint_as_float(v[1]);
+            }
             pm[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (base + kNH * kD + h), 0, kSc1));
             pl[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (base + kNH * kD + kNH + h), 0, kSc1));
         }
@@ -466,22 +480,39 @@ __global__ __launch_bounds__(kDecNT) void k_attend_dec(
             const bool use = b0 + k < parts && pm[k] != -INFINITY;
             const float pmk = use ? pm[k] : -INFINITY;
             const float mn = fmaxf(Mg, pmk);
-            const float a = (Mg == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mg - mn);
-            const float b = use ? __builtin_amdgcn_exp2f(pmk - mn) : 0.f;
-            Lg = Lg * a + pl[k] * b;
-            G0 = G0 * a + p0[k] * b;
-            G1 = G1 * a + p1[k] * b;
+            const float fa = (Mg == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mg - mn);
+            const float fb = use ? __builtin_amdgcn_exp2f(pmk - mn) : 0.f;
+            Lg = Lg * fa + pl[k] * fb;
+#pragma unroll
+            for (int c = 0; c < DPT; ++c) G[c] = G[c] * fa + pv[k][c] * fb;
             Mg = mn;
         }
     }
-    if (h < n_heads) {
-        const float inv = Lg > 0.f ? 1.f / Lg : 0.f;
-        *reinterpret_cast<f32x4*>(op) = G0 * inv;
-        *reinterpret_cast<f32x4*>(op + 4) = G1 * inv;
-    }
+    store_out(G, Lg);
     // the counter back to zero for the next call, only now: vector memory operations complete
     // in order, so a store issued before the partial loads would hold up every one of them
     if (t == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Standalone decode attention: 4 waves per workgroup, parts = gridDim.x / n_q workgroups per
+// query.  The arguments of the first level of loads lead (preloaded into SGPRs at launch).
+template <bool kFp4, bool kWin, bool kW8>
+__global__ __launch_bounds__(kDecNT) void k_attend_dec(
+    const int32_t* kv_len, const int64_t* kv_row0, const int64_t* swa_row0, const int64_t* replay,
+    const int32_t* idx, const uint16_t* q, const uint16_t* win_new, int top_k, int n_heads, int n_q, int u4,
+    int32_t max_len, int64_t cache_rows, const uint8_t* codes, const uint8_t* scales, const void* swa, int swa_cap,
+    int64_t swa_rows, int window, float scale_log2, float* out, float* part, uint32_t* ctrl) {
+    __shared__ __align__(16) uint8_t s_tile[kDecWaves * kTileB];
+    __shared__ float s_m[kDecWaves][kNH], s_l[kDecWaves][kNH];
+    __shared__ uint32_t s_ticket;
+    const AttendArgs a{q,        codes,   scales,   kv_row0, kv_len, max_len, cache_rows, idx,        top_k,
+                       swa,      swa_row0, swa_cap, swa_rows, window, replay, n_heads,   scale_log2, out,
+                       win_new};
+    // workgroups i + n_q * s serve query i (with n_q a multiple of 8 they share one XCD)
+    const int i = (int)blockIdx.x % n_q, s = (int)blockIdx.x / n_q;
+    const AttendPre pre = attend_pre<kWin>(i, a);
+    attend_dec_body<kFp4, kWin, kW8, kDecWaves>(i, s, (int)gridDim.x / n_q, u4, a, idx + (int64_t)i * top_k, pre,
+                                                s_tile, s_m, s_l, s_ticket, part, ctrl);
 }
 
 // Decode attention of n_q queries (their entries split over workgroups).  part: n_q * parts

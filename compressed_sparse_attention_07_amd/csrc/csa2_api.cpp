@@ -18,8 +18,6 @@ constexpr int kFullTile = CSA2_SCAN_TILE;  // must match the scan kernel's tile
 constexpr int kFilterTile = 8192;
 constexpr int kHistBins = 2048;
 constexpr size_t kAlign = 256;
-constexpr int kLayerMaxPoolElems = 512 * 32;  // pool positions the one-kernel Reindex layer takes
-constexpr int kLayerMaxTopK = 1024;          // selected entries it keeps in LDS
 
 struct Thresh {
     int32_t digit, above, in_bucket, total;
@@ -58,14 +56,6 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
                                 const IndexWs& ws, int32_t* idx_out, int select, hipStream_t stream,
                                 hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr,
                                 hipEvent_t ev_sel_start = nullptr, hipEvent_t ev_sel_stop = nullptr);
-hipError_t launch_reindex_layer(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_sc, int mx,
-                                int idx_heads, const int32_t* pool, int pool_blocks, const IndexWs& ws,
-                                int32_t* idx_out, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                                const int64_t* kv_row0, const int32_t* kv_len, int n_q, int32_t max_len,
-                                int64_t cache_rows, int top_k, const void* swa, int window_fp8,
-                                const int64_t* swa_row0, int swa_cap, int64_t swa_rows, int window,
-                                const int64_t* replay, int n_heads, float softmax_scale, float* out,
-                                const uint16_t* win_new, hipStream_t stream);
 hipError_t launch_token_append(const uint16_t* x, const uint16_t* k_new, int64_t n_tok, const int64_t* dst_rows,
                                uint8_t* codes, uint8_t* scales, void* k_idx, uint8_t* k_scales, int64_t cap_rows,
                                hipStream_t stream);
@@ -79,7 +69,7 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
                          const int32_t* kv_len, int n_q, int32_t max_len, int64_t cache_rows, const int32_t* idx,
                          int top_k, const void* swa, int window_fp8, const int64_t* swa_row0, int swa_cap,
                          int64_t swa_rows, int window, const int64_t* replay, int n_heads, float softmax_scale,
-                         float* out, const uint16_t* win_new, int dec, float* part, uint32_t* ctrl, hipStream_t stream,
+                         float* out, const uint16_t* win_new, float* part, uint32_t* ctrl, hipStream_t stream,
                          hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 int attend_dec_parts(int top_k, int window);
 int attend_split_max_queries();
@@ -455,9 +445,44 @@ static int attend_common(const uint16_t* q, const uint8_t* codes, const uint8_t*
     return launch_status(launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub,
                                        seqs.cache_rows, idx, top_k, swa, window_fp8, swa_row0,
                                        window > 0 ? swa_cap : 1, swa_rows, window, replay, n_heads, softmax_scale,
-                                       out, window > 0 ? win_new : nullptr, 1, aw.part, aw.ctrl,
+                                       out, window > 0 ? win_new : nullptr, aw.part, aw.ctrl,
                                        static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_start),
                                        static_cast<hipEvent_t>(ev_stop)));
+}
+
+// A Reindex layer: csa2_index_reindex's scoring and selection kernels, then csa2_attend's kernel.
+static int reindex_attend_common(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
+                                 const csa2_seqs& seqs, int32_t idx_heads, const int32_t* pool, int32_t pool_blocks,
+                                 int32_t block, int32_t top_k, int32_t* idx_out, const uint16_t* q,
+                                 const uint8_t* codes, const uint8_t* scales, void* swa, int32_t window_fp8,
+                                 const int64_t* swa_row0, int32_t swa_cap, int64_t swa_rows, int32_t window,
+                                 const int64_t* replay_start, const uint16_t* win_new, int32_t n_heads,
+                                 float softmax_scale, float* out, void* ws, size_t ws_bytes, void* att_ws,
+                                 size_t att_ws_bytes, void* stream) {
+    const int mx = k_scales != nullptr ? 1 : 0;
+    if (window_fp8 != 0 && window_fp8 != 1) return CSA2_ERR_SHAPE;
+    int st = check_reindex(q_idx, w, k_idx, k_scales, mx, seqs, idx_heads, pool, pool_blocks, block, top_k, idx_out,
+                           ws, ws_bytes);
+    if (st) return st;
+    st = check_attend(q, codes, scales, seqs, idx_out, top_k, swa, swa_row0, swa_cap, swa_rows, window, n_heads,
+                      softmax_scale, out, win_new);
+    if (st || seqs.n_q == 0) return st;
+    size_t need_a = 0;
+    carve_attend(nullptr, seqs.n_q, top_k, window, &need_a);
+    if (need_a > 0 && (att_ws == nullptr || att_ws_bytes < need_a || !aligned16(att_ws))) return CSA2_ERR_WORKSPACE;
+    const AttendWs aw = carve_attend(att_ws, seqs.n_q, top_k, window, &need_a);
+    size_t need = 0;
+    const IndexWs wsp = carve_reindex(ws, seqs.n_q, top_k, pool_blocks, &need);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_index_reindex(q_idx, w, k_idx, k_scales, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
+                                        seqs.max_len_ub, seqs.cache_rows, idx_heads, pool, pool_blocks, top_k, wsp,
+                                        idx_out, 1, s);
+    if (e != hipSuccess) return CSA2_ERR_LAUNCH;
+    e = launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub, seqs.cache_rows,
+                      idx_out, top_k, swa, window_fp8, swa_row0, window > 0 ? swa_cap : 1, swa_rows, window,
+                      replay_start, n_heads, softmax_scale, out, window > 0 ? win_new : nullptr, aw.part, aw.ctrl,
+                      s);
+    return launch_status(e);
 }
 
 int csa2_attend(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, csa2_seqs seqs, const int32_t* idx,
@@ -492,34 +517,10 @@ int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx
                         const uint8_t* scales, void* swa, int32_t window_fp8, const int64_t* swa_row0,
                         int32_t swa_cap, int64_t swa_rows, int32_t window, const int64_t* replay_start,
                         const uint16_t* win_new, int32_t n_heads, float softmax_scale, float* out, void* ws,
-                        size_t ws_bytes, void* stream) {
-    const int mx = k_scales != nullptr ? 1 : 0;
-    if (window_fp8 != 0 && window_fp8 != 1) return CSA2_ERR_SHAPE;
-    int st = check_reindex(q_idx, w, k_idx, k_scales, mx, seqs, idx_heads, pool, pool_blocks, block, top_k, idx_out,
-                           ws, ws_bytes);
-    if (st) return st;
-    st = check_attend(q, codes, scales, seqs, idx_out, top_k, swa, swa_row0, swa_cap, swa_rows, window, n_heads,
-                      softmax_scale, out, win_new);
-    if (st || seqs.n_q == 0) return st;
-    size_t need = 0;
-    const IndexWs wsp = carve_reindex(ws, seqs.n_q, top_k, pool_blocks, &need);
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    const uint16_t* wn = window > 0 ? win_new : nullptr;
-    if (pool_blocks * 8 <= kLayerMaxPoolElems && top_k <= kLayerMaxTopK)
-        return launch_status(launch_reindex_layer(q_idx, w, k_idx, k_scales, mx, idx_heads, pool, pool_blocks, wsp,
-                                                  idx_out, q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q,
-                                                  seqs.max_len_ub, seqs.cache_rows, top_k, swa, window_fp8, swa_row0,
-                                                  window > 0 ? swa_cap : 1, swa_rows, window, replay_start, n_heads,
-                                                  softmax_scale, out, wn, s));
-    hipError_t e = launch_index_reindex(q_idx, w, k_idx, k_scales, mx, seqs.kv_row0, seqs.kv_len, seqs.n_q,
-                                        seqs.max_len_ub, seqs.cache_rows, idx_heads, pool, pool_blocks, top_k, wsp,
-                                        idx_out, 1, s);
-    if (e != hipSuccess) return CSA2_ERR_LAUNCH;
-    // (no attention workspace here: the decode form that splits the output dimensions)
-    e = launch_attend(q, codes, scales, seqs.kv_row0, seqs.kv_len, seqs.n_q, seqs.max_len_ub, seqs.cache_rows,
-                      idx_out, top_k, swa, window_fp8, swa_row0, window > 0 ? swa_cap : 1, swa_rows, window,
-                      replay_start, n_heads, softmax_scale, out, wn, 0, nullptr, nullptr, s);
-    return launch_status(e);
+                        size_t ws_bytes, void* att_ws, size_t att_ws_bytes, void* stream) {
+    return reindex_attend_common(q_idx, w, k_idx, k_scales, seqs, idx_heads, pool, pool_blocks, block, top_k, idx_out,
+                                 q, codes, scales, swa, window_fp8, swa_row0, swa_cap, swa_rows, window, replay_start,
+                                 win_new, n_heads, softmax_scale, out, ws, ws_bytes, att_ws, att_ws_bytes, stream);
 }
 
 int csa2_token_append(const uint16_t* x, const uint16_t* k_new, int64_t n_tok, const int64_t* dst_rows,

@@ -1054,7 +1054,7 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     QFrag qf;
     load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
     __syncthreads();
-    reindex_score_chunks<HI, MX, kScoreNT / kWave, false>(grp * cpw, (grp + 1) * cpw, n, row0,
+    reindex_score_chunks<HI, MX, kScoreNT / kWave>(grp * cpw, (grp + 1) * cpw, n, row0,
                                                           pool + (int64_t)i * pool_blocks, pool_blocks, qf, k_idx,
                                                           k_sc, ws.keys + (int64_t)i * n_elem, sh_hist);
     __syncthreads();
@@ -1092,8 +1092,7 @@ __global__ __launch_bounds__(NT) void k_idx_reindex_select(uint32_t* __restrict_
     IndexWs ws{};
     ws.keys = keys;
     ws.hist = hist;
-    reindex_select_query<NT, EPT>(blockIdx.x, pool, pool_blocks, top_k, ws, idx_out, nullptr, s_hist, s_scan, s_or,
-                                  &sh_th);
+    reindex_select_query<NT, EPT>(blockIdx.x, pool, pool_blocks, top_k, ws, idx_out, s_hist, s_scan, s_or, &sh_th);
 }
 
 // ----------------------------------------------------------------------------------------

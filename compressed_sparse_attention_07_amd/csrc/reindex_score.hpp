@@ -33,9 +33,7 @@ __device__ __forceinline__ void reindex_item(int b, int chunks, int& i, int& chu
 // lanes r < 8 taking slot 2m and r >= 8 slot 2m + 1; wave wid takes units m0 + NW u.  Writes
 // each position's order-preserving key (0 for positions outside [0, n) or -1 slots) to keys
 // [slot * 8 + p % 8] and counts the first digit of every nonzero key in sh_hist (LDS).
-// COHERENT: the keys are written with agent-scope stores (written through to memory), for a
-// workgroup of another XCD that reads them inside the same kernel.
-template <int HI, bool MX, int NW, bool COHERENT>
+template <int HI, bool MX, int NW>
 __device__ __forceinline__ void reindex_score_chunks(int c0, int c1, int n, int64_t row0,
                                                      const int32_t* __restrict__ qpool, int pool_blocks,
                                                      const QFrag& qf, const void* __restrict__ k_idx,
@@ -89,10 +87,7 @@ __device__ __forceinline__ void reindex_score_chunks(int c0, int c1, int n, int6
             const float sc = n > 0 ? mfma_score<HI>(qf, kb[u][0], kb[u][1]) : 0.f;
             const uint32_t key = ok ? score_key(sc) : 0u;
             if (g == 0 && slot < pool_blocks) {
-                if constexpr (COHERENT)
-                    __hip_atomic_store(&keys[slot * 8 + (r & 7)], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                else
-                    keys[slot * 8 + (r & 7)] = key;
+                keys[slot * 8 + (r & 7)] = key;
                 if (key) atomicAdd(&sh_hist[key >> 21], 1u);
             }
         }

@@ -1,5 +1,5 @@
-// Reindex-mode selection of one query, shared by the selection kernel and the fused
-// selection + attention kernel (one workgroup of NT threads; EPT pool elements per thread).
+// Reindex-mode selection of one query (one workgroup of NT threads; EPT pool elements per
+// thread).
 //
 // Article "DeepSeek-V4.1-Flash: Pushing KV Cache Compression to 890 Bytes per Token", section
 // IX: a Reindex layer takes its own Top-K inside the shared pool.  The pool is ascending, so
@@ -13,32 +13,12 @@
 
 namespace csa2 {
 
-// Eight keys at p (16-byte aligned) as two uint4.  COHERENT: agent-scope loads, which see what
-// workgroups on other XCDs wrote with agent-scope stores earlier in the same kernel.
-template <bool COHERENT>
-__device__ __forceinline__ void load_keys8(const uint32_t* p, uint4& a, uint4& b) {
-    if constexpr (COHERENT) {
-        const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
-        uint64_t v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = __hip_atomic_load(q + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        a = make_uint4((uint32_t)v[0], (uint32_t)(v[0] >> 32), (uint32_t)v[1], (uint32_t)(v[1] >> 32));
-        b = make_uint4((uint32_t)v[2], (uint32_t)(v[2] >> 32), (uint32_t)v[3], (uint32_t)(v[3] >> 32));
-    } else {
-        a = *reinterpret_cast<const uint4*>(p);
-        b = *reinterpret_cast<const uint4*>(p + 4);
-    }
-}
-
-// Writes the query's selection to idx_out[i * top_k ..] and, when lds_idx is given, to that
-// LDS row as well (entries past the selection: -1).  Every thread of the workgroup must call
-// it; it ends with the selection written (the caller synchronises before reading lds_idx).
-// COHERENT: the keys and the first-digit histogram were written earlier in the same kernel
-// (by other workgroups, possibly on other XCDs) and are read with agent-scope loads.
-template <int NT, int EPT, bool COHERENT = false>
+// Writes the query's selection to idx_out[i * top_k ..] (entries past the selection: -1).
+// Every thread of the workgroup must call it.
+template <int NT, int EPT>
 __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __restrict__ pool, int pool_blocks,
                                                      int top_k, const IndexWs& ws, int32_t* __restrict__ idx_out,
-                                                     int32_t* lds_idx, uint32_t (*s_hist)[kHistBins], int* s_scan,
+                                                     uint32_t (*s_hist)[kHistBins], int* s_scan,
                                                      uint32_t* s_or, Thresh* sh_th_p) {
     Thresh& sh_th = *sh_th_p;
     const int t = threadIdx.x;
@@ -55,7 +35,8 @@ __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __res
         uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
         int32_t blk = -1;
         if (e0 + j < n_elem) {  // n_elem is a multiple of 8: the whole block is there
-            load_keys8<COHERENT>(keys + e0 + j, a, b);
+            a = *reinterpret_cast<const uint4*>(keys + e0 + j);
+            b = *reinterpret_cast<const uint4*>(keys + e0 + j + 4);
             blk = qpool[(e0 + j) >> 3];
         }
         kv[j] = a.x; kv[j + 1] = a.y; kv[j + 2] = a.z; kv[j + 3] = a.w;
@@ -66,16 +47,7 @@ __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __res
     if (t < 2) s_or[t] = 0u;
     // first digit: histogram accumulated by the score kernel (its barriers also cover the
     // clearing above)
-    if constexpr (COHERENT) {
-        constexpr int BPT = kHistBins / NT;
-        uint32_t h[BPT];
-#pragma unroll
-        for (int j = 0; j < BPT; ++j)
-            h[j] = __hip_atomic_load(gh + kHistBins - 1 - (BPT * t + j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        find_threshold_regs<NT>(h, top_k, s_scan, &sh_th);
-    } else {
-        find_threshold<NT>(gh, top_k, s_scan, &sh_th);
-    }
+    find_threshold<NT>(gh, top_k, s_scan, &sh_th);
     Thresh th = sh_th;
     uint32_t T = 1u;           // selected: key > T, or key == T among the first need_eq of them
     int need_eq = INT32_MAX;   // (keys are >= 1 for every valid element; 0 marks padding)
@@ -142,14 +114,12 @@ __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __res
             if (sel) {
                 const int32_t v = pb[j >> 3] * 8 + (j & 7);
                 out[off] = v;
-                if (lds_idx != nullptr) lds_idx[off] = v;
                 ++off;
             }
         }
     }
     for (int j = total + t; j < top_k; j += NT) {
         out[j] = -1;
-        if (lds_idx != nullptr) lds_idx[j] = -1;
     }
     for (int b = t; b < kHistBins; b += NT) gh[b] = 0u;
 }

@@ -124,10 +124,8 @@ class Runner:
     def __init__(self, wl: Workload, device="cuda", keep_host=False, seed=0, copies=1, fused_reindex=False):
         """copies > 1 keeps that many device copies of the KV sets (identical values); step() then
         rotates through them so consecutive steps never re-read a set that a last-level cache
-        could still hold.  fused_reindex: Reindex layers run as csa2_reindex_attend (one kernel)
-        rather than csa2_index_reindex + csa2_attend (three).  Off by default: on the decode
-        workloads the one-kernel form measured slower per step (the in-kernel hand-off from the
-        scoring workgroups to the selecting one costs more than a kernel boundary)."""
+        could still hold.  fused_reindex: Reindex layers run as one csa2_reindex_attend call (the
+        same three kernels as csa2_index_reindex + csa2_attend, issued by one entry point)."""
         self.wl = wl
         self.fused_reindex = fused_reindex
         self.device = device
@@ -337,12 +335,12 @@ class Runner:
                                          self.ws_full, shared_kv=shared, stream=stream)
                 pool_built = pool_built or want_pool > 0
                 idx = L.idx
-            elif L.mode == "R" and self.fused_reindex:
+            elif L.mode == "R" and self.fused_reindex and timing is None:
                 C.csa2_reindex_attend(L.q_idx, L.w, st.k_codes if wl.keys_mx else st.k_idx,
                                       st.k_scales if wl.keys_mx else None, self.seqs, self.pool, wl.top_k, L.idx, L.q,
                                       st.codes, st.scales, L.swa, self.swa_row0, self.swa_cap, wl.window, self.scale,
                                       L.out, self.ws_re, window_fp8=wl.window_fp8, replay_start=self.replay,
-                                      win_new=L.win_new, stream=stream)
+                                      win_new=L.win_new, att_ws=self.ws_att, stream=stream)
                 continue
             elif L.mode == "R" and timing is not None:
                 C.csa2_index_reindex_timed(L.q_idx, L.w, st.k_codes if wl.keys_mx else st.k_idx,

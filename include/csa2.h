@@ -328,10 +328,10 @@ int csa2_index_reindex_noalloc(const uint16_t* q_idx, const float* w, const uint
                                int32_t top_k, int32_t* idx_out, void* stream);
 
 /*
- * csa2_reindex_attend -- one Reindex layer in one kernel: csa2_index_reindex (or _mx)
- * followed by csa2_attend (or _fp8win) over the selection it produced.  [Article]
- * sections VIII-IX (a Reindex layer selects its own Top-K inside the shared pool) and
- * section VI (the layer then attends its selection plus its window).
+ * csa2_reindex_attend -- one Reindex layer: csa2_index_reindex (or _mx) followed by
+ * csa2_attend (or _fp8win) over the selection it produced.  [Article] sections VIII-IX (a
+ * Reindex layer selects its own Top-K inside the shared pool) and section VI (the layer then
+ * attends its selection plus its window).
  *
  *   q_idx, w, pool, pool_blocks, block, top_k, idx_out, ws, ws_bytes: as for
  *           csa2_index_reindex (CSA2_OP_INDEX_REINDEX workspace); idx_heads is its n_heads.
@@ -340,18 +340,17 @@ int csa2_index_reindex_noalloc(const uint16_t* q_idx, const float* w, const uint
  *   q, codes, scales, swa, swa_row0, swa_cap, swa_rows, window, win_new, n_heads,
  *   softmax_scale, out: as for csa2_attend; window_fp8 = 0: swa holds bf16, 1: E4M3 bytes.
  *   replay_start  device int64 [n_q] or NULL: as for csa2_attend_fp8win (either format).
- * idx_out receives the selection (a Reuse layer that follows attends with it), equal to
- * that of csa2_index_reindex, and out the attention over it, within the same tolerance of
- * the exact result as csa2_attend (its arithmetic is csa2_attend's for calls of more than
- * 64 queries; for fewer, csa2_attend splits each query's entries over several workgroups
- * and may round differently).  With pool_blocks * 8 <=
- * 16,384 and top_k <= 1,024 it is one kernel: every workgroup scores one 512-position
- * chunk of a pool, and the last workgroup of each query to finish (an agent-scope
- * ticket counter in the workspace) selects and attends; larger sizes take the separate
- * kernels.  On MI355X the separate calls measured faster (the in-kernel hand-off costs
- * more than a kernel boundary), so this entry point is the single-launch form for
- * callers that want one, not the fast path.  All arguments are checked before anything
- * is launched; the errors are those of the separate calls.
+ *   att_ws, att_ws_bytes  the attention workspace, as for csa2_attend
+ *           (CSA2_OP_ATTEND with the same n_q, top_k and window; may be NULL when that size
+ *           is 0).
+ * idx_out receives the selection (a Reuse layer that follows attends with it), equal to that
+ * of csa2_index_reindex, and out the attention over it, equal to that of csa2_attend: the call
+ * issues the separate calls' kernels (scoring, selection, attention) in one go.  Two fused
+ * forms measured slower on MI355X and are not used: everything in one kernel (the last scoring
+ * workgroup of a query selecting and attending), and the selection and attention in one kernel
+ * (one compute unit then forms all 512 entries' logits, where the attention kernel spreads
+ * them over five).  All arguments are checked before anything is launched; the errors are
+ * those of the separate calls.
  */
 int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
                         csa2_seqs seqs, int32_t idx_heads, const int32_t* pool, int32_t pool_blocks,
@@ -359,7 +358,8 @@ int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx
                         const uint8_t* codes, const uint8_t* scales, void* swa, int32_t window_fp8,
                         const int64_t* swa_row0, int32_t swa_cap, int64_t swa_rows, int32_t window,
                         const int64_t* replay_start, const uint16_t* win_new, int32_t n_heads,
-                        float softmax_scale, float* out, void* ws, size_t ws_bytes, void* stream);
+                        float softmax_scale, float* out, void* ws, size_t ws_bytes, void* att_ws,
+                        size_t att_ws_bytes, void* stream);
 
 /*
  * csa2_token_append -- the decode step's own token for a Full layer's cache set: its

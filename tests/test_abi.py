@@ -118,11 +118,13 @@ def test_reindex_attend_validation():
     L = C.lib()
     need_r = C.csa2_workspace_bytes(C.OP_INDEX_REINDEX, 2, 0, 0, 512, 2048)
 
+    need_a = C.csa2_workspace_bytes(C.OP_ATTEND, 2, 0, 0, 512, 128)
+
     def call(pool_blocks=2048, top_k=512, idx_heads=4, heads=16, window=128, cap=128, fp8=0, k_scales=None,
-             idx_out=FAKE, q=FAKE, swa=FAKE, ws_bytes=need_r, s=None):
+             idx_out=FAKE, q=FAKE, swa=FAKE, ws_bytes=need_r, s=None, att_ws=FAKE, att_bytes=need_a):
         return L.csa2_reindex_attend(FAKE, FAKE, FAKE, k_scales, s or seqs(), idx_heads, FAKE, pool_blocks, 8, top_k,
                                      idx_out, q, FAKE, FAKE, swa, fp8, FAKE, cap, 1000, window, None, None, heads,
-                                     ctypes.c_float(0.1), FAKE, FAKE, ws_bytes, None)
+                                     ctypes.c_float(0.1), FAKE, FAKE, ws_bytes, att_ws, att_bytes, None)
 
     assert call(pool_blocks=0) == C.ERR_SHAPE
     assert call(idx_heads=9) == C.ERR_SHAPE
@@ -133,6 +135,8 @@ def test_reindex_attend_validation():
     assert call(q=None) == C.ERR_NULL
     assert call(swa=None) == C.ERR_NULL
     assert call(ws_bytes=need_r - 1) == C.ERR_WORKSPACE
+    assert call(att_ws=None) == C.ERR_WORKSPACE                    # the attention workspace is checked too
+    assert call(att_bytes=need_a - 1) == C.ERR_WORKSPACE
     assert call(k_scales=ctypes.c_void_p(0x10001)) == C.ERR_SHAPE    # MXFP4 scales must be 2-byte aligned
     assert call(s=seqs(n_q=0)) == C.OK
 

@@ -509,15 +509,17 @@ def test_index_reindex_unsorted_pool_follows_element_order():
     assert np.array_equal(idx.cpu().numpy()[0], cand[chosen])
 
 
-@pytest.mark.parametrize("pool_blocks,top_k,window", [(2048, 512, 128), (300, 64, 0), (3000, 512, 128), (1, 4, 16)])
+@pytest.mark.parametrize("pool_blocks,top_k,window", [(2048, 512, 128), (300, 64, 0), (3000, 512, 128), (1, 4, 16),
+                                                      (512, 512, 300), (2048, 100, 256), (2048, 700, 128)])
 def test_reindex_attend_equals_separate_calls_and_oracle(pool_blocks, top_k, window):
-    # csa2_reindex_attend (one kernel for pools of <= 2,048 blocks, the separate kernels above
-    # that) against csa2_index_reindex followed by csa2_attend: the same indices; both outputs
-    # against the oracle (csa2_attend splits a decode query's entries over workgroups, the
-    # one-kernel layer does not, so the two may round differently)
+    # csa2_reindex_attend (scoring + the fused selection/attention kernel for top_k <= 512,
+    # the separate kernels above that) against csa2_index_reindex followed by csa2_attend: the
+    # same indices; both outputs against the oracle (the two split the entries over workgroups
+    # differently, so they may round differently).  Windows of 300 and 256 take more than one
+    # workgroup per query in the fused kernel (a cross-workgroup merge) or only the selecting one.
     lengths = [40000, 777, 0, 16, 25001]
     ic = IndexCase(W_T + 70, lengths, n_heads=4)
-    ac = AttendCase(W_T + 70, lengths, n_heads=16, window=max(window, 1), swa_cap=128)
+    ac = AttendCase(W_T + 70, lengths, n_heads=16, window=max(window, 1), swa_cap=max(window, 128))
     _, pool, _ = ic.run_full(512, pool_blocks)
     q2 = synth.int_bf16(W_T + 70, synth.T_IDX_Q, (len(lengths), 4, 64), seq=5)
     w2 = synth.int_weights(W_T + 70, synth.T_IDX_W, (len(lengths), 4), seq=5)
