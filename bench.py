@@ -15,9 +15,9 @@ launches record at the kernel's start and end in K eager steps, with its share o
 algorithmic GB/s and its fraction of HBM peak; `roofline` is the entry with the largest share.
 `kv_gather` is the attention's cache gathers (72 B per selected FP4 entry, 256 B per bf16 window
 entry) per launch over the attention kernel's duration.  `bulk_append` times fp4_kv_append of
-2^20 tokens; `stream_ceiling` a plain 1 GiB device copy and a 1 GiB read-only reduction (torch),
-the rates this HBM delivers in practice.  `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload on the host's cores.  "also" further holds the 1M-context workload in
+2^20 tokens; `stream_ceiling` a plain 1 GiB device copy (torch) and a 1 GiB streaming read (the
+library's own read kernel), the rates this HBM delivers in practice.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload on the host's cores.  "also" further holds the 1M-context workload in
 the pages' storage formats (FP8 window with SWA Bounded Replay, MXFP4 indexer keys, both), the two
 prefill chunks (chunk tokens/s, MFMA roofline of the scoring), the single 4K-context sequence and
 the ragged mix of 64 sequences.  The 64K workload rotates two device copies of its inputs so that
@@ -58,9 +58,10 @@ def kernel_name(family: str, n_q: int) -> str:
     return KERNEL_NAMES[family]
 
 
-# sources whose text decides each timed kernel's code (compiler flags included): a committed counter
-# summary is used for `traffic` only while these still hash to the value recorded in it
-_COMMON = ["compressed_sparse_attention_07_amd/csrc/csa2_device.hpp", "compressed_sparse_attention_07_amd/build.py"]
+# sources whose text decides each timed kernel's code, and the compiler flags of the translation
+# units that hold it: a committed counter summary is used for `traffic` only while these still
+# hash to the value recorded in it
+_COMMON = ["compressed_sparse_attention_07_amd/csrc/csa2_device.hpp"]
 KERNEL_SOURCES = {
     "scan": ["compressed_sparse_attention_07_amd/csrc/scan_full.hpp",
              "compressed_sparse_attention_07_amd/csrc/scan_common.hpp"] + _COMMON,
@@ -72,12 +73,17 @@ KERNEL_SOURCES = {
                "compressed_sparse_attention_07_amd/csrc/attend_common.hpp",
                "compressed_sparse_attention_07_amd/csrc/pack_common.hpp"] + _COMMON,
 }
+KERNEL_UNITS = {"scan": ["indexer.hip"], "reindex_score": ["indexer.hip"], "reindex_select": ["indexer.hip"],
+                "attend": ["attend.hip", "attend_decode.hip"]}
 
 
 def source_sha(family: str) -> str:
+    from compressed_sparse_attention_07_amd import build as B
     h = hashlib.sha256()
     for p in KERNEL_SOURCES[family]:
         h.update(open(os.path.join(ROOT, p), "rb").read())
+    for u in KERNEL_UNITS[family]:
+        h.update(" ".join(f for f in B.FLAGS + B.EXTRA.get(u, []) if not f.startswith("-I")).encode())
     return h.hexdigest()[:16]
 
 
@@ -245,27 +251,39 @@ def bulk_append(reps: int = 10) -> dict:
 
 
 def stream_ceiling() -> dict:
-    """What the HBM delivers to plain streaming kernels in this run: a 1 GiB device copy (read +
-    write) and a 1 GiB read-only reduction, both torch kernels, best of 5."""
+    """What the HBM delivers to plain streaming kernels in this run, best of 5 each: a 1 GiB device
+    copy (torch, read + write) and a 1 GiB streaming read (the library's csa2_stream_read: 16-byte
+    loads over the whole chip, timed by the kernel's own events)."""
     import torch
+    from compressed_sparse_attention_07_amd import csa2 as C
     nbytes = 1 << 30
     x = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     y = torch.empty_like(x)
+    sink = torch.empty(C.lib().csa2_stream_read_groups(), dtype=torch.int32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in ev:
+        e.record()
+
+    def copy():
+        ev[0].record()
+        y.copy_(x)
+        ev[1].record()
+
+    def read():
+        C.csa2_stream_read(x, sink, ev[0], ev[1])
+
     out = {}
-    for name, fn, moved in (("copy", lambda: y.copy_(x), 2 * nbytes), ("read", lambda: x.sum(), nbytes)):
+    for name, fn, moved in (("copy", copy, 2 * nbytes), ("read", read, nbytes)):
         fn()
         torch.cuda.synchronize()
         best = 1e9
         for _ in range(5):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
             fn()
-            b.record()
             torch.cuda.synchronize()
-            best = min(best, a.elapsed_time(b) / 1e3)
+            best = min(best, ev[0].elapsed_time(ev[1]) / 1e3)
         out[f"{name}_gbps"] = round(moved / best / 1e9, 1)
     out["frac_of_peak"] = {k: round(v / HBM_PEAK_GBPS, 4) for k, v in out.items()}
-    del x, y
+    del x, y, sink
     torch.cuda.empty_cache()
     return out
 

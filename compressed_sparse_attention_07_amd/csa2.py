@@ -36,6 +36,8 @@ EXPORTS = (
     "csa2_index_full_scan_timed",
     "csa2_index_reindex_timed",
     "csa2_attend_timed",
+    "csa2_stream_read_groups",
+    "csa2_stream_read",
     "csa2_index_reindex_mx",
     "csa2_attend",
     "csa2_attend_fp8win",
@@ -102,6 +104,10 @@ def lib() -> ctypes.CDLL:
         L.csa2_attend_timed.argtypes = [vp, vp, vp, SeqsC, vp, i32, vp, vp, i32, i64, i32, vp, i32, f32, vp, vp, sz,
                                         vp, vp, vp]
         L.csa2_window_append.argtypes = [vp, i64, vp, i64, vp, i32, i64, vp]
+        L.csa2_stream_read_groups.argtypes = []
+        L.csa2_stream_read_groups.restype = ctypes.c_int
+        L.csa2_stream_read.argtypes = [vp, sz, vp, sz, vp, vp, vp]
+        L.csa2_stream_read.restype = ctypes.c_int
         L.csa2_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
         L.csa2_workspace_bytes.restype = sz
         L.csa2_workspace_init.argtypes = [vp, sz, vp]
@@ -370,6 +376,14 @@ def csa2_attend_timed(q, codes, scales, seqs: Seqs, idx, swa, swa_row0, swa_cap:
         _ptr(q), _ptr(codes), _ptr(scales), seqs.c(), _ptr(idx), top_k, _ptr(swa), _ptr(swa_row0), swa_cap,
         swa_rows, window, _ptr(win_new), n_heads, ctypes.c_float(softmax_scale), _ptr(out), _ptr(ws), ws.numel(),
         _stream(stream), _event(start_event), _event(stop_event)))
+
+
+def csa2_stream_read(src, sink, start_event, stop_event, stream=None) -> None:
+    """Measurement: a plain streaming read of src (device, 16-byte aligned) with the kernel's own
+    start and end recorded into two torch events; sink: uint32 [csa2_stream_read_groups()]."""
+    _check("csa2_stream_read", lib().csa2_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                                      sink.numel(), _stream(stream), _event(start_event),
+                                                      _event(stop_event)))
 
 
 def csa2_index_reindex_mx(q_idx, w, k_codes, k_scales, seqs: Seqs, pool, top_k: int, idx_out, ws,

@@ -75,6 +75,9 @@ int attend_dec_parts(int top_k, int window);
 int attend_split_max_queries();
 size_t attend_dec_part_bytes();
 hipError_t launch_zero(void* ws, size_t bytes, hipStream_t stream);
+int stream_read_groups();
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int groups, hipStream_t stream,
+                              hipEvent_t ev_start, hipEvent_t ev_stop);
 
 namespace {
 
@@ -521,6 +524,20 @@ int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx
     return reindex_attend_common(q_idx, w, k_idx, k_scales, seqs, idx_heads, pool, pool_blocks, block, top_k, idx_out,
                                  q, codes, scales, swa, window_fp8, swa_row0, swa_cap, swa_rows, window, replay_start,
                                  win_new, n_heads, softmax_scale, out, ws, ws_bytes, att_ws, att_ws_bytes, stream);
+}
+
+int csa2_stream_read_groups(void) { return stream_read_groups(); }
+
+int csa2_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream,
+                     void* start_event, void* stop_event) {
+    const int st = refuse_capture(stream, start_event, stop_event);
+    if (st) return st;
+    if (src == nullptr || sink == nullptr) return CSA2_ERR_NULL;
+    if (!aligned16(src) || bytes % 16 != 0 || bytes == 0) return CSA2_ERR_SHAPE;
+    const int groups = stream_read_groups();
+    if (sink_words < (size_t)groups) return CSA2_ERR_SHAPE;
+    return launch_status(launch_stream_read(src, bytes, sink, groups, static_cast<hipStream_t>(stream),
+                                            static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)));
 }
 
 int csa2_token_append(const uint16_t* x, const uint16_t* k_new, int64_t n_tok, const int64_t* dst_rows,

@@ -65,6 +65,39 @@ __device__ __forceinline__ uint4 buf_ld16(BufRsrc rs, int voff, int soff) {
     return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 
+// 16-byte load marked non-temporal (streamed past the caches)
+__device__ __forceinline__ uint4 buf_ld16_nt(BufRsrc rs, int voff, int soff) {
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 2);
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
+// Whole-row loads for the MFMA key fragments (bf16 keys, 128-byte rows).  The two loads of a
+// 16-position step each read 8 whole rows: in 16-lane group x, lane i < 8 reads 16-byte chunk x
+// of row i and lane i >= 8 chunk x + 4 of row i - 8 (rows 8..15 in the second load).  One
+// exchange of half groups then gives the layout mfma_score takes (lane (x, i): chunk x, then
+// chunk x + 4, of row i): lanes i >= 8 of the first fragment take the second load's lanes
+// i - 8, lanes i < 8 of the second fragment the first load's lanes i + 8.
+__device__ __forceinline__ int rowline_voff(int lane) {
+    const int i = lane & 15, x = lane >> 4;
+    return (i & 7) * 128 + (x + 4 * (i >> 3)) * 16;
+}
+
+__device__ __forceinline__ void rowline_to_frags(uint4& a, uint4& b, int lane) {
+    const bool hi = (lane & 8) != 0;
+    uint32_t* pa = &a.x;
+    uint32_t* pb = &b.x;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t from_b = (uint32_t)__builtin_amdgcn_mov_dpp((int)pb[d], 0x118, 0xF, 0xF, true);  // row_shr:8
+        const uint32_t from_a = (uint32_t)__builtin_amdgcn_mov_dpp((int)pa[d], 0x108, 0xF, 0xF, true);  // row_shl:8
+        const uint32_t na = hi ? from_b : pa[d];
+        const uint32_t nb = hi ? pb[d] : from_a;
+        pa[d] = na;
+        pb[d] = nb;
+    }
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 

@@ -42,6 +42,9 @@ __device__ __forceinline__ void score_full_body(
     const uint8_t* __restrict__ k_sc, int pool_blocks, const IndexWs& ws) {
     __shared__ uint32_t sh_hist[kHistBins];
     __shared__ uint32_t sh_bhist[kHistBins];
+    // per wave: the keys and block keys of its batches of the current unit (16-position layout)
+    __shared__ __align__(16) uint32_t sh_key[kScoreNT / kWave][LP ? 4 : kFullTile / 4];
+    __shared__ __align__(16) uint32_t sh_bk[kScoreNT / kWave][LP ? 4 : kFullTile / 32];
 
     const int t = threadIdx.x;
     const int lane = __lane_id();
@@ -112,6 +115,30 @@ __device__ __forceinline__ void score_full_body(
 
     // one step = 64 consecutive positions of the workgroup (16 per wave); U steps per batch
     constexpr int U = CSA2_SCAN_U;
+    // the 16-position layout's staged keys (see below): the wave's first key of the unit they
+    // belong to, and how many batches of it
+    constexpr int WR = 16 * U;  // positions per wave per batch
+    uint32_t* s_key = sh_key[wid];
+    uint32_t* s_bk = sh_bk[wid];
+    uint32_t* pend_k = nullptr;
+    uint32_t* pend_b = nullptr;
+    int pend_j = 0;
+    auto write_run = [&]() {
+        if (pend_j > 0) {  // (uniform) batch q's 16U keys go to pend_k + q 64U, from lanes 32 (q & 1) ..
+            for (int q0 = 0; q0 < pend_j; q0 += 2) {
+                const int q = q0 + (lane >> 5);
+                if (q < pend_j)
+                    *reinterpret_cast<uint4*>(pend_k + q * 64 * U + 4 * (lane & 31)) =
+                        *reinterpret_cast<const uint4*>(s_key + q * WR + 4 * (lane & 31));
+            }
+            if (want_pool && lane < pend_j * (WR / 32)) {  // batch q's 2U block keys, 4 per lane
+                const int q = lane / (WR / 32), c = lane % (WR / 32);
+                *reinterpret_cast<uint4*>(pend_b + q * 8 * U + 4 * c) =
+                    *reinterpret_cast<const uint4*>(s_bk + q * (WR / 8) + 4 * c);
+            }
+            pend_j = 0;
+        }
+    };
     static_assert((kFullTile / 4) % (64 * U) == 0 && (kFullTile / 4) % (256 * CSA2_SCAN_U_LP) == 0,
                   "a quarter tile holds whole load batches");
     for (int unit = ub; unit < ue; ++unit) {
@@ -213,51 +240,76 @@ __device__ __forceinline__ void score_full_body(
                 }
             }
         } else {
-            const int voff = (16 * wid + r) * kRowB + (MX ? 4 : 16) * g;
-            const int voff_s = (16 * wid + r) * 2;
+            // A batch of U steps covers 16U consecutive positions of each wave (64U of the
+            // workgroup), so a wave's keys of one batch form one aligned run of 16U keys and 2U
+            // block keys.  The runs of all the unit's batches are staged in LDS and written with
+            // 16-byte stores once the next unit's first key loads are out (a store ahead of them
+            // would hold them up: memory operations of a wave complete in order), so the unit's
+            // keys reach memory together.  Keys of positions at or past n in a run are written as
+            // 0 inside the query's own tile; every reader bounds its keys by n.
+            // bf16 keys: whole-row loads, non-temporal (rowline_voff; on 128-byte rows these
+            // measured faster than loads of half rows in the fragment layout)
+            const int voff = MX ? (WR * wid + r) * kRowB + 4 * g : WR * wid * kRowB + rowline_voff(lane);
+            const int voff_s = (WR * wid + r) * 2;
+            int jd = 0;  // batches of this unit done
             for (int b = b_lo; b < b_hi; b += 64 * U) {
                 const int pb = p_tile + b;
                 if (pb >= n) break;
+                if (b == b_lo) {
+                    write_run();  // the previous unit's runs
+                    wave_lds_sync();
+                }
                 uint4 kb[U][2];
                 uint32_t kc[U][2], ks[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     if constexpr (MX) {
-                        kc[u][0] = buf_ld4(rs, voff, (b + 64 * u) * kRowB);
-                        kc[u][1] = buf_ld4(rs, voff + 16, (b + 64 * u) * kRowB);
-                        ks[u] = buf_ld2(rss, voff_s, (b + 64 * u) * 2);
+                        kc[u][0] = buf_ld4(rs, voff, (b + 16 * u) * kRowB);
+                        kc[u][1] = buf_ld4(rs, voff + 16, (b + 16 * u) * kRowB);
+                        ks[u] = buf_ld2(rss, voff_s, (b + 16 * u) * 2);
                     } else {
-                        kb[u][0] = buf_ld16(rs, voff, (b + 64 * u) * kRowB);
-                        kb[u][1] = buf_ld16(rs, voff + 64, (b + 64 * u) * kRowB);
+                        kb[u][0] = buf_ld16_nt(rs, voff, (b + 16 * u) * kRowB);
+                        kb[u][1] = buf_ld16_nt(rs, voff + 8 * kRowB, (b + 16 * u) * kRowB);
                     }
+                    __builtin_amdgcn_sched_barrier(0);  // in step order: step 0 waits for its own loads only
                 }
+                const int j = (b - b_lo) / (64 * U);  // batch of the unit
+                const int pw = pb + WR * wid;         // first position of this wave's run
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int p0 = pb + 64 * u + 16 * wid;  // first of this wave's 16 positions
+                    const int p0 = pw + 16 * u;  // first of this step's 16 positions
                     const int p = p0 + r;
                     if constexpr (MX) {
                         kb[u][0] = mx_frag(kc[u][0], ks[u] & 0xffu);
                         kb[u][1] = mx_frag(kc[u][1], ks[u] >> 8);
+                    } else {
+                        rowline_to_frags(kb[u][0], kb[u][1], lane);
                     }
                     const float sc = mfma_score<HI>(qf, kb[u][0], kb[u][1]);
                     const bool mine = g == 0 && p < n;
                     const uint32_t key = mine ? score_key(sc) : 0u;
-                    if (mine) {
-                        ws.keys[key_base + p] = key;
-                        atomicAdd(&sh_hist[key >> 21], 1u);
-                    }
+                    if (g == 0) s_key[j * WR + 16 * u + r] = key;
+                    if (mine) atomicAdd(&sh_hist[key >> 21], 1u);
                     if (want_pool) {
                         const uint32_t bk = max_over_8_lanes(key);
                         const int pblk = p0 + (r & 8);  // the 8-position pool block of lanes 4 / 12
-                        if (g == 0 && (r & 7) == 4 && pblk < n) {
-                            ws.bkeys[key_base / 8 + (pblk >> 3)] = bk;
-                            atomicAdd(&sh_bhist[bk >> 21], 1u);
+                        if (g == 0 && (r & 7) == 4) {
+                            s_bk[j * (WR / 8) + 2 * u + (r >> 3)] = pblk < n ? bk : 0u;
+                            if (pblk < n) atomicAdd(&sh_bhist[bk >> 21], 1u);
                         }
                     }
                 }
+                jd = j + 1;
+            }
+            if (jd > 0) {  // (uniform)
+                wave_lds_sync();
+                pend_k = ws.keys + key_base + p_tile + b_lo + WR * wid;
+                pend_b = ws.bkeys + (key_base + p_tile + b_lo + WR * wid) / 8;
+                pend_j = jd;
             }
         }
     }
+    if constexpr (!LP) write_run();
     if (cur >= 0) {
         __syncthreads();
         flush();
@@ -290,7 +342,7 @@ __device__ __forceinline__ void score_full_body(
 // Tile map and metadata from k_idx_prep.  The tile map and everything the first loads of a
 // tile need lead the arguments (preloaded into SGPRs at launch); ws supplies the output areas.
 template <int HI, bool MX, bool LP, bool SPLIT>
-__global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
+__global__ __launch_bounds__(kScoreNT) __attribute__((amdgpu_waves_per_eu(CSA2_SCAN_WGS_PER_CU))) void k_idx_score_full(
     const int32_t* tmap, QMeta* qmeta, const int64_t* __restrict__ kv_row0, const uint16_t* __restrict__ q_idx,
     const float* __restrict__ w, const void* __restrict__ k_idx, int grid_tiles, int sub_log2, int n_heads,
     const uint8_t* __restrict__ k_sc, int pool_blocks, IndexWs ws) {
@@ -302,7 +354,7 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_score_full(
 // lengths, rows and query count lead the arguments, so the first loads wait on nothing else.
 // fmap_out != 0: the filter pass runs next and reads its tile map from ws.fmap.
 template <int HI, bool MX, bool LP, bool SPLIT>
-__global__ __launch_bounds__(kScoreNT) void k_idx_score_full_self(
+__global__ __launch_bounds__(kScoreNT) __attribute__((amdgpu_waves_per_eu(CSA2_SCAN_WGS_PER_CU))) void k_idx_score_full_self(
     const int32_t* __restrict__ kv_len, const int64_t* __restrict__ kv_row0, int n_q, int32_t max_len,
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const void* __restrict__ k_idx, int grid_tiles,
     int sub_log2, int64_t cache_rows, int n_heads, const uint8_t* __restrict__ k_sc, int pool_blocks,

@@ -52,6 +52,20 @@ int csa2_attend_timed(const uint16_t* q, const uint8_t* codes, const uint8_t* sc
                       int32_t n_heads, float softmax_scale, float* out, void* ws, size_t ws_bytes,
                       void* stream, void* start_event, void* stop_event);
 
+/*
+ * csa2_stream_read_groups -- the number of workgroups (and sink words) of csa2_stream_read on the
+ * current device.
+ * csa2_stream_read -- not a step of the method: a plain streaming read of `bytes` bytes at src
+ * (device, 16-byte aligned, bytes a multiple of 16) with 16-byte loads spread over the whole
+ * chip, the reference for what this HBM delivers to a read-only kernel in the same run.  Each
+ * workgroup writes one word folded from what it read to sink (device uint32 [sink_words],
+ * sink_words >= csa2_stream_read_groups()).  The events (as above) record the kernel's own start
+ * and end.
+ */
+int csa2_stream_read_groups(void);
+int csa2_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream,
+                     void* start_event, void* stop_event);
+
 #ifdef __cplusplus
 }
 #endif

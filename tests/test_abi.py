@@ -162,6 +162,16 @@ def test_token_and_window_append_validation():
     assert win(n=0, x=None) == C.OK
 
 
+def test_stream_read_validation():
+    L = C.lib()
+    sink = ctypes.c_void_p(0x20000)
+    assert L.csa2_stream_read(None, 1 << 20, sink, 4096, None, None, None) == C.ERR_NULL
+    assert L.csa2_stream_read(FAKE, 1 << 20, None, 4096, None, None, None) == C.ERR_NULL
+    assert L.csa2_stream_read(ctypes.c_void_p(0x10008), 1 << 20, sink, 4096, None, None, None) == C.ERR_SHAPE
+    assert L.csa2_stream_read(FAKE, (1 << 20) + 4, sink, 4096, None, None, None) == C.ERR_SHAPE
+    assert L.csa2_stream_read(FAKE, 0, sink, 4096, None, None, None) == C.ERR_SHAPE
+
+
 def test_workspace_sizes():
     # Full: grows with the context bound; Reindex: with pool size only; Attend: with splits
     a = C.csa2_workspace_bytes(C.OP_INDEX_FULL, 8, 8 << 20, 1 << 20, 512, 2048)

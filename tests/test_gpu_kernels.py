@@ -628,3 +628,20 @@ def test_attend_dense_equivalence_all_positions():
         kt = kv[None, None].expand(1, 16, -1, -1)
         ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=1 / np.sqrt(128))[0, :, 0].numpy()
         assert np.abs(out[i] - ref).max() <= 2e-3 * np.abs(kv.numpy()).max()
+
+
+# ---------------------------------------------------------------- measurement read kernel
+@pytest.mark.parametrize("n_words", [4, 1 << 16, (1 << 22) + 12])
+def test_stream_read_covers_every_word_once(n_words):
+    """The read kernel folds every word it reads with XOR into one word per workgroup: the XOR of
+    the sink is the XOR of the whole buffer only if each word is read exactly once."""
+    g = np.random.default_rng(n_words)
+    x = g.integers(-2**31, 2**31, size=n_words, dtype=np.int64).astype(np.int32)
+    sink = torch.full((C.lib().csa2_stream_read_groups(),), 0, dtype=torch.int32, device=DEV)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in ev:
+        e.record()
+    C.csa2_stream_read(torch.from_numpy(x).to(DEV), sink, ev[0], ev[1])
+    torch.cuda.synchronize()
+    assert np.bitwise_xor.reduce(sink.cpu().numpy()) == np.bitwise_xor.reduce(x)
+    assert ev[0].elapsed_time(ev[1]) >= 0.0
