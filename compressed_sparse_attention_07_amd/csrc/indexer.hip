@@ -1180,7 +1180,7 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
                     constexpr bool S = decltype(split)::value;
                     return mx ? (n_heads <= 4 ? k_idx_score_full_self<4, true, true, S>
                                               : k_idx_score_full_self<8, true, false, S>)
-                              : (n_heads <= 4 ? k_idx_score_full_self<4, false, CSA2_SCAN_LP_BF16 != 0, S>
+                              : (n_heads <= 4 ? k_idx_score_full_self<4, false, false, S>
                                               : k_idx_score_full_self<8, false, false, S>);
                 };
                 auto kern = sub_log2 == 0 ? pick(std::false_type{}) : pick(std::true_type{});
@@ -1197,7 +1197,7 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
                 auto pick = [&](auto split) {
                     constexpr bool S = decltype(split)::value;
                     return mx ? (n_heads <= 4 ? k_idx_score_full<4, true, true, S> : k_idx_score_full<8, true, false, S>)
-                              : (n_heads <= 4 ? k_idx_score_full<4, false, CSA2_SCAN_LP_BF16 != 0, S>
+                              : (n_heads <= 4 ? k_idx_score_full<4, false, false, S>
                                               : k_idx_score_full<8, false, false, S>);
                 };
                 auto kern = sub_log2 == 0 ? pick(std::false_type{}) : pick(std::true_type{});

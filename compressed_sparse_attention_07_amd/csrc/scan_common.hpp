@@ -12,7 +12,6 @@ constexpr int kScoreNT = 256;
 // Scan-kernel shape (compile-time; the defaults are the tuned ones):
 //   CSA2_SCAN_TILE  positions per tile of the tile map,
 //   CSA2_SCAN_U     64-position steps per load batch (each lane has 2U 16-byte loads in flight),
-//   CSA2_SCAN_NT    streaming (slc) key loads,
 //   CSA2_SCAN_WGS_PER_CU  resident workgroups of the persistent scan per compute unit.
 #ifndef CSA2_SCAN_TILE
 #define CSA2_SCAN_TILE 4096
@@ -20,19 +19,12 @@ constexpr int kScoreNT = 256;
 #ifndef CSA2_SCAN_U
 #define CSA2_SCAN_U 8
 #endif
-#ifndef CSA2_SCAN_NT
-#define CSA2_SCAN_NT 0
-#endif
 #ifndef CSA2_SCAN_WGS_PER_CU
 #define CSA2_SCAN_WGS_PER_CU 4
 #endif
-//   CSA2_SCAN_U_LP  256-position steps per load batch in the lane-per-position layout,
-//   CSA2_SCAN_LP_BF16  bf16 keys also take the lane-per-position layout (MXFP4 keys always do).
+//   CSA2_SCAN_U_LP  256-position steps per load batch in the lane-per-position layout.
 #ifndef CSA2_SCAN_U_LP
 #define CSA2_SCAN_U_LP 4
-#endif
-#ifndef CSA2_SCAN_LP_BF16
-#define CSA2_SCAN_LP_BF16 0
 #endif
 constexpr int kFullTile = CSA2_SCAN_TILE;       // positions per Full-scan workgroup
 constexpr int kReindexTile = 512;               // pool positions (64 blocks) per Reindex workgroup
@@ -55,13 +47,8 @@ __device__ __forceinline__ BufRsrc tile_rsrc(const void* p, int bytes) {
 }
 
 __device__ __forceinline__ uint4 buf_ld16(BufRsrc rs, int voff, int soff) {
-#if CSA2_SCAN_NT
-    constexpr int aux = 2;  // slc: streaming
-#else
-    constexpr int aux = 0;
-#endif
     typedef int i32x4 __attribute__((ext_vector_type(4)));
-    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, aux);
+    const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
     return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
 }
 

@@ -21,7 +21,7 @@ namespace csa2 {
 // single workgroup.
 // MX: keys are MXFP4 (k_idx = code bytes [rows, 32], k_sc = E8M0 bytes [rows, 2]) instead of
 // bf16 (k_idx = [rows, 64] bf16, k_sc unused).
-// LP: the lane-per-position layout (QFragLP; at most 4 heads): a wave step covers 64
+// LP: the lane-per-position layout (QFragLP; MXFP4 keys, at most 4 heads): a wave step covers 64
 // positions with one score per lane, so the per-position epilogue (ReLU-weighted head sum,
 // key, stores, histogram atomics, block maximum) costs a quarter of the instructions of the
 // 16-position layout; the lane reads its own row (16-byte loads, 32 B per MXFP4 row).
@@ -48,7 +48,7 @@ __device__ __forceinline__ void score_full_body(
 
     const int t = threadIdx.x;
     const int lane = __lane_id();
-    const int wid = t / kWave;
+    const int wid = __builtin_amdgcn_readfirstlane(t / kWave);  // (uniform: scalar registers)
     const int g = lane >> 4, r = lane & 15;
     const bool want_pool = pool_blocks > 0;
     if constexpr (!SPLIT) sub_log2 = 0;
@@ -89,7 +89,7 @@ __device__ __forceinline__ void score_full_body(
         sh_hist[b] = 0u;
         sh_bhist[b] = 0u;
     }
-    static_assert(!LP || HI == 4, "the lane-per-position layout holds 4 heads");
+    static_assert(!LP || (HI == 4 && MX), "the lane-per-position layout: MXFP4 keys, 4 heads");
     int cur = -1;  // query whose counts the LDS histograms hold
     QMeta qm{};
     int64_t row0 = 0;
@@ -224,8 +224,9 @@ __device__ __forceinline__ void score_full_body(
                     const bool mine = p < n;
                     const uint32_t key = mine ? score_key(sc) : 0u;
                     // (non-temporal stores here: with 34-byte MXFP4 rows the key writes are an eighth
-                    // of the traffic, and streaming them past the caches measured 11 % faster; the
-                    // bf16 layout below measured slower with them)
+                    // of the traffic, and streaming them past the caches measured 11 % faster.  The
+                    // whole-line loads and staged key runs of the layout below measured slower here:
+                    // 52 -> 57 us at 1M x 8 queries, each of the two alone 61-63 us)
                     if (mine) {
                         __builtin_nontemporal_store(key, &ws.keys[key_base + p]);
                         atomicAdd(&sh_hist[key >> 21], 1u);
