@@ -207,7 +207,7 @@ struct RadixShared {
     uint32_t hist[kHistBins];
     int scan[16];
     int digit, above, inb;
-    uint32_t low_or;  // OR of the bucket's key bits below the current digit
+    uint32_t low_or;  // nonzero: some key of the bucket has a bit below the current digit
 };
 
 // Key-only threshold among m composites in LDS whose keys all lie in first-digit bucket d1:
@@ -243,7 +243,7 @@ __device__ KeyThr lds_key_threshold(const uint64_t* c, int m, int need, int d1, 
                 low |= key & ((1u << shift) - 1u);
             }
         }
-        if (low != 0u) atomicOr(&R.low_or, low);
+        if (__ballot(low != 0u) != 0ull && (t & (kWave - 1)) == 0) R.low_or = 1u;  // (one flag store per wave)
         __syncthreads();
         // when no key of the bucket has a bit below this digit, every key of the sub-bucket the
         // digit selects is the same key: a further pass could not split it (the ties at that

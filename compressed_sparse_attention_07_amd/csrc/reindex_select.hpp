@@ -71,7 +71,9 @@ __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __res
                         atomicAdd(&s_hist[hb][(kv[j] >> shift) & ((1u << w) - 1u)], 1u);
                         low |= kv[j] & ((1u << shift) - 1u);
                     }
-                if (low != 0u) atomicOr(&s_or[hb], low);
+                // only whether any key has such a bit matters: one flag store per wave (an atomic OR
+                // per holding thread serialised on one LDS word)
+                if (__ballot(low != 0u) != 0ull && (t & (kWave - 1)) == 0) s_or[hb] = 1u;
                 __syncthreads();
                 // no key of the bucket has a bit below this digit: every key of the sub-bucket
                 // the digit selects equals T, so a further pass could not split it
