@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_prefill_sample(
 // ----------------------------------------------------------------------------------------
 constexpr int kPcQ = 64;         // queries per workgroup: 16 per wave
 constexpr int kPcPos = 4096;     // positions per workgroup
-constexpr int kPcStage = 128;    // positions per LDS key stage (8 MFMA tiles)
+constexpr int kPcStage = 64;     // positions per LDS key stage (4 MFMA tiles; 128 measured slower: 2 workgroups per CU)
 constexpr int kPcRowB = 144;     // bytes per staged key row: 128 + 16, which spreads rows over the banks
 constexpr int kPcRing = 512;     // ring entries per wave (a tile adds at most 256)
 constexpr int kPcDW = 16;        // digits at and above the sampled one counted in LDS
@@ -448,67 +448,77 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_prefill_cand(
         ring_n = 0;
     };
 
-    // ---- key stages: thread t moves 64 bytes (row t / 2, half t % 2) ----
-    const int ld_row = t >> 1, ld_half = t & 1;
-    uint4 stg[4];
+    // ---- key stages: thread t moves kLdB bytes (part t % kLdParts of row t / kLdParts) ----
+    constexpr int kLdB = kPcStage * 128 / kScoreNT;  // bytes per thread per stage
+    constexpr int kLdParts = 128 / kLdB;             // threads per row
+    static_assert(kLdB % 16 == 0 && 128 % kLdB == 0 && kPcPos % kPcStage == 0, "stage shape");
+    const int ld_row = t / kLdParts, ld_part = t % kLdParts;
+    uint4 stg[kLdB / 16];
     auto load_stage = [&](int ps) {
         const int p = ps + ld_row;
-        const uint16_t* src = k_idx + (row0 + p) * 64 + 32 * ld_half;
+        const uint16_t* src = k_idx + (row0 + p) * 64 + (kLdB / 2) * ld_part;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kLdB / 16; ++j)
             stg[j] = p < p_end ? *reinterpret_cast<const uint4*>(src + 8 * j) : make_uint4(0, 0, 0, 0);
     };
     auto store_stage = [&](int buf) {
-        uint8_t* dst = sh_keys[buf] + ld_row * kPcRowB + 64 * ld_half;
+        uint8_t* dst = sh_keys[buf] + ld_row * kPcRowB + kLdB * ld_part;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(dst + 16 * j) = stg[j];
+        for (int j = 0; j < kLdB / 16; ++j) *reinterpret_cast<uint4*>(dst + 16 * j) = stg[j];
     };
-    // scores of one stage; ALL: every position of the stage is visible to the wave's queries
-    auto score_stage = [&](int buf, int ps, auto all_tag) {
+    // scores of one stage; ALL: every position of the stage is visible to the wave's queries.
+    // Tiles go in pairs: both tiles' MFMAs are issued before the first tile's epilogue, so the
+    // second tile's products run while the first one's scores are formed; the ring append is
+    // branch-free (a store under the kept lanes' mask).
+    auto tile_mfma = [&](const uint8_t* kb, int u, f32x4_t (&acc)[4]) {
+        const uint8_t* kr = kb + (16 * u + r) * kPcRowB + 16 * g;
+        const bf16x8_t b0 = as_bf16x8(*reinterpret_cast<const uint4*>(kr));
+        const bf16x8_t b1 = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 64));
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            f32x4_t a = {0.f, 0.f, 0.f, 0.f};
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][0], b0, a, 0, 0, 0);
+            a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][1], b1, a, 0, 0, 0);
+            acc[h] = a;
+        }
+    };
+    auto tile_epilogue = [&](const f32x4_t (&acc)[4], int ps, int u, auto all_tag) {
         constexpr bool ALL = decltype(all_tag)::value;
+        if (ring_n > kPcRing - 256) flush();  // wave-uniform
+        const int p = ps + 16 * u + r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float sc = 0.f;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], relu(acc[h][i]), sc);
+            const bool ok = ALL || p < nq[i];
+            // the sum starts from +0, so it is never -0: flip every bit of a negative
+            // score, only the sign bit of the others
+            const uint32_t sb = __float_as_uint(sc);
+            const uint32_t key = ok ? sb ^ ((uint32_t)((int32_t)sb >> 31) | 0x80000000u) : 0u;
+            const bool kept = ok && key >= tk[i];
+            const uint64_t m = __ballot(kept);
+            const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (kept) ring[ring_n + rank] = ((uint64_t)key << 32) | ((uint32_t)(4 * g + i) << 26) | (uint32_t)p;
+            ring_n += __popcll(m);
+            if constexpr (POOL) {
+                const uint32_t bk = max_over_8_lanes(key);  // lanes 4 / 12 of the row
+                const int pblk = ps + 16 * u + (r & 8);
+                if ((r & 7) == 4 && pblk < nq[i])
+                    ws.bkeys[sh_base[wq0 + 4 * g + i] / 8 + (pblk >> 3)] = bk;
+            }
+        }
+    };
+    auto score_stage = [&](int buf, int ps, auto all_tag) {
         const uint8_t* kb = sh_keys[buf];
-#pragma unroll 2
-        for (int u = 0; u < kPcStage / 16; ++u) {
-            if (ring_n > kPcRing - 256) flush();  // wave-uniform
-            const uint8_t* kr = kb + (16 * u + r) * kPcRowB + 16 * g;
-            const bf16x8_t b0 = as_bf16x8(*reinterpret_cast<const uint4*>(kr));
-            const bf16x8_t b1 = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 64));
-            f32x4_t acc[4];
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                f32x4_t a = {0.f, 0.f, 0.f, 0.f};
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][0], b0, a, 0, 0, 0);
-                a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][1], b1, a, 0, 0, 0);
-                acc[h] = a;
-            }
-            const int p = ps + 16 * u + r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float sc = 0.f;
-#pragma unroll
-                for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], relu(acc[h][i]), sc);
-                const bool ok = ALL || p < nq[i];
-                // the sum starts from +0, so it is never -0: flip every bit of a negative
-                // score, only the sign bit of the others
-                const uint32_t sb = __float_as_uint(sc);
-                const uint32_t key = ok ? sb ^ ((uint32_t)((int32_t)sb >> 31) | 0x80000000u) : 0u;
-                const bool kept = ok && key >= tk[i];
-                const uint64_t m = __ballot(kept);
-                if (m) {  // wave-uniform
-                    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    if (kept)
-                        ring[ring_n + rank] =
-                            ((uint64_t)key << 32) | ((uint32_t)(4 * g + i) << 26) | (uint32_t)p;
-                    ring_n += __popcll(m);
-                }
-                if constexpr (POOL) {
-                    const uint32_t bk = max_over_8_lanes(key);  // lanes 4 / 12 of the row
-                    const int pblk = ps + 16 * u + (r & 8);
-                    if ((r & 7) == 4 && pblk < nq[i])
-                        ws.bkeys[sh_base[wq0 + 4 * g + i] / 8 + (pblk >> 3)] = bk;
-                }
-            }
+        static_assert((kPcStage / 16) % 2 == 0, "tiles in pairs");
+        for (int u = 0; u < kPcStage / 16; u += 2) {
+            f32x4_t acc0[4], acc1[4];
+            tile_mfma(kb, u, acc0);
+            tile_mfma(kb, u + 1, acc1);
+            tile_epilogue(acc0, ps, u, all_tag);
+            tile_epilogue(acc1, ps, u + 1, all_tag);
         }
     };
 
