@@ -7,12 +7,12 @@
 //   section XI  - cached FP4 values are dequantised before attention (no FP4 matmul).
 // The cached latent is both key and value; 16 query heads share it.
 //
-// One workgroup (8 waves) per query.  At decode sizes this kernel is latency-bound (a few
-// hundred KB per launch), so it is built to put every memory access of the query in flight
-// at once and to keep the per-entry instruction count low:
+// One workgroup (W waves) per query; used for calls with more queries than a decode batch (a
+// prefill chunk's tokens), where the queries fill the chip by themselves.  It puts every
+// memory access of a round in flight at once and keeps the per-entry instruction count low:
 //   * work goes in rounds; in one round wave w owns FP4 blocks (16 entries each)
-//     32R + 4w .. 32R + 4w + 3 and window block 8R + w.  Top-512 with a 128 window is one
-//     round.  All gathers of a round are issued before anything waits on them.
+//     4WR + 4w .. 4WR + 4w + 3 and window block WR + w.  All gathers of a round are issued
+//     before anything waits on them.
 //   * FP4 entries are dequantised to f16 (hardware E2M1 -> f16, then one packed f16 multiply
 //     by the E4M3 group scale: both factors and the product are exact in f16) and contracted
 //     on v_mfma_f32_16x16x32_f16; window entries stay bf16 (v_mfma_f32_16x16x32_bf16).
@@ -25,7 +25,7 @@
 //     4 x 16 sub-block the MFMA A operand needs.  P is f16 for FP4 entries (one MFMA) and a
 //     bf16 hi + lo pair for window entries (two MFMAs, ~16 mantissa bits).
 //   * waves merge once at the end: (max, sum, O) of each wave go through LDS and each
-//     thread finishes four outputs.
+//     thread finishes the outputs of one head's 128 / (4 W) dimensions.
 // MFMA 16x16x32 lane layout (checked on gfx950): lane l supplies row/column l%16 of A/B and
 // eight K elements chosen by the lane group l/16 (the same K set for A and B); the
 // accumulator of lane l holds rows 4*(l/16)+i, column l%16.  16x16x16: four K elements.
@@ -44,8 +44,11 @@
 
 namespace csa2 {
 
-constexpr int kAttWaves = 8;
-constexpr int kAttNT = kAttWaves * 64;
+// waves per workgroup: 4, at most 256 VGPRs each (two waves per SIMD), so two queries share a
+// compute unit (8 waves with every VGPR they ask for kept one query per unit: 123 -> 92 us for a
+// 4,096-token prefill chunk)
+constexpr int kAttWaves = 4;
+constexpr int kAttWavesPerEu = 2;
 constexpr int kRB = 4;                       // FP4 blocks per wave per round
 static_assert(kNH * kOStride * 4 <= kTileB, "a wave's merge rows fit in its tile");
 
@@ -400,24 +403,32 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
             *reinterpret_cast<f32x4*>(&ob[r * kOStride + 16 * db + 4 * g]) = o[db];
     }
     __syncthreads();
-    constexpr int kTpH = 32;          // threads per head, four dimensions each
+    constexpr int kTpH = WAVES * kWave / kNH;  // threads per head
+    constexpr int kDv = kD / kTpH / 4;         // four-dimension vectors per thread
+    static_assert(kTpH * kNH == WAVES * kWave && kDv >= 1, "merge thread layout");
     const int h = t / kTpH;
-    const int d0 = 4 * (t % kTpH);
-    if (h < n_heads && t < kNH * kTpH) {
+    const int d0 = 4 * kDv * (t % kTpH);
+    if (h < n_heads) {
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) M = fmaxf(M, s_m[w][h]);
         float L = 0.f;
-        f32x4 O = {0.f, 0.f, 0.f, 0.f};
+        f32x4 O[kDv];
+#pragma unroll
+        for (int v = 0; v < kDv; ++v) O[v] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) {
             const float f = (s_m[w][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_m[w][h] - M);
             L = fmaf(s_l[w][h], f, L);
-            O += f * *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds.tile + w * kTileB) +
-                                                    h * kOStride + d0);
+            const float* ob = reinterpret_cast<const float*>(lds.tile + w * kTileB) + h * kOStride + d0;
+#pragma unroll
+            for (int v = 0; v < kDv; ++v) O[v] += f * *reinterpret_cast<const f32x4*>(ob + 4 * v);
         }
-        const f32x4 res = L > 0.f ? O / L : f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(out + ((int64_t)i * n_heads + h) * kD + d0) = res;
+#pragma unroll
+        for (int v = 0; v < kDv; ++v) {
+            const f32x4 res = L > 0.f ? O[v] / L : f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4*>(out + ((int64_t)i * n_heads + h) * kD + d0 + 4 * v) = res;
+        }
     }
     // the new window entry into its store row, after every read of the store by this query
     // (wave 0, two channels per lane); whether or not the replay bound lets it be attended
@@ -436,20 +447,22 @@ __device__ __forceinline__ void attend_query(int i, const AttendArgs& a, const i
 // The arguments one by one (not the AttendArgs block), those of the first level of loads first:
 // the leading ones are preloaded into SGPRs at launch, so those loads need no scalar load of
 // the argument block before them.
-template <bool kFp4, bool kWin, bool kW8>
-__global__ __launch_bounds__(kAttNT) void k_attend(const int32_t* kv_len, const int64_t* kv_row0,
+template <bool kFp4, bool kWin, bool kW8, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(kAttWavesPerEu))) void k_attend(
+    const int32_t* kv_len, const int64_t* kv_row0,
                                                    const int64_t* swa_row0, const int64_t* replay, const int32_t* idx,
                                                    const uint16_t* q, int top_k, int n_heads, int32_t max_len,
                                                    int64_t cache_rows, const uint8_t* codes, const uint8_t* scales,
                                                    const void* swa, int swa_cap, int64_t swa_rows, int window,
                                                    float scale_log2, float* out, const uint16_t* win_new) {
-    __shared__ __align__(16) uint8_t s_tile[kAttWaves * kTileB];
-    __shared__ float s_m[kAttWaves][kNH], s_l[kAttWaves][kNH];
+    __shared__ __align__(16) uint8_t s_tile[W * kTileB];
+    __shared__ float s_m[W][kNH], s_l[W][kNH];
     const AttendArgs a{q,        codes,   scales,   kv_row0, kv_len, max_len, cache_rows, idx,   top_k,
                        swa,      swa_row0, swa_cap, swa_rows, window, replay, n_heads,   scale_log2, out,
                        win_new};
     const int i = (int)blockIdx.x;
-    attend_query<kFp4, kWin, kW8>(i, a, idx + (int64_t)i * top_k, AttendLds{s_tile, s_m, s_l}, attend_pre<kWin>(i, a));
+    attend_query<kFp4, kWin, kW8, W>(i, a, idx + (int64_t)i * top_k, AttendLds{s_tile, s_m, s_l},
+                                     attend_pre<kWin>(i, a));
 }
 
 hipError_t launch_attend_dec(const uint16_t* q, const uint8_t* codes, const uint8_t* scales, const int64_t* kv_row0,
@@ -475,22 +488,23 @@ hipError_t launch_attend(const uint16_t* q, const uint8_t* codes, const uint8_t*
                                  win_new, part, ctrl, stream, ev_start, ev_stop);
     const float scale_log2 = softmax_scale * 1.4426950408889634f;
     const bool fp4 = top_k > 0, win = window > 0 && swa_rows > 0;
-    using K = decltype(&k_attend<true, true, false>);
+    constexpr int W = kAttWaves;
+    using K = decltype(&k_attend<true, true, false, W>);
     K kern;
     if (window_fp8)
-        kern = fp4 ? (win ? k_attend<true, true, true> : k_attend<true, false, true>)
-                   : (win ? k_attend<false, true, true> : k_attend<false, false, true>);
+        kern = fp4 ? (win ? k_attend<true, true, true, W> : k_attend<true, false, true, W>)
+                   : (win ? k_attend<false, true, true, W> : k_attend<false, false, true, W>);
     else
-        kern = fp4 ? (win ? k_attend<true, true, false> : k_attend<true, false, false>)
-                   : (win ? k_attend<false, true, false> : k_attend<false, false, false>);
+        kern = fp4 ? (win ? k_attend<true, true, false, W> : k_attend<true, false, false, W>)
+                   : (win ? k_attend<false, true, false, W> : k_attend<false, false, false, W>);
     const dim3 grid((unsigned)n_q);
     // ev_start / ev_stop (may be null): the kernel's own start and end, recorded by its launch
     if (ev_start != nullptr || ev_stop != nullptr)
-        hipExtLaunchKernelGGL(kern, grid, dim3(kAttNT), 0, stream, ev_start, ev_stop, 0, kv_len, kv_row0, swa_row0,
+        hipExtLaunchKernelGGL(kern, grid, dim3(W * 64), 0, stream, ev_start, ev_stop, 0, kv_len, kv_row0, swa_row0,
                               replay, idx, q, top_k, n_heads, max_len, cache_rows, codes, scales, swa, swa_cap, swa_rows,
                               window, scale_log2, out, win_new);
     else
-        hipLaunchKernelGGL(kern, grid, dim3(kAttNT), 0, stream, kv_len, kv_row0, swa_row0, replay, idx, q, top_k,
+        hipLaunchKernelGGL(kern, grid, dim3(W * 64), 0, stream, kv_len, kv_row0, swa_row0, replay, idx, q, top_k,
                            n_heads, max_len, cache_rows, codes, scales, swa, swa_cap, swa_rows, window, scale_log2, out,
                            win_new);
     return hipGetLastError();
