@@ -141,7 +141,10 @@ __global__ __launch_bounds__(kPrepNT) void k_idx_prep(const int64_t* __restrict_
 // heads (ReLU, weights) into the score and its order-preserving key.
 // The chunk's selection takes two passes over the scores:
 //   sample     - k_idx_prefill_sample scores one 16-position tile in kPfStride and counts the
-//                keys' first digits per query (LDS histogram, two 16-bit counters per word);
+//                keys' first digits per query (LDS histogram: the 1,024 digits of
+//                non-negative scores as two 16-bit counters per word, and one word that counts
+//                every negative score as digit 0, the lowest: a threshold that falls among
+//                negative scores then keeps every position, never too few);
 //                k_idx_prefill_thresh turns the counts into the query's sampled threshold
 //                digit: the digit holding the K-th largest key of the sample;
 //   candidates - k_idx_prefill_cand scores every position and keeps those whose first digit is
@@ -171,7 +174,8 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_prefill_sample(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, int n_px, int n_qg,
     IndexWs ws) {
-    __shared__ __align__(16) uint32_t sh_hist[kPfQ][kHistBins / 2];
+    constexpr int kSw = kHistBins / 4;  // words of the non-negative digits; word kSw counts the rest
+    __shared__ __align__(16) uint32_t sh_hist[kPfQ][kSw + 4];
     __shared__ int sh_n[kPfQ];
     const int t = threadIdx.x;
     const int lane = __lane_id();
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_prefill_sample(
 #pragma unroll
     for (int k = 0; k < kPfQ; ++k) n_max = max(n_max, sh_n[k]);
     if (p_wg >= n_max) return;  // uniform: nothing visible in this position chunk
-    for (int k = t; k < kPfQ * kHistBins / 8; k += kScoreNT)
+    for (int k = t; k < kPfQ * (kSw + 4) / 4; k += kScoreNT)
         reinterpret_cast<uint4*>(&sh_hist[0][0])[k] = make_uint4(0, 0, 0, 0);
     // A fragments: query q0 + r, head h, channels 32s + 8g .. +8 ; weights of queries q0 + 4g + i
     bf16x8_t qa[4][2];
@@ -263,15 +267,16 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_prefill_sample(
                 for (int h = 0; h < 4; ++h) sc = fmaf(wq[i][h], relu(acc[h][i]), sc);
                 if (ALL || p < nq[i]) {
                     // the sum starts from +0, so it is never -0: flip every bit of a negative
-                    // score, only the sign bit of the others.  First digit = key >> 21; two
-                    // 16-bit counters per word: digit d and d + 1024 share word d & 1023 (the
-                    // key's top bit picks the half: an increment of 1 or 1 << 16), so
-                    // neighbouring digits, which nearby scores often take, update different words
+                    // score, only the sign bit of the others.  First digit = key >> 21; for a
+                    // non-negative score, digits 1024 + j and 1536 + j share word j (the
+                    // increment is 1 or 1 << 16), so neighbouring digits, which nearby scores
+                    // often take, update different words; a negative score counts in word kSw
                     const uint32_t sb = __float_as_uint(sc);
                     const uint32_t key = sb ^ ((uint32_t)((int32_t)sb >> 31) | 0x80000000u);
-                    const uint32_t word = (key >> 21) & 0x3ffu;
-                    const uint32_t half = key >> 31;
-                    atomicAdd(&sh_hist[4 * g + i][word], 1u + half * 0xffffu);
+                    const bool pos = (key >> 31) != 0u;
+                    const uint32_t dd = (key >> 21) & 0x3ffu;  // digit - 1024 (non-negative scores)
+                    const uint32_t word = pos ? (dd & (kSw - 1)) : (uint32_t)kSw;
+                    atomicAdd(&sh_hist[4 * g + i][word], pos ? 1u + (dd / kSw) * 0xffffu : 1u);
                 }
             }
         }
@@ -287,17 +292,18 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_prefill_sample(
             score_batch(kb, base, std::false_type{});
     }
     __syncthreads();
-    for (int k = t; k < kPfQ * kHistBins / 8; k += kScoreNT) {
-        const int ql = k / (kHistBins / 8);
-        const uint4 v = reinterpret_cast<const uint4*>(&sh_hist[0][0])[k];
-        if ((v.x | v.y | v.z | v.w) == 0u || q0 + ql >= n_q) continue;
+    // counts -> the queries' global histograms: word j's halves are digits 1024 + j and
+    // 1536 + j, word kSw is digit 0
+    for (int k = t; k < kPfQ * (kSw + 1); k += kScoreNT) {
+        const int ql = k / (kSw + 1), j = k % (kSw + 1);
+        const uint32_t c = sh_hist[ql][j];
+        if (c == 0u || q0 + ql >= n_q) continue;
         uint32_t* gh = ws.hist + (int64_t)(q0 + ql) * 2 * kHistBins;
-        const int wd = 4 * (k % (kHistBins / 8));
-        const uint32_t c[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (c[j] & 0xffffu) atomicAdd(&gh[wd + j], c[j] & 0xffffu);
-            if (c[j] >> 16) atomicAdd(&gh[wd + j + kHistBins / 2], c[j] >> 16);
+        if (j == kSw) {
+            atomicAdd(&gh[0], c);
+        } else {
+            if (c & 0xffffu) atomicAdd(&gh[kHistBins / 2 + j], c & 0xffffu);
+            if (c >> 16) atomicAdd(&gh[kHistBins / 2 + kSw + j], c >> 16);
         }
     }
 }
