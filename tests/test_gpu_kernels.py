@@ -397,6 +397,22 @@ def test_index_prefill_fractional_and_negative_weights():
         assert np.array_equal(pool_m[t], rp), t
 
 
+def test_index_prefill_all_negative_weights():
+    # every score <= 0: the sample's threshold falls among negative scores, which its histogram
+    # counts as digit 0, so every visible position becomes a candidate; still bit-exact
+    C_, T = 9000, 48
+    case = SharedIndexCase(W_T + 84, C_ + T, C_ + 1 + np.arange(T), n_heads=4)
+    m = np.random.default_rng(84).integers(1, 257, size=case.w.shape)
+    case.w = (-m / 64.0).astype(np.float32)
+    case.w_dev = torch.from_numpy(case.w).to(DEV)
+    idx_m, pool_m, _ = case.run_full(512, 300, shared_kv=1)
+    idx_m, pool_m = idx_m.cpu().numpy(), pool_m.cpu().numpy()
+    for t in range(T):
+        ri, rp = case.oracle_full(t, 512, 300)
+        assert np.array_equal(idx_m[t], ri), t
+        assert np.array_equal(pool_m[t], rp), t
+
+
 def test_index_reindex_many_queries_whole_pool_per_workgroup():
     # >= 512 queries with 2,048-block pools: each Reindex workgroup scores a whole pool and adds
     # its counts to the query's histogram once; every token checked against the oracle
