@@ -1048,7 +1048,7 @@ __global__ __launch_bounds__(NT) void k_idx_select_cands(QMeta* qmeta, uint32_t*
 // cpw: chunks per workgroup (a divisor of the chunk count).  Many queries (a prefill chunk's
 // tokens): each workgroup scores cpw consecutive chunks of its query and adds its first-digit
 // counts to the query's histogram once, which divides the global atomics by cpw.
-template <int HI, bool MX>
+template <int HI, bool MX, bool LP>
 __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     const int32_t* __restrict__ pool, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
     const int64_t* __restrict__ kv_row0, const int32_t* __restrict__ kv_len, int pool_blocks, int n_heads, int cpw,
@@ -1067,12 +1067,22 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     const int n_elem = pool_blocks * 8;
 
     for (int b = t; b < kHistBins; b += kScoreNT) sh_hist[b] = 0u;
-    QFrag qf;
-    load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
-    __syncthreads();
-    reindex_score_chunks<HI, MX, kScoreNT / kWave>(grp * cpw, (grp + 1) * cpw, n, row0,
-                                                          pool + (int64_t)i * pool_blocks, pool_blocks, qf, k_idx,
-                                                          k_sc, ws.keys + (int64_t)i * n_elem, sh_hist);
+    if constexpr (LP) {  // bf16 keys, at most 4 heads: one position per lane
+        static_assert(!MX && HI == 4, "the lane-per-position form takes bf16 keys and 4 heads");
+        QFragLP qf;
+        load_qfrag_lp(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
+        __syncthreads();
+        reindex_score_chunks_lp<kScoreNT / kWave>(grp * cpw, (grp + 1) * cpw, n, row0,
+                                                  pool + (int64_t)i * pool_blocks, pool_blocks, qf, k_idx,
+                                                  ws.keys + (int64_t)i * n_elem, sh_hist);
+    } else {
+        QFrag qf;
+        load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
+        __syncthreads();
+        reindex_score_chunks<HI, MX, kScoreNT / kWave>(grp * cpw, (grp + 1) * cpw, n, row0,
+                                                       pool + (int64_t)i * pool_blocks, pool_blocks, qf, k_idx,
+                                                       k_sc, ws.keys + (int64_t)i * n_elem, sh_hist);
+    }
     __syncthreads();
     uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
     for (int b = t; b < kHistBins; b += kScoreNT) {
@@ -1274,8 +1284,11 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
     // flush per query instead of one per chunk
     const int cpw = (n_q >= 512 && chunks % 32 == 0) ? 32 : 1;
     const dim3 grid((unsigned)(chunks / cpw * n_q));  // (query, chunk group) items, see reindex_item
-    auto kern = mx ? (n_heads <= 4 ? k_idx_reindex_score<4, true> : k_idx_reindex_score<8, true>)
-                   : (n_heads <= 4 ? k_idx_reindex_score<4, false> : k_idx_reindex_score<8, false>);
+    // a prefill chunk's whole pools, bf16 keys, at most 4 heads: the lane-per-position form
+    const bool lp = cpw == 32 && !mx && n_heads <= 4;
+    auto kern = mx ? (n_heads <= 4 ? k_idx_reindex_score<4, true, false> : k_idx_reindex_score<8, true, false>)
+                   : lp ? k_idx_reindex_score<4, false, true>
+                        : (n_heads <= 4 ? k_idx_reindex_score<4, false, false> : k_idx_reindex_score<8, false, false>);
     // ev_start / ev_stop, ev_sel_start / ev_sel_stop (may be null): the scoring kernel's and the
     // selection kernel's own start and end, recorded by their launches
     if (ev_start != nullptr || ev_stop != nullptr)

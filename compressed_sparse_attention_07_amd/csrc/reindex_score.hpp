@@ -94,4 +94,61 @@ __device__ __forceinline__ void reindex_score_chunks(int c0, int c1, int n, int6
     }
 }
 
+// The lane-per-position form (bf16 keys, at most 4 heads; QFragLP, as the decode scan's MXFP4
+// layout): a wave step covers 8 pool slots = 64 positions, lane l taking row l % 8 of slot
+// l / 8; the lane reads its row's 128 bytes (8 loads) and eight block-diagonal MFMAs leave the
+// four head dot products of its own position in its accumulator, so the per-position epilogue
+// (ReLU-weighted sum, key, store, histogram) runs once per position instead of in one lane of
+// four.  Wave wid takes steps 2 wid, 2 wid + 1 of each chunk (both steps' loads in flight).
+template <int NW>
+__device__ __forceinline__ void reindex_score_chunks_lp(int c0, int c1, int n, int64_t row0,
+                                                        const int32_t* __restrict__ qpool, int pool_blocks,
+                                                        const QFragLP& qf, const void* __restrict__ k_idx,
+                                                        uint32_t* __restrict__ keys, uint32_t* sh_hist) {
+    const int lane = __lane_id();
+    const int wid = threadIdx.x / kWave;
+    constexpr int kSteps = kReindexTile / 64 / NW;  // 64-position steps per wave per chunk
+    static_assert(kSteps * 64 * NW == kReindexTile, "whole steps per chunk");
+    for (int chunk = c0; chunk < c1; ++chunk) {
+        int slot[kSteps], blk[kSteps];
+        uint4 kr[kSteps][8];
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) {
+            slot[j] = chunk * (kReindexTile / 8) + 8 * (kSteps * wid + j) + (lane >> 3);
+            blk[j] = slot[j] < pool_blocks ? qpool[slot[j]] : -1;
+        }
+        if (n > 0) {
+            // absent rows read the sequence's first row (n > 0) and are masked below
+#pragma unroll
+            for (int j = 0; j < kSteps; ++j) {
+                const int64_t p = (int64_t)blk[j] * 8 + (lane & 7);
+                const bool ok = blk[j] >= 0 && p < n;
+                const uint4* row = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k_idx) +
+                                                                  (row0 + (ok ? p : 0)) * 64);
+#pragma unroll
+                for (int s2 = 0; s2 < 8; ++s2) kr[j][s2] = row[s2];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kSteps; ++j) {
+            const int64_t p = (int64_t)blk[j] * 8 + (lane & 7);
+            const bool ok = n > 0 && blk[j] >= 0 && p < n;
+            float sc = 0.f;
+            if (n > 0) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < 8; ++s2)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.a[s2], as_bf16x8(kr[j][s2]), acc, 0, 0, 0);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) sc = fmaf(qf.w[h], relu(acc[h]), sc);
+            }
+            const uint32_t key = ok ? score_key(sc) : 0u;
+            if (slot[j] < pool_blocks) {
+                keys[slot[j] * 8 + (lane & 7)] = key;
+                if (key) atomicAdd(&sh_hist[key >> 21], 1u);
+            }
+        }
+    }
+}
+
 }  // namespace csa2
