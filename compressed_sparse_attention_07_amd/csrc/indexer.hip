@@ -1067,14 +1067,14 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     const int n_elem = pool_blocks * 8;
 
     for (int b = t; b < kHistBins; b += kScoreNT) sh_hist[b] = 0u;
-    if constexpr (LP) {  // bf16 keys, at most 4 heads: one position per lane
-        static_assert(!MX && HI == 4, "the lane-per-position form takes bf16 keys and 4 heads");
+    if constexpr (LP) {  // at most 4 heads: one position per lane
+        static_assert(HI == 4, "the lane-per-position form takes at most 4 heads");
         QFragLP qf;
         load_qfrag_lp(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
         __syncthreads();
-        reindex_score_chunks_lp<kScoreNT / kWave>(grp * cpw, (grp + 1) * cpw, n, row0,
-                                                  pool + (int64_t)i * pool_blocks, pool_blocks, qf, k_idx,
-                                                  ws.keys + (int64_t)i * n_elem, sh_hist);
+        reindex_score_chunks_lp<MX, kScoreNT / kWave>(grp * cpw, (grp + 1) * cpw, n, row0,
+                                                      pool + (int64_t)i * pool_blocks, pool_blocks, qf, k_idx, k_sc,
+                                                      ws.keys + (int64_t)i * n_elem, sh_hist);
     } else {
         QFrag qf;
         load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
@@ -1284,11 +1284,12 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
     // flush per query instead of one per chunk
     const int cpw = (n_q >= 512 && chunks % 32 == 0) ? 32 : 1;
     const dim3 grid((unsigned)(chunks / cpw * n_q));  // (query, chunk group) items, see reindex_item
-    // bf16 keys, at most 4 heads, and a prefill chunk's whole pools or a small decode batch: the
+    // at most 4 heads, and a prefill chunk's whole pools or a small decode batch: the
     // lane-per-position form (a lane's rows need one block id per 64 positions, where the 16-position
     // form waits on 8: at 8 queries 5.6 -> 5.0 us; at 32, where the loads set the time, 14.4 -> 14.7)
-    const bool lp = !mx && n_heads <= 4 && (cpw == 32 || n_q <= 16);
-    auto kern = mx ? (n_heads <= 4 ? k_idx_reindex_score<4, true, false> : k_idx_reindex_score<8, true, false>)
+    const bool lp = n_heads <= 4 && (cpw == 32 || n_q <= 16);
+    auto kern = mx ? (lp ? k_idx_reindex_score<4, true, true>
+                         : (n_heads <= 4 ? k_idx_reindex_score<4, true, false> : k_idx_reindex_score<8, true, false>))
                    : lp ? k_idx_reindex_score<4, false, true>
                         : (n_heads <= 4 ? k_idx_reindex_score<4, false, false> : k_idx_reindex_score<8, false, false>);
     // ev_start / ev_stop, ev_sel_start / ev_sel_stop (may be null): the scoring kernel's and the

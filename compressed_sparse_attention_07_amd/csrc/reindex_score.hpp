@@ -94,24 +94,28 @@ __device__ __forceinline__ void reindex_score_chunks(int c0, int c1, int n, int6
     }
 }
 
-// The lane-per-position form (bf16 keys, at most 4 heads; QFragLP, as the decode scan's MXFP4
-// layout): a wave step covers 8 pool slots = 64 positions, lane l taking row l % 8 of slot
-// l / 8; the lane reads its row's 128 bytes (8 loads) and eight block-diagonal MFMAs leave the
-// four head dot products of its own position in its accumulator, so the per-position epilogue
-// (ReLU-weighted sum, key, store, histogram) runs once per position instead of in one lane of
-// four.  Wave wid takes steps 2 wid, 2 wid + 1 of each chunk (both steps' loads in flight).
-template <int NW>
+// The lane-per-position form (at most 4 heads; QFragLP, as the decode scan's MXFP4 layout): a
+// wave step covers 8 pool slots = 64 positions, lane l taking row l % 8 of slot l / 8; the lane
+// reads its own row (128 bytes of bf16 in 8 loads, or 32 MXFP4 code bytes in 2 and their 2
+// scale bytes) and eight block-diagonal MFMAs leave the four head dot products of its position
+// in its accumulator, so the per-position epilogue (ReLU-weighted sum, key, store, histogram)
+// runs once per position instead of in one lane of four.  Wave wid takes steps 2 wid, 2 wid + 1
+// of each chunk (both steps' loads in flight).
+template <bool MX, int NW>
 __device__ __forceinline__ void reindex_score_chunks_lp(int c0, int c1, int n, int64_t row0,
                                                         const int32_t* __restrict__ qpool, int pool_blocks,
                                                         const QFragLP& qf, const void* __restrict__ k_idx,
-                                                        uint32_t* __restrict__ keys, uint32_t* sh_hist) {
+                                                        const uint8_t* __restrict__ k_sc, uint32_t* __restrict__ keys,
+                                                        uint32_t* sh_hist) {
     const int lane = __lane_id();
     const int wid = threadIdx.x / kWave;
     constexpr int kSteps = kReindexTile / 64 / NW;  // 64-position steps per wave per chunk
     static_assert(kSteps * 64 * NW == kReindexTile, "whole steps per chunk");
     for (int chunk = c0; chunk < c1; ++chunk) {
+        constexpr int kLd = MX ? 2 : 8;  // 16-byte loads per row
         int slot[kSteps], blk[kSteps];
-        uint4 kr[kSteps][8];
+        uint4 kr[kSteps][kLd];
+        uint32_t ks[kSteps];
 #pragma unroll
         for (int j = 0; j < kSteps; ++j) {
             slot[j] = chunk * (kReindexTile / 8) + 8 * (kSteps * wid + j) + (lane >> 3);
@@ -123,10 +127,11 @@ __device__ __forceinline__ void reindex_score_chunks_lp(int c0, int c1, int n, i
             for (int j = 0; j < kSteps; ++j) {
                 const int64_t p = (int64_t)blk[j] * 8 + (lane & 7);
                 const bool ok = blk[j] >= 0 && p < n;
-                const uint4* row = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k_idx) +
-                                                                  (row0 + (ok ? p : 0)) * 64);
+                const int64_t kr_row = row0 + (ok ? p : 0);
+                const uint4* row = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(k_idx) + kr_row * 16 * kLd);
 #pragma unroll
-                for (int s2 = 0; s2 < 8; ++s2) kr[j][s2] = row[s2];
+                for (int s2 = 0; s2 < kLd; ++s2) kr[j][s2] = row[s2];
+                if constexpr (MX) ks[j] = *reinterpret_cast<const uint16_t*>(k_sc + kr_row * 2);
             }
         }
 #pragma unroll
@@ -137,8 +142,17 @@ __device__ __forceinline__ void reindex_score_chunks_lp(int c0, int c1, int n, i
             if (n > 0) {
                 f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s2 = 0; s2 < 8; ++s2)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.a[s2], as_bf16x8(kr[j][s2]), acc, 0, 0, 0);
+                for (int s2 = 0; s2 < 8; ++s2) {
+                    uint4 kf;
+                    if constexpr (MX) {  // k-step s2 lies in scale block s2 / 4
+                        const uint4& c = kr[j][s2 >> 2];
+                        const uint32_t dw = (s2 & 3) == 0 ? c.x : (s2 & 3) == 1 ? c.y : (s2 & 3) == 2 ? c.z : c.w;
+                        kf = mx_frag(dw, s2 < 4 ? (ks[j] & 0xffu) : (ks[j] >> 8));
+                    } else {
+                        kf = kr[j][s2];
+                    }
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf.a[s2], as_bf16x8(kf), acc, 0, 0, 0);
+                }
 #pragma unroll
                 for (int h = 0; h < 4; ++h) sc = fmaf(qf.w[h], relu(acc[h]), sc);
             }
