@@ -338,7 +338,7 @@ __host__ __device__ __forceinline__ int pc_items_per_xcd(int n_px, int n_qg) {
 }
 
 template <bool POOL>
-__global__ __launch_bounds__(kScoreNT) void k_idx_prefill_cand(
+__global__ __launch_bounds__(kScoreNT) __attribute__((amdgpu_waves_per_eu(4))) void k_idx_prefill_cand(
     const uint16_t* __restrict__ q_idx, const float* __restrict__ w, const uint16_t* __restrict__ k_idx,
     const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, int n_px, int n_qg,
     IndexWs ws) {
@@ -473,9 +473,9 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_prefill_cand(
         for (int j = 0; j < kLdB / 16; ++j) *reinterpret_cast<uint4*>(dst + 16 * j) = stg[j];
     };
     // scores of one stage; ALL: every position of the stage is visible to the wave's queries.
-    // Tiles go in pairs: both tiles' MFMAs are issued before the first tile's epilogue, so the
-    // second tile's products run while the first one's scores are formed; the ring append is
-    // branch-free (a store under the kept lanes' mask).
+    // The ring append is branch-free (a store under the kept lanes' mask).  One tile at a time
+    // keeps the kernel within 128 VGPRs, four waves per SIMD: tiles in pairs (the second tile's
+    // MFMAs issued before the first one's epilogue) needed 146 and measured 9 % slower.
     auto tile_mfma = [&](const uint8_t* kb, int u, f32x4_t (&acc)[4]) {
         const uint8_t* kr = kb + (16 * u + r) * kPcRowB + 16 * g;
         const bf16x8_t b0 = as_bf16x8(*reinterpret_cast<const uint4*>(kr));
@@ -518,13 +518,10 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_prefill_cand(
     };
     auto score_stage = [&](int buf, int ps, auto all_tag) {
         const uint8_t* kb = sh_keys[buf];
-        static_assert((kPcStage / 16) % 2 == 0, "tiles in pairs");
-        for (int u = 0; u < kPcStage / 16; u += 2) {
-            f32x4_t acc0[4], acc1[4];
-            tile_mfma(kb, u, acc0);
-            tile_mfma(kb, u + 1, acc1);
-            tile_epilogue(acc0, ps, u, all_tag);
-            tile_epilogue(acc1, ps, u + 1, all_tag);
+        for (int u = 0; u < kPcStage / 16; ++u) {
+            f32x4_t acc[4];
+            tile_mfma(kb, u, acc);
+            tile_epilogue(acc, ps, u, all_tag);
         }
     };
 
