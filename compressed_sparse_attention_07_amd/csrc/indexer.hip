@@ -784,19 +784,24 @@ struct CompositeList {
 
 constexpr int kSelNT = 1024;  // threads of the per-query selection workgroups
 constexpr int kSelNTMany = 512, kSortCapMany = 2048;  // the same for a prefill chunk's many queries
+// A prefill chunk's selections of at most kSelMaxMany entries (top_k, and the pool list's size
+// when there is one) size their output buffers for that: 48 KB of LDS, three workgroups per
+// compute unit instead of two (kMaxSelect: 73 KB).
+constexpr int kSelMaxMany = 1024;
 
-template <int CAP>
+// MS: the largest selection (top_k or pool blocks) the LDS output buffers hold
+template <int CAP, int MS = kMaxSelect>
 struct SmallSel {
     uint64_t cand[CAP];
-    uint32_t sel[kMaxSelect + 4];
+    uint32_t sel[MS + 4];
     RadixShared R;
     int cnt;
     int nt;
 };
-template <int CAP>
+template <int CAP, int MS = kMaxSelect>
 union SelLds {
     SelectSharedT<CAP> big;
-    SmallSel<CAP> small;
+    SmallSel<CAP, MS> small;
 };
 
 constexpr int kTieCap = 1024;  // equal keys at the threshold ordered by direct counting
@@ -807,16 +812,16 @@ constexpr int kSelScanMax = 16384;
 template <int NT>
 constexpr int sel_scan_u() { return kSelScanMax / (4 * NT); }  // four-key loads per thread
 
-// Ascending output of up to kMaxSelect selected positions (sel[] in LDS).
-template <int NT>
+// Ascending output of up to MS selected positions (sel[] in LDS).
+template <int NT, int MS = kMaxSelect>
 struct AscLds {
-    uint32_t scratch[2 * kAscB + kMaxSelect];
+    uint32_t scratch[2 * kAscB + MS];
     int scan[NT / kWave];
     uint32_t mm[2];
 };
 
-template <int NT>
-__device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, int32_t* out, AscLds<NT>& A) {
+template <int NT, int MS>
+__device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, int32_t* out, AscLds<NT, MS>& A) {
     bucket_write_ascending<NT>(sel, total, k, out, A.scratch, A.scan, A.mm);
 }
 
@@ -824,8 +829,8 @@ __device__ __forceinline__ void sort_out(const uint32_t* sel, int total, int k, 
 // digit d1) and W.sel[0, W.cnt) the positions already selected (those above the bucket); adds
 // the `need` best of the bucket to W.sel and returns how many W.sel holds.  The threshold KEY
 // comes first (at most two radix passes); equal keys at it are ranked by position.
-template <int NT, int CAP>
-__device__ int select_bucket_lds(SmallSel<CAP>& W, AscLds<NT>& A, int m, int need, int d1) {
+template <int NT, int CAP, int MS>
+__device__ int select_bucket_lds(SmallSel<CAP, MS>& W, AscLds<NT, MS>& A, int m, int need, int d1) {
     const int t = threadIdx.x;
     const bool any = need > 0 && m > 0;
     const KeyThr kt = any ? lds_key_threshold<NT>(W.cand, m, need, d1, W.R) : KeyThr{0u, -1, 0};
@@ -879,7 +884,7 @@ __device__ int select_bucket_lds(SmallSel<CAP>& W, AscLds<NT>& A, int m, int nee
 // radix path).  Decode: 1,024 threads, 8,192; a prefill chunk's thousands of queries: 512 and
 // 2,048, which halves the LDS so that two workgroups share a compute unit.
 // ----------------------------------------------------------------------------------------
-template <int NT, int CAP>
+template <int NT, int CAP, int MS>
 // (as in the filter pass: the first loads' workspace areas lead the arguments, preloaded)
 __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* hist, uint32_t* keys, uint32_t* bkeys,
                                                         int top_k, int pool_blocks, int scan_keys, int list0, IndexWs ws,
@@ -889,8 +894,8 @@ __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* 
     ws.hist = hist;
     ws.keys = keys;
     ws.bkeys = bkeys;
-    __shared__ SelLds<CAP> U;
-    __shared__ AscLds<NT> A;
+    __shared__ SelLds<CAP, MS> U;
+    __shared__ AscLds<NT, MS> A;
     __shared__ Thresh sh_th;
     const int i = blockIdx.x;
     const int which = list0 + (int)blockIdx.y;  // 0: positions, 1: pool blocks
@@ -931,7 +936,7 @@ __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* 
         __syncthreads();
     }
     if (small) {
-        SmallSel<CAP>& W = U.small;
+        SmallSel<CAP, MS>& W = U.small;
         if (!scan_keys) {
             for (int e = t; e < th.in_bucket; e += NT) W.cand[e] = cand[e];
             for (int j = t; j < n_sure; j += NT) W.sel[j] = (uint32_t)sure[j];
@@ -941,7 +946,7 @@ __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* 
             W.nt = 0;
         }
         __syncthreads();
-        const int total = select_bucket_lds<NT, CAP>(W, A, th.in_bucket, need, th.digit);
+        const int total = select_bucket_lds<NT, CAP, MS>(W, A, th.in_bucket, need, th.digit);
         sort_out(W.sel, total, k, out, A);
     } else {
         SelectSharedT<CAP>& S = U.big;
@@ -972,11 +977,11 @@ __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* 
 // bucket (heavy ties), to the radix passes over the global list.
 // Leaves the query's histogram and candidate counter zero for the next call.
 // ----------------------------------------------------------------------------------------
-template <int NT, int CAP>
+template <int NT, int CAP, int MS>
 __global__ __launch_bounds__(NT) void k_idx_select_cands(QMeta* qmeta, uint32_t* ctrl_all, uint32_t* hist_all,
                                                          uint64_t* cand_all, int top_k, int32_t* __restrict__ idx_out) {
-    __shared__ SelLds<CAP> U;
-    __shared__ AscLds<NT> A;
+    __shared__ SelLds<CAP, MS> U;
+    __shared__ AscLds<NT, MS> A;
     __shared__ Thresh sh_th;
     const int i = blockIdx.x;
     const int t = threadIdx.x;
@@ -989,7 +994,7 @@ __global__ __launch_bounds__(NT) void k_idx_select_cands(QMeta* qmeta, uint32_t*
     int32_t* out = idx_out + (int64_t)i * top_k;
     // the candidates are distinct visible positions: at most n of them
     const int m = (int)min((int64_t)ctrl[kCtlCandIdx], (int64_t)max(qm.n, 0));
-    SmallSel<CAP>& W = U.small;
+    SmallSel<CAP, MS>& W = U.small;
     find_threshold_regs<NT>(h, top_k, W.R.scan, &sh_th);
     const Thresh th = sh_th;
     if (th.digit < 0) {
@@ -1019,7 +1024,7 @@ __global__ __launch_bounds__(NT) void k_idx_select_cands(QMeta* qmeta, uint32_t*
             }
         }
         __syncthreads();
-        const int total = select_bucket_lds<NT, CAP>(W, A, th.in_bucket, top_k - th.above, th.digit);
+        const int total = select_bucket_lds<NT, CAP, MS>(W, A, th.in_bucket, top_k - th.above, th.digit);
         sort_out(W.sel, total, top_k, out, A);
     } else {
         SelectSharedT<CAP>& S = U.big;
@@ -1250,17 +1255,24 @@ hipError_t launch_index_full(const uint16_t* q_idx, const float* w, const void* 
             if (e != hipSuccess) return e;
         }
         const bool many = prefill && n_q >= 512;
+        const bool many_small = many && top_k <= kSelMaxMany;  // (the position list)
         if (prefill) {
             // positions: the exact Top-K among each query's candidates; pool blocks (when asked
             // for): the threshold-bucket selection over the filtered block lists
-            auto candk = many ? k_idx_select_cands<kSelNTMany, kSortCapMany> : k_idx_select_cands<kSelNT, kSortCap>;
+            auto candk = many_small ? k_idx_select_cands<kSelNTMany, kSortCapMany, kSelMaxMany>
+                         : many     ? k_idx_select_cands<kSelNTMany, kSortCapMany, kMaxSelect>
+                                    : k_idx_select_cands<kSelNT, kSortCap, kMaxSelect>;
             hipLaunchKernelGGL(candk, dim3(n_q), dim3(many ? kSelNTMany : kSelNT), 0, stream, ws.qmeta, ws.ctrl,
                                ws.hist, ws.cand_idx, top_k, idx_out);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess || pool_blocks <= 0) return e;
         }
-        auto selk = many ? k_idx_select_full<kSelNTMany, kSortCapMany> : k_idx_select_full<kSelNT, kSortCap>;
+        // (a prefill chunk selects only its pool list here; decode selects both lists)
         const int list0 = prefill ? 1 : 0;
+        const bool sel_small = many && (prefill ? pool_blocks : max(top_k, pool_blocks)) <= kSelMaxMany;
+        auto selk = sel_small ? k_idx_select_full<kSelNTMany, kSortCapMany, kSelMaxMany>
+                    : many    ? k_idx_select_full<kSelNTMany, kSortCapMany, kMaxSelect>
+                              : k_idx_select_full<kSelNT, kSortCap, kMaxSelect>;
         hipLaunchKernelGGL(selk, dim3(n_q, pool_blocks > 0 && !prefill ? 2 : 1), dim3(many ? kSelNTMany : kSelNT), 0,
                            stream, ws.qmeta, ws.hist, ws.keys, ws.bkeys, top_k, pool_blocks, scan_keys, list0, ws,
                            idx_out, pool_out);
