@@ -498,6 +498,39 @@ def test_index_fractional_weights_full_and_reindex(negative):
         assert np.array_equal(idx2[i], case.oracle_reindex(i, pool_np[i], 512, q=q2[i], w=w2[i])), i
 
 
+@pytest.mark.parametrize("n_q,n_heads", [(16, 4), (17, 4), (16, 8)])
+def test_index_reindex_lane_per_position_and_row_forms(n_q, n_heads):
+    # up to 16 queries with at most 4 heads score one position per lane; 17 queries, or 8 heads,
+    # take the 16-position form: both against the oracle on ragged contexts (pools with padding)
+    lengths = np.random.default_rng(95 + n_q).integers(1, 40000, size=n_q)
+    lengths[0], lengths[-1] = 9, 16384
+    case = IndexCase(W_T + 95 + n_q, lengths, n_heads=n_heads)
+    _, pool, _ = case.run_full(512, 2048)
+    q2 = synth.int_bf16(W_T + 95, synth.T_IDX_Q, (n_q, n_heads, 64), seq=11)
+    w2 = synth.int_weights(W_T + 95, synth.T_IDX_W, (n_q, n_heads), seq=11)
+    idx2, _ = case.run_reindex(pool, 512, q_dev=bf16_tensor(q2), w_dev=torch.from_numpy(w2).to(DEV))
+    idx2, pool_np = idx2.cpu().numpy(), pool.cpu().numpy()
+    for i in range(n_q):
+        assert np.array_equal(idx2[i], case.oracle_reindex(i, pool_np[i], 512, q=q2[i], w=w2[i])), i
+
+
+@pytest.mark.parametrize("top_k,pool_blocks", [(1024, 1024), (1025, 1025)])
+def test_index_prefill_selection_sizes_around_lds_lists(top_k, pool_blocks):
+    # 512 queries of one chunk: selections of at most 1,024 entries are gathered in LDS lists of
+    # that size, larger ones in the 2,048-entry form; both sides of the limit, for the position
+    # list and the pool list, every query against the oracle
+    T = 512
+    lengths = np.random.default_rng(96).integers(1, 12000, size=T)
+    lengths[:4] = [8200, 8192, 1024, 3]
+    case = SharedIndexCase(W_T + 96, 12000, lengths, n_heads=4)
+    idx, pool, _ = case.run_full(top_k, pool_blocks, shared_kv=1)
+    idx, pool = idx.cpu().numpy(), pool.cpu().numpy()
+    for t in range(T):
+        ri, rp = case.oracle_full(t, top_k, pool_blocks)
+        assert np.array_equal(idx[t], ri), t
+        assert np.array_equal(pool[t], rp), t
+
+
 def test_index_reindex_pool_with_padding_and_out_of_range_blocks():
     lengths = [1000, 50]
     case = IndexCase(W_T + 4, lengths, n_heads=4)

@@ -146,3 +146,20 @@ def test_index_reindex_mx_bit_exact():
         r0, n = int(case.row0[i]), int(lengths[i])
         ref = O.index_reindex_mx(q2[i], w2[i], case.kc_ref[r0:r0 + n], case.ks_ref[r0:r0 + n], n, pool_np[i], 512, 8)
         assert np.array_equal(idx2[i], ref), i
+
+
+@pytest.mark.parametrize("n_q", [16, 17])
+def test_index_reindex_mx_lane_per_position_and_row_forms(n_q):
+    # 16 queries: one position per lane; 17: the 16-position form (both read the E8M0 scales)
+    lengths = np.random.default_rng(40 + n_q).integers(1, 30000, size=n_q)
+    lengths[0] = 13
+    case = MxCase(W_MX + 40 + n_q, lengths, n_heads=4, scale_rows=True)
+    _, pool = case.run_full_mx(512, 1024)
+    pool_np = pool.cpu().numpy()
+    q2 = synth.int_bf16(W_MX + 40, synth.T_IDX_Q, (n_q, 4, 64), seq=3)
+    w2 = synth.int_weights(W_MX + 40, synth.T_IDX_W, (n_q, 4), seq=3)
+    idx2 = case.run_reindex_mx(pool, 512, q_dev=bf16_tensor(q2), w_dev=torch.from_numpy(w2).to(DEV)).cpu().numpy()
+    for i in range(n_q):
+        r0, n = int(case.row0[i]), int(lengths[i])
+        ref = O.index_reindex_mx(q2[i], w2[i], case.kc_ref[r0:r0 + n], case.ks_ref[r0:r0 + n], n, pool_np[i], 512, 8)
+        assert np.array_equal(idx2[i], ref), i
