@@ -10,6 +10,7 @@
 #pragma once
 
 #include "csa2_device.hpp"
+#include "scan_common.hpp"
 
 namespace csa2 {
 
@@ -28,26 +29,26 @@ __device__ __forceinline__ void reindex_select_query(int i, const int32_t* __res
     const uint32_t* keys = ws.keys + (int64_t)i * n_elem;
     uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins;
 
+    // the first-digit histogram (accumulated by the score kernel) is requested first, so its
+    // threshold search runs while the keys are still in flight
+    uint32_t h[kHistBins / NT];
+    hist_load<NT>(gh, h);
     uint32_t kv[EPT];
     int32_t pb[EPT / 8];  // pool blocks of this thread's elements
+    // bounded views: elements past n_elem (a multiple of 8) read as key 0, padding, and are
+    // never selected; the loads need no branch, so the histogram's wait leaves them in flight
+    const BufRsrc rk = tile_rsrc(keys, n_elem * 4), rp = tile_rsrc(qpool, pool_blocks * 4);
 #pragma unroll
     for (int j = 0; j < EPT; j += 8) {
-        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
-        int32_t blk = -1;
-        if (e0 + j < n_elem) {  // n_elem is a multiple of 8: the whole block is there
-            a = *reinterpret_cast<const uint4*>(keys + e0 + j);
-            b = *reinterpret_cast<const uint4*>(keys + e0 + j + 4);
-            blk = qpool[(e0 + j) >> 3];
-        }
+        const uint4 a = buf_ld16(rk, (e0 + j) * 4, 0), b = buf_ld16(rk, (e0 + j) * 4 + 16, 0);
         kv[j] = a.x; kv[j + 1] = a.y; kv[j + 2] = a.z; kv[j + 3] = a.w;
         kv[j + 4] = b.x; kv[j + 5] = b.y; kv[j + 6] = b.z; kv[j + 7] = b.w;
-        pb[j >> 3] = blk;
+        pb[j >> 3] = (int32_t)buf_ld4(rp, ((e0 + j) >> 3) * 4, 0);
     }
     for (int b = t; b < 2 * kHistBins; b += NT) (&s_hist[0][0])[b] = 0u;
     if (t < 2) s_or[t] = 0u;
-    // first digit: histogram accumulated by the score kernel (its barriers also cover the
-    // clearing above)
-    find_threshold<NT>(gh, top_k, s_scan, &sh_th);
+    // first digit (the search's barriers also cover the clearing above)
+    find_threshold_regs<NT>(h, top_k, s_scan, &sh_th);
     Thresh th = sh_th;
     uint32_t T = 1u;           // selected: key > T, or key == T among the first need_eq of them
     int need_eq = INT32_MAX;   // (keys are >= 1 for every valid element; 0 marks padding)
