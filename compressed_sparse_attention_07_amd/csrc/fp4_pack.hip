@@ -47,30 +47,62 @@ constexpr ScaleLut make_scale_lut() {
 
 __device__ constexpr ScaleLut kScaleLut = make_scale_lut();
 
+// (m & a) | (~m & b) as one instruction: written out, because the compiler otherwise re-forms
+// these selects and the code-bit merges into two or three instructions each
+__device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) {
+    uint32_t d;
+    asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "v"(m), "v"(a), "v"(b));
+    return d;
+}
+
 // One 16-channel FP4 group: w = 8 dwords of bf16 pairs (channel 2k in the low half) ->
 // codes (lo: channels 0..7, hi: 8..15; low nibble = even channel) and the E4M3 scale code.
+// The seven E2M1 midpoint thresholds m * s (m = 1/4, 3/4, 5/4, 7/4, 5/2, 7/2, 5) are s, 3s, 5s
+// and 7s times powers of two: four exact bf16 patterns (s has at most 4 significant bits, 7s at
+// most 7) and exponent-field subtractions give all seven.  Each pair of channels then takes the
+// three-level compare tree of e2m1_pair on 16-bit lanes (|x| >= t3; >= t5 or t1; > one of t6,
+// t4, t2, t0), with ">= t" written as "> t - 1" so that every level's mask is a code bit.
+__device__ __forceinline__ uint32_t bf16_both_halves(float x) {  // x's bf16 pattern (exact) in both halves
+    return __builtin_amdgcn_perm(__float_as_uint(x), __float_as_uint(x), 0x03020302u);
+}
+
 __device__ __forceinline__ uint32_t fp4_pack_group(const uint32_t (&w)[8], uint32_t& lo, uint32_t& hi) {
-    // amax: bf16 magnitudes order like their 15-bit patterns
-    uint32_t am = 0;
+    // magnitudes (bf16 magnitudes order like their 15-bit patterns) and their maximum
+    uint32_t A[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) am = max(am, max(w[k] & 0x7fffu, (w[k] >> 16) & 0x7fffu));
+    for (int k = 0; k < 8; ++k) A[k] = w[k] & 0x7fff7fffu;
+    u16x2_t mx = __builtin_bit_cast(u16x2_t, A[0]);
+#pragma unroll
+    for (int k = 1; k < 8; ++k) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2_t, A[k]));
+    const uint32_t am = max((uint32_t)mx[0], (uint32_t)mx[1]);
     const int sc = kScaleLut.c[am];
     const float s = e4m3_pos_value(sc);
-    constexpr float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-    uint32_t T[7];
-#pragma unroll
-    for (int k = 0; k < 7; ++k) {
-        const uint32_t b = __float_as_uint(kMid[k] * s) >> 16;  // exact (low half is zero)
-        T[k] = sc == 0 ? 0x7fff7fffu : (b | (b << 16));
-    }
-    uint32_t byte[8];
+    const uint32_t Q1 = bf16_both_halves(s), Q3 = bf16_both_halves(3.0f * s), Q5 = bf16_both_halves(5.0f * s),
+                   Q7 = bf16_both_halves(7.0f * s);
+    // (s >= 2^-9 when sc > 0: no field borrows across the halves; sc == 0 is handled below)
+    constexpr uint32_t kE2 = 0x01000100u, kE1 = 0x00800080u, kOne = 0x00010001u;
+    const uint32_t T0 = Q1 - kE2, T1m = Q3 - kE2 - kOne, T2 = Q5 - kE2, T3m = Q7 - kE2 - kOne;
+    const uint32_t T4 = Q5 - kE1, T5m = Q7 - kE1 - kOne, T6 = Q5;
+    uint32_t c[8];  // code of channel 2k in bits 0..3, of channel 2k + 1 in bits 16..19
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        const uint32_t c = e2m1_pair(w[k], T);
-        byte[k] = (c | (c >> 12)) & 0xffu;  // channel 2k in the low nibble, 2k + 1 in the high one
+        const uint32_t a = A[k];
+        const uint32_t g4 = lt16_mask(T3m, a);                       // |x| >= t3
+        const uint32_t pa = bfi32(g4, T6, T2), pb = bfi32(g4, T4, T0);
+        const uint32_t g2 = lt16_mask(bfi32(g4, T5m, T1m), a);       // |x| >= t5 (or t1)
+        const uint32_t g1 = lt16_mask(bfi32(g2, pa, pb), a);         // |x| > t6, t4, t2 (or t0)
+        const uint32_t sg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, w[k]) >> (unsigned short)12);
+        c[k] = bfi32(0x00040004u, g4, bfi32(0x00020002u, g2, bfi32(0x00010001u, g1, sg)));  // sign: bit 3
     }
-    lo = byte[0] | (byte[1] << 8) | (byte[2] << 16) | (byte[3] << 24);
-    hi = byte[4] | (byte[5] << 8) | (byte[6] << 16) | (byte[7] << 24);
+    // bytes: channel pairs (2k, 2k + 1) as one byte each, even channel in the low nibble
+    auto four = [&](int k0) {
+        const uint32_t x0 = __builtin_amdgcn_perm(c[k0 + 1], c[k0], 0x06040200u);
+        const uint32_t x1 = __builtin_amdgcn_perm(c[k0 + 3], c[k0 + 2], 0x06040200u);
+        return __builtin_amdgcn_perm(x1 | (x1 >> 4), x0 | (x0 >> 4), 0x06040200u);
+    };
+    const uint32_t keep = sc == 0 ? 0x88888888u : 0xffffffffu;  // a zero scale codes every magnitude 0
+    lo = four(0) & keep;
+    hi = four(4) & keep;
     return (uint32_t)sc;
 }
 
@@ -132,17 +164,16 @@ __global__ __launch_bounds__(256) void k_fp4_pack128(const uint16_t* __restrict_
                                v[k][1][0], v[k][1][1], v[k][1][2], v[k][1][3]};
         uint32_t lo, hi;
         const uint32_t sc = fp4_pack_group(w, lo, hi);
-        // the token's 8 scale bytes, gathered in its 8 lanes (aligned groups of 8 lanes)
-        uint32_t slo = g < 4 ? sc << (8 * g) : 0u, shi = g >= 4 ? sc << (8 * (g - 4)) : 0u;
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-            slo |= (uint32_t)__shfl_xor((int)slo, o, kWave);
-            shi |= (uint32_t)__shfl_xor((int)shi, o, kWave);
-        }
+        // the token's 8 scale bytes: each quad of lanes ORs its four (quad_perm exchanges), and
+        // the token's first lane takes the second quad's word from 4 lanes up (row_shl:4)
+        uint32_t sq = sc << (8 * (g & 3));
+        sq |= (uint32_t)__builtin_amdgcn_mov_dpp((int)sq, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+        sq |= (uint32_t)__builtin_amdgcn_mov_dpp((int)sq, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+        const uint32_t sh4 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sq, 0x104, 0xF, 0xF, true);
         const int64_t r = row[k];
         if (r >= 0 && r < cap_rows) {
             *reinterpret_cast<uint2*>(codes + r * 64 + g * 8) = make_uint2(lo, hi);
-            if (g == 0) *reinterpret_cast<uint2*>(scales + r * 8) = make_uint2(slo, shi);
+            if (g == 0) *reinterpret_cast<uint2*>(scales + r * 8) = make_uint2(sq, sh4);
         }
     }
 }
