@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kScoreNT) __attribute__((amdgpu_waves_per_eu(4))) v
     const int64_t* __restrict__ kv_row0, int n_q, int64_t cache_rows, int n_heads, int n_px, int n_qg,
     IndexWs ws) {
     __shared__ __align__(16) uint8_t sh_keys[2][kPcStage * kPcRowB];
-    __shared__ uint64_t sh_ring[kScoreNT / kWave][kPcRing];
+    __shared__ uint32_t sh_ring[kScoreNT / kWave][2 * kPcRing];  // per wave: keys, then low words
     __shared__ uint32_t sh_dcnt[kScoreNT / kWave][16 * kPcDW];   // [wave][row * kPcDW + digit offset]
     __shared__ uint32_t sh_qcur[kScoreNT / kWave][16];
     __shared__ int sh_n[kPcQ];
@@ -410,8 +410,9 @@ __global__ __launch_bounds__(kScoreNT) __attribute__((amdgpu_waves_per_eu(4))) v
         tk[i] = d < 0 ? 0u : (uint32_t)d << 21;
     }
 
-    // ---- the wave's candidate ring ----
-    uint64_t* ring = sh_ring[wid];
+    // ---- the wave's candidate ring: entry e = key ring[e], low word ring[kPcRing + e] (two
+    // 4-byte stores at one address and an offset, no register pair to assemble) ----
+    uint32_t* ring = sh_ring[wid];
     uint32_t* dcnt = sh_dcnt[wid];
     uint32_t* qcur = sh_qcur[wid];
     int ring_n = 0;  // wave-uniform
@@ -419,9 +420,9 @@ __global__ __launch_bounds__(kScoreNT) __attribute__((amdgpu_waves_per_eu(4))) v
         if (lane < 16) qcur[lane] = 0u;
         wave_lds_sync();
         for (int e = lane; e < ring_n; e += kWave) {
-            const uint64_t v = ring[e];
-            const int row = (int)((uint32_t)v >> 26) & 15;
-            const int d = (int)(v >> 53);
+            const uint32_t lo = ring[kPcRing + e];
+            const int row = (int)(lo >> 26) & 15;
+            const int d = (int)(ring[e] >> 21);
             const int d0 = sh_thr[wq0 + row];
             atomicAdd(&qcur[row], 1u);
             if (d0 >= 0 && d - d0 < kPcDW)
@@ -445,10 +446,10 @@ __global__ __launch_bounds__(kScoreNT) __attribute__((amdgpu_waves_per_eu(4))) v
         }
         wave_lds_sync();
         for (int e = lane; e < ring_n; e += kWave) {
-            const uint64_t v = ring[e];
-            const int row = (int)((uint32_t)v >> 26) & 15;
+            const uint32_t lo = ring[kPcRing + e];
+            const int row = (int)(lo >> 26) & 15;
             const uint32_t slot = atomicAdd(&qcur[row], 1u);
-            ws.cand_idx[sh_base[wq0 + row] + slot] = composite((uint32_t)(v >> 32), (uint32_t)v & (kPcMaxPos - 1));
+            ws.cand_idx[sh_base[wq0 + row] + slot] = composite(ring[e], lo & (kPcMaxPos - 1));
         }
         wave_lds_sync();
         ring_n = 0;
@@ -491,6 +492,8 @@ __global__ __launch_bounds__(kScoreNT) __attribute__((amdgpu_waves_per_eu(4))) v
     auto tile_epilogue = [&](const f32x4_t (&acc)[4], int ps, int u, auto all_tag) {
         constexpr bool ALL = decltype(all_tag)::value;
         if (ring_n > kPcRing - 256) flush();  // wave-uniform
+        // (kept in a scalar register, so the count and the slot base cost no vector instruction)
+        int rn = __builtin_amdgcn_readfirstlane(ring_n);
         const int p = ps + 16 * u + r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -504,10 +507,14 @@ __global__ __launch_bounds__(kScoreNT) __attribute__((amdgpu_waves_per_eu(4))) v
             const uint32_t key = ok ? sb ^ ((uint32_t)((int32_t)sb >> 31) | 0x80000000u) : 0u;
             const bool kept = ok && key >= tk[i];
             const uint64_t m = __ballot(kept);
-            const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (kept) ring[ring_n + rank] = ((uint64_t)key << 32) | ((uint32_t)(4 * g + i) << 26) | (uint32_t)p;
-            ring_n += __popcll(m);
+            // slot = entries so far + kept lanes below this one
+            const int e = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)rn));
+            if (kept) {
+                ring[e] = key;
+                ring[kPcRing + e] = ((uint32_t)(4 * g + i) << 26) | (uint32_t)p;
+            }
+            rn += __popcll(m);
             if constexpr (POOL) {
                 const uint32_t bk = max_over_8_lanes(key);  // lanes 4 / 12 of the row
                 const int pblk = ps + 16 * u + (r & 8);
@@ -515,6 +522,7 @@ __global__ __launch_bounds__(kScoreNT) __attribute__((amdgpu_waves_per_eu(4))) v
                     ws.bkeys[sh_base[wq0 + 4 * g + i] / 8 + (pblk >> 3)] = bk;
             }
         }
+        ring_n = rn;
     };
     auto score_stage = [&](int buf, int ps, auto all_tag) {
         const uint8_t* kb = sh_keys[buf];
