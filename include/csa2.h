@@ -345,12 +345,13 @@ int csa2_index_reindex_noalloc(const uint16_t* q_idx, const float* w, const uint
  *           is 0).
  * idx_out receives the selection (a Reuse layer that follows attends with it), equal to that
  * of csa2_index_reindex, and out the attention over it, equal to that of csa2_attend: the call
- * issues the separate calls' kernels (scoring, selection, attention) in one go.  Two fused
+ * issues the separate calls' kernels (scoring, selection, attention) in one go.  Three fused
  * forms measured slower on MI355X and are not used: everything in one kernel (the last scoring
- * workgroup of a query selecting and attending), and the selection and attention in one kernel
+ * workgroup of a query selecting and attending); the selection and attention in one kernel
  * (one compute unit then forms all 512 entries' logits, where the attention kernel spreads
- * them over five).  All arguments are checked before anything is launched; the errors are
- * those of the separate calls.
+ * them over five); and every attention workgroup repeating the selection itself with its four
+ * waves (a selection four times slower than with sixteen).  All arguments are checked before
+ * anything is launched; the errors are those of the separate calls.
  */
 int csa2_reindex_attend(const uint16_t* q_idx, const float* w, const void* k_idx, const uint8_t* k_scales,
                         csa2_seqs seqs, int32_t idx_heads, const int32_t* pool, int32_t pool_blocks,

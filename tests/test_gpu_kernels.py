@@ -561,11 +561,10 @@ def test_index_reindex_unsorted_pool_follows_element_order():
 @pytest.mark.parametrize("pool_blocks,top_k,window", [(2048, 512, 128), (300, 64, 0), (3000, 512, 128), (1, 4, 16),
                                                       (512, 512, 300), (2048, 100, 256), (2048, 700, 128)])
 def test_reindex_attend_equals_separate_calls_and_oracle(pool_blocks, top_k, window):
-    # csa2_reindex_attend (scoring + the fused selection/attention kernel for top_k <= 512,
-    # the separate kernels above that) against csa2_index_reindex followed by csa2_attend: the
-    # same indices; both outputs against the oracle (the two split the entries over workgroups
-    # differently, so they may round differently).  Windows of 300 and 256 take more than one
-    # workgroup per query in the fused kernel (a cross-workgroup merge) or only the selecting one.
+    # csa2_reindex_attend (one call issuing the scoring, selection and attention kernels)
+    # against csa2_index_reindex followed by csa2_attend: the same indices and the same attention
+    # bit for bit; both against the oracle.  Windows of 300 and 256 give 7 and 3 attention
+    # workgroups per query (a cross-workgroup merge); window 0 attends the selection alone.
     lengths = [40000, 777, 0, 16, 25001]
     ic = IndexCase(W_T + 70, lengths, n_heads=4)
     ac = AttendCase(W_T + 70, lengths, n_heads=16, window=max(window, 1), swa_cap=max(window, 128))
@@ -587,6 +586,7 @@ def test_reindex_attend_equals_separate_calls_and_oracle(pool_blocks, top_k, win
                           ac.swa_dev, ac.swa_row0_dev, ac.swa_cap, window, scale, out_b, ws)
     torch.cuda.synchronize()
     assert np.array_equal(idx_b.cpu().numpy(), idx_a)
+    assert np.array_equal(out_b.cpu().numpy(), out_a.cpu().numpy())
     pool_np = pool.cpu().numpy()
     for i in range(n_q):
         assert np.array_equal(idx_a[i], ic.oracle_reindex(i, pool_np[i], top_k, q=q2[i], w=w2[i])), i

@@ -185,16 +185,16 @@ def test_workload7_mxfp4_keys_fp8_window_with_replay():
 
 @pytest.mark.parametrize("wid", [1, 7])
 def test_fused_reindex_layers_equal_separate_calls(wid):
-    # the fused Reindex selection + attention gives the separate calls' indices exactly; its
-    # attention (one workgroup per query, where the separate decode call splits each query's
-    # entries over workgroups, so the two may round differently) is checked against the oracle
-    # on strided queries of every layer
-    idxs = []
+    # Reindex layers through the one-call entry point (csa2_reindex_attend) and through the
+    # separate calls: the same indices and the same attention outputs bit for bit; the one-call
+    # step against the oracle on strided queries of every layer
+    idxs, outs = [], []
     for fused in (True, False):
         r = W.Runner(W.WORKLOADS[wid], fused_reindex=fused, keep_host=fused)
         r.step()
         torch.cuda.synchronize()
         idxs.append([L.idx.cpu().numpy() if L.idx is not None else None for L in r.layers])
+        outs.append([L.out.cpu().numpy() for L in r.layers])
         if fused:
             _check_step(r, [], _strided(r.n_q, 8), rows_sample=200)
         del r
@@ -202,6 +202,8 @@ def test_fused_reindex_layers_equal_separate_calls(wid):
     for l, (ia, ib) in enumerate(zip(*idxs)):
         if ia is not None:
             assert np.array_equal(ia, ib), l
+    for l, (oa, ob) in enumerate(zip(*outs)):
+        assert np.array_equal(oa, ob), l
 
 
 def test_workload3_prefill_4096_on_128k():
