@@ -55,17 +55,18 @@ __device__ __forceinline__ uint32_t bfi32(uint32_t m, uint32_t a, uint32_t b) {
     return d;
 }
 
-// One 16-channel FP4 group: w = 8 dwords of bf16 pairs (channel 2k in the low half) ->
-// codes (lo: channels 0..7, hi: 8..15; low nibble = even channel) and the E4M3 scale code.
-// The seven E2M1 midpoint thresholds m * s (m = 1/4, 3/4, 5/4, 7/4, 5/2, 7/2, 5) are s, 3s, 5s
-// and 7s times powers of two: four exact bf16 patterns (s has at most 4 significant bits, 7s at
-// most 7) and exponent-field subtractions give all seven.  Each pair of channels then takes the
-// three-level compare tree of e2m1_pair on 16-bit lanes (|x| >= t3; >= t5 or t1; > one of t6,
-// t4, t2, t0), with ">= t" written as "> t - 1" so that every level's mask is a code bit.
 __device__ __forceinline__ uint32_t bf16_both_halves(float x) {  // x's bf16 pattern (exact) in both halves
     return __builtin_amdgcn_perm(__float_as_uint(x), __float_as_uint(x), 0x03020302u);
 }
 
+// One 16-channel FP4 group: w = 8 dwords of bf16 pairs (channel 2k in the low half) ->
+// codes (lo: channels 0..7, hi: 8..15; low nibble = even channel) and the E4M3 scale code.
+// The seven E2M1 midpoint thresholds m * s (m = 1/4, 3/4, 5/4, 7/4, 5/2, 7/2, 5) are s, 3s, 5s
+// and 7s times powers of two: four exact bf16 patterns (s has at most 4 significant bits, 7s at
+// most 7) and exponent-field subtractions give all seven.  Each pair of channels then replaces
+// e2m1_code's seven compares by a three-level tree on 16-bit lanes (|x| >= t3; >= t5 or t1; >
+// one of t6, t4, t2, t0: e2m1_code's tie rules), with ">= t" written as "> t - 1" so that every
+// level's mask is a code bit.
 __device__ __forceinline__ uint32_t fp4_pack_group(const uint32_t (&w)[8], uint32_t& lo, uint32_t& hi) {
     // magnitudes (bf16 magnitudes order like their 15-bit patterns) and their maximum
     uint32_t A[8];

@@ -51,17 +51,14 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t bits16, float s) {
     return mag | ((bits16 >> 12) & 0x8u);
 }
 
-// E2M1 codes of two bf16 values at once (one per 16-bit half of w) against a group's seven
-// midpoint thresholds T[k] (t_k = m_k * s as a bf16 bit pattern in both halves; all ones for a zero
-// scale, so every magnitude codes 0).  Each t_k has at most 7 significant bits (an E4M3 scale
-// times a midpoint of the E2M1 grid), so it is an exact bf16 value, and for non-negative values
-// the 15-bit patterns order like the values: the comparisons are 16-bit integer ones, two values
-// per instruction.  The seven compares of e2m1_code become a three-level tree: c4 = |x| >= t3,
-// then t5 or t1 (>=), then one of t6, t4, t2, t0 (>); the tie rules are e2m1_code's.
-// Returns the 4-bit codes (sign bit 3) in bits 0..3 and 16..19.
+// Two 16-bit lanes compared at once: all ones in each half of the result where the half of a is
+// below the half of b.  Exact as long as the two halves differ by less than 2^15 (the FP4
+// packer's operands are 15-bit bf16 magnitude patterns and thresholds).  Non-negative bf16
+// values order like their 15-bit patterns, so the packer decides E2M1 codes two channels per
+// instruction with these.
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t lt16_mask(uint32_t a, uint32_t b) {  // all ones in a half where a < b
+__device__ __forceinline__ uint32_t lt16_mask(uint32_t a, uint32_t b) {
     const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2_t, a) - __builtin_bit_cast(u16x2_t, b));
     uint32_t m;
     // the sign of each 16-bit difference spread over its half (one packed shift; written out
@@ -70,17 +67,6 @@ __device__ __forceinline__ uint32_t lt16_mask(uint32_t a, uint32_t b) {  // all 
     // bits 31..16 of each operand, which an inline constant 15 leaves zero.
     asm("v_pk_ashrrev_i16 %0, %1, %2" : "=v"(m) : "s"(0x000f000fu), "v"(d));
     return m;
-}
-
-__device__ __forceinline__ uint32_t pick(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
-
-__device__ __forceinline__ uint32_t e2m1_pair(uint32_t w, const uint32_t (&T)[7]) {
-    const uint32_t A = w & 0x7fff7fffu;
-    const uint32_t m4 = lt16_mask(A, T[3]);           // |x| < t3
-    const uint32_t m2 = lt16_mask(A, pick(m4, T[1], T[5]));
-    const uint32_t tl = pick(m4, pick(m2, T[0], T[2]), pick(m2, T[4], T[6]));
-    const uint32_t m1 = lt16_mask(tl, A);             // |x| > the last threshold
-    return (~m4 & 0x00040004u) | (~m2 & 0x00020002u) | (m1 & 0x00010001u) | ((w >> 12) & 0x00080008u);
 }
 
 // One 32-channel MXFP4 block (microscaling conversion): scale X = 2^(floor(log2 amax) - 2), its
