@@ -173,6 +173,9 @@ __device__ __forceinline__ void score_full_body(
                 load_qfrag_lp(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
             else
                 load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
+            // the query's fragments complete here (once per query), so the batch loop's waits
+            // count only its own key loads: vmcnt(0)
+            __builtin_amdgcn_s_waitcnt(0x0f70);
         }
         const int n = qm.n;
         const int64_t key_base = (int64_t)qm.start * kFullTile;
@@ -252,6 +255,24 @@ __device__ __forceinline__ void score_full_body(
             // measured faster than loads of half rows in the fragment layout)
             const int voff = MX ? (WR * wid + r) * kRowB + 4 * g : WR * wid * kRowB + rowline_voff(lane);
             const int voff_s = (WR * wid + r) * 2;
+            // Loads are pipelined across the unit's batches: once step u of a batch is scored,
+            // its registers take step u of the next batch, so a wave always has U steps of loads
+            // in flight (no gap of a memory latency between batches).  A step of a batch that
+            // does not exist is loaded through a lane offset past the view: zeros, no access.
+            constexpr int kNoRow = 1 << 30;
+            uint4 kb[U][2];
+            uint32_t kc[U][2], ks[U];
+            auto issue = [&](int u, int bb, bool real) {
+                const int vo = real ? voff : kNoRow;
+                if constexpr (MX) {
+                    kc[u][0] = buf_ld4(rs, vo, (bb + 16 * u) * kRowB);
+                    kc[u][1] = buf_ld4(rs, vo + 16, (bb + 16 * u) * kRowB);
+                    ks[u] = buf_ld2(rss, real ? voff_s : kNoRow, (bb + 16 * u) * 2);
+                } else {
+                    kb[u][0] = buf_ld16_nt(rs, vo, (bb + 16 * u) * kRowB);
+                    kb[u][1] = buf_ld16_nt(rs, vo + 8 * kRowB, (bb + 16 * u) * kRowB);
+                }
+            };
             int jd = 0;  // batches of this unit done
             for (int b = b_lo; b < b_hi; b += 64 * U) {
                 const int pb = p_tile + b;
@@ -259,21 +280,14 @@ __device__ __forceinline__ void score_full_body(
                 if (b == b_lo) {
                     write_run();  // the previous unit's runs
                     wave_lds_sync();
-                }
-                uint4 kb[U][2];
-                uint32_t kc[U][2], ks[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    if constexpr (MX) {
-                        kc[u][0] = buf_ld4(rs, voff, (b + 16 * u) * kRowB);
-                        kc[u][1] = buf_ld4(rs, voff + 16, (b + 16 * u) * kRowB);
-                        ks[u] = buf_ld2(rss, voff_s, (b + 16 * u) * 2);
-                    } else {
-                        kb[u][0] = buf_ld16_nt(rs, voff, (b + 16 * u) * kRowB);
-                        kb[u][1] = buf_ld16_nt(rs, voff + 8 * kRowB, (b + 16 * u) * kRowB);
+                    for (int u = 0; u < U; ++u) {
+                        issue(u, b, true);
+                        __builtin_amdgcn_sched_barrier(0);  // in step order: step 0 waits for its own loads only
                     }
-                    __builtin_amdgcn_sched_barrier(0);  // in step order: step 0 waits for its own loads only
                 }
+                const int bn = b + 64 * U;
+                const bool next = bn < b_hi && p_tile + bn < n;  // (uniform) the unit has another batch
                 const int j = (b - b_lo) / (64 * U);  // batch of the unit
                 const int pw = pb + WR * wid;         // first position of this wave's run
 #pragma unroll
@@ -299,6 +313,8 @@ __device__ __forceinline__ void score_full_body(
                             if (pblk < n) atomicAdd(&sh_bhist[bk >> 21], 1u);
                         }
                     }
+                    issue(u, bn, next);  // this step's registers: step u of the next batch
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 jd = j + 1;
             }
