@@ -193,18 +193,26 @@ __device__ __forceinline__ void score_full_body(
             constexpr int kLd = kRowB / 16;  // 16-byte loads per row
             const int voff = (64 * wid + lane) * kRowB;
             const int voff_s = (64 * wid + lane) * 2;
+            // loads pipelined across batches as in the 16-position layout below
+            constexpr int kNoRow = 1 << 30;
+            uint4 kr[UL][kLd];
+            uint32_t ks[UL];
+            auto issue = [&](int u, int bb, bool real) {
+#pragma unroll
+                for (int j = 0; j < kLd; ++j)
+                    kr[u][j] = buf_ld16(rs, (real ? voff : kNoRow) + 16 * j, (bb + 256 * u) * kRowB);
+                if constexpr (MX) ks[u] = buf_ld2(rss, real ? voff_s : kNoRow, (bb + 256 * u) * 2);
+            };
             for (int b = b_lo; b < b_hi; b += 256 * UL) {
                 const int pb = p_tile + b;
                 if (pb >= n) break;
-                uint4 kr[UL][kLd];
-                uint32_t ks[UL];
+                if (b == b_lo) {
 #pragma unroll
-                for (int u = 0; u < UL; ++u) {
-#pragma unroll
-                    for (int j = 0; j < kLd; ++j) kr[u][j] = buf_ld16(rs, voff + 16 * j, (b + 256 * u) * kRowB);
-                    if constexpr (MX) ks[u] = buf_ld2(rss, voff_s, (b + 256 * u) * 2);
+                    for (int u = 0; u < UL; ++u) issue(u, b, true);
+                    __builtin_amdgcn_sched_barrier(0);  // every load of the batch goes out first
                 }
-                __builtin_amdgcn_sched_barrier(0);  // every load of the batch goes out first
+                const int bn = b + 256 * UL;
+                const bool next = bn < b_hi && p_tile + bn < n;  // (uniform) the unit has another batch
 #pragma unroll
                 for (int u = 0; u < UL; ++u) {
                     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -241,6 +249,8 @@ __device__ __forceinline__ void score_full_body(
                             atomicAdd(&sh_bhist[bk >> 21], 1u);
                         }
                     }
+                    issue(u, bn, next);  // this step's registers: step u of the next batch
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         } else {
