@@ -1058,6 +1058,8 @@ __global__ __launch_bounds__(NT) void k_idx_select_cands(QMeta* qmeta, uint32_t*
 // cpw: chunks per workgroup (a divisor of the chunk count).  Many queries (a prefill chunk's
 // tokens): each workgroup scores cpw consecutive chunks of its query and adds its first-digit
 // counts to the query's histogram once, which divides the global atomics by cpw.
+constexpr int kReindexWholePool = 32;  // chunks per workgroup when it scores a whole pool
+
 template <int HI, bool MX, bool LP>
 __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     const int32_t* __restrict__ pool, const uint16_t* __restrict__ q_idx, const float* __restrict__ w,
@@ -1079,12 +1081,26 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_reindex_score(
     for (int b = t; b < kHistBins; b += kScoreNT) sh_hist[b] = 0u;
     if constexpr (LP) {  // at most 4 heads: one position per lane
         static_assert(HI == 4, "the lane-per-position form takes at most 4 heads");
+        // a workgroup with many chunks (a prefill chunk's tokens: a whole pool each) stages their
+        // block ids in LDS first
+        __shared__ int32_t sh_pool[kReindexWholePool * (kReindexTile / 8)];
+        const bool staged = cpw > 1;  // (uniform; cpw is 1 or kReindexWholePool)
+        const int32_t* qpool = pool + (int64_t)i * pool_blocks;
+        if (staged) {
+            const int s0 = grp * cpw * (kReindexTile / 8), cnt = min(cpw * (kReindexTile / 8), pool_blocks - s0);
+            for (int k = t; k < cnt; k += kScoreNT) sh_pool[k] = qpool[s0 + k];
+        }
         QFragLP qf;
         load_qfrag_lp(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
         __syncthreads();
-        reindex_score_chunks_lp<MX, kScoreNT / kWave>(grp * cpw, (grp + 1) * cpw, n, row0,
-                                                      pool + (int64_t)i * pool_blocks, pool_blocks, qf, k_idx, k_sc,
-                                                      ws.keys + (int64_t)i * n_elem, sh_hist);
+        if (staged)
+            reindex_score_chunks_lp<MX, kScoreNT / kWave, true>(grp * cpw, (grp + 1) * cpw, n, row0, qpool, pool_blocks,
+                                                                qf, k_idx, k_sc, ws.keys + (int64_t)i * n_elem, sh_hist,
+                                                                sh_pool);
+        else
+            reindex_score_chunks_lp<MX, kScoreNT / kWave, false>(grp * cpw, (grp + 1) * cpw, n, row0, qpool,
+                                                                 pool_blocks, qf, k_idx, k_sc,
+                                                                 ws.keys + (int64_t)i * n_elem, sh_hist, nullptr);
     } else {
         QFrag qf;
         load_qfrag(qf, q_idx + (int64_t)i * n_heads * 64, w + (int64_t)i * n_heads, n_heads, lane);
@@ -1299,7 +1315,7 @@ hipError_t launch_index_reindex(const uint16_t* q_idx, const float* w, const voi
     const int chunks = (pool_blocks * 8 + kReindexTile - 1) / kReindexTile;
     // many queries (>= 512: a prefill chunk): a whole pool of 32 chunks per workgroup, one histogram
     // flush per query instead of one per chunk
-    const int cpw = (n_q >= 512 && chunks % 32 == 0) ? 32 : 1;
+    const int cpw = (n_q >= 512 && chunks % kReindexWholePool == 0) ? kReindexWholePool : 1;
     const dim3 grid((unsigned)(chunks / cpw * n_q));  // (query, chunk group) items, see reindex_item
     // at most 4 heads, and a prefill chunk's whole pools or a small decode batch: the
     // lane-per-position form (a lane's rows need one block id per 64 positions, where the 16-position

@@ -101,12 +101,15 @@ __device__ __forceinline__ void reindex_score_chunks(int c0, int c1, int n, int6
 // in its accumulator, so the per-position epilogue (ReLU-weighted sum, key, store, histogram)
 // runs once per position instead of in one lane of four.  Wave wid takes steps 2 wid, 2 wid + 1
 // of each chunk (both steps' loads in flight).
-template <bool MX, int NW>
+// STAGED: the block ids of chunks c0 .. c1 - 1 are already in LDS (lpool[k] = block id of pool
+// slot c0 * kReindexTile / 8 + k), so that each chunk's rows wait on one memory latency instead
+// of two (a workgroup that scores many chunks stages them once); otherwise they come from qpool.
+template <bool MX, int NW, bool STAGED>
 __device__ __forceinline__ void reindex_score_chunks_lp(int c0, int c1, int n, int64_t row0,
                                                         const int32_t* __restrict__ qpool, int pool_blocks,
                                                         const QFragLP& qf, const void* __restrict__ k_idx,
                                                         const uint8_t* __restrict__ k_sc, uint32_t* __restrict__ keys,
-                                                        uint32_t* sh_hist) {
+                                                        uint32_t* sh_hist, const int32_t* lpool) {
     const int lane = __lane_id();
     const int wid = threadIdx.x / kWave;
     constexpr int kSteps = kReindexTile / 64 / NW;  // 64-position steps per wave per chunk
@@ -119,7 +122,10 @@ __device__ __forceinline__ void reindex_score_chunks_lp(int c0, int c1, int n, i
 #pragma unroll
         for (int j = 0; j < kSteps; ++j) {
             slot[j] = chunk * (kReindexTile / 8) + 8 * (kSteps * wid + j) + (lane >> 3);
-            blk[j] = slot[j] < pool_blocks ? qpool[slot[j]] : -1;
+            if constexpr (STAGED)
+                blk[j] = slot[j] < pool_blocks ? lpool[slot[j] - c0 * (kReindexTile / 8)] : -1;
+            else
+                blk[j] = slot[j] < pool_blocks ? qpool[slot[j]] : -1;
         }
         if (n > 0) {
             // absent rows read the sequence's first row (n > 0) and are masked below
