@@ -946,8 +946,23 @@ __global__ __launch_bounds__(NT) void k_idx_select_full(QMeta* qmeta, uint32_t* 
     if (small) {
         SmallSel<CAP, MS>& W = U.small;
         if (!scan_keys) {
-            for (int e = t; e < th.in_bucket; e += NT) W.cand[e] = cand[e];
-            for (int j = t; j < n_sure; j += NT) W.sel[j] = (uint32_t)sure[j];
+            // both lists requested before either is stored (clamped indices): one memory
+            // latency, not one per NT elements of each
+            constexpr int kPc = CAP / NT, kPs = (MS + NT - 1) / NT;
+            const int inb = th.in_bucket;
+            uint64_t cv[kPc];
+            int32_t sv[kPs];
+#pragma unroll
+            for (int k = 0; k < kPc; ++k)  // (k * NT < inb is uniform: no load past the list's last slot group)
+                cv[k] = k * NT < inb ? cand[min(k * NT + t, inb - 1)] : 0ull;
+#pragma unroll
+            for (int k = 0; k < kPs; ++k) sv[k] = k * NT < n_sure ? sure[min(k * NT + t, n_sure - 1)] : 0;
+#pragma unroll
+            for (int k = 0; k < kPc; ++k)
+                if (k * NT + t < inb) W.cand[k * NT + t] = cv[k];
+#pragma unroll
+            for (int k = 0; k < kPs; ++k)
+                if (k * NT + t < n_sure) W.sel[k * NT + t] = (uint32_t)sv[k];
         }
         if (t == 0) {
             W.cnt = n_sure;
@@ -1019,16 +1034,26 @@ __global__ __launch_bounds__(NT) void k_idx_select_cands(QMeta* qmeta, uint32_t*
             W.R.inb = 0;  // (counts the bucket's fill until the radix passes)
         }
         __syncthreads();
-        for (int e = t; e < m; e += NT) {
-            const uint64_t c = cand[e];
-            const int d = (int)(c >> 53);
-            // (the histogram counts exactly these candidates: the slots stay below above / in_bucket)
-            if (d > th.digit) {
-                const int j = atomicAdd(&W.cnt, 1);
-                if (j < top_k) W.sel[j] = composite_pos(c);
-            } else if (d == th.digit) {
-                const int j = atomicAdd(&W.R.inb, 1);
-                if (j < CAP) W.cand[j] = c;
+        // kPre candidates per thread are requested before any is examined (clamped indices, no
+        // branch around the loads): one memory latency per kPre * NT candidates, not per NT
+        constexpr int kPre = 16;
+        for (int e0 = 0; e0 < m; e0 += kPre * NT) {
+            uint64_t cv[kPre];
+#pragma unroll
+            for (int k = 0; k < kPre; ++k) cv[k] = cand[min(e0 + k * NT + t, m - 1)];
+#pragma unroll
+            for (int k = 0; k < kPre; ++k) {
+                if (e0 + k * NT + t >= m) continue;
+                const uint64_t c = cv[k];
+                const int d = (int)(c >> 53);
+                // (the histogram counts exactly these candidates: the slots stay below above / in_bucket)
+                if (d > th.digit) {
+                    const int j = atomicAdd(&W.cnt, 1);
+                    if (j < top_k) W.sel[j] = composite_pos(c);
+                } else if (d == th.digit) {
+                    const int j = atomicAdd(&W.R.inb, 1);
+                    if (j < CAP) W.cand[j] = c;
+                }
             }
         }
         __syncthreads();
