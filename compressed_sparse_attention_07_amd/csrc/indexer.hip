@@ -585,7 +585,15 @@ __global__ __launch_bounds__(kScoreNT) void k_idx_block_hist(const int64_t* __re
     __syncthreads();
     const uint32_t* bk = ws.bkeys + (int64_t)qm.start * kFullTile / 8;
     const int b1 = min(nb, b0 + kBhChunk);
-    for (int b = b0 + t; b < b1; b += kScoreNT) atomicAdd(&sh[bk[b] >> 21], 1u);
+    // every block key of the thread requested before the first is counted (clamped indices, no
+    // branch around the loads): one memory latency rather than one per kScoreNT keys
+    constexpr int kPer = kBhChunk / kScoreNT;
+    uint32_t v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) v[k] = bk[min(b0 + k * kScoreNT + t, b1 - 1)];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        if (b0 + k * kScoreNT + t < b1) atomicAdd(&sh[v[k] >> 21], 1u);
     __syncthreads();
     uint32_t* gh = ws.hist + (int64_t)i * 2 * kHistBins + kHistBins;
     for (int b = t; b < kHistBins; b += kScoreNT)
