@@ -123,13 +123,16 @@ __device__ __forceinline__ void score_full_body(
     uint32_t* pend_k = nullptr;
     uint32_t* pend_b = nullptr;
     int pend_j = 0;
+    // (the key runs are stored non-temporally, streamed past the caches: 1M x 8 queries 186 ->
+    // 178 us; the block keys, an eighth as many, stay cached)
+    typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
     auto write_run = [&]() {
         if (pend_j > 0) {  // (uniform) batch q's 16U keys go to pend_k + q 64U, from lanes 32 (q & 1) ..
             for (int q0 = 0; q0 < pend_j; q0 += 2) {
                 const int q = q0 + (lane >> 5);
                 if (q < pend_j)
-                    *reinterpret_cast<uint4*>(pend_k + q * 64 * U + 4 * (lane & 31)) =
-                        *reinterpret_cast<const uint4*>(s_key + q * WR + 4 * (lane & 31));
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4_nt*>(s_key + q * WR + 4 * (lane & 31)),
+                                                reinterpret_cast<u32x4_nt*>(pend_k + q * 64 * U + 4 * (lane & 31)));
             }
             if (want_pool && lane < pend_j * (WR / 32)) {  // batch q's 2U block keys, 4 per lane
                 const int q = lane / (WR / 32), c = lane % (WR / 32);
