@@ -614,7 +614,7 @@ __device__ __forceinline__ void load_quads(uint4 (&q)[U], const uint32_t* keys, 
     const int n = e_end > e0 ? e_end - e0 : 0;
     const BufRsrc rs = tile_rsrc(keys + e0, ((n + 3) & ~3) * 4);
 #pragma unroll
-    for (int u = 0; u < U; ++u) q[u] = buf_ld16(rs, 16 * (u * NT + (int)threadIdx.x), 0);
+    for (int u = 0; u < U; ++u) q[u] = buf_ld16_nt(rs, 16 * (u * NT + (int)threadIdx.x), 0);  // (read once)
 }
 
 template <int NT, int U>
